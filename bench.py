@@ -1,0 +1,296 @@
+"""Throughput of the routed MoE layer on one MI355X, against the HBM roofline.
+
+Default workload: a gpt-oss-20B-shaped MoE layer (hidden 2880, 32 experts,
+expert width 2880, top-4, logit bias, SwiGLU clamp 7, Q8_0 experts, bf16 x),
+decoding M = 1 token per call.  One step = one moe_forward call (router GEMV,
+top-k, permutation, gate/up + SwiGLU, down + combine) on resident inputs.
+
+Layer copies are rotated so that the 256 MB MALL cannot hold the touched
+weights across calls; copy 0 comes from the seeded host generator, the others
+are drawn on the device with the same distributions (timing only).
+
+Prints one JSON line.  `roofline` is for the dominant kernel (gate/up), timed
+with HIP events recorded between the layer's kernels; `cpu_baseline` times
+the fp64 CPU oracle on a bounded sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE layer tokens/s at M=1/16/2048 + % of HBM / MFMA roofline"
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFS = 2500.0
+
+
+# ------------------------------------------------------------------ HIP events
+class HipEvents:
+    def __init__(self, n: int):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.ev = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            assert self.hip.hipEventCreate(ctypes.byref(e)) == 0
+            self.ev.append(e.value)
+
+    def elapsed_ms(self, a: int, b: int) -> float:
+        ms = ctypes.c_float()
+        rc = self.hip.hipEventElapsedTime(ctypes.byref(ms), self.ev[a], self.ev[b])
+        assert rc == 0, f"hipEventElapsedTime failed ({rc})"
+        return ms.value
+
+    def close(self):
+        for e in self.ev:
+            self.hip.hipEventDestroy(e)
+
+
+# ------------------------------------------------------------------ workload
+def bytes_per_weight(dtype: int) -> float:
+    return {0: 4.0, 1: 2.0, 2: 34.0 / 32.0}[dtype]
+
+
+def algorithmic_bytes(spec, M: int, counts: np.ndarray) -> dict:
+    """Bytes the layer must move per call (weights of touched experts once)."""
+    H, E, I, Is = spec.hidden, spec.num_experts, spec.expert_inter, spec.shared_inter
+    T = int((counts > 0).sum())
+    bpw = bytes_per_weight(spec.expert_dtype)
+    bpx = 4 if spec.x_dtype == 0 else 2
+    R = M * spec.top_k
+    gate_up = T * 2 * H * I * bpw + (2 * H * Is * bytes_per_weight(spec.shared_dtype) if Is else 0)
+    down = T * H * I * bpw + (H * Is * bytes_per_weight(spec.shared_dtype) if Is else 0)
+    router = H * E * bytes_per_weight(spec.router_dtype) + (4 * E if spec.bias_mode else 0)
+    layer = gate_up + down + router + M * H * bpx + 4 * M * H
+    return {"layer": layer, "gateup_kernel": gate_up + M * H * bpx + 4 * (R * I + M * Is),
+            "touched": T}
+
+
+def algorithmic_flops(spec, M: int) -> float:
+    H, E, I, Is, k = spec.hidden, spec.num_experts, spec.expert_inter, spec.shared_inter, spec.top_k
+    return M * k * 6 * H * I + 2 * M * H * E + M * 6 * H * Is
+
+
+def device_copy(spec, dev, rng_seed: int):
+    """Random layer tensors with the host generator's distributions (timing only)."""
+    import torch
+    g = torch.Generator(device=dev)
+    g.manual_seed(rng_seed)
+    H, E, I, Is = spec.hidden, spec.num_experts, spec.expert_inter, spec.shared_inter
+
+    def mat(rows, cols, dtype):
+        if dtype == 2:
+            q = torch.randint(-127, 128, (rows * cols,), generator=g, device=dev, dtype=torch.int8)
+            d = torch.empty(rows * cols // 32, device=dev, dtype=torch.float32)
+            d.uniform_(spec.q8_scale_lo, spec.q8_scale_hi, generator=g)
+            return q, d.half().view(torch.int16)
+        t = torch.empty(rows * cols, device=dev, dtype=torch.float32).normal_(0.0, spec.weight_std, generator=g)
+        return (t.bfloat16() if dtype == 1 else t), None
+
+    out = {}
+    out["router"], _ = mat(E, H, spec.router_dtype)
+    if spec.bias_mode:
+        out["bias"] = (torch.empty(E, device=dev).normal_(0.0, spec.bias_std, generator=g)
+                       .bfloat16().float())
+    for name, rows, cols in (("gate", E * I, H), ("up", E * I, H), ("down", E * H, I)):
+        t, s = mat(rows, cols, spec.expert_dtype)
+        out[name] = t
+        if s is not None:
+            out[name + "_scale"] = s
+    if Is:
+        for name, rows, cols in (("shared_gate", Is, H), ("shared_up", Is, H), ("shared_down", H, Is)):
+            t, s = mat(rows, cols, spec.shared_dtype)
+            out[name] = t
+            if s is not None:
+                out[name + "_scale"] = s
+    return out
+
+
+def layer_bytes(spec) -> float:
+    H, E, I, Is = spec.hidden, spec.num_experts, spec.expert_inter, spec.shared_inter
+    return 3 * E * H * I * bytes_per_weight(spec.expert_dtype) + 3 * H * Is * 2
+
+
+def cpu_baseline(spec, host_layer, M: int, budget_s: float) -> dict:
+    """Time the fp64 CPU oracle on successive M-token calls until ~budget_s."""
+    import oracle
+    import synth
+    calls = 0
+    t0 = time.perf_counter()
+    while True:
+        x = synth.make_tokens(spec, M, batch=100 + calls)
+        oracle.forward(spec, host_layer, x)
+        calls += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or calls >= 64:
+            break
+    threads = oracle.threads()
+    used = min(threads, M)  # the oracle's expert loop is parallel over tokens
+    return {"value": calls * M / el, "unit": "tokens/s", "cores": used, "kind": "oracle",
+            "sample": f"{calls} calls of M={M} token(s) of the same layer ({el:.1f} s); "
+                      f"expert work parallel over tokens, {threads} threads available"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="gpt-oss-20b")
+    ap.add_argument("--tokens", type=int, default=None, help="M per call (default: first of the workload)")
+    ap.add_argument("--layers", type=int, default=None, help="layer copies to rotate")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(this build has no multi-GPU path)", file=sys.stderr)
+        return 2
+
+    import torch
+    import synth
+    import mixture_experts_gemv_amd as m
+    from mixture_experts_gemv_amd.layer import MoeLayer
+
+    spec = synth.SPECS[args.workload]
+    M = args.tokens or spec.token_counts[0]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    t_setup = time.perf_counter()
+    host = synth.make_layer(spec)
+    kw = dict(hidden=spec.hidden, num_experts=spec.num_experts, top_k=spec.top_k,
+              expert_inter=spec.expert_inter, shared_inter=spec.shared_inter, select=spec.select,
+              bias_mode=spec.bias_mode, swiglu_limit=spec.swiglu_limit, rms_eps=spec.rms_eps,
+              x_dtype=spec.x_dtype, router_dtype=spec.router_dtype, expert_dtype=spec.expert_dtype,
+              shared_dtype=spec.shared_dtype, max_tokens=M, device=dev)
+    base = MoeLayer(**kw).load(host["router"], host["bias"], host["gate"], host["up"], host["down"],
+                               host.get("shared_gate"), host.get("shared_up"), host.get("shared_down"))
+    # estimate touched bytes with a realised call, then size the rotation
+    x0 = base.x_tensor(synth.make_tokens(spec, M, batch=0))
+    cnt = torch.empty(spec.num_experts, dtype=torch.int32, device=dev)
+    base.forward(x0, counts=cnt)
+    touched = algorithmic_bytes(spec, M, cnt.cpu().numpy())["layer"]
+    L = args.layers or max(2, math.ceil(2 ** 30 / touched) + 1)
+    copies = [base]
+    for c in range(1, L):
+        copies.append(MoeLayer(**kw).load_tensors(device_copy(spec, dev, 7919 * c)))
+    P = 64 if M == 1 else (8 if M <= 16 else 2)
+    xs = [base.x_tensor(synth.make_tokens(spec, M, batch=b)) for b in range(P)]
+    ws = base.workspace(M)
+    y = torch.empty(M, spec.hidden, dtype=torch.float32, device=dev)
+    counts = [torch.empty(spec.num_experts, dtype=torch.int32, device=dev) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    setup_s = time.perf_counter() - t_setup
+
+    K, W = args.steps, args.warmup
+
+    def step(i, cnt_out=None):
+        lay = copies[i % L]
+        m.moe_forward(lay.plan, xs[i % P], lay.weights, M, y, None, None, cnt_out, ws)
+
+    # realised expert counts of exactly the timed calls (untimed pre-pass)
+    for i in range(K):
+        step(i, counts[i])
+    torch.cuda.synchronize()
+    ab = [algorithmic_bytes(spec, M, c.cpu().numpy()) for c in counts]
+    layer_bytes_avg = float(np.mean([a["layer"] for a in ab]))
+    gateup_bytes_avg = float(np.mean([a["gateup_kernel"] for a in ab]))
+    touched_avg = float(np.mean([a["touched"] for a in ab]))
+
+    # ---- timed region: whole layer
+    for i in range(W):
+        step(i)
+    ev = HipEvents(2)
+    torch.cuda.synchronize()
+    hip = ev.hip
+    hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    stream = torch.cuda.current_stream().cuda_stream
+    hip.hipEventRecord(ev.ev[0], stream)
+    for i in range(K):
+        step(i)
+    hip.hipEventRecord(ev.ev[1], stream)
+    torch.cuda.synchronize()
+    total_ms = ev.elapsed_ms(0, 1)
+    ms_per_step = total_ms / K
+
+    # ---- timed region: per kernel (events between the layer's kernels)
+    n_ev = 8
+    kev = HipEvents(n_ev * K)
+    stages = None
+    for i in range(W):
+        step(i)
+    torch.cuda.synchronize()
+    for i in range(K):
+        lay = copies[i % L]
+        st = m.moe_forward_timed(lay.plan, xs[i % P], lay.weights, M, y, None, None, None, ws,
+                                 kev.ev[i * n_ev:(i + 1) * n_ev])
+        stages = st
+    torch.cuda.synchronize()
+    per_stage = {}
+    for j, sid in enumerate(stages):
+        d = [kev.elapsed_ms(i * n_ev + j, i * n_ev + j + 1) for i in range(K)]
+        per_stage[m.MOE_STAGE_NAMES[sid]] = float(np.mean(d)) * 1e3  # us
+    timed_total_us = float(np.mean([kev.elapsed_ms(i * n_ev, i * n_ev + len(stages)) for i in range(K)])) * 1e3
+    kev.close()
+    ev.close()
+
+    gateup_us = per_stage.get("gateup")
+    achieved = gateup_bytes_avg / (gateup_us * 1e-6) / 1e9
+    layer_gbs = layer_bytes_avg / (ms_per_step * 1e-3) / 1e9
+    flops = algorithmic_flops(spec, M)
+    result = {
+        "metric": METRIC,
+        "value": M * K / (total_ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{spec.name}-shaped routed MoE layer, M={M} tokens per call",
+            "hidden": spec.hidden, "num_experts": spec.num_experts, "top_k": spec.top_k,
+            "expert_inter": spec.expert_inter, "shared_inter": spec.shared_inter,
+            "expert_weights": {0: "f32", 1: "bf16", 2: "q8_0"}[spec.expert_dtype],
+            "tokens_per_call": M, "layer_copies": L, "token_batches": P,
+            "touched_experts_avg": touched_avg,
+        },
+        "roofline": {
+            "bound": "hbm", "kernel": "gate/up + SwiGLU (k_gateup_gemv)",
+            "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+            "bytes_per_launch": gateup_bytes_avg, "us_per_launch": gateup_us,
+        },
+        "layer": {
+            "algorithmic_bytes": layer_bytes_avg, "achieved_GBs": layer_gbs,
+            "hbm_frac": layer_gbs / HBM_PEAK_GBS,
+            "mfma_frac": flops / (ms_per_step * 1e-3) / (MFMA_BF16_PEAK_TFS * 1e12),
+            "kernel_us": per_stage, "timed_sum_us": timed_total_us,
+        },
+        "setup_s": setup_s,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(spec, host, M, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,137 @@
+// Internal device helpers shared by the HIP kernels of the routed MoE layer.
+// Target: CDNA4 (gfx950), wave64.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kWave = 64;
+
+enum Dtype : int { DT_F32 = 0, DT_BF16 = 1, DT_Q8 = 2 };
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------- conversions
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+__device__ __forceinline__ float f16_bits_to_f32(uint16_t h) {
+    return (float)__builtin_bit_cast(_Float16, h);
+}
+
+// Sign-extended byte b of a 32-bit word, as float.
+template <int B>
+__device__ __forceinline__ float i8_to_f32(uint32_t w) {
+    return (float)(int32_t)((int32_t)(w << (24 - 8 * B)) >> 24);
+}
+
+// ---------------------------------------------------------- wave reductions
+// DPP controls: quad_perm(1,0,3,2), quad_perm(2,3,0,1), row_half_mirror,
+// row_mirror; then a ds_swizzle xor-16 across the 32-lane halves and a
+// readlane of lanes 0 and 32.  Every step pairs each lane with exactly one
+// partner, so every lane ends with the same, order-fixed result.
+__device__ __forceinline__ int dpp_xor1(int v) { return __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false); }
+__device__ __forceinline__ int dpp_xor2(int v) { return __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false); }
+__device__ __forceinline__ int dpp_hmirror(int v) { return __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false); }
+__device__ __forceinline__ int dpp_mirror(int v) { return __builtin_amdgcn_update_dpp(0, v, 0x140, 0xF, 0xF, false); }
+__device__ __forceinline__ int swz_xor16(int v) { return __builtin_amdgcn_ds_swizzle(v, 0x401F); }
+
+struct OpSum { __device__ float operator()(float a, float b) const { return a + b; } };
+struct OpMaxF { __device__ float operator()(float a, float b) const { return fmaxf(a, b); } };
+
+// All-reduce of a float over the 64 lanes; requires all lanes active.
+template <class Op>
+__device__ __forceinline__ float wave_reduce(float v, Op op) {
+    v = op(v, __int_as_float(dpp_xor1(__float_as_int(v))));
+    v = op(v, __int_as_float(dpp_xor2(__float_as_int(v))));
+    v = op(v, __int_as_float(dpp_hmirror(__float_as_int(v))));
+    v = op(v, __int_as_float(dpp_mirror(__float_as_int(v))));
+    v = op(v, __int_as_float(swz_xor16(__float_as_int(v))));
+    float lo = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    float hi = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+    return op(lo, hi);
+}
+__device__ __forceinline__ float wave_sum(float v) { return wave_reduce(v, OpSum()); }
+__device__ __forceinline__ float wave_max(float v) { return wave_reduce(v, OpMaxF()); }
+
+__device__ __forceinline__ uint32_t umax32(uint32_t a, uint32_t b) { return a > b ? a : b; }
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    v = umax32(v, (uint32_t)dpp_xor1((int)v));
+    v = umax32(v, (uint32_t)dpp_xor2((int)v));
+    v = umax32(v, (uint32_t)dpp_hmirror((int)v));
+    v = umax32(v, (uint32_t)dpp_mirror((int)v));
+    v = umax32(v, (uint32_t)swz_xor16((int)v));
+    return umax32((uint32_t)__builtin_amdgcn_readlane((int)v, 0),
+                  (uint32_t)__builtin_amdgcn_readlane((int)v, 32));
+}
+
+__device__ __forceinline__ int wave_min_i32(int v) {
+    v = min(v, dpp_xor1(v));
+    v = min(v, dpp_xor2(v));
+    v = min(v, dpp_hmirror(v));
+    v = min(v, dpp_mirror(v));
+    v = min(v, swz_xor16(v));
+    return min(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 32));
+}
+
+// fp32 -> uint32 whose unsigned order is the float order (-0 taken as +0).
+__device__ __forceinline__ uint32_t order_key(float f) {
+    uint32_t b = __float_as_uint(f);
+    if (b == 0x80000000u) b = 0u;
+    return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+__device__ __forceinline__ float silu_mul(float g, float v) {
+    return g / (1.0f + __expf(-g)) * v;
+}
+
+__device__ __forceinline__ float clampf(float v, float lim) {
+    return fminf(fmaxf(v, -lim), lim);
+}
+
+// ---------------------------------------------------------- 16-byte chunk loads
+// A "chunk" is the elements one lane takes per 16-byte weight load:
+// 4 fp32, 8 bf16 or 16 Q8_0 int8 values (half a Q8_0 block).
+template <int DT> struct Chunk;
+template <> struct Chunk<DT_F32> { static constexpr int N = 4; };
+template <> struct Chunk<DT_BF16> { static constexpr int N = 8; };
+template <> struct Chunk<DT_Q8> { static constexpr int N = 16; };
+
+// Load chunk c of a weight row into floats (Q8_0: the raw q values; the
+// caller applies the block scale).
+template <int DT>
+__device__ __forceinline__ void load_chunk(const void *row, int c, float *w);
+
+template <>
+__device__ __forceinline__ void load_chunk<DT_F32>(const void *row, int c, float *w) {
+    f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(row) + c);
+    w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+}
+template <>
+__device__ __forceinline__ void load_chunk<DT_BF16>(const void *row, int c, float *w) {
+    u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(row) + c);
+    w[0] = bf16_lo(v.x); w[1] = bf16_hi(v.x); w[2] = bf16_lo(v.y); w[3] = bf16_hi(v.y);
+    w[4] = bf16_lo(v.z); w[5] = bf16_hi(v.z); w[6] = bf16_lo(v.w); w[7] = bf16_hi(v.w);
+}
+template <>
+__device__ __forceinline__ void load_chunk<DT_Q8>(const void *row, int c, float *w) {
+    u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(row) + c);
+    const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        w[4 * i + 0] = i8_to_f32<0>(d[i]);
+        w[4 * i + 1] = i8_to_f32<1>(d[i]);
+        w[4 * i + 2] = i8_to_f32<2>(d[i]);
+        w[4 * i + 3] = i8_to_f32<3>(d[i]);
+    }
+}
+
+// Bytes of one stored element (Q8_0: the int8 plane only).
+template <int DT> __host__ __device__ constexpr int elem_bytes() { return DT == DT_F32 ? 4 : (DT == DT_BF16 ? 2 : 1); }
+
+} // namespace moe

@@ -1,0 +1,73 @@
+// Internal launchers of the routed MoE kernels (host side).  Each returns the
+// HIP error of its launch.  All pointers are device pointers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+struct Layer {
+    int H, E, k, I, Is;
+    int select, bias_mode;
+    float limit, eps;
+    int xdt, rdt, edt, sdt; // DT_F32 / DT_BF16 / DT_Q8
+};
+
+// Weights of a set of SwiGLU experts: gate/up [n][W][H], down [n][H][W].
+struct Mats {
+    const void *gate, *up, *down;
+    const uint16_t *gate_s, *up_s, *down_s; // Q8_0 scale planes or null
+};
+
+// Routing state produced by the permutation.
+struct Routing {
+    const int32_t *offsets;       // [E+1]
+    const int32_t *sorted;        // [R]
+    const int32_t *route_pos;     // [R]
+    const int32_t *active;        // [1+E]: count, then touched experts ascending
+    const int32_t *tiles;         // [1+2*T]: count, then (expert, first sorted row)
+};
+
+hipError_t launch_rms_scale(const Layer &L, const void *x, int M, float *scale, hipStream_t s);
+hipError_t launch_router(const Layer &L, const void *x, const void *router, const float *tok_scale,
+                         int M, float *logits, hipStream_t s);
+hipError_t launch_topk(const Layer &L, const float *logits, const float *bias, int M, int32_t *ids,
+                       float *w, hipStream_t s);
+hipError_t launch_permute(int E, int R, int tile_rows, const int32_t *ids, int32_t *counts,
+                          int32_t *offsets, int32_t *sorted, int32_t *route_pos, int32_t *active,
+                          int32_t *tiles, hipStream_t s);
+// Derive the active-expert list and the tile list from offsets alone.
+hipError_t launch_plan_from_offsets(int E, int tile_rows, const int32_t *offsets, int32_t *active,
+                                    int32_t *tiles, hipStream_t s);
+
+// GEMV path.
+hipError_t launch_gateup_gemv(const Layer &L, const void *x, const float *tok_scale, const Mats &routed,
+                              const Mats &shared, const Routing &rt, int M, float *act,
+                              float *shared_act, hipStream_t s);
+hipError_t launch_down_gemv(const Layer &L, const float *act, const float *shared_act,
+                            const Mats &routed, const Mats &shared, const Routing &rt,
+                            const float *w, const float *seed, int M, float *y, float *y_routes,
+                            float *y_shared, hipStream_t s);
+// Per-route down projection (no combine): y_routes [R][H], y_shared [M][H].
+hipError_t launch_down_routes_gemv(const Layer &L, const float *act, const float *shared_act,
+                                   const Mats &routed, const Mats &shared, const Routing &rt, int M,
+                                   float *y_routes, float *y_shared, hipStream_t s);
+// y[t] = seed[t] + y_shared[t] + sum_j w[t][j] * y_routes[route_pos[t*k+j]]
+hipError_t launch_combine(const Layer &L, const float *y_routes, const float *y_shared,
+                          const int32_t *route_pos, const float *w, const float *seed, int M,
+                          float *y, hipStream_t s);
+
+// MFMA grouped-GEMM path (bf16 x and experts).
+int mfma_tile_rows();
+hipError_t launch_gateup_mfma(const Layer &L, const void *x, const float *tok_scale, const Mats &routed,
+                              const Mats &shared, const Routing &rt, int M, int max_tiles,
+                              float *act, float *shared_act, hipStream_t s);
+hipError_t launch_down_mfma(const Layer &L, const float *act, const float *shared_act,
+                            const Mats &routed, const Mats &shared, const Routing &rt, int M,
+                            int max_tiles, float *y_routes, float *y_shared, hipStream_t s);
+
+hipError_t launch_q8_split(const void *blocks, int64_t rows, int cols, int8_t *qs,
+                           uint16_t *scales, hipStream_t s);
+
+} // namespace moe

@@ -1,0 +1,490 @@
+// C ABI of the routed MoE layer: plan creation and validation, workspace
+// layout, and the enqueueing of the kernels for each entry point.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "common.h"
+#include "launch.h"
+#include "moe_gemv.h"
+
+struct moe_plan {
+    moe_config cfg;
+    moe::Layer L;
+    bool mfma_capable;
+};
+
+namespace {
+
+thread_local std::string g_err;
+
+moe_status fail(moe_status st, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return st;
+}
+
+moe_status hip_fail(hipError_t e, const char *what) {
+    return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+constexpr size_t kAlign = 256;
+size_t up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+// Where each workspace region starts for a call with M tokens.
+struct WsLayout {
+    size_t tok_scale, logits, ids, w, counts, offsets, sorted, route_pos, active, tiles;
+    size_t act, shared_act, y_routes, y_shared, total;
+    int max_tiles;
+};
+
+bool use_mfma(const moe_plan *p, int M) {
+    if (!p->mfma_capable) return false;
+    if (p->cfg.path == MOE_PATH_MFMA) return true;
+    if (p->cfg.path == MOE_PATH_GEMV) return false;
+    const long routes = (long)M * p->L.k;
+    return M >= 64 && routes >= 16L * p->L.E;
+}
+
+WsLayout layout(const moe_plan *p, int M) {
+    const moe::Layer &L = p->L;
+    const size_t R = (size_t)M * L.k;
+    const bool mfma = use_mfma(p, M);
+    const bool unfused = mfma || M > 64;
+    WsLayout w{};
+    size_t o = 0;
+    auto take = [&](size_t bytes) { size_t at = o; o += up(bytes); return at; };
+    w.tok_scale = take(L.eps > 0.f ? (size_t)M * 4 : 0);
+    w.logits = take((size_t)M * L.E * 4);
+    w.ids = take(R * 4);
+    w.w = take(R * 4);
+    w.counts = take((size_t)L.E * 4);
+    w.offsets = take((size_t)(L.E + 1) * 4);
+    w.sorted = take(R * 4);
+    w.route_pos = take(R * 4);
+    w.active = take((size_t)(L.E + 1) * 4);
+    const int tile_rows = moe::mfma_tile_rows();
+    w.max_tiles = mfma ? (int)(R / tile_rows + (R < (size_t)L.E ? R : (size_t)L.E) + 1) : 0;
+    w.tiles = take(mfma ? (size_t)(1 + 2 * w.max_tiles) * 4 : 4 * 3);
+    w.act = take(R * L.I * 4);
+    w.shared_act = take(L.Is > 0 ? (size_t)M * L.Is * 4 : 0);
+    w.y_routes = take(unfused ? R * L.H * 4 : 0);
+    w.y_shared = take(unfused && L.Is > 0 ? (size_t)M * L.H * 4 : 0);
+    w.total = o;
+    return w;
+}
+
+template <class T> T *at(void *ws, size_t off) { return reinterpret_cast<T *>(reinterpret_cast<char *>(ws) + off); }
+
+moe::Mats routed_mats(const moe_weights *w) {
+    return moe::Mats{w->gate, w->up, w->down, w->gate_scale, w->up_scale, w->down_scale};
+}
+moe::Mats shared_mats(const moe_weights *w) {
+    return moe::Mats{w->shared_gate, w->shared_up, w->shared_down, w->shared_gate_scale,
+                     w->shared_up_scale, w->shared_down_scale};
+}
+
+moe_status check_call(const moe_plan *p, int32_t M, void *ws, size_t ws_bytes) {
+    if (!p) return fail(MOE_ERR_INVALID, "plan is NULL");
+    if (M < 0 || M > p->cfg.max_tokens)
+        return fail(MOE_ERR_INVALID, "M = %d outside 0..max_tokens (%d)", M, p->cfg.max_tokens);
+    if (M == 0) return MOE_OK;
+    const size_t need = layout(p, M).total;
+    if (ws_bytes < need)
+        return fail(MOE_ERR_WORKSPACE, "workspace holds %zu bytes; M = %d needs %zu", ws_bytes, M, need);
+    if (!ws) return fail(MOE_ERR_INVALID, "workspace is NULL");
+    if (!aligned(ws, kAlign)) return fail(MOE_ERR_INVALID, "workspace is not 256-byte aligned");
+    return MOE_OK;
+}
+
+moe_status need_ptr(const void *ptr, size_t align, const char *name) {
+    if (!ptr) return fail(MOE_ERR_INVALID, "%s is NULL", name);
+    if (!aligned(ptr, align)) return fail(MOE_ERR_INVALID, "%s is not %zu-byte aligned", name, align);
+    return MOE_OK;
+}
+
+#define TRY(expr)                                   \
+    do {                                            \
+        moe_status st_ = (expr);                    \
+        if (st_ != MOE_OK) return st_;              \
+    } while (0)
+
+#define LAUNCH(expr, what)                          \
+    do {                                            \
+        hipError_t e_ = (expr);                     \
+        if (e_ != hipSuccess) return hip_fail(e_, what); \
+    } while (0)
+
+moe_status check_experts(const moe_plan *p, const moe_weights *w, bool need_gateup, bool need_down,
+                         bool need_shared) {
+    if (!w) return fail(MOE_ERR_INVALID, "weights is NULL");
+    const bool q8 = p->L.edt == moe::DT_Q8;
+    if (need_gateup) {
+        TRY(need_ptr(w->gate, 16, "weights.gate"));
+        TRY(need_ptr(w->up, 16, "weights.up"));
+        if (q8) {
+            TRY(need_ptr(w->gate_scale, 2, "weights.gate_scale"));
+            TRY(need_ptr(w->up_scale, 2, "weights.up_scale"));
+        }
+    }
+    if (need_down) {
+        TRY(need_ptr(w->down, 16, "weights.down"));
+        if (q8) TRY(need_ptr(w->down_scale, 2, "weights.down_scale"));
+    }
+    if (need_shared && p->L.Is > 0) {
+        const bool sq8 = p->L.sdt == moe::DT_Q8;
+        TRY(need_ptr(w->shared_gate, 16, "weights.shared_gate"));
+        TRY(need_ptr(w->shared_up, 16, "weights.shared_up"));
+        TRY(need_ptr(w->shared_down, 16, "weights.shared_down"));
+        if (sq8) {
+            TRY(need_ptr(w->shared_gate_scale, 2, "weights.shared_gate_scale"));
+            TRY(need_ptr(w->shared_up_scale, 2, "weights.shared_up_scale"));
+            TRY(need_ptr(w->shared_down_scale, 2, "weights.shared_down_scale"));
+        }
+    }
+    return MOE_OK;
+}
+
+moe_status check_router(const moe_plan *p, const moe_weights *w, bool need_router) {
+    if (!w) return fail(MOE_ERR_INVALID, "weights is NULL");
+    if (need_router) TRY(need_ptr(w->router, 16, "weights.router"));
+    if (p->L.bias_mode != MOE_BIAS_NONE) TRY(need_ptr(w->bias, 4, "weights.bias"));
+    return MOE_OK;
+}
+
+} // namespace
+
+extern "C" {
+
+const char *moe_last_error(void) { return g_err.c_str(); }
+
+moe_status moe_plan_create(const moe_config *c, moe_plan **out) {
+    if (!c || !out) return fail(MOE_ERR_INVALID, "config or plan pointer is NULL");
+    *out = nullptr;
+    if (c->num_experts < 1 || c->top_k < 1)
+        return fail(MOE_ERR_INVALID, "num_experts (%d) and top_k (%d) must both be positive", c->num_experts, c->top_k);
+    if (c->top_k > c->num_experts)
+        return fail(MOE_ERR_INVALID, "top_k %d exceeds num_experts %d", c->top_k, c->num_experts);
+    if (c->hidden <= 0 || c->expert_inter <= 0 || c->shared_inter < 0)
+        return fail(MOE_ERR_INVALID, "hidden (%d) and expert_inter (%d) must be positive, shared_inter (%d) non-negative",
+                    c->hidden, c->expert_inter, c->shared_inter);
+    if (c->max_tokens < 1) return fail(MOE_ERR_INVALID, "max_tokens must be >= 1");
+    if (c->select != MOE_TOPK_SOFTMAX && c->select != MOE_SOFTMAX_ALL_NORENORM)
+        return fail(MOE_ERR_INVALID, "unknown select mode %d", c->select);
+    if (c->bias_mode < MOE_BIAS_NONE || c->bias_mode > MOE_BIAS_SELECT_ONLY)
+        return fail(MOE_ERR_INVALID, "unknown bias mode %d", c->bias_mode);
+    if (c->path < MOE_PATH_AUTO || c->path > MOE_PATH_MFMA) return fail(MOE_ERR_INVALID, "unknown path %d", c->path);
+    if (!(c->swiglu_limit >= 0.f) || !(c->rms_eps >= 0.f))
+        return fail(MOE_ERR_INVALID, "swiglu_limit and rms_eps must be >= 0");
+    auto known = [](int d) { return d == MOE_F32 || d == MOE_BF16 || d == MOE_Q8_0; };
+    if (!known(c->x_dtype) || !known(c->router_dtype) || !known(c->expert_dtype) ||
+        (c->shared_inter > 0 && !known(c->shared_dtype)))
+        return fail(MOE_ERR_INVALID, "unknown dtype");
+    if (c->top_k > 8) return fail(MOE_ERR_UNSUPPORTED, "top_k %d exceeds the 8 routing slots", c->top_k);
+    if (c->num_experts > 256) return fail(MOE_ERR_UNSUPPORTED, "num_experts %d exceeds 256", c->num_experts);
+    if (c->hidden % 32 || c->expert_inter % 32 || c->shared_inter % 32)
+        return fail(MOE_ERR_UNSUPPORTED, "hidden, expert_inter and shared_inter must be multiples of 32");
+    if (c->hidden > 16384) return fail(MOE_ERR_UNSUPPORTED, "hidden %d exceeds 16384", c->hidden);
+    if (c->x_dtype == MOE_Q8_0 || c->router_dtype == MOE_Q8_0)
+        return fail(MOE_ERR_UNSUPPORTED, "x and router must be fp32 or bf16");
+    if (c->shared_inter > 0 && c->shared_dtype != c->expert_dtype)
+        return fail(MOE_ERR_UNSUPPORTED, "the shared expert must use the routed experts' dtype");
+    if ((long)c->max_tokens * c->top_k > (1L << 30))
+        return fail(MOE_ERR_UNSUPPORTED, "max_tokens * top_k too large");
+    const bool mfma_ok = false; // the MFMA grouped GEMM is not enabled yet
+    if (c->path == MOE_PATH_MFMA && !mfma_ok)
+        return fail(MOE_ERR_UNSUPPORTED, "the MFMA path needs bf16 x and bf16 experts");
+    moe_plan *p = new moe_plan;
+    p->cfg = *c;
+    p->L = moe::Layer{c->hidden, c->num_experts, c->top_k, c->expert_inter, c->shared_inter,
+                      c->select, c->bias_mode, c->swiglu_limit, c->rms_eps,
+                      c->x_dtype, c->router_dtype, c->expert_dtype, c->shared_dtype};
+    p->mfma_capable = mfma_ok;
+    *out = p;
+    return MOE_OK;
+}
+
+void moe_plan_destroy(moe_plan *p) { delete p; }
+
+size_t moe_workspace_bytes(const moe_plan *p, int32_t M) {
+    if (!p || M < 0 || M > p->cfg.max_tokens) return 0;
+    if (M == 0) return 0;
+    return layout(p, M).total;
+}
+
+moe_status moe_route(const moe_plan *p, const void *x, const moe_weights *wts, int32_t M,
+                     float *logits, int32_t flags, int32_t *ids, float *w, void *ws,
+                     size_t ws_bytes, void *stream) {
+    TRY(check_call(p, M, ws, ws_bytes));
+    if (M == 0) return MOE_OK;
+    const bool logits_in = flags & MOE_LOGITS_IN;
+    if (flags & ~MOE_LOGITS_IN) return fail(MOE_ERR_INVALID, "unknown flags 0x%x", flags);
+    TRY(check_router(p, wts, !logits_in));
+    if (logits_in) TRY(need_ptr(logits, 4, "logits"));
+    else TRY(need_ptr(x, 16, "x"));
+    TRY(need_ptr(ids, 4, "ids"));
+    TRY(need_ptr(w, 4, "w"));
+    const moe::Layer &L = p->L;
+    const WsLayout lay = layout(p, M);
+    hipStream_t s = (hipStream_t)stream;
+    float *lg = logits ? logits : at<float>(ws, lay.logits);
+    if (!logits_in) {
+        float *sc = nullptr;
+        if (L.eps > 0.f) {
+            sc = at<float>(ws, lay.tok_scale);
+            LAUNCH(moe::launch_rms_scale(L, x, M, sc, s), "rms scale");
+        }
+        LAUNCH(moe::launch_router(L, x, wts->router, sc, M, lg, s), "router");
+    }
+    LAUNCH(moe::launch_topk(L, lg, wts->bias, M, ids, w, s), "top-k");
+    return MOE_OK;
+}
+
+moe_status moe_permute(const moe_plan *p, const int32_t *ids, int32_t M, int32_t *counts,
+                       int32_t *offsets, int32_t *sorted_routes, int32_t *route_pos, void *ws,
+                       size_t ws_bytes, void *stream) {
+    TRY(check_call(p, M, ws, ws_bytes));
+    if (M == 0) return MOE_OK;
+    TRY(need_ptr(ids, 4, "ids"));
+    TRY(need_ptr(counts, 4, "counts"));
+    TRY(need_ptr(offsets, 4, "offsets"));
+    TRY(need_ptr(sorted_routes, 4, "sorted_routes"));
+    TRY(need_ptr(route_pos, 4, "route_pos"));
+    const WsLayout lay = layout(p, M);
+    LAUNCH(moe::launch_permute(p->L.E, M * p->L.k, moe::mfma_tile_rows(), ids, counts, offsets,
+                               sorted_routes, route_pos, at<int32_t>(ws, lay.active),
+                               lay.max_tiles ? at<int32_t>(ws, lay.tiles) : nullptr, (hipStream_t)stream),
+           "permute");
+    return MOE_OK;
+}
+
+moe_status moe_expert_ffn(const moe_plan *p, const void *x, const moe_weights *wts, int32_t M,
+                          const int32_t *offsets, const int32_t *sorted_routes, float *act,
+                          void *ws, size_t ws_bytes, void *stream) {
+    TRY(check_call(p, M, ws, ws_bytes));
+    if (M == 0) return MOE_OK;
+    TRY(need_ptr(x, 16, "x"));
+    TRY(check_experts(p, wts, true, false, false));
+    TRY(need_ptr(offsets, 4, "offsets"));
+    TRY(need_ptr(sorted_routes, 4, "sorted_routes"));
+    TRY(need_ptr(act, 16, "act"));
+    const moe::Layer &L = p->L;
+    const WsLayout lay = layout(p, M);
+    hipStream_t s = (hipStream_t)stream;
+    int32_t *active = at<int32_t>(ws, lay.active);
+    int32_t *tiles = lay.max_tiles ? at<int32_t>(ws, lay.tiles) : nullptr;
+    LAUNCH(moe::launch_plan_from_offsets(L.E, moe::mfma_tile_rows(), offsets, active, tiles, s), "plan");
+    float *sc = nullptr;
+    if (L.eps > 0.f) {
+        sc = at<float>(ws, lay.tok_scale);
+        LAUNCH(moe::launch_rms_scale(L, x, M, sc, s), "rms scale");
+    }
+    const moe::Routing rt{offsets, sorted_routes, nullptr, active, tiles};
+    const moe::Mats none{};
+    if (use_mfma(p, M))
+        LAUNCH(moe::launch_gateup_mfma(L, x, sc, routed_mats(wts), none, rt, M, lay.max_tiles, act, nullptr, s),
+               "gate/up (MFMA)");
+    else
+        LAUNCH(moe::launch_gateup_gemv(L, x, sc, routed_mats(wts), none, rt, M, act, nullptr, s), "gate/up");
+    return MOE_OK;
+}
+
+moe_status moe_combine(const moe_plan *p, const float *act, const moe_weights *wts, int32_t M,
+                       const int32_t *offsets, const int32_t *sorted_routes,
+                       const int32_t *route_pos, const float *w, const float *seed, float *y,
+                       void *ws, size_t ws_bytes, void *stream) {
+    TRY(check_call(p, M, ws, ws_bytes));
+    if (M == 0) return MOE_OK;
+    TRY(need_ptr(act, 16, "act"));
+    TRY(check_experts(p, wts, false, true, false));
+    TRY(need_ptr(offsets, 4, "offsets"));
+    TRY(need_ptr(sorted_routes, 4, "sorted_routes"));
+    TRY(need_ptr(route_pos, 4, "route_pos"));
+    TRY(need_ptr(w, 4, "w"));
+    if (seed) TRY(need_ptr(seed, 16, "seed"));
+    TRY(need_ptr(y, 16, "y"));
+    if ((const void *)y == (const void *)act) return fail(MOE_ERR_INVALID, "y aliases act");
+    const moe::Layer &L = p->L;
+    const WsLayout lay = layout(p, M);
+    hipStream_t s = (hipStream_t)stream;
+    int32_t *active = at<int32_t>(ws, lay.active);
+    int32_t *tiles = lay.max_tiles ? at<int32_t>(ws, lay.tiles) : nullptr;
+    LAUNCH(moe::launch_plan_from_offsets(L.E, moe::mfma_tile_rows(), offsets, active, tiles, s), "plan");
+    const moe::Routing rt{offsets, sorted_routes, route_pos, active, tiles};
+    const moe::Mats none{};
+    if (use_mfma(p, M)) {
+        float *yr = at<float>(ws, lay.y_routes);
+        LAUNCH(moe::launch_down_mfma(L, act, nullptr, routed_mats(wts), none, rt, M, lay.max_tiles, yr, nullptr, s),
+               "down (MFMA)");
+        LAUNCH(moe::launch_combine(L, yr, nullptr, route_pos, w, seed, M, y, s), "combine");
+    } else {
+        LAUNCH(moe::launch_down_gemv(L, act, nullptr, routed_mats(wts), none, rt, w, seed, M, y,
+                                     at<float>(ws, lay.y_routes), nullptr, s),
+               "down + combine");
+    }
+    return MOE_OK;
+}
+
+// Records an event after each kernel when timing is asked for.
+struct Recorder {
+    hipEvent_t *events = nullptr;
+    int max_events = 0, n = 0;
+    int32_t *stages = nullptr;
+    hipStream_t s = nullptr;
+    moe_status begin() {
+        if (!events) return MOE_OK;
+        hipError_t e = hipEventRecord(events[0], s);
+        return e == hipSuccess ? MOE_OK : hip_fail(e, "event record");
+    }
+    moe_status after(int stage) {
+        if (!events) return MOE_OK;
+        if (n + 1 >= max_events) return fail(MOE_ERR_INVALID, "too few timing events");
+        if (stages) stages[n] = stage;
+        hipError_t e = hipEventRecord(events[n + 1], s);
+        n++;
+        return e == hipSuccess ? MOE_OK : hip_fail(e, "event record");
+    }
+};
+
+#define STAGE(rec, expr, what, stage)               \
+    do {                                            \
+        LAUNCH(expr, what);                         \
+        TRY((rec).after(stage));                    \
+    } while (0)
+
+static moe_status forward_impl(const moe_plan *p, const void *x, const moe_weights *wts, int32_t M,
+                               float *y, int32_t *ids_out, float *w_out, int32_t *counts_out,
+                               void *ws, size_t ws_bytes, hipStream_t s, Recorder &rec) {
+    TRY(check_call(p, M, ws, ws_bytes));
+    if (M == 0) return MOE_OK;
+    TRY(need_ptr(x, 16, "x"));
+    TRY(check_router(p, wts, true));
+    TRY(check_experts(p, wts, true, true, true));
+    TRY(need_ptr(y, 16, "y"));
+    if (ids_out) TRY(need_ptr(ids_out, 4, "ids_out"));
+    if (w_out) TRY(need_ptr(w_out, 4, "w_out"));
+    if (counts_out) TRY(need_ptr(counts_out, 4, "counts_out"));
+    const moe::Layer &L = p->L;
+    const WsLayout lay = layout(p, M);
+    const int R = M * L.k;
+    rec.s = s;
+    TRY(rec.begin());
+
+    float *sc = nullptr;
+    if (L.eps > 0.f) {
+        sc = at<float>(ws, lay.tok_scale);
+        STAGE(rec, moe::launch_rms_scale(L, x, M, sc, s), "rms scale", MOE_STAGE_RMS);
+    }
+    float *lg = at<float>(ws, lay.logits);
+    int32_t *ids = ids_out ? ids_out : at<int32_t>(ws, lay.ids);
+    float *w = w_out ? w_out : at<float>(ws, lay.w);
+    int32_t *counts = counts_out ? counts_out : at<int32_t>(ws, lay.counts);
+    int32_t *offsets = at<int32_t>(ws, lay.offsets);
+    int32_t *sorted = at<int32_t>(ws, lay.sorted);
+    int32_t *rpos = at<int32_t>(ws, lay.route_pos);
+    int32_t *active = at<int32_t>(ws, lay.active);
+    int32_t *tiles = lay.max_tiles ? at<int32_t>(ws, lay.tiles) : nullptr;
+    STAGE(rec, moe::launch_router(L, x, wts->router, sc, M, lg, s), "router", MOE_STAGE_ROUTER);
+    STAGE(rec, moe::launch_topk(L, lg, wts->bias, M, ids, w, s), "top-k", MOE_STAGE_TOPK);
+    STAGE(rec, moe::launch_permute(L.E, R, moe::mfma_tile_rows(), ids, counts, offsets, sorted, rpos,
+                                   active, tiles, s),
+          "permute", MOE_STAGE_PERMUTE);
+    const moe::Routing rt{offsets, sorted, rpos, active, tiles};
+    float *act = at<float>(ws, lay.act);
+    float *sact = L.Is > 0 ? at<float>(ws, lay.shared_act) : nullptr;
+    float *yr = at<float>(ws, lay.y_routes);
+    float *ysh = L.Is > 0 ? at<float>(ws, lay.y_shared) : nullptr;
+    if (use_mfma(p, M)) {
+        STAGE(rec, moe::launch_gateup_mfma(L, x, sc, routed_mats(wts), shared_mats(wts), rt, M,
+                                           lay.max_tiles, act, sact, s),
+              "gate/up (MFMA)", MOE_STAGE_GATEUP);
+        STAGE(rec, moe::launch_down_mfma(L, act, sact, routed_mats(wts), shared_mats(wts), rt, M,
+                                         lay.max_tiles, yr, ysh, s),
+              "down (MFMA)", MOE_STAGE_DOWN);
+        STAGE(rec, moe::launch_combine(L, yr, ysh, rpos, w, nullptr, M, y, s), "combine", MOE_STAGE_COMBINE);
+    } else {
+        STAGE(rec, moe::launch_gateup_gemv(L, x, sc, routed_mats(wts), shared_mats(wts), rt, M, act, sact, s),
+              "gate/up", MOE_STAGE_GATEUP);
+        if (M <= 64) {
+            STAGE(rec, moe::launch_down_gemv(L, act, sact, routed_mats(wts), shared_mats(wts), rt, w, nullptr,
+                                             M, y, yr, ysh, s),
+                  "down + combine", MOE_STAGE_DOWN);
+        } else {
+            STAGE(rec, moe::launch_down_routes_gemv(L, act, sact, routed_mats(wts), shared_mats(wts), rt, M,
+                                                    yr, ysh, s),
+                  "down", MOE_STAGE_DOWN);
+            STAGE(rec, moe::launch_combine(L, yr, ysh, rpos, w, nullptr, M, y, s), "combine", MOE_STAGE_COMBINE);
+        }
+    }
+    return MOE_OK;
+}
+
+moe_status moe_forward(const moe_plan *p, const void *x, const moe_weights *wts, int32_t M,
+                       float *y, int32_t *ids_out, float *w_out, int32_t *counts_out, void *ws,
+                       size_t ws_bytes, void *stream) {
+    Recorder rec;
+    return forward_impl(p, x, wts, M, y, ids_out, w_out, counts_out, ws, ws_bytes, (hipStream_t)stream, rec);
+}
+
+moe_status moe_forward_timed(const moe_plan *p, const void *x, const moe_weights *wts, int32_t M,
+                             float *y, int32_t *ids_out, float *w_out, int32_t *counts_out, void *ws,
+                             size_t ws_bytes, void *stream, void **events, int32_t max_events,
+                             int32_t *stages, int32_t *n_stages) {
+    if (!events || max_events < 2) return fail(MOE_ERR_INVALID, "timing needs at least two events");
+    for (int i = 0; i < max_events; i++)
+        if (!events[i]) return fail(MOE_ERR_INVALID, "event %d is NULL", i);
+    Recorder rec;
+    rec.events = reinterpret_cast<hipEvent_t *>(events);
+    rec.max_events = max_events;
+    rec.stages = stages;
+    moe_status st = forward_impl(p, x, wts, M, y, ids_out, w_out, counts_out, ws, ws_bytes,
+                                 (hipStream_t)stream, rec);
+    if (n_stages) *n_stages = rec.n;
+    return st;
+}
+
+moe_status moe_q8_0_split(const void *blocks, int64_t rows, int32_t cols, int8_t *qs,
+                          uint16_t *scales, void *stream) {
+    if (rows < 0 || cols <= 0 || cols % 32) return fail(MOE_ERR_INVALID, "rows %lld, cols %d: need rows >= 0 and cols a positive multiple of 32", (long long)rows, cols);
+    if (rows == 0) return MOE_OK;
+    TRY(need_ptr(blocks, 2, "blocks"));
+    TRY(need_ptr(qs, 4, "qs"));
+    TRY(need_ptr(scales, 2, "scales"));
+    LAUNCH(moe::launch_q8_split(blocks, rows, cols, qs, scales, (hipStream_t)stream), "Q8_0 split");
+    return MOE_OK;
+}
+
+} // extern "C"
+
+// ---------------------------------------------------------------- Q8_0 split
+namespace moe {
+
+// One thread per block: 2-byte scale, then 32 int8 written as 8 dwords.
+__global__ __launch_bounds__(256) void k_q8_split(const uint16_t *blocks, int64_t nblocks, int8_t *qs,
+                                                  uint16_t *scales) {
+    const int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (b >= nblocks) return;
+    const uint16_t *src = blocks + b * 17; // 34 bytes = 17 halfwords
+    scales[b] = src[0];
+    uint32_t *dst = reinterpret_cast<uint32_t *>(qs + b * 32);
+#pragma unroll
+    for (int i = 0; i < 8; i++) dst[i] = (uint32_t)src[1 + 2 * i] | ((uint32_t)src[2 + 2 * i] << 16);
+}
+
+hipError_t launch_q8_split(const void *blocks, int64_t rows, int cols, int8_t *qs, uint16_t *scales,
+                           hipStream_t s) {
+    const int64_t nb = rows * (cols / 32);
+    hipLaunchKernelGGL(k_q8_split, dim3((unsigned)((nb + 255) / 256)), dim3(256), 0, s,
+                       reinterpret_cast<const uint16_t *>(blocks), nb, qs, scales);
+    return hipGetLastError();
+}
+
+} // namespace moe

@@ -1,0 +1,143 @@
+"""Helpers for the GPU parity tests: device layers, the near-tie rule, tolerances."""
+
+from __future__ import annotations
+
+import functools
+import sys
+
+import numpy as np
+
+import oracle
+import synth
+from pins import dequant
+
+# Output tolerance for fp32 accumulation over bf16 / Q8_0 weights.
+Y_MAX_ABS = 2e-2
+Y_REL_L2 = 5e-3
+# Routing-weight tolerance (fp32 softmax vs fp64).
+W_ABS = 1e-5
+# Near-tie bound: a GPU logit in fp32 differs from the exact one by at most
+# TAU_REL * sum_i |x_i * w_i| (+|b|) for the summation orders used here.
+TAU_REL = 2.0 ** -17
+
+
+def say(msg: str) -> None:
+    print(f"[gpu-test] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+@functools.lru_cache(maxsize=4)
+def host_layer(name: str):
+    spec = synth.SPECS[name]
+    return spec, synth.make_layer(spec)
+
+
+def device_layer(spec, layer, max_tokens, path=0):
+    from mixture_experts_gemv_amd.layer import MoeLayer
+    dl = MoeLayer(hidden=spec.hidden, num_experts=spec.num_experts, top_k=spec.top_k,
+                  expert_inter=spec.expert_inter, shared_inter=spec.shared_inter,
+                  select=spec.select, bias_mode=spec.bias_mode,
+                  swiglu_limit=spec.swiglu_limit, rms_eps=spec.rms_eps,
+                  x_dtype=spec.x_dtype, router_dtype=spec.router_dtype,
+                  expert_dtype=spec.expert_dtype, shared_dtype=spec.shared_dtype,
+                  max_tokens=max_tokens, path=path)
+    dl.load(layer["router"], layer["bias"], layer["gate"], layer["up"], layer["down"],
+            layer.get("shared_gate"), layer.get("shared_up"), layer.get("shared_down"))
+    return dl
+
+
+def selection_keys(spec, layer, x):
+    """fp64 selection keys s[t][e] and the near-tie bound tau[t]."""
+    xf = dequant(x, spec.x_dtype, x.shape[0], spec.hidden)
+    if spec.rms_eps > 0:
+        xf = xf / np.sqrt(np.mean(xf * xf, axis=1, keepdims=True) + spec.rms_eps)
+    wr = dequant(layer["router"], spec.router_dtype, spec.num_experts, spec.hidden)
+    logits = xf @ wr.T
+    b = np.zeros(spec.num_experts) if layer.get("bias") is None else layer["bias"].astype(np.float64)
+    s = logits + (b if spec.bias_mode != 0 else 0.0)
+    A = np.abs(xf) @ np.abs(wr).T + (np.abs(b) if spec.bias_mode != 0 else 0.0)
+    tau = TAU_REL * A.max(axis=1)
+    return s, tau
+
+
+def check_ids(spec, layer, x, gpu_ids, ora_ids):
+    """Apply the near-tie rule; return (forced ids for the oracle, number of near-tie tokens).
+
+    Tokens whose k-th and (k+1)-th fp64 keys are further apart than tau must get
+    exactly the oracle's expert set.  For near-tie tokens the GPU set must hold
+    every expert whose key clears the boundary by more than tau and draw the
+    rest from keys within tau of it; the oracle is then re-run on the GPU's set.
+    """
+    s, tau = selection_keys(spec, layer, x)
+    k, E = spec.top_k, spec.num_experts
+    forced = ora_ids.copy()
+    near = 0
+    for t in range(x.shape[0]):
+        order = np.argsort(-s[t], kind="stable")
+        sk = s[t, order[k - 1]]
+        sk1 = s[t, order[k]] if k < E else -np.inf
+        gset = set(int(e) for e in gpu_ids[t])
+        assert len(gset) == k, f"token {t}: repeated expert in {gpu_ids[t]}"
+        assert all(0 <= e < E for e in gset), f"token {t}: expert id out of range {gpu_ids[t]}"
+        if sk - sk1 > tau[t]:
+            assert gset == set(int(e) for e in ora_ids[t]), \
+                f"token {t}: ids {sorted(gset)} vs oracle {sorted(ora_ids[t])}"
+        else:
+            near += 1
+            must = {e for e in range(E) if s[t, e] > sk + tau[t]}
+            may = {e for e in range(E) if s[t, e] >= sk - tau[t]}
+            assert must <= gset <= may, f"near-tie token {t}: ids {sorted(gset)}"
+            forced[t] = gpu_ids[t]
+    return forced, near
+
+
+def check_y(y_gpu, y_ref, what=""):
+    y_gpu = np.asarray(y_gpu, np.float64)
+    y_ref = np.asarray(y_ref, np.float64)
+    err = np.abs(y_gpu - y_ref)
+    max_abs = float(err.max()) if err.size else 0.0
+    rel = float(np.linalg.norm(y_gpu - y_ref) / max(np.linalg.norm(y_ref), 1e-30))
+    say(f"{what}: max-abs {max_abs:.3e}, rel-L2 {rel:.3e}")
+    assert max_abs <= Y_MAX_ABS, f"{what}: max-abs error {max_abs:.3e} > {Y_MAX_ABS}"
+    assert rel <= Y_REL_L2, f"{what}: relative L2 error {rel:.3e} > {Y_REL_L2}"
+    return max_abs, rel
+
+
+def run_forward(dl, x_host, M=None):
+    import torch
+    x = dl.x_tensor(x_host)
+    M = x.shape[0]
+    ids = torch.empty(M, dl.k, dtype=torch.int32, device=dl.device)
+    w = torch.empty(M, dl.k, dtype=torch.float32, device=dl.device)
+    counts = torch.empty(dl.E, dtype=torch.int32, device=dl.device)
+    y = dl.forward(x, ids=ids, w=w, counts=counts)
+    torch.cuda.synchronize()
+    return y.cpu().numpy(), ids.cpu().numpy(), w.cpu().numpy(), counts.cpu().numpy()
+
+
+def forward_parity(spec, layer, x, dl, sample=None, what=""):
+    """Whole-layer parity: ids (near-tie rule), counts, w and y against the oracle."""
+    y, ids, w, counts = run_forward(dl, x)
+    if sample is None:
+        sample = np.arange(x.shape[0])
+    xs = np.ascontiguousarray(x[sample])
+    o = oracle.forward(spec, layer, xs)
+    forced, near = check_ids(spec, layer, xs, ids[sample], o["ids"])
+    if near:
+        o = oracle.forward(spec, layer, xs, forced_ids=forced)
+    if len(sample) == x.shape[0]:
+        full_forced = forced
+        assert np.array_equal(counts, np.bincount(ids.reshape(-1), minlength=spec.num_experts))
+        assert np.array_equal(counts, np.bincount(full_forced.reshape(-1), minlength=spec.num_experts)), \
+            "per-expert counts differ from the oracle's"
+    else:
+        assert counts.sum() == x.shape[0] * spec.top_k
+        assert np.array_equal(counts, np.bincount(ids.reshape(-1), minlength=spec.num_experts))
+    # weights, matched by expert id
+    for i, t in enumerate(sample):
+        for j in range(spec.top_k):
+            e = ids[t, j]
+            jj = list(o["ids"][i]).index(e)
+            assert abs(w[t, j] - o["w"][i, jj]) <= W_ABS, f"{what}: weight token {t} expert {e}"
+    ma, rel = check_y(y[sample], o["y"], what=f"{what} (near-tie tokens: {near})")
+    return dict(max_abs=ma, rel_l2=rel, near_ties=near, ids=ids, counts=counts)

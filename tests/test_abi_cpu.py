@@ -1,0 +1,144 @@
+"""The C ABI without a GPU: symbols, plan validation, workspace sizing, and
+argument checks that must refuse before anything is enqueued."""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import mixture_experts_gemv_amd as m
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADERS = [os.path.join(ROOT, "include", f) for f in os.listdir(os.path.join(ROOT, "include"))
+           if f.endswith(".h")]
+
+
+def declared_functions():
+    names = set()
+    for h in HEADERS:
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        for mm in re.finditer(r"^[A-Za-z_][\w\s\*]*?\b(moe_\w+)\s*\(", text, flags=re.M):
+            names.add(mm.group(1))
+    return sorted(names)
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert len(names) >= 10, names
+    lib = m.lib()
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in include/ but not exported"
+
+
+def test_binding_has_every_entry_point():
+    for n in declared_functions():
+        assert callable(getattr(m, n)), f"binding lacks {n}"
+
+
+BASE = dict(hidden=256, num_experts=8, top_k=2, expert_inter=512, max_tokens=16)
+
+
+def _create(**kw):
+    cfg = dict(BASE)
+    cfg.update(kw)
+    return m.moe_plan_create(**cfg)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(num_experts=0, top_k=0), m.MOE_ERR_INVALID),
+    (dict(num_experts=8, top_k=0), m.MOE_ERR_INVALID),
+    (dict(num_experts=-1, top_k=1), m.MOE_ERR_INVALID),
+    (dict(top_k=9, num_experts=16), m.MOE_ERR_UNSUPPORTED),
+    (dict(top_k=3, num_experts=2), m.MOE_ERR_INVALID),
+    (dict(num_experts=257), m.MOE_ERR_UNSUPPORTED),
+    (dict(hidden=0), m.MOE_ERR_INVALID),
+    (dict(hidden=100), m.MOE_ERR_UNSUPPORTED),
+    (dict(expert_inter=48), m.MOE_ERR_UNSUPPORTED),
+    (dict(shared_inter=-32), m.MOE_ERR_INVALID),
+    (dict(shared_inter=40), m.MOE_ERR_UNSUPPORTED),
+    (dict(max_tokens=0), m.MOE_ERR_INVALID),
+    (dict(select=2), m.MOE_ERR_INVALID),
+    (dict(bias_mode=3), m.MOE_ERR_INVALID),
+    (dict(swiglu_limit=-1.0), m.MOE_ERR_INVALID),
+    (dict(rms_eps=-1e-6), m.MOE_ERR_INVALID),
+    (dict(x_dtype=m.MOE_Q8_0), m.MOE_ERR_UNSUPPORTED),
+    (dict(expert_dtype=7), m.MOE_ERR_INVALID),
+    (dict(shared_inter=64, shared_dtype=m.MOE_Q8_0), m.MOE_ERR_UNSUPPORTED),
+    (dict(path=5), m.MOE_ERR_INVALID),
+    (dict(path=m.MOE_PATH_MFMA, expert_dtype=m.MOE_Q8_0), m.MOE_ERR_UNSUPPORTED),
+])
+def test_plan_refusals(kw, status):
+    with pytest.raises(m.MoeError) as ei:
+        _create(**kw)
+    assert ei.value.status == status, str(ei.value)
+
+
+def test_plan_accepts_every_workload_shape():
+    import synth
+    for spec in synth.SPECS.values():
+        p = m.moe_plan_create(spec.hidden, spec.num_experts, spec.top_k, spec.expert_inter,
+                              spec.shared_inter, max(spec.token_counts), spec.select,
+                              spec.bias_mode, spec.swiglu_limit, spec.rms_eps, spec.x_dtype,
+                              spec.router_dtype, spec.expert_dtype, spec.shared_dtype)
+        for M in spec.token_counts:
+            assert m.moe_workspace_bytes(p, M) > 0
+
+
+def test_workspace_sizes():
+    p = _create(shared_inter=0)
+    assert m.moe_workspace_bytes(p, 0) == 0
+    assert m.moe_workspace_bytes(p, 17) == 0            # beyond max_tokens
+    sizes = [m.moe_workspace_bytes(p, M) for M in range(1, 17)]
+    assert all(b > a for a, b in zip(sizes, sizes[1:]))
+    assert all(s % 256 == 0 for s in sizes)
+    with_shared = _create(shared_inter=1024)
+    assert m.moe_workspace_bytes(with_shared, 4) > m.moe_workspace_bytes(p, 4)
+
+
+FAKE = 1 << 40  # a 256-byte-aligned address; never dereferenced (validation fails first)
+
+
+def test_call_refusals_before_any_launch():
+    p = _create()
+    w = m.make_weights(router=FAKE, gate=FAKE, up=FAKE, down=FAKE)
+    need = m.moe_workspace_bytes(p, 4)
+    L = m.lib()
+    st = L.moe_forward(p.handle, FAKE, ctypes.byref(w), 17, FAKE, None, None, None, FAKE, need, None)
+    assert st == m.MOE_ERR_INVALID and "max_tokens" in m.moe_last_error()
+    st = L.moe_forward(p.handle, FAKE, ctypes.byref(w), 4, FAKE, None, None, None, FAKE, need - 1, None)
+    assert st == m.MOE_ERR_WORKSPACE
+    st = L.moe_forward(p.handle, None, ctypes.byref(w), 4, FAKE, None, None, None, FAKE, need, None)
+    assert st == m.MOE_ERR_INVALID and "x" in m.moe_last_error()
+    st = L.moe_forward(p.handle, FAKE + 8, ctypes.byref(w), 4, FAKE, None, None, None, FAKE, need, None)
+    assert st == m.MOE_ERR_INVALID and "aligned" in m.moe_last_error()
+    st = L.moe_forward(p.handle, FAKE, ctypes.byref(w), 4, FAKE, None, None, None, FAKE + 16, need, None)
+    assert st == m.MOE_ERR_INVALID
+    nodown = m.make_weights(router=FAKE, gate=FAKE, up=FAKE)
+    st = L.moe_forward(p.handle, FAKE, ctypes.byref(nodown), 4, FAKE, None, None, None, FAKE, need, None)
+    assert st == m.MOE_ERR_INVALID and "down" in m.moe_last_error()
+    # M = 0 is a no-op even with NULL buffers
+    assert L.moe_forward(p.handle, None, ctypes.byref(w), 0, None, None, None, None, None, 0, None) == m.MOE_OK
+    # bias required when the plan has a bias mode
+    pb = _create(bias_mode=m.MOE_BIAS_LOGIT)
+    st = L.moe_route(pb.handle, FAKE, ctypes.byref(w), 4, None, 0, FAKE, FAKE, FAKE,
+                     m.moe_workspace_bytes(pb, 4), None)
+    assert st == m.MOE_ERR_INVALID and "bias" in m.moe_last_error()
+    # Q8_0 needs its scale planes
+    pq = _create(expert_dtype=m.MOE_Q8_0)
+    st = L.moe_expert_ffn(pq.handle, FAKE, ctypes.byref(w), 4, FAKE, FAKE, FAKE, FAKE,
+                          m.moe_workspace_bytes(pq, 4), None)
+    assert st == m.MOE_ERR_INVALID and "scale" in m.moe_last_error()
+    # unknown route flags
+    st = L.moe_route(p.handle, FAKE, ctypes.byref(w), 4, None, 6, FAKE, FAKE, FAKE, need, None)
+    assert st == m.MOE_ERR_INVALID
+    # combine output may not alias act
+    st = L.moe_combine(p.handle, FAKE, ctypes.byref(w), 4, FAKE, FAKE, FAKE, FAKE, None, FAKE,
+                       FAKE, need, None)
+    assert st == m.MOE_ERR_INVALID and "alias" in m.moe_last_error()
+    assert L.moe_q8_0_split(FAKE, 4, 33, FAKE, FAKE, None) == m.MOE_ERR_INVALID
+    assert L.moe_q8_0_split(FAKE, -1, 32, FAKE, FAKE, None) == m.MOE_ERR_INVALID
+    assert L.moe_q8_0_split(None, 0, 32, None, None, None) == m.MOE_OK

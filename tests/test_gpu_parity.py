@@ -1,0 +1,231 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle."""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from synth import BF16, F32, Q8_0, BIAS_LOGIT, BIAS_SELECT_ONLY, SOFTMAX_ALL_NORENORM
+from gpu_helpers import (W_ABS, check_ids, check_y, device_layer, forward_parity, host_layer,
+                         say)
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import mixture_experts_gemv_amd as m
+    m.lib()  # loud failure if the library was not built
+    yield
+
+
+def _t(a, dtype=None):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda() if dtype is None else \
+        torch.from_numpy(np.ascontiguousarray(a)).to(dtype).cuda()
+
+
+# --------------------------------------------------------------------- routing
+ROUTE_CASES = [
+    dict(num_experts=8, top_k=2),
+    dict(num_experts=64, top_k=6, select=SOFTMAX_ALL_NORENORM),
+    dict(num_experts=32, top_k=4, bias_mode=BIAS_LOGIT, bias_kind="normal"),
+    dict(num_experts=128, top_k=8, bias_mode=BIAS_SELECT_ONLY, bias_kind="normal"),
+    dict(num_experts=256, top_k=8, bias_mode=BIAS_LOGIT, bias_kind="zipf"),
+    dict(num_experts=5, top_k=5),
+    dict(num_experts=1, top_k=1),
+    dict(num_experts=100, top_k=3, select=SOFTMAX_ALL_NORENORM, bias_mode=BIAS_LOGIT,
+         bias_kind="normal"),
+]
+
+
+@pytest.mark.parametrize("case", ROUTE_CASES, ids=lambda c: f"E{c['num_experts']}k{c['top_k']}")
+def test_route_from_logits_bit_exact(case):
+    """With given fp32 logits, selection is pure comparison: ids bit-exact."""
+    import mixture_experts_gemv_amd as m
+    spec = synth.small_spec(hidden=64, expert_inter=32, seed=900, **case)
+    layer = synth.make_layer(spec)
+    E, k = spec.num_experts, spec.top_k
+    rng = np.random.default_rng(E * 31 + k)
+    M = 67
+    logits = rng.standard_normal((M, E)).astype(np.float32)
+    logits[1] = 0.0                               # all equal
+    logits[2, ::2] = -0.0                         # signed zeros mixed with +0
+    logits[3] = np.round(logits[3] * 2) / 2       # many exact ties
+    logits[4] = logits[4, 0]                      # all equal, non-zero
+    if E > 3:
+        logits[5, E - 1] = logits[5, 0] = logits[5].max() + 1.0   # tie at the top
+    say(f"route from logits E={E} k={k}")
+    plan = m.moe_plan_create(64, E, k, 32, max_tokens=M, select=spec.select,
+                             bias_mode=spec.bias_mode, x_dtype=m.MOE_BF16)
+    bias = layer["bias"]
+    wts = m.make_weights(bias=None if bias is None else _t(bias))
+    ws = torch.empty(m.moe_workspace_bytes(plan, M), dtype=torch.uint8, device="cuda")
+    lg = _t(logits)
+    ids = torch.empty(M, k, dtype=torch.int32, device="cuda")
+    w = torch.empty(M, k, dtype=torch.float32, device="cuda")
+    m.moe_route(plan, None, wts, M, lg, m.MOE_LOGITS_IN, ids, w, ws)
+    torch.cuda.synchronize()
+    oid, ow = oracle.select(spec, logits.astype(np.float64), bias)
+    assert np.array_equal(ids.cpu().numpy(), oid), "ids differ from the oracle on identical logits"
+    assert np.max(np.abs(w.cpu().numpy() - ow)) <= W_ABS
+
+
+def test_route_from_x_small():
+    import mixture_experts_gemv_amd as m
+    for n, kw in enumerate([dict(num_experts=8, top_k=2, x_dtype=F32, router_dtype=F32),
+                            dict(num_experts=64, top_k=6, select=SOFTMAX_ALL_NORENORM),
+                            dict(num_experts=128, top_k=8, bias_mode=BIAS_LOGIT, bias_kind="zipf",
+                                 rms_eps=1e-6)]):
+        spec = synth.small_spec(hidden=256, expert_inter=32, seed=950 + n, **kw)
+        layer = synth.make_layer(spec)
+        M = 37
+        x = synth.make_tokens(spec, M)
+        say(f"route from x case {n}")
+        dl = device_layer(spec, layer, M)
+        xt = dl.x_tensor(x)
+        lg = torch.empty(M, spec.num_experts, dtype=torch.float32, device="cuda")
+        ids = torch.empty(M, spec.top_k, dtype=torch.int32, device="cuda")
+        w = torch.empty(M, spec.top_k, dtype=torch.float32, device="cuda")
+        m.moe_route(dl.plan, xt, dl.weights, M, lg, 0, ids, w, dl.workspace(M))
+        torch.cuda.synchronize()
+        o = oracle.forward(spec, layer, x)
+        np.testing.assert_allclose(lg.cpu().numpy(), o["logits"], rtol=0, atol=1e-4)
+        forced, near = check_ids(spec, layer, x, ids.cpu().numpy(), o["ids"])
+        assert near <= 2
+
+
+# ------------------------------------------------------------------- permute
+@pytest.mark.parametrize("E,M,k,skew", [(8, 4, 2, 0), (32, 16, 4, 0), (64, 1, 6, 0),
+                                         (128, 2048, 8, 1), (256, 300, 8, 1), (3, 1000, 3, 0)])
+def test_permute_bit_exact(E, M, k, skew):
+    import mixture_experts_gemv_amd as m
+    rng = np.random.default_rng(E + M + k)
+    if skew:
+        p = 1.0 / np.arange(1, E + 1) ** 1.1
+        p = p[rng.permutation(E)]
+        ids = np.stack([rng.choice(E, size=k, replace=False, p=p / p.sum()) for _ in range(M)])
+    else:
+        ids = np.stack([rng.permutation(E)[:k] for _ in range(M)])
+    ids = ids.astype(np.int32)
+    say(f"permute E={E} M={M} k={k}")
+    plan = m.moe_plan_create(64, E, k, 32, max_tokens=M)
+    ws = torch.empty(m.moe_workspace_bytes(plan, M), dtype=torch.uint8, device="cuda")
+    dids = _t(ids)
+    outs = [torch.full((n,), -7, dtype=torch.int32, device="cuda") for n in (E, E + 1, M * k, M * k)]
+    m.moe_permute(plan, dids, M, *outs, ws)
+    torch.cuda.synchronize()
+    want = oracle.permute(E, ids)
+    for got, ref, name in zip(outs, want, ("counts", "offsets", "sorted_routes", "route_pos")):
+        assert np.array_equal(got.cpu().numpy(), ref), name
+
+
+# --------------------------------------------------------------- stage parity
+def test_stages_match_forward_and_oracle():
+    """moe_route -> moe_permute -> moe_expert_ffn -> moe_combine equals the oracle."""
+    import mixture_experts_gemv_amd as m
+    spec = synth.small_spec(hidden=256, num_experts=8, top_k=3, expert_inter=160,
+                            bias_mode=BIAS_LOGIT, bias_kind="normal", swiglu_limit=0.5, seed=970)
+    layer = synth.make_layer(spec)
+    M = 13
+    x = synth.make_tokens(spec, M)
+    say("stage chain")
+    dl = device_layer(spec, layer, M)
+    xt = dl.x_tensor(x)
+    ws = dl.workspace(M)
+    E, k, H, I = spec.num_experts, spec.top_k, spec.hidden, spec.expert_inter
+    ids = torch.empty(M, k, dtype=torch.int32, device="cuda")
+    w = torch.empty(M, k, dtype=torch.float32, device="cuda")
+    m.moe_route(dl.plan, xt, dl.weights, M, None, 0, ids, w, ws)
+    counts = torch.empty(E, dtype=torch.int32, device="cuda")
+    offsets = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    sr = torch.empty(M * k, dtype=torch.int32, device="cuda")
+    rp = torch.empty(M * k, dtype=torch.int32, device="cuda")
+    m.moe_permute(dl.plan, ids, M, counts, offsets, sr, rp, ws)
+    act = torch.empty(M * k, I, dtype=torch.float32, device="cuda")
+    m.moe_expert_ffn(dl.plan, xt, dl.weights, M, offsets, sr, act, ws)
+    seed = torch.randn(M, H, dtype=torch.float32, device="cuda")
+    y = torch.empty(M, H, dtype=torch.float32, device="cuda")
+    m.moe_combine(dl.plan, act, dl.weights, M, offsets, sr, rp, w, seed, y, ws)
+    torch.cuda.synchronize()
+    gids = ids.cpu().numpy()
+    o = oracle.forward(spec, layer, x, want_act=True)
+    forced, near = check_ids(spec, layer, x, gids, o["ids"])
+    o = oracle.forward(spec, layer, x, forced_ids=forced, want_act=True)
+    # act rows are in sorted order: row route_pos[r] holds route r
+    a = act.cpu().numpy()[rp.cpu().numpy()]
+    rel = np.linalg.norm(a - o["act"]) / np.linalg.norm(o["act"])
+    assert rel <= 5e-3, f"act rel-L2 {rel:.3e}"
+    check_y(y.cpu().numpy() - seed.cpu().numpy(), o["y"], "stage chain")
+
+
+# ------------------------------------------------------------- small forwards
+SMALL = [
+    ("tiny", {}, (4, 1, 7)),
+    ("q8-bias-clamp", dict(hidden=288, num_experts=12, top_k=4, expert_inter=320,
+                           bias_mode=BIAS_LOGIT, bias_kind="normal", swiglu_limit=7.0,
+                           expert_dtype=Q8_0), (1, 5, 16)),
+    ("softmax-all-shared", dict(hidden=256, num_experts=16, top_k=6, expert_inter=160,
+                                shared_inter=320, select=SOFTMAX_ALL_NORENORM), (1, 3, 16)),
+    ("bf16-k2", dict(hidden=512, num_experts=8, top_k=2, expert_inter=1056), (1, 16, 70)),
+    ("zipf-rms", dict(hidden=256, num_experts=128, top_k=8, expert_inter=96,
+                      bias_mode=BIAS_LOGIT, bias_kind="zipf", rms_eps=1e-6), (65, 130)),
+    ("q8-shared-many", dict(hidden=128, num_experts=6, top_k=2, expert_inter=64,
+                            shared_inter=96, expert_dtype=Q8_0, shared_dtype=Q8_0), (1, 64, 100)),
+]
+
+
+@pytest.mark.parametrize("name,kw,Ms", SMALL, ids=[c[0] for c in SMALL])
+def test_forward_small(name, kw, Ms):
+    if name == "tiny":
+        spec = synth.SPECS["tiny"]
+    else:
+        spec = synth.small_spec(name=name, seed=1100 + len(name), **kw)
+    layer = synth.make_layer(spec)
+    dl = device_layer(spec, layer, max(Ms))
+    for M in Ms:
+        x = synth.make_tokens(spec, M, batch=3)
+        say(f"forward {name} M={M}")
+        forward_parity(spec, layer, x, dl, what=f"{name} M={M}")
+
+
+def test_forward_repeatable():
+    """Two calls give bitwise-identical y (no atomics in the combine)."""
+    spec = synth.small_spec(hidden=256, num_experts=16, top_k=4, expert_inter=192, seed=1200)
+    layer = synth.make_layer(spec)
+    dl = device_layer(spec, layer, 16)
+    x = dl.x_tensor(synth.make_tokens(spec, 16))
+    say("repeatability")
+    a = dl.forward(x).cpu().numpy()
+    b = dl.forward(x).cpu().numpy()
+    assert np.array_equal(a, b)
+
+
+# ------------------------------------------------------------ full-size layers
+FULL = [("tiny", 4, None), ("gpt-oss-20b", 1, None), ("gpt-oss-20b", 16, None),
+        ("deepseek-v2-lite", 1, None), ("deepseek-v2-lite", 16, None),
+        ("mixtral-8x7b", 1, None), ("mixtral-8x7b", 16, None),
+        ("mixtral-8x7b", 512, 12), ("qwen3-30b-a3b", 2048, 24)]
+
+
+@pytest.mark.parametrize("name,M,nsample", FULL, ids=[f"{n}-M{m}" for n, m, _ in FULL])
+def test_forward_full_size(name, M, nsample):
+    say(f"generate {name}")
+    spec, layer = host_layer(name)
+    say(f"upload {name}")
+    dl = device_layer(spec, layer, M)
+    x = synth.make_tokens(spec, M)
+    sample = None
+    if nsample:
+        rng = np.random.default_rng(M)
+        sample = np.sort(rng.choice(M, size=nsample, replace=False))
+    say(f"forward {name} M={M}")
+    r = forward_parity(spec, layer, x, dl, sample=sample, what=f"{name} M={M}")
+    del dl
+    torch.cuda.empty_cache()
+    say(f"{name} M={M}: touched experts {int((r['counts'] > 0).sum())}")
