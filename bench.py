@@ -154,6 +154,7 @@ def main() -> int:
     ap.add_argument("--layers", type=int, default=None, help="layer copies to rotate")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true", help="time eager launches only")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -223,7 +224,29 @@ def main() -> int:
         step(i)
     hip.hipEventRecord(ev.ev[1], stream)
     torch.cuda.synchronize()
-    total_ms = ev.elapsed_ms(0, 1)
+    eager_ms = ev.elapsed_ms(0, 1)
+
+    # ---- timed region: the same K steps captured in one HIP graph, replayed
+    graph_ms = None
+    if not args.no_graph:
+        cap = torch.cuda.Stream()
+        cap.wait_stream(torch.cuda.current_stream())
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(cap):
+            with torch.cuda.graph(g, stream=cap):
+                for i in range(K):
+                    step(i)
+        torch.cuda.current_stream().wait_stream(cap)
+        torch.cuda.synchronize()
+        g.replay()                      # warm replay
+        torch.cuda.synchronize()
+        hip.hipEventRecord(ev.ev[0], stream)
+        g.replay()
+        hip.hipEventRecord(ev.ev[1], stream)
+        torch.cuda.synchronize()
+        graph_ms = ev.elapsed_ms(0, 1)
+        del g
+    total_ms = graph_ms if graph_ms is not None else eager_ms
     ms_per_step = total_ms / K
 
     # ---- timed region: per kernel (events between the layer's kernels)
@@ -271,7 +294,9 @@ def main() -> int:
             "expert_weights": {0: "f32", 1: "bf16", 2: "q8_0"}[spec.expert_dtype],
             "tokens_per_call": M, "layer_copies": L, "token_batches": P,
             "touched_experts_avg": touched_avg,
+            "timing": "hip_graph_replay" if graph_ms is not None else "eager",
         },
+        "eager": {"tokens_per_s": M * K / (eager_ms * 1e-3), "ms_per_step": eager_ms / K},
         "roofline": {
             "bound": "hbm", "kernel": "gate/up + SwiGLU (k_gateup_gemv)",
             "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",

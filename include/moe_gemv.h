@@ -44,9 +44,13 @@
  *    MOE_ERR_HIP reports a failed kernel launch; work enqueued before it may
  *    have run.
  *  - Workspace: `ws` must hold moe_workspace_bytes(plan, M) bytes, 256-byte
- *    aligned.  Its contents between calls are not meaningful and need no
- *    initialisation.  Calls that share one workspace must be ordered on one
- *    stream.
+ *    aligned, and must be initialised once (moe_workspace_init, or zero-filled)
+ *    before its first use: its first 256 bytes hold ticket words that
+ *    workgroups of one kernel use to elect the last finisher.  Every call that
+ *    completes leaves them as it found them (zero); the rest of the workspace
+ *    carries nothing between calls.  After MOE_ERR_HIP, initialise it again.
+ *    Calls that share one workspace must be ordered on one stream; calls on
+ *    different streams need different workspaces.
  *  - M = 0 is a no-op returning MOE_OK.
  */
 #ifndef MOE_GEMV_H
@@ -140,6 +144,10 @@ void moe_plan_destroy(moe_plan *plan);
  * max_tokens); returns 0 for M out of range.  Regions for unused features
  * (shared expert, pre-norm, the MFMA path) take no space. */
 size_t moe_workspace_bytes(const moe_plan *plan, int32_t M);
+
+/* Zero the ticket words of a workspace (one small kernel on `stream`).  Call
+ * once after allocating a workspace, and again after a MOE_ERR_HIP. */
+moe_status moe_workspace_init(const moe_plan *plan, void *ws, size_t ws_bytes, void *stream);
 
 /* Text of the last non-OK status returned on the calling thread. */
 const char *moe_last_error(void);

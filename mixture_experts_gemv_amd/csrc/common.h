@@ -131,6 +131,35 @@ __device__ __forceinline__ void load_chunk<DT_Q8>(const void *row, int c, float 
     }
 }
 
+// Raw 16-byte chunk load (no conversion) and its decoding, so that a group of
+// loads can be issued before any of them is used.
+__device__ __forceinline__ u32x4 load_raw(const void *row, int c) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(row) + c);
+}
+
+template <int DT>
+__device__ __forceinline__ void decode_chunk(u32x4 v, float *w) {
+    if constexpr (DT == DT_F32) {
+        w[0] = __uint_as_float(v.x); w[1] = __uint_as_float(v.y);
+        w[2] = __uint_as_float(v.z); w[3] = __uint_as_float(v.w);
+    } else if constexpr (DT == DT_BF16) {
+        w[0] = bf16_lo(v.x); w[1] = bf16_hi(v.x); w[2] = bf16_lo(v.y); w[3] = bf16_hi(v.y);
+        w[4] = bf16_lo(v.z); w[5] = bf16_hi(v.z); w[6] = bf16_lo(v.w); w[7] = bf16_hi(v.w);
+    } else {
+        const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            w[4 * i + 0] = i8_to_f32<0>(d[i]);
+            w[4 * i + 1] = i8_to_f32<1>(d[i]);
+            w[4 * i + 2] = i8_to_f32<2>(d[i]);
+            w[4 * i + 3] = i8_to_f32<3>(d[i]);
+        }
+    }
+}
+
+// Wave-uniform copy of a value the compiler cannot prove uniform.
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
 // Bytes of one stored element (Q8_0: the int8 plane only).
 template <int DT> __host__ __device__ constexpr int elem_bytes() { return DT == DT_F32 ? 4 : (DT == DT_BF16 ? 2 : 1); }
 

@@ -13,6 +13,7 @@
 //   them in slot order.
 #include "common.h"
 #include "launch.h"
+#include "topk.h"
 
 namespace moe {
 
@@ -479,6 +480,395 @@ hipError_t launch_down_gemv(const Layer &L, const float *act, const float *share
     if (L.edt == DT_BF16) hipLaunchKernelGGL(k_down_combine_gemv<DT_BF16>, grid, dim3(kThreads), 0, s, a);
     else if (L.edt == DT_Q8) hipLaunchKernelGGL(k_down_combine_gemv<DT_Q8>, grid, dim3(kThreads), 0, s, a);
     else hipLaunchKernelGGL(k_down_combine_gemv<DT_F32>, grid, dim3(kThreads), 0, s, a);
+    return hipGetLastError();
+}
+
+// ================================================================ M = 1 decode
+// With one token every touched expert sees the same x, and the sorted
+// position of the route to the u-th touched expert is u.
+//
+// gate/up: each wave holds x in registers (lane l owns chunks l, l+64, ...)
+// and streams a contiguous range of (slot, row) pairs, RP pairs at a time,
+// issuing all 2*RP*CPL 16-byte loads of a group before using them.
+// Both kernels run the token's top-k from the router logits in their prologue
+// (one wave's DPP rounds, overlapped with the first loads), so the single-token
+// path needs no routing kernel of its own and no cross-workgroup handoff.
+struct M1Route {
+    const float *logits, *bias;
+    int E, k, select, bias_mode;
+};
+
+// Slot -> expert table of the k picks in ascending expert id (wave-uniform).
+// (Named fields rather than an array, so the table stays in scalar registers.)
+struct M1Slots {
+    int e0, e1, e2, e3, e4, e5, e6, e7;
+    __device__ int expert(int s) const {
+        return s == 0 ? e0 : s == 1 ? e1 : s == 2 ? e2 : s == 3 ? e3 : s == 4 ? e4 : s == 5 ? e5 : s == 6 ? e6 : e7;
+    }
+    __device__ void set(int s, int v) {
+        e0 = s == 0 ? v : e0; e1 = s == 1 ? v : e1; e2 = s == 2 ? v : e2; e3 = s == 3 ? v : e3;
+        e4 = s == 4 ? v : e4; e5 = s == 5 ? v : e5; e6 = s == 6 ? v : e6; e7 = s == 7 ? v : e7;
+    }
+};
+
+__device__ __forceinline__ M1Slots m1_slots(const M1Route &rt, int lane, int *my_id, float *my_w, int *my_rank) {
+    topk_wave_core(rt.logits, rt.bias, rt.E, rt.k, rt.select, rt.bias_mode, lane, my_id, my_w);
+    *my_rank = pick_rank(*my_id, rt.k, lane);
+    M1Slots s{0, 0, 0, 0, 0, 0, 0, 0};
+    for (int j = 0; j < rt.k; j++)
+        s.set(__builtin_amdgcn_readlane(*my_rank, j), __builtin_amdgcn_readlane(*my_id, j));
+    return s;
+}
+
+struct M1GateUpArgs {
+    const void *x;
+    const float *tok_scale;
+    Mats routed, shared;
+    M1Route rt;
+    int32_t *ids_out, *counts_out; // written by the first wave
+    float *w_out;
+    int H, I, Is, k;
+    int total_pairs, pairs_per_wave;
+    float limit;
+    float *act, *shared_act;
+};
+
+template <int XDT, int WDT, int CPL, int RP>
+__global__ __launch_bounds__(kThreads) void k_gateup_m1(M1GateUpArgs a) {
+    constexpr int N = Chunk<WDT>::N;
+    const int lane = threadIdx.x & 63;
+    const int gw = uniform(blockIdx.x * kWaves + (threadIdx.x >> 6));
+    const int p_begin = gw * a.pairs_per_wave;
+    if (p_begin >= a.total_pairs) return;
+    const int p_end = min(a.total_pairs, p_begin + a.pairs_per_wave);
+    const int H = a.H, nch = H / N;
+    const float sc = a.tok_scale ? a.tok_scale[0] : 1.0f;
+    int my_id, my_rank;
+    float my_w;
+    const M1Slots slots = m1_slots(a.rt, lane, &my_id, &my_w, &my_rank);
+    if (gw == 0) {
+        if (lane < a.k) {
+            a.ids_out[lane] = my_id;
+            a.w_out[lane] = my_w;
+        }
+        if (a.counts_out)
+            for (int e = lane; e < a.rt.E; e += kWave) {
+                int c = 0;
+                for (int u = 0; u < a.k; u++) c += slots.expert(u) == e;
+                a.counts_out[e] = c;
+            }
+    }
+    // x chunks this lane multiplies; lanes past the row end hold zeros and
+    // load (harmless) duplicates of the last chunk.
+    int cl[CPL];
+    float xr[CPL][N];
+#pragma unroll
+    for (int cc = 0; cc < CPL; cc++) {
+        const int c = lane + kWave * cc;
+        cl[cc] = min(c, nch - 1);
+        const float m = c < nch ? sc : 0.f;
+#pragma unroll
+        for (int n4 = 0; n4 < N; n4 += 4) {
+            if constexpr (XDT == DT_BF16) {
+                const u32x2 q = reinterpret_cast<const u32x2 *>(reinterpret_cast<const uint16_t *>(a.x) + cl[cc] * N + n4)[0];
+                xr[cc][n4] = bf16_lo(q.x) * m; xr[cc][n4 + 1] = bf16_hi(q.x) * m;
+                xr[cc][n4 + 2] = bf16_lo(q.y) * m; xr[cc][n4 + 3] = bf16_hi(q.y) * m;
+            } else {
+                const f32x4 q = reinterpret_cast<const f32x4 *>(reinterpret_cast<const float *>(a.x) + cl[cc] * N + n4)[0];
+                xr[cc][n4] = q.x * m; xr[cc][n4 + 1] = q.y * m; xr[cc][n4 + 2] = q.z * m; xr[cc][n4 + 3] = q.w * m;
+            }
+        }
+    }
+    const int routed_pairs = a.k * a.I;
+    const size_t row_bytes = (size_t)H * elem_bytes<WDT>();
+    for (int p = p_begin; p < p_end; p += RP) {
+        const char *grow[RP], *urow[RP];
+        const uint16_t *gsr[RP], *usr[RP];
+        int slot[RP], irow[RP];
+#pragma unroll
+        for (int r = 0; r < RP; r++) {
+            const int q = min(p + r, p_end - 1);
+            size_t row;
+            const Mats *m;
+            if (q < routed_pairs) {
+                slot[r] = q / a.I;
+                irow[r] = q - slot[r] * a.I;
+                row = (size_t)slots.expert(slot[r]) * a.I + irow[r];
+                m = &a.routed;
+            } else {
+                slot[r] = -1;
+                irow[r] = q - routed_pairs;
+                row = irow[r];
+                m = &a.shared;
+            }
+            grow[r] = reinterpret_cast<const char *>(m->gate) + row * row_bytes;
+            urow[r] = reinterpret_cast<const char *>(m->up) + row * row_bytes;
+            if constexpr (WDT == DT_Q8) {
+                gsr[r] = m->gate_s + row * (H / 32);
+                usr[r] = m->up_s + row * (H / 32);
+            }
+        }
+        // issue every load of the group first
+        u32x4 rg[RP][CPL], ru[RP][CPL];
+        uint16_t hg[RP][CPL], hu[RP][CPL];
+#pragma unroll
+        for (int r = 0; r < RP; r++)
+#pragma unroll
+            for (int cc = 0; cc < CPL; cc++) {
+                rg[r][cc] = load_raw(grow[r], cl[cc]);
+                ru[r][cc] = load_raw(urow[r], cl[cc]);
+                if constexpr (WDT == DT_Q8) {
+                    hg[r][cc] = gsr[r][cl[cc] >> 1];
+                    hu[r][cc] = usr[r][cl[cc] >> 1];
+                }
+            }
+#pragma unroll
+        for (int r = 0; r < RP; r++) {
+            float g = 0.f, v = 0.f;
+#pragma unroll
+            for (int cc = 0; cc < CPL; cc++) {
+                float wg[N], wu[N];
+                decode_chunk<WDT>(rg[r][cc], wg);
+                decode_chunk<WDT>(ru[r][cc], wu);
+                float pg = 0.f, pu = 0.f;
+#pragma unroll
+                for (int n = 0; n < N; n++) {
+                    pg = fmaf(wg[n], xr[cc][n], pg);
+                    pu = fmaf(wu[n], xr[cc][n], pu);
+                }
+                if constexpr (WDT == DT_Q8) {
+                    g = fmaf(f16_bits_to_f32(hg[r][cc]), pg, g);
+                    v = fmaf(f16_bits_to_f32(hu[r][cc]), pu, v);
+                } else {
+                    g += pg;
+                    v += pu;
+                }
+            }
+            g = wave_sum(g);
+            v = wave_sum(v);
+            if (a.limit > 0.f) {
+                g = clampf(g, a.limit);
+                v = clampf(v, a.limit);
+            }
+            if (lane == 0 && p + r < p_end) {
+                const float h = silu_mul(g, v);
+                if (slot[r] >= 0) a.act[(size_t)slot[r] * a.I + irow[r]] = h;
+                else a.shared_act[irow[r]] = h;
+            }
+        }
+    }
+}
+
+// down (M = 1): a workgroup owns kM1Rows output rows; its 256 threads stride
+// over the concatenated chunks of every touched expert's rows (then the
+// shared expert's), kM1Unroll rounds at a time with every load of the rounds
+// issued first.  Each chunk's dot is scaled by its route's weight before the
+// block reduction, which is done in a fixed order.
+constexpr int kM1Rows = 4;
+constexpr int kM1Unroll = 2;
+constexpr int kMaxSlots = 9; // top-k slots + the shared expert
+
+struct M1DownArgs {
+    const float *act, *shared_act;
+    Mats routed, shared;
+    M1Route rt;
+    const float *seed;
+    int H, I, Is, k;
+    float *y;
+};
+
+template <int WDT>
+__global__ __launch_bounds__(kThreads) void k_down_m1(M1DownArgs a) {
+    constexpr int N = Chunk<WDT>::N;
+    __shared__ const char *s_row[kMaxSlots];
+    __shared__ const uint16_t *s_sc[kMaxSlots];
+    __shared__ const float *s_act[kMaxSlots];
+    __shared__ float s_w[kMaxSlots];
+    __shared__ int s_width[kMaxSlots];
+    __shared__ float s_part[kWaves][kM1Rows];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int H = a.H, h0 = blockIdx.x * kM1Rows;
+    const int n_routed = a.k; // with M = 1 every slot is a touched expert
+    const int nch = a.I / N, nch_s = a.Is / N;
+    if (wave == 0) {
+        int my_id, my_rank;
+        float my_w;
+        topk_wave_core(a.rt.logits, a.rt.bias, a.rt.E, a.rt.k, a.rt.select, a.rt.bias_mode, lane, &my_id, &my_w);
+        my_rank = pick_rank(my_id, a.k, lane);
+        if (lane < n_routed) {
+            // slot = rank in ascending expert id, which is the act row of the pick
+            const size_t row = (size_t)my_id * H + h0;
+            s_row[my_rank] = reinterpret_cast<const char *>(a.routed.down) + row * a.I * elem_bytes<WDT>();
+            if constexpr (WDT == DT_Q8) s_sc[my_rank] = a.routed.down_s + row * (a.I / 32);
+            s_act[my_rank] = a.act + (size_t)my_rank * a.I;
+            s_w[my_rank] = my_w;
+            s_width[my_rank] = a.I;
+        }
+    }
+    if (tid == n_routed && a.Is > 0) {
+        s_row[tid] = reinterpret_cast<const char *>(a.shared.down) + (size_t)h0 * a.Is * elem_bytes<WDT>();
+        if constexpr (WDT == DT_Q8) s_sc[tid] = a.shared.down_s + (size_t)h0 * (a.Is / 32);
+        s_act[tid] = a.shared_act;
+        s_w[tid] = 1.0f;
+        s_width[tid] = a.Is;
+    }
+    __syncthreads();
+    const int n_tasks = n_routed * nch + (a.Is > 0 ? nch_s : 0);
+    const int last_row = min(kM1Rows, H - h0) - 1;
+    float acc[kM1Rows];
+#pragma unroll
+    for (int r = 0; r < kM1Rows; r++) acc[r] = 0.f;
+    for (int t0 = 0; t0 < n_tasks; t0 += kThreads * kM1Unroll) {
+        u32x4 raw[kM1Unroll][kM1Rows];
+        uint16_t hs[kM1Unroll][kM1Rows];
+        f32x4 av[kM1Unroll][N / 4];
+        float wt[kM1Unroll];
+#pragma unroll
+        for (int u = 0; u < kM1Unroll; u++) {
+            const int t = t0 + u * kThreads + tid;
+            const int tc = min(t, n_tasks - 1);
+            int slot, c;
+            if (tc < n_routed * nch) {
+                slot = tc / nch;
+                c = tc - slot * nch;
+            } else {
+                slot = n_routed;
+                c = tc - n_routed * nch;
+            }
+            const int width = s_width[slot];
+            const size_t rb = (size_t)width * elem_bytes<WDT>();
+            const char *row0 = s_row[slot];
+            wt[u] = t < n_tasks ? s_w[slot] : 0.f;
+#pragma unroll
+            for (int r = 0; r < kM1Rows; r++) {
+                const int rr = min(r, last_row);
+                raw[u][r] = load_raw(row0 + rr * rb, c);
+                if constexpr (WDT == DT_Q8) hs[u][r] = s_sc[slot][(size_t)rr * (width / 32) + (c >> 1)];
+            }
+            const f32x4 *ap = reinterpret_cast<const f32x4 *>(s_act[slot] + c * N);
+#pragma unroll
+            for (int n4 = 0; n4 < N / 4; n4++) av[u][n4] = ap[n4];
+        }
+#pragma unroll
+        for (int u = 0; u < kM1Unroll; u++) {
+#pragma unroll
+            for (int r = 0; r < kM1Rows; r++) {
+                float wv[N];
+                decode_chunk<WDT>(raw[u][r], wv);
+                float d = 0.f;
+#pragma unroll
+                for (int n4 = 0; n4 < N / 4; n4++) {
+                    d = fmaf(wv[4 * n4], av[u][n4].x, d);
+                    d = fmaf(wv[4 * n4 + 1], av[u][n4].y, d);
+                    d = fmaf(wv[4 * n4 + 2], av[u][n4].z, d);
+                    d = fmaf(wv[4 * n4 + 3], av[u][n4].w, d);
+                }
+                if constexpr (WDT == DT_Q8) d *= f16_bits_to_f32(hs[u][r]);
+                acc[r] = fmaf(wt[u], d, acc[r]);
+            }
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < kM1Rows; r++) {
+        const float v = wave_sum(acc[r]);
+        if (lane == 0) s_part[wave][r] = v;
+    }
+    __syncthreads();
+    if (tid <= last_row) {
+        float v = a.seed ? a.seed[h0 + tid] : 0.f;
+#pragma unroll
+        for (int wv = 0; wv < kWaves; wv++) v += s_part[wv][tid];
+        a.y[h0 + tid] = v;
+    }
+}
+
+// Chunks per lane of a row of H elements, and the instantiated values.
+static int m1_cpl(int H, int N) { return (H / N + kWave - 1) / kWave; }
+
+template <int XDT, int WDT, int RP>
+static bool m1_gateup_dispatch(int cpl, const M1GateUpArgs &a, int grid, hipStream_t s) {
+#define M1_CASE(C) \
+    case C: hipLaunchKernelGGL((k_gateup_m1<XDT, WDT, C, RP>), dim3(grid), dim3(kThreads), 0, s, a); return true;
+    switch (cpl) {
+        M1_CASE(1) M1_CASE(2) M1_CASE(3) M1_CASE(4) M1_CASE(5) M1_CASE(6) M1_CASE(8)
+    default: return false;
+    }
+#undef M1_CASE
+}
+
+bool m1_supported(const Layer &L) {
+    const int N = L.edt == DT_Q8 ? 16 : (L.edt == DT_BF16 ? 8 : 4);
+    const int c = m1_cpl(L.H, N);
+    return c <= 8 && c != 7;
+}
+
+static M1Route m1_route(const Layer &L, const float *logits, const float *bias) {
+    return M1Route{logits, L.bias_mode ? bias : nullptr, L.E, L.k, L.select, L.bias_mode};
+}
+
+hipError_t launch_gateup_m1(const Layer &L, const void *x, const float *tok_scale, const Mats &routed,
+                            const Mats &shared, const float *logits, const float *bias, int32_t *ids_out,
+                            float *w_out, int32_t *counts_out, float *act, float *shared_act,
+                            hipStream_t s) {
+    M1GateUpArgs a;
+    a.x = x;
+    a.tok_scale = tok_scale;
+    a.routed = routed;
+    a.shared = shared;
+    a.rt = m1_route(L, logits, bias);
+    a.ids_out = ids_out;
+    a.w_out = w_out;
+    a.counts_out = counts_out;
+    a.H = L.H;
+    a.I = L.I;
+    a.Is = shared_act ? L.Is : 0;
+    a.k = L.k;
+    a.limit = L.limit;
+    a.act = act;
+    a.shared_act = shared_act;
+    a.total_pairs = L.k * L.I + a.Is;
+    const int N = L.edt == DT_Q8 ? 16 : (L.edt == DT_BF16 ? 8 : 4);
+    const int cpl = m1_cpl(L.H, N);
+    const int RP = cpl <= 4 ? 2 : 1; // keep about 16 loads of a group in flight
+    const int max_waves = 2048;
+    int ppw = (a.total_pairs + max_waves - 1) / max_waves;
+    ppw = (ppw + RP - 1) / RP * RP;
+    a.pairs_per_wave = ppw;
+    const int waves = (a.total_pairs + ppw - 1) / ppw;
+    const int grid = (waves + kWaves - 1) / kWaves;
+    bool ok;
+    if (L.xdt == DT_BF16) {
+        if (L.edt == DT_Q8) ok = RP == 2 ? m1_gateup_dispatch<DT_BF16, DT_Q8, 2>(cpl, a, grid, s) : m1_gateup_dispatch<DT_BF16, DT_Q8, 1>(cpl, a, grid, s);
+        else if (L.edt == DT_BF16) ok = RP == 2 ? m1_gateup_dispatch<DT_BF16, DT_BF16, 2>(cpl, a, grid, s) : m1_gateup_dispatch<DT_BF16, DT_BF16, 1>(cpl, a, grid, s);
+        else ok = RP == 2 ? m1_gateup_dispatch<DT_BF16, DT_F32, 2>(cpl, a, grid, s) : m1_gateup_dispatch<DT_BF16, DT_F32, 1>(cpl, a, grid, s);
+    } else {
+        if (L.edt == DT_Q8) ok = RP == 2 ? m1_gateup_dispatch<DT_F32, DT_Q8, 2>(cpl, a, grid, s) : m1_gateup_dispatch<DT_F32, DT_Q8, 1>(cpl, a, grid, s);
+        else if (L.edt == DT_BF16) ok = RP == 2 ? m1_gateup_dispatch<DT_F32, DT_BF16, 2>(cpl, a, grid, s) : m1_gateup_dispatch<DT_F32, DT_BF16, 1>(cpl, a, grid, s);
+        else ok = RP == 2 ? m1_gateup_dispatch<DT_F32, DT_F32, 2>(cpl, a, grid, s) : m1_gateup_dispatch<DT_F32, DT_F32, 1>(cpl, a, grid, s);
+    }
+    if (!ok) return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+hipError_t launch_down_m1(const Layer &L, const float *act, const float *shared_act, const Mats &routed,
+                          const Mats &shared, const float *logits, const float *bias, const float *seed,
+                          float *y, hipStream_t s) {
+    M1DownArgs a;
+    a.act = act;
+    a.shared_act = shared_act;
+    a.routed = routed;
+    a.shared = shared;
+    a.rt = m1_route(L, logits, bias);
+    a.seed = seed;
+    a.H = L.H;
+    a.I = L.I;
+    a.Is = shared_act ? L.Is : 0;
+    a.k = L.k;
+    a.y = y;
+    const dim3 grid((L.H + kM1Rows - 1) / kM1Rows);
+    if (L.edt == DT_BF16) hipLaunchKernelGGL(k_down_m1<DT_BF16>, grid, dim3(kThreads), 0, s, a);
+    else if (L.edt == DT_Q8) hipLaunchKernelGGL(k_down_m1<DT_Q8>, grid, dim3(kThreads), 0, s, a);
+    else hipLaunchKernelGGL(k_down_m1<DT_F32>, grid, dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }
 

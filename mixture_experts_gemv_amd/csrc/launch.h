@@ -37,6 +37,15 @@ hipError_t launch_topk(const Layer &L, const float *logits, const float *bias, i
 hipError_t launch_permute(int E, int R, int tile_rows, const int32_t *ids, int32_t *counts,
                           int32_t *offsets, int32_t *sorted, int32_t *route_pos, int32_t *active,
                           int32_t *tiles, hipStream_t s);
+// Router + top-k + permutation in one launch for M <= route_small_max_tokens();
+// `ticket` is a workspace word that must be zero before the call (the kernel
+// leaves it zero).
+int route_small_max_tokens();
+hipError_t launch_route_small(const Layer &L, const void *x, const void *router, const float *bias,
+                              const float *tok_scale, int M, float *logits, int32_t *ids, float *w,
+                              int32_t *counts, int32_t *offsets, int32_t *sorted, int32_t *route_pos,
+                              int32_t *active, uint32_t *ticket, hipStream_t s);
+hipError_t launch_zero_words(uint32_t *p, int n, hipStream_t s);
 // Derive the active-expert list and the tile list from offsets alone.
 hipError_t launch_plan_from_offsets(int E, int tile_rows, const int32_t *offsets, int32_t *active,
                                     int32_t *tiles, hipStream_t s);
@@ -57,6 +66,20 @@ hipError_t launch_down_routes_gemv(const Layer &L, const float *act, const float
 hipError_t launch_combine(const Layer &L, const float *y_routes, const float *y_shared,
                           const int32_t *route_pos, const float *w, const float *seed, int M,
                           float *y, hipStream_t s);
+
+// M = 1 decode kernels (x shared by every touched expert).
+bool m1_supported(const Layer &L);
+// Both take the router logits and run the token's top-k in their prologue.
+hipError_t launch_gateup_m1(const Layer &L, const void *x, const float *tok_scale, const Mats &routed,
+                            const Mats &shared, const float *logits, const float *bias, int32_t *ids_out,
+                            float *w_out, int32_t *counts_out, float *act, float *shared_act,
+                            hipStream_t s);
+hipError_t launch_down_m1(const Layer &L, const float *act, const float *shared_act, const Mats &routed,
+                          const Mats &shared, const float *logits, const float *bias, const float *seed,
+                          float *y, hipStream_t s);
+// Router logits only (M <= route_small_max_tokens()).
+hipError_t launch_router_small(const Layer &L, const void *x, const void *router, const float *tok_scale,
+                               int M, float *logits, hipStream_t s);
 
 // MFMA grouped-GEMM path (bf16 x and experts).
 int mfma_tile_rows();

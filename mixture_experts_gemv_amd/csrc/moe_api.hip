@@ -37,11 +37,12 @@ moe_status hip_fail(hipError_t e, const char *what) {
 bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 constexpr size_t kAlign = 256;
+constexpr size_t kSyncBytes = 256; // ticket words at the start of every workspace
 size_t up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 // Where each workspace region starts for a call with M tokens.
 struct WsLayout {
-    size_t tok_scale, logits, ids, w, counts, offsets, sorted, route_pos, active, tiles;
+    size_t sync, tok_scale, logits, ids, w, counts, offsets, sorted, route_pos, active, tiles;
     size_t act, shared_act, y_routes, y_shared, total;
     int max_tiles;
 };
@@ -62,6 +63,7 @@ WsLayout layout(const moe_plan *p, int M) {
     WsLayout w{};
     size_t o = 0;
     auto take = [&](size_t bytes) { size_t at = o; o += up(bytes); return at; };
+    w.sync = take(kSyncBytes);
     w.tok_scale = take(L.eps > 0.f ? (size_t)M * 4 : 0);
     w.logits = take((size_t)M * L.E * 4);
     w.ids = take(R * 4);
@@ -392,17 +394,28 @@ static moe_status forward_impl(const moe_plan *p, const void *x, const moe_weigh
     int32_t *rpos = at<int32_t>(ws, lay.route_pos);
     int32_t *active = at<int32_t>(ws, lay.active);
     int32_t *tiles = lay.max_tiles ? at<int32_t>(ws, lay.tiles) : nullptr;
-    STAGE(rec, moe::launch_router(L, x, wts->router, sc, M, lg, s), "router", MOE_STAGE_ROUTER);
-    STAGE(rec, moe::launch_topk(L, lg, wts->bias, M, ids, w, s), "top-k", MOE_STAGE_TOPK);
-    STAGE(rec, moe::launch_permute(L.E, R, moe::mfma_tile_rows(), ids, counts, offsets, sorted, rpos,
-                                   active, tiles, s),
-          "permute", MOE_STAGE_PERMUTE);
+    const bool mfma = use_mfma(p, M);
+    const bool single = M == 1 && !mfma && moe::m1_supported(L);
+    if (single) {
+        // one token: the expert kernels run the top-k themselves from the logits
+        STAGE(rec, moe::launch_router_small(L, x, wts->router, sc, M, lg, s), "router", MOE_STAGE_ROUTER);
+    } else if (M <= moe::route_small_max_tokens() && !mfma) {
+        STAGE(rec, moe::launch_route_small(L, x, wts->router, wts->bias, sc, M, lg, ids, w, counts, offsets,
+                                           sorted, rpos, active, at<uint32_t>(ws, lay.sync), s),
+              "route", MOE_STAGE_ROUTER);
+    } else {
+        STAGE(rec, moe::launch_router(L, x, wts->router, sc, M, lg, s), "router", MOE_STAGE_ROUTER);
+        STAGE(rec, moe::launch_topk(L, lg, wts->bias, M, ids, w, s), "top-k", MOE_STAGE_TOPK);
+        STAGE(rec, moe::launch_permute(L.E, R, moe::mfma_tile_rows(), ids, counts, offsets, sorted, rpos,
+                                       active, tiles, s),
+              "permute", MOE_STAGE_PERMUTE);
+    }
     const moe::Routing rt{offsets, sorted, rpos, active, tiles};
     float *act = at<float>(ws, lay.act);
     float *sact = L.Is > 0 ? at<float>(ws, lay.shared_act) : nullptr;
     float *yr = at<float>(ws, lay.y_routes);
     float *ysh = L.Is > 0 ? at<float>(ws, lay.y_shared) : nullptr;
-    if (use_mfma(p, M)) {
+    if (mfma) {
         STAGE(rec, moe::launch_gateup_mfma(L, x, sc, routed_mats(wts), shared_mats(wts), rt, M,
                                            lay.max_tiles, act, sact, s),
               "gate/up (MFMA)", MOE_STAGE_GATEUP);
@@ -410,6 +423,13 @@ static moe_status forward_impl(const moe_plan *p, const void *x, const moe_weigh
                                          lay.max_tiles, yr, ysh, s),
               "down (MFMA)", MOE_STAGE_DOWN);
         STAGE(rec, moe::launch_combine(L, yr, ysh, rpos, w, nullptr, M, y, s), "combine", MOE_STAGE_COMBINE);
+    } else if (single) {
+        STAGE(rec, moe::launch_gateup_m1(L, x, sc, routed_mats(wts), shared_mats(wts), lg, wts->bias, ids, w,
+                                         counts_out, act, sact, s),
+              "gate/up", MOE_STAGE_GATEUP);
+        STAGE(rec, moe::launch_down_m1(L, act, sact, routed_mats(wts), shared_mats(wts), lg, wts->bias, nullptr,
+                                       y, s),
+              "down + combine", MOE_STAGE_DOWN);
     } else {
         STAGE(rec, moe::launch_gateup_gemv(L, x, sc, routed_mats(wts), shared_mats(wts), rt, M, act, sact, s),
               "gate/up", MOE_STAGE_GATEUP);
@@ -449,6 +469,16 @@ moe_status moe_forward_timed(const moe_plan *p, const void *x, const moe_weights
                                  (hipStream_t)stream, rec);
     if (n_stages) *n_stages = rec.n;
     return st;
+}
+
+moe_status moe_workspace_init(const moe_plan *p, void *ws, size_t ws_bytes, void *stream) {
+    if (!p) return fail(MOE_ERR_INVALID, "plan is NULL");
+    if (ws_bytes == 0) return MOE_OK;
+    if (ws_bytes < kSyncBytes) return fail(MOE_ERR_WORKSPACE, "workspace smaller than %zu bytes", kSyncBytes);
+    TRY(need_ptr(ws, kAlign, "workspace"));
+    LAUNCH(moe::launch_zero_words(reinterpret_cast<uint32_t *>(ws), (int)(kSyncBytes / 4), (hipStream_t)stream),
+           "workspace init");
+    return MOE_OK;
 }
 
 moe_status moe_q8_0_split(const void *blocks, int64_t rows, int32_t cols, int8_t *qs,

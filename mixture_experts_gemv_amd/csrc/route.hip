@@ -1,7 +1,12 @@
 // Routing kernels: RMS pre-norm scale, router GEMV, wave top-k + softmax, and
 // the expert histogram / scan / stable scatter of the routes.
+//
+// For small batches one kernel does all of it: each workgroup computes the
+// logits of a few experts for every token, and the last workgroup to finish
+// (an atomic ticket in the workspace) runs the top-k and the permutation.
 #include "common.h"
 #include "launch.h"
+#include "topk.h"
 
 namespace moe {
 
@@ -20,6 +25,8 @@ __device__ __forceinline__ void load8(const void *row, int c8, float *v) {
     }
 }
 
+template <int DT> constexpr int dt_bytes() { return DT == DT_BF16 ? 2 : 4; }
+
 // ------------------------------------------------------------------ pre-norm
 // scale[t] = 1 / sqrt(mean_i x[t][i]^2 + eps); one wave per token.
 template <int XDT>
@@ -27,7 +34,7 @@ __global__ __launch_bounds__(256) void k_rms_scale(const void *x, int M, int H, 
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     if (t >= M) return;
-    const char *row = reinterpret_cast<const char *>(x) + (size_t)t * H * (XDT == DT_BF16 ? 2 : 4);
+    const char *row = reinterpret_cast<const char *>(x) + (size_t)t * H * dt_bytes<XDT>();
     float s = 0.f;
     for (int c = lane; c < H / 8; c += kWave) {
         float v[8];
@@ -48,9 +55,54 @@ hipError_t launch_rms_scale(const Layer &L, const void *x, int M, float *scale, 
     return hipGetLastError();
 }
 
-// ---------------------------------------------------------------- router GEMV
+// ---------------------------------------------------------------- router dots
+// One wave: logits of expert row `wrow` for tokens t0..t0+nt-1 (nt <= TM).
+// Lanes stride the row in 8-element pieces, kRouterCB pieces per lane per
+// block with every load of a block issued before use (indices past the row
+// end are clamped and their products masked); each token's sum is
+// wave-reduced.
+constexpr int kRouterCB = 4;
+
+template <int XDT, int RDT, int TM>
+__device__ __forceinline__ void router_dots(const void *x, const void *wrow, int H, int t0, int nt,
+                                            int lane, float (&acc)[TM], int cb = 0, int ce = -1) {
+    const size_t xrow = (size_t)H * dt_bytes<XDT>();
+    const char *xb = reinterpret_cast<const char *>(x) + (size_t)t0 * xrow;
+    const int nch = ce < 0 ? H / 8 : ce;  // this wave covers 8-element pieces cb..nch-1
+#pragma unroll
+    for (int i = 0; i < TM; i++) acc[i] = 0.f;
+    for (int c0 = cb; c0 < nch; c0 += kWave * kRouterCB) {
+        float w[kRouterCB][8];
+        int cc[kRouterCB];
+#pragma unroll
+        for (int j = 0; j < kRouterCB; j++) {
+            const int c = c0 + lane + kWave * j;
+            cc[j] = min(c, nch - 1);
+            load8<RDT>(wrow, cc[j], w[j]);
+            if (c >= nch)
+#pragma unroll
+                for (int i = 0; i < 8; i++) w[j][i] = 0.f;
+        }
+#pragma unroll
+        for (int tm = 0; tm < TM; tm++) {
+            if (tm < nt) {
+                float xv[kRouterCB][8];
+#pragma unroll
+                for (int j = 0; j < kRouterCB; j++) load8<XDT>(xb + tm * xrow, cc[j], xv[j]);
+#pragma unroll
+                for (int j = 0; j < kRouterCB; j++)
+#pragma unroll
+                    for (int i = 0; i < 8; i++) acc[tm] = fmaf(w[j][i], xv[j][i], acc[tm]);
+            }
+        }
+    }
+#pragma unroll
+    for (int tm = 0; tm < TM; tm++)
+        if (tm < nt) acc[tm] = wave_sum(acc[tm]);
+}
+
 // logits[t][e] = scale[t] * sum_i x[t][i] * router[e][i].  One wave per
-// (expert, group of TM tokens); lanes stride the row in 8-element pieces.
+// (expert, group of TM tokens).
 constexpr int kRouterTM = 8;
 
 template <int XDT, int RDT>
@@ -61,31 +113,15 @@ __global__ __launch_bounds__(64) void k_router_gemv(const void *x, const void *r
     const int t0 = blockIdx.y * kRouterTM;
     const int lane = threadIdx.x;
     const int nt = min(kRouterTM, M - t0);
-    const size_t xrow_bytes = (size_t)H * (XDT == DT_BF16 ? 2 : 4);
-    const char *wrow = reinterpret_cast<const char *>(router) + (size_t)e * H * (RDT == DT_BF16 ? 2 : 4);
-    const char *xbase = reinterpret_cast<const char *>(x) + (size_t)t0 * xrow_bytes;
+    const char *wrow = reinterpret_cast<const char *>(router) + (size_t)e * H * dt_bytes<RDT>();
     float acc[kRouterTM];
-#pragma unroll
-    for (int i = 0; i < kRouterTM; i++) acc[i] = 0.f;
-    for (int c = lane; c < H / 8; c += kWave) {
-        float w[8];
-        load8<RDT>(wrow, c, w);
-#pragma unroll
-        for (int tm = 0; tm < kRouterTM; tm++) {
-            if (tm < nt) {
-                float xv[8];
-                load8<XDT>(xbase + tm * xrow_bytes, c, xv);
-#pragma unroll
-                for (int i = 0; i < 8; i++) acc[tm] = fmaf(w[i], xv[i], acc[tm]);
-            }
-        }
-    }
+    router_dots<XDT, RDT, kRouterTM>(x, wrow, H, t0, nt, lane, acc);
 #pragma unroll
     for (int tm = 0; tm < kRouterTM; tm++) {
-        if (tm < nt) {
-            float v = wave_sum(acc[tm]);
+        if (tm < nt && lane == 0) {
+            float v = acc[tm];
             if (tok_scale) v *= tok_scale[t0 + tm];
-            if (lane == 0) logits[(size_t)(t0 + tm) * E + e] = v;
+            logits[(size_t)(t0 + tm) * E + e] = v;
         }
     }
 }
@@ -109,8 +145,18 @@ hipError_t launch_router(const Layer &L, const void *x, const void *router, cons
 // Selection key s = logit (+ bias for LOGIT and SELECT_ONLY); softmax input
 // u = logit (+ bias for LOGIT).  k rounds of a wave argmax on the
 // order-preserving key, ties to the lower expert id.
-constexpr int kMaxE = 256;
-constexpr int kKeysPerLane = kMaxE / kWave;
+__device__ void topk_wave(const float *lrow, const float *bias, int E, int k, int select,
+                          int bias_mode, int lane, int32_t *ids_row, float *w_row,
+                          int *lds_ids = nullptr) {
+    int id;
+    float wt;
+    topk_wave_core(lrow, bias, E, k, select, bias_mode, lane, &id, &wt);
+    if (lane < k) {
+        ids_row[lane] = id;
+        w_row[lane] = wt;
+        if (lds_ids) lds_ids[lane] = id;
+    }
+}
 
 __global__ __launch_bounds__(256) void k_topk(const float *logits, const float *bias, int M, int E,
                                               int k, int select, int bias_mode, int32_t *ids,
@@ -118,64 +164,8 @@ __global__ __launch_bounds__(256) void k_topk(const float *logits, const float *
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     if (t >= M) return;
-    const float *lrow = logits + (size_t)t * E;
-    uint32_t key[kKeysPerLane];
-    float u[kKeysPerLane];
-#pragma unroll
-    for (int c = 0; c < kKeysPerLane; c++) {
-        const int e = lane + kWave * c;
-        if (e < E) {
-            const float l = lrow[e];
-            const float b = bias ? bias[e] : 0.f;
-            const float sk = bias_mode != 0 ? l + b : l;
-            u[c] = bias_mode == 1 ? l + b : l;
-            key[c] = order_key(sk);
-        } else {
-            u[c] = -INFINITY;
-            key[c] = 0u;
-        }
-    }
-    uint32_t taken = 0u;
-    int my_id = 0;          // lane j keeps the id chosen in round j
-    float my_u = -INFINITY; // and its softmax input
-    for (int j = 0; j < k; j++) {
-        uint32_t bk = 0u;
-        int bid = 0x7fffffff;
-        float bu = 0.f;
-#pragma unroll
-        for (int c = 0; c < kKeysPerLane; c++) {
-            const int e = lane + kWave * c;
-            const bool cand = e < E && !((taken >> c) & 1u);
-            if (cand && (bid == 0x7fffffff || key[c] > bk)) { bk = key[c]; bid = e; bu = u[c]; }
-        }
-        const uint32_t mk = wave_max_u32(bid == 0x7fffffff ? 0u : bk);
-        const int win = wave_min_i32((bid != 0x7fffffff && bk == mk) ? bid : 0x7fffffff);
-        if ((win & 63) == lane) taken |= 1u << (win >> 6);
-        const float wu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bid == win ? bu : 0.f), win & 63));
-        if (lane == j) { my_id = win; my_u = wu; }
-    }
-    float wj;
-    if (select == 0) {
-        const float m = wave_max(lane < k ? my_u : -INFINITY);
-        const float ex = lane < k ? expf(my_u - m) : 0.f;
-        const float z = wave_sum(ex);
-        wj = ex / z;
-    } else {
-        float m = -INFINITY;
-#pragma unroll
-        for (int c = 0; c < kKeysPerLane; c++) m = fmaxf(m, u[c]);
-        m = wave_max(m);
-        float z = 0.f;
-#pragma unroll
-        for (int c = 0; c < kKeysPerLane; c++)
-            if (lane + kWave * c < E) z += expf(u[c] - m);
-        z = wave_sum(z);
-        wj = expf(my_u - m) / z;
-    }
-    if (lane < k) {
-        ids[(size_t)t * k + lane] = my_id;
-        w[(size_t)t * k + lane] = wj;
-    }
+    topk_wave(logits + (size_t)t * E, bias, E, k, select, bias_mode, lane, ids + (size_t)t * k,
+              w + (size_t)t * k);
 }
 
 hipError_t launch_topk(const Layer &L, const float *logits, const float *bias, int M, int32_t *ids,
@@ -186,7 +176,7 @@ hipError_t launch_topk(const Layer &L, const float *logits, const float *bias, i
 }
 
 // ---------------------------------------------------------------- permutation
-// One workgroup of 16 waves.  Wave w owns a contiguous slice of routes.
+// One workgroup of NW waves.  Wave w owns a contiguous slice of routes.
 //  1. per-wave expert histogram in LDS;
 //  2. per expert, the exclusive sum over waves (so slices keep their order)
 //     and the total; an exclusive scan over experts gives offsets;
@@ -194,26 +184,41 @@ hipError_t launch_topk(const Layer &L, const float *logits, const float *bias, i
 //     expert find each other with 8 ballots (one per bit of the id) and take
 //     consecutive places in lane order, which keeps the scatter stable;
 //  4. the touched-expert list and the GEMM tile list come from the counts.
-constexpr int kPermWaves = 16;
-constexpr int kPermThreads = kPermWaves * kWave;
+// ids outside 0..E-1 get no place, so every write stays in bounds whatever
+// the caller passes.
+struct PermuteOut {
+    int32_t *counts, *offsets, *sorted, *route_pos, *active, *tiles;
+    int tile_rows;
+};
+
+template <int NW>
+struct PermuteSmem {
+    int hist[NW][kMaxE];
+    int cnt[kMaxE];
+    int off[kMaxE + 1];
+    int scan[kMaxE + 1];
+};
 
 // Exclusive scan of v over threads 0..255 (others pass 0); returns the
-// thread's exclusive prefix and the total in *total.  All threads call it.
-__device__ int block_scan_256(int v, int *lds /*[256+1]*/, int *total) {
-    const int tid = threadIdx.x;
-    if (tid < 256) lds[tid] = v;
-    __syncthreads();
-    for (int off = 1; off < 256; off <<= 1) {
-        int add = 0;
-        if (tid < 256 && tid >= off) add = lds[tid - off];
-        __syncthreads();
-        if (tid < 256) lds[tid] += add;
-        __syncthreads();
+// thread's exclusive prefix and the total in *total.  All threads of the
+// block call it; the block has at least 256 threads.  Waves 0-3 scan their
+// 64 values with shuffles, then add the totals of the waves before them.
+__device__ int block_scan_256(int v, int *lds /*[>= 4]*/, int *total) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    int x = tid < 256 ? v : 0;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        const int y = __shfl_up(x, off);
+        if (lane >= off) x += y;
     }
-    const int incl = tid < 256 ? lds[tid] : 0;
-    *total = lds[255];
+    if (wave < 4 && lane == kWave - 1) lds[wave] = x;
     __syncthreads();
-    return incl - v;
+    int before = 0;
+#pragma unroll
+    for (int w = 0; w < 4; w++) before += (w < wave) ? lds[w] : 0;
+    *total = lds[0] + lds[1] + lds[2] + lds[3];
+    __syncthreads();
+    return tid < 256 ? x + before - v : 0;
 }
 
 __device__ void write_plan(int E, int tile_rows, const int *cnt, const int *off, int *scan_lds,
@@ -237,47 +242,39 @@ __device__ void write_plan(int E, int tile_rows, const int *cnt, const int *off,
     }
 }
 
-__global__ __launch_bounds__(kPermThreads) void k_permute(const int32_t *ids, int R, int E, int tile_rows,
-                                                         int32_t *counts, int32_t *offsets,
-                                                         int32_t *sorted, int32_t *route_pos,
-                                                         int32_t *active, int32_t *tiles) {
-    __shared__ int hist[kPermWaves][kMaxE];
-    __shared__ int cnt[kMaxE];
-    __shared__ int off[kMaxE + 1];
-    __shared__ int scan[kMaxE + 1];
+template <int NW>
+__device__ void permute_block(const int32_t *ids, int R, int E, const PermuteOut &o, PermuteSmem<NW> &sm) {
     const int tid = threadIdx.x;
     const int wv = tid >> 6, lane = tid & 63;
-    for (int i = tid; i < kPermWaves * kMaxE; i += kPermThreads) (&hist[0][0])[i] = 0;
+    for (int i = tid; i < NW * kMaxE; i += NW * kWave) (&sm.hist[0][0])[i] = 0;
     __syncthreads();
-    const int per = (((R + kPermWaves - 1) / kPermWaves) + 63) / 64 * 64;
+    const int per = (((R + NW - 1) / NW) + 63) / 64 * 64;
     const int r0 = min(R, wv * per), r1 = min(R, r0 + per);
-    // ids outside 0..E-1 are skipped (they get no place), which keeps every
-    // write in bounds whatever the caller passes.
     for (int r = r0 + lane; r < r1; r += kWave) {
         const int e = ids[r];
-        if (e >= 0 && e < E) atomicAdd(&hist[wv][e], 1);
+        if (e >= 0 && e < E) atomicAdd(&sm.hist[wv][e], 1);
     }
     __syncthreads();
-    if (tid < E) {
+    for (int e = tid; e < E; e += NW * kWave) {
         int sacc = 0;
-        for (int w = 0; w < kPermWaves; w++) {
-            const int c = hist[w][tid];
-            hist[w][tid] = sacc;
+        for (int w = 0; w < NW; w++) {
+            const int c = sm.hist[w][e];
+            sm.hist[w][e] = sacc;
             sacc += c;
         }
-        cnt[tid] = sacc;
+        sm.cnt[e] = sacc;
     }
     __syncthreads();
     int total;
-    const int ex = block_scan_256(tid < E ? cnt[tid] : 0, scan, &total);
+    const int ex = block_scan_256(tid < E ? sm.cnt[tid] : 0, sm.scan, &total);
     if (tid < E) {
-        off[tid] = ex;
-        counts[tid] = cnt[tid];
-        offsets[tid] = ex;
+        sm.off[tid] = ex;
+        o.counts[tid] = sm.cnt[tid];
+        o.offsets[tid] = ex;
     }
     if (tid == 0) {
-        off[E] = total;
-        offsets[E] = total;
+        sm.off[E] = total;
+        o.offsets[E] = total;
     }
     __syncthreads();
     const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
@@ -293,20 +290,26 @@ __global__ __launch_bounds__(kPermThreads) void k_permute(const int32_t *ids, in
             peers &= ((e >> b) & 1) ? m : ~m;
         }
         const int rank = __popcll(peers & lt_mask);
-        int pos = 0;
         if (valid) {
-            pos = off[e] + hist[wv][e] + rank;
-            sorted[pos] = r;
-            route_pos[r] = pos;
+            const int pos = sm.off[e] + sm.hist[wv][e] + rank;
+            o.sorted[pos] = r;
+            o.route_pos[r] = pos;
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
-        if (valid && rank == 0) hist[wv][e] += __popcll(peers);
+        if (valid && rank == 0) sm.hist[wv][e] += __popcll(peers);
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
     }
     __syncthreads();
-    write_plan(E, tile_rows, cnt, off, scan, active, tiles);
+    write_plan(E, o.tile_rows, sm.cnt, sm.off, sm.scan, o.active, o.tiles);
+}
+
+constexpr int kPermWaves = 16;
+
+__global__ __launch_bounds__(kPermWaves * kWave) void k_permute(const int32_t *ids, int R, int E, PermuteOut o) {
+    __shared__ PermuteSmem<kPermWaves> sm;
+    permute_block<kPermWaves>(ids, R, E, o, sm);
 }
 
 __global__ __launch_bounds__(256) void k_plan_from_offsets(int E, int tile_rows, const int32_t *offsets,
@@ -326,8 +329,8 @@ __global__ __launch_bounds__(256) void k_plan_from_offsets(int E, int tile_rows,
 hipError_t launch_permute(int E, int R, int tile_rows, const int32_t *ids, int32_t *counts,
                           int32_t *offsets, int32_t *sorted, int32_t *route_pos, int32_t *active,
                           int32_t *tiles, hipStream_t s) {
-    hipLaunchKernelGGL(k_permute, dim3(1), dim3(kPermThreads), 0, s, ids, R, E, tile_rows, counts,
-                       offsets, sorted, route_pos, active, tiles);
+    PermuteOut o{counts, offsets, sorted, route_pos, active, tiles, tile_rows};
+    hipLaunchKernelGGL(k_permute, dim3(1), dim3(kPermWaves * kWave), 0, s, ids, R, E, o);
     return hipGetLastError();
 }
 
@@ -335,6 +338,175 @@ hipError_t launch_plan_from_offsets(int E, int tile_rows, const int32_t *offsets
                                     int32_t *tiles, hipStream_t s) {
     hipLaunchKernelGGL(k_plan_from_offsets, dim3(1), dim3(256), 0, s, E, tile_rows, offsets, active,
                        tiles);
+    return hipGetLastError();
+}
+
+// ----------------------------------------------------- fused small-batch route
+// Workgroup e computes expert e's logits for all M <= kSmallM tokens (its
+// waves split the row; partial dots meet in LDS) and stores them; then it
+// takes a ticket.  The workgroup
+// holding the last ticket sees every logit (release/acquire at agent scope
+// around the ticket), runs the top-k of every token and the permutation, and
+// returns the ticket counter to zero for the next call.
+constexpr int kSmallM = 16;
+
+struct RouteSmallArgs {
+    const void *x, *router;
+    const float *bias, *tok_scale;
+    int M, H, E, k, select, bias_mode;
+    float *logits;
+    int32_t *ids;
+    float *w;
+    PermuteOut o;
+    uint32_t *ticket;
+};
+
+constexpr int kRouteWaves = 4;
+constexpr int kSmallRoutes = 2 * kWave; // routes the one-wave permutation handles
+
+// Exclusive prefix over the 64 lanes of a wave (shuffle scan); total in *tot.
+__device__ __forceinline__ int wave_excl_scan(int v, int lane, int *tot) {
+    int x = v;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        const int y = __shfl_up(x, off);
+        if (lane >= off) x += y;
+    }
+    *tot = __shfl(x, kWave - 1);
+    return x - v;
+}
+
+// Stable counting sort of R <= 128 routes by expert, by one wave, from ids in
+// LDS.  Lane l owns routes l and l+64 and experts l, l+64, l+128, l+192.  A
+// route's place is the number of routes with a smaller expert id plus the
+// number of earlier routes with the same id.
+__device__ void permute_wave(const int *s_ids, int R, int E, int lane, const PermuteOut &o) {
+    const int r0 = lane, r1 = lane + kWave;
+    const int e0 = r0 < R ? s_ids[r0] : 0x7fffffff;
+    const int e1 = r1 < R ? s_ids[r1] : 0x7fffffff;
+    int pos0 = 0, pos1 = 0;
+    int cnt[kKeysPerLane] = {0, 0, 0, 0};
+    for (int r = 0; r < R; r++) {
+        const int v = s_ids[r];
+        pos0 += (v < e0) || (v == e0 && r < r0);
+        pos1 += (v < e1) || (v == e1 && r < r1);
+#pragma unroll
+        for (int c = 0; c < kKeysPerLane; c++) cnt[c] += v == lane + kWave * c;
+    }
+    if (r0 < R && e0 >= 0 && e0 < E) { o.sorted[pos0] = r0; o.route_pos[r0] = pos0; }
+    if (r1 < R && e1 >= 0 && e1 < E) { o.sorted[pos1] = r1; o.route_pos[r1] = pos1; }
+    int base = 0, abase = 0;
+#pragma unroll
+    for (int c = 0; c < kKeysPerLane; c++) {
+        const int e = lane + kWave * c;
+        const int n = e < E ? cnt[c] : 0;
+        int tot, atot;
+        const int ex = wave_excl_scan(n, lane, &tot);
+        const int aex = wave_excl_scan(n > 0 ? 1 : 0, lane, &atot);
+        if (e < E) {
+            o.counts[e] = n;
+            o.offsets[e] = base + ex;
+            if (n > 0) o.active[1 + abase + aex] = e;
+        }
+        base += tot;
+        abase += atot;
+    }
+    if (lane == 0) {
+        o.offsets[E] = base;
+        o.active[0] = abase;
+    }
+}
+
+template <int XDT, int RDT, bool TAIL>
+__global__ __launch_bounds__(kRouteWaves * kWave) void k_route_small(RouteSmallArgs a) {
+    __shared__ float s_part[kRouteWaves][kSmallM];
+    __shared__ int s_ids[kSmallRoutes];
+    __shared__ int last;
+    const int wave = uniform(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    // workgroup e computes expert e's logits; wave w takes a quarter of the row
+    const int e = blockIdx.x;
+    const int nch = a.H / 8;
+    const int cb = wave * nch / kRouteWaves, ce = (wave + 1) * nch / kRouteWaves;
+    const char *wrow = reinterpret_cast<const char *>(a.router) + (size_t)e * a.H * dt_bytes<RDT>();
+    for (int t0 = 0; t0 < a.M; t0 += 8) {
+        float acc[8];
+        const int nt = min(8, a.M - t0);
+        router_dots<XDT, RDT, 8>(a.x, wrow, a.H, t0, nt, lane, acc, cb, ce);
+#pragma unroll
+        for (int tm = 0; tm < 8; tm++)
+            if (tm < nt && lane == 0) s_part[wave][t0 + tm] = acc[tm];
+    }
+    __syncthreads();
+    if (threadIdx.x < a.M) {
+        const int t = threadIdx.x;
+        float v = 0.f;
+#pragma unroll
+        for (int w = 0; w < kRouteWaves; w++) v += s_part[w][t];
+        if (a.tok_scale) v *= a.tok_scale[t];
+        a.logits[(size_t)t * a.E + e] = v;
+    }
+    if constexpr (!TAIL) return;
+    __threadfence();
+    __syncthreads();
+    if (threadIdx.x == 0) last = atomicAdd(a.ticket, 1u) == gridDim.x - 1;
+    __syncthreads();
+    if (!last) return;
+    __threadfence();
+    for (int t = wave; t < a.M; t += kRouteWaves)
+        topk_wave(a.logits + (size_t)t * a.E, a.bias, a.E, a.k, a.select, a.bias_mode, lane,
+                  a.ids + (size_t)t * a.k, a.w + (size_t)t * a.k, s_ids + t * a.k);
+    __syncthreads();
+    if (wave == 0) permute_wave(s_ids, a.M * a.k, a.E, lane, a.o);
+    if (threadIdx.x == 0) {
+        __threadfence();
+        atomicExch(a.ticket, 0u);
+    }
+}
+
+int route_small_max_tokens() { return kSmallM; }
+
+template <bool TAIL>
+static void route_small_dispatch(const Layer &L, const RouteSmallArgs &a, hipStream_t s) {
+    const dim3 grid(L.E), block(kRouteWaves * kWave);
+    if (L.xdt == DT_BF16 && L.rdt == DT_BF16)
+        hipLaunchKernelGGL((k_route_small<DT_BF16, DT_BF16, TAIL>), grid, block, 0, s, a);
+    else if (L.xdt == DT_BF16)
+        hipLaunchKernelGGL((k_route_small<DT_BF16, DT_F32, TAIL>), grid, block, 0, s, a);
+    else if (L.rdt == DT_BF16)
+        hipLaunchKernelGGL((k_route_small<DT_F32, DT_BF16, TAIL>), grid, block, 0, s, a);
+    else
+        hipLaunchKernelGGL((k_route_small<DT_F32, DT_F32, TAIL>), grid, block, 0, s, a);
+}
+
+hipError_t launch_route_small(const Layer &L, const void *x, const void *router, const float *bias,
+                              const float *tok_scale, int M, float *logits, int32_t *ids, float *w,
+                              int32_t *counts, int32_t *offsets, int32_t *sorted, int32_t *route_pos,
+                              int32_t *active, uint32_t *ticket, hipStream_t s) {
+    if (M > kSmallM) return hipErrorInvalidValue;
+    RouteSmallArgs a{x, router, L.bias_mode ? bias : nullptr, tok_scale, M, L.H, L.E, L.k, L.select,
+                     L.bias_mode, logits, ids, w,
+                     PermuteOut{counts, offsets, sorted, route_pos, active, nullptr, 1}, ticket};
+    route_small_dispatch<true>(L, a, s);
+    return hipGetLastError();
+}
+
+hipError_t launch_router_small(const Layer &L, const void *x, const void *router, const float *tok_scale,
+                               int M, float *logits, hipStream_t s) {
+    if (M > kSmallM) return hipErrorInvalidValue;
+    RouteSmallArgs a{x, router, nullptr, tok_scale, M, L.H, L.E, L.k, L.select, L.bias_mode, logits,
+                     nullptr, nullptr, PermuteOut{}, nullptr};
+    route_small_dispatch<false>(L, a, s);
+    return hipGetLastError();
+}
+
+// Zero `n` 32-bit words (used for the workspace's ticket words).
+__global__ void k_zero_words(uint32_t *p, int n) {
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i < n) p[i] = 0u;
+}
+
+hipError_t launch_zero_words(uint32_t *p, int n, hipStream_t s) {
+    hipLaunchKernelGGL(k_zero_words, dim3((n + 255) / 256), dim3(256), 0, s, p, n);
     return hipGetLastError();
 }
 

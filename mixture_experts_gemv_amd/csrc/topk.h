@@ -1,0 +1,95 @@
+// Wave-level top-k with softmax weights (device code shared by the routing
+// and the single-token expert kernels).
+#pragma once
+
+#include "common.h"
+
+namespace moe {
+
+constexpr int kMaxE = 256;
+constexpr int kKeysPerLane = kMaxE / kWave;
+
+// One wave selects the top-k experts of one token from its logit row.
+// Lane l holds experts l, l+64, l+128, l+192.  Selection key
+// s = logit (+ bias for LOGIT and SELECT_ONLY); softmax input u = logit
+// (+ bias for LOGIT).  k rounds of a wave argmax on the order-preserving key,
+// ties to the lower expert id.  On return lane j < k holds the j-th pick
+// (descending key) in *id and its weight in *wt: softmax over the k picks
+// (select 0) or the all-expert softmax read at the pick (select 1).
+__device__ inline void topk_wave_core(const float *lrow, const float *bias, int E, int k, int select,
+                                      int bias_mode, int lane, int *id, float *wt) {
+    uint32_t key[kKeysPerLane];
+    float u[kKeysPerLane];
+    float lv[kKeysPerLane], bv[kKeysPerLane];
+    // all loads first (clamped index, masked below) so they overlap
+#pragma unroll
+    for (int c = 0; c < kKeysPerLane; c++) {
+        const int e = min(lane + kWave * c, E - 1);
+        lv[c] = lrow[e];
+        bv[c] = bias ? bias[e] : 0.f;
+    }
+#pragma unroll
+    for (int c = 0; c < kKeysPerLane; c++) {
+        const int e = lane + kWave * c;
+        if (e < E) {
+            const float sk = bias_mode != 0 ? lv[c] + bv[c] : lv[c];
+            u[c] = bias_mode == 1 ? lv[c] + bv[c] : lv[c];
+            key[c] = order_key(sk);
+        } else {
+            u[c] = -INFINITY;
+            key[c] = 0u;
+        }
+    }
+    uint32_t taken = 0u;
+    int my_id = 0;
+    float my_u = -INFINITY;
+    for (int j = 0; j < k; j++) {
+        uint32_t bk = 0u;
+        int bid = 0x7fffffff;
+        float bu = 0.f;
+#pragma unroll
+        for (int c = 0; c < kKeysPerLane; c++) {
+            const int e = lane + kWave * c;
+            const bool cand = e < E && !((taken >> c) & 1u);
+            if (cand && (bid == 0x7fffffff || key[c] > bk)) { bk = key[c]; bid = e; bu = u[c]; }
+        }
+        const uint32_t mk = wave_max_u32(bid == 0x7fffffff ? 0u : bk);
+        const int win = wave_min_i32((bid != 0x7fffffff && bk == mk) ? bid : 0x7fffffff);
+        if ((win & 63) == lane) taken |= 1u << (win >> 6);
+        const float wu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bid == win ? bu : 0.f), win & 63));
+        if (lane == j) { my_id = win; my_u = wu; }
+    }
+    float wj;
+    if (select == 0) {
+        const float m = wave_max(lane < k ? my_u : -INFINITY);
+        const float ex = lane < k ? expf(my_u - m) : 0.f;
+        const float z = wave_sum(ex);
+        wj = ex / z;
+    } else {
+        float m = -INFINITY;
+#pragma unroll
+        for (int c = 0; c < kKeysPerLane; c++) m = fmaxf(m, u[c]);
+        m = wave_max(m);
+        float z = 0.f;
+#pragma unroll
+        for (int c = 0; c < kKeysPerLane; c++)
+            if (lane + kWave * c < E) z += expf(u[c] - m);
+        z = wave_sum(z);
+        wj = expf(my_u - m) / z;
+    }
+    *id = my_id;
+    *wt = wj;
+}
+
+// Rank of lane j's pick among the k picks in ascending expert id (lanes < k):
+// the order in which a one-token batch lists its touched experts.
+__device__ inline int pick_rank(int my_id, int k, int lane) {
+    int rank = 0;
+    for (int j = 0; j < k; j++) {
+        const int other = __builtin_amdgcn_readlane(my_id, j);
+        rank += other < my_id;
+    }
+    return lane < k ? rank : 0;
+}
+
+} // namespace moe

@@ -194,6 +194,24 @@ def test_forward_small(name, kw, Ms):
         forward_parity(spec, layer, x, dl, what=f"{name} M={M}")
 
 
+def test_workspace_reuse_across_calls():
+    """One workspace, many calls of different M: the ticket words come back to
+    zero after every call, so each result equals a fresh-workspace result."""
+    spec = synth.small_spec(hidden=256, num_experts=16, top_k=4, expert_inter=192,
+                            bias_mode=BIAS_LOGIT, bias_kind="normal", seed=1210)
+    layer = synth.make_layer(spec)
+    dl = device_layer(spec, layer, 16)
+    ws = dl.workspace(16)
+    for n, M in enumerate((1, 16, 3, 1, 9, 16, 1)):
+        x = dl.x_tensor(synth.make_tokens(spec, M, batch=n))
+        say(f"workspace reuse call {n} M={M}")
+        a = dl.forward(x, ws=ws).cpu().numpy()
+        b = dl.forward(x).cpu().numpy()
+        assert np.array_equal(a, b), f"call {n} (M={M}) differs with a reused workspace"
+    words = ws[:256].view(torch.int32).cpu().numpy()
+    assert not words.any(), "ticket words not returned to zero"
+
+
 def test_forward_repeatable():
     """Two calls give bitwise-identical y (no atomics in the combine)."""
     spec = synth.small_spec(hidden=256, num_experts=16, top_k=4, expert_inter=192, seed=1200)
