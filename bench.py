@@ -17,7 +17,6 @@ the fp64 CPU oracle on a bounded sample of the same workload.
 from __future__ import annotations
 
 import argparse
-import ctypes
 import json
 import math
 import os
@@ -32,31 +31,8 @@ sys.path.insert(0, ROOT)
 METRIC = "MoE layer tokens/s at M=1/16/2048 + % of HBM / MFMA roofline"
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFS = 2500.0
-
-
-# ------------------------------------------------------------------ HIP events
-class HipEvents:
-    def __init__(self, n: int):
-        self.hip = ctypes.CDLL("libamdhip64.so")
-        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
-        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
-                                                 ctypes.c_void_p]
-        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
-        self.ev = []
-        for _ in range(n):
-            e = ctypes.c_void_p()
-            assert self.hip.hipEventCreate(ctypes.byref(e)) == 0
-            self.ev.append(e.value)
-
-    def elapsed_ms(self, a: int, b: int) -> float:
-        ms = ctypes.c_float()
-        rc = self.hip.hipEventElapsedTime(ctypes.byref(ms), self.ev[a], self.ev[b])
-        assert rc == 0, f"hipEventElapsedTime failed ({rc})"
-        return ms.value
-
-    def close(self):
-        for e in self.ev:
-            self.hip.hipEventDestroy(e)
+# gate/up + SwiGLU kernel of each moe_forward path (the layer's dominant kernel)
+GATEUP_KERNEL = {"single": "k_gateup_m1", "gemv": "k_gateup_gemv", "mfma": "k_gemm<0"}
 
 
 # ------------------------------------------------------------------ workload
@@ -155,6 +131,8 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches only")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="run 5 plain 256 MiB device copies (counter calibration) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -162,8 +140,21 @@ def main() -> int:
         return 2
 
     import torch
+    if args.copy_probe:
+        # A plain device copy of known size: the reference reading of the HBM
+        # byte counters (FETCH_SIZE, WRITE_SIZE) under rocprofv3 --pmc.
+        n = 256 << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes_per_copy": n, "copies": 5}), flush=True)
+        return 0
     import synth
     import mixture_experts_gemv_amd as m
+    from mixture_experts_gemv_amd import profiling
+    from mixture_experts_gemv_amd.events import HipEvents
     from mixture_experts_gemv_amd.layer import MoeLayer
 
     spec = synth.SPECS[args.workload]
@@ -216,13 +207,11 @@ def main() -> int:
         step(i)
     ev = HipEvents(2)
     torch.cuda.synchronize()
-    hip = ev.hip
-    hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
     stream = torch.cuda.current_stream().cuda_stream
-    hip.hipEventRecord(ev.ev[0], stream)
+    ev.record(0, stream)
     for i in range(K):
         step(i)
-    hip.hipEventRecord(ev.ev[1], stream)
+    ev.record(1, stream)
     torch.cuda.synchronize()
     eager_ms = ev.elapsed_ms(0, 1)
 
@@ -240,17 +229,18 @@ def main() -> int:
         torch.cuda.synchronize()
         g.replay()                      # warm replay
         torch.cuda.synchronize()
-        hip.hipEventRecord(ev.ev[0], stream)
+        ev.record(0, stream)
         g.replay()
-        hip.hipEventRecord(ev.ev[1], stream)
+        ev.record(1, stream)
         torch.cuda.synchronize()
         graph_ms = ev.elapsed_ms(0, 1)
         del g
     total_ms = graph_ms if graph_ms is not None else eager_ms
     ms_per_step = total_ms / K
 
-    # ---- timed region: per kernel (events between the layer's kernels)
-    n_ev = 8
+    # ---- timed region: per kernel (start/end events recorded by each
+    # kernel's own dispatch, on the layer's stream)
+    n_ev = 16
     kev = HipEvents(n_ev * K)
     stages = None
     for i in range(W):
@@ -264,13 +254,19 @@ def main() -> int:
     torch.cuda.synchronize()
     per_stage = {}
     for j, sid in enumerate(stages):
-        d = [kev.elapsed_ms(i * n_ev + j, i * n_ev + j + 1) for i in range(K)]
+        d = [kev.elapsed_ms(i * n_ev + 2 * j, i * n_ev + 2 * j + 1) for i in range(K)]
         per_stage[m.MOE_STAGE_NAMES[sid]] = float(np.mean(d)) * 1e3  # us
-    timed_total_us = float(np.mean([kev.elapsed_ms(i * n_ev, i * n_ev + len(stages)) for i in range(K)])) * 1e3
+    timed_total_us = float(np.mean([kev.elapsed_ms(i * n_ev, i * n_ev + 2 * len(stages) - 1)
+                                    for i in range(K)])) * 1e3
     kev.close()
     ev.close()
 
+    run = m.moe_forward_path(base.plan, M)
+    kernel = GATEUP_KERNEL[m.MOE_RUN_NAMES[run]]
+    tag = f"{spec.name}_M{M}"
+    trec = profiling.load_traffic(os.path.join(ROOT, "profiles"), kernel, tag)
     gateup_us = per_stage.get("gateup")
+    gateup_flops = M * spec.top_k * 4 * spec.hidden * spec.expert_inter + M * 4 * spec.hidden * spec.shared_inter
     achieved = gateup_bytes_avg / (gateup_us * 1e-6) / 1e9
     layer_gbs = layer_bytes_avg / (ms_per_step * 1e-3) / 1e9
     flops = algorithmic_flops(spec, M)
@@ -298,10 +294,13 @@ def main() -> int:
         },
         "eager": {"tokens_per_s": M * K / (eager_ms * 1e-3), "ms_per_step": eager_ms / K},
         "roofline": {
-            "bound": "hbm", "kernel": "gate/up + SwiGLU (k_gateup_gemv)",
+            "bound": "hbm", "kernel": kernel, "path": m.MOE_RUN_NAMES[run],
             "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": trec["traffic_bytes"] if trec else None,
+            "traffic_source": os.path.basename(trec["_file"]) if trec else None,
             "bytes_per_launch": gateup_bytes_avg, "us_per_launch": gateup_us,
+            "mfma_frac": gateup_flops / (gateup_us * 1e-6) / (MFMA_BF16_PEAK_TFS * 1e12),
         },
         "layer": {
             "algorithmic_bytes": layer_bytes_avg, "achieved_GBs": layer_gbs,

@@ -211,16 +211,30 @@ typedef enum {
     MOE_STAGE_COMBINE = 6  /* weighted combine (unfused forms only) */
 } moe_stage;
 
-/* moe_forward with timing: the same kernels on the same stream, with
- * events[0] recorded before the first kernel and events[i+1] after the i-th.
- * events are hipEvent_t handles created by the caller; max_events >= 8 is
- * always enough.  stages[i] (moe_stage) names the i-th kernel and *n_stages
- * receives their number.  Used to attribute time to kernels. */
+/* moe_forward with timing: the same kernels on the same stream, each launched
+ * with hipExtLaunchKernel so that events[2i] is recorded when the i-th stage's
+ * kernel starts and events[2i+1] when it ends (the dispatch gap between
+ * kernels is outside every pair, as in a profiler's kernel trace).  events are
+ * hipEvent_t handles created by the caller; max_events >= 14 is always enough
+ * (MOE_ERR_INVALID when a stage finds no free pair).  stages[i] (moe_stage)
+ * names the i-th stage and *n_stages receives their number.  Not for use
+ * under stream capture.  Used to attribute time to kernels. */
 moe_status moe_forward_timed(const moe_plan *plan, const void *x, const moe_weights *wts,
                              int32_t M, float *y, int32_t *ids_out, float *w_out,
                              int32_t *counts_out, void *ws, size_t ws_bytes, void *stream,
                              void **events, int32_t max_events, int32_t *stages,
                              int32_t *n_stages);
+
+/* Kernel family moe_forward launches for an M-token call under this plan. */
+typedef enum {
+    MOE_RUN_SINGLE = 0, /* one token: router, then two self-routing expert GEMVs */
+    MOE_RUN_GEMV = 1,   /* routing + permutation, then gathered GEMV kernels */
+    MOE_RUN_MFMA = 2    /* routing + permutation, then the MFMA grouped GEMM */
+} moe_run;
+
+/* The moe_run value for M tokens, or -1 (moe_last_error set) when the plan is
+ * NULL or M is outside [1, max_tokens].  Pure host logic, no device work. */
+int32_t moe_forward_path(const moe_plan *plan, int32_t M);
 
 /* Convert Q8_0 blocks (34 bytes: little-endian fp16 scale, then 32 int8) of a
  * [rows][cols] matrix, cols a multiple of 32, into the two planes the layer

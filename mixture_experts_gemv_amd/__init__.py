@@ -82,6 +82,8 @@ def lib() -> ctypes.CDLL:
         L.moe_q8_0_split.argtypes = [P, ctypes.c_int64, I32, P, P, P]
         L.moe_workspace_init.argtypes = [P, P, SZ, P]
         L.moe_workspace_init.restype = I32
+        L.moe_forward_path.argtypes = [P, I32]
+        L.moe_forward_path.restype = I32
         for f in ("moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_forward",
                   "moe_forward_timed", "moe_q8_0_split"):
             getattr(L, f).restype = I32
@@ -199,6 +201,15 @@ def moe_forward(plan, x, weights, M, y, ids_out, w_out, counts_out, ws, stream=N
 
 
 MOE_STAGE_NAMES = ("rms", "router", "topk", "permute", "gateup", "down", "combine")
+MOE_RUN_NAMES = ("single", "gemv", "mfma")
+
+
+def moe_forward_path(plan, M) -> int:
+    """moe_run value (0 single, 1 gemv, 2 mfma) of an M-token moe_forward."""
+    r = lib().moe_forward_path(plan.handle, M)
+    if r < 0:
+        raise MoeError(1, lib().moe_last_error().decode())
+    return r
 
 
 def moe_forward_timed(plan, x, weights, M, y, ids_out, w_out, counts_out, ws, events,

@@ -2,12 +2,37 @@
 // Target: CDNA4 (gfx950), wave64.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace moe {
 
 constexpr int kWave = 64;
+
+// ---------------------------------------------------------------- launches
+// Optional timing of the kernels one stage of the layer launches.  While
+// `stop` is set, every launch goes through hipExtLaunchKernel: the first one
+// records `start` when it begins and each one records `stop` when it ends, so
+// the pair spans exactly the stage's kernels, as a profiler's kernel trace
+// does, without the dispatch gap in front of them.
+struct StageTimer {
+    hipEvent_t start = nullptr, stop = nullptr;
+    int launches = 0;
+};
+StageTimer &stage_timer(); // per host thread
+
+template <typename... P, typename... A>
+inline void launch_kernel(void (*k)(P...), dim3 grid, dim3 block, uint32_t shm, hipStream_t s, A... args) {
+    StageTimer &t = stage_timer();
+    if (t.stop) {
+        hipExtLaunchKernelGGL(k, grid, block, shm, s, t.launches == 0 ? t.start : nullptr, t.stop, 0,
+                              static_cast<P>(args)...);
+        t.launches++;
+    } else {
+        hipLaunchKernelGGL(k, grid, block, shm, s, static_cast<P>(args)...);
+    }
+}
 
 enum Dtype : int { DT_F32 = 0, DT_BF16 = 1, DT_Q8 = 2 };
 

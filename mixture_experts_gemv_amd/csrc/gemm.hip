@@ -1,19 +1,427 @@
-// MFMA grouped-GEMM path of the routed MoE layer (bf16, large batches).
+// MFMA grouped-GEMM path of the routed MoE layer (bf16 operands, fp32
+// accumulate), for batches large enough that every touched expert sees many
+// tokens: the per-expert products are then real dense contractions.
+//
+// One kernel template, four uses:
+//   gate/up  A = gathered token rows of x, B = gate and up rows of the tile's
+//            expert, epilogue silu(clamp(g)) * clamp(v) -> act (fp32);
+//   down     A = act rows (fp32, split into bf16 hi + lo so the product keeps
+//            about 16 bits of act), B = down rows -> per-route outputs;
+//   shared   the same two with identity rows (all tokens), for a shared expert.
+// (The router has its own small-tile kernel at the end of this file.)
+//
+// Tiles: kBM = 128 rows (tokens or routes of one expert, so that most
+// experts' tokens share one pass over the weights) x 128 (gate/up: 32 columns
+// of gate and of up per wave) or 256 (down: 64 columns per wave) output
+// columns, kBK = 64 reduction elements per step.  Four waves each own all
+// 128 rows of their columns and issue v_mfma_f32_32x32x16_bf16.  The A tile
+// is gathered into LDS (double buffered, rows padded against bank
+// conflicts); B fragments are loaded from HBM straight into registers in the
+// MFMA operand layout, one step ahead.
 #include "common.h"
 #include "launch.h"
 
 namespace moe {
 
-int mfma_tile_rows() { return 128; }
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-hipError_t launch_gateup_mfma(const Layer &, const void *, const float *, const Mats &, const Mats &,
-                              const Routing &, int, int, float *, float *, hipStream_t) {
-    return hipErrorNotSupported;
+constexpr int kMB = 4;              // 32-row blocks per wave
+constexpr int kBM = 32 * kMB;       // rows per tile
+constexpr int kBK = 64;
+constexpr int kLdsRow = kBK + 8;    // bf16 elements per LDS row (144 bytes)
+constexpr int kGW = 4;
+constexpr int kGThreads = kGW * kWave;
+
+int mfma_tile_rows() { return kBM; }
+
+enum GemmKind { GK_GATEUP = 0, GK_PLAIN = 1 };
+
+struct GemmArgs {
+    const void *a;           // x: bf16 [rows][K]; act: fp32 [rows][K] (rows = sorted positions)
+    const int32_t *sorted;   // x rows of routed tiles: token = sorted[p] / k_route; null: row = p
+    int k_route;
+    const int32_t *tiles;    // tile list (layout in the permutation); null: identity tiles
+    const int32_t *offsets;  // expert row ranges (routed tiles)
+    int E;                   // experts (tile list layout)
+    int M;                   // identity tiles: number of rows
+    int max_tiles;           // tile slots in the grid
+    int ksplit;              // reduction split: slice ks writes out + ks * slab
+    size_t slab;
+    const uint16_t *b0, *b1; // bf16 [experts][N][K]; b1 only for gate/up
+    size_t b_stride;         // elements between experts' matrices
+    int N, K;
+    const float *tok_scale;  // per-token scale of the products (pre-norm), or null
+    float limit;             // gate/up clamp (0 = off)
+    float *out;              // fp32 [rows][ldo]
+    int ldo;
+    int n_ntiles;            // column tiles
+};
+
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+    const uint32_t u = __float_as_uint(f);
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
-hipError_t launch_down_mfma(const Layer &, const float *, const float *, const Mats &, const Mats &,
-                            const Routing &, int, int, float *, float *, hipStream_t) {
-    return hipErrorNotSupported;
+template <int KIND>
+struct GemmShape {
+    static constexpr int NB = 2;                                  // 32-column B blocks per wave
+    static constexpr int WCOLS = KIND == GK_GATEUP ? 32 : 64;     // output columns per wave
+    static constexpr int COLS = kGW * WCOLS;                      // output columns per tile
+};
+
+template <int KIND, bool A_F32>
+__global__ __launch_bounds__(kGThreads, 2) void k_gemm(GemmArgs a) {
+    constexpr int NS = A_F32 ? 2 : 1;      // bf16 planes of A (hi, lo)
+    constexpr int NB = GemmShape<KIND>::NB;
+    constexpr int WCOLS = GemmShape<KIND>::WCOLS;
+    __shared__ __attribute__((aligned(16))) uint16_t sA[2][NS][kBM * kLdsRow];
+    __shared__ const char *s_src[kBM];
+    __shared__ int s_tok[kBM];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = uniform(tid >> 6);
+
+    // ---- which tile, column block and reduction slice.  g runs over an
+    // expert's (slice, column block, token tile) with the token tile fastest.
+    // Consecutive workgroups land on different XCDs, so the column blocks of
+    // one expert spread over all eight L2s and HBM channels at once; the
+    // token tiles of a column block follow one another in launch order.
+    // (Renumbering so that each XCD takes a contiguous run, or putting the
+    // tile index fastest across experts, measured 10-30% slower.)
+    const int g = blockIdx.x;
+    const int per_tile = a.n_ntiles * a.ksplit; // workgroups per token tile
+    int e = 0, ts, Te, p0, nrows;
+    if (a.tiles) {
+        const int q = g / per_tile;
+        if (q >= a.tiles[0]) return;
+        const int32_t *pairs = a.tiles + 2 + a.E;
+        e = pairs[2 * q];
+        ts = a.tiles[1 + e];
+        Te = a.tiles[2 + e] - ts;
+    } else {
+        ts = 0;
+        Te = (a.M + kBM - 1) / kBM;
+        if (g >= Te * per_tile) return;
+    }
+    const int local = g - ts * per_tile;
+    const int ks = local / (Te * a.n_ntiles);
+    const int rem = local - ks * Te * a.n_ntiles;
+    const int nt = rem / Te, tl = rem - nt * Te;
+    if (a.tiles) {
+        p0 = a.tiles[2 + a.E + 2 * (ts + tl) + 1];
+        nrows = min(kBM, a.offsets[e + 1] - p0);
+    } else {
+        p0 = tl * kBM;
+        nrows = min(kBM, a.M - p0);
+    }
+    if (tid < kBM) {
+        const int p = p0 + min(tid, nrows - 1);
+        const int t = a.sorted ? a.sorted[p] / a.k_route : p;
+        s_src[tid] = A_F32 ? reinterpret_cast<const char *>(a.a) + (size_t)p * a.K * 4
+                           : reinterpret_cast<const char *>(a.a) + (size_t)t * a.K * 2;
+        s_tok[tid] = t;
+    }
+
+    const int K = a.K, N = a.N, NK = K / kBK;
+    const int kb = ks * NK / a.ksplit, nk = (ks + 1) * NK / a.ksplit - kb; // this slice's K steps
+    const int colw = nt * GemmShape<KIND>::COLS + wave * WCOLS;
+    const bool wave_on = colw < N;
+    // B row of this lane for each column block (gate/up: block 0 gate, 1 up)
+    const uint16_t *brow[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; nb++) {
+        const uint16_t *mat = (KIND == GK_GATEUP && nb == 1) ? a.b1 : a.b0;
+        const int col = KIND == GK_GATEUP ? colw + (lane & 31) : colw + nb * 32 + (lane & 31);
+        brow[nb] = mat + (size_t)e * a.b_stride + (size_t)min(col, N - 1) * K + 8 * (lane >> 5);
+    }
+    __syncthreads();
+
+    // ---- A staging: global -> registers -> LDS
+    constexpr int CPR = A_F32 ? 16 : 8;               // 16-byte chunks per row per K step
+    constexpr int A_CHUNKS = kBM * CPR / kGThreads;   // per thread
+    auto load_a = [&](int k0, u32x4 (&r)[A_CHUNKS]) {
+#pragma unroll
+        for (int j = 0; j < A_CHUNKS; j++) {
+            const int c = tid + kGThreads * j;
+            const int row = c / CPR, col = c % CPR;
+            r[j] = *reinterpret_cast<const u32x4 *>(s_src[row] + (size_t)k0 * (A_F32 ? 4 : 2) + col * 16);
+        }
+    };
+    auto store_a = [&](int buf, const u32x4 (&r)[A_CHUNKS]) {
+#pragma unroll
+        for (int j = 0; j < A_CHUNKS; j++) {
+            const int c = tid + kGThreads * j;
+            const int row = c / CPR, col = c % CPR;
+            if constexpr (A_F32) {
+                const float f[4] = {__uint_as_float(r[j].x), __uint_as_float(r[j].y),
+                                    __uint_as_float(r[j].z), __uint_as_float(r[j].w)};
+                uint32_t hi[4], lo[4];
+#pragma unroll
+                for (int q = 0; q < 4; q++) {
+                    hi[q] = f32_to_bf16_rne(f[q]);
+                    lo[q] = f32_to_bf16_rne(f[q] - __uint_as_float(hi[q] << 16));
+                }
+                const u32x2 vh = {hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16)};
+                const u32x2 vl = {lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16)};
+                *reinterpret_cast<u32x2 *>(&sA[buf][0][row * kLdsRow + col * 4]) = vh;
+                if constexpr (NS == 2) *reinterpret_cast<u32x2 *>(&sA[buf][NS - 1][row * kLdsRow + col * 4]) = vl;
+            } else {
+                *reinterpret_cast<u32x4 *>(&sA[buf][0][row * kLdsRow + col * 8]) = r[j];
+            }
+        }
+    };
+    // ---- B fragments for one K step: [substep][column block]
+    auto load_b = [&](int k0, u32x4 (&bq)[4][NB]) {
+#pragma unroll
+        for (int s = 0; s < 4; s++)
+#pragma unroll
+            for (int nb = 0; nb < NB; nb++)
+                bq[s][nb] = *reinterpret_cast<const u32x4 *>(brow[nb] + k0 + 16 * s);
+    };
+
+    f32x16 acc[kMB][NB];
+#pragma unroll
+    for (int mb = 0; mb < kMB; mb++)
+#pragma unroll
+        for (int nb = 0; nb < NB; nb++)
+#pragma unroll
+            for (int r = 0; r < 16; r++) acc[mb][nb][r] = 0.f;
+
+    auto compute = [&](int buf, const u32x4 (&bq)[4][NB]) {
+#pragma unroll
+        for (int s = 0; s < 4; s++) {
+#pragma unroll
+            for (int mb = 0; mb < kMB; mb++) {
+                const int off = (mb * 32 + (lane & 31)) * kLdsRow + 16 * s + 8 * (lane >> 5);
+#pragma unroll
+                for (int h = 0; h < NS; h++) {
+                    const bf16x8 af = *reinterpret_cast<const bf16x8 *>(&sA[buf][h][off]);
+#pragma unroll
+                    for (int nb = 0; nb < NB; nb++) {
+                        const bf16x8 bf = __builtin_bit_cast(bf16x8, bq[s][nb]);
+                        acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bf, acc[mb][nb], 0, 0, 0);
+                    }
+                }
+            }
+        }
+    };
+
+    u32x4 bq0[4][NB], bq1[4][NB];
+    {
+        u32x4 ar[A_CHUNKS];
+        load_a(kb * kBK, ar);
+        if (wave_on) load_b(kb * kBK, bq0);
+        store_a(0, ar);
+    }
+    __syncthreads();
+    auto step = [&](int kt, const u32x4 (&cur)[4][NB], u32x4 (&nxt)[4][NB]) {
+        const bool more = kt + 1 < nk;
+        u32x4 ar[A_CHUNKS];
+        if (more) {
+            load_a((kb + kt + 1) * kBK, ar);
+            if (wave_on) load_b((kb + kt + 1) * kBK, nxt);
+        }
+        if (wave_on) compute(kt & 1, cur);
+        if (more) store_a((kt + 1) & 1, ar);
+        __syncthreads();
+    };
+    for (int kt = 0; kt < nk; kt += 2) {
+        step(kt, bq0, bq1);
+        if (kt + 1 < nk) step(kt + 1, bq1, bq0);
+    }
+    if (!wave_on) return;
+
+    // ---- epilogue
+#pragma unroll
+    for (int mb = 0; mb < kMB; mb++) {
+#pragma unroll
+        for (int r = 0; r < 16; r++) {
+            const int m = mb * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+            if (m >= nrows) continue;
+            const float sc = a.tok_scale ? a.tok_scale[s_tok[m]] : 1.0f;
+            float *orow = a.out + ks * a.slab + (size_t)(p0 + m) * a.ldo;
+            if constexpr (KIND == GK_GATEUP) {
+                const int i = colw + (lane & 31);
+                if (i < N) {
+                    float gv = acc[mb][0][r] * sc, uv = acc[mb][1][r] * sc;
+                    if (a.limit > 0.f) {
+                        gv = clampf(gv, a.limit);
+                        uv = clampf(uv, a.limit);
+                    }
+                    orow[i] = silu_mul(gv, uv);
+                }
+            } else {
+#pragma unroll
+                for (int nb = 0; nb < NB; nb++) {
+                    const int n = colw + nb * 32 + (lane & 31);
+                    if (n < N) orow[n] = acc[mb][nb][r] * sc;
+                }
+            }
+        }
+    }
+}
+
+static hipError_t run_gemm(int kind, bool a_f32, GemmArgs &a, hipStream_t s) {
+    const int cols = kind == GK_GATEUP ? GemmShape<GK_GATEUP>::COLS : GemmShape<GK_PLAIN>::COLS;
+    a.n_ntiles = (a.N + cols - 1) / cols;
+    if (a.ksplit < 1) a.ksplit = 1;
+    const long blocks = (long)a.max_tiles * a.n_ntiles * a.ksplit;
+    if (blocks == 0) return hipSuccess;
+    const unsigned grid = (unsigned)((blocks + 7) / 8 * 8);
+    if (kind == GK_GATEUP)
+        launch_kernel((k_gemm<GK_GATEUP, false>), dim3(grid), dim3(kGThreads), 0, s, a);
+    else if (a_f32)
+        launch_kernel((k_gemm<GK_PLAIN, true>), dim3(grid), dim3(kGThreads), 0, s, a);
+    else
+        launch_kernel((k_gemm<GK_PLAIN, false>), dim3(grid), dim3(kGThreads), 0, s, a);
+    return hipGetLastError();
+}
+
+bool mfma_supported(const Layer &L) {
+    return L.xdt == DT_BF16 && L.edt == DT_BF16 && (L.Is == 0 || L.sdt == DT_BF16) && L.H % kBK == 0 &&
+           L.I % kBK == 0 && L.Is % kBK == 0;
+}
+
+// Reduction slices of the routed down projection: enough workgroups to fill
+// the chip (about 512) when an M-token batch has few token tiles, keeping at
+// least 4 K steps per slice.  The slices' outputs are summed, in slice order,
+// by the combine.
+int down_ksplit(const Layer &L, int M) {
+    const long tiles = ((long)M * L.k + kBM - 1) / kBM;
+    const long ntiles = (L.H + GemmShape<GK_PLAIN>::COLS - 1) / GemmShape<GK_PLAIN>::COLS;
+    const int nk = L.I / kBK;
+    int S = 1;
+    while (tiles * ntiles * S < 512 && S < 4 && nk / (2 * S) >= 4) S *= 2;
+    return S;
+}
+
+hipError_t launch_gateup_mfma(const Layer &L, const void *x, const float *tok_scale, const Mats &routed,
+                              const Mats &shared, const Routing &rt, int M, int max_tiles,
+                              float *act, float *shared_act, hipStream_t s) {
+    if (act) {
+        GemmArgs a{};
+        a.a = x;
+        a.sorted = rt.sorted;
+        a.k_route = L.k;
+        a.tiles = rt.tiles;
+        a.offsets = rt.offsets;
+        a.E = L.E;
+        a.max_tiles = max_tiles;
+        a.b0 = static_cast<const uint16_t *>(routed.gate);
+        a.b1 = static_cast<const uint16_t *>(routed.up);
+        a.b_stride = (size_t)L.I * L.H;
+        a.N = L.I;
+        a.K = L.H;
+        a.tok_scale = tok_scale;
+        a.limit = L.limit;
+        a.out = act;
+        a.ldo = L.I;
+        hipError_t err = run_gemm(GK_GATEUP, false, a, s);
+        if (err != hipSuccess) return err;
+    }
+    if (shared_act && L.Is > 0) {
+        GemmArgs a{};
+        a.a = x;
+        a.M = M;
+        a.max_tiles = (M + kBM - 1) / kBM;
+        a.b0 = static_cast<const uint16_t *>(shared.gate);
+        a.b1 = static_cast<const uint16_t *>(shared.up);
+        a.N = L.Is;
+        a.K = L.H;
+        a.tok_scale = tok_scale;
+        a.limit = 0.f; // the shared expert is not clamped
+        a.out = shared_act;
+        a.ldo = L.Is;
+        return run_gemm(GK_GATEUP, false, a, s);
+    }
+    return hipSuccess;
+}
+
+hipError_t launch_down_mfma(const Layer &L, const float *act, const float *shared_act,
+                            const Mats &routed, const Mats &shared, const Routing &rt, int M,
+                            int max_tiles, float *y_routes, float *y_shared, hipStream_t s) {
+    if (act) {
+        GemmArgs a{};
+        a.a = act;
+        a.tiles = rt.tiles;
+        a.offsets = rt.offsets;
+        a.E = L.E;
+        a.max_tiles = max_tiles;
+        a.ksplit = down_ksplit(L, M);
+        a.slab = (size_t)M * L.k * L.H;
+        a.b0 = static_cast<const uint16_t *>(routed.down);
+        a.b_stride = (size_t)L.H * L.I;
+        a.N = L.H;
+        a.K = L.I;
+        a.out = y_routes;
+        a.ldo = L.H;
+        hipError_t err = run_gemm(GK_PLAIN, true, a, s);
+        if (err != hipSuccess) return err;
+    }
+    if (shared_act && L.Is > 0) {
+        GemmArgs a{};
+        a.a = shared_act;
+        a.M = M;
+        a.max_tiles = (M + kBM - 1) / kBM;
+        a.b0 = static_cast<const uint16_t *>(shared.down);
+        a.N = L.H;
+        a.K = L.Is;
+        a.out = y_shared;
+        a.ldo = L.H;
+        return run_gemm(GK_PLAIN, true, a, s);
+    }
+    return hipSuccess;
+}
+
+// ------------------------------------------------------------------ router
+// logits[t][e] = scale[t] * x[t] . router[e] for many tokens: one wave per
+// tile of 16 tokens x 16 experts, v_mfma_f32_16x16x32_bf16 over K, operands
+// loaded from global (L2) straight into registers, kRtUnroll steps ahead.
+typedef float f32x4m __attribute__((ext_vector_type(4)));
+constexpr int kRtUnroll = 4;
+
+__global__ __launch_bounds__(256) void k_router_mfma16(const uint16_t *x, const uint16_t *router,
+                                                       const float *tok_scale, int M, int E, int K,
+                                                       float *logits) {
+    const int lane = threadIdx.x & 63;
+    const int ntE = (E + 15) / 16;
+    const int gw = uniform(blockIdx.x * 4 + (threadIdx.x >> 6));
+    const int tm = gw / ntE, te = gw % ntE;
+    if (tm * 16 >= M) return;
+    const int t = min(tm * 16 + (lane & 15), M - 1);
+    const int e = min(te * 16 + (lane & 15), E - 1);
+    const uint16_t *arow = x + (size_t)t * K + 8 * (lane >> 4);
+    const uint16_t *brow = router + (size_t)e * K + 8 * (lane >> 4);
+    f32x4m acc = {0.f, 0.f, 0.f, 0.f};
+    for (int k0 = 0; k0 < K; k0 += 32 * kRtUnroll) {
+        u32x4 av[kRtUnroll], bv[kRtUnroll];
+#pragma unroll
+        for (int u = 0; u < kRtUnroll; u++) {
+            const int k = min(k0 + 32 * u, K - 32);
+            av[u] = *reinterpret_cast<const u32x4 *>(arow + k);
+            bv[u] = *reinterpret_cast<const u32x4 *>(brow + k);
+        }
+#pragma unroll
+        for (int u = 0; u < kRtUnroll; u++)
+            if (k0 + 32 * u < K)
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av[u]),
+                                                              __builtin_bit_cast(bf16x8, bv[u]), acc, 0, 0, 0);
+    }
+    const int col = te * 16 + (lane & 15);
+#pragma unroll
+    for (int r = 0; r < 4; r++) {
+        const int row = tm * 16 + 4 * (lane >> 4) + r;
+        if (row < M && col < E) logits[(size_t)row * E + col] = acc[r] * (tok_scale ? tok_scale[row] : 1.0f);
+    }
+}
+
+hipError_t launch_router_mfma(const Layer &L, const void *x, const void *router, const float *tok_scale,
+                              int M, float *logits, hipStream_t s) {
+    const int waves = ((M + 15) / 16) * ((L.E + 15) / 16);
+    launch_kernel(k_router_mfma16, dim3((waves + 3) / 4), dim3(256), 0, s,
+                       static_cast<const uint16_t *>(x), static_cast<const uint16_t *>(router), tok_scale, M,
+                       L.E, L.H, logits);
+    return hipGetLastError();
 }
 
 } // namespace moe

@@ -196,9 +196,9 @@ __global__ __launch_bounds__(kThreads) void k_gateup_gemv(GateUpArgs a) {
 template <int XDT, int WDT>
 static void gateup_dispatch(const GateUpArgs &a, int grid, int tb, size_t lds, hipStream_t s) {
     if (tb == 1)
-        hipLaunchKernelGGL((k_gateup_gemv<XDT, WDT, 1>), dim3(grid), dim3(kThreads), lds, s, a);
+        launch_kernel((k_gateup_gemv<XDT, WDT, 1>), dim3(grid), dim3(kThreads), lds, s, a);
     else
-        hipLaunchKernelGGL((k_gateup_gemv<XDT, WDT, 4>), dim3(grid), dim3(kThreads), lds, s, a);
+        launch_kernel((k_gateup_gemv<XDT, WDT, 4>), dim3(grid), dim3(kThreads), lds, s, a);
 }
 
 hipError_t launch_gateup_gemv(const Layer &L, const void *x, const float *tok_scale, const Mats &routed,
@@ -459,9 +459,9 @@ hipError_t launch_down_routes_gemv(const Layer &L, const float *act, const float
                                  y_routes, y_shared);
     const dim3 grid(a.seg_routed * a.tiles_H + (a.Is > 0 ? a.tiles_H : 0));
     if (grid.x == 0) return hipSuccess;
-    if (L.edt == DT_BF16) hipLaunchKernelGGL(k_down_routes_gemv<DT_BF16>, grid, dim3(kThreads), 0, s, a);
-    else if (L.edt == DT_Q8) hipLaunchKernelGGL(k_down_routes_gemv<DT_Q8>, grid, dim3(kThreads), 0, s, a);
-    else hipLaunchKernelGGL(k_down_routes_gemv<DT_F32>, grid, dim3(kThreads), 0, s, a);
+    if (L.edt == DT_BF16) launch_kernel(k_down_routes_gemv<DT_BF16>, grid, dim3(kThreads), 0, s, a);
+    else if (L.edt == DT_Q8) launch_kernel(k_down_routes_gemv<DT_Q8>, grid, dim3(kThreads), 0, s, a);
+    else launch_kernel(k_down_routes_gemv<DT_F32>, grid, dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }
 
@@ -477,9 +477,9 @@ hipError_t launch_down_gemv(const Layer &L, const float *act, const float *share
     }
     const DownArgs a = down_args(L, act, shared_act, routed, shared, rt, w, seed, M, y, y_routes, y_shared);
     const dim3 grid(a.tiles_H);
-    if (L.edt == DT_BF16) hipLaunchKernelGGL(k_down_combine_gemv<DT_BF16>, grid, dim3(kThreads), 0, s, a);
-    else if (L.edt == DT_Q8) hipLaunchKernelGGL(k_down_combine_gemv<DT_Q8>, grid, dim3(kThreads), 0, s, a);
-    else hipLaunchKernelGGL(k_down_combine_gemv<DT_F32>, grid, dim3(kThreads), 0, s, a);
+    if (L.edt == DT_BF16) launch_kernel(k_down_combine_gemv<DT_BF16>, grid, dim3(kThreads), 0, s, a);
+    else if (L.edt == DT_Q8) launch_kernel(k_down_combine_gemv<DT_Q8>, grid, dim3(kThreads), 0, s, a);
+    else launch_kernel(k_down_combine_gemv<DT_F32>, grid, dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }
 
@@ -788,7 +788,7 @@ static int m1_cpl(int H, int N) { return (H / N + kWave - 1) / kWave; }
 template <int XDT, int WDT, int RP>
 static bool m1_gateup_dispatch(int cpl, const M1GateUpArgs &a, int grid, hipStream_t s) {
 #define M1_CASE(C) \
-    case C: hipLaunchKernelGGL((k_gateup_m1<XDT, WDT, C, RP>), dim3(grid), dim3(kThreads), 0, s, a); return true;
+    case C: launch_kernel((k_gateup_m1<XDT, WDT, C, RP>), dim3(grid), dim3(kThreads), 0, s, a); return true;
     switch (cpl) {
         M1_CASE(1) M1_CASE(2) M1_CASE(3) M1_CASE(4) M1_CASE(5) M1_CASE(6) M1_CASE(8)
     default: return false;
@@ -866,17 +866,19 @@ hipError_t launch_down_m1(const Layer &L, const float *act, const float *shared_
     a.k = L.k;
     a.y = y;
     const dim3 grid((L.H + kM1Rows - 1) / kM1Rows);
-    if (L.edt == DT_BF16) hipLaunchKernelGGL(k_down_m1<DT_BF16>, grid, dim3(kThreads), 0, s, a);
-    else if (L.edt == DT_Q8) hipLaunchKernelGGL(k_down_m1<DT_Q8>, grid, dim3(kThreads), 0, s, a);
-    else hipLaunchKernelGGL(k_down_m1<DT_F32>, grid, dim3(kThreads), 0, s, a);
+    if (L.edt == DT_BF16) launch_kernel(k_down_m1<DT_BF16>, grid, dim3(kThreads), 0, s, a);
+    else if (L.edt == DT_Q8) launch_kernel(k_down_m1<DT_Q8>, grid, dim3(kThreads), 0, s, a);
+    else launch_kernel(k_down_m1<DT_F32>, grid, dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }
 
 // -------------------------------------------------------------------- combine
-// One thread per (token, 4 consecutive h); slots summed in order j = 0..k-1.
+// One thread per (token, 4 consecutive h); slots summed in order j = 0..k-1,
+// each slot's partial slices (a split reduction) summed in slice order first.
 __global__ __launch_bounds__(256) void k_combine(const float *y_routes, const float *y_shared,
                                                  const int32_t *route_pos, const float *w,
-                                                 const float *seed, int M, int H, int k, float *y) {
+                                                 const float *seed, int M, int H, int k, int S,
+                                                 size_t slab, float *y) {
     const int H4 = H / 4;
     const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
     if (idx >= (size_t)M * H4) return;
@@ -885,7 +887,9 @@ __global__ __launch_bounds__(256) void k_combine(const float *y_routes, const fl
     if (y_shared) acc += reinterpret_cast<const f32x4 *>(y_shared + (size_t)t * H)[c];
     for (int j = 0; j < k; j++) {
         const int r = t * k + j;
-        const f32x4 v = reinterpret_cast<const f32x4 *>(y_routes + (size_t)route_pos[r] * H)[c];
+        const float *row = y_routes + (size_t)route_pos[r] * H;
+        f32x4 v = reinterpret_cast<const f32x4 *>(row)[c];
+        for (int sl = 1; sl < S; sl++) v += reinterpret_cast<const f32x4 *>(row + sl * slab)[c];
         const float wt = w[r];
         acc.x = fmaf(wt, v.x, acc.x);
         acc.y = fmaf(wt, v.y, acc.y);
@@ -897,10 +901,10 @@ __global__ __launch_bounds__(256) void k_combine(const float *y_routes, const fl
 
 hipError_t launch_combine(const Layer &L, const float *y_routes, const float *y_shared,
                           const int32_t *route_pos, const float *w, const float *seed, int M,
-                          float *y, hipStream_t s) {
+                          float *y, hipStream_t s, int slices) {
     const size_t n = (size_t)M * (L.H / 4);
-    hipLaunchKernelGGL(k_combine, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, y_routes, y_shared,
-                       route_pos, w, seed, M, L.H, L.k, y);
+    launch_kernel(k_combine, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, y_routes, y_shared,
+                       route_pos, w, seed, M, L.H, L.k, slices, (size_t)M * L.k * L.H, y);
     return hipGetLastError();
 }
 

@@ -62,10 +62,13 @@ hipError_t launch_down_gemv(const Layer &L, const float *act, const float *share
 hipError_t launch_down_routes_gemv(const Layer &L, const float *act, const float *shared_act,
                                    const Mats &routed, const Mats &shared, const Routing &rt, int M,
                                    float *y_routes, float *y_shared, hipStream_t s);
-// y[t] = seed[t] + y_shared[t] + sum_j w[t][j] * y_routes[route_pos[t*k+j]]
+// y[t] = seed[t] + y_shared[t] + sum_j w[t][j] * sum_s y_routes[s][route_pos[t*k+j]]
+// (s over `slices` partial results of a split reduction, slab M*k*H apart).
 hipError_t launch_combine(const Layer &L, const float *y_routes, const float *y_shared,
                           const int32_t *route_pos, const float *w, const float *seed, int M,
-                          float *y, hipStream_t s);
+                          float *y, hipStream_t s, int slices = 1);
+// Reduction slices of the MFMA down projection for an M-token call.
+int down_ksplit(const Layer &L, int M);
 
 // M = 1 decode kernels (x shared by every touched expert).
 bool m1_supported(const Layer &L);
@@ -83,6 +86,9 @@ hipError_t launch_router_small(const Layer &L, const void *x, const void *router
 
 // MFMA grouped-GEMM path (bf16 x and experts).
 int mfma_tile_rows();
+bool mfma_supported(const Layer &L);
+hipError_t launch_router_mfma(const Layer &L, const void *x, const void *router, const float *tok_scale,
+                              int M, float *logits, hipStream_t s);
 hipError_t launch_gateup_mfma(const Layer &L, const void *x, const float *tok_scale, const Mats &routed,
                               const Mats &shared, const Routing &rt, int M, int max_tiles,
                               float *act, float *shared_act, hipStream_t s);

@@ -75,10 +75,10 @@ WsLayout layout(const moe_plan *p, int M) {
     w.active = take((size_t)(L.E + 1) * 4);
     const int tile_rows = moe::mfma_tile_rows();
     w.max_tiles = mfma ? (int)(R / tile_rows + (R < (size_t)L.E ? R : (size_t)L.E) + 1) : 0;
-    w.tiles = take(mfma ? (size_t)(1 + 2 * w.max_tiles) * 4 : 4 * 3);
+    w.tiles = take(mfma ? (size_t)(2 + L.E + 2 * w.max_tiles) * 4 : 4 * 3);
     w.act = take(R * L.I * 4);
     w.shared_act = take(L.Is > 0 ? (size_t)M * L.Is * 4 : 0);
-    w.y_routes = take(unfused ? R * L.H * 4 : 0);
+    w.y_routes = take(unfused ? (mfma ? moe::down_ksplit(L, M) : 1) * R * L.H * 4 : 0);
     w.y_shared = take(unfused && L.Is > 0 ? (size_t)M * L.H * 4 : 0);
     w.total = o;
     return w;
@@ -164,6 +164,13 @@ moe_status check_router(const moe_plan *p, const moe_weights *w, bool need_route
 
 } // namespace
 
+namespace moe {
+StageTimer &stage_timer() {
+    static thread_local StageTimer t;
+    return t;
+}
+} // namespace moe
+
 extern "C" {
 
 const char *moe_last_error(void) { return g_err.c_str(); }
@@ -201,14 +208,16 @@ moe_status moe_plan_create(const moe_config *c, moe_plan **out) {
         return fail(MOE_ERR_UNSUPPORTED, "the shared expert must use the routed experts' dtype");
     if ((long)c->max_tokens * c->top_k > (1L << 30))
         return fail(MOE_ERR_UNSUPPORTED, "max_tokens * top_k too large");
-    const bool mfma_ok = false; // the MFMA grouped GEMM is not enabled yet
+    const moe::Layer L{c->hidden, c->num_experts, c->top_k, c->expert_inter, c->shared_inter,
+                       c->select, c->bias_mode, c->swiglu_limit, c->rms_eps,
+                       c->x_dtype, c->router_dtype, c->expert_dtype, c->shared_dtype};
+    const bool mfma_ok = moe::mfma_supported(L);
     if (c->path == MOE_PATH_MFMA && !mfma_ok)
-        return fail(MOE_ERR_UNSUPPORTED, "the MFMA path needs bf16 x and bf16 experts");
+        return fail(MOE_ERR_UNSUPPORTED,
+                    "the MFMA path needs bf16 x and experts and hidden, expert_inter, shared_inter multiples of 64");
     moe_plan *p = new moe_plan;
     p->cfg = *c;
-    p->L = moe::Layer{c->hidden, c->num_experts, c->top_k, c->expert_inter, c->shared_inter,
-                      c->select, c->bias_mode, c->swiglu_limit, c->rms_eps,
-                      c->x_dtype, c->router_dtype, c->expert_dtype, c->shared_dtype};
+    p->L = L;
     p->mfma_capable = mfma_ok;
     *out = p;
     return MOE_OK;
@@ -326,7 +335,8 @@ moe_status moe_combine(const moe_plan *p, const float *act, const moe_weights *w
         float *yr = at<float>(ws, lay.y_routes);
         LAUNCH(moe::launch_down_mfma(L, act, nullptr, routed_mats(wts), none, rt, M, lay.max_tiles, yr, nullptr, s),
                "down (MFMA)");
-        LAUNCH(moe::launch_combine(L, yr, nullptr, route_pos, w, seed, M, y, s), "combine");
+        LAUNCH(moe::launch_combine(L, yr, nullptr, route_pos, w, seed, M, y, s, moe::down_ksplit(L, M)),
+               "combine");
     } else {
         LAUNCH(moe::launch_down_gemv(L, act, nullptr, routed_mats(wts), none, rt, w, seed, M, y,
                                      at<float>(ws, lay.y_routes), nullptr, s),
@@ -336,30 +346,37 @@ moe_status moe_combine(const moe_plan *p, const float *act, const moe_weights *w
 }
 
 // Records an event after each kernel when timing is asked for.
+// Per-stage timing for moe_forward_timed: events[2i] and events[2i+1] bracket
+// the kernels of the i-th stage that launched any (see moe::StageTimer).
 struct Recorder {
     hipEvent_t *events = nullptr;
     int max_events = 0, n = 0;
     int32_t *stages = nullptr;
-    hipStream_t s = nullptr;
-    moe_status begin() {
-        if (!events) return MOE_OK;
-        hipError_t e = hipEventRecord(events[0], s);
-        return e == hipSuccess ? MOE_OK : hip_fail(e, "event record");
+    ~Recorder() {
+        if (events) moe::stage_timer() = moe::StageTimer{};
     }
-    moe_status after(int stage) {
+    moe_status arm() {
         if (!events) return MOE_OK;
-        if (n + 1 >= max_events) return fail(MOE_ERR_INVALID, "too few timing events");
+        if (2 * n + 1 >= max_events) return fail(MOE_ERR_INVALID, "too few timing events");
+        moe::stage_timer() = moe::StageTimer{events[2 * n], events[2 * n + 1], 0};
+        return MOE_OK;
+    }
+    void after(int stage) {
+        if (!events) return;
+        moe::StageTimer &t = moe::stage_timer();
+        const bool launched = t.launches > 0;
+        t = moe::StageTimer{};
+        if (!launched) return;
         if (stages) stages[n] = stage;
-        hipError_t e = hipEventRecord(events[n + 1], s);
         n++;
-        return e == hipSuccess ? MOE_OK : hip_fail(e, "event record");
     }
 };
 
 #define STAGE(rec, expr, what, stage)               \
     do {                                            \
+        TRY((rec).arm());                           \
         LAUNCH(expr, what);                         \
-        TRY((rec).after(stage));                    \
+        (rec).after(stage);                         \
     } while (0)
 
 static moe_status forward_impl(const moe_plan *p, const void *x, const moe_weights *wts, int32_t M,
@@ -377,8 +394,6 @@ static moe_status forward_impl(const moe_plan *p, const void *x, const moe_weigh
     const moe::Layer &L = p->L;
     const WsLayout lay = layout(p, M);
     const int R = M * L.k;
-    rec.s = s;
-    TRY(rec.begin());
 
     float *sc = nullptr;
     if (L.eps > 0.f) {
@@ -404,7 +419,10 @@ static moe_status forward_impl(const moe_plan *p, const void *x, const moe_weigh
                                            sorted, rpos, active, at<uint32_t>(ws, lay.sync), s),
               "route", MOE_STAGE_ROUTER);
     } else {
-        STAGE(rec, moe::launch_router(L, x, wts->router, sc, M, lg, s), "router", MOE_STAGE_ROUTER);
+        if (mfma && L.rdt == moe::DT_BF16)
+            STAGE(rec, moe::launch_router_mfma(L, x, wts->router, sc, M, lg, s), "router (MFMA)", MOE_STAGE_ROUTER);
+        else
+            STAGE(rec, moe::launch_router(L, x, wts->router, sc, M, lg, s), "router", MOE_STAGE_ROUTER);
         STAGE(rec, moe::launch_topk(L, lg, wts->bias, M, ids, w, s), "top-k", MOE_STAGE_TOPK);
         STAGE(rec, moe::launch_permute(L.E, R, moe::mfma_tile_rows(), ids, counts, offsets, sorted, rpos,
                                        active, tiles, s),
@@ -422,7 +440,8 @@ static moe_status forward_impl(const moe_plan *p, const void *x, const moe_weigh
         STAGE(rec, moe::launch_down_mfma(L, act, sact, routed_mats(wts), shared_mats(wts), rt, M,
                                          lay.max_tiles, yr, ysh, s),
               "down (MFMA)", MOE_STAGE_DOWN);
-        STAGE(rec, moe::launch_combine(L, yr, ysh, rpos, w, nullptr, M, y, s), "combine", MOE_STAGE_COMBINE);
+        STAGE(rec, moe::launch_combine(L, yr, ysh, rpos, w, nullptr, M, y, s, moe::down_ksplit(L, M)), "combine",
+              MOE_STAGE_COMBINE);
     } else if (single) {
         STAGE(rec, moe::launch_gateup_m1(L, x, sc, routed_mats(wts), shared_mats(wts), lg, wts->bias, ids, w,
                                          counts_out, act, sact, s),
@@ -471,6 +490,14 @@ moe_status moe_forward_timed(const moe_plan *p, const void *x, const moe_weights
     return st;
 }
 
+int32_t moe_forward_path(const moe_plan *p, int32_t M) {
+    if (!p) return fail(MOE_ERR_INVALID, "plan is NULL"), -1;
+    if (M < 1 || M > p->cfg.max_tokens)
+        return fail(MOE_ERR_INVALID, "M = %d outside [1, %d]", M, p->cfg.max_tokens), -1;
+    if (use_mfma(p, M)) return MOE_RUN_MFMA;
+    return M == 1 && moe::m1_supported(p->L) ? MOE_RUN_SINGLE : MOE_RUN_GEMV;
+}
+
 moe_status moe_workspace_init(const moe_plan *p, void *ws, size_t ws_bytes, void *stream) {
     if (!p) return fail(MOE_ERR_INVALID, "plan is NULL");
     if (ws_bytes == 0) return MOE_OK;
@@ -512,7 +539,7 @@ __global__ __launch_bounds__(256) void k_q8_split(const uint16_t *blocks, int64_
 hipError_t launch_q8_split(const void *blocks, int64_t rows, int cols, int8_t *qs, uint16_t *scales,
                            hipStream_t s) {
     const int64_t nb = rows * (cols / 32);
-    hipLaunchKernelGGL(k_q8_split, dim3((unsigned)((nb + 255) / 256)), dim3(256), 0, s,
+    launch_kernel(k_q8_split, dim3((unsigned)((nb + 255) / 256)), dim3(256), 0, s,
                        reinterpret_cast<const uint16_t *>(blocks), nb, qs, scales);
     return hipGetLastError();
 }

@@ -49,9 +49,9 @@ __global__ __launch_bounds__(256) void k_rms_scale(const void *x, int M, int H, 
 hipError_t launch_rms_scale(const Layer &L, const void *x, int M, float *scale, hipStream_t s) {
     dim3 grid((M + 3) / 4);
     if (L.xdt == DT_BF16)
-        hipLaunchKernelGGL(k_rms_scale<DT_BF16>, grid, dim3(256), 0, s, x, M, L.H, L.eps, scale);
+        launch_kernel(k_rms_scale<DT_BF16>, grid, dim3(256), 0, s, x, M, L.H, L.eps, scale);
     else
-        hipLaunchKernelGGL(k_rms_scale<DT_F32>, grid, dim3(256), 0, s, x, M, L.H, L.eps, scale);
+        launch_kernel(k_rms_scale<DT_F32>, grid, dim3(256), 0, s, x, M, L.H, L.eps, scale);
     return hipGetLastError();
 }
 
@@ -130,13 +130,13 @@ hipError_t launch_router(const Layer &L, const void *x, const void *router, cons
                          int M, float *logits, hipStream_t s) {
     dim3 grid(L.E, (M + kRouterTM - 1) / kRouterTM);
     if (L.xdt == DT_BF16 && L.rdt == DT_BF16)
-        hipLaunchKernelGGL((k_router_gemv<DT_BF16, DT_BF16>), grid, dim3(64), 0, s, x, router, tok_scale, M, L.H, L.E, logits);
+        launch_kernel((k_router_gemv<DT_BF16, DT_BF16>), grid, dim3(64), 0, s, x, router, tok_scale, M, L.H, L.E, logits);
     else if (L.xdt == DT_BF16)
-        hipLaunchKernelGGL((k_router_gemv<DT_BF16, DT_F32>), grid, dim3(64), 0, s, x, router, tok_scale, M, L.H, L.E, logits);
+        launch_kernel((k_router_gemv<DT_BF16, DT_F32>), grid, dim3(64), 0, s, x, router, tok_scale, M, L.H, L.E, logits);
     else if (L.rdt == DT_BF16)
-        hipLaunchKernelGGL((k_router_gemv<DT_F32, DT_BF16>), grid, dim3(64), 0, s, x, router, tok_scale, M, L.H, L.E, logits);
+        launch_kernel((k_router_gemv<DT_F32, DT_BF16>), grid, dim3(64), 0, s, x, router, tok_scale, M, L.H, L.E, logits);
     else
-        hipLaunchKernelGGL((k_router_gemv<DT_F32, DT_F32>), grid, dim3(64), 0, s, x, router, tok_scale, M, L.H, L.E, logits);
+        launch_kernel((k_router_gemv<DT_F32, DT_F32>), grid, dim3(64), 0, s, x, router, tok_scale, M, L.H, L.E, logits);
     return hipGetLastError();
 }
 
@@ -170,7 +170,7 @@ __global__ __launch_bounds__(256) void k_topk(const float *logits, const float *
 
 hipError_t launch_topk(const Layer &L, const float *logits, const float *bias, int M, int32_t *ids,
                        float *w, hipStream_t s) {
-    hipLaunchKernelGGL(k_topk, dim3((M + 3) / 4), dim3(256), 0, s, logits, L.bias_mode ? bias : nullptr,
+    launch_kernel(k_topk, dim3((M + 3) / 4), dim3(256), 0, s, logits, L.bias_mode ? bias : nullptr,
                        M, L.E, L.k, L.select, L.bias_mode, ids, w);
     return hipGetLastError();
 }
@@ -221,6 +221,11 @@ __device__ int block_scan_256(int v, int *lds /*[>= 4]*/, int *total) {
     return tid < 256 ? x + before - v : 0;
 }
 
+// Touched-expert list and GEMM tile list.  Tile list layout (E experts):
+//   tiles[0]           number of tiles T
+//   tiles[1 + e]       first tile of expert e (e = 0..E; tiles[1 + E] = T)
+//   tiles[2 + E + 2i]  expert of tile i;  tiles[3 + E + 2i]  its first sorted row
+// An expert's tiles are consecutive, tile_rows rows each (the last ragged).
 __device__ void write_plan(int E, int tile_rows, const int *cnt, const int *off, int *scan_lds,
                            int32_t *active, int32_t *tiles) {
     const int tid = threadIdx.x;
@@ -233,12 +238,18 @@ __device__ void write_plan(int E, int tile_rows, const int *cnt, const int *off,
         int n_tiles;
         const int nt = (c + tile_rows - 1) / tile_rows;
         const int ti = block_scan_256(nt, scan_lds, &n_tiles);
-        if (tid < E)
+        int32_t *pairs = tiles + 2 + E;
+        if (tid < E) {
+            tiles[1 + tid] = ti;
             for (int j = 0; j < nt; j++) {
-                tiles[1 + 2 * (ti + j)] = tid;
-                tiles[2 + 2 * (ti + j)] = off[tid] + j * tile_rows;
+                pairs[2 * (ti + j)] = tid;
+                pairs[2 * (ti + j) + 1] = off[tid] + j * tile_rows;
             }
-        if (tid == 0) tiles[0] = n_tiles;
+        }
+        if (tid == 0) {
+            tiles[0] = n_tiles;
+            tiles[1 + E] = n_tiles;
+        }
     }
 }
 
@@ -330,13 +341,13 @@ hipError_t launch_permute(int E, int R, int tile_rows, const int32_t *ids, int32
                           int32_t *offsets, int32_t *sorted, int32_t *route_pos, int32_t *active,
                           int32_t *tiles, hipStream_t s) {
     PermuteOut o{counts, offsets, sorted, route_pos, active, tiles, tile_rows};
-    hipLaunchKernelGGL(k_permute, dim3(1), dim3(kPermWaves * kWave), 0, s, ids, R, E, o);
+    launch_kernel(k_permute, dim3(1), dim3(kPermWaves * kWave), 0, s, ids, R, E, o);
     return hipGetLastError();
 }
 
 hipError_t launch_plan_from_offsets(int E, int tile_rows, const int32_t *offsets, int32_t *active,
                                     int32_t *tiles, hipStream_t s) {
-    hipLaunchKernelGGL(k_plan_from_offsets, dim3(1), dim3(256), 0, s, E, tile_rows, offsets, active,
+    launch_kernel(k_plan_from_offsets, dim3(1), dim3(256), 0, s, E, tile_rows, offsets, active,
                        tiles);
     return hipGetLastError();
 }
@@ -469,13 +480,13 @@ template <bool TAIL>
 static void route_small_dispatch(const Layer &L, const RouteSmallArgs &a, hipStream_t s) {
     const dim3 grid(L.E), block(kRouteWaves * kWave);
     if (L.xdt == DT_BF16 && L.rdt == DT_BF16)
-        hipLaunchKernelGGL((k_route_small<DT_BF16, DT_BF16, TAIL>), grid, block, 0, s, a);
+        launch_kernel((k_route_small<DT_BF16, DT_BF16, TAIL>), grid, block, 0, s, a);
     else if (L.xdt == DT_BF16)
-        hipLaunchKernelGGL((k_route_small<DT_BF16, DT_F32, TAIL>), grid, block, 0, s, a);
+        launch_kernel((k_route_small<DT_BF16, DT_F32, TAIL>), grid, block, 0, s, a);
     else if (L.rdt == DT_BF16)
-        hipLaunchKernelGGL((k_route_small<DT_F32, DT_BF16, TAIL>), grid, block, 0, s, a);
+        launch_kernel((k_route_small<DT_F32, DT_BF16, TAIL>), grid, block, 0, s, a);
     else
-        hipLaunchKernelGGL((k_route_small<DT_F32, DT_F32, TAIL>), grid, block, 0, s, a);
+        launch_kernel((k_route_small<DT_F32, DT_F32, TAIL>), grid, block, 0, s, a);
 }
 
 hipError_t launch_route_small(const Layer &L, const void *x, const void *router, const float *bias,
@@ -506,7 +517,7 @@ __global__ void k_zero_words(uint32_t *p, int n) {
 }
 
 hipError_t launch_zero_words(uint32_t *p, int n, hipStream_t s) {
-    hipLaunchKernelGGL(k_zero_words, dim3((n + 255) / 256), dim3(256), 0, s, p, n);
+    launch_kernel(k_zero_words, dim3((n + 255) / 256), dim3(256), 0, s, p, n);
     return hipGetLastError();
 }
 

@@ -142,3 +142,28 @@ def test_call_refusals_before_any_launch():
     assert L.moe_q8_0_split(FAKE, 4, 33, FAKE, FAKE, None) == m.MOE_ERR_INVALID
     assert L.moe_q8_0_split(FAKE, -1, 32, FAKE, FAKE, None) == m.MOE_ERR_INVALID
     assert L.moe_q8_0_split(None, 0, 32, None, None, None) == m.MOE_OK
+
+
+def test_forward_path_choice():
+    import synth
+    want = {("gpt-oss-20b", 1): "single", ("gpt-oss-20b", 16): "gemv",
+            ("mixtral-8x7b", 1): "single", ("mixtral-8x7b", 512): "mfma",
+            ("qwen3-30b-a3b", 2048): "mfma", ("deepseek-v2-lite", 16): "gemv"}
+    for (name, M), run in want.items():
+        spec = synth.SPECS[name]
+        p = m.moe_plan_create(spec.hidden, spec.num_experts, spec.top_k, spec.expert_inter,
+                              spec.shared_inter, max(spec.token_counts), spec.select,
+                              spec.bias_mode, spec.swiglu_limit, spec.rms_eps, spec.x_dtype,
+                              spec.router_dtype, spec.expert_dtype, spec.shared_dtype)
+        assert m.MOE_RUN_NAMES[m.moe_forward_path(p, M)] == run, (name, M)
+        with pytest.raises(m.MoeError):
+            m.moe_forward_path(p, 0)
+        with pytest.raises(m.MoeError):
+            m.moe_forward_path(p, max(spec.token_counts) + 1)
+    mix = synth.SPECS["mixtral-8x7b"]
+    forced = m.moe_plan_create(mix.hidden, mix.num_experts, mix.top_k, mix.expert_inter, 0, 512,
+                               mix.select, mix.bias_mode, mix.swiglu_limit, mix.rms_eps,
+                               mix.x_dtype, mix.router_dtype, mix.expert_dtype, mix.shared_dtype,
+                               path=m.MOE_PATH_GEMV)
+    assert m.moe_forward_path(forced, 512) == 1
+    assert m.lib().moe_forward_path(None, 1) == -1

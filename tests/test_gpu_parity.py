@@ -194,6 +194,67 @@ def test_forward_small(name, kw, Ms):
         forward_parity(spec, layer, x, dl, what=f"{name} M={M}")
 
 
+MFMA_SMALL = [
+    ("k2", dict(hidden=256, num_experts=8, top_k=2, expert_inter=192), (64, 70, 200)),
+    ("bias-clamp", dict(hidden=128, num_experts=6, top_k=3, expert_inter=128, bias_mode=BIAS_LOGIT,
+                        bias_kind="normal", swiglu_limit=0.3), (65, 130)),
+    ("all-shared", dict(hidden=192, num_experts=16, top_k=6, expert_inter=64, shared_inter=320,
+                        select=SOFTMAX_ALL_NORENORM), (3, 100)),
+    ("zipf-rms", dict(hidden=256, num_experts=64, top_k=8, expert_inter=128, bias_mode=BIAS_LOGIT,
+                      bias_kind="zipf", rms_eps=1e-6), (1, 257)),
+    ("wide-n", dict(hidden=128, num_experts=4, top_k=1, expert_inter=576), (129,)),
+]
+
+
+@pytest.mark.parametrize("name,kw,Ms", MFMA_SMALL, ids=[c[0] for c in MFMA_SMALL])
+def test_forward_mfma_small(name, kw, Ms):
+    """The MFMA grouped-GEMM path (forced), at sizes spanning several tiles with
+    ragged row and column tails, against the oracle."""
+    import mixture_experts_gemv_amd as m
+    spec = synth.small_spec(name=name, seed=1300 + len(name), **kw)
+    layer = synth.make_layer(spec)
+    dl = device_layer(spec, layer, max(Ms), path=m.MOE_PATH_MFMA)
+    for M in Ms:
+        x = synth.make_tokens(spec, M, batch=5)
+        say(f"forward (MFMA) {name} M={M}")
+        forward_parity(spec, layer, x, dl, what=f"mfma {name} M={M}")
+
+
+def test_stages_mfma():
+    """moe_expert_ffn and moe_combine on the MFMA path equal the oracle."""
+    import mixture_experts_gemv_amd as m
+    spec = synth.small_spec(hidden=256, num_experts=8, top_k=2, expert_inter=320,
+                            bias_mode=BIAS_LOGIT, bias_kind="normal", swiglu_limit=1.0, seed=1350)
+    layer = synth.make_layer(spec)
+    M = 150
+    x = synth.make_tokens(spec, M)
+    say("stage chain (MFMA)")
+    dl = device_layer(spec, layer, M, path=m.MOE_PATH_MFMA)
+    xt = dl.x_tensor(x)
+    ws = dl.workspace(M)
+    E, k, H, I = spec.num_experts, spec.top_k, spec.hidden, spec.expert_inter
+    ids = torch.empty(M, k, dtype=torch.int32, device="cuda")
+    w = torch.empty(M, k, dtype=torch.float32, device="cuda")
+    m.moe_route(dl.plan, xt, dl.weights, M, None, 0, ids, w, ws)
+    counts = torch.empty(E, dtype=torch.int32, device="cuda")
+    offsets = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    sr = torch.empty(M * k, dtype=torch.int32, device="cuda")
+    rp = torch.empty(M * k, dtype=torch.int32, device="cuda")
+    m.moe_permute(dl.plan, ids, M, counts, offsets, sr, rp, ws)
+    act = torch.empty(M * k, I, dtype=torch.float32, device="cuda")
+    m.moe_expert_ffn(dl.plan, xt, dl.weights, M, offsets, sr, act, ws)
+    y = torch.empty(M, H, dtype=torch.float32, device="cuda")
+    m.moe_combine(dl.plan, act, dl.weights, M, offsets, sr, rp, w, None, y, ws)
+    torch.cuda.synchronize()
+    o = oracle.forward(spec, layer, x, want_act=True)
+    forced, near = check_ids(spec, layer, x, ids.cpu().numpy(), o["ids"])
+    o = oracle.forward(spec, layer, x, forced_ids=forced, want_act=True)
+    a = act.cpu().numpy()[rp.cpu().numpy()]
+    rel = np.linalg.norm(a - o["act"]) / np.linalg.norm(o["act"])
+    assert rel <= 5e-3, f"act rel-L2 {rel:.3e}"
+    check_y(y.cpu().numpy(), o["y"], "stage chain (MFMA)")
+
+
 def test_workspace_reuse_across_calls():
     """One workspace, many calls of different M: the ticket words come back to
     zero after every call, so each result equals a fresh-workspace result."""
@@ -222,6 +283,45 @@ def test_forward_repeatable():
     a = dl.forward(x).cpu().numpy()
     b = dl.forward(x).cpu().numpy()
     assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("M,path,want", [
+    (1, 0, ["router", "gateup", "down"]),
+    (9, 0, ["router", "gateup", "down"]),
+    (128, 2, ["router", "topk", "permute", "gateup", "down", "combine"]),
+])
+def test_forward_timed_matches_forward(M, path, want):
+    """moe_forward_timed launches the same kernels (bitwise-equal y), brackets
+    each stage with a positive event interval, and leaves later untimed calls
+    unaffected."""
+    import mixture_experts_gemv_amd as m
+    from mixture_experts_gemv_amd.events import HipEvents
+    spec = synth.small_spec(hidden=256, num_experts=16, top_k=4, expert_inter=192,
+                            bias_mode=BIAS_LOGIT, bias_kind="normal", seed=1230)
+    layer = synth.make_layer(spec)
+    dl = device_layer(spec, layer, M, path=path)
+    x = dl.x_tensor(synth.make_tokens(spec, M))
+    ws = dl.workspace(M)
+    say(f"timed forward M={M} path={path}")
+    ref = dl.forward(x, ws=ws).cpu().numpy()
+    y = torch.empty(M, spec.hidden, dtype=torch.float32, device="cuda:0")
+    ev = HipEvents(16)
+    try:
+        st = m.moe_forward_timed(dl.plan, x, dl.weights, M, y, None, None, None, ws, ev.ev)
+        torch.cuda.synchronize()
+        assert [m.MOE_STAGE_NAMES[i] for i in st] == want
+        for j in range(len(st)):
+            assert ev.elapsed_ms(2 * j, 2 * j + 1) > 0.0
+            if j:
+                assert ev.elapsed_ms(2 * j - 1, 2 * j) >= 0.0
+        assert np.array_equal(y.cpu().numpy(), ref)
+        with pytest.raises(m.MoeError):
+            m.moe_forward_timed(dl.plan, x, dl.weights, M, y, None, None, None, ws, ev.ev[:3])
+        torch.cuda.synchronize()
+    finally:
+        ev.close()
+    after = dl.forward(x, ws=ws).cpu().numpy()
+    assert np.array_equal(after, ref)
 
 
 # ------------------------------------------------------------ full-size layers
