@@ -58,11 +58,6 @@ struct GemmArgs {
     int n_ntiles;            // column tiles
 };
 
-__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
-    const uint32_t u = __float_as_uint(f);
-    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-}
-
 template <int KIND>
 struct GemmShape {
     static constexpr int NB = 2;                                  // 32-column B blocks per wave

@@ -1,16 +1,27 @@
 // Bandwidth-bound GEMV path of the routed MoE layer (decode and small batches).
 //
-// gate/up: one workgroup per (touched expert, tile of kPairsPerWG rows of I).
-//   The tokens routed to the expert are staged in LDS as fp32, kTB at a time;
-//   each wave streams kRowPairs gate rows and the matching up rows with 16-byte
-//   loads, dequantising in registers (bf16 -> fp32, Q8_0 q * block scale), and
-//   writes act = silu(clamp(g)) * clamp(v) for every staged token.
-// down:    one workgroup per tile of rows of H.  For M <= 64 each wave owns kRH
-//   output rows and loops over every touched expert in ascending id (then the
-//   shared expert), so every y element is summed by one wave in a fixed order:
-//   no atomics, bitwise-repeatable.  Lane t accumulates token t.
-//   For M > 64 the per-route results go to y_routes and a combine kernel sums
-//   them in slot order.
+// After routing and permutation, every touched expert's weight rows are
+// streamed from HBM once and dotted with the vectors routed to that expert.
+//
+// gate/up: a workgroup owns one tile of kRowsTileGU rows of one touched expert
+//   (or of the shared expert).  The x rows of the expert's tokens are copied
+//   into LDS as stored (bf16 or fp32).  Each wave streams its kRowsPerWaveGU
+//   rows RP at a time, issuing every 16-byte load of a group (gate and up)
+//   before using any, and dots each row with every staged token (kTV tokens
+//   per pass over the loaded rows).  With bf16 x
+//   and bf16 or Q8_0 weights the products run on v_dot2c_f32_bf16: bf16
+//   weights are used as loaded, Q8_0 int8 values convert to bf16 exactly, and
+//   the fp16 block scale multiplies each chunk's dot.  The per-token pre-norm
+//   scale multiplies the finished dot.  Epilogue: clamp (routed experts only),
+//   silu(g) * v -> act.
+// down: a workgroup owns (touched expert, tile of kRowsTileDN rows of H, slice of
+//   the reduction over I).  The slice of the expert's act rows is copied into
+//   LDS (fp32), each wave streams its rows RP at a time (every load of a group
+//   issued first), and each row's dots are written to y_routes[slice][route][h]
+//   (y_shared[slice][token][h] for the shared expert); the combine kernel sums
+//   slices and routes in a fixed order, so results are bitwise repeatable.
+// Vectors beyond what LDS holds are taken in further passes over the tile.
+// One token (M = 1) has its own kernels further down.
 #include "common.h"
 #include "launch.h"
 #include "topk.h"
@@ -19,192 +30,332 @@ namespace moe {
 
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * kWave;
-constexpr int kRowPairs = 2;                         // gate/up row pairs per wave pass
-constexpr int kPairsPerWave = 4;
-constexpr int kPairsPerWG = kWaves * kPairsPerWave;  // rows of I per workgroup
+// Rows per wave of one workgroup tile (measured: smaller gate/up tiles, i.e.
+// more workgroups, stream faster; the down tiles prefer 16 rows per wave).
+constexpr int kRowsPerWaveGU = 8;
+constexpr int kRowsTileGU = kWaves * kRowsPerWaveGU;
+constexpr int kRowsPerWaveDN = 16;
+constexpr int kRowsTileDN = kWaves * kRowsPerWaveDN;
+constexpr int kTV = 4;                   // vectors dotted per pass over loaded rows
+constexpr int kStageMax = 8;             // vectors one LDS stage holds, at most
+constexpr int kStageBytes = 64 * 1024;   // LDS for staged vectors, per workgroup
+constexpr int kSliceMax = 2048;          // reduction elements per down slice
 
-struct GateUpArgs {
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c,
+                                           false);
+}
+
+// The 16 int8 of a Q8_0 chunk as 8 words of bf16 pairs (exact: |q| <= 127).
+__device__ __forceinline__ void q8_to_bf16x2(u32x4 v, uint32_t (&o)[8]) {
+    const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const uint32_t f0 = __float_as_uint(i8_to_f32<0>(d[i])), f1 = __float_as_uint(i8_to_f32<1>(d[i]));
+        const uint32_t f2 = __float_as_uint(i8_to_f32<2>(d[i])), f3 = __float_as_uint(i8_to_f32<3>(d[i]));
+        o[2 * i] = __builtin_amdgcn_perm(f1, f0, 0x07060302u);
+        o[2 * i + 1] = __builtin_amdgcn_perm(f3, f2, 0x07060302u);
+    }
+}
+
+// ------------------------------------------------------------------ gate/up
+struct RowsGateUp {
     const void *x;
     const float *tok_scale;
     Mats routed, shared;
     const int32_t *offsets, *sorted, *active;
     int M, H, k, I, Is;
-    int seg_routed;  // workgroup slots for routed experts (>= touched experts)
-    int tiles_I, tiles_Is;
+    int max_routed;           // routed expert slots in the grid (>= touched experts)
+    int tiles_I, tiles_Is;    // row tiles per routed / shared expert
+    int ncap;                 // token rows one LDS stage holds
     float limit;
     float *act, *shared_act;
 };
 
-template <int XDT>
-__device__ __forceinline__ void stage_token(const void *x, int t, int H, float *dst, float scale) {
-    if constexpr (XDT == DT_BF16) {
-        const u32x4 *src = reinterpret_cast<const u32x4 *>(reinterpret_cast<const uint16_t *>(x) + (size_t)t * H);
-        for (int c = threadIdx.x; c < H / 8; c += kThreads) {
-            u32x4 q = src[c];
-            f32x4 a = {bf16_lo(q.x), bf16_hi(q.x), bf16_lo(q.y), bf16_hi(q.y)};
-            f32x4 b = {bf16_lo(q.z), bf16_hi(q.z), bf16_lo(q.w), bf16_hi(q.w)};
-            reinterpret_cast<f32x4 *>(dst)[2 * c] = a * scale;
-            reinterpret_cast<f32x4 *>(dst)[2 * c + 1] = b * scale;
-        }
-    } else {
-        const f32x4 *src = reinterpret_cast<const f32x4 *>(reinterpret_cast<const float *>(x) + (size_t)t * H);
-        for (int c = threadIdx.x; c < H / 4; c += kThreads) reinterpret_cast<f32x4 *>(dst)[c] = src[c] * scale;
-    }
-}
+// The loads of one row group: RP rows of gate and of up, CPL chunks per lane.
+template <int WDT, int CPL, int RP>
+struct GateUpLoads {
+    u32x4 g[RP][CPL], u[RP][CPL];
+    uint16_t hg[RP][CPL], hu[RP][CPL];
+};
 
-template <int XDT, int WDT, int TB>
-__global__ __launch_bounds__(kThreads) void k_gateup_gemv(GateUpArgs a) {
-    extern __shared__ float xs[]; // [TB][H]
+template <int XDT, int WDT, int CPL, int RP>
+__global__ __launch_bounds__(kThreads) void k_gateup_rows(RowsGateUp a) {
+    extern __shared__ __attribute__((aligned(16))) unsigned char s_x[]; // [ncap][H] as stored
     constexpr int N = Chunk<WDT>::N;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    constexpr int NG = kRowsPerWaveGU / RP;
+    constexpr bool DOT2 = XDT == DT_BF16 && WDT != DT_F32;
+    constexpr int XB = XDT == DT_BF16 ? 2 : 4;
+    constexpr int NW = N / 2; // bf16 pair words per chunk (dot2 form)
+    using Loads = GateUpLoads<WDT, CPL, RP>;
+    const int tid = threadIdx.x, lane = tid & 63, wave = uniform(tid >> 6);
     const int H = a.H;
 
-    // ---- which rows of which expert this workgroup owns
-    int b = blockIdx.x;
-    const void *gbase, *ubase;
-    const uint16_t *gsb = nullptr, *usb = nullptr;
-    int width, row0, ntok, p0 = 0;
-    bool is_shared;
-    if (b < a.seg_routed * a.tiles_I) {
+    // ---- segment (touched expert or shared expert) and row tile
+    int b = blockIdx.x, width, p0 = 0, n, rt;
+    bool shared;
+    size_t mrow0;
+    if (b < a.max_routed * a.tiles_I) {
         const int u = b / a.tiles_I;
         if (u >= a.active[0]) return;
         const int e = a.active[1 + u];
+        rt = b - u * a.tiles_I;
         width = a.I;
-        row0 = (b % a.tiles_I) * kPairsPerWG;
         p0 = a.offsets[e];
-        ntok = a.offsets[e + 1] - p0;
-        const size_t mat = (size_t)e * a.I * H;
-        gbase = reinterpret_cast<const char *>(a.routed.gate) + mat * elem_bytes<WDT>();
-        ubase = reinterpret_cast<const char *>(a.routed.up) + mat * elem_bytes<WDT>();
-        if constexpr (WDT == DT_Q8) {
-            gsb = a.routed.gate_s + mat / 32;
-            usb = a.routed.up_s + mat / 32;
-        }
-        is_shared = false;
+        n = a.offsets[e + 1] - p0;
+        shared = false;
+        mrow0 = (size_t)e * a.I;
     } else {
-        b -= a.seg_routed * a.tiles_I;
+        rt = b - a.max_routed * a.tiles_I;
+        if (rt >= a.tiles_Is) return;
         width = a.Is;
-        row0 = b * kPairsPerWG;
-        ntok = a.M;
-        gbase = a.shared.gate;
-        ubase = a.shared.up;
-        if constexpr (WDT == DT_Q8) {
-            gsb = a.shared.gate_s;
-            usb = a.shared.up_s;
-        }
-        is_shared = true;
+        n = a.M;
+        shared = true;
+        mrow0 = 0;
     }
-    const size_t row_bytes = (size_t)H * elem_bytes<WDT>();
+    const Mats &m = shared ? a.shared : a.routed;
+    const size_t rbytes = (size_t)H * elem_bytes<WDT>();
+    const char *gbase = reinterpret_cast<const char *>(m.gate) + mrow0 * rbytes;
+    const char *ubase = reinterpret_cast<const char *>(m.up) + mrow0 * rbytes;
+    const uint16_t *gsb = nullptr, *usb = nullptr;
+    if constexpr (WDT == DT_Q8) {
+        gsb = m.gate_s + mrow0 * (H / 32);
+        usb = m.up_s + mrow0 * (H / 32);
+    }
+    const int row_w = rt * kRowsTileGU + wave * kRowsPerWaveGU; // this wave's first row
+    const int nch = H / N;
+    const int ncb = (nch + kWave * CPL - 1) / (kWave * CPL); // chunk blocks per row
+    const int ng = row_w < width ? min(NG, (width - row_w) / RP) : 0;
+    const int nsteps = ng * ncb; // (row group, chunk block) steps of this wave
+    const int cpr = H * XB / 16; // 16-byte pieces per staged row
 
-    for (int tok0 = 0; tok0 < ntok; tok0 += TB) {
-        __syncthreads();
+    auto chunks = [&](int cb, int (&cl)[CPL], bool (&ok)[CPL]) {
 #pragma unroll
-        for (int tb = 0; tb < TB; tb++) {
-            if (tok0 + tb < ntok) {
-                const int t = is_shared ? tok0 + tb : a.sorted[p0 + tok0 + tb] / a.k;
-                const float sc = a.tok_scale ? a.tok_scale[t] : 1.0f;
-                stage_token<XDT>(a.x, t, H, xs + tb * H, sc);
-            } else {
-                for (int c = threadIdx.x; c < H; c += kThreads) xs[tb * H + c] = 0.f;
+        for (int cc = 0; cc < CPL; cc++) {
+            const int c = cb * kWave * CPL + lane + kWave * cc;
+            ok[cc] = c < nch;
+            cl[cc] = min(c, nch - 1);
+        }
+    };
+    auto load = [&](Loads &B, int st) {
+        const int g = st / ncb, cb = st - g * ncb;
+        const int i0 = row_w + g * RP;
+        int cl[CPL];
+        bool ok[CPL];
+        chunks(cb, cl, ok);
+#pragma unroll
+        for (int r = 0; r < RP; r++)
+#pragma unroll
+            for (int cc = 0; cc < CPL; cc++) {
+                B.g[r][cc] = load_raw(gbase + (size_t)(i0 + r) * rbytes, cl[cc]);
+                B.u[r][cc] = load_raw(ubase + (size_t)(i0 + r) * rbytes, cl[cc]);
+                if constexpr (WDT == DT_Q8) {
+                    B.hg[r][cc] = gsb[(size_t)(i0 + r) * (H / 32) + (cl[cc] >> 1)];
+                    B.hu[r][cc] = usb[(size_t)(i0 + r) * (H / 32) + (cl[cc] >> 1)];
+                }
+            }
+    };
+
+    float ag[RP][kTV], au[RP][kTV];
+    // dots of the loaded chunks with staged tokens j0..j0+nj-1
+    auto dots = [&](const Loads &B, int cb, int j0, int nj) {
+        int cl[CPL];
+        bool ok[CPL];
+        chunks(cb, cl, ok);
+#pragma unroll
+        for (int cc = 0; cc < CPL; cc++) {
+#pragma unroll
+            for (int r = 0; r < RP; r++) {
+                if constexpr (DOT2) {
+                    uint32_t wg[NW], wu[NW];
+                    if constexpr (WDT == DT_Q8) {
+                        q8_to_bf16x2(B.g[r][cc], wg);
+                        q8_to_bf16x2(B.u[r][cc], wu);
+                    } else {
+                        wg[0] = B.g[r][cc].x; wg[1] = B.g[r][cc].y; wg[2] = B.g[r][cc].z; wg[3] = B.g[r][cc].w;
+                        wu[0] = B.u[r][cc].x; wu[1] = B.u[r][cc].y; wu[2] = B.u[r][cc].z; wu[3] = B.u[r][cc].w;
+                    }
+                    const float scg = WDT == DT_Q8 ? f16_bits_to_f32(B.hg[r][cc]) : 1.f;
+                    const float scu = WDT == DT_Q8 ? f16_bits_to_f32(B.hu[r][cc]) : 1.f;
+#pragma unroll
+                    for (int j = 0; j < kTV; j++) {
+                        if (j < nj) {
+                            const u32x4 *xp = reinterpret_cast<const u32x4 *>(
+                                s_x + ((size_t)(j0 + j) * H + (size_t)cl[cc] * N) * 2);
+                            uint32_t xw[NW];
+#pragma unroll
+                            for (int q4 = 0; q4 < NW / 4; q4++) {
+                                const u32x4 v = xp[q4];
+                                xw[4 * q4] = ok[cc] ? v.x : 0u;
+                                xw[4 * q4 + 1] = ok[cc] ? v.y : 0u;
+                                xw[4 * q4 + 2] = ok[cc] ? v.z : 0u;
+                                xw[4 * q4 + 3] = ok[cc] ? v.w : 0u;
+                            }
+                            if constexpr (WDT == DT_Q8) {
+                                float sg = 0.f, su = 0.f;
+#pragma unroll
+                                for (int q = 0; q < NW; q++) {
+                                    sg = dot2_bf16(wg[q], xw[q], sg);
+                                    su = dot2_bf16(wu[q], xw[q], su);
+                                }
+                                ag[r][j] = fmaf(scg, sg, ag[r][j]);
+                                au[r][j] = fmaf(scu, su, au[r][j]);
+                            } else {
+#pragma unroll
+                                for (int q = 0; q < NW; q++) {
+                                    ag[r][j] = dot2_bf16(wg[q], xw[q], ag[r][j]);
+                                    au[r][j] = dot2_bf16(wu[q], xw[q], au[r][j]);
+                                }
+                            }
+                        }
+                    }
+                } else {
+                    float wg[N], wu[N];
+                    decode_chunk<WDT>(B.g[r][cc], wg);
+                    decode_chunk<WDT>(B.u[r][cc], wu);
+                    float scg = ok[cc] ? 1.f : 0.f, scu = scg;
+                    if constexpr (WDT == DT_Q8) {
+                        scg *= f16_bits_to_f32(B.hg[r][cc]);
+                        scu *= f16_bits_to_f32(B.hu[r][cc]);
+                    }
+#pragma unroll
+                    for (int j = 0; j < kTV; j++) {
+                        if (j < nj) {
+                            float xv[N];
+                            const unsigned char *xp = s_x + ((size_t)(j0 + j) * H + (size_t)cl[cc] * N) * XB;
+                            if constexpr (XDT == DT_BF16 && N == 4) {
+                                const u32x2 v = reinterpret_cast<const u32x2 *>(xp)[0];
+                                xv[0] = bf16_lo(v.x); xv[1] = bf16_hi(v.x);
+                                xv[2] = bf16_lo(v.y); xv[3] = bf16_hi(v.y);
+                            } else {
+#pragma unroll
+                                for (int q4 = 0; q4 < N * XB / 16; q4++) {
+                                    const u32x4 v = reinterpret_cast<const u32x4 *>(xp)[q4];
+                                    if constexpr (XDT == DT_BF16) {
+                                        xv[8 * q4] = bf16_lo(v.x); xv[8 * q4 + 1] = bf16_hi(v.x);
+                                        xv[8 * q4 + 2] = bf16_lo(v.y); xv[8 * q4 + 3] = bf16_hi(v.y);
+                                        xv[8 * q4 + 4] = bf16_lo(v.z); xv[8 * q4 + 5] = bf16_hi(v.z);
+                                        xv[8 * q4 + 6] = bf16_lo(v.w); xv[8 * q4 + 7] = bf16_hi(v.w);
+                                    } else {
+                                        xv[4 * q4] = __uint_as_float(v.x); xv[4 * q4 + 1] = __uint_as_float(v.y);
+                                        xv[4 * q4 + 2] = __uint_as_float(v.z); xv[4 * q4 + 3] = __uint_as_float(v.w);
+                                    }
+                                }
+                            }
+                            float pg = 0.f, pu = 0.f;
+#pragma unroll
+                            for (int i = 0; i < N; i++) {
+                                pg = fmaf(wg[i], xv[i], pg);
+                                pu = fmaf(wu[i], xv[i], pu);
+                            }
+                            ag[r][j] = fmaf(scg, pg, ag[r][j]);
+                            au[r][j] = fmaf(scu, pu, au[r][j]);
+                        }
+                    }
+                }
             }
         }
-        __syncthreads();
-
-        for (int q = 0; q < kPairsPerWave; q += kRowPairs) {
-            const int ib = row0 + wave * kPairsPerWave + q;
-            if (ib >= width) break; // uniform per wave
-            const char *grow[kRowPairs], *urow[kRowPairs];
-            const uint16_t *gsr[kRowPairs], *usr[kRowPairs];
+    };
+    // one (row, token) result per reduction pair: clamp, SwiGLU, store
+    auto epilogue = [&](int i0, int jt, int nj) {
 #pragma unroll
-            for (int r = 0; r < kRowPairs; r++) {
-                const int i = min(ib + r, width - 1);
-                grow[r] = reinterpret_cast<const char *>(gbase) + (size_t)i * row_bytes;
-                urow[r] = reinterpret_cast<const char *>(ubase) + (size_t)i * row_bytes;
-                if constexpr (WDT == DT_Q8) {
-                    gsr[r] = gsb + (size_t)i * (H / 32);
-                    usr[r] = usb + (size_t)i * (H / 32);
-                }
-            }
-            float ag[kRowPairs][TB], au[kRowPairs][TB];
+        for (int j = 0; j < kTV; j++) {
+            if (j < nj) {
+                const int jj = jt + j;
+                const int t = shared ? jj : a.sorted[p0 + jj] / a.k;
+                const float sc = a.tok_scale ? a.tok_scale[t] : 1.0f;
 #pragma unroll
-            for (int r = 0; r < kRowPairs; r++)
-#pragma unroll
-                for (int tb = 0; tb < TB; tb++) ag[r][tb] = au[r][tb] = 0.f;
-
-            for (int c = lane; c < H / N; c += kWave) {
-                float wg[kRowPairs][N], wu[kRowPairs][N];
-                float sg[kRowPairs], su[kRowPairs];
-#pragma unroll
-                for (int r = 0; r < kRowPairs; r++) {
-                    load_chunk<WDT>(grow[r], c, wg[r]);
-                    load_chunk<WDT>(urow[r], c, wu[r]);
-                    if constexpr (WDT == DT_Q8) {
-                        sg[r] = f16_bits_to_f32(gsr[r][c >> 1]);
-                        su[r] = f16_bits_to_f32(usr[r][c >> 1]);
-                    }
-                }
-#pragma unroll
-                for (int tb = 0; tb < TB; tb++) {
-                    float xv[N];
-#pragma unroll
-                    for (int n4 = 0; n4 < N / 4; n4++) {
-                        f32x4 v = reinterpret_cast<const f32x4 *>(xs + tb * H + c * N)[n4];
-                        xv[4 * n4] = v.x; xv[4 * n4 + 1] = v.y; xv[4 * n4 + 2] = v.z; xv[4 * n4 + 3] = v.w;
-                    }
-#pragma unroll
-                    for (int r = 0; r < kRowPairs; r++) {
-                        float pg = 0.f, pu = 0.f;
-#pragma unroll
-                        for (int n = 0; n < N; n++) {
-                            pg = fmaf(wg[r][n], xv[n], pg);
-                            pu = fmaf(wu[r][n], xv[n], pu);
-                        }
-                        if constexpr (WDT == DT_Q8) {
-                            ag[r][tb] = fmaf(sg[r], pg, ag[r][tb]);
-                            au[r][tb] = fmaf(su[r], pu, au[r][tb]);
-                        } else {
-                            ag[r][tb] += pg;
-                            au[r][tb] += pu;
-                        }
-                    }
-                }
-            }
-#pragma unroll
-            for (int r = 0; r < kRowPairs; r++) {
-#pragma unroll
-                for (int tb = 0; tb < TB; tb++) {
-                    float g = wave_sum(ag[r][tb]);
-                    float v = wave_sum(au[r][tb]);
-                    if (a.limit > 0.f) {
+                for (int r = 0; r < RP; r++) {
+                    float g = wave_sum(ag[r][j]) * sc;
+                    float v = wave_sum(au[r][j]) * sc;
+                    if (!shared && a.limit > 0.f) { // the shared expert is not clamped
                         g = clampf(g, a.limit);
                         v = clampf(v, a.limit);
                     }
-                    const int i = ib + r;
-                    if (lane == 0 && i < width && tok0 + tb < ntok) {
+                    if (lane == 0) {
                         const float h = silu_mul(g, v);
-                        if (is_shared)
-                            a.shared_act[(size_t)(tok0 + tb) * a.Is + i] = h;
-                        else
-                            a.act[(size_t)(p0 + tok0 + tb) * a.I + i] = h;
+                        if (shared) a.shared_act[(size_t)jj * a.Is + i0 + r] = h;
+                        else a.act[(size_t)(p0 + jj) * a.I + i0 + r] = h;
                     }
                 }
             }
+        }
+    };
+    // a step's work once its loads are in: with one chunk block per row every
+    // staged token is done from the registers (kTV at a time); with several,
+    // the stage holds at most kTV tokens and the sums run across the blocks.
+    auto compute = [&](const Loads &B, int st, int s0, int ns) {
+        const int g = st / ncb, cb = st - g * ncb;
+        const int i0 = row_w + g * RP;
+        for (int j0 = 0; j0 < ns; j0 += kTV) {
+            const int nj = min(kTV, ns - j0);
+            if (cb == 0)
+#pragma unroll
+                for (int r = 0; r < RP; r++)
+#pragma unroll
+                    for (int j = 0; j < kTV; j++) ag[r][j] = au[r][j] = 0.f;
+            dots(B, cb, j0, nj);
+            if (cb == ncb - 1) epilogue(i0, s0 + j0, nj);
+        }
+    };
+
+    for (int s0 = 0; s0 < n; s0 += a.ncap) {
+        const int ns = min(a.ncap, n - s0);
+        __syncthreads(); // the previous stage is no longer read
+        for (int q = tid; q < ns * cpr; q += kThreads) {
+            const int j = q / cpr, c = q - j * cpr;
+            const int t = shared ? s0 + j : a.sorted[p0 + s0 + j] / a.k;
+            reinterpret_cast<u32x4 *>(s_x)[q] =
+                reinterpret_cast<const u32x4 *>(reinterpret_cast<const char *>(a.x) + (size_t)t * H * XB)[c];
+        }
+        __syncthreads();
+        // (Issuing the next step's loads before computing the current one
+        // measured slower: the extra registers cost more than the overlap.)
+        for (int st = 0; st < nsteps; st++) {
+            Loads B;
+            load(B, st);
+            compute(B, st, s0, ns);
         }
     }
 }
 
+// Chunks per lane per row for a reduction of `chunks` 16-byte chunks, from the
+// instantiated set (larger reductions loop over blocks of 8 * 64 chunks).
+static int rows_cpl(int chunks) {
+    const int c = (chunks + kWave - 1) / kWave;
+    return c <= 4 ? (c < 1 ? 1 : c) : 8;
+}
+
 template <int XDT, int WDT>
-static void gateup_dispatch(const GateUpArgs &a, int grid, int tb, size_t lds, hipStream_t s) {
-    if (tb == 1)
-        launch_kernel((k_gateup_gemv<XDT, WDT, 1>), dim3(grid), dim3(kThreads), lds, s, a);
-    else
-        launch_kernel((k_gateup_gemv<XDT, WDT, 4>), dim3(grid), dim3(kThreads), lds, s, a);
+static void gateup_rows_dispatch(int cpl, const RowsGateUp &a, int grid, size_t lds, hipStream_t s) {
+    switch (cpl) {
+    case 1: launch_kernel((k_gateup_rows<XDT, WDT, 1, 2>), dim3(grid), dim3(kThreads), (uint32_t)lds, s, a); break;
+    case 2: launch_kernel((k_gateup_rows<XDT, WDT, 2, 2>), dim3(grid), dim3(kThreads), (uint32_t)lds, s, a); break;
+    case 3: launch_kernel((k_gateup_rows<XDT, WDT, 3, 2>), dim3(grid), dim3(kThreads), (uint32_t)lds, s, a); break;
+    case 4: launch_kernel((k_gateup_rows<XDT, WDT, 4, 2>), dim3(grid), dim3(kThreads), (uint32_t)lds, s, a); break;
+    default: launch_kernel((k_gateup_rows<XDT, WDT, 8, 1>), dim3(grid), dim3(kThreads), (uint32_t)lds, s, a); break;
+    }
+}
+
+static int chunk_elems(int dt) { return dt == DT_Q8 ? 16 : (dt == DT_BF16 ? 8 : 4); }
+
+// Token rows one LDS stage of the gate/up kernel holds: up to kStageMax, as
+// LDS allows, and at most kTV when a row spans several chunk blocks.
+int gemv_stage_tokens(const Layer &L) {
+    const int xb = L.xdt == DT_BF16 ? 2 : 4;
+    int n = kStageBytes / (L.H * xb);
+    if (n > kStageMax) n = kStageMax;
+    const int nch = L.H / chunk_elems(L.edt), cpl = rows_cpl(nch);
+    if (nch > kWave * cpl && n > kTV) n = kTV;
+    return n;
 }
 
 hipError_t launch_gateup_gemv(const Layer &L, const void *x, const float *tok_scale, const Mats &routed,
                               const Mats &shared, const Routing &rt, int M, float *act,
                               float *shared_act, hipStream_t s) {
-    GateUpArgs a;
+    RowsGateUp a;
     a.x = x;
     a.tok_scale = tok_scale;
     a.routed = routed;
@@ -217,269 +368,268 @@ hipError_t launch_gateup_gemv(const Layer &L, const void *x, const float *tok_sc
     a.k = L.k;
     a.I = L.I;
     a.Is = shared_act ? L.Is : 0;
-    a.seg_routed = act ? (L.E < M * L.k ? L.E : M * L.k) : 0;
-    a.tiles_I = (L.I + kPairsPerWG - 1) / kPairsPerWG;
-    a.tiles_Is = (a.Is + kPairsPerWG - 1) / kPairsPerWG;
+    a.max_routed = act ? (L.E < M * L.k ? L.E : M * L.k) : 0;
+    a.tiles_I = (L.I + kRowsTileGU - 1) / kRowsTileGU;
+    a.tiles_Is = (a.Is + kRowsTileGU - 1) / kRowsTileGU;
     a.limit = L.limit;
     a.act = act;
     a.shared_act = shared_act;
-    const int grid = a.seg_routed * a.tiles_I + a.tiles_Is;
+    const int xb = L.xdt == DT_BF16 ? 2 : 4;
+    a.ncap = gemv_stage_tokens(L);
+    if (a.ncap < 1) return hipErrorInvalidValue;
+    // a segment holds at most M tokens (a token picks an expert at most once)
+    const size_t lds = (size_t)(M < a.ncap ? M : a.ncap) * L.H * xb;
+    const int grid = a.max_routed * a.tiles_I + a.tiles_Is;
     if (grid == 0) return hipSuccess;
-    const int tb = (M == 1 || 4 * L.H > 16384) ? 1 : 4;   // staged tokens must fit 64 KB of LDS
-    const size_t lds = (size_t)tb * L.H * sizeof(float);
+    const int cpl = rows_cpl(L.H / chunk_elems(L.edt));
     if (L.xdt == DT_BF16) {
-        if (L.edt == DT_BF16) gateup_dispatch<DT_BF16, DT_BF16>(a, grid, tb, lds, s);
-        else if (L.edt == DT_Q8) gateup_dispatch<DT_BF16, DT_Q8>(a, grid, tb, lds, s);
-        else gateup_dispatch<DT_BF16, DT_F32>(a, grid, tb, lds, s);
+        if (L.edt == DT_BF16) gateup_rows_dispatch<DT_BF16, DT_BF16>(cpl, a, grid, lds, s);
+        else if (L.edt == DT_Q8) gateup_rows_dispatch<DT_BF16, DT_Q8>(cpl, a, grid, lds, s);
+        else gateup_rows_dispatch<DT_BF16, DT_F32>(cpl, a, grid, lds, s);
     } else {
-        if (L.edt == DT_BF16) gateup_dispatch<DT_F32, DT_BF16>(a, grid, tb, lds, s);
-        else if (L.edt == DT_Q8) gateup_dispatch<DT_F32, DT_Q8>(a, grid, tb, lds, s);
-        else gateup_dispatch<DT_F32, DT_F32>(a, grid, tb, lds, s);
+        if (L.edt == DT_BF16) gateup_rows_dispatch<DT_F32, DT_BF16>(cpl, a, grid, lds, s);
+        else if (L.edt == DT_Q8) gateup_rows_dispatch<DT_F32, DT_Q8>(cpl, a, grid, lds, s);
+        else gateup_rows_dispatch<DT_F32, DT_F32>(cpl, a, grid, lds, s);
     }
     return hipGetLastError();
 }
 
-// -------------------------------------------------------------------- down
-constexpr int kRH = 2;                     // output rows per wave
-constexpr int kRowsPerWG = kWaves * kRH;   // rows of H per workgroup
-constexpr int kDTB = 4;                    // routes per inner step
-
-struct DownArgs {
+// ------------------------------------------------------------------ down
+struct RowsDown {
     const float *act, *shared_act;
     Mats routed, shared;
-    const int32_t *offsets, *sorted, *active;
-    const float *w, *seed;
-    int M, H, k, I, Is;
-    float *y;
-    float *y_routes, *y_shared; // unfused form
-    int seg_routed;             // unfused: workgroup slots for routed experts
-    int tiles_H;                // unfused: row tiles of H per segment
+    const int32_t *offsets, *active;
+    int M, H, I, Is;
+    int max_routed, tiles_H;
+    int S, KS;      // routed experts: reduction slices over I and their width
+    int Ss, KSs;    // shared expert: slices over Is
+    int ncap;       // act rows one LDS stage holds
+    float *y_routes, *y_shared;
+    size_t slab_r, slab_s;
 };
 
-// dot[r][tb] = sum_i down_row_r[i] * act_tb[i] over one expert's rows, for
-// kDTB consecutive act rows starting at arow (rows past n are skipped).
-template <int WDT>
-__device__ __forceinline__ void down_dots(const char *const *drow, const uint16_t *const *dsr, int width,
-                                          const float *arow, int n, int lane, float (&dot)[kRH][kDTB]) {
+template <int WDT, int CPL, int RP>
+struct DownLoads {
+    u32x4 w[RP][CPL];
+    uint16_t h[RP][CPL];
+};
+
+template <int WDT, int CPL, int RP>
+__global__ __launch_bounds__(kThreads) void k_down_rows(RowsDown a) {
+    extern __shared__ __attribute__((aligned(16))) float s_act[]; // [ncap][KS] fp32
     constexpr int N = Chunk<WDT>::N;
-#pragma unroll
-    for (int r = 0; r < kRH; r++)
-#pragma unroll
-        for (int tb = 0; tb < kDTB; tb++) dot[r][tb] = 0.f;
-    for (int c = lane; c < width / N; c += kWave) {
-        float wd[kRH][N], sd[kRH];
-#pragma unroll
-        for (int r = 0; r < kRH; r++) {
-            load_chunk<WDT>(drow[r], c, wd[r]);
-            if constexpr (WDT == DT_Q8) sd[r] = f16_bits_to_f32(dsr[r][c >> 1]);
-        }
-#pragma unroll
-        for (int tb = 0; tb < kDTB; tb++) {
-            if (tb < n) {
-                float av[N];
-#pragma unroll
-                for (int n4 = 0; n4 < N / 4; n4++) {
-                    f32x4 v = reinterpret_cast<const f32x4 *>(arow + (size_t)tb * width + c * N)[n4];
-                    av[4 * n4] = v.x; av[4 * n4 + 1] = v.y; av[4 * n4 + 2] = v.z; av[4 * n4 + 3] = v.w;
-                }
-#pragma unroll
-                for (int r = 0; r < kRH; r++) {
-                    float p = 0.f;
-#pragma unroll
-                    for (int i = 0; i < N; i++) p = fmaf(wd[r][i], av[i], p);
-                    if constexpr (WDT == DT_Q8) dot[r][tb] = fmaf(sd[r], p, dot[r][tb]);
-                    else dot[r][tb] += p;
-                }
-            }
-        }
-    }
-}
-
-// Fused down + combine for M <= 64.
-template <int WDT>
-__global__ __launch_bounds__(kThreads) void k_down_combine_gemv(DownArgs a) {
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    constexpr int NG = kRowsPerWaveDN / RP;
+    using Loads = DownLoads<WDT, CPL, RP>;
+    const int tid = threadIdx.x, lane = tid & 63, wave = uniform(tid >> 6);
     const int H = a.H;
-    const int h0 = (blockIdx.x * kWaves + wave) * kRH;
-    if (h0 >= H) return;
-    float yacc[kRH];
-    int hr[kRH];
-#pragma unroll
-    for (int r = 0; r < kRH; r++) {
-        hr[r] = min(h0 + r, H - 1);
-        yacc[r] = (a.seed && lane < a.M) ? a.seed[(size_t)lane * H + hr[r]] : 0.f;
-    }
-    const char *drow[kRH];
-    const uint16_t *dsr[kRH];
-    float dot[kRH][kDTB];
-    // shared expert: weight 1, route = token
-    if (a.Is > 0) {
-#pragma unroll
-        for (int r = 0; r < kRH; r++) {
-            drow[r] = reinterpret_cast<const char *>(a.shared.down) + (size_t)hr[r] * a.Is * elem_bytes<WDT>();
-            if constexpr (WDT == DT_Q8) dsr[r] = a.shared.down_s + (size_t)hr[r] * (a.Is / 32);
-        }
-        for (int t0 = 0; t0 < a.M; t0 += kDTB) {
-            const int n = min(kDTB, a.M - t0);
-            down_dots<WDT>(drow, dsr, a.Is, a.shared_act + (size_t)t0 * a.Is, n, lane, dot);
-#pragma unroll
-            for (int tb = 0; tb < kDTB; tb++)
-                if (tb < n) {
-#pragma unroll
-                    for (int r = 0; r < kRH; r++) {
-                        const float d = wave_sum(dot[r][tb]);
-                        if (lane == t0 + tb) yacc[r] += d;
-                    }
-                }
-        }
-    }
-    const int n_active = a.active[0];
-    for (int u = 0; u < n_active; u++) {
-        const int e = a.active[1 + u];
-        const int p0 = a.offsets[e], p1 = a.offsets[e + 1];
-#pragma unroll
-        for (int r = 0; r < kRH; r++) {
-            const size_t row = (size_t)e * H + hr[r];
-            drow[r] = reinterpret_cast<const char *>(a.routed.down) + row * a.I * elem_bytes<WDT>();
-            if constexpr (WDT == DT_Q8) dsr[r] = a.routed.down_s + row * (a.I / 32);
-        }
-        for (int p = p0; p < p1; p += kDTB) {
-            const int n = min(kDTB, p1 - p);
-            down_dots<WDT>(drow, dsr, a.I, a.act + (size_t)p * a.I, n, lane, dot);
-#pragma unroll
-            for (int tb = 0; tb < kDTB; tb++)
-                if (tb < n) {
-                    const int route = a.sorted[p + tb];
-                    const int t = route / a.k;
-                    const float wt = a.w[route];
-#pragma unroll
-                    for (int r = 0; r < kRH; r++) {
-                        const float d = wave_sum(dot[r][tb]);
-                        if (lane == t) yacc[r] = fmaf(wt, d, yacc[r]);
-                    }
-                }
-        }
-    }
-    if (lane < a.M) {
-#pragma unroll
-        for (int r = 0; r < kRH; r++)
-            if (h0 + r < H) a.y[(size_t)lane * H + h0 + r] = yacc[r];
-    }
-}
 
-// Unfused down for M > 64: y_routes[p][h] and y_shared[t][h].
-template <int WDT>
-__global__ __launch_bounds__(kThreads) void k_down_routes_gemv(DownArgs a) {
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int H = a.H;
-    int b = blockIdx.x;
-    int width, p0, n_rows;
-    const char *dbase;
-    const uint16_t *dsb = nullptr;
-    const float *abase;
-    float *out;
-    if (b < a.seg_routed * a.tiles_H) {
-        const int u = b / a.tiles_H;
+    int b = blockIdx.x, width, p0 = 0, n, rt, ks, KS;
+    bool shared;
+    size_t mrow0;
+    const float *vec;
+    const int per_routed = a.S * a.tiles_H;
+    if (b < a.max_routed * per_routed) {
+        const int u = b / per_routed;
         if (u >= a.active[0]) return;
         const int e = a.active[1 + u];
-        b %= a.tiles_H;
+        const int rem = b - u * per_routed;
+        ks = rem / a.tiles_H;
+        rt = rem - ks * a.tiles_H;
         width = a.I;
+        KS = a.KS;
         p0 = a.offsets[e];
-        n_rows = a.offsets[e + 1] - p0;
-        dbase = reinterpret_cast<const char *>(a.routed.down) + (size_t)e * H * a.I * elem_bytes<WDT>();
-        if constexpr (WDT == DT_Q8) dsb = a.routed.down_s + (size_t)e * H * (a.I / 32);
-        abase = a.act;
-        out = a.y_routes;
+        n = a.offsets[e + 1] - p0;
+        shared = false;
+        mrow0 = (size_t)e * H;
+        vec = a.act + (size_t)p0 * a.I;
     } else {
-        b -= a.seg_routed * a.tiles_H;
+        const int rem = b - a.max_routed * per_routed;
+        ks = rem / a.tiles_H;
+        if (ks >= a.Ss) return;
+        rt = rem - ks * a.tiles_H;
         width = a.Is;
-        p0 = 0;
-        n_rows = a.M;
-        dbase = reinterpret_cast<const char *>(a.shared.down);
-        if constexpr (WDT == DT_Q8) dsb = a.shared.down_s;
-        abase = a.shared_act;
-        out = a.y_shared;
+        KS = a.KSs;
+        n = a.M;
+        shared = true;
+        mrow0 = 0;
+        vec = a.shared_act;
     }
-    const int h0 = (b * kWaves + wave) * kRH;
-    if (h0 >= H) return;
-    const char *drow[kRH];
-    const uint16_t *dsr[kRH];
+    const Mats &m = shared ? a.shared : a.routed;
+    const int k0 = ks * KS, klen = min(KS, width - k0);
+    const size_t rbytes = (size_t)width * elem_bytes<WDT>();
+    const char *dbase = reinterpret_cast<const char *>(m.down) + mrow0 * rbytes + (size_t)k0 * elem_bytes<WDT>();
+    const uint16_t *dsb = nullptr;
+    if constexpr (WDT == DT_Q8) dsb = m.down_s + mrow0 * (width / 32) + k0 / 32;
+    float *out = shared ? a.y_shared + ks * a.slab_s : a.y_routes + ks * a.slab_r + (size_t)p0 * H;
+    const int row_w = rt * kRowsTileDN + wave * kRowsPerWaveDN;
+    const int nch = klen / N;
+    const int ncb = (nch + kWave * CPL - 1) / (kWave * CPL);
+    const int ng = row_w < H ? min(NG, (H - row_w) / RP) : 0;
+    const int nsteps = ng * ncb;
+    const int cpr = klen / 4; // 16-byte pieces per staged row slice
+
+    auto chunks = [&](int cb, int (&cl)[CPL], bool (&ok)[CPL]) {
 #pragma unroll
-    for (int r = 0; r < kRH; r++) {
-        const int h = min(h0 + r, H - 1);
-        drow[r] = dbase + (size_t)h * width * elem_bytes<WDT>();
-        if constexpr (WDT == DT_Q8) dsr[r] = dsb + (size_t)h * (width / 32);
-    }
-    float dot[kRH][kDTB];
-    for (int p = 0; p < n_rows; p += kDTB) {
-        const int n = min(kDTB, n_rows - p);
-        down_dots<WDT>(drow, dsr, width, abase + (size_t)(p0 + p) * width, n, lane, dot);
+        for (int cc = 0; cc < CPL; cc++) {
+            const int c = cb * kWave * CPL + lane + kWave * cc;
+            ok[cc] = c < nch;
+            cl[cc] = min(c, nch - 1);
+        }
+    };
+    auto load = [&](Loads &B, int st) {
+        const int g = st / ncb, cb = st - g * ncb;
+        const int h0 = row_w + g * RP;
+        int cl[CPL];
+        bool ok[CPL];
+        chunks(cb, cl, ok);
 #pragma unroll
-        for (int tb = 0; tb < kDTB; tb++)
-            if (tb < n) {
+        for (int r = 0; r < RP; r++)
 #pragma unroll
-                for (int r = 0; r < kRH; r++) {
-                    const float d = wave_sum(dot[r][tb]);
-                    if (lane == 0 && h0 + r < H) out[(size_t)(p0 + p + tb) * H + h0 + r] = d;
+            for (int cc = 0; cc < CPL; cc++) {
+                B.w[r][cc] = load_raw(dbase + (size_t)(h0 + r) * rbytes, cl[cc]);
+                if constexpr (WDT == DT_Q8) B.h[r][cc] = dsb[(size_t)(h0 + r) * (width / 32) + (cl[cc] >> 1)];
+            }
+    };
+    float acc[RP][kTV];
+    auto dots = [&](const Loads &B, int cb, int j0, int nj) {
+        int cl[CPL];
+        bool ok[CPL];
+        chunks(cb, cl, ok);
+#pragma unroll
+        for (int cc = 0; cc < CPL; cc++) {
+            float wv[RP][N];
+#pragma unroll
+            for (int r = 0; r < RP; r++) {
+                decode_chunk<WDT>(B.w[r][cc], wv[r]);
+                float sc = ok[cc] ? 1.f : 0.f;
+                if constexpr (WDT == DT_Q8) sc *= f16_bits_to_f32(B.h[r][cc]);
+#pragma unroll
+                for (int i = 0; i < N; i++) wv[r][i] *= sc;
+            }
+#pragma unroll
+            for (int j = 0; j < kTV; j++) {
+                if (j < nj) {
+                    const f32x4 *ap = reinterpret_cast<const f32x4 *>(s_act + (size_t)(j0 + j) * KS + cl[cc] * N);
+                    float av[N];
+#pragma unroll
+                    for (int q4 = 0; q4 < N / 4; q4++) {
+                        const f32x4 v = ap[q4];
+                        av[4 * q4] = v.x; av[4 * q4 + 1] = v.y; av[4 * q4 + 2] = v.z; av[4 * q4 + 3] = v.w;
+                    }
+#pragma unroll
+                    for (int r = 0; r < RP; r++)
+#pragma unroll
+                        for (int i = 0; i < N; i++) acc[r][j] = fmaf(wv[r][i], av[i], acc[r][j]);
                 }
             }
+        }
+    };
+    auto compute = [&](const Loads &B, int st, int s0, int ns) {
+        const int g = st / ncb, cb = st - g * ncb;
+        const int h0 = row_w + g * RP;
+        for (int j0 = 0; j0 < ns; j0 += kTV) {
+            const int nj = min(kTV, ns - j0);
+            if (cb == 0)
+#pragma unroll
+                for (int r = 0; r < RP; r++)
+#pragma unroll
+                    for (int j = 0; j < kTV; j++) acc[r][j] = 0.f;
+            dots(B, cb, j0, nj);
+            if (cb == ncb - 1) {
+#pragma unroll
+                for (int j = 0; j < kTV; j++) {
+                    if (j < nj) {
+                        const int jj = s0 + j0 + j;
+#pragma unroll
+                        for (int r = 0; r < RP; r++) {
+                            const float v = wave_sum(acc[r][j]);
+                            if (lane == 0) out[(size_t)jj * H + h0 + r] = v;
+                        }
+                    }
+                }
+            }
+        }
+    };
+
+    for (int s0 = 0; s0 < n; s0 += a.ncap) {
+        const int ns = min(a.ncap, n - s0);
+        __syncthreads();
+        for (int q = tid; q < ns * cpr; q += kThreads) {
+            const int j = q / cpr, c = q - j * cpr;
+            reinterpret_cast<f32x4 *>(s_act + (size_t)j * KS)[c] =
+                reinterpret_cast<const f32x4 *>(vec + (size_t)(s0 + j) * width + k0)[c];
+        }
+        __syncthreads();
+        for (int st = 0; st < nsteps; st++) {
+            Loads B;
+            load(B, st);
+            compute(B, st, s0, ns);
+        }
     }
 }
 
-static DownArgs down_args(const Layer &L, const float *act, const float *shared_act, const Mats &routed,
-                          const Mats &shared, const Routing &rt, const float *w, const float *seed, int M,
-                          float *y, float *y_routes, float *y_shared) {
-    DownArgs a;
+// Slices of a down reduction of `width` elements: each at most kSliceMax
+// wide, a multiple of 32 (whole Q8_0 blocks), as even as that allows.
+static void down_slices(int width, int *S, int *KS) {
+    if (width <= 0) {
+        *S = 0;
+        *KS = 0;
+        return;
+    }
+    *S = (width + kSliceMax - 1) / kSliceMax;
+    *KS = ((width + *S - 1) / *S + 31) / 32 * 32;
+    *S = (width + *KS - 1) / *KS;
+}
+
+int down_gemv_slices(int width) {
+    int S, KS;
+    down_slices(width, &S, &KS);
+    return S;
+}
+
+template <int WDT>
+static void down_rows_dispatch(int cpl, const RowsDown &a, int grid, size_t lds, hipStream_t s) {
+    switch (cpl) {
+    case 1: launch_kernel((k_down_rows<WDT, 1, 4>), dim3(grid), dim3(kThreads), (uint32_t)lds, s, a); break;
+    case 2: launch_kernel((k_down_rows<WDT, 2, 4>), dim3(grid), dim3(kThreads), (uint32_t)lds, s, a); break;
+    case 3: launch_kernel((k_down_rows<WDT, 3, 4>), dim3(grid), dim3(kThreads), (uint32_t)lds, s, a); break;
+    case 4: launch_kernel((k_down_rows<WDT, 4, 4>), dim3(grid), dim3(kThreads), (uint32_t)lds, s, a); break;
+    default: launch_kernel((k_down_rows<WDT, 8, 2>), dim3(grid), dim3(kThreads), (uint32_t)lds, s, a); break;
+    }
+}
+
+hipError_t launch_down_gemv(const Layer &L, const float *act, const float *shared_act, const Mats &routed,
+                            const Mats &shared, const Routing &rt, int M, float *y_routes, float *y_shared,
+                            hipStream_t s) {
+    RowsDown a;
     a.act = act;
     a.shared_act = shared_act;
     a.routed = routed;
     a.shared = shared;
     a.offsets = rt.offsets;
-    a.sorted = rt.sorted;
     a.active = rt.active;
-    a.w = w;
-    a.seed = seed;
     a.M = M;
     a.H = L.H;
-    a.k = L.k;
     a.I = L.I;
     a.Is = shared_act ? L.Is : 0;
-    a.y = y;
+    a.max_routed = act ? (L.E < M * L.k ? L.E : M * L.k) : 0;
+    a.tiles_H = (L.H + kRowsTileDN - 1) / kRowsTileDN;
+    down_slices(L.I, &a.S, &a.KS);
+    down_slices(a.Is, &a.Ss, &a.KSs);
+    const int ks_max = a.KS > a.KSs ? a.KS : a.KSs;
+    a.ncap = kStageBytes / (ks_max * 4);
+    if (a.ncap > kStageMax) a.ncap = kStageMax;
     a.y_routes = y_routes;
     a.y_shared = y_shared;
-    a.seg_routed = act ? (L.E < M * L.k ? L.E : M * L.k) : 0;
-    a.tiles_H = (L.H + kRowsPerWG - 1) / kRowsPerWG;
-    return a;
-}
-
-hipError_t launch_down_routes_gemv(const Layer &L, const float *act, const float *shared_act,
-                                   const Mats &routed, const Mats &shared, const Routing &rt, int M,
-                                   float *y_routes, float *y_shared, hipStream_t s) {
-    const DownArgs a = down_args(L, act, shared_act, routed, shared, rt, nullptr, nullptr, M, nullptr,
-                                 y_routes, y_shared);
-    const dim3 grid(a.seg_routed * a.tiles_H + (a.Is > 0 ? a.tiles_H : 0));
-    if (grid.x == 0) return hipSuccess;
-    if (L.edt == DT_BF16) launch_kernel(k_down_routes_gemv<DT_BF16>, grid, dim3(kThreads), 0, s, a);
-    else if (L.edt == DT_Q8) launch_kernel(k_down_routes_gemv<DT_Q8>, grid, dim3(kThreads), 0, s, a);
-    else launch_kernel(k_down_routes_gemv<DT_F32>, grid, dim3(kThreads), 0, s, a);
-    return hipGetLastError();
-}
-
-hipError_t launch_down_gemv(const Layer &L, const float *act, const float *shared_act,
-                            const Mats &routed, const Mats &shared, const Routing &rt,
-                            const float *w, const float *seed, int M, float *y, float *y_routes,
-                            float *y_shared, hipStream_t s) {
-    if (M > kWave) {
-        hipError_t err = launch_down_routes_gemv(L, act, shared_act, routed, shared, rt, M, y_routes,
-                                                 y_shared, s);
-        if (err != hipSuccess) return err;
-        return launch_combine(L, y_routes, shared_act ? y_shared : nullptr, rt.route_pos, w, seed, M, y, s);
-    }
-    const DownArgs a = down_args(L, act, shared_act, routed, shared, rt, w, seed, M, y, y_routes, y_shared);
-    const dim3 grid(a.tiles_H);
-    if (L.edt == DT_BF16) launch_kernel(k_down_combine_gemv<DT_BF16>, grid, dim3(kThreads), 0, s, a);
-    else if (L.edt == DT_Q8) launch_kernel(k_down_combine_gemv<DT_Q8>, grid, dim3(kThreads), 0, s, a);
-    else launch_kernel(k_down_combine_gemv<DT_F32>, grid, dim3(kThreads), 0, s, a);
+    a.slab_r = (size_t)M * L.k * L.H;
+    a.slab_s = (size_t)M * L.H;
+    const size_t lds = (size_t)(M < a.ncap ? M : a.ncap) * ks_max * 4;
+    const int grid = a.max_routed * a.S * a.tiles_H + a.Ss * a.tiles_H;
+    if (grid == 0) return hipSuccess;
+    const int cpl = rows_cpl(ks_max / chunk_elems(L.edt));
+    if (L.edt == DT_BF16) down_rows_dispatch<DT_BF16>(cpl, a, grid, lds, s);
+    else if (L.edt == DT_Q8) down_rows_dispatch<DT_Q8>(cpl, a, grid, lds, s);
+    else down_rows_dispatch<DT_F32>(cpl, a, grid, lds, s);
     return hipGetLastError();
 }
 
@@ -646,7 +796,7 @@ __global__ __launch_bounds__(kThreads) void k_gateup_m1(M1GateUpArgs a) {
             }
             g = wave_sum(g);
             v = wave_sum(v);
-            if (a.limit > 0.f) {
+            if (a.limit > 0.f && slot[r] >= 0) { // the shared expert is not clamped
                 g = clampf(g, a.limit);
                 v = clampf(v, a.limit);
             }
@@ -873,18 +1023,24 @@ hipError_t launch_down_m1(const Layer &L, const float *act, const float *shared_
 }
 
 // -------------------------------------------------------------------- combine
-// One thread per (token, 4 consecutive h); slots summed in order j = 0..k-1,
-// each slot's partial slices (a split reduction) summed in slice order first.
+// One thread per (token, 4 consecutive h): seed, then the shared expert's
+// slices in order, then slots j = 0..k-1, each slot's slices (partial sums of
+// a split reduction) summed in slice order before its weight is applied.
 __global__ __launch_bounds__(256) void k_combine(const float *y_routes, const float *y_shared,
                                                  const int32_t *route_pos, const float *w,
                                                  const float *seed, int M, int H, int k, int S,
-                                                 size_t slab, float *y) {
+                                                 size_t slab, int Ss, size_t slab_s, float *y) {
     const int H4 = H / 4;
     const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
     if (idx >= (size_t)M * H4) return;
     const int t = (int)(idx / H4), c = (int)(idx % H4);
     f32x4 acc = seed ? reinterpret_cast<const f32x4 *>(seed + (size_t)t * H)[c] : f32x4{0.f, 0.f, 0.f, 0.f};
-    if (y_shared) acc += reinterpret_cast<const f32x4 *>(y_shared + (size_t)t * H)[c];
+    if (y_shared) {
+        const float *row = y_shared + (size_t)t * H;
+        f32x4 v = reinterpret_cast<const f32x4 *>(row)[c];
+        for (int sl = 1; sl < Ss; sl++) v += reinterpret_cast<const f32x4 *>(row + sl * slab_s)[c];
+        acc += v;
+    }
     for (int j = 0; j < k; j++) {
         const int r = t * k + j;
         const float *row = y_routes + (size_t)route_pos[r] * H;
@@ -901,10 +1057,11 @@ __global__ __launch_bounds__(256) void k_combine(const float *y_routes, const fl
 
 hipError_t launch_combine(const Layer &L, const float *y_routes, const float *y_shared,
                           const int32_t *route_pos, const float *w, const float *seed, int M,
-                          float *y, hipStream_t s, int slices) {
+                          float *y, hipStream_t s, int slices, int shared_slices) {
     const size_t n = (size_t)M * (L.H / 4);
     launch_kernel(k_combine, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, y_routes, y_shared,
-                       route_pos, w, seed, M, L.H, L.k, slices, (size_t)M * L.k * L.H, y);
+                  route_pos, w, seed, M, L.H, L.k, slices, (size_t)M * L.k * L.H, shared_slices,
+                  (size_t)M * L.H, y);
     return hipGetLastError();
 }
 

@@ -26,7 +26,8 @@ struct Routing {
     const int32_t *sorted;        // [R]
     const int32_t *route_pos;     // [R]
     const int32_t *active;        // [1+E]: count, then touched experts ascending
-    const int32_t *tiles;         // [1+2*T]: count, then (expert, first sorted row)
+    const int32_t *tiles;         // MFMA tile list: [0] count T, [1+e] first tile of expert e
+                                  // (e = 0..E), then T pairs (expert, first sorted row)
 };
 
 hipError_t launch_rms_scale(const Layer &L, const void *x, int M, float *scale, hipStream_t s);
@@ -37,36 +38,34 @@ hipError_t launch_topk(const Layer &L, const float *logits, const float *bias, i
 hipError_t launch_permute(int E, int R, int tile_rows, const int32_t *ids, int32_t *counts,
                           int32_t *offsets, int32_t *sorted, int32_t *route_pos, int32_t *active,
                           int32_t *tiles, hipStream_t s);
-// Router + top-k + permutation in one launch for M <= route_small_max_tokens();
-// `ticket` is a workspace word that must be zero before the call (the kernel
-// leaves it zero).
+// Router + top-k + permutation for M <= route_small_max_tokens() (two launches).
 int route_small_max_tokens();
 hipError_t launch_route_small(const Layer &L, const void *x, const void *router, const float *bias,
                               const float *tok_scale, int M, float *logits, int32_t *ids, float *w,
                               int32_t *counts, int32_t *offsets, int32_t *sorted, int32_t *route_pos,
-                              int32_t *active, uint32_t *ticket, hipStream_t s);
+                              int32_t *active, hipStream_t s);
 hipError_t launch_zero_words(uint32_t *p, int n, hipStream_t s);
 // Derive the active-expert list and the tile list from offsets alone.
 hipError_t launch_plan_from_offsets(int E, int tile_rows, const int32_t *offsets, int32_t *active,
                                     int32_t *tiles, hipStream_t s);
 
-// GEMV path.
+// GEMV path (any M; the expert's vectors are staged in LDS).
+// Tokens one LDS stage of the gate/up kernel holds (0: hidden too large).
+int gemv_stage_tokens(const Layer &L);
 hipError_t launch_gateup_gemv(const Layer &L, const void *x, const float *tok_scale, const Mats &routed,
                               const Mats &shared, const Routing &rt, int M, float *act,
                               float *shared_act, hipStream_t s);
-hipError_t launch_down_gemv(const Layer &L, const float *act, const float *shared_act,
-                            const Mats &routed, const Mats &shared, const Routing &rt,
-                            const float *w, const float *seed, int M, float *y, float *y_routes,
-                            float *y_shared, hipStream_t s);
-// Per-route down projection (no combine): y_routes [R][H], y_shared [M][H].
-hipError_t launch_down_routes_gemv(const Layer &L, const float *act, const float *shared_act,
-                                   const Mats &routed, const Mats &shared, const Routing &rt, int M,
-                                   float *y_routes, float *y_shared, hipStream_t s);
-// y[t] = seed[t] + y_shared[t] + sum_j w[t][j] * sum_s y_routes[s][route_pos[t*k+j]]
-// (s over `slices` partial results of a split reduction, slab M*k*H apart).
+// Per-route down products, split over the reduction:
+// y_routes [down_gemv_slices(I)][M*k][H], y_shared [down_gemv_slices(Is)][M][H].
+hipError_t launch_down_gemv(const Layer &L, const float *act, const float *shared_act, const Mats &routed,
+                            const Mats &shared, const Routing &rt, int M, float *y_routes, float *y_shared,
+                            hipStream_t s);
+int down_gemv_slices(int width);
+// y[t] = seed[t] + sum_s y_shared[s][t] + sum_j w[t][j] * sum_s y_routes[s][route_pos[t*k+j]]
+// (slices of a split reduction, slabs M*k*H and M*H apart).
 hipError_t launch_combine(const Layer &L, const float *y_routes, const float *y_shared,
                           const int32_t *route_pos, const float *w, const float *seed, int M,
-                          float *y, hipStream_t s, int slices = 1);
+                          float *y, hipStream_t s, int slices, int shared_slices);
 // Reduction slices of the MFMA down projection for an M-token call.
 int down_ksplit(const Layer &L, int M);
 

@@ -59,7 +59,6 @@ WsLayout layout(const moe_plan *p, int M) {
     const moe::Layer &L = p->L;
     const size_t R = (size_t)M * L.k;
     const bool mfma = use_mfma(p, M);
-    const bool unfused = mfma || M > 64;
     WsLayout w{};
     size_t o = 0;
     auto take = [&](size_t bytes) { size_t at = o; o += up(bytes); return at; };
@@ -78,8 +77,8 @@ WsLayout layout(const moe_plan *p, int M) {
     w.tiles = take(mfma ? (size_t)(2 + L.E + 2 * w.max_tiles) * 4 : 4 * 3);
     w.act = take(R * L.I * 4);
     w.shared_act = take(L.Is > 0 ? (size_t)M * L.Is * 4 : 0);
-    w.y_routes = take(unfused ? (mfma ? moe::down_ksplit(L, M) : 1) * R * L.H * 4 : 0);
-    w.y_shared = take(unfused && L.Is > 0 ? (size_t)M * L.H * 4 : 0);
+    w.y_routes = take((size_t)(mfma ? moe::down_ksplit(L, M) : moe::down_gemv_slices(L.I)) * R * L.H * 4);
+    w.y_shared = take(L.Is > 0 ? (size_t)(mfma ? 1 : moe::down_gemv_slices(L.Is)) * M * L.H * 4 : 0);
     w.total = o;
     return w;
 }
@@ -335,17 +334,17 @@ moe_status moe_combine(const moe_plan *p, const float *act, const moe_weights *w
         float *yr = at<float>(ws, lay.y_routes);
         LAUNCH(moe::launch_down_mfma(L, act, nullptr, routed_mats(wts), none, rt, M, lay.max_tiles, yr, nullptr, s),
                "down (MFMA)");
-        LAUNCH(moe::launch_combine(L, yr, nullptr, route_pos, w, seed, M, y, s, moe::down_ksplit(L, M)),
+        LAUNCH(moe::launch_combine(L, yr, nullptr, route_pos, w, seed, M, y, s, moe::down_ksplit(L, M), 0),
                "combine");
     } else {
-        LAUNCH(moe::launch_down_gemv(L, act, nullptr, routed_mats(wts), none, rt, w, seed, M, y,
-                                     at<float>(ws, lay.y_routes), nullptr, s),
-               "down + combine");
+        float *yr = at<float>(ws, lay.y_routes);
+        LAUNCH(moe::launch_down_gemv(L, act, nullptr, routed_mats(wts), none, rt, M, yr, nullptr, s), "down");
+        LAUNCH(moe::launch_combine(L, yr, nullptr, route_pos, w, seed, M, y, s, moe::down_gemv_slices(L.I), 0),
+               "combine");
     }
     return MOE_OK;
 }
 
-// Records an event after each kernel when timing is asked for.
 // Per-stage timing for moe_forward_timed: events[2i] and events[2i+1] bracket
 // the kernels of the i-th stage that launched any (see moe::StageTimer).
 struct Recorder {
@@ -416,7 +415,7 @@ static moe_status forward_impl(const moe_plan *p, const void *x, const moe_weigh
         STAGE(rec, moe::launch_router_small(L, x, wts->router, sc, M, lg, s), "router", MOE_STAGE_ROUTER);
     } else if (M <= moe::route_small_max_tokens() && !mfma) {
         STAGE(rec, moe::launch_route_small(L, x, wts->router, wts->bias, sc, M, lg, ids, w, counts, offsets,
-                                           sorted, rpos, active, at<uint32_t>(ws, lay.sync), s),
+                                           sorted, rpos, active, s),
               "route", MOE_STAGE_ROUTER);
     } else {
         if (mfma && L.rdt == moe::DT_BF16)
@@ -440,7 +439,7 @@ static moe_status forward_impl(const moe_plan *p, const void *x, const moe_weigh
         STAGE(rec, moe::launch_down_mfma(L, act, sact, routed_mats(wts), shared_mats(wts), rt, M,
                                          lay.max_tiles, yr, ysh, s),
               "down (MFMA)", MOE_STAGE_DOWN);
-        STAGE(rec, moe::launch_combine(L, yr, ysh, rpos, w, nullptr, M, y, s, moe::down_ksplit(L, M)), "combine",
+        STAGE(rec, moe::launch_combine(L, yr, ysh, rpos, w, nullptr, M, y, s, moe::down_ksplit(L, M), 1), "combine",
               MOE_STAGE_COMBINE);
     } else if (single) {
         STAGE(rec, moe::launch_gateup_m1(L, x, sc, routed_mats(wts), shared_mats(wts), lg, wts->bias, ids, w,
@@ -452,16 +451,11 @@ static moe_status forward_impl(const moe_plan *p, const void *x, const moe_weigh
     } else {
         STAGE(rec, moe::launch_gateup_gemv(L, x, sc, routed_mats(wts), shared_mats(wts), rt, M, act, sact, s),
               "gate/up", MOE_STAGE_GATEUP);
-        if (M <= 64) {
-            STAGE(rec, moe::launch_down_gemv(L, act, sact, routed_mats(wts), shared_mats(wts), rt, w, nullptr,
-                                             M, y, yr, ysh, s),
-                  "down + combine", MOE_STAGE_DOWN);
-        } else {
-            STAGE(rec, moe::launch_down_routes_gemv(L, act, sact, routed_mats(wts), shared_mats(wts), rt, M,
-                                                    yr, ysh, s),
-                  "down", MOE_STAGE_DOWN);
-            STAGE(rec, moe::launch_combine(L, yr, ysh, rpos, w, nullptr, M, y, s), "combine", MOE_STAGE_COMBINE);
-        }
+        STAGE(rec, moe::launch_down_gemv(L, act, sact, routed_mats(wts), shared_mats(wts), rt, M, yr, ysh, s),
+              "down", MOE_STAGE_DOWN);
+        STAGE(rec, moe::launch_combine(L, yr, ysh, rpos, w, nullptr, M, y, s, moe::down_gemv_slices(L.I),
+                                       moe::down_gemv_slices(L.Is)),
+              "combine", MOE_STAGE_COMBINE);
     }
     return MOE_OK;
 }

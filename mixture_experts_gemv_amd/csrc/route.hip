@@ -1,9 +1,9 @@
 // Routing kernels: RMS pre-norm scale, router GEMV, wave top-k + softmax, and
 // the expert histogram / scan / stable scatter of the routes.
 //
-// For small batches one kernel does all of it: each workgroup computes the
-// logits of a few experts for every token, and the last workgroup to finish
-// (an atomic ticket in the workspace) runs the top-k and the permutation.
+// For small batches a router kernel with one workgroup per (expert, 4 tokens)
+// is followed by one workgroup that runs every token's top-k and the
+// permutation.
 #include "common.h"
 #include "launch.h"
 #include "topk.h"
@@ -57,13 +57,12 @@ hipError_t launch_rms_scale(const Layer &L, const void *x, int M, float *scale, 
 
 // ---------------------------------------------------------------- router dots
 // One wave: logits of expert row `wrow` for tokens t0..t0+nt-1 (nt <= TM).
-// Lanes stride the row in 8-element pieces, kRouterCB pieces per lane per
-// block with every load of a block issued before use (indices past the row
-// end are clamped and their products masked); each token's sum is
-// wave-reduced.
-constexpr int kRouterCB = 4;
-
-template <int XDT, int RDT, int TM>
+// Lanes stride the row in 8-element pieces, CB pieces per lane per block.
+// Every load of a block (the router pieces and the pieces of all TM tokens)
+// is issued unconditionally before any is used: indices past the row end or
+// past the last token are clamped, and their products masked.  Each token's
+// sum is wave-reduced.
+template <int XDT, int RDT, int TM, int CB>
 __device__ __forceinline__ void router_dots(const void *x, const void *wrow, int H, int t0, int nt,
                                             int lane, float (&acc)[TM], int cb = 0, int ce = -1) {
     const size_t xrow = (size_t)H * dt_bytes<XDT>();
@@ -71,39 +70,42 @@ __device__ __forceinline__ void router_dots(const void *x, const void *wrow, int
     const int nch = ce < 0 ? H / 8 : ce;  // this wave covers 8-element pieces cb..nch-1
 #pragma unroll
     for (int i = 0; i < TM; i++) acc[i] = 0.f;
-    for (int c0 = cb; c0 < nch; c0 += kWave * kRouterCB) {
-        float w[kRouterCB][8];
-        int cc[kRouterCB];
+    for (int c0 = cb; c0 < nch; c0 += kWave * CB) {
+        float w[CB][8];
+        int cc[CB];
 #pragma unroll
-        for (int j = 0; j < kRouterCB; j++) {
+        for (int j = 0; j < CB; j++) {
             const int c = c0 + lane + kWave * j;
             cc[j] = min(c, nch - 1);
             load8<RDT>(wrow, cc[j], w[j]);
-            if (c >= nch)
-#pragma unroll
-                for (int i = 0; i < 8; i++) w[j][i] = 0.f;
         }
+        float xv[TM][CB][8];
 #pragma unroll
         for (int tm = 0; tm < TM; tm++) {
-            if (tm < nt) {
-                float xv[kRouterCB][8];
+            const int tc = min(tm, nt - 1);
 #pragma unroll
-                for (int j = 0; j < kRouterCB; j++) load8<XDT>(xb + tm * xrow, cc[j], xv[j]);
-#pragma unroll
-                for (int j = 0; j < kRouterCB; j++)
-#pragma unroll
-                    for (int i = 0; i < 8; i++) acc[tm] = fmaf(w[j][i], xv[j][i], acc[tm]);
-            }
+            for (int j = 0; j < CB; j++) load8<XDT>(xb + tc * xrow, cc[j], xv[tm][j]);
         }
+#pragma unroll
+        for (int j = 0; j < CB; j++) {
+            const float mk = c0 + lane + kWave * j < nch ? 1.f : 0.f;
+#pragma unroll
+            for (int i = 0; i < 8; i++) w[j][i] *= mk;
+        }
+#pragma unroll
+        for (int tm = 0; tm < TM; tm++)
+#pragma unroll
+            for (int j = 0; j < CB; j++)
+#pragma unroll
+                for (int i = 0; i < 8; i++) acc[tm] = fmaf(w[j][i], xv[tm][j][i], acc[tm]);
     }
 #pragma unroll
-    for (int tm = 0; tm < TM; tm++)
-        if (tm < nt) acc[tm] = wave_sum(acc[tm]);
+    for (int tm = 0; tm < TM; tm++) acc[tm] = tm < nt ? wave_sum(acc[tm]) : 0.f;
 }
 
 // logits[t][e] = scale[t] * sum_i x[t][i] * router[e][i].  One wave per
 // (expert, group of TM tokens).
-constexpr int kRouterTM = 8;
+constexpr int kRouterTM = 4;
 
 template <int XDT, int RDT>
 __global__ __launch_bounds__(64) void k_router_gemv(const void *x, const void *router,
@@ -115,7 +117,7 @@ __global__ __launch_bounds__(64) void k_router_gemv(const void *x, const void *r
     const int nt = min(kRouterTM, M - t0);
     const char *wrow = reinterpret_cast<const char *>(router) + (size_t)e * H * dt_bytes<RDT>();
     float acc[kRouterTM];
-    router_dots<XDT, RDT, kRouterTM>(x, wrow, H, t0, nt, lane, acc);
+    router_dots<XDT, RDT, kRouterTM, 2>(x, wrow, H, t0, nt, lane, acc);
 #pragma unroll
     for (int tm = 0; tm < kRouterTM; tm++) {
         if (tm < nt && lane == 0) {
@@ -352,13 +354,14 @@ hipError_t launch_plan_from_offsets(int E, int tile_rows, const int32_t *offsets
     return hipGetLastError();
 }
 
-// ----------------------------------------------------- fused small-batch route
-// Workgroup e computes expert e's logits for all M <= kSmallM tokens (its
-// waves split the row; partial dots meet in LDS) and stores them; then it
-// takes a ticket.  The workgroup
-// holding the last ticket sees every logit (release/acquire at agent scope
-// around the ticket), runs the top-k of every token and the permutation, and
-// returns the ticket counter to zero for the next call.
+// ----------------------------------------------------- small-batch route
+// Two launches for M <= kSmallM tokens.  The router kernel: workgroup (e, g)
+// computes expert e's logits for tokens 4g..4g+3 (its waves split the row;
+// partial dots meet in LDS).  Then one workgroup loads every logit into LDS
+// with one round of loads, runs each token's top-k (one wave per token) and
+// the permutation.  (Handing over inside one kernel instead, the last
+// workgroup to take a ticket after a device-scope release doing the select,
+// measured about 6 us slower with 128 workgroups than the second launch.)
 constexpr int kSmallM = 16;
 
 struct RouteSmallArgs {
@@ -369,148 +372,122 @@ struct RouteSmallArgs {
     int32_t *ids;
     float *w;
     PermuteOut o;
-    uint32_t *ticket;
 };
 
 constexpr int kRouteWaves = 4;
-constexpr int kSmallRoutes = 2 * kWave; // routes the one-wave permutation handles
+constexpr int kRouteTM = 4;    // tokens per workgroup
+constexpr int kSmallRoutes = kSmallM * 8; // routes of a small batch (top_k <= 8)
 
-// Exclusive prefix over the 64 lanes of a wave (shuffle scan); total in *tot.
-__device__ __forceinline__ int wave_excl_scan(int v, int lane, int *tot) {
-    int x = v;
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-        const int y = __shfl_up(x, off);
-        if (lane >= off) x += y;
-    }
-    *tot = __shfl(x, kWave - 1);
-    return x - v;
-}
-
-// Stable counting sort of R <= 128 routes by expert, by one wave, from ids in
-// LDS.  Lane l owns routes l and l+64 and experts l, l+64, l+128, l+192.  A
-// route's place is the number of routes with a smaller expert id plus the
-// number of earlier routes with the same id.
-__device__ void permute_wave(const int *s_ids, int R, int E, int lane, const PermuteOut &o) {
-    const int r0 = lane, r1 = lane + kWave;
-    const int e0 = r0 < R ? s_ids[r0] : 0x7fffffff;
-    const int e1 = r1 < R ? s_ids[r1] : 0x7fffffff;
-    int pos0 = 0, pos1 = 0;
-    int cnt[kKeysPerLane] = {0, 0, 0, 0};
-    for (int r = 0; r < R; r++) {
-        const int v = s_ids[r];
-        pos0 += (v < e0) || (v == e0 && r < r0);
-        pos1 += (v < e1) || (v == e1 && r < r1);
-#pragma unroll
-        for (int c = 0; c < kKeysPerLane; c++) cnt[c] += v == lane + kWave * c;
-    }
-    if (r0 < R && e0 >= 0 && e0 < E) { o.sorted[pos0] = r0; o.route_pos[r0] = pos0; }
-    if (r1 < R && e1 >= 0 && e1 < E) { o.sorted[pos1] = r1; o.route_pos[r1] = pos1; }
-    int base = 0, abase = 0;
-#pragma unroll
-    for (int c = 0; c < kKeysPerLane; c++) {
-        const int e = lane + kWave * c;
-        const int n = e < E ? cnt[c] : 0;
-        int tot, atot;
-        const int ex = wave_excl_scan(n, lane, &tot);
-        const int aex = wave_excl_scan(n > 0 ? 1 : 0, lane, &atot);
-        if (e < E) {
-            o.counts[e] = n;
-            o.offsets[e] = base + ex;
-            if (n > 0) o.active[1 + abase + aex] = e;
-        }
-        base += tot;
-        abase += atot;
-    }
-    if (lane == 0) {
-        o.offsets[E] = base;
-        o.active[0] = abase;
-    }
-}
-
-template <int XDT, int RDT, bool TAIL>
-__global__ __launch_bounds__(kRouteWaves * kWave) void k_route_small(RouteSmallArgs a) {
-    __shared__ float s_part[kRouteWaves][kSmallM];
-    __shared__ int s_ids[kSmallRoutes];
-    __shared__ int last;
+template <int XDT, int RDT>
+__global__ __launch_bounds__(kRouteWaves * kWave) void k_router_small(RouteSmallArgs a) {
+    __shared__ float s_part[kRouteWaves][kRouteTM];
     const int wave = uniform(threadIdx.x >> 6), lane = threadIdx.x & 63;
-    // workgroup e computes expert e's logits; wave w takes a quarter of the row
-    const int e = blockIdx.x;
+    const int e = blockIdx.x, t0 = blockIdx.y * kRouteTM;
+    const int nt = min(kRouteTM, a.M - t0);
     const int nch = a.H / 8;
     const int cb = wave * nch / kRouteWaves, ce = (wave + 1) * nch / kRouteWaves;
     const char *wrow = reinterpret_cast<const char *>(a.router) + (size_t)e * a.H * dt_bytes<RDT>();
-    for (int t0 = 0; t0 < a.M; t0 += 8) {
-        float acc[8];
-        const int nt = min(8, a.M - t0);
-        router_dots<XDT, RDT, 8>(a.x, wrow, a.H, t0, nt, lane, acc, cb, ce);
+    float acc[kRouteTM];
+    router_dots<XDT, RDT, kRouteTM, 2>(a.x, wrow, a.H, t0, nt, lane, acc, cb, ce);
+    if (lane == 0)
 #pragma unroll
-        for (int tm = 0; tm < 8; tm++)
-            if (tm < nt && lane == 0) s_part[wave][t0 + tm] = acc[tm];
-    }
+        for (int tm = 0; tm < kRouteTM; tm++) s_part[wave][tm] = acc[tm];
     __syncthreads();
-    if (threadIdx.x < a.M) {
-        const int t = threadIdx.x;
+    if (threadIdx.x < nt) {
+        const int t = t0 + threadIdx.x;
         float v = 0.f;
 #pragma unroll
-        for (int w = 0; w < kRouteWaves; w++) v += s_part[w][t];
+        for (int w = 0; w < kRouteWaves; w++) v += s_part[w][threadIdx.x];
         if (a.tok_scale) v *= a.tok_scale[t];
         a.logits[(size_t)t * a.E + e] = v;
     }
-    if constexpr (!TAIL) return;
-    __threadfence();
+}
+
+// One wave per token for the top-k, then one thread per route for its place
+// (routes of smaller experts, then earlier routes of the same expert: a
+// stable counting sort) and one thread per expert for its count; offsets and
+// the touched-expert list are block scans of the counts.
+constexpr int kSelWaves = kSmallM;
+
+__global__ __launch_bounds__(kSelWaves * kWave) void k_select_small(RouteSmallArgs a) {
+    __shared__ int s_ids[kSmallRoutes];
+    __shared__ float s_logit[kSmallM * kMaxE];
+    __shared__ float s_bias[kMaxE];
+    __shared__ int s_scan[4];
+    const int tid = threadIdx.x, wave = uniform(tid >> 6), lane = tid & 63;
+    const int R = a.M * a.k;
+    for (int i = tid; i < a.M * a.E; i += kSelWaves * kWave) s_logit[i] = a.logits[i];
+    if (a.bias)
+        for (int i = tid; i < a.E; i += kSelWaves * kWave) s_bias[i] = a.bias[i];
     __syncthreads();
-    if (threadIdx.x == 0) last = atomicAdd(a.ticket, 1u) == gridDim.x - 1;
+    if (wave < a.M)
+        topk_wave(s_logit + wave * a.E, a.bias ? s_bias : nullptr, a.E, a.k, a.select, a.bias_mode, lane,
+                  a.ids + (size_t)wave * a.k, a.w + (size_t)wave * a.k, s_ids + wave * a.k);
     __syncthreads();
-    if (!last) return;
-    __threadfence();
-    for (int t = wave; t < a.M; t += kRouteWaves)
-        topk_wave(a.logits + (size_t)t * a.E, a.bias, a.E, a.k, a.select, a.bias_mode, lane,
-                  a.ids + (size_t)t * a.k, a.w + (size_t)t * a.k, s_ids + t * a.k);
-    __syncthreads();
-    if (wave == 0) permute_wave(s_ids, a.M * a.k, a.E, lane, a.o);
-    if (threadIdx.x == 0) {
-        __threadfence();
-        atomicExch(a.ticket, 0u);
+    if (tid < R) {
+        const int e = s_ids[tid];
+        int pos = 0;
+        for (int r = 0; r < R; r++) {
+            const int v = s_ids[r];
+            pos += (v < e) || (v == e && r < tid);
+        }
+        a.o.sorted[pos] = tid;
+        a.o.route_pos[tid] = pos;
+    }
+    int cnt = 0;
+    if (tid < a.E)
+        for (int r = 0; r < R; r++) cnt += s_ids[r] == tid;
+    int tot, atot;
+    const int off = block_scan_256(tid < a.E ? cnt : 0, s_scan, &tot);
+    const int aoff = block_scan_256(tid < a.E && cnt > 0 ? 1 : 0, s_scan, &atot);
+    if (tid < a.E) {
+        a.o.counts[tid] = cnt;
+        a.o.offsets[tid] = off;
+        if (cnt > 0) a.o.active[1 + aoff] = tid;
+    }
+    if (tid == 0) {
+        a.o.offsets[a.E] = tot;
+        a.o.active[0] = atot;
     }
 }
 
 int route_small_max_tokens() { return kSmallM; }
 
-template <bool TAIL>
-static void route_small_dispatch(const Layer &L, const RouteSmallArgs &a, hipStream_t s) {
-    const dim3 grid(L.E), block(kRouteWaves * kWave);
+static void router_small_dispatch(const Layer &L, const RouteSmallArgs &a, hipStream_t s) {
+    const dim3 grid(L.E, (a.M + kRouteTM - 1) / kRouteTM), block(kRouteWaves * kWave);
     if (L.xdt == DT_BF16 && L.rdt == DT_BF16)
-        launch_kernel((k_route_small<DT_BF16, DT_BF16, TAIL>), grid, block, 0, s, a);
+        launch_kernel((k_router_small<DT_BF16, DT_BF16>), grid, block, 0, s, a);
     else if (L.xdt == DT_BF16)
-        launch_kernel((k_route_small<DT_BF16, DT_F32, TAIL>), grid, block, 0, s, a);
+        launch_kernel((k_router_small<DT_BF16, DT_F32>), grid, block, 0, s, a);
     else if (L.rdt == DT_BF16)
-        launch_kernel((k_route_small<DT_F32, DT_BF16, TAIL>), grid, block, 0, s, a);
+        launch_kernel((k_router_small<DT_F32, DT_BF16>), grid, block, 0, s, a);
     else
-        launch_kernel((k_route_small<DT_F32, DT_F32, TAIL>), grid, block, 0, s, a);
+        launch_kernel((k_router_small<DT_F32, DT_F32>), grid, block, 0, s, a);
 }
 
 hipError_t launch_route_small(const Layer &L, const void *x, const void *router, const float *bias,
                               const float *tok_scale, int M, float *logits, int32_t *ids, float *w,
                               int32_t *counts, int32_t *offsets, int32_t *sorted, int32_t *route_pos,
-                              int32_t *active, uint32_t *ticket, hipStream_t s) {
-    if (M > kSmallM) return hipErrorInvalidValue;
-    RouteSmallArgs a{x, router, L.bias_mode ? bias : nullptr, tok_scale, M, L.H, L.E, L.k, L.select,
-                     L.bias_mode, logits, ids, w,
-                     PermuteOut{counts, offsets, sorted, route_pos, active, nullptr, 1}, ticket};
-    route_small_dispatch<true>(L, a, s);
+                              int32_t *active, hipStream_t s) {
+    if (M > kSmallM || M * L.k > kSmallRoutes) return hipErrorInvalidValue;
+    const RouteSmallArgs a{x, router, L.bias_mode ? bias : nullptr, tok_scale, M, L.H, L.E, L.k, L.select,
+                           L.bias_mode, logits, ids, w,
+                           PermuteOut{counts, offsets, sorted, route_pos, active, nullptr, 1}};
+    router_small_dispatch(L, a, s);
+    launch_kernel(k_select_small, dim3(1), dim3(kSelWaves * kWave), 0, s, a);
     return hipGetLastError();
 }
 
 hipError_t launch_router_small(const Layer &L, const void *x, const void *router, const float *tok_scale,
                                int M, float *logits, hipStream_t s) {
     if (M > kSmallM) return hipErrorInvalidValue;
-    RouteSmallArgs a{x, router, nullptr, tok_scale, M, L.H, L.E, L.k, L.select, L.bias_mode, logits,
-                     nullptr, nullptr, PermuteOut{}, nullptr};
-    route_small_dispatch<false>(L, a, s);
+    const RouteSmallArgs a{x, router, nullptr, tok_scale, M, L.H, L.E, L.k, L.select, L.bias_mode, logits,
+                           nullptr, nullptr, PermuteOut{}};
+    router_small_dispatch(L, a, s);
     return hipGetLastError();
 }
 
-// Zero `n` 32-bit words (used for the workspace's ticket words).
+// Zero `n` 32-bit words (the workspace's reserved synchronisation words).
 __global__ void k_zero_words(uint32_t *p, int n) {
     const int i = blockIdx.x * 256 + threadIdx.x;
     if (i < n) p[i] = 0u;

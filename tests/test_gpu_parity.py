@@ -177,6 +177,11 @@ SMALL = [
                       bias_mode=BIAS_LOGIT, bias_kind="zipf", rms_eps=1e-6), (65, 130)),
     ("q8-shared-many", dict(hidden=128, num_experts=6, top_k=2, expert_inter=64,
                             shared_inter=96, expert_dtype=Q8_0, shared_dtype=Q8_0), (1, 64, 100)),
+    ("shared-clamp", dict(hidden=320, num_experts=10, top_k=3, expert_inter=128, shared_inter=192,
+                          swiglu_limit=0.05), (1, 7, 33)),
+    ("f32x-q8", dict(hidden=160, num_experts=5, top_k=2, expert_inter=64, x_dtype=F32,
+                     router_dtype=F32, expert_dtype=Q8_0), (1, 2, 12)),
+    ("wide-h", dict(hidden=4608, num_experts=4, top_k=2, expert_inter=64), (1, 3)),
 ]
 
 
@@ -287,7 +292,7 @@ def test_forward_repeatable():
 
 @pytest.mark.parametrize("M,path,want", [
     (1, 0, ["router", "gateup", "down"]),
-    (9, 0, ["router", "gateup", "down"]),
+    (9, 0, ["router", "gateup", "down", "combine"]),
     (128, 2, ["router", "topk", "permute", "gateup", "down", "combine"]),
 ])
 def test_forward_timed_matches_forward(M, path, want):
