@@ -32,7 +32,7 @@ METRIC = "MoE layer tokens/s at M=1/16/2048 + % of HBM / MFMA roofline"
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFS = 2500.0
 # gate/up + SwiGLU kernel of each moe_forward path (the layer's dominant kernel)
-GATEUP_KERNEL = {"single": "k_gateup_m1", "gemv": "k_gateup_gemv", "mfma": "k_gemm<0"}
+GATEUP_KERNEL = {"single": "k_gateup_m1", "gemv": "k_gateup_rows", "mfma": "k_gemm<0"}
 
 
 # ------------------------------------------------------------------ workload
@@ -41,7 +41,10 @@ def bytes_per_weight(dtype: int) -> float:
 
 
 def algorithmic_bytes(spec, M: int, counts: np.ndarray) -> dict:
-    """Bytes the layer must move per call (weights of touched experts once)."""
+    """Bytes the layer must move per call (weights of touched experts once).
+
+    `gateup_kernel` is what the gate/up kernel itself must move: the touched
+    experts' gate and up rows, x and act."""
     H, E, I, Is = spec.hidden, spec.num_experts, spec.expert_inter, spec.shared_inter
     T = int((counts > 0).sum())
     bpw = bytes_per_weight(spec.expert_dtype)
@@ -51,8 +54,8 @@ def algorithmic_bytes(spec, M: int, counts: np.ndarray) -> dict:
     down = T * H * I * bpw + (H * Is * bytes_per_weight(spec.shared_dtype) if Is else 0)
     router = H * E * bytes_per_weight(spec.router_dtype) + (4 * E if spec.bias_mode else 0)
     layer = gate_up + down + router + M * H * bpx + 4 * M * H
-    return {"layer": layer, "gateup_kernel": gate_up + M * H * bpx + 4 * (R * I + M * Is),
-            "touched": T}
+    gk = gate_up + M * H * bpx + 4 * (R * I + M * Is)
+    return {"layer": layer, "gateup_kernel": gk, "touched": T}
 
 
 def algorithmic_flops(spec, M: int) -> float:
@@ -197,6 +200,7 @@ def main() -> int:
     for i in range(K):
         step(i, counts[i])
     torch.cuda.synchronize()
+    run = m.moe_forward_path(base.plan, M)
     ab = [algorithmic_bytes(spec, M, c.cpu().numpy()) for c in counts]
     layer_bytes_avg = float(np.mean([a["layer"] for a in ab]))
     gateup_bytes_avg = float(np.mean([a["gateup_kernel"] for a in ab]))
@@ -261,7 +265,6 @@ def main() -> int:
     kev.close()
     ev.close()
 
-    run = m.moe_forward_path(base.plan, M)
     kernel = GATEUP_KERNEL[m.MOE_RUN_NAMES[run]]
     tag = f"{spec.name}_M{M}"
     trec = profiling.load_traffic(os.path.join(ROOT, "profiles"), kernel, tag)

@@ -188,6 +188,23 @@ __device__ __forceinline__ void decode_chunk(u32x4 v, float *w) {
     }
 }
 
+// 8 consecutive elements of a row stored as fp32 or bf16, as floats.
+template <int DT>
+__device__ __forceinline__ void load8(const void *row, int c8, float *v) {
+    if constexpr (DT == DT_BF16) {
+        u32x4 q = reinterpret_cast<const u32x4 *>(row)[c8];
+        v[0] = bf16_lo(q.x); v[1] = bf16_hi(q.x); v[2] = bf16_lo(q.y); v[3] = bf16_hi(q.y);
+        v[4] = bf16_lo(q.z); v[5] = bf16_hi(q.z); v[6] = bf16_lo(q.w); v[7] = bf16_hi(q.w);
+    } else {
+        const f32x4 *p = reinterpret_cast<const f32x4 *>(row) + 2 * c8;
+        f32x4 a = p[0], b = p[1];
+        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+        v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    }
+}
+
+template <int DT> constexpr int dt_bytes() { return DT == DT_BF16 ? 2 : 4; }
+
 // Wave-uniform copy of a value the compiler cannot prove uniform.
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 

@@ -640,9 +640,10 @@ hipError_t launch_down_gemv(const Layer &L, const float *act, const float *share
 // gate/up: each wave holds x in registers (lane l owns chunks l, l+64, ...)
 // and streams a contiguous range of (slot, row) pairs, RP pairs at a time,
 // issuing all 2*RP*CPL 16-byte loads of a group before using them.
-// Both kernels run the token's top-k from the router logits in their prologue
-// (one wave's DPP rounds, overlapped with the first loads), so the single-token
-// path needs no routing kernel of its own and no cross-workgroup handoff.
+// The gate/up kernel runs the token's top-k from the router logits in its
+// prologue (every wave, DPP rounds); its first wave writes the picks and their
+// weights, which the down kernel reads.  (Computing the logits inside every
+// gate/up workgroup instead of in a router kernel measured slower.)
 struct M1Route {
     const float *logits, *bias;
     int E, k, select, bias_mode;
@@ -693,23 +694,9 @@ __global__ __launch_bounds__(kThreads) void k_gateup_m1(M1GateUpArgs a) {
     const int p_end = min(a.total_pairs, p_begin + a.pairs_per_wave);
     const int H = a.H, nch = H / N;
     const float sc = a.tok_scale ? a.tok_scale[0] : 1.0f;
-    int my_id, my_rank;
-    float my_w;
-    const M1Slots slots = m1_slots(a.rt, lane, &my_id, &my_w, &my_rank);
-    if (gw == 0) {
-        if (lane < a.k) {
-            a.ids_out[lane] = my_id;
-            a.w_out[lane] = my_w;
-        }
-        if (a.counts_out)
-            for (int e = lane; e < a.rt.E; e += kWave) {
-                int c = 0;
-                for (int u = 0; u < a.k; u++) c += slots.expert(u) == e;
-                a.counts_out[e] = c;
-            }
-    }
-    // x chunks this lane multiplies; lanes past the row end hold zeros and
-    // load (harmless) duplicates of the last chunk.
+    // x chunks this lane multiplies (loaded before the top-k, which does not
+    // need them); lanes past the row end hold zeros and load (harmless)
+    // duplicates of the last chunk.
     int cl[CPL];
     float xr[CPL][N];
 #pragma unroll
@@ -728,6 +715,21 @@ __global__ __launch_bounds__(kThreads) void k_gateup_m1(M1GateUpArgs a) {
                 xr[cc][n4] = q.x * m; xr[cc][n4 + 1] = q.y * m; xr[cc][n4 + 2] = q.z * m; xr[cc][n4 + 3] = q.w * m;
             }
         }
+    }
+    int my_id, my_rank;
+    float my_w;
+    const M1Slots slots = m1_slots(a.rt, lane, &my_id, &my_w, &my_rank);
+    if (gw == 0) {
+        if (lane < a.k) {
+            a.ids_out[lane] = my_id;
+            a.w_out[lane] = my_w;
+        }
+        if (a.counts_out)
+            for (int e = lane; e < a.rt.E; e += kWave) {
+                int c = 0;
+                for (int u = 0; u < a.k; u++) c += slots.expert(u) == e;
+                a.counts_out[e] = c;
+            }
     }
     const int routed_pairs = a.k * a.I;
     const size_t row_bytes = (size_t)H * elem_bytes<WDT>();
@@ -809,7 +811,8 @@ __global__ __launch_bounds__(kThreads) void k_gateup_m1(M1GateUpArgs a) {
     }
 }
 
-// down (M = 1): a workgroup owns kM1Rows output rows; its 256 threads stride
+// down (M = 1): a workgroup reads the k picks and weights the gate/up kernel
+// wrote, then owns kM1Rows output rows; its 256 threads stride
 // over the concatenated chunks of every touched expert's rows (then the
 // shared expert's), kM1Unroll rounds at a time with every load of the rounds
 // issued first.  Each chunk's dot is scaled by its route's weight before the
@@ -821,7 +824,8 @@ constexpr int kMaxSlots = 9; // top-k slots + the shared expert
 struct M1DownArgs {
     const float *act, *shared_act;
     Mats routed, shared;
-    M1Route rt;
+    const int32_t *ids; // [k] picks, written by the gate/up kernel
+    const float *w;     // [k] their weights
     const float *seed;
     int H, I, Is, k;
     float *y;
@@ -841,10 +845,9 @@ __global__ __launch_bounds__(kThreads) void k_down_m1(M1DownArgs a) {
     const int n_routed = a.k; // with M = 1 every slot is a touched expert
     const int nch = a.I / N, nch_s = a.Is / N;
     if (wave == 0) {
-        int my_id, my_rank;
-        float my_w;
-        topk_wave_core(a.rt.logits, a.rt.bias, a.rt.E, a.rt.k, a.rt.select, a.rt.bias_mode, lane, &my_id, &my_w);
-        my_rank = pick_rank(my_id, a.k, lane);
+        const int my_id = a.ids[min(lane, a.k - 1)];
+        const float my_w = a.w[min(lane, a.k - 1)];
+        const int my_rank = pick_rank(my_id, a.k, lane);
         if (lane < n_routed) {
             // slot = rank in ascending expert id, which is the act row of the pick
             const size_t row = (size_t)my_id * H + h0;
@@ -1001,14 +1004,15 @@ hipError_t launch_gateup_m1(const Layer &L, const void *x, const float *tok_scal
 }
 
 hipError_t launch_down_m1(const Layer &L, const float *act, const float *shared_act, const Mats &routed,
-                          const Mats &shared, const float *logits, const float *bias, const float *seed,
+                          const Mats &shared, const int32_t *ids, const float *w, const float *seed,
                           float *y, hipStream_t s) {
     M1DownArgs a;
     a.act = act;
     a.shared_act = shared_act;
     a.routed = routed;
     a.shared = shared;
-    a.rt = m1_route(L, logits, bias);
+    a.ids = ids;
+    a.w = w;
     a.seed = seed;
     a.H = L.H;
     a.I = L.I;

@@ -71,17 +71,19 @@ int down_ksplit(const Layer &L, int M);
 
 // M = 1 decode kernels (x shared by every touched expert).
 bool m1_supported(const Layer &L);
-// Both take the router logits and run the token's top-k in their prologue.
+// Router logits only (M <= route_small_max_tokens()).
+hipError_t launch_router_small(const Layer &L, const void *x, const void *router, const float *tok_scale,
+                               int M, float *logits, hipStream_t s);
+// Top-k from the logits and gate/up in one kernel; writes ids_out / w_out
+// ([k]) and counts_out ([E], may be null).
 hipError_t launch_gateup_m1(const Layer &L, const void *x, const float *tok_scale, const Mats &routed,
                             const Mats &shared, const float *logits, const float *bias, int32_t *ids_out,
                             float *w_out, int32_t *counts_out, float *act, float *shared_act,
                             hipStream_t s);
+// Down projection and combine from the picks and weights the gate/up kernel wrote.
 hipError_t launch_down_m1(const Layer &L, const float *act, const float *shared_act, const Mats &routed,
-                          const Mats &shared, const float *logits, const float *bias, const float *seed,
+                          const Mats &shared, const int32_t *ids, const float *w, const float *seed,
                           float *y, hipStream_t s);
-// Router logits only (M <= route_small_max_tokens()).
-hipError_t launch_router_small(const Layer &L, const void *x, const void *router, const float *tok_scale,
-                               int M, float *logits, hipStream_t s);
 
 // MFMA grouped-GEMM path (bf16 x and experts).
 int mfma_tile_rows();

@@ -411,7 +411,7 @@ static moe_status forward_impl(const moe_plan *p, const void *x, const moe_weigh
     const bool mfma = use_mfma(p, M);
     const bool single = M == 1 && !mfma && moe::m1_supported(L);
     if (single) {
-        // one token: the expert kernels run the top-k themselves from the logits
+        // one token: the gate/up kernel runs the top-k itself from the logits
         STAGE(rec, moe::launch_router_small(L, x, wts->router, sc, M, lg, s), "router", MOE_STAGE_ROUTER);
     } else if (M <= moe::route_small_max_tokens() && !mfma) {
         STAGE(rec, moe::launch_route_small(L, x, wts->router, wts->bias, sc, M, lg, ids, w, counts, offsets,
@@ -444,9 +444,8 @@ static moe_status forward_impl(const moe_plan *p, const void *x, const moe_weigh
     } else if (single) {
         STAGE(rec, moe::launch_gateup_m1(L, x, sc, routed_mats(wts), shared_mats(wts), lg, wts->bias, ids, w,
                                          counts_out, act, sact, s),
-              "gate/up", MOE_STAGE_GATEUP);
-        STAGE(rec, moe::launch_down_m1(L, act, sact, routed_mats(wts), shared_mats(wts), lg, wts->bias, nullptr,
-                                       y, s),
+              "top-k + gate/up", MOE_STAGE_GATEUP);
+        STAGE(rec, moe::launch_down_m1(L, act, sact, routed_mats(wts), shared_mats(wts), ids, w, nullptr, y, s),
               "down + combine", MOE_STAGE_DOWN);
     } else {
         STAGE(rec, moe::launch_gateup_gemv(L, x, sc, routed_mats(wts), shared_mats(wts), rt, M, act, sact, s),
