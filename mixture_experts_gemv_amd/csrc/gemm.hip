@@ -2,7 +2,7 @@
 // accumulate), for batches large enough that every touched expert sees many
 // tokens: the per-expert products are then real dense contractions.
 //
-// One kernel template, four uses:
+// Uses:
 //   gate/up  A = gathered token rows of x, B = gate and up rows of the tile's
 //            expert, epilogue silu(clamp(g)) * clamp(v) -> act (fp32);
 //   down     A = act rows (fp32, split into bf16 hi + lo so the product keeps
@@ -13,11 +13,18 @@
 // Tiles: kBM = 128 rows (tokens or routes of one expert, so that most
 // experts' tokens share one pass over the weights) x 128 (gate/up: 32 columns
 // of gate and of up per wave) or 256 (down: 64 columns per wave) output
-// columns, kBK = 64 reduction elements per step.  Four waves each own all
-// 128 rows of their columns and issue v_mfma_f32_32x32x16_bf16.  The A tile
-// is gathered into LDS (double buffered, rows padded against bank
-// conflicts); B fragments are loaded from HBM straight into registers in the
-// MFMA operand layout, one step ahead.
+// columns.  Four waves each own all 128 rows of their columns and issue
+// v_mfma_f32_32x32x16_bf16.
+//
+// Two kernels:
+//   k_gemm_lds (bf16 A: gate/up)  both operands go global -> LDS with
+//     asynchronous 16-byte copies (global_load_lds_dwordx4) in a 3-stage
+//     pipeline, 64 reduction elements a stage, XOR-swizzled rows;
+//   k_gemm_reg (fp32 A: down)  A is staged through registers into LDS
+//     (double buffered, split into bf16 hi/lo once as it is written), B
+//     fragments are loaded straight into registers, one step ahead.
+// (The asynchronous-copy form with fp32 A measured slower: every wave then
+// splits the whole A tile into hi/lo itself.)
 #include "common.h"
 #include "launch.h"
 
@@ -28,8 +35,8 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kMB = 4;              // 32-row blocks per wave
 constexpr int kBM = 32 * kMB;       // rows per tile
-constexpr int kBK = 64;
-constexpr int kLdsRow = kBK + 8;    // bf16 elements per LDS row (144 bytes)
+constexpr int kBK = 64;            // reduction granularity of K (both kernels need K % 64 == 0)
+constexpr int kLdsRow = kBK + 8;   // bf16 elements per padded LDS row of the register-staged kernel
 constexpr int kGW = 4;
 constexpr int kGThreads = kGW * kWave;
 
@@ -65,8 +72,243 @@ struct GemmShape {
     static constexpr int COLS = kGW * WCOLS;                      // output columns per tile
 };
 
+// Reduction elements per pipeline stage and number of LDS stages of the
+// asynchronous-copy kernel (48 KB a stage: 16 KB of A, 32 KB of B).
+constexpr int kStageK = 64;
+constexpr int kStages = 3;
+
+typedef __attribute__((address_space(3))) void *lds_ptr;
+
+// 16-byte LDS read issued as inline assembly: the compiler cannot see that it
+// reads LDS, so it does not wait for every outstanding global->LDS copy
+// before it (it cannot tell which stage a copy writes).  The caller waits for
+// the results with lds_wait.
+__device__ __forceinline__ u32x4 lds_load16(const unsigned char *p) {
+    u32x4 r;
+    const uint32_t addr = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const unsigned char *)p;
+    asm volatile("ds_read_b128 %0, %1" : "=v"(r) : "v"(addr));
+    return r;
+}
+
+// Wait for this lane's LDS reads; the values pass through the statements so
+// that nothing using them is scheduled before the wait.
+template <int N>
+__device__ __forceinline__ void lds_wait(u32x4 (&v)[N]) {
+    asm volatile("s_waitcnt lgkmcnt(0)");
+#pragma unroll
+    for (int i = 0; i < N; i++) asm volatile("" : "+v"(v[i]));
+}
+
+// Asynchronous 16-byte copy global -> LDS for each lane: lane i writes LDS
+// bytes l + 16*i (l wave-uniform).  Completion is tracked by vmcnt.
+__device__ __forceinline__ void copy16_lds(const void *g, unsigned char *l) {
+    __builtin_amdgcn_global_load_lds(g, (lds_ptr)l, 16, 0, 0);
+}
+
+// s_waitcnt immediate (gfx9 encoding) that waits for at most n outstanding
+// vector memory operations and for nothing else.
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+template <int KIND>
+__global__ __launch_bounds__(kGThreads, 1) void k_gemm_lds(GemmArgs a) {
+    constexpr int NB = GemmShape<KIND>::NB;
+    constexpr int WCOLS = GemmShape<KIND>::WCOLS;
+    constexpr int BK = kStageK;                    // reduction elements per stage
+    constexpr int NST = kStages;                   // LDS stages
+    constexpr int ARB = BK * 2;                    // A bytes per row per stage
+    constexpr int BRB = BK * 2;                    // B bytes per column per stage
+    constexpr int BCH = BRB / 16;                  // 16-byte chunks per B column per stage
+    constexpr int WBC = 64;                        // B columns per wave (gate/up: 32 gate + 32 up)
+    constexpr int A_BYTES = kBM * ARB;
+    constexpr int WB_BYTES = WBC * BRB;            // one wave's B per stage
+    constexpr int ST_BYTES = A_BYTES + kGW * WB_BYTES;
+    constexpr int A_DMA = kBM * ARB / (kWave * 16) / kGW; // A copies per wave per stage (each 1 KB)
+    constexpr int B_DMA = WB_BYTES / (kWave * 16);        // B copies per wave per stage
+    constexpr int LPS = A_DMA + B_DMA;             // copies per lane per stage
+    // one LDS array per stage: the compiler's wait tracking can then tell the
+    // copies into one stage from the operand reads of another
+    __shared__ __attribute__((aligned(16))) unsigned char sm0[ST_BYTES], sm1[ST_BYTES], sm2[ST_BYTES];
+    __shared__ __attribute__((aligned(16))) unsigned char sm3[NST > 3 ? ST_BYTES : 16];
+    __shared__ const char *s_src[kBM];
+    __shared__ int s_tok[kBM];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = uniform(tid >> 6);
+
+    // ---- which tile, column block and reduction slice.  The workgroups of
+    // one expert cover its column units c = (slice, column block) for every
+    // token tile tl; the token tiles of a unit go to one XCD (equal g mod 8)
+    // one after another, so the unit's weights are read from HBM about once
+    // and then served by that XCD's L2.
+    const int g = blockIdx.x;
+    const int per_tile = a.n_ntiles * a.ksplit;
+    const int per_pad = (per_tile + 7) / 8 * 8;
+    int e = 0, ts, Te, p0, nrows;
+    if (a.tiles) {
+        const int q = g / per_pad;
+        if (q >= a.tiles[0]) return;
+        const int32_t *pairs = a.tiles + 2 + a.E;
+        e = pairs[2 * q];
+        ts = a.tiles[1 + e];
+        Te = a.tiles[2 + e] - ts;
+    } else {
+        ts = 0;
+        Te = (a.M + kBM - 1) / kBM;
+        if (g >= Te * per_pad) return;
+    }
+    const int local = g - ts * per_pad;
+    const int grp = local / (8 * Te), r8 = local - grp * 8 * Te;
+    const int tl = r8 >> 3, cu = grp * 8 + (r8 & 7);
+    if (cu >= per_tile) return;
+    const int ks = cu / a.n_ntiles, nt = cu - ks * a.n_ntiles;
+    if (a.tiles) {
+        p0 = a.tiles[2 + a.E + 2 * (ts + tl) + 1];
+        nrows = min(kBM, a.offsets[e + 1] - p0);
+    } else {
+        p0 = tl * kBM;
+        nrows = min(kBM, a.M - p0);
+    }
+    if (tid < kBM) {
+        const int p = p0 + min(tid, nrows - 1);
+        const int t = a.sorted ? a.sorted[p] / a.k_route : p;
+        s_src[tid] = reinterpret_cast<const char *>(a.a) + (size_t)t * a.K * 2;
+        s_tok[tid] = t;
+    }
+    __syncthreads();
+
+    const int K = a.K, N = a.N, NKS = K / BK;
+    const int kb = ks * NKS / a.ksplit, nk = (ks + 1) * NKS / a.ksplit - kb; // this slice's stages
+    const int colw = nt * GemmShape<KIND>::COLS + wave * WCOLS;
+    const bool wave_on = colw < N;
+
+    // ---- copy sources.  A copy of 1 KB fills 8 LDS rows of 128 bytes (A)
+    // or 64 / BCH B columns; lane i writes LDS bytes i*16..i*16+15, which hold
+    // logical 16-byte chunk (slot ^ row) of its row: an XOR swizzle that keeps
+    // the MFMA operand reads below free of most bank conflicts.
+    const char *asrc[A_DMA];
+#pragma unroll
+    for (int q = 0; q < A_DMA; q++) {
+        const int r = (wave * A_DMA + q) * 8 + (lane >> 3), c = (lane & 7) ^ (r & 7);
+        asrc[q] = s_src[r] + c * 16;
+    }
+    const char *bsrc[B_DMA];
+#pragma unroll
+    for (int q = 0; q < B_DMA; q++) {
+        const int cl = q * (kWave / BCH) + lane / BCH, c = (lane % BCH) ^ (cl % BCH);
+        const uint16_t *mat = (KIND == GK_GATEUP && cl >= 32) ? a.b1 : a.b0;
+        const int col = KIND == GK_GATEUP ? colw + (cl & 31) : colw + cl;
+        bsrc[q] = reinterpret_cast<const char *>(mat + (size_t)e * a.b_stride + (size_t)min(col, N - 1) * K) + c * 16;
+    }
+    auto issue = [&](int kt, unsigned char *st) {
+        const size_t ka = (size_t)(kb + kt) * ARB, kbb = (size_t)(kb + kt) * BRB;
+#pragma unroll
+        for (int q = 0; q < A_DMA; q++)
+            copy16_lds(asrc[q] + ka, st + (wave * A_DMA + q) * 1024);
+#pragma unroll
+        for (int q = 0; q < B_DMA; q++)
+            copy16_lds(bsrc[q] + kbb, st + A_BYTES + wave * WB_BYTES + q * 1024);
+    };
+
+    f32x16 acc[kMB][NB];
+#pragma unroll
+    for (int mb = 0; mb < kMB; mb++)
+#pragma unroll
+        for (int nb = 0; nb < NB; nb++)
+#pragma unroll
+            for (int r = 0; r < 16; r++) acc[mb][nb][r] = 0.f;
+
+    auto compute = [&](const unsigned char *st) {
+        const unsigned char *bw = st + A_BYTES + wave * WB_BYTES;
+#pragma unroll
+        for (int s = 0; s < BK / 16; s++) {
+            // every read of the substep first, one wait, then the MFMAs
+            u32x4 v[NB + kMB];
+#pragma unroll
+            for (int nb = 0; nb < NB; nb++) {
+                const int cl = nb * 32 + (lane & 31), c = 2 * s + (lane >> 5);
+                v[nb] = lds_load16(bw + cl * BRB + ((c ^ (cl % BCH)) * 16));
+            }
+#pragma unroll
+            for (int mb = 0; mb < kMB; mb++) {
+                const int r = mb * 32 + (lane & 31), c = 2 * s + (lane >> 5);
+                v[NB + mb] = lds_load16(st + r * ARB + ((c ^ (r & 7)) * 16));
+            }
+            lds_wait(v);
+#pragma unroll
+            for (int mb = 0; mb < kMB; mb++)
+#pragma unroll
+                for (int nb = 0; nb < NB; nb++)
+                    acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, v[NB + mb]),
+                                                                          __builtin_bit_cast(bf16x8, v[nb]),
+                                                                          acc[mb][nb], 0, 0, 0);
+        }
+    };
+
+    // ---- NST-stage pipeline: stage kt is computed while stages kt+1 ..
+    // kt+NST-1 are in flight.  The copies write LDS asynchronously: each lane
+    // waits (vmcnt) until its copies of stage kt have landed, then the
+    // workgroup barrier makes every lane's copies visible.
+    // stage kt lives in buffer kt % NST; the buffers are named explicitly in
+    // an NST-way unrolled loop
+    auto step = [&](int kt, const unsigned char *cur, unsigned char *nxt) {
+        const int ahead = min(nk, kt + NST - 1) - (kt + 1); // stages issued after kt
+        if (ahead >= 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * LPS));
+        else if (ahead == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(LPS));
+        else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        __builtin_amdgcn_s_barrier();
+        if (kt + NST - 1 < nk) issue(kt + NST - 1, nxt);
+        if (wave_on) compute(cur);
+    };
+    if (nk > 0) issue(0, sm0);
+    if (nk > 1) issue(1, sm1);
+    if constexpr (NST == 3) {
+        for (int k0 = 0; k0 < nk; k0 += 3) {
+            step(k0, sm0, sm2);
+            if (k0 + 1 < nk) step(k0 + 1, sm1, sm0);
+            if (k0 + 2 < nk) step(k0 + 2, sm2, sm1);
+        }
+    } else {
+        if (nk > 2) issue(2, sm2);
+        for (int k0 = 0; k0 < nk; k0 += 4) {
+            step(k0, sm0, sm3);
+            if (k0 + 1 < nk) step(k0 + 1, sm1, sm0);
+            if (k0 + 2 < nk) step(k0 + 2, sm2, sm1);
+            if (k0 + 3 < nk) step(k0 + 3, sm3, sm2);
+        }
+    }
+    if (!wave_on) return;
+
+    // ---- epilogue
+#pragma unroll
+    for (int mb = 0; mb < kMB; mb++) {
+#pragma unroll
+        for (int r = 0; r < 16; r++) {
+            const int m = mb * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+            if (m >= nrows) continue;
+            const float sc = a.tok_scale ? a.tok_scale[s_tok[m]] : 1.0f;
+            float *orow = a.out + ks * a.slab + (size_t)(p0 + m) * a.ldo;
+            if constexpr (KIND == GK_GATEUP) {
+                const int i = colw + (lane & 31);
+                if (i < N) {
+                    float gv = acc[mb][0][r] * sc, uv = acc[mb][1][r] * sc;
+                    if (a.limit > 0.f) {
+                        gv = clampf(gv, a.limit);
+                        uv = clampf(uv, a.limit);
+                    }
+                    orow[i] = silu_mul(gv, uv);
+                }
+            } else {
+#pragma unroll
+                for (int nb = 0; nb < NB; nb++) {
+                    const int n = colw + nb * 32 + (lane & 31);
+                    if (n < N) orow[n] = acc[mb][nb][r] * sc;
+                }
+            }
+        }
+    }
+}
+
 template <int KIND, bool A_F32>
-__global__ __launch_bounds__(kGThreads, 2) void k_gemm(GemmArgs a) {
+__global__ __launch_bounds__(kGThreads, 2) void k_gemm_reg(GemmArgs a) {
     constexpr int NS = A_F32 ? 2 : 1;      // bf16 planes of A (hi, lo)
     constexpr int NB = GemmShape<KIND>::NB;
     constexpr int WCOLS = GemmShape<KIND>::WCOLS;
@@ -260,15 +502,20 @@ static hipError_t run_gemm(int kind, bool a_f32, GemmArgs &a, hipStream_t s) {
     const int cols = kind == GK_GATEUP ? GemmShape<GK_GATEUP>::COLS : GemmShape<GK_PLAIN>::COLS;
     a.n_ntiles = (a.N + cols - 1) / cols;
     if (a.ksplit < 1) a.ksplit = 1;
-    const long blocks = (long)a.max_tiles * a.n_ntiles * a.ksplit;
-    if (blocks == 0) return hipSuccess;
-    const unsigned grid = (unsigned)((blocks + 7) / 8 * 8);
-    if (kind == GK_GATEUP)
-        launch_kernel((k_gemm<GK_GATEUP, false>), dim3(grid), dim3(kGThreads), 0, s, a);
-    else if (a_f32)
-        launch_kernel((k_gemm<GK_PLAIN, true>), dim3(grid), dim3(kGThreads), 0, s, a);
-    else
-        launch_kernel((k_gemm<GK_PLAIN, false>), dim3(grid), dim3(kGThreads), 0, s, a);
+    const int per_tile = a.n_ntiles * a.ksplit;
+    if ((long)a.max_tiles * per_tile == 0) return hipSuccess;
+    if (a_f32) {
+        // fp32 A (the down projection's act): register-staged kernel, A split
+        // into bf16 hi/lo once per workgroup as it is written to LDS
+        const unsigned grid = (unsigned)(((long)a.max_tiles * per_tile + 7) / 8 * 8);
+        launch_kernel((k_gemm_reg<GK_PLAIN, true>), dim3(grid), dim3(kGThreads), 0, s, a);
+    } else {
+        const unsigned grid = (unsigned)((long)a.max_tiles * ((per_tile + 7) / 8 * 8));
+        if (kind == GK_GATEUP)
+            launch_kernel((k_gemm_lds<GK_GATEUP>), dim3(grid), dim3(kGThreads), 0, s, a);
+        else
+            launch_kernel((k_gemm_lds<GK_PLAIN>), dim3(grid), dim3(kGThreads), 0, s, a);
+    }
     return hipGetLastError();
 }
 
