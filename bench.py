@@ -32,7 +32,7 @@ METRIC = "MoE layer tokens/s at M=1/16/2048 + % of HBM / MFMA roofline"
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFS = 2500.0
 # gate/up + SwiGLU kernel of each moe_forward path (the layer's dominant kernel)
-GATEUP_KERNEL = {"single": "k_gateup_m1", "gemv": "k_gateup_rows", "mfma": "k_gemm<0"}
+GATEUP_KERNEL = {"single": "k_gateup_m1", "gemv": "k_gateup_rows", "mfma": "k_gemm_lds<0"}
 
 
 # ------------------------------------------------------------------ workload
