@@ -4,9 +4,10 @@
 //
 // Uses:
 //   gate/up  A = gathered token rows of x, B = gate and up rows of the tile's
-//            expert, epilogue silu(clamp(g)) * clamp(v) -> act (fp32);
-//   down     A = act rows (fp32, split into bf16 hi + lo so the product keeps
-//            about 16 bits of act), B = down rows -> per-route outputs;
+//            expert, epilogue silu(clamp(g)) * clamp(v) -> act, written as
+//            fp32 or, inside the layer, as split bf16 hi/lo pairs;
+//   down     A = act rows carried as bf16 hi + lo (so the product keeps about
+//            16 bits of act), B = down rows -> per-route outputs;
 //   shared   the same two with identity rows (all tokens), for a shared expert.
 // (The router has its own small-tile kernel at the end of this file.)
 //
@@ -17,14 +18,17 @@
 // v_mfma_f32_32x32x16_bf16.
 //
 // Two kernels:
-//   k_gemm_lds (bf16 A: gate/up)  both operands go global -> LDS with
-//     asynchronous 16-byte copies (global_load_lds_dwordx4) in a 3-stage
-//     pipeline, 64 reduction elements a stage, XOR-swizzled rows;
-//   k_gemm_reg (fp32 A: down)  A is staged through registers into LDS
-//     (double buffered, split into bf16 hi/lo once as it is written), B
-//     fragments are loaded straight into registers, one step ahead.
-// (The asynchronous-copy form with fp32 A measured slower: every wave then
-// splits the whole A tile into hi/lo itself.)
+//   k_gemm_lds  both operands go global -> LDS with asynchronous 16-byte
+//     copies (global_load_lds_dwordx4) in a 3-stage pipeline, XOR-swizzled
+//     rows; 64 reduction elements a stage for bf16 A, 32 for split A (whose
+//     stage rows hold hi and lo chunks, and whose MFMAs run once per half);
+//   k_gemm_reg (fp32 A handed in by a caller of the stage-wise entry points)
+//     A is staged through registers into LDS (double buffered, split into
+//     hi/lo once as it is written), B fragments are loaded straight into
+//     registers, one step ahead.
+// (Rounding act to a single bf16 instead measured about 1.5x faster in the
+// down GEMM, but at an output error of about 1.6e-3 relative L2 against
+// about 2.5e-6 with the split.)
 #include "common.h"
 #include "launch.h"
 
@@ -60,8 +64,9 @@ struct GemmArgs {
     int N, K;
     const float *tok_scale;  // per-token scale of the products (pre-norm), or null
     float limit;             // gate/up clamp (0 = off)
-    float *out;              // fp32 [rows][ldo]
+    float *out;              // fp32 [rows][ldo]; gate/up with out_split: hi/lo bf16 rows (below)
     int ldo;
+    int out_split;           // gate/up: write act as interleaved bf16 hi/lo (the split A of down)
     int n_ntiles;            // column tiles
 };
 
@@ -72,8 +77,9 @@ struct GemmShape {
     static constexpr int COLS = kGW * WCOLS;                      // output columns per tile
 };
 
-// Reduction elements per pipeline stage and number of LDS stages of the
-// asynchronous-copy kernel (48 KB a stage: 16 KB of A, 32 KB of B).
+// Reduction elements per pipeline stage (bf16 A; half that for split A) and
+// number of LDS stages of the asynchronous-copy kernel.  A stage is 16 KB of
+// A plus 32 KB (gate/up) or, with split A, 16 KB (down) of B.
 constexpr int kStageK = 64;
 constexpr int kStages = 3;
 
@@ -109,13 +115,28 @@ __device__ __forceinline__ void copy16_lds(const void *g, unsigned char *l) {
 // vector memory operations and for nothing else.
 constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
-template <int KIND>
+// Split A rows.  The down GEMM's A is the fp32 act, carried as two bf16
+// numbers per element: hi = bf16(v) and lo = bf16(v - hi), so that
+// hi*b + lo*b keeps about 16 bits of v.  A row of K elements is stored as
+// K/8 pairs of 16-byte chunks (8 hi values, then the same 8 elements' lo
+// values): 4K bytes, the size of the fp32 row.
+__device__ __forceinline__ size_t split_pos(int i) { return (size_t)(i >> 3) * 16 + (i & 7); }
+
+// XOR swizzle of a 16-byte chunk within an LDS row of CH chunks: rows of 8
+// chunks (128 B) xor with row % 8; rows of 4 chunks (64 B, two rows per 128
+// bytes of banks) xor with (row / 2) % 4.  Either way the 8 rows one
+// ds_read_b128 phase touches land on 8 different 16-byte bank groups.
+template <int CH>
+__device__ __forceinline__ int swz(int row) { return CH == 8 ? (row & 7) : ((row >> 1) & 3); }
+
+template <int KIND, bool AS>
 __global__ __launch_bounds__(kGThreads, 1) void k_gemm_lds(GemmArgs a) {
     constexpr int NB = GemmShape<KIND>::NB;
     constexpr int WCOLS = GemmShape<KIND>::WCOLS;
-    constexpr int BK = kStageK;                    // reduction elements per stage
+    constexpr int AP = AS ? 2 : 1;                 // bf16 values of A per element (split: hi, lo)
+    constexpr int BK = kStageK / AP;               // reduction elements per stage
     constexpr int NST = kStages;                   // LDS stages
-    constexpr int ARB = BK * 2;                    // A bytes per row per stage
+    constexpr int ARB = BK * 2 * AP;               // A bytes per row per stage
     constexpr int BRB = BK * 2;                    // B bytes per column per stage
     constexpr int ACH = ARB / 16;                  // 16-byte chunks per A row per stage
     constexpr int BCH = BRB / 16;                  // 16-byte chunks per B column per stage
@@ -170,7 +191,7 @@ __global__ __launch_bounds__(kGThreads, 1) void k_gemm_lds(GemmArgs a) {
     if (tid < kBM) {
         const int p = p0 + min(tid, nrows - 1);
         const int t = a.sorted ? a.sorted[p] / a.k_route : p;
-        s_src[tid] = reinterpret_cast<const char *>(a.a) + (size_t)t * a.K * 2;
+        s_src[tid] = reinterpret_cast<const char *>(a.a) + (size_t)t * a.K * 2 * AP;
         s_tok[tid] = t;
     }
     __syncthreads();
@@ -187,13 +208,13 @@ __global__ __launch_bounds__(kGThreads, 1) void k_gemm_lds(GemmArgs a) {
     const char *asrc[A_DMA];
 #pragma unroll
     for (int q = 0; q < A_DMA; q++) {
-        const int r = (wave * A_DMA + q) * (kWave / ACH) + lane / ACH, c = (lane % ACH) ^ (r % ACH);
+        const int r = (wave * A_DMA + q) * (kWave / ACH) + lane / ACH, c = (lane % ACH) ^ swz<ACH>(r);
         asrc[q] = s_src[r] + c * 16;
     }
     const char *bsrc[B_DMA];
 #pragma unroll
     for (int q = 0; q < B_DMA; q++) {
-        const int cl = q * (kWave / BCH) + lane / BCH, c = (lane % BCH) ^ (cl % BCH);
+        const int cl = q * (kWave / BCH) + lane / BCH, c = (lane % BCH) ^ swz<BCH>(cl);
         const uint16_t *mat = (KIND == GK_GATEUP && cl >= 32) ? a.b1 : a.b0;
         const int col = KIND == GK_GATEUP ? colw + (cl & 31) : colw + cl;
         bsrc[q] = reinterpret_cast<const char *>(mat + (size_t)e * a.b_stride + (size_t)min(col, N - 1) * K) + c * 16;
@@ -220,26 +241,33 @@ __global__ __launch_bounds__(kGThreads, 1) void k_gemm_lds(GemmArgs a) {
         const unsigned char *bw = st + A_BYTES + wave * WB_BYTES;
 #pragma unroll
         for (int s = 0; s < BK / 16; s++) {
-            // every read of the substep first, one wait, then the MFMAs
-            u32x4 v[NB + kMB];
+            // every read of the substep first, one wait, then the MFMAs.
+            // Lane l takes the 8 reduction elements g = 2s + l/32 of its row
+            // or column (split A: chunk 2g holds their hi, 2g+1 their lo).
+            const int g8 = 2 * s + (lane >> 5);
+            u32x4 v[NB + AP * kMB];
 #pragma unroll
             for (int nb = 0; nb < NB; nb++) {
-                const int cl = nb * 32 + (lane & 31), c = 2 * s + (lane >> 5);
-                v[nb] = lds_load16(bw + cl * BRB + ((c ^ (cl % BCH)) * 16));
+                const int cl = nb * 32 + (lane & 31);
+                v[nb] = lds_load16(bw + cl * BRB + ((g8 ^ swz<BCH>(cl)) * 16));
             }
 #pragma unroll
             for (int mb = 0; mb < kMB; mb++) {
-                const int r = mb * 32 + (lane & 31), c = 2 * s + (lane >> 5);
-                v[NB + mb] = lds_load16(st + r * ARB + ((c ^ (r % ACH)) * 16));
+                const int r = mb * 32 + (lane & 31);
+#pragma unroll
+                for (int h = 0; h < AP; h++)
+                    v[NB + AP * mb + h] = lds_load16(st + r * ARB + (((AP * g8 + h) ^ swz<ACH>(r)) * 16));
             }
             lds_wait(v);
 #pragma unroll
             for (int mb = 0; mb < kMB; mb++)
 #pragma unroll
                 for (int nb = 0; nb < NB; nb++)
-                    acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, v[NB + mb]),
-                                                                          __builtin_bit_cast(bf16x8, v[nb]),
-                                                                          acc[mb][nb], 0, 0, 0);
+#pragma unroll
+                    for (int h = 0; h < AP; h++)
+                        acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                            __builtin_bit_cast(bf16x8, v[NB + AP * mb + h]), __builtin_bit_cast(bf16x8, v[nb]),
+                            acc[mb][nb], 0, 0, 0);
         }
     };
 
@@ -284,7 +312,15 @@ __global__ __launch_bounds__(kGThreads, 1) void k_gemm_lds(GemmArgs a) {
                         gv = clampf(gv, a.limit);
                         uv = clampf(uv, a.limit);
                     }
-                    orow[i] = silu_mul(gv, uv);
+                    const float h = silu_mul(gv, uv);
+                    if (a.out_split) {
+                        uint16_t *srow = reinterpret_cast<uint16_t *>(a.out) + (size_t)(p0 + m) * a.ldo * 2;
+                        const uint32_t hi = f32_to_bf16_rne(h);
+                        srow[split_pos(i)] = (uint16_t)hi;
+                        srow[split_pos(i) + 8] = (uint16_t)f32_to_bf16_rne(h - __uint_as_float(hi << 16));
+                    } else {
+                        orow[i] = h;
+                    }
                 }
             } else {
 #pragma unroll
@@ -475,7 +511,15 @@ __global__ __launch_bounds__(kGThreads, 2) void k_gemm_reg(GemmArgs a) {
                         gv = clampf(gv, a.limit);
                         uv = clampf(uv, a.limit);
                     }
-                    orow[i] = silu_mul(gv, uv);
+                    const float h = silu_mul(gv, uv);
+                    if (a.out_split) {
+                        uint16_t *srow = reinterpret_cast<uint16_t *>(a.out) + (size_t)(p0 + m) * a.ldo * 2;
+                        const uint32_t hi = f32_to_bf16_rne(h);
+                        srow[split_pos(i)] = (uint16_t)hi;
+                        srow[split_pos(i) + 8] = (uint16_t)f32_to_bf16_rne(h - __uint_as_float(hi << 16));
+                    } else {
+                        orow[i] = h;
+                    }
                 }
             } else {
 #pragma unroll
@@ -488,23 +532,27 @@ __global__ __launch_bounds__(kGThreads, 2) void k_gemm_reg(GemmArgs a) {
     }
 }
 
-static hipError_t run_gemm(int kind, bool a_f32, GemmArgs &a, hipStream_t s) {
+// a_mode: 0 = bf16 A rows (gate/up), 1 = split A rows (hi/lo pairs), 2 = fp32 A rows
+// (both down).
+static hipError_t run_gemm(int kind, int a_mode, GemmArgs &a, hipStream_t s) {
     const int cols = kind == GK_GATEUP ? GemmShape<GK_GATEUP>::COLS : GemmShape<GK_PLAIN>::COLS;
     a.n_ntiles = (a.N + cols - 1) / cols;
     if (a.ksplit < 1) a.ksplit = 1;
     const int per_tile = a.n_ntiles * a.ksplit;
     if ((long)a.max_tiles * per_tile == 0) return hipSuccess;
-    if (a_f32) {
-        // fp32 A (the down projection's act): register-staged kernel, A split
+    if (a_mode == 2) {
+        // fp32 A (act handed in by a caller): register-staged kernel, A split
         // into bf16 hi/lo once per workgroup as it is written to LDS
         const unsigned grid = (unsigned)(((long)a.max_tiles * per_tile + 7) / 8 * 8);
         launch_kernel((k_gemm_reg<GK_PLAIN, true>), dim3(grid), dim3(kGThreads), 0, s, a);
     } else {
         const unsigned grid = (unsigned)((long)a.max_tiles * ((per_tile + 7) / 8 * 8));
-        if (kind == GK_GATEUP)
-            launch_kernel((k_gemm_lds<GK_GATEUP>), dim3(grid), dim3(kGThreads), 0, s, a);
+        if (kind == GK_GATEUP && a_mode == 0)
+            launch_kernel((k_gemm_lds<GK_GATEUP, false>), dim3(grid), dim3(kGThreads), 0, s, a);
+        else if (kind == GK_PLAIN && a_mode == 1)
+            launch_kernel((k_gemm_lds<GK_PLAIN, true>), dim3(grid), dim3(kGThreads), 0, s, a);
         else
-            launch_kernel((k_gemm_lds<GK_PLAIN>), dim3(grid), dim3(kGThreads), 0, s, a);
+            return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }
@@ -529,7 +577,7 @@ int down_ksplit(const Layer &L, int M) {
 
 hipError_t launch_gateup_mfma(const Layer &L, const void *x, const float *tok_scale, const Mats &routed,
                               const Mats &shared, const Routing &rt, int M, int max_tiles,
-                              float *act, float *shared_act, hipStream_t s) {
+                              float *act, float *shared_act, bool act_split, hipStream_t s) {
     if (act) {
         GemmArgs a{};
         a.a = x;
@@ -548,7 +596,8 @@ hipError_t launch_gateup_mfma(const Layer &L, const void *x, const float *tok_sc
         a.limit = L.limit;
         a.out = act;
         a.ldo = L.I;
-        hipError_t err = run_gemm(GK_GATEUP, false, a, s);
+        a.out_split = act_split;
+        hipError_t err = run_gemm(GK_GATEUP, 0, a, s);
         if (err != hipSuccess) return err;
     }
     if (shared_act && L.Is > 0) {
@@ -564,14 +613,15 @@ hipError_t launch_gateup_mfma(const Layer &L, const void *x, const float *tok_sc
         a.limit = 0.f; // the shared expert is not clamped
         a.out = shared_act;
         a.ldo = L.Is;
-        return run_gemm(GK_GATEUP, false, a, s);
+        a.out_split = act_split;
+        return run_gemm(GK_GATEUP, 0, a, s);
     }
     return hipSuccess;
 }
 
 hipError_t launch_down_mfma(const Layer &L, const float *act, const float *shared_act,
                             const Mats &routed, const Mats &shared, const Routing &rt, int M,
-                            int max_tiles, float *y_routes, float *y_shared, hipStream_t s) {
+                            int max_tiles, float *y_routes, float *y_shared, bool act_split, hipStream_t s) {
     if (act) {
         GemmArgs a{};
         a.a = act;
@@ -587,7 +637,7 @@ hipError_t launch_down_mfma(const Layer &L, const float *act, const float *share
         a.K = L.I;
         a.out = y_routes;
         a.ldo = L.H;
-        hipError_t err = run_gemm(GK_PLAIN, true, a, s);
+        hipError_t err = run_gemm(GK_PLAIN, act_split ? 1 : 2, a, s);
         if (err != hipSuccess) return err;
     }
     if (shared_act && L.Is > 0) {
@@ -600,7 +650,7 @@ hipError_t launch_down_mfma(const Layer &L, const float *act, const float *share
         a.K = L.Is;
         a.out = y_shared;
         a.ldo = L.H;
-        return run_gemm(GK_PLAIN, true, a, s);
+        return run_gemm(GK_PLAIN, act_split ? 1 : 2, a, s);
     }
     return hipSuccess;
 }

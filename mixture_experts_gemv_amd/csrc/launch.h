@@ -92,10 +92,12 @@ hipError_t launch_router_mfma(const Layer &L, const void *x, const void *router,
                               int M, float *logits, hipStream_t s);
 hipError_t launch_gateup_mfma(const Layer &L, const void *x, const float *tok_scale, const Mats &routed,
                               const Mats &shared, const Routing &rt, int M, int max_tiles,
-                              float *act, float *shared_act, hipStream_t s);
+                              float *act, float *shared_act, bool act_split, hipStream_t s);
+// act_split: act / shared_act rows hold the hi/lo bf16 pairs the gate/up GEMM
+// writes with act_split (same size as fp32 rows); else fp32 rows.
 hipError_t launch_down_mfma(const Layer &L, const float *act, const float *shared_act,
                             const Mats &routed, const Mats &shared, const Routing &rt, int M,
-                            int max_tiles, float *y_routes, float *y_shared, hipStream_t s);
+                            int max_tiles, float *y_routes, float *y_shared, bool act_split, hipStream_t s);
 
 hipError_t launch_q8_split(const void *blocks, int64_t rows, int cols, int8_t *qs,
                            uint16_t *scales, hipStream_t s);

@@ -300,7 +300,7 @@ moe_status moe_expert_ffn(const moe_plan *p, const void *x, const moe_weights *w
     const moe::Routing rt{offsets, sorted_routes, nullptr, active, tiles};
     const moe::Mats none{};
     if (use_mfma(p, M))
-        LAUNCH(moe::launch_gateup_mfma(L, x, sc, routed_mats(wts), none, rt, M, lay.max_tiles, act, nullptr, s),
+        LAUNCH(moe::launch_gateup_mfma(L, x, sc, routed_mats(wts), none, rt, M, lay.max_tiles, act, nullptr, false, s),
                "gate/up (MFMA)");
     else
         LAUNCH(moe::launch_gateup_gemv(L, x, sc, routed_mats(wts), none, rt, M, act, nullptr, s), "gate/up");
@@ -332,7 +332,7 @@ moe_status moe_combine(const moe_plan *p, const float *act, const moe_weights *w
     const moe::Mats none{};
     if (use_mfma(p, M)) {
         float *yr = at<float>(ws, lay.y_routes);
-        LAUNCH(moe::launch_down_mfma(L, act, nullptr, routed_mats(wts), none, rt, M, lay.max_tiles, yr, nullptr, s),
+        LAUNCH(moe::launch_down_mfma(L, act, nullptr, routed_mats(wts), none, rt, M, lay.max_tiles, yr, nullptr, false, s),
                "down (MFMA)");
         LAUNCH(moe::launch_combine(L, yr, nullptr, route_pos, w, seed, M, y, s, moe::down_ksplit(L, M), 0),
                "combine");
@@ -434,10 +434,10 @@ static moe_status forward_impl(const moe_plan *p, const void *x, const moe_weigh
     float *ysh = L.Is > 0 ? at<float>(ws, lay.y_shared) : nullptr;
     if (mfma) {
         STAGE(rec, moe::launch_gateup_mfma(L, x, sc, routed_mats(wts), shared_mats(wts), rt, M,
-                                           lay.max_tiles, act, sact, s),
+                                           lay.max_tiles, act, sact, true, s),
               "gate/up (MFMA)", MOE_STAGE_GATEUP);
         STAGE(rec, moe::launch_down_mfma(L, act, sact, routed_mats(wts), shared_mats(wts), rt, M,
-                                         lay.max_tiles, yr, ysh, s),
+                                         lay.max_tiles, yr, ysh, true, s),
               "down (MFMA)", MOE_STAGE_DOWN);
         STAGE(rec, moe::launch_combine(L, yr, ysh, rpos, w, nullptr, M, y, s, moe::down_ksplit(L, M), 1), "combine",
               MOE_STAGE_COMBINE);
