@@ -45,10 +45,11 @@
  *    have run.
  *  - Workspace: `ws` must hold moe_workspace_bytes(plan, M) bytes, 256-byte
  *    aligned, and must be initialised once (moe_workspace_init, or zero-filled)
- *    before its first use: its first 256 bytes hold ticket words that
- *    workgroups of one kernel use to elect the last finisher.  Every call that
- *    completes leaves them as it found them (zero); the rest of the workspace
- *    carries nothing between calls.  After MOE_ERR_HIP, initialise it again.
+ *    before its first use: its first 256 bytes are reserved for counters with
+ *    which the workgroups of one kernel could elect a last finisher (none of
+ *    the current kernels uses them; a call that completes leaves them zero).
+ *    The rest of the workspace carries nothing between calls.  After
+ *    MOE_ERR_HIP, initialise it again.
  *    Calls that share one workspace must be ordered on one stream; calls on
  *    different streams need different workspaces.
  *  - M = 0 is a no-op returning MOE_OK.
@@ -145,8 +146,9 @@ void moe_plan_destroy(moe_plan *plan);
  * (shared expert, pre-norm, the MFMA path) take no space. */
 size_t moe_workspace_bytes(const moe_plan *plan, int32_t M);
 
-/* Zero the ticket words of a workspace (one small kernel on `stream`).  Call
- * once after allocating a workspace, and again after a MOE_ERR_HIP. */
+/* Zero the reserved counter words of a workspace (one small kernel on
+ * `stream`).  Call once after allocating a workspace, and again after a
+ * MOE_ERR_HIP. */
 moe_status moe_workspace_init(const moe_plan *plan, void *ws, size_t ws_bytes, void *stream);
 
 /* Text of the last non-OK status returned on the calling thread. */

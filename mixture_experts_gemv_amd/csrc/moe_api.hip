@@ -37,7 +37,7 @@ moe_status hip_fail(hipError_t e, const char *what) {
 bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 constexpr size_t kAlign = 256;
-constexpr size_t kSyncBytes = 256; // ticket words at the start of every workspace
+constexpr size_t kSyncBytes = 256; // reserved counter words at the start of every workspace
 size_t up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 // Where each workspace region starts for a call with M tokens.

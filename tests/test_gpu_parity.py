@@ -261,8 +261,8 @@ def test_stages_mfma():
 
 
 def test_workspace_reuse_across_calls():
-    """One workspace, many calls of different M: the ticket words come back to
-    zero after every call, so each result equals a fresh-workspace result."""
+    """One workspace, many calls of different M: each result equals a
+    fresh-workspace result, and the reserved counter words stay zero."""
     spec = synth.small_spec(hidden=256, num_experts=16, top_k=4, expert_inter=192,
                             bias_mode=BIAS_LOGIT, bias_kind="normal", seed=1210)
     layer = synth.make_layer(spec)
@@ -275,7 +275,7 @@ def test_workspace_reuse_across_calls():
         b = dl.forward(x).cpu().numpy()
         assert np.array_equal(a, b), f"call {n} (M={M}) differs with a reused workspace"
     words = ws[:256].view(torch.int32).cpu().numpy()
-    assert not words.any(), "ticket words not returned to zero"
+    assert not words.any(), "reserved counter words not zero"
 
 
 def test_forward_repeatable():
