@@ -157,9 +157,10 @@ __global__ __launch_bounds__(kGThreads, 1) void k_gemm_lds(GemmArgs a) {
 
     // ---- which tile, column block and reduction slice.  The workgroups of
     // one expert cover its column units c = (slice, column block) for every
-    // token tile tl; the token tiles of a unit go to one XCD (equal g mod 8)
-    // one after another, so the unit's weights are read from HBM about once
-    // and then served by that XCD's L2.
+    // token tile tl.  XCD x (equal g mod 8) takes the contiguous unit range
+    // [x * per_pad / 8, (x + 1) * per_pad / 8), all token tiles of each: a
+    // unit's weights are read from HBM about once, and an XCD's units share
+    // one reduction slice of the A rows, which its L2 then serves.
     const int g = blockIdx.x;
     const int per_tile = a.n_ntiles * a.ksplit;
     const int per_pad = (per_tile + 7) / 8 * 8;
@@ -178,7 +179,7 @@ __global__ __launch_bounds__(kGThreads, 1) void k_gemm_lds(GemmArgs a) {
     }
     const int local = g - ts * per_pad;
     const int grp = local / (8 * Te), r8 = local - grp * 8 * Te;
-    const int tl = r8 >> 3, cu = grp * 8 + (r8 & 7);
+    const int tl = r8 >> 3, cu = (r8 & 7) * (per_pad >> 3) + grp;
     if (cu >= per_tile) return;
     const int ks = cu / a.n_ntiles, nt = cu - ks * a.n_ntiles;
     if (a.tiles) {
@@ -656,53 +657,64 @@ hipError_t launch_down_mfma(const Layer &L, const float *act, const float *share
 }
 
 // ------------------------------------------------------------------ router
-// logits[t][e] = scale[t] * x[t] . router[e] for many tokens: one wave per
-// tile of 16 tokens x 16 experts, v_mfma_f32_16x16x32_bf16 over K, operands
-// loaded from global (L2) straight into registers, kRtUnroll steps ahead.
+// logits[t][e] = scale[t] * x[t] . router[e] for many tokens: one workgroup
+// per tile of 16 tokens x 16 experts, v_mfma_f32_16x16x32_bf16 over K.  The
+// kRtWaves waves split the 32-element K steps into contiguous ranges; each
+// wave loads kRtUnroll steps of both operands from global (L2) straight into
+// registers before using them.  The waves' partial tiles meet in LDS and are
+// summed in wave order.
 typedef float f32x4m __attribute__((ext_vector_type(4)));
-constexpr int kRtUnroll = 4;
+constexpr int kRtWaves = 8;
+constexpr int kRtUnroll = 8;
 
-__global__ __launch_bounds__(256) void k_router_mfma16(const uint16_t *x, const uint16_t *router,
-                                                       const float *tok_scale, int M, int E, int K,
-                                                       float *logits) {
-    const int lane = threadIdx.x & 63;
+__global__ __launch_bounds__(kRtWaves * kWave) void k_router_mfma16(const uint16_t *x, const uint16_t *router,
+                                                                   const float *tok_scale, int M, int E, int K,
+                                                                   float *logits) {
+    __shared__ f32x4m s_part[kRtWaves][kWave];
+    const int lane = threadIdx.x & 63, wave = uniform(threadIdx.x >> 6);
     const int ntE = (E + 15) / 16;
-    const int gw = uniform(blockIdx.x * 4 + (threadIdx.x >> 6));
-    const int tm = gw / ntE, te = gw % ntE;
-    if (tm * 16 >= M) return;
+    const int tm = blockIdx.x / ntE, te = blockIdx.x % ntE;
     const int t = min(tm * 16 + (lane & 15), M - 1);
     const int e = min(te * 16 + (lane & 15), E - 1);
     const uint16_t *arow = x + (size_t)t * K + 8 * (lane >> 4);
     const uint16_t *brow = router + (size_t)e * K + 8 * (lane >> 4);
+    const int NS = K / 32, s0 = wave * NS / kRtWaves, s1 = (wave + 1) * NS / kRtWaves;
     f32x4m acc = {0.f, 0.f, 0.f, 0.f};
-    for (int k0 = 0; k0 < K; k0 += 32 * kRtUnroll) {
+    for (int sb = s0; sb < s1; sb += kRtUnroll) {
         u32x4 av[kRtUnroll], bv[kRtUnroll];
 #pragma unroll
         for (int u = 0; u < kRtUnroll; u++) {
-            const int k = min(k0 + 32 * u, K - 32);
+            const int k = 32 * min(sb + u, s1 - 1);
             av[u] = *reinterpret_cast<const u32x4 *>(arow + k);
             bv[u] = *reinterpret_cast<const u32x4 *>(brow + k);
         }
 #pragma unroll
         for (int u = 0; u < kRtUnroll; u++)
-            if (k0 + 32 * u < K)
+            if (sb + u < s1)
                 acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av[u]),
                                                               __builtin_bit_cast(bf16x8, bv[u]), acc, 0, 0, 0);
     }
+    s_part[wave][lane] = acc;
+    __syncthreads();
+    if (wave != 0) return;
+    f32x4m sum = s_part[0][lane];
+#pragma unroll
+    for (int w = 1; w < kRtWaves; w++) sum += s_part[w][lane];
     const int col = te * 16 + (lane & 15);
 #pragma unroll
     for (int r = 0; r < 4; r++) {
         const int row = tm * 16 + 4 * (lane >> 4) + r;
-        if (row < M && col < E) logits[(size_t)row * E + col] = acc[r] * (tok_scale ? tok_scale[row] : 1.0f);
+        if (row < M && col < E) logits[(size_t)row * E + col] = sum[r] * (tok_scale ? tok_scale[row] : 1.0f);
     }
 }
 
 hipError_t launch_router_mfma(const Layer &L, const void *x, const void *router, const float *tok_scale,
                               int M, float *logits, hipStream_t s) {
-    const int waves = ((M + 15) / 16) * ((L.E + 15) / 16);
-    launch_kernel(k_router_mfma16, dim3((waves + 3) / 4), dim3(256), 0, s,
-                       static_cast<const uint16_t *>(x), static_cast<const uint16_t *>(router), tok_scale, M,
-                       L.E, L.H, logits);
+    if (L.H % 32) return hipErrorInvalidValue;
+    const int tiles = ((M + 15) / 16) * ((L.E + 15) / 16);
+    launch_kernel(k_router_mfma16, dim3(tiles), dim3(kRtWaves * kWave), 0, s,
+                  static_cast<const uint16_t *>(x), static_cast<const uint16_t *>(router), tok_scale, M,
+                  L.E, L.H, logits);
     return hipGetLastError();
 }
 
