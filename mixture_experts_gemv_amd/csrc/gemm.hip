@@ -157,16 +157,18 @@ __global__ __launch_bounds__(kGThreads, 1) void k_gemm_lds(GemmArgs a) {
 
     // ---- which tile, column block and reduction slice.  The workgroups of
     // one expert cover its column units c = (slice, column block) for every
-    // token tile tl.  XCD x (equal g mod 8) takes the contiguous unit range
-    // [x * per_pad / 8, (x + 1) * per_pad / 8), all token tiles of each: a
+    // token tile tl, per_tile units a tile.  When per_tile is a multiple of 8,
+    // XCD x (equal g mod 8) takes the contiguous unit range
+    // [x * per_tile / 8, (x + 1) * per_tile / 8), all token tiles of each: a
     // unit's weights are read from HBM about once, and an XCD's units share
-    // one reduction slice of the A rows, which its L2 then serves.
+    // one reduction slice of the A rows, which its L2 then serves.  Otherwise
+    // the workgroups run through (tl, c) in tile-major order, so that every
+    // XCD gets work.
     const int g = blockIdx.x;
     const int per_tile = a.n_ntiles * a.ksplit;
-    const int per_pad = (per_tile + 7) / 8 * 8;
     int e = 0, ts, Te, p0, nrows;
     if (a.tiles) {
-        const int q = g / per_pad;
+        const int q = g / per_tile;
         if (q >= a.tiles[0]) return;
         const int32_t *pairs = a.tiles + 2 + a.E;
         e = pairs[2 * q];
@@ -175,12 +177,18 @@ __global__ __launch_bounds__(kGThreads, 1) void k_gemm_lds(GemmArgs a) {
     } else {
         ts = 0;
         Te = (a.M + kBM - 1) / kBM;
-        if (g >= Te * per_pad) return;
+        if (g >= Te * per_tile) return;
     }
-    const int local = g - ts * per_pad;
-    const int grp = local / (8 * Te), r8 = local - grp * 8 * Te;
-    const int tl = r8 >> 3, cu = (r8 & 7) * (per_pad >> 3) + grp;
-    if (cu >= per_tile) return;
+    const int local = g - ts * per_tile;
+    int tl, cu;
+    if ((per_tile & 7) == 0) {
+        const int grp = local / (8 * Te), r8 = local - grp * 8 * Te;
+        tl = r8 >> 3;
+        cu = (r8 & 7) * (per_tile >> 3) + grp;
+    } else {
+        tl = local / per_tile;
+        cu = local - tl * per_tile;
+    }
     const int ks = cu / a.n_ntiles, nt = cu - ks * a.n_ntiles;
     if (a.tiles) {
         p0 = a.tiles[2 + a.E + 2 * (ts + tl) + 1];
@@ -547,7 +555,7 @@ static hipError_t run_gemm(int kind, int a_mode, GemmArgs &a, hipStream_t s) {
         const unsigned grid = (unsigned)(((long)a.max_tiles * per_tile + 7) / 8 * 8);
         launch_kernel((k_gemm_reg<GK_PLAIN, true>), dim3(grid), dim3(kGThreads), 0, s, a);
     } else {
-        const unsigned grid = (unsigned)((long)a.max_tiles * ((per_tile + 7) / 8 * 8));
+        const unsigned grid = (unsigned)((long)a.max_tiles * per_tile);
         if (kind == GK_GATEUP && a_mode == 0)
             launch_kernel((k_gemm_lds<GK_GATEUP, false>), dim3(grid), dim3(kGThreads), 0, s, a);
         else if (kind == GK_PLAIN && a_mode == 1)

@@ -239,6 +239,8 @@ __device__ void write_plan(int E, int tile_rows, const int *cnt, const int *off,
     }
 }
 
+constexpr int kPermChunk = 16; // route ids per lane loaded together
+
 template <int NW>
 __device__ void permute_block(const int32_t *ids, int R, int E, const PermuteOut &o, PermuteSmem<NW> &sm) {
     const int tid = threadIdx.x;
@@ -247,9 +249,24 @@ __device__ void permute_block(const int32_t *ids, int R, int E, const PermuteOut
     __syncthreads();
     const int per = (((R + NW - 1) / NW) + 63) / 64 * 64;
     const int r0 = min(R, wv * per), r1 = min(R, r0 + per);
-    for (int r = r0 + lane; r < r1; r += kWave) {
-        const int e = ids[r];
-        if (e >= 0 && e < E) atomicAdd(&sm.hist[wv][e], 1);
+    // ids of routes base + 64 j + lane, j < kPermChunk, all loads issued first
+    // (index clamped into the wave's range; -1 past its end)
+    auto load_chunk = [&](int base, int (&ev)[kPermChunk]) {
+#pragma unroll
+        for (int j = 0; j < kPermChunk; j++) ev[j] = ids[min(base + j * kWave + lane, r1 - 1)];
+#pragma unroll
+        for (int j = 0; j < kPermChunk; j++)
+            if (base + j * kWave + lane >= r1) ev[j] = -1;
+    };
+    // a wave whose routes fit one chunk keeps its ids in registers for the
+    // scatter below
+    const bool one_chunk = per <= kWave * kPermChunk;
+    int ev[kPermChunk];
+    for (int base = r0; base < r1; base += kWave * kPermChunk) {
+        load_chunk(base, ev);
+#pragma unroll
+        for (int j = 0; j < kPermChunk; j++)
+            if (ev[j] >= 0 && ev[j] < E) atomicAdd(&sm.hist[wv][ev[j]], 1);
     }
     __syncthreads();
     for (int e = tid; e < E; e += NW * kWave) {
@@ -275,28 +292,33 @@ __device__ void permute_block(const int32_t *ids, int R, int E, const PermuteOut
     }
     __syncthreads();
     const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    for (int base = r0; base < r1; base += kWave) {
-        const int r = base + lane;
-        int e = r < r1 ? ids[r] : -1;
-        const bool valid = e >= 0 && e < E;
-        if (!valid) e = 0;
-        uint64_t peers = __ballot(valid);
+    for (int cb = r0; cb < r1; cb += kWave * kPermChunk) {
+        if (!one_chunk) load_chunk(cb, ev);
 #pragma unroll
-        for (int b = 0; b < 8; b++) {
-            const uint64_t m = __ballot(valid && ((e >> b) & 1));
-            peers &= ((e >> b) & 1) ? m : ~m;
+        for (int j = 0; j < kPermChunk; j++) {
+            if (cb + j * kWave >= r1) break; // wave-uniform: the rest of the chunk is past the range
+            const int r = cb + j * kWave + lane;
+            int e = ev[j];
+            const bool valid = e >= 0 && e < E;
+            if (!valid) e = 0;
+            uint64_t peers = __ballot(valid);
+#pragma unroll
+            for (int b = 0; b < 8; b++) {
+                const uint64_t m = __ballot(valid && ((e >> b) & 1));
+                peers &= ((e >> b) & 1) ? m : ~m;
+            }
+            const int rank = __popcll(peers & lt_mask);
+            if (valid) {
+                const int pos = sm.off[e] + sm.hist[wv][e] + rank;
+                o.sorted[pos] = r;
+                o.route_pos[r] = pos;
+            }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            if (valid && rank == 0) sm.hist[wv][e] += __popcll(peers);
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
         }
-        const int rank = __popcll(peers & lt_mask);
-        if (valid) {
-            const int pos = sm.off[e] + sm.hist[wv][e] + rank;
-            o.sorted[pos] = r;
-            o.route_pos[r] = pos;
-        }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        if (valid && rank == 0) sm.hist[wv][e] += __popcll(peers);
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
     }
     __syncthreads();
     write_plan(E, o.tile_rows, sm.cnt, sm.off, sm.scan, o.active, o.tiles);
