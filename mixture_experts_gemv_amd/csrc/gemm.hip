@@ -11,8 +11,9 @@
 //   shared   the same two with identity rows (all tokens), for a shared expert.
 // (The router has its own small-tile kernel at the end of this file.)
 //
-// Tiles: kBM = 128 rows (tokens or routes of one expert, so that most
-// experts' tokens share one pass over the weights) x 128 (gate/up: 32 columns
+// Tiles: 128 rows (tokens or routes of one expert, so that most experts'
+// tokens share one pass over the weights), or 32 rows when a batch gives the
+// experts few routes each (less MFMA and LDS work on empty rows), x 128 (gate/up: 32 columns
 // of gate and of up per wave) or 256 (down: 64 columns per wave) output
 // columns.  Four waves each own all 128 rows of their columns and issue
 // v_mfma_f32_32x32x16_bf16.
@@ -44,6 +45,10 @@ constexpr int kLdsRow = kBK + 8;   // bf16 elements per padded LDS row of the re
 constexpr int kGW = 4;
 constexpr int kGThreads = kGW * kWave;
 
+// Rows of the grouped GEMM's tiles for a batch of M tokens: 32 while the
+// experts average at most 32 routes each, else 128.  The stage-wise entry
+// points with fp32 act (register-staged kernel) always use kBM.
+int mfma_tile_rows(const Layer &L, int M) { return (long)M * L.k <= 32L * L.E ? 32 : kBM; }
 int mfma_tile_rows() { return kBM; }
 
 enum GemmKind { GK_GATEUP = 0, GK_PLAIN = 1 };
@@ -67,6 +72,7 @@ struct GemmArgs {
     float *out;              // fp32 [rows][ldo]; gate/up with out_split: hi/lo bf16 rows (below)
     int ldo;
     int out_split;           // gate/up: write act as interleaved bf16 hi/lo (the split A of down)
+    int tile_rows;           // rows per tile of the LDS kernel (32 or 128; the tile list's)
     int n_ntiles;            // column tiles
 };
 
@@ -129,8 +135,9 @@ __device__ __forceinline__ size_t split_pos(int i) { return (size_t)(i >> 3) * 1
 template <int CH>
 __device__ __forceinline__ int swz(int row) { return CH == 8 ? (row & 7) : ((row >> 1) & 3); }
 
-template <int KIND, bool AS>
+template <int KIND, bool AS, int MB>
 __global__ __launch_bounds__(kGThreads, 1) void k_gemm_lds(GemmArgs a) {
+    constexpr int BM = 32 * MB;                    // rows per tile
     constexpr int NB = GemmShape<KIND>::NB;
     constexpr int WCOLS = GemmShape<KIND>::WCOLS;
     constexpr int AP = AS ? 2 : 1;                 // bf16 values of A per element (split: hi, lo)
@@ -141,17 +148,17 @@ __global__ __launch_bounds__(kGThreads, 1) void k_gemm_lds(GemmArgs a) {
     constexpr int ACH = ARB / 16;                  // 16-byte chunks per A row per stage
     constexpr int BCH = BRB / 16;                  // 16-byte chunks per B column per stage
     constexpr int WBC = 64;                        // B columns per wave (gate/up: 32 gate + 32 up)
-    constexpr int A_BYTES = kBM * ARB;
+    constexpr int A_BYTES = BM * ARB;
     constexpr int WB_BYTES = WBC * BRB;            // one wave's B per stage
     constexpr int ST_BYTES = A_BYTES + kGW * WB_BYTES;
-    constexpr int A_DMA = kBM * ARB / (kWave * 16) / kGW; // A copies per wave per stage (each 1 KB)
+    constexpr int A_DMA = BM * ARB / (kWave * 16) / kGW; // A copies per wave per stage (each 1 KB)
     constexpr int B_DMA = WB_BYTES / (kWave * 16);        // B copies per wave per stage
     constexpr int LPS = A_DMA + B_DMA;             // copies per lane per stage
     // one LDS array per stage, named explicitly in an NST-way unrolled loop
     // (measured faster than one array indexed by kt % NST)
     __shared__ __attribute__((aligned(16))) unsigned char sm0[ST_BYTES], sm1[ST_BYTES], sm2[ST_BYTES];
-    __shared__ const char *s_src[kBM];
-    __shared__ int s_tok[kBM];
+    __shared__ const char *s_src[BM];
+    __shared__ int s_tok[BM];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = uniform(tid >> 6);
 
@@ -176,7 +183,7 @@ __global__ __launch_bounds__(kGThreads, 1) void k_gemm_lds(GemmArgs a) {
         Te = a.tiles[2 + e] - ts;
     } else {
         ts = 0;
-        Te = (a.M + kBM - 1) / kBM;
+        Te = (a.M + BM - 1) / BM;
         if (g >= Te * per_tile) return;
     }
     const int local = g - ts * per_tile;
@@ -192,12 +199,12 @@ __global__ __launch_bounds__(kGThreads, 1) void k_gemm_lds(GemmArgs a) {
     const int ks = cu / a.n_ntiles, nt = cu - ks * a.n_ntiles;
     if (a.tiles) {
         p0 = a.tiles[2 + a.E + 2 * (ts + tl) + 1];
-        nrows = min(kBM, a.offsets[e + 1] - p0);
+        nrows = min(BM, a.offsets[e + 1] - p0);
     } else {
-        p0 = tl * kBM;
-        nrows = min(kBM, a.M - p0);
+        p0 = tl * BM;
+        nrows = min(BM, a.M - p0);
     }
-    if (tid < kBM) {
+    if (tid < BM) {
         const int p = p0 + min(tid, nrows - 1);
         const int t = a.sorted ? a.sorted[p] / a.k_route : p;
         s_src[tid] = reinterpret_cast<const char *>(a.a) + (size_t)t * a.K * 2 * AP;
@@ -238,9 +245,9 @@ __global__ __launch_bounds__(kGThreads, 1) void k_gemm_lds(GemmArgs a) {
             copy16_lds(bsrc[q] + kbb, st + A_BYTES + wave * WB_BYTES + q * 1024);
     };
 
-    f32x16 acc[kMB][NB];
+    f32x16 acc[MB][NB];
 #pragma unroll
-    for (int mb = 0; mb < kMB; mb++)
+    for (int mb = 0; mb < MB; mb++)
 #pragma unroll
         for (int nb = 0; nb < NB; nb++)
 #pragma unroll
@@ -254,14 +261,14 @@ __global__ __launch_bounds__(kGThreads, 1) void k_gemm_lds(GemmArgs a) {
             // Lane l takes the 8 reduction elements g = 2s + l/32 of its row
             // or column (split A: chunk 2g holds their hi, 2g+1 their lo).
             const int g8 = 2 * s + (lane >> 5);
-            u32x4 v[NB + AP * kMB];
+            u32x4 v[NB + AP * MB];
 #pragma unroll
             for (int nb = 0; nb < NB; nb++) {
                 const int cl = nb * 32 + (lane & 31);
                 v[nb] = lds_load16(bw + cl * BRB + ((g8 ^ swz<BCH>(cl)) * 16));
             }
 #pragma unroll
-            for (int mb = 0; mb < kMB; mb++) {
+            for (int mb = 0; mb < MB; mb++) {
                 const int r = mb * 32 + (lane & 31);
 #pragma unroll
                 for (int h = 0; h < AP; h++)
@@ -269,7 +276,7 @@ __global__ __launch_bounds__(kGThreads, 1) void k_gemm_lds(GemmArgs a) {
             }
             lds_wait(v);
 #pragma unroll
-            for (int mb = 0; mb < kMB; mb++)
+            for (int mb = 0; mb < MB; mb++)
 #pragma unroll
                 for (int nb = 0; nb < NB; nb++)
 #pragma unroll
@@ -306,7 +313,7 @@ __global__ __launch_bounds__(kGThreads, 1) void k_gemm_lds(GemmArgs a) {
 
     // ---- epilogue
 #pragma unroll
-    for (int mb = 0; mb < kMB; mb++) {
+    for (int mb = 0; mb < MB; mb++) {
 #pragma unroll
         for (int r = 0; r < 16; r++) {
             const int m = mb * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
@@ -550,18 +557,24 @@ static hipError_t run_gemm(int kind, int a_mode, GemmArgs &a, hipStream_t s) {
     const int per_tile = a.n_ntiles * a.ksplit;
     if ((long)a.max_tiles * per_tile == 0) return hipSuccess;
     if (a_mode == 2) {
+        if (a.tile_rows != kBM) return hipErrorInvalidValue;
         // fp32 A (act handed in by a caller): register-staged kernel, A split
         // into bf16 hi/lo once per workgroup as it is written to LDS
         const unsigned grid = (unsigned)(((long)a.max_tiles * per_tile + 7) / 8 * 8);
         launch_kernel((k_gemm_reg<GK_PLAIN, true>), dim3(grid), dim3(kGThreads), 0, s, a);
     } else {
         const unsigned grid = (unsigned)((long)a.max_tiles * per_tile);
-        if (kind == GK_GATEUP && a_mode == 0)
-            launch_kernel((k_gemm_lds<GK_GATEUP, false>), dim3(grid), dim3(kGThreads), 0, s, a);
-        else if (kind == GK_PLAIN && a_mode == 1)
-            launch_kernel((k_gemm_lds<GK_PLAIN, true>), dim3(grid), dim3(kGThreads), 0, s, a);
-        else
+        const bool small = a.tile_rows == 32;
+        if (!small && a.tile_rows != kBM) return hipErrorInvalidValue;
+        if (kind == GK_GATEUP && a_mode == 0) {
+            if (small) launch_kernel((k_gemm_lds<GK_GATEUP, false, 1>), dim3(grid), dim3(kGThreads), 0, s, a);
+            else launch_kernel((k_gemm_lds<GK_GATEUP, false, kMB>), dim3(grid), dim3(kGThreads), 0, s, a);
+        } else if (kind == GK_PLAIN && a_mode == 1) {
+            if (small) launch_kernel((k_gemm_lds<GK_PLAIN, true, 1>), dim3(grid), dim3(kGThreads), 0, s, a);
+            else launch_kernel((k_gemm_lds<GK_PLAIN, true, kMB>), dim3(grid), dim3(kGThreads), 0, s, a);
+        } else {
             return hipErrorInvalidValue;
+        }
     }
     return hipGetLastError();
 }
@@ -575,8 +588,8 @@ bool mfma_supported(const Layer &L) {
 // the chip (about 512) when an M-token batch has few token tiles, keeping at
 // least 4 K steps per slice.  The slices' outputs are summed, in slice order,
 // by the combine.
-int down_ksplit(const Layer &L, int M) {
-    const long tiles = ((long)M * L.k + kBM - 1) / kBM;
+int down_ksplit(const Layer &L, int M, int tile_rows) {
+    const long tiles = ((long)M * L.k + tile_rows - 1) / tile_rows;
     const long ntiles = (L.H + GemmShape<GK_PLAIN>::COLS - 1) / GemmShape<GK_PLAIN>::COLS;
     const int nk = L.I / kBK;
     int S = 1;
@@ -585,10 +598,11 @@ int down_ksplit(const Layer &L, int M) {
 }
 
 hipError_t launch_gateup_mfma(const Layer &L, const void *x, const float *tok_scale, const Mats &routed,
-                              const Mats &shared, const Routing &rt, int M, int max_tiles,
+                              const Mats &shared, const Routing &rt, int M, int max_tiles, int tile_rows,
                               float *act, float *shared_act, bool act_split, hipStream_t s) {
     if (act) {
         GemmArgs a{};
+        a.tile_rows = tile_rows;
         a.a = x;
         a.sorted = rt.sorted;
         a.k_route = L.k;
@@ -613,7 +627,8 @@ hipError_t launch_gateup_mfma(const Layer &L, const void *x, const float *tok_sc
         GemmArgs a{};
         a.a = x;
         a.M = M;
-        a.max_tiles = (M + kBM - 1) / kBM;
+        a.tile_rows = M <= 32 ? 32 : kBM;
+        a.max_tiles = (M + a.tile_rows - 1) / a.tile_rows;
         a.b0 = static_cast<const uint16_t *>(shared.gate);
         a.b1 = static_cast<const uint16_t *>(shared.up);
         a.N = L.Is;
@@ -630,7 +645,8 @@ hipError_t launch_gateup_mfma(const Layer &L, const void *x, const float *tok_sc
 
 hipError_t launch_down_mfma(const Layer &L, const float *act, const float *shared_act,
                             const Mats &routed, const Mats &shared, const Routing &rt, int M,
-                            int max_tiles, float *y_routes, float *y_shared, bool act_split, hipStream_t s) {
+                            int max_tiles, int tile_rows, float *y_routes, float *y_shared, bool act_split,
+                            hipStream_t s) {
     if (act) {
         GemmArgs a{};
         a.a = act;
@@ -638,7 +654,8 @@ hipError_t launch_down_mfma(const Layer &L, const float *act, const float *share
         a.offsets = rt.offsets;
         a.E = L.E;
         a.max_tiles = max_tiles;
-        a.ksplit = down_ksplit(L, M);
+        a.tile_rows = tile_rows;
+        a.ksplit = down_ksplit(L, M, tile_rows);
         a.slab = (size_t)M * L.k * L.H;
         a.b0 = static_cast<const uint16_t *>(routed.down);
         a.b_stride = (size_t)L.H * L.I;
@@ -653,7 +670,8 @@ hipError_t launch_down_mfma(const Layer &L, const float *act, const float *share
         GemmArgs a{};
         a.a = shared_act;
         a.M = M;
-        a.max_tiles = (M + kBM - 1) / kBM;
+        a.tile_rows = act_split && M <= 32 ? 32 : kBM;
+        a.max_tiles = (M + a.tile_rows - 1) / a.tile_rows;
         a.b0 = static_cast<const uint16_t *>(shared.down);
         a.N = L.H;
         a.K = L.Is;

@@ -67,7 +67,7 @@ hipError_t launch_combine(const Layer &L, const float *y_routes, const float *y_
                           const int32_t *route_pos, const float *w, const float *seed, int M,
                           float *y, hipStream_t s, int slices, int shared_slices);
 // Reduction slices of the MFMA down projection for an M-token call.
-int down_ksplit(const Layer &L, int M);
+int down_ksplit(const Layer &L, int M, int tile_rows);
 
 // M = 1 decode kernels (x shared by every touched expert).
 bool m1_supported(const Layer &L);
@@ -86,18 +86,20 @@ hipError_t launch_down_m1(const Layer &L, const float *act, const float *shared_
                           float *y, hipStream_t s);
 
 // MFMA grouped-GEMM path (bf16 x and experts).
-int mfma_tile_rows();
+int mfma_tile_rows();                          // tiles of the stage-wise entry points
+int mfma_tile_rows(const Layer &L, int M);     // tiles of the layer call for M tokens
 bool mfma_supported(const Layer &L);
 hipError_t launch_router_mfma(const Layer &L, const void *x, const void *router, const float *tok_scale,
                               int M, float *logits, hipStream_t s);
 hipError_t launch_gateup_mfma(const Layer &L, const void *x, const float *tok_scale, const Mats &routed,
-                              const Mats &shared, const Routing &rt, int M, int max_tiles,
+                              const Mats &shared, const Routing &rt, int M, int max_tiles, int tile_rows,
                               float *act, float *shared_act, bool act_split, hipStream_t s);
 // act_split: act / shared_act rows hold the hi/lo bf16 pairs the gate/up GEMM
 // writes with act_split (same size as fp32 rows); else fp32 rows.
 hipError_t launch_down_mfma(const Layer &L, const float *act, const float *shared_act,
                             const Mats &routed, const Mats &shared, const Routing &rt, int M,
-                            int max_tiles, float *y_routes, float *y_shared, bool act_split, hipStream_t s);
+                            int max_tiles, int tile_rows, float *y_routes, float *y_shared, bool act_split,
+                            hipStream_t s);
 
 hipError_t launch_q8_split(const void *blocks, int64_t rows, int cols, int8_t *qs,
                            uint16_t *scales, hipStream_t s);

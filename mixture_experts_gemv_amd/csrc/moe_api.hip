@@ -4,6 +4,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
 #include <string>
 
 #include "common.h"
@@ -51,8 +52,11 @@ bool use_mfma(const moe_plan *p, int M) {
     if (!p->mfma_capable) return false;
     if (p->cfg.path == MOE_PATH_MFMA) return true;
     if (p->cfg.path == MOE_PATH_GEMV) return false;
+    // From about two routes per expert on, the grouped GEMM (32-row tiles at
+    // small batches) beats the per-row kernels, whose dot-product work grows
+    // with the tokens each expert sees.
     const long routes = (long)M * p->L.k;
-    return M >= 64 && routes >= 16L * p->L.E;
+    return M >= 8 && routes >= 2L * p->L.E;
 }
 
 WsLayout layout(const moe_plan *p, int M) {
@@ -72,12 +76,16 @@ WsLayout layout(const moe_plan *p, int M) {
     w.sorted = take(R * 4);
     w.route_pos = take(R * 4);
     w.active = take((size_t)(L.E + 1) * 4);
-    const int tile_rows = moe::mfma_tile_rows();
+    // tile capacity for the smaller of the two tile heights (the layer call's
+    // or the stage-wise entry points')
+    const int tile_rows = std::min(moe::mfma_tile_rows(), moe::mfma_tile_rows(L, M));
     w.max_tiles = mfma ? (int)(R / tile_rows + (R < (size_t)L.E ? R : (size_t)L.E) + 1) : 0;
     w.tiles = take(mfma ? (size_t)(2 + L.E + 2 * w.max_tiles) * 4 : 4 * 3);
     w.act = take(R * L.I * 4);
     w.shared_act = take(L.Is > 0 ? (size_t)M * L.Is * 4 : 0);
-    w.y_routes = take((size_t)(mfma ? moe::down_ksplit(L, M) : moe::down_gemv_slices(L.I)) * R * L.H * 4);
+    // (fewer tile rows never give more reduction slices)
+    w.y_routes = take((size_t)(mfma ? moe::down_ksplit(L, M, moe::mfma_tile_rows()) : moe::down_gemv_slices(L.I)) *
+                      R * L.H * 4);
     w.y_shared = take(L.Is > 0 ? (size_t)(mfma ? 1 : moe::down_gemv_slices(L.Is)) * M * L.H * 4 : 0);
     w.total = o;
     return w;
@@ -300,7 +308,8 @@ moe_status moe_expert_ffn(const moe_plan *p, const void *x, const moe_weights *w
     const moe::Routing rt{offsets, sorted_routes, nullptr, active, tiles};
     const moe::Mats none{};
     if (use_mfma(p, M))
-        LAUNCH(moe::launch_gateup_mfma(L, x, sc, routed_mats(wts), none, rt, M, lay.max_tiles, act, nullptr, false, s),
+        LAUNCH(moe::launch_gateup_mfma(L, x, sc, routed_mats(wts), none, rt, M, lay.max_tiles, moe::mfma_tile_rows(),
+                                       act, nullptr, false, s),
                "gate/up (MFMA)");
     else
         LAUNCH(moe::launch_gateup_gemv(L, x, sc, routed_mats(wts), none, rt, M, act, nullptr, s), "gate/up");
@@ -332,9 +341,11 @@ moe_status moe_combine(const moe_plan *p, const float *act, const moe_weights *w
     const moe::Mats none{};
     if (use_mfma(p, M)) {
         float *yr = at<float>(ws, lay.y_routes);
-        LAUNCH(moe::launch_down_mfma(L, act, nullptr, routed_mats(wts), none, rt, M, lay.max_tiles, yr, nullptr, false, s),
+        LAUNCH(moe::launch_down_mfma(L, act, nullptr, routed_mats(wts), none, rt, M, lay.max_tiles, moe::mfma_tile_rows(),
+                                     yr, nullptr, false, s),
                "down (MFMA)");
-        LAUNCH(moe::launch_combine(L, yr, nullptr, route_pos, w, seed, M, y, s, moe::down_ksplit(L, M), 0),
+        LAUNCH(moe::launch_combine(L, yr, nullptr, route_pos, w, seed, M, y, s,
+                                   moe::down_ksplit(L, M, moe::mfma_tile_rows()), 0),
                "combine");
     } else {
         float *yr = at<float>(ws, lay.y_routes);
@@ -409,6 +420,7 @@ static moe_status forward_impl(const moe_plan *p, const void *x, const moe_weigh
     int32_t *active = at<int32_t>(ws, lay.active);
     int32_t *tiles = lay.max_tiles ? at<int32_t>(ws, lay.tiles) : nullptr;
     const bool mfma = use_mfma(p, M);
+    const int rows = moe::mfma_tile_rows(L, M); // tile height of the grouped GEMMs
     const bool single = M == 1 && !mfma && moe::m1_supported(L);
     if (single) {
         // one token: the gate/up kernel runs the top-k itself from the logits
@@ -423,8 +435,7 @@ static moe_status forward_impl(const moe_plan *p, const void *x, const moe_weigh
         else
             STAGE(rec, moe::launch_router(L, x, wts->router, sc, M, lg, s), "router", MOE_STAGE_ROUTER);
         STAGE(rec, moe::launch_topk(L, lg, wts->bias, M, ids, w, s), "top-k", MOE_STAGE_TOPK);
-        STAGE(rec, moe::launch_permute(L.E, R, moe::mfma_tile_rows(), ids, counts, offsets, sorted, rpos,
-                                       active, tiles, s),
+        STAGE(rec, moe::launch_permute(L.E, R, rows, ids, counts, offsets, sorted, rpos, active, tiles, s),
               "permute", MOE_STAGE_PERMUTE);
     }
     const moe::Routing rt{offsets, sorted, rpos, active, tiles};
@@ -434,13 +445,13 @@ static moe_status forward_impl(const moe_plan *p, const void *x, const moe_weigh
     float *ysh = L.Is > 0 ? at<float>(ws, lay.y_shared) : nullptr;
     if (mfma) {
         STAGE(rec, moe::launch_gateup_mfma(L, x, sc, routed_mats(wts), shared_mats(wts), rt, M,
-                                           lay.max_tiles, act, sact, true, s),
+                                           lay.max_tiles, rows, act, sact, true, s),
               "gate/up (MFMA)", MOE_STAGE_GATEUP);
         STAGE(rec, moe::launch_down_mfma(L, act, sact, routed_mats(wts), shared_mats(wts), rt, M,
-                                         lay.max_tiles, yr, ysh, true, s),
+                                         lay.max_tiles, rows, yr, ysh, true, s),
               "down (MFMA)", MOE_STAGE_DOWN);
-        STAGE(rec, moe::launch_combine(L, yr, ysh, rpos, w, nullptr, M, y, s, moe::down_ksplit(L, M), 1), "combine",
-              MOE_STAGE_COMBINE);
+        STAGE(rec, moe::launch_combine(L, yr, ysh, rpos, w, nullptr, M, y, s, moe::down_ksplit(L, M, rows), 1),
+              "combine", MOE_STAGE_COMBINE);
     } else if (single) {
         STAGE(rec, moe::launch_gateup_m1(L, x, sc, routed_mats(wts), shared_mats(wts), lg, wts->bias, ids, w,
                                          counts_out, act, sact, s),
