@@ -30,6 +30,8 @@
 // (Rounding act to a single bf16 instead measured about 1.5x faster in the
 // down GEMM, but at an output error of about 1.6e-3 relative L2 against
 // about 2.5e-6 with the split.)
+#include <algorithm>
+
 #include "common.h"
 #include "launch.h"
 
@@ -587,9 +589,11 @@ bool mfma_supported(const Layer &L) {
 // Reduction slices of the routed down projection: enough workgroups to fill
 // the chip (about 512) when an M-token batch has few token tiles, keeping at
 // least 4 K steps per slice.  The slices' outputs are summed, in slice order,
-// by the combine.
+// by the combine.  Token tiles are estimated as at least one per expert the
+// routes can touch.
 int down_ksplit(const Layer &L, int M, int tile_rows) {
-    const long tiles = ((long)M * L.k + tile_rows - 1) / tile_rows;
+    const long R = (long)M * L.k;
+    const long tiles = std::max(std::min(R, (long)L.E), (R + tile_rows - 1) / tile_rows);
     const long ntiles = (L.H + GemmShape<GK_PLAIN>::COLS - 1) / GemmShape<GK_PLAIN>::COLS;
     const int nk = L.I / kBK;
     int S = 1;
