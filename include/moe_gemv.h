@@ -36,6 +36,8 @@
  *    (e.g. gate [E][I][H] int8) and fp16 scales, one per 32 consecutive
  *    elements along the reduction dimension (gate_scale [E][I][H/32]).  Value =
  *    scale * q.  moe_q8_0_split converts 34-byte GGUF-style blocks into them.
+ *    Weight planes must be 16-byte aligned and scale planes 4-byte aligned
+ *    (MOE_ERR_INVALID otherwise).
  *  - Routes: route r = t*top_k + j is slot j of token t.  "Sorted position" p
  *    is the route's index in expert-major order (experts ascending, routes
  *    ascending inside an expert), as produced by moe_permute.

@@ -66,8 +66,10 @@ struct GemmArgs {
     int max_tiles;           // tile slots in the grid
     int ksplit;              // reduction split: slice ks writes out + ks * slab
     size_t slab;
-    const uint16_t *b0, *b1; // bf16 [experts][N][K]; b1 only for gate/up
+    const uint16_t *b0, *b1; // bf16 [experts][N][K], or Q8_0 int8 planes; b1 only for gate/up
     size_t b_stride;         // elements between experts' matrices
+    const uint16_t *s0, *s1; // Q8_0: fp16 block scales [experts][N][K/32] of b0, b1
+    size_t s_stride;         // Q8_0: scales between experts' matrices
     int N, K;
     const float *tok_scale;  // per-token scale of the products (pre-norm), or null
     float limit;             // gate/up clamp (0 = off)
@@ -135,27 +137,73 @@ __device__ __forceinline__ size_t split_pos(int i) { return (size_t)(i >> 3) * 1
 // bytes of banks) xor with (row / 2) % 4.  Either way the 8 rows one
 // ds_read_b128 phase touches land on 8 different 16-byte bank groups.
 template <int CH>
-__device__ __forceinline__ int swz(int row) { return CH == 8 ? (row & 7) : ((row >> 1) & 3); }
+__device__ __forceinline__ int swz(int row) { return CH >= 8 ? (row & 7) : ((row >> 1) & 3); }
 
-template <int KIND, bool AS, int MB>
+// 8- and 4-byte LDS reads, issued like lds_load16 (the caller waits).
+__device__ __forceinline__ u32x2 lds_load8(const unsigned char *p) {
+    u32x2 r;
+    const uint32_t addr = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const unsigned char *)p;
+    asm volatile("ds_read_b64 %0, %1" : "=v"(r) : "v"(addr));
+    return r;
+}
+__device__ __forceinline__ uint32_t lds_load4(const unsigned char *p) {
+    uint32_t r;
+    const uint32_t addr = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const unsigned char *)p;
+    asm volatile("ds_read_b32 %0, %1" : "=v"(r) : "v"(addr));
+    return r;
+}
+template <typename T>
+__device__ __forceinline__ void lds_keep(T &v) { asm volatile("" : "+v"(v)); }
+
+// 4-byte asynchronous copy global -> LDS: lane i writes LDS bytes l + 4*i.
+__device__ __forceinline__ void copy4_lds(const void *g, unsigned char *l) {
+    __builtin_amdgcn_global_load_lds(g, (lds_ptr)l, 4, 0, 0);
+}
+
+// 8 Q8_0 int8 values (two words) as 8 bf16 (exact: |q| <= 127).
+__device__ __forceinline__ u32x4 q8x8_to_bf16(u32x2 w) {
+    u32x4 o;
+    const uint32_t f0 = __float_as_uint(i8_to_f32<0>(w.x)), f1 = __float_as_uint(i8_to_f32<1>(w.x));
+    const uint32_t f2 = __float_as_uint(i8_to_f32<2>(w.x)), f3 = __float_as_uint(i8_to_f32<3>(w.x));
+    const uint32_t f4 = __float_as_uint(i8_to_f32<0>(w.y)), f5 = __float_as_uint(i8_to_f32<1>(w.y));
+    const uint32_t f6 = __float_as_uint(i8_to_f32<2>(w.y)), f7 = __float_as_uint(i8_to_f32<3>(w.y));
+    o.x = __builtin_amdgcn_perm(f1, f0, 0x07060302u);
+    o.y = __builtin_amdgcn_perm(f3, f2, 0x07060302u);
+    o.z = __builtin_amdgcn_perm(f5, f4, 0x07060302u);
+    o.w = __builtin_amdgcn_perm(f7, f6, 0x07060302u);
+    return o;
+}
+
+// BQ: B is Q8_0 (int8 plane plus fp16 scales per 32 reduction elements).
+// Its stages span 64 reduction elements (two scale blocks; the int8 columns
+// take half the LDS of bf16 ones), and a 4-byte copy per lane brings each
+// column's two scales along.  Each block's products are accumulated by the
+// MFMAs separately and added to the accumulator times the column's scale.
+// (Stages of 128 elements with 32-row tiles measured no faster.)
+template <int KIND, bool AS, int MB, bool BQ>
 __global__ __launch_bounds__(kGThreads, 1) void k_gemm_lds(GemmArgs a) {
     constexpr int BM = 32 * MB;                    // rows per tile
     constexpr int NB = GemmShape<KIND>::NB;
     constexpr int WCOLS = GemmShape<KIND>::WCOLS;
     constexpr int AP = AS ? 2 : 1;                 // bf16 values of A per element (split: hi, lo)
-    constexpr int BK = kStageK / AP;               // reduction elements per stage
+    constexpr int EB = BQ ? 1 : 2;                 // bytes per B element
+    constexpr int BK = BQ ? kStageK : kStageK / AP; // reduction elements per stage
+    constexpr int NBLK = BK / 32;                  // Q8_0 scale blocks per stage
+    constexpr int SCP = BQ ? NBLK / 2 : 0;         // 4-byte scale copies per lane per stage
     constexpr int NST = kStages;                   // LDS stages
     constexpr int ARB = BK * 2 * AP;               // A bytes per row per stage
-    constexpr int BRB = BK * 2;                    // B bytes per column per stage
+    constexpr int BRB = BK * EB;                   // B bytes per column per stage
     constexpr int ACH = ARB / 16;                  // 16-byte chunks per A row per stage
     constexpr int BCH = BRB / 16;                  // 16-byte chunks per B column per stage
     constexpr int WBC = 64;                        // B columns per wave (gate/up: 32 gate + 32 up)
     constexpr int A_BYTES = BM * ARB;
     constexpr int WB_BYTES = WBC * BRB;            // one wave's B per stage
-    constexpr int ST_BYTES = A_BYTES + kGW * WB_BYTES;
+    constexpr int WS_BYTES = BQ ? WBC * 2 * NBLK : 0; // one wave's scales per stage
+    constexpr int ST_BYTES = A_BYTES + kGW * WB_BYTES + kGW * WS_BYTES;
     constexpr int A_DMA = BM * ARB / (kWave * 16) / kGW; // A copies per wave per stage (each 1 KB)
     constexpr int B_DMA = WB_BYTES / (kWave * 16);        // B copies per wave per stage
-    constexpr int LPS = A_DMA + B_DMA;             // copies per lane per stage
+    constexpr int LPS = A_DMA + B_DMA + SCP;       // copies per lane per stage
+    static_assert(!BQ || NBLK % 2 == 0, "Q8_0 scales are copied in pairs of blocks");
     // one LDS array per stage, named explicitly in an NST-way unrolled loop
     // (measured faster than one array indexed by kt % NST)
     __shared__ __attribute__((aligned(16))) unsigned char sm0[ST_BYTES], sm1[ST_BYTES], sm2[ST_BYTES];
@@ -235,16 +283,30 @@ __global__ __launch_bounds__(kGThreads, 1) void k_gemm_lds(GemmArgs a) {
         const int cl = q * (kWave / BCH) + lane / BCH, c = (lane % BCH) ^ swz<BCH>(cl);
         const uint16_t *mat = (KIND == GK_GATEUP && cl >= 32) ? a.b1 : a.b0;
         const int col = KIND == GK_GATEUP ? colw + (cl & 31) : colw + cl;
-        bsrc[q] = reinterpret_cast<const char *>(mat + (size_t)e * a.b_stride + (size_t)min(col, N - 1) * K) + c * 16;
+        bsrc[q] = reinterpret_cast<const char *>(mat) + ((size_t)e * a.b_stride + (size_t)min(col, N - 1) * K) * EB +
+                  c * 16;
+    }
+    // Q8_0: lane i copies the two scales of column i of the wave's 64
+    const char *ssrc = nullptr;
+    if constexpr (BQ) {
+        const uint16_t *sm = (KIND == GK_GATEUP && lane >= 32) ? a.s1 : a.s0;
+        const int col = KIND == GK_GATEUP ? colw + (lane & 31) : colw + lane;
+        ssrc = reinterpret_cast<const char *>(sm + a.s_stride * e + (size_t)min(col, N - 1) * (K / 32));
     }
     auto issue = [&](int kt, unsigned char *st) {
-        const size_t ka = (size_t)(kb + kt) * ARB, kbb = (size_t)(kb + kt) * BRB;
+        const int k0 = (kb + kt) * BK; // first reduction element of stage kt
+        const size_t ka = (size_t)k0 * 2 * AP, kbb = (size_t)k0 * EB;
 #pragma unroll
         for (int q = 0; q < A_DMA; q++)
             copy16_lds(asrc[q] + ka, st + (wave * A_DMA + q) * 1024);
 #pragma unroll
         for (int q = 0; q < B_DMA; q++)
             copy16_lds(bsrc[q] + kbb, st + A_BYTES + wave * WB_BYTES + q * 1024);
+        if constexpr (BQ)
+#pragma unroll
+            for (int j = 0; j < SCP; j++)
+                copy4_lds(ssrc + (size_t)(k0 / 32) * 2 + 4 * j,
+                          st + A_BYTES + kGW * WB_BYTES + wave * WS_BYTES + j * (kWave * 4));
     };
 
     f32x16 acc[MB][NB];
@@ -257,35 +319,102 @@ __global__ __launch_bounds__(kGThreads, 1) void k_gemm_lds(GemmArgs a) {
 
     auto compute = [&](const unsigned char *st) {
         const unsigned char *bw = st + A_BYTES + wave * WB_BYTES;
+        if constexpr (!BQ) {
 #pragma unroll
-        for (int s = 0; s < BK / 16; s++) {
-            // every read of the substep first, one wait, then the MFMAs.
-            // Lane l takes the 8 reduction elements g = 2s + l/32 of its row
-            // or column (split A: chunk 2g holds their hi, 2g+1 their lo).
-            const int g8 = 2 * s + (lane >> 5);
-            u32x4 v[NB + AP * MB];
+            for (int s = 0; s < BK / 16; s++) {
+                // every read of the substep first, one wait, then the MFMAs.
+                // Lane l takes the 8 reduction elements g = 2s + l/32 of its
+                // row or column (split A: chunk 2g holds their hi, 2g+1 their lo).
+                const int g8 = 2 * s + (lane >> 5);
+                u32x4 v[NB + AP * MB];
 #pragma unroll
-            for (int nb = 0; nb < NB; nb++) {
-                const int cl = nb * 32 + (lane & 31);
-                v[nb] = lds_load16(bw + cl * BRB + ((g8 ^ swz<BCH>(cl)) * 16));
-            }
+                for (int nb = 0; nb < NB; nb++) {
+                    const int cl = nb * 32 + (lane & 31);
+                    v[nb] = lds_load16(bw + cl * BRB + ((g8 ^ swz<BCH>(cl)) * 16));
+                }
 #pragma unroll
-            for (int mb = 0; mb < MB; mb++) {
-                const int r = mb * 32 + (lane & 31);
-#pragma unroll
-                for (int h = 0; h < AP; h++)
-                    v[NB + AP * mb + h] = lds_load16(st + r * ARB + (((AP * g8 + h) ^ swz<ACH>(r)) * 16));
-            }
-            lds_wait(v);
-#pragma unroll
-            for (int mb = 0; mb < MB; mb++)
-#pragma unroll
-                for (int nb = 0; nb < NB; nb++)
+                for (int mb = 0; mb < MB; mb++) {
+                    const int r = mb * 32 + (lane & 31);
 #pragma unroll
                     for (int h = 0; h < AP; h++)
-                        acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                            __builtin_bit_cast(bf16x8, v[NB + AP * mb + h]), __builtin_bit_cast(bf16x8, v[nb]),
-                            acc[mb][nb], 0, 0, 0);
+                        v[NB + AP * mb + h] = lds_load16(st + r * ARB + (((AP * g8 + h) ^ swz<ACH>(r)) * 16));
+                }
+                lds_wait(v);
+#pragma unroll
+                for (int mb = 0; mb < MB; mb++)
+#pragma unroll
+                    for (int nb = 0; nb < NB; nb++)
+#pragma unroll
+                        for (int h = 0; h < AP; h++)
+                            acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                                __builtin_bit_cast(bf16x8, v[NB + AP * mb + h]), __builtin_bit_cast(bf16x8, v[nb]),
+                                acc[mb][nb], 0, 0, 0);
+            }
+        } else {
+            // this lane's columns' scales of the stage: fp16 pairs (blocks 2j, 2j+1)
+            uint32_t sw[NB][SCP];
+#pragma unroll
+            for (int nb = 0; nb < NB; nb++)
+#pragma unroll
+                for (int j = 0; j < SCP; j++)
+                    sw[nb][j] = lds_load4(st + A_BYTES + kGW * WB_BYTES + wave * WS_BYTES + j * (kWave * 4) +
+                                          (nb * 32 + (lane & 31)) * 4);
+#pragma unroll
+            for (int bl = 0; bl < NBLK; bl++) {
+                f32x16 blk[MB][NB];
+#pragma unroll
+                for (int s = 2 * bl; s < 2 * bl + 2; s++) {
+                    // column bytes 16s + 8 (l/32) .. +7 of chunk s; A as above
+                    const int g8 = 2 * s + (lane >> 5);
+                    u32x2 q[NB];
+                    u32x4 v[AP * MB];
+#pragma unroll
+                    for (int nb = 0; nb < NB; nb++) {
+                        const int cl = nb * 32 + (lane & 31);
+                        q[nb] = lds_load8(bw + cl * BRB + ((s ^ swz<BCH>(cl)) * 16) + 8 * (lane >> 5));
+                    }
+#pragma unroll
+                    for (int mb = 0; mb < MB; mb++) {
+                        const int r = mb * 32 + (lane & 31);
+#pragma unroll
+                        for (int h = 0; h < AP; h++)
+                            v[AP * mb + h] = lds_load16(st + r * ARB + (((AP * g8 + h) ^ swz<ACH>(r)) * 16));
+                    }
+                    asm volatile("s_waitcnt lgkmcnt(0)");
+#pragma unroll
+                    for (int nb = 0; nb < NB; nb++) lds_keep(q[nb]);
+#pragma unroll
+                    for (int i = 0; i < AP * MB; i++) lds_keep(v[i]);
+                    if (s == 2 * bl) {
+#pragma unroll
+                        for (int nb = 0; nb < NB; nb++)
+#pragma unroll
+                            for (int j = 0; j < SCP; j++) lds_keep(sw[nb][j]);
+                    }
+#pragma unroll
+                    for (int nb = 0; nb < NB; nb++) {
+                        const u32x4 bv = q8x8_to_bf16(q[nb]);
+#pragma unroll
+                        for (int mb = 0; mb < MB; mb++)
+#pragma unroll
+                            for (int h = 0; h < AP; h++) {
+                                const f32x16 c = (s == 2 * bl && h == 0) ? f32x16{} : blk[mb][nb];
+                                blk[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                                    __builtin_bit_cast(bf16x8, v[AP * mb + h]), __builtin_bit_cast(bf16x8, bv), c,
+                                    0, 0, 0);
+                            }
+                    }
+                }
+#pragma unroll
+                for (int nb = 0; nb < NB; nb++) {
+                    const uint32_t pair = sw[nb][bl >> 1];
+                    const float sc = f16_bits_to_f32((uint16_t)((bl & 1) ? pair >> 16 : pair));
+#pragma unroll
+                    for (int mb = 0; mb < MB; mb++)
+#pragma unroll
+                        for (int r = 0; r < 16; r++) acc[mb][nb][r] = fmaf(sc, blk[mb][nb][r], acc[mb][nb][r]);
+                }
+            }
         }
     };
 
@@ -551,39 +680,44 @@ __global__ __launch_bounds__(kGThreads, 2) void k_gemm_reg(GemmArgs a) {
 }
 
 // a_mode: 0 = bf16 A rows (gate/up), 1 = split A rows (hi/lo pairs), 2 = fp32 A rows
-// (both down).
-static hipError_t run_gemm(int kind, int a_mode, GemmArgs &a, hipStream_t s) {
+// (both down).  bq: B is Q8_0 (a.s0 / a.s1 hold its scales); not with fp32 A.
+template <int KIND, bool AS>
+static void launch_lds(const GemmArgs &a, bool bq, unsigned grid, hipStream_t s) {
+    if (a.tile_rows == 32) {
+        if (bq) launch_kernel((k_gemm_lds<KIND, AS, 1, true>), dim3(grid), dim3(kGThreads), 0, s, a);
+        else launch_kernel((k_gemm_lds<KIND, AS, 1, false>), dim3(grid), dim3(kGThreads), 0, s, a);
+    } else {
+        if (bq) launch_kernel((k_gemm_lds<KIND, AS, kMB, true>), dim3(grid), dim3(kGThreads), 0, s, a);
+        else launch_kernel((k_gemm_lds<KIND, AS, kMB, false>), dim3(grid), dim3(kGThreads), 0, s, a);
+    }
+}
+
+static hipError_t run_gemm(int kind, int a_mode, bool bq, GemmArgs &a, hipStream_t s) {
     const int cols = kind == GK_GATEUP ? GemmShape<GK_GATEUP>::COLS : GemmShape<GK_PLAIN>::COLS;
     a.n_ntiles = (a.N + cols - 1) / cols;
     if (a.ksplit < 1) a.ksplit = 1;
     const int per_tile = a.n_ntiles * a.ksplit;
     if ((long)a.max_tiles * per_tile == 0) return hipSuccess;
     if (a_mode == 2) {
-        if (a.tile_rows != kBM) return hipErrorInvalidValue;
         // fp32 A (act handed in by a caller): register-staged kernel, A split
         // into bf16 hi/lo once per workgroup as it is written to LDS
+        if (a.tile_rows != kBM || bq) return hipErrorInvalidValue;
         const unsigned grid = (unsigned)(((long)a.max_tiles * per_tile + 7) / 8 * 8);
         launch_kernel((k_gemm_reg<GK_PLAIN, true>), dim3(grid), dim3(kGThreads), 0, s, a);
     } else {
         const unsigned grid = (unsigned)((long)a.max_tiles * per_tile);
-        const bool small = a.tile_rows == 32;
-        if (!small && a.tile_rows != kBM) return hipErrorInvalidValue;
-        if (kind == GK_GATEUP && a_mode == 0) {
-            if (small) launch_kernel((k_gemm_lds<GK_GATEUP, false, 1>), dim3(grid), dim3(kGThreads), 0, s, a);
-            else launch_kernel((k_gemm_lds<GK_GATEUP, false, kMB>), dim3(grid), dim3(kGThreads), 0, s, a);
-        } else if (kind == GK_PLAIN && a_mode == 1) {
-            if (small) launch_kernel((k_gemm_lds<GK_PLAIN, true, 1>), dim3(grid), dim3(kGThreads), 0, s, a);
-            else launch_kernel((k_gemm_lds<GK_PLAIN, true, kMB>), dim3(grid), dim3(kGThreads), 0, s, a);
-        } else {
-            return hipErrorInvalidValue;
-        }
+        if (a.tile_rows != 32 && a.tile_rows != kBM) return hipErrorInvalidValue;
+        if (kind == GK_GATEUP && a_mode == 0) launch_lds<GK_GATEUP, false>(a, bq, grid, s);
+        else if (kind == GK_PLAIN && a_mode == 1) launch_lds<GK_PLAIN, true>(a, bq, grid, s);
+        else return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }
 
 bool mfma_supported(const Layer &L) {
-    return L.xdt == DT_BF16 && L.edt == DT_BF16 && (L.Is == 0 || L.sdt == DT_BF16) && L.H % kBK == 0 &&
-           L.I % kBK == 0 && L.Is % kBK == 0;
+    const auto ok = [](int dt) { return dt == DT_BF16 || dt == DT_Q8; };
+    return L.xdt == DT_BF16 && ok(L.edt) && (L.Is == 0 || ok(L.sdt)) && L.H % kBK == 0 && L.I % kBK == 0 &&
+           L.Is % kBK == 0;
 }
 
 // Reduction slices of the routed down projection: enough workgroups to fill
@@ -617,6 +751,9 @@ hipError_t launch_gateup_mfma(const Layer &L, const void *x, const float *tok_sc
         a.b0 = static_cast<const uint16_t *>(routed.gate);
         a.b1 = static_cast<const uint16_t *>(routed.up);
         a.b_stride = (size_t)L.I * L.H;
+        a.s0 = routed.gate_s;
+        a.s1 = routed.up_s;
+        a.s_stride = (size_t)L.I * (L.H / 32);
         a.N = L.I;
         a.K = L.H;
         a.tok_scale = tok_scale;
@@ -624,7 +761,7 @@ hipError_t launch_gateup_mfma(const Layer &L, const void *x, const float *tok_sc
         a.out = act;
         a.ldo = L.I;
         a.out_split = act_split;
-        hipError_t err = run_gemm(GK_GATEUP, 0, a, s);
+        hipError_t err = run_gemm(GK_GATEUP, 0, L.edt == DT_Q8, a, s);
         if (err != hipSuccess) return err;
     }
     if (shared_act && L.Is > 0) {
@@ -635,6 +772,8 @@ hipError_t launch_gateup_mfma(const Layer &L, const void *x, const float *tok_sc
         a.max_tiles = (M + a.tile_rows - 1) / a.tile_rows;
         a.b0 = static_cast<const uint16_t *>(shared.gate);
         a.b1 = static_cast<const uint16_t *>(shared.up);
+        a.s0 = shared.gate_s;
+        a.s1 = shared.up_s;
         a.N = L.Is;
         a.K = L.H;
         a.tok_scale = tok_scale;
@@ -642,7 +781,7 @@ hipError_t launch_gateup_mfma(const Layer &L, const void *x, const float *tok_sc
         a.out = shared_act;
         a.ldo = L.Is;
         a.out_split = act_split;
-        return run_gemm(GK_GATEUP, 0, a, s);
+        return run_gemm(GK_GATEUP, 0, L.sdt == DT_Q8, a, s);
     }
     return hipSuccess;
 }
@@ -663,11 +802,13 @@ hipError_t launch_down_mfma(const Layer &L, const float *act, const float *share
         a.slab = (size_t)M * L.k * L.H;
         a.b0 = static_cast<const uint16_t *>(routed.down);
         a.b_stride = (size_t)L.H * L.I;
+        a.s0 = routed.down_s;
+        a.s_stride = (size_t)L.H * (L.I / 32);
         a.N = L.H;
         a.K = L.I;
         a.out = y_routes;
         a.ldo = L.H;
-        hipError_t err = run_gemm(GK_PLAIN, act_split ? 1 : 2, a, s);
+        hipError_t err = run_gemm(GK_PLAIN, act_split ? 1 : 2, L.edt == DT_Q8, a, s);
         if (err != hipSuccess) return err;
     }
     if (shared_act && L.Is > 0) {
@@ -677,11 +818,12 @@ hipError_t launch_down_mfma(const Layer &L, const float *act, const float *share
         a.tile_rows = act_split && M <= 32 ? 32 : kBM;
         a.max_tiles = (M + a.tile_rows - 1) / a.tile_rows;
         a.b0 = static_cast<const uint16_t *>(shared.down);
+        a.s0 = shared.down_s;
         a.N = L.H;
         a.K = L.Is;
         a.out = y_shared;
         a.ldo = L.H;
-        return run_gemm(GK_PLAIN, act_split ? 1 : 2, a, s);
+        return run_gemm(GK_PLAIN, act_split ? 1 : 2, L.sdt == DT_Q8, a, s);
     }
     return hipSuccess;
 }

@@ -52,11 +52,13 @@ bool use_mfma(const moe_plan *p, int M) {
     if (!p->mfma_capable) return false;
     if (p->cfg.path == MOE_PATH_MFMA) return true;
     if (p->cfg.path == MOE_PATH_GEMV) return false;
-    // From about two routes per expert on, the grouped GEMM (32-row tiles at
-    // small batches) beats the per-row kernels, whose dot-product work grows
-    // with the tokens each expert sees.
+    // From about two routes per expert on (four with Q8_0 experts, whose
+    // int8 conversion and block scales cost the grouped GEMM more), the
+    // grouped GEMM (32-row tiles at small batches) beats the per-row kernels,
+    // whose dot-product work grows with the tokens each expert sees.
     const long routes = (long)M * p->L.k;
-    return M >= 8 && routes >= 2L * p->L.E;
+    const long per_expert = p->L.edt == moe::DT_Q8 ? 4 : 2;
+    return M >= 8 && routes >= per_expert * p->L.E;
 }
 
 WsLayout layout(const moe_plan *p, int M) {
@@ -83,9 +85,13 @@ WsLayout layout(const moe_plan *p, int M) {
     w.tiles = take(mfma ? (size_t)(2 + L.E + 2 * w.max_tiles) * 4 : 4 * 3);
     w.act = take(R * L.I * 4);
     w.shared_act = take(L.Is > 0 ? (size_t)M * L.Is * 4 : 0);
-    // (fewer tile rows never give more reduction slices)
-    w.y_routes = take((size_t)(mfma ? moe::down_ksplit(L, M, moe::mfma_tile_rows()) : moe::down_gemv_slices(L.I)) *
-                      R * L.H * 4);
+    // (fewer tile rows never give more reduction slices; moe_combine with
+    // Q8_0 experts uses the row kernels' slices even when the layer call
+    // takes the grouped GEMM)
+    const size_t slices = mfma ? std::max(moe::down_ksplit(L, M, moe::mfma_tile_rows()),
+                                          L.edt == moe::DT_Q8 ? moe::down_gemv_slices(L.I) : 1)
+                               : moe::down_gemv_slices(L.I);
+    w.y_routes = take(slices * R * L.H * 4);
     w.y_shared = take(L.Is > 0 ? (size_t)(mfma ? 1 : moe::down_gemv_slices(L.Is)) * M * L.H * 4 : 0);
     w.total = o;
     return w;
@@ -140,13 +146,13 @@ moe_status check_experts(const moe_plan *p, const moe_weights *w, bool need_gate
         TRY(need_ptr(w->gate, 16, "weights.gate"));
         TRY(need_ptr(w->up, 16, "weights.up"));
         if (q8) {
-            TRY(need_ptr(w->gate_scale, 2, "weights.gate_scale"));
-            TRY(need_ptr(w->up_scale, 2, "weights.up_scale"));
+            TRY(need_ptr(w->gate_scale, 4, "weights.gate_scale"));
+            TRY(need_ptr(w->up_scale, 4, "weights.up_scale"));
         }
     }
     if (need_down) {
         TRY(need_ptr(w->down, 16, "weights.down"));
-        if (q8) TRY(need_ptr(w->down_scale, 2, "weights.down_scale"));
+        if (q8) TRY(need_ptr(w->down_scale, 4, "weights.down_scale"));
     }
     if (need_shared && p->L.Is > 0) {
         const bool sq8 = p->L.sdt == moe::DT_Q8;
@@ -154,9 +160,9 @@ moe_status check_experts(const moe_plan *p, const moe_weights *w, bool need_gate
         TRY(need_ptr(w->shared_up, 16, "weights.shared_up"));
         TRY(need_ptr(w->shared_down, 16, "weights.shared_down"));
         if (sq8) {
-            TRY(need_ptr(w->shared_gate_scale, 2, "weights.shared_gate_scale"));
-            TRY(need_ptr(w->shared_up_scale, 2, "weights.shared_up_scale"));
-            TRY(need_ptr(w->shared_down_scale, 2, "weights.shared_down_scale"));
+            TRY(need_ptr(w->shared_gate_scale, 4, "weights.shared_gate_scale"));
+            TRY(need_ptr(w->shared_up_scale, 4, "weights.shared_up_scale"));
+            TRY(need_ptr(w->shared_down_scale, 4, "weights.shared_down_scale"));
         }
     }
     return MOE_OK;
@@ -339,7 +345,8 @@ moe_status moe_combine(const moe_plan *p, const float *act, const moe_weights *w
     LAUNCH(moe::launch_plan_from_offsets(L.E, moe::mfma_tile_rows(), offsets, active, tiles, s), "plan");
     const moe::Routing rt{offsets, sorted_routes, route_pos, active, tiles};
     const moe::Mats none{};
-    if (use_mfma(p, M)) {
+    // (the fp32-act grouped GEMM reads bf16 weights only)
+    if (use_mfma(p, M) && L.edt == moe::DT_BF16) {
         float *yr = at<float>(ws, lay.y_routes);
         LAUNCH(moe::launch_down_mfma(L, act, nullptr, routed_mats(wts), none, rt, M, lay.max_tiles, moe::mfma_tile_rows(),
                                      yr, nullptr, false, s),

@@ -69,7 +69,8 @@ def _create(**kw):
     (dict(expert_dtype=7), m.MOE_ERR_INVALID),
     (dict(shared_inter=64, shared_dtype=m.MOE_Q8_0), m.MOE_ERR_UNSUPPORTED),
     (dict(path=5), m.MOE_ERR_INVALID),
-    (dict(path=m.MOE_PATH_MFMA, expert_dtype=m.MOE_Q8_0), m.MOE_ERR_UNSUPPORTED),
+    (dict(path=m.MOE_PATH_MFMA, x_dtype=m.MOE_F32), m.MOE_ERR_UNSUPPORTED),
+    (dict(path=m.MOE_PATH_MFMA, expert_dtype=m.MOE_F32), m.MOE_ERR_UNSUPPORTED),
 ])
 def test_plan_refusals(kw, status):
     with pytest.raises(m.MoeError) as ei:
@@ -146,8 +147,8 @@ def test_call_refusals_before_any_launch():
 
 def test_forward_path_choice():
     import synth
-    # gpt-oss: Q8_0 experts have no MFMA path; the others switch to it from
-    # about two routes per expert (Mixtral M=16: 4, DeepSeek M=16: 1.5)
+    # the grouped GEMM from two routes per expert (four with Q8_0 experts):
+    # Mixtral M=16: 4, DeepSeek M=16: 1.5, gpt-oss (Q8_0) M=16: 2
     want = {("gpt-oss-20b", 1): "single", ("gpt-oss-20b", 16): "gemv",
             ("mixtral-8x7b", 1): "single", ("mixtral-8x7b", 16): "mfma", ("mixtral-8x7b", 512): "mfma",
             ("qwen3-30b-a3b", 2048): "mfma", ("deepseek-v2-lite", 16): "gemv"}

@@ -210,6 +210,10 @@ MFMA_SMALL = [
     ("zipf-rms", dict(hidden=256, num_experts=64, top_k=8, expert_inter=128, bias_mode=BIAS_LOGIT,
                       bias_kind="zipf", rms_eps=1e-6), (1, 257)),
     ("wide-n", dict(hidden=128, num_experts=4, top_k=1, expert_inter=576), (129,)),
+    ("q8", dict(hidden=256, num_experts=8, top_k=2, expert_inter=192, expert_dtype=Q8_0), (16, 70, 200)),
+    ("q8-shared-bias-clamp", dict(hidden=192, num_experts=16, top_k=4, expert_inter=128, shared_inter=256,
+                                  expert_dtype=Q8_0, shared_dtype=Q8_0, bias_mode=BIAS_LOGIT,
+                                  bias_kind="normal", swiglu_limit=0.5), (3, 33, 100)),
 ]
 
 
@@ -227,11 +231,14 @@ def test_forward_mfma_small(name, kw, Ms):
         forward_parity(spec, layer, x, dl, what=f"mfma {name} M={M}")
 
 
-def test_stages_mfma():
-    """moe_expert_ffn and moe_combine on the MFMA path equal the oracle."""
+@pytest.mark.parametrize("wdt", [BF16, Q8_0], ids=["bf16", "q8"])
+def test_stages_mfma(wdt):
+    """moe_expert_ffn and moe_combine on the MFMA path equal the oracle (with
+    Q8_0 experts moe_combine's fp32 act takes the row kernels)."""
     import mixture_experts_gemv_amd as m
     spec = synth.small_spec(hidden=256, num_experts=8, top_k=2, expert_inter=320,
-                            bias_mode=BIAS_LOGIT, bias_kind="normal", swiglu_limit=1.0, seed=1350)
+                            bias_mode=BIAS_LOGIT, bias_kind="normal", swiglu_limit=1.0, seed=1350,
+                            expert_dtype=wdt)
     layer = synth.make_layer(spec)
     M = 150
     x = synth.make_tokens(spec, M)
