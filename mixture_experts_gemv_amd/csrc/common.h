@@ -62,14 +62,16 @@ __device__ __forceinline__ float i8_to_f32(uint32_t w) {
 
 // ---------------------------------------------------------- wave reductions
 // DPP controls: quad_perm(1,0,3,2), quad_perm(2,3,0,1), row_half_mirror,
-// row_mirror; then a ds_swizzle xor-16 across the 32-lane halves and a
-// readlane of lanes 0 and 32.  Every step pairs each lane with exactly one
-// partner, so every lane ends with the same, order-fixed result.
+// row_mirror.  Each step pairs every lane with exactly one partner in its
+// 16-lane row, so after the four steps every lane of a row holds that row's
+// result; the four rows' results are then read from lanes 0, 16, 32 and 48
+// and combined as (r0 op r1) op (r2 op r3), so every lane ends with the same,
+// order-fixed value.  (Reading the rows out with readlane replaces a
+// ds_swizzle step, which goes through the LDS unit.)
 __device__ __forceinline__ int dpp_xor1(int v) { return __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false); }
 __device__ __forceinline__ int dpp_xor2(int v) { return __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false); }
 __device__ __forceinline__ int dpp_hmirror(int v) { return __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false); }
 __device__ __forceinline__ int dpp_mirror(int v) { return __builtin_amdgcn_update_dpp(0, v, 0x140, 0xF, 0xF, false); }
-__device__ __forceinline__ int swz_xor16(int v) { return __builtin_amdgcn_ds_swizzle(v, 0x401F); }
 
 struct OpSum { __device__ float operator()(float a, float b) const { return a + b; } };
 struct OpMaxF { __device__ float operator()(float a, float b) const { return fmaxf(a, b); } };
@@ -81,10 +83,12 @@ __device__ __forceinline__ float wave_reduce(float v, Op op) {
     v = op(v, __int_as_float(dpp_xor2(__float_as_int(v))));
     v = op(v, __int_as_float(dpp_hmirror(__float_as_int(v))));
     v = op(v, __int_as_float(dpp_mirror(__float_as_int(v))));
-    v = op(v, __int_as_float(swz_xor16(__float_as_int(v))));
-    float lo = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
-    float hi = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
-    return op(lo, hi);
+    const int b = __float_as_int(v);
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(b, 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(b, 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(b, 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(b, 48));
+    return op(op(r0, r1), op(r2, r3));
 }
 __device__ __forceinline__ float wave_sum(float v) { return wave_reduce(v, OpSum()); }
 __device__ __forceinline__ float wave_max(float v) { return wave_reduce(v, OpMaxF()); }
@@ -96,9 +100,8 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
     v = umax32(v, (uint32_t)dpp_xor2((int)v));
     v = umax32(v, (uint32_t)dpp_hmirror((int)v));
     v = umax32(v, (uint32_t)dpp_mirror((int)v));
-    v = umax32(v, (uint32_t)swz_xor16((int)v));
-    return umax32((uint32_t)__builtin_amdgcn_readlane((int)v, 0),
-                  (uint32_t)__builtin_amdgcn_readlane((int)v, 32));
+    return umax32(umax32((uint32_t)__builtin_amdgcn_readlane((int)v, 0), (uint32_t)__builtin_amdgcn_readlane((int)v, 16)),
+                  umax32((uint32_t)__builtin_amdgcn_readlane((int)v, 32), (uint32_t)__builtin_amdgcn_readlane((int)v, 48)));
 }
 
 __device__ __forceinline__ int wave_min_i32(int v) {
@@ -106,8 +109,8 @@ __device__ __forceinline__ int wave_min_i32(int v) {
     v = min(v, dpp_xor2(v));
     v = min(v, dpp_hmirror(v));
     v = min(v, dpp_mirror(v));
-    v = min(v, swz_xor16(v));
-    return min(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 32));
+    return min(min(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
+               min(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
 }
 
 // fp32 -> uint32 whose unsigned order is the float order (-0 taken as +0).
