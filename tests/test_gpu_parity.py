@@ -339,7 +339,7 @@ def test_forward_timed_matches_forward(M, path, want):
 
 
 # ------------------------------------------------------------ full-size layers
-FULL = [("tiny", 4, None), ("gpt-oss-20b", 1, None), ("gpt-oss-20b", 16, None),
+FULL = [("tiny", 4, None), ("gpt-oss-20b", 1, None), ("gpt-oss-20b", 16, None), ("gpt-oss-20b", 64, 8),
         ("deepseek-v2-lite", 1, None), ("deepseek-v2-lite", 16, None),
         ("mixtral-8x7b", 1, None), ("mixtral-8x7b", 16, None),
         ("mixtral-8x7b", 512, 12), ("qwen3-30b-a3b", 2048, 24)]
@@ -347,6 +347,8 @@ FULL = [("tiny", 4, None), ("gpt-oss-20b", 1, None), ("gpt-oss-20b", 16, None),
 
 @pytest.mark.parametrize("name,M,nsample", FULL, ids=[f"{n}-M{m}" for n, m, _ in FULL])
 def test_forward_full_size(name, M, nsample):
+    """Every workload at its real shape (gpt-oss-shaped M = 64: the Q8_0
+    grouped GEMM, 2880-wide matrices with a ragged last column tile)."""
     say(f"generate {name}")
     spec, layer = host_layer(name)
     say(f"upload {name}")
