@@ -90,7 +90,8 @@ typedef enum {
 typedef enum {
     MOE_PATH_AUTO = 0, /* GEMV kernels for small batches, MFMA grouped GEMM for large */
     MOE_PATH_GEMV = 1, /* always the bandwidth-bound GEMV kernels */
-    MOE_PATH_MFMA = 2  /* always the MFMA grouped GEMM (bf16 x and experts only) */
+    MOE_PATH_MFMA = 2  /* always the MFMA grouped GEMM (bf16 x; bf16 or Q8_0 experts;
+                          H, I and Is multiples of 64) */
 } moe_path;
 
 /* Layer description.  Validated once by moe_plan_create (fail at open). */
@@ -135,8 +136,9 @@ typedef struct moe_plan moe_plan; /* host-side, library-owned */
 /* Validate `cfg` and build a plan.  MOE_ERR_INVALID for inconsistent values
  * (E or k < 1, k > E, H, I <= 0, Is < 0, max_tokens < 1, unknown enums);
  * MOE_ERR_UNSUPPORTED for k > 8, E > 256, H, I or Is not a multiple of 32, a
- * dtype combination the kernels do not cover, or MOE_PATH_MFMA without bf16 x
- * and bf16 experts.  Refusal happens here, before any device work, in the
+ * dtype combination the kernels do not cover, or MOE_PATH_MFMA without bf16 x,
+ * bf16 or Q8_0 experts and H, I, Is multiples of 64.  Refusal happens here,
+ * before any device work, in the
  * manner of the pages' state constructors (llama/state.rs and
  * deepseek2/state.rs, the `build` functions' open-time checks).
  * On success *plan owns host memory only; free it with moe_plan_destroy. */
