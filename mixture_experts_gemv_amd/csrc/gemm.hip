@@ -1,6 +1,6 @@
 // MFMA grouped-GEMM path of the routed MoE layer (bf16 operands, fp32
-// accumulate), for batches large enough that every touched expert sees many
-// tokens: the per-expert products are then real dense contractions.
+// accumulate), for batches in which the touched experts see several tokens
+// each: the per-expert products are then dense contractions.
 //
 // Uses:
 //   gate/up  A = gathered token rows of x, B = gate and up rows of the tile's
@@ -9,23 +9,26 @@
 //   down     A = act rows carried as bf16 hi + lo (so the product keeps about
 //            16 bits of act), B = down rows -> per-route outputs;
 //   shared   the same two with identity rows (all tokens), for a shared expert.
-// (The router has its own small-tile kernel at the end of this file.)
+// B is bf16 or Q8_0 (int8 plus fp16 scales per 32 reduction elements,
+// converted exactly to bf16 in registers; each block's products are scaled
+// once).  (The router has its own small-tile kernel at the end of this file.)
 //
 // Tiles: 128 rows (tokens or routes of one expert, so that most experts'
 // tokens share one pass over the weights), or 32 rows when a batch gives the
-// experts few routes each (less MFMA and LDS work on empty rows), x 128 (gate/up: 32 columns
-// of gate and of up per wave) or 256 (down: 64 columns per wave) output
-// columns.  Four waves each own all 128 rows of their columns and issue
-// v_mfma_f32_32x32x16_bf16.
+// experts few routes each (less MFMA and LDS work on empty rows), x 128
+// (gate/up: 32 columns of gate and of up per wave) or 256 (down: 64 columns
+// per wave) output columns.  Four waves each own all rows of their columns
+// and issue v_mfma_f32_32x32x16_bf16.
 //
 // Two kernels:
-//   k_gemm_lds  both operands go global -> LDS with asynchronous 16-byte
-//     copies (global_load_lds_dwordx4) in a 3-stage pipeline, XOR-swizzled
-//     rows; 64 reduction elements a stage for bf16 A, 32 for split A (whose
-//     stage rows hold hi and lo chunks, and whose MFMAs run once per half);
-//   k_gemm_reg (fp32 A handed in by a caller of the stage-wise entry points)
-//     A is staged through registers into LDS (double buffered, split into
-//     hi/lo once as it is written), B fragments are loaded straight into
+//   k_gemm_lds  both operands go global -> LDS with asynchronous copies
+//     (global_load_lds_dwordx4) in a 3-stage pipeline, XOR-swizzled rows;
+//     64 reduction elements a stage for bf16 A or Q8_0 B, else 32 for split A
+//     (whose stage rows hold hi and lo chunks, and whose MFMAs run once per
+//     half);
+//   k_gemm_reg (fp32 A handed in by a caller of the stage-wise entry points,
+//     bf16 B) A is staged through registers into LDS (double buffered, split
+//     into hi/lo once as it is written), B fragments are loaded straight into
 //     registers, one step ahead.
 // (Rounding act to a single bf16 instead measured about 1.5x faster in the
 // down GEMM, but at an output error of about 1.6e-3 relative L2 against

@@ -16,6 +16,12 @@ Usage (on the output directories rocprofv3 wrote)::
     python -m mixture_experts_gemv_amd.profiling traffic --kernel k_gateup_m1 \\
         --workload gpt-oss-20b_M1 --fetch DIR --write DIR --copy-fetch DIR \\
         --copy-write DIR --copy-bytes N --command C --out FILE.json
+    python -m mixture_experts_gemv_amd.profiling restamp profiles --commit C
+
+The digest covers the code only (comments and layout removed), so a comment
+edit keeps the records valid; `restamp` re-stamps records after such edits
+once it has checked that the code equals that of the commit the counters
+were taken at.
 """
 
 from __future__ import annotations
@@ -34,16 +40,26 @@ ROOT = os.path.dirname(PKG)
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 
 
+_COMMENT = re.compile(r"//[^\n]*|/\*.*?\*/", re.S)
+
+
+def _code_only(text: str) -> str:
+    """C/C++ source with comments removed and whitespace runs collapsed, so
+    that editing a comment does not change the digest of the code."""
+    return " ".join(_COMMENT.sub(" ", text).split())
+
+
 def source_digest() -> str:
-    """sha256 over the library's kernel and ABI sources (names and bytes)."""
+    """sha256 over the library's kernel and ABI sources (file names and code,
+    comments and layout excluded)."""
     h = hashlib.sha256()
     files = sorted(glob.glob(os.path.join(PKG, "csrc", "*")) + glob.glob(os.path.join(ROOT, "include", "*.h")))
     for f in files:
-        if not os.path.isfile(f):
+        if not os.path.isfile(f) or not f.endswith((".hip", ".h", ".cpp", ".cc")):
             continue
         h.update(os.path.basename(f).encode() + b"\0")
-        with open(f, "rb") as fh:
-            h.update(fh.read())
+        with open(f, encoding="utf-8") as fh:
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()
 
 
@@ -141,6 +157,35 @@ def load_traffic(profiles_dir: str, kernel: str, workload: str) -> dict | None:
     return None
 
 
+def restamp(args) -> int:
+    """Give the traffic records in `args.dir` the current digest, after
+    checking that every source's code (comments and layout aside) equals its
+    code at `args.commit`, the commit the counters were taken at."""
+    import subprocess
+    srcs = sorted(glob.glob(os.path.join(PKG, "csrc", "*")) + glob.glob(os.path.join(ROOT, "include", "*.h")))
+    for f in srcs:
+        if not f.endswith((".hip", ".h", ".cpp", ".cc")):
+            continue
+        rel = os.path.relpath(f, ROOT)
+        old = subprocess.run(["git", "-C", ROOT, "show", f"{args.commit}:{rel}"], capture_output=True, text=True)
+        if old.returncode != 0:
+            print(f"{rel}: not in {args.commit}", file=sys.stderr)
+            return 1
+        with open(f, encoding="utf-8") as fh:
+            if _code_only(old.stdout) != _code_only(fh.read()):
+                print(f"{rel}: code differs from {args.commit}; take the counters again", file=sys.stderr)
+                return 1
+    digest = source_digest()
+    for f in sorted(glob.glob(os.path.join(args.dir, "*.traffic.json"))):
+        with open(f) as fh:
+            rec = json.load(fh)
+        rec["source_sha256"] = digest
+        with open(f, "w") as fh:
+            json.dump(rec, fh, indent=1)
+            fh.write("\n")
+    return 0
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(prog="python -m mixture_experts_gemv_amd.profiling")
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -153,7 +198,12 @@ def main(argv=None) -> int:
     for k in ("kernel", "workload", "fetch", "write", "copy-fetch", "copy-write", "command", "out"):
         t.add_argument("--" + k, required=True)
     t.add_argument("--copy-bytes", type=int, required=True)
+    r = sub.add_parser("restamp")
+    r.add_argument("dir")
+    r.add_argument("--commit", required=True)
     args = ap.parse_args(argv)
+    if args.cmd == "restamp":
+        return restamp(args)
     (write_stats if args.cmd == "stats" else write_traffic)(args)
     return 0
 
