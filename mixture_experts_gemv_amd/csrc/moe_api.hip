@@ -227,7 +227,8 @@ moe_status moe_plan_create(const moe_config *c, moe_plan **out) {
     const bool mfma_ok = moe::mfma_supported(L);
     if (c->path == MOE_PATH_MFMA && !mfma_ok)
         return fail(MOE_ERR_UNSUPPORTED,
-                    "the MFMA path needs bf16 x and experts and hidden, expert_inter, shared_inter multiples of 64");
+                    "the MFMA path needs bf16 x, bf16 or Q8_0 experts and hidden, expert_inter, shared_inter "
+                    "multiples of 64");
     moe_plan *p = new moe_plan;
     p->cfg = *c;
     p->L = L;
