@@ -287,7 +287,9 @@ def main() -> int:
         "dtype": "f32",
         "data": "synthetic",
         "config": {
-            "workload": f"{spec.name}-shaped routed MoE layer, M={M} tokens per call",
+            "workload": (f"{spec.name}-shaped dense SwiGLU layer (one expert, top-1), M={M} tokens per call"
+                         if spec.num_experts == 1 else
+                         f"{spec.name}-shaped routed MoE layer, M={M} tokens per call"),
             "hidden": spec.hidden, "num_experts": spec.num_experts, "top_k": spec.top_k,
             "expert_inter": spec.expert_inter, "shared_inter": spec.shared_inter,
             "expert_weights": {0: "f32", 1: "bf16", 2: "q8_0"}[spec.expert_dtype],

@@ -724,8 +724,8 @@ bool mfma_supported(const Layer &L) {
 }
 
 // Reduction slices of the routed down projection: enough workgroups to fill
-// the chip (about 512) when an M-token batch has few token tiles, keeping at
-// least 4 K steps per slice.  The slices' outputs are summed, in slice order,
+// the chip (about 512) when an M-token batch has few token tiles (up to 16
+// slices, for one-expert layers), keeping at least 4 K steps per slice.  The slices' outputs are summed, in slice order,
 // by the combine.  Token tiles are estimated as at least one per expert the
 // routes can touch.
 int down_ksplit(const Layer &L, int M, int tile_rows) {
@@ -734,7 +734,7 @@ int down_ksplit(const Layer &L, int M, int tile_rows) {
     const long ntiles = (L.H + GemmShape<GK_PLAIN>::COLS - 1) / GemmShape<GK_PLAIN>::COLS;
     const int nk = L.I / kBK;
     int S = 1;
-    while (tiles * ntiles * S < 512 && S < 4 && nk / (2 * S) >= 4) S *= 2;
+    while (tiles * ntiles * S < 512 && S < 16 && nk / (2 * S) >= 4) S *= 2;
     return S;
 }
 

@@ -99,6 +99,11 @@ SPECS: Dict[str, LayerSpec] = {
         name="qwen3-30b-a3b", hidden=2048, num_experts=128, top_k=8,
         expert_inter=768, bias_mode=BIAS_LOGIT, bias_kind="zipf",
         rms_eps=1e-6, seed=1005, token_counts=(2048,)),
+    # the dense lead layer of the DeepSeek-V2-Lite shape (layer 0: one dense
+    # SwiGLU 10944 wide), run as the one-expert, top-1 case of the same path
+    "deepseek-v2-lite-dense": LayerSpec(
+        name="deepseek-v2-lite-dense", hidden=2048, num_experts=1, top_k=1,
+        expert_inter=10944, seed=1006, token_counts=(1, 16, 512)),
 }
 
 _NTHREADS = max(1, min(16, len(os.sched_getaffinity(0))))

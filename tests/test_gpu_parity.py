@@ -342,7 +342,9 @@ def test_forward_timed_matches_forward(M, path, want):
 FULL = [("tiny", 4, None), ("gpt-oss-20b", 1, None), ("gpt-oss-20b", 16, None), ("gpt-oss-20b", 64, 8),
         ("deepseek-v2-lite", 1, None), ("deepseek-v2-lite", 16, None),
         ("mixtral-8x7b", 1, None), ("mixtral-8x7b", 16, None),
-        ("mixtral-8x7b", 512, 12), ("qwen3-30b-a3b", 2048, 24)]
+        ("mixtral-8x7b", 512, 12), ("qwen3-30b-a3b", 2048, 24),
+        ("deepseek-v2-lite-dense", 1, None), ("deepseek-v2-lite-dense", 16, None),
+        ("deepseek-v2-lite-dense", 512, 8)]
 
 
 @pytest.mark.parametrize("name,M,nsample", FULL, ids=[f"{n}-M{m}" for n, m, _ in FULL])
