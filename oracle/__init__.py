@@ -39,6 +39,8 @@ MUTANTS = {
     14: "selection-only bias leaks into the softmax",
     15: "gate clamped from above only",
     16: "pre-norm applied to the router input only",
+    17: "sigmoid mode adds the correction bias to the logit",
+    18: "sigmoid mode leaves the weights unnormalised",
 }
 
 

@@ -19,7 +19,13 @@
  *         RealGptOssState.per_expert_ones (the per-expert weighting is a
  *         no-op, so selection reduces to softmax over the selected), or
  *       - softmax over all experts, then top-k with NO renormalisation:
- *         deepseek2/state.rs module doc (decoder-layer sketch).
+ *         deepseek2/state.rs module doc (decoder-layer sketch), or
+ *       - sigmoid scores: llama/state.rs, RealLlamaState::build (the
+ *         MiniMax branch requires sigmoid router scoring and a finite fp32
+ *         per-expert e_score_correction_bias).  Reading: the correction bias
+ *         is added to the sigmoid score for the selection only, and the
+ *         weights are the selected experts' sigmoid scores divided by their
+ *         sum.
  *   expert          SwiGLU down(silu(gate.x) * (up.x)) per selected expert,
  *       optionally clamped: gptoss/state.rs module doc (clamped SwiGLU).
  *   combine         y = shared + sum_j w_j * expert_j(x), seeded with zeros
@@ -50,7 +56,7 @@
 #include <string.h>
 
 enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_Q8_0 = 2 };
-enum { ORC_TOPK_SOFTMAX = 0, ORC_SOFTMAX_ALL_NORENORM = 1 };
+enum { ORC_TOPK_SOFTMAX = 0, ORC_SOFTMAX_ALL_NORENORM = 1, ORC_SIGMOID_NORM = 2 };
 enum { ORC_BIAS_NONE = 0, ORC_BIAS_LOGIT = 1, ORC_BIAS_SELECT_ONLY = 2 };
 
 typedef struct {
@@ -80,7 +86,9 @@ enum {
     MUT_SELECT_ONLY_BIAS_IN_SOFTMAX = 14,
     MUT_CLAMP_GATE_UPPER_ONLY = 15,
     MUT_NORM_ROUTER_ONLY = 16,
-    MUT_COUNT = 17
+    MUT_SIGMOID_BIAS_BEFORE = 17,   /* sigmoid mode: correction bias added to the logit, not the score */
+    MUT_SIGMOID_NO_RENORM = 18,     /* sigmoid mode: weights are the raw scores */
+    MUT_COUNT = 19
 };
 static int orc_mutant = MUT_NONE;
 
@@ -171,8 +179,9 @@ void orc_router_logits(const orc_layer *L, int M, const double *xn, const void *
 }
 
 /* ---- steps 2-4: bias, top-k, weights for one token ----
- * s = selection key, u = softmax input:
- *   NONE: s = u = l;  LOGIT: s = u = l + b;  SELECT_ONLY: s = l + b, u = l.
+ * s = selection key, u = softmax input (sigmoid mode: the score):
+ *   NONE: s = u = l;  LOGIT: s = u = l + b;  SELECT_ONLY: s = l + b, u = l;
+ *   sigmoid mode: u = sigmoid(l), s = u (+ b with any bias mode).
  * If `forced` is non-NULL its k ids are taken as the selection (slot order
  * kept) and only the weights are computed. */
 static void orc_select_token(const orc_layer *L, const double *l, const float *bias,
@@ -184,6 +193,14 @@ static void orc_select_token(const orc_layer *L, const double *l, const float *b
     for (int e = 0; e < E; e++) {
         double b = bias ? (double)bias[e] : 0.0;
         s[e] = u[e] = l[e];
+        if (L->select == ORC_SIGMOID_NORM) {
+            const double bb = L->bias_mode != ORC_BIAS_NONE ? b : 0.0;
+            u[e] = 1.0 / (1.0 + exp(-l[e]));
+            s[e] = u[e] + bb;
+            if (orc_mutant == MUT_SIGMOID_BIAS_BEFORE)
+                s[e] = 1.0 / (1.0 + exp(-(l[e] + bb)));
+            continue;
+        }
         if (L->bias_mode == ORC_BIAS_LOGIT) {
             s[e] = l[e] + b;
             u[e] = l[e] + b;
@@ -214,7 +231,14 @@ static void orc_select_token(const orc_layer *L, const double *l, const float *b
     }
     int over_all = (L->select == ORC_SOFTMAX_ALL_NORENORM && orc_mutant != MUT_ALL_MODE_RENORMALISES) ||
                    (L->select == ORC_TOPK_SOFTMAX && orc_mutant == MUT_TOPK_SOFTMAX_OVER_ALL);
-    if (!over_all) {
+    if (L->select == ORC_SIGMOID_NORM) {
+        /* the selected experts' scores, divided by their sum */
+        double z = 0.0;
+        for (int j = 0; j < k; j++)
+            z += u[ids[j]];
+        for (int j = 0; j < k; j++)
+            w[j] = orc_mutant == MUT_SIGMOID_NO_RENORM ? u[ids[j]] : u[ids[j]] / z;
+    } else if (!over_all) {
         /* softmax restricted to the k selected experts */
         double m = u[ids[0]];
         for (int j = 1; j < k; j++)

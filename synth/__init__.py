@@ -36,7 +36,7 @@ from typing import Dict, Optional
 import numpy as np
 
 F32, BF16, Q8_0 = 0, 1, 2
-TOPK_SOFTMAX, SOFTMAX_ALL_NORENORM = 0, 1
+TOPK_SOFTMAX, SOFTMAX_ALL_NORENORM, SIGMOID_NORM = 0, 1, 2
 BIAS_NONE, BIAS_LOGIT, BIAS_SELECT_ONLY = 0, 1, 2
 
 STREAMS = ("x", "router", "bias", "gate", "up", "down", "shared_gate",

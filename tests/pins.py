@@ -30,7 +30,7 @@ import numpy as np
 import oracle
 import synth
 from synth import BF16, F32, Q8_0, BIAS_LOGIT, BIAS_NONE, BIAS_SELECT_ONLY
-from synth import SOFTMAX_ALL_NORENORM, TOPK_SOFTMAX
+from synth import SIGMOID_NORM, SOFTMAX_ALL_NORENORM, TOPK_SOFTMAX
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
@@ -199,6 +199,58 @@ def pin_bias_semantics():
 
 
 # ---------------------------------------------------------------------------
+# sigmoid scoring with a selection-only correction bias
+# (llama/state.rs, RealLlamaState::build, MiniMax branch; weights read as the
+# selected scores divided by their sum)
+# ---------------------------------------------------------------------------
+def _sig(v):
+    return 1.0 / (1.0 + math.exp(-v))
+
+
+def pin_sigmoid_scoring():
+    spec = _spec(num_experts=6, top_k=3, select=SIGMOID_NORM, seed=17)
+    rng = np.random.default_rng(17)
+    logits = rng.standard_normal((24, 6)) * 2.0
+    bias = (rng.standard_normal(6) * 0.2).astype(np.float32)
+    for mode, b in ((BIAS_NONE, None), (BIAS_SELECT_ONLY, bias)):
+        ids, w = oracle.select(spec.replace(bias_mode=mode), logits, b)
+        assert np.all(np.abs(w.sum(axis=1) - 1.0) <= 1e-12), "sigmoid weights must sum to 1"
+        for t in range(logits.shape[0]):
+            sc = [_sig(v) for v in logits[t]]
+            key = [sc[e] + (float(b[e]) if b is not None else 0.0) for e in range(6)]
+            want = sorted(range(6), key=lambda e: (-key[e], e))[:3]
+            assert list(ids[t]) == want, f"sigmoid selection: {ids[t]} vs {want}"
+            z = sum(sc[e] for e in want)
+            for j, e in enumerate(want):
+                assert abs(w[t, j] - sc[e] / z) <= 1e-13, "weight = score / sum of selected scores"
+    # without a bias the selection is the plain top-k of the logits (sigmoid is monotone)
+    ids_s, _ = oracle.select(spec, logits)
+    ids_t, _ = oracle.select(spec.replace(select=TOPK_SOFTMAX), logits)
+    assert np.array_equal(ids_s, ids_t)
+    # the correction bias is added to the score, not to the logit: with logits
+    # (10, 0, -3) and bias (0, 0.6, 0), sigmoid(10) + 0 < sigmoid(0) + 0.6 picks
+    # expert 1, while sigmoid(10) > sigmoid(0 + 0.6) would pick expert 0
+    one = spec.replace(num_experts=3, top_k=1, bias_mode=BIAS_SELECT_ONLY)
+    ids1, w1 = oracle.select(one, np.array([[10.0, 0.0, -3.0]]), np.array([0.0, 0.6, 0.0], np.float32))
+    assert ids1[0, 0] == 1 and abs(w1[0, 0] - 1.0) <= 1e-15, ids1
+    # a bias that keeps the set keeps the weights
+    idsn, wn = oracle.select(spec, logits)
+    for t in range(logits.shape[0]):
+        bb = np.zeros(6, np.float32)
+        bb[idsn[t, 0]] = 0.5
+        ids_b, w_b = oracle.select(spec.replace(bias_mode=BIAS_SELECT_ONLY), logits[t:t + 1], bb)
+        assert set(ids_b[0]) == set(idsn[t])
+        order = [list(ids_b[0]).index(e) for e in idsn[t]]
+        _close(w_b[0][order], wn[t], rtol=1e-13, what="correction bias changed the weights")
+    # two experts, k = 2: closed form
+    two = spec.replace(num_experts=2, top_k=2)
+    ids2, w2 = oracle.select(two, np.array([[1.5, -0.5]]))
+    a, b2 = _sig(1.5), _sig(-0.5)
+    assert list(ids2[0]) == [0, 1]
+    _close(w2[0], np.array([a / (a + b2), b2 / (a + b2)]), rtol=1e-14, what="two-expert sigmoid weights")
+
+
+# ---------------------------------------------------------------------------
 # P5: brute force on tiny shapes (pure Python, no numpy algebra)
 # ---------------------------------------------------------------------------
 def _py_f16(bits):
@@ -257,9 +309,13 @@ def _py_layer(spec, layer, x):
     for t in range(M):
         xr = X[t]
         lg = [sum(a * b for a, b in zip(R[e], xr)) for e in range(E)]
-        s = [lg[e] + (bias[e] if spec.bias_mode in (BIAS_LOGIT, BIAS_SELECT_ONLY) else 0.0)
-             for e in range(E)]
-        u = [lg[e] + (bias[e] if spec.bias_mode == BIAS_LOGIT else 0.0) for e in range(E)]
+        if spec.select == SIGMOID_NORM:
+            u = [1.0 / (1.0 + math.exp(-lg[e])) for e in range(E)]
+            s = [u[e] + (bias[e] if spec.bias_mode != BIAS_NONE else 0.0) for e in range(E)]
+        else:
+            s = [lg[e] + (bias[e] if spec.bias_mode in (BIAS_LOGIT, BIAS_SELECT_ONLY) else 0.0)
+                 for e in range(E)]
+            u = [lg[e] + (bias[e] if spec.bias_mode == BIAS_LOGIT else 0.0) for e in range(E)]
         best = None
         for sub in itertools.combinations(range(E), k):    # lexicographic order
             tot = sum(s[e] for e in sub)
@@ -272,6 +328,9 @@ def _py_layer(spec, layer, x):
             m = max(u[e] for e in sub)
             z = sum(math.exp(u[e] - m) for e in sub)
             w = {e: math.exp(u[e] - m) / z for e in sub}
+        elif spec.select == SIGMOID_NORM:
+            z = sum(u[e] for e in sub)
+            w = {e: u[e] / z for e in sub}
         else:
             m = max(u)
             z = sum(math.exp(v - m) for v in u)
@@ -297,6 +356,8 @@ BRUTE_CASES = [
          bias_kind="normal", bias_std=1.0, shared_inter=4, swiglu_limit=0.05),
     dict(hidden=64, num_experts=4, top_k=2, expert_inter=32, expert_dtype=Q8_0,
          router_dtype=BF16, x_dtype=BF16, rms_eps=1e-3),
+    dict(hidden=8, num_experts=6, top_k=3, expert_inter=4, select=SIGMOID_NORM,
+         bias_mode=BIAS_SELECT_ONLY, bias_kind="normal", bias_std=0.3, router_dtype=F32),
 ]
 
 
@@ -333,14 +394,14 @@ def pin_brute_force():
 # P6: x = 0
 # ---------------------------------------------------------------------------
 def pin_zero_input():
-    for select in (TOPK_SOFTMAX, SOFTMAX_ALL_NORENORM):
+    for select in (TOPK_SOFTMAX, SOFTMAX_ALL_NORENORM, SIGMOID_NORM):
         spec = _spec(num_experts=6, top_k=3, select=select, shared_inter=32, rms_eps=1e-6, seed=15)
         layer = synth.make_layer(spec)
         x = np.zeros((2, spec.hidden), np.float32)
         o = oracle.forward(spec, layer, x)
         assert np.all(o["logits"] == 0.0)
         assert np.array_equal(o["ids"], np.tile(np.arange(3, dtype=np.int32), (2, 1))), o["ids"]
-        want = 1.0 / 3 if select == TOPK_SOFTMAX else 1.0 / 6
+        want = 1.0 / 6 if select == SOFTMAX_ALL_NORENORM else 1.0 / 3
         _close(o["w"], np.full((2, 3), want), what="uniform weights at x = 0")
         assert np.all(o["y"] == 0.0), "y must vanish at x = 0"
 
@@ -541,4 +602,5 @@ PINS = [
     pin_brute_force, pin_zero_input, pin_relabel_invariance, pin_token_independence,
     pin_clamp, pin_q8_vs_bf16, pin_single_expert_dense, pin_permute,
     pin_prenorm_scale_invariance, pin_golden_selection, pin_golden_layer, pin_golden_q8_0,
+    pin_sigmoid_scoring,
 ]
