@@ -77,8 +77,12 @@ typedef enum {
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_Q8_0 = 2 } moe_dtype;
 
 typedef enum {
-    MOE_TOPK_SOFTMAX = 0,        /* softmax over the k selected logits */
-    MOE_SOFTMAX_ALL_NORENORM = 1 /* softmax over all E, read at the k, not renormalised */
+    MOE_TOPK_SOFTMAX = 0,         /* softmax over the k selected logits */
+    MOE_SOFTMAX_ALL_NORENORM = 1, /* softmax over all E, read at the k, not renormalised */
+    MOE_SIGMOID_NORM = 2          /* scores sigmoid(logit); the bias (MOE_BIAS_SELECT_ONLY)
+                                     is added to the score for the selection; weights are
+                                     the selected scores divided by their sum
+                                     (llama/state.rs, RealLlamaState::build, MiniMax branch) */
 } moe_select;
 
 typedef enum {

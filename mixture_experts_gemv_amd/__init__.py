@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libmoe_gemv.so")
 
 MOE_OK, MOE_ERR_INVALID, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
 MOE_F32, MOE_BF16, MOE_Q8_0 = 0, 1, 2
-MOE_TOPK_SOFTMAX, MOE_SOFTMAX_ALL_NORENORM = 0, 1
+MOE_TOPK_SOFTMAX, MOE_SOFTMAX_ALL_NORENORM, MOE_SIGMOID_NORM = 0, 1, 2
 MOE_BIAS_NONE, MOE_BIAS_LOGIT, MOE_BIAS_SELECT_ONLY = 0, 1, 2
 MOE_PATH_AUTO, MOE_PATH_GEMV, MOE_PATH_MFMA = 0, 1, 2
 MOE_LOGITS_IN = 1

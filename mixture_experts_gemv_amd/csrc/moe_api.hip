@@ -199,7 +199,7 @@ moe_status moe_plan_create(const moe_config *c, moe_plan **out) {
         return fail(MOE_ERR_INVALID, "hidden (%d) and expert_inter (%d) must be positive, shared_inter (%d) non-negative",
                     c->hidden, c->expert_inter, c->shared_inter);
     if (c->max_tokens < 1) return fail(MOE_ERR_INVALID, "max_tokens must be >= 1");
-    if (c->select != MOE_TOPK_SOFTMAX && c->select != MOE_SOFTMAX_ALL_NORENORM)
+    if (c->select != MOE_TOPK_SOFTMAX && c->select != MOE_SOFTMAX_ALL_NORENORM && c->select != MOE_SIGMOID_NORM)
         return fail(MOE_ERR_INVALID, "unknown select mode %d", c->select);
     if (c->bias_mode < MOE_BIAS_NONE || c->bias_mode > MOE_BIAS_SELECT_ONLY)
         return fail(MOE_ERR_INVALID, "unknown bias mode %d", c->bias_mode);
@@ -210,6 +210,8 @@ moe_status moe_plan_create(const moe_config *c, moe_plan **out) {
     if (!known(c->x_dtype) || !known(c->router_dtype) || !known(c->expert_dtype) ||
         (c->shared_inter > 0 && !known(c->shared_dtype)))
         return fail(MOE_ERR_INVALID, "unknown dtype");
+    if (c->select == MOE_SIGMOID_NORM && c->bias_mode == MOE_BIAS_LOGIT)
+        return fail(MOE_ERR_UNSUPPORTED, "sigmoid scoring takes its bias for the selection only (MOE_BIAS_SELECT_ONLY)");
     if (c->top_k > 8) return fail(MOE_ERR_UNSUPPORTED, "top_k %d exceeds the 8 routing slots", c->top_k);
     if (c->num_experts > 256) return fail(MOE_ERR_UNSUPPORTED, "num_experts %d exceeds 256", c->num_experts);
     if (c->hidden % 32 || c->expert_inter % 32 || c->shared_inter % 32)

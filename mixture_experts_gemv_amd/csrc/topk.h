@@ -15,7 +15,10 @@ constexpr int kKeysPerLane = kMaxE / kWave;
 // (+ bias for LOGIT).  k rounds of a wave argmax on the order-preserving key,
 // ties to the lower expert id.  On return lane j < k holds the j-th pick
 // (descending key) in *id and its weight in *wt: softmax over the k picks
-// (select 0) or the all-expert softmax read at the pick (select 1).
+// (select 0), the all-expert softmax read at the pick (select 1), or, with
+// sigmoid scores (select 2), the pick's score sigmoid(logit) divided by the
+// sum of the picks' scores; there the bias (any bias mode) is added to the
+// score for the selection only.
 __device__ inline void topk_wave_core(const float *lrow, const float *bias, int E, int k, int select,
                                       int bias_mode, int lane, int *id, float *wt) {
     uint32_t key[kKeysPerLane];
@@ -32,9 +35,14 @@ __device__ inline void topk_wave_core(const float *lrow, const float *bias, int 
     for (int c = 0; c < kKeysPerLane; c++) {
         const int e = lane + kWave * c;
         if (e < E) {
-            const float sk = bias_mode != 0 ? lv[c] + bv[c] : lv[c];
-            u[c] = bias_mode == 1 ? lv[c] + bv[c] : lv[c];
-            key[c] = order_key(sk);
+            if (select == 2) {
+                u[c] = 1.0f / (1.0f + expf(-lv[c]));
+                key[c] = order_key(bias_mode != 0 ? u[c] + bv[c] : u[c]);
+            } else {
+                const float sk = bias_mode != 0 ? lv[c] + bv[c] : lv[c];
+                u[c] = bias_mode == 1 ? lv[c] + bv[c] : lv[c];
+                key[c] = order_key(sk);
+            }
         } else {
             u[c] = -INFINITY;
             key[c] = 0u;
@@ -60,7 +68,10 @@ __device__ inline void topk_wave_core(const float *lrow, const float *bias, int 
         if (lane == j) { my_id = win; my_u = wu; }
     }
     float wj;
-    if (select == 0) {
+    if (select == 2) {
+        const float z = wave_sum(lane < k ? my_u : 0.f);
+        wj = my_u / z;
+    } else if (select == 0) {
         const float m = wave_max(lane < k ? my_u : -INFINITY);
         const float ex = lane < k ? expf(my_u - m) : 0.f;
         const float z = wave_sum(ex);

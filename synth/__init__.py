@@ -104,6 +104,14 @@ SPECS: Dict[str, LayerSpec] = {
     "deepseek-v2-lite-dense": LayerSpec(
         name="deepseek-v2-lite-dense", hidden=2048, num_experts=1, top_k=1,
         expert_inter=10944, seed=1006, token_counts=(1, 16, 512)),
+    # sigmoid scoring with a selection-only correction bias and an fp32 router,
+    # as the pages' MiniMax branch requires; the shape (not on the pages) is
+    # chosen at the ABI's 256-expert limit
+    "sigmoid-e256": LayerSpec(
+        name="sigmoid-e256", hidden=3072, num_experts=256, top_k=8,
+        expert_inter=1536, select=SIGMOID_NORM, bias_mode=BIAS_SELECT_ONLY,
+        bias_kind="normal", bias_std=0.05, router_dtype=F32, seed=1007,
+        token_counts=(1, 16)),
 }
 
 _NTHREADS = max(1, min(16, len(os.sched_getaffinity(0))))

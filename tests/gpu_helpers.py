@@ -10,6 +10,7 @@ import numpy as np
 import oracle
 import synth
 from pins import dequant
+from synth import SIGMOID_NORM
 
 # Output tolerance for fp32 accumulation over bf16 / Q8_0 weights.
 Y_MAX_ABS = 2e-2
@@ -19,6 +20,9 @@ W_ABS = 1e-5
 # Near-tie bound: a GPU logit in fp32 differs from the exact one by at most
 # TAU_REL * sum_i |x_i * w_i| (+|b|) for the summation orders used here.
 TAU_REL = 2.0 ** -17
+# Sigmoid scoring: the fp32 sigmoid of a logit and the add of the correction
+# bias are each within a few units of 2^-24 of the exact values.
+SIGMOID_TAU = 2.0 ** -20
 
 
 def say(msg: str) -> None:
@@ -54,9 +58,13 @@ def selection_keys(spec, layer, x):
     wr = dequant(layer["router"], spec.router_dtype, spec.num_experts, spec.hidden)
     logits = xf @ wr.T
     b = np.zeros(spec.num_experts) if layer.get("bias") is None else layer["bias"].astype(np.float64)
-    s = logits + (b if spec.bias_mode != 0 else 0.0)
     A = np.abs(xf) @ np.abs(wr).T + (np.abs(b) if spec.bias_mode != 0 else 0.0)
     tau = TAU_REL * A.max(axis=1)
+    if spec.select == SIGMOID_NORM:
+        # key sigmoid(l) + b: sigmoid' <= 1/4 carries the logit bound over, and
+        # the fp32 sigmoid and add are covered by SIGMOID_TAU
+        return 1.0 / (1.0 + np.exp(-logits)) + (b if spec.bias_mode != 0 else 0.0), tau / 4 + SIGMOID_TAU
+    s = logits + (b if spec.bias_mode != 0 else 0.0)
     return s, tau
 
 
@@ -69,10 +77,15 @@ def check_ids(spec, layer, x, gpu_ids, ora_ids):
     rest from keys within tau of it; the oracle is then re-run on the GPU's set.
     """
     s, tau = selection_keys(spec, layer, x)
-    k, E = spec.top_k, spec.num_experts
+    return check_ids_keys(s, tau, spec.top_k, gpu_ids, ora_ids)
+
+
+def check_ids_keys(s, tau, k, gpu_ids, ora_ids):
+    """The near-tie rule on given fp64 keys s[t][e] and bounds tau[t]."""
+    E = s.shape[1]
     forced = ora_ids.copy()
     near = 0
-    for t in range(x.shape[0]):
+    for t in range(s.shape[0]):
         order = np.argsort(-s[t], kind="stable")
         sk = s[t, order[k - 1]]
         sk1 = s[t, order[k]] if k < E else -np.inf

@@ -61,7 +61,6 @@ def _create(**kw):
     (dict(shared_inter=-32), m.MOE_ERR_INVALID),
     (dict(shared_inter=40), m.MOE_ERR_UNSUPPORTED),
     (dict(max_tokens=0), m.MOE_ERR_INVALID),
-    (dict(select=2), m.MOE_ERR_INVALID),
     (dict(bias_mode=3), m.MOE_ERR_INVALID),
     (dict(swiglu_limit=-1.0), m.MOE_ERR_INVALID),
     (dict(rms_eps=-1e-6), m.MOE_ERR_INVALID),
@@ -69,6 +68,8 @@ def _create(**kw):
     (dict(expert_dtype=7), m.MOE_ERR_INVALID),
     (dict(shared_inter=64, shared_dtype=m.MOE_Q8_0), m.MOE_ERR_UNSUPPORTED),
     (dict(path=5), m.MOE_ERR_INVALID),
+    (dict(select=3), m.MOE_ERR_INVALID),
+    (dict(select=m.MOE_SIGMOID_NORM, bias_mode=m.MOE_BIAS_LOGIT), m.MOE_ERR_UNSUPPORTED),
     (dict(path=m.MOE_PATH_MFMA, x_dtype=m.MOE_F32), m.MOE_ERR_UNSUPPORTED),
     (dict(path=m.MOE_PATH_MFMA, expert_dtype=m.MOE_F32), m.MOE_ERR_UNSUPPORTED),
 ])

@@ -7,9 +7,9 @@ import pytest
 
 import oracle
 import synth
-from synth import BF16, F32, Q8_0, BIAS_LOGIT, BIAS_SELECT_ONLY, SOFTMAX_ALL_NORENORM
-from gpu_helpers import (W_ABS, check_ids, check_y, device_layer, forward_parity, host_layer,
-                         say)
+from synth import BF16, F32, Q8_0, BIAS_LOGIT, BIAS_SELECT_ONLY, SIGMOID_NORM, SOFTMAX_ALL_NORENORM
+from gpu_helpers import (SIGMOID_TAU, W_ABS, check_ids, check_ids_keys, check_y, device_layer,
+                         forward_parity, host_layer, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -74,6 +74,58 @@ def test_route_from_logits_bit_exact(case):
     oid, ow = oracle.select(spec, logits.astype(np.float64), bias)
     assert np.array_equal(ids.cpu().numpy(), oid), "ids differ from the oracle on identical logits"
     assert np.max(np.abs(w.cpu().numpy() - ow)) <= W_ABS
+
+
+SIGMOID_ROUTE_CASES = [
+    dict(num_experts=32, top_k=4, select=SIGMOID_NORM),
+    dict(num_experts=256, top_k=8, select=SIGMOID_NORM, bias_mode=BIAS_SELECT_ONLY, bias_kind="normal",
+         bias_std=0.1),
+    dict(num_experts=7, top_k=7, select=SIGMOID_NORM, bias_mode=BIAS_SELECT_ONLY, bias_kind="normal"),
+]
+
+
+@pytest.mark.parametrize("case", SIGMOID_ROUTE_CASES, ids=lambda c: f"E{c['num_experts']}k{c['top_k']}")
+def test_route_from_logits_sigmoid(case):
+    """Sigmoid scoring from given fp32 logits.  The key sigmoid(l) + b is
+    computed in fp32, so two logits can share a key (large logits saturate to
+    1): ids follow the near-tie rule with SIGMOID_TAU on the fp64 keys, and
+    weights match the oracle run on the GPU's selection."""
+    import mixture_experts_gemv_amd as m
+    spec = synth.small_spec(hidden=64, expert_inter=32, seed=910, **case)
+    layer = synth.make_layer(spec)
+    E, k = spec.num_experts, spec.top_k
+    rng = np.random.default_rng(E * 37 + k)
+    M = 40
+    logits = (rng.standard_normal((M, E)) * 2.0).astype(np.float32)
+    logits[1] = 0.0                                            # all equal
+    logits[2] = 20.0 + 0.25 * np.arange(E, dtype=np.float32)   # scores saturate to 1 in fp32
+    logits[3] = np.round(logits[3] * 2) / 2                    # many exact ties
+    logits[4, ::2] = -0.0
+    say(f"sigmoid route from logits E={E} k={k}")
+    plan = m.moe_plan_create(64, E, k, 32, max_tokens=M, select=spec.select,
+                             bias_mode=spec.bias_mode, x_dtype=m.MOE_BF16)
+    bias = layer["bias"]
+    wts = m.make_weights(bias=None if bias is None else _t(bias))
+    ws = torch.empty(m.moe_workspace_bytes(plan, M), dtype=torch.uint8, device="cuda")
+    ids = torch.empty(M, k, dtype=torch.int32, device="cuda")
+    w = torch.empty(M, k, dtype=torch.float32, device="cuda")
+    m.moe_route(plan, None, wts, M, _t(logits), m.MOE_LOGITS_IN, ids, w, ws)
+    torch.cuda.synchronize()
+    gids, gw = ids.cpu().numpy(), w.cpu().numpy()
+    l64 = logits.astype(np.float64)
+    b64 = np.zeros(E) if bias is None else bias.astype(np.float64)
+    keys = 1.0 / (1.0 + np.exp(-l64)) + (b64 if spec.bias_mode else 0.0)
+    oid, _ = oracle.select(spec, l64, bias)
+    forced, near = check_ids_keys(keys, np.full(M, SIGMOID_TAU), k, gids, oid)
+    say(f"near-tie tokens: {near}")
+    if not spec.bias_mode:
+        assert near >= 1, "the saturated row must count as a near-tie"
+    fid, fw = oracle.select(spec, l64, bias, forced_ids=forced)
+    for t in range(M):
+        for j in range(k):
+            jj = list(fid[t]).index(gids[t, j])
+            assert abs(gw[t, j] - fw[t, jj]) <= W_ABS, f"token {t}: weight of expert {gids[t, j]}"
+        assert abs(gw[t].sum() - 1.0) <= 1e-5
 
 
 def test_route_from_x_small():
@@ -182,6 +234,9 @@ SMALL = [
     ("f32x-q8", dict(hidden=160, num_experts=5, top_k=2, expert_inter=64, x_dtype=F32,
                      router_dtype=F32, expert_dtype=Q8_0), (1, 2, 12)),
     ("wide-h", dict(hidden=4608, num_experts=4, top_k=2, expert_inter=64), (1, 3)),
+    ("sigmoid-bias", dict(hidden=256, num_experts=16, top_k=4, expert_inter=128, select=SIGMOID_NORM,
+                          bias_mode=BIAS_SELECT_ONLY, bias_kind="normal", bias_std=0.05,
+                          router_dtype=F32), (1, 5, 16)),
 ]
 
 
@@ -214,6 +269,8 @@ MFMA_SMALL = [
     ("q8-shared-bias-clamp", dict(hidden=192, num_experts=16, top_k=4, expert_inter=128, shared_inter=256,
                                   expert_dtype=Q8_0, shared_dtype=Q8_0, bias_mode=BIAS_LOGIT,
                                   bias_kind="normal", swiglu_limit=0.5), (3, 33, 100)),
+    ("sigmoid-e64", dict(hidden=256, num_experts=64, top_k=8, expert_inter=128, select=SIGMOID_NORM,
+                         bias_mode=BIAS_SELECT_ONLY, bias_kind="normal", bias_std=0.05), (1, 70)),
 ]
 
 
@@ -344,7 +401,7 @@ FULL = [("tiny", 4, None), ("gpt-oss-20b", 1, None), ("gpt-oss-20b", 16, None), 
         ("mixtral-8x7b", 1, None), ("mixtral-8x7b", 16, None),
         ("mixtral-8x7b", 512, 12), ("qwen3-30b-a3b", 2048, 24),
         ("deepseek-v2-lite-dense", 1, None), ("deepseek-v2-lite-dense", 16, None),
-        ("deepseek-v2-lite-dense", 512, 8)]
+        ("deepseek-v2-lite-dense", 512, 8), ("sigmoid-e256", 1, None), ("sigmoid-e256", 16, None)]
 
 
 @pytest.mark.parametrize("name,M,nsample", FULL, ids=[f"{n}-M{m}" for n, m, _ in FULL])
