@@ -41,6 +41,10 @@ MUTANTS = {
     16: "pre-norm applied to the router input only",
     17: "sigmoid mode adds the correction bias to the logit",
     18: "sigmoid mode leaves the weights unnormalised",
+    19: "MXFP4 element 2j read from the high nibble",
+    20: "MXFP4 scale exponent bias 128",
+    21: "MXFP4 exponent field 0 given an implicit one",
+    22: "MXFP4 reads the next block's scale",
 }
 
 

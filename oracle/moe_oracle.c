@@ -35,6 +35,17 @@
  *   Q8_0            32-element blocks, fp16 scale then 32 int8:
  *       deepseek2/state.rs, RealDeepseek2State::build (Q8_0 dots walk whole
  *       32-element blocks).
+ *   MXFP4           gpt-oss's routed expert pair is MXFP4: gptoss/state.rs
+ *       module doc (the clamp rides inside the MXFP4 routed pair),
+ *       BatchedRoutedScratch.wide_blobs and RealGptOssState::ensure_batched
+ *       (the MXFP4 batched pair and its argument buffer).  The pages
+ *       give no encoding, so the element and scale formats are those of the
+ *       OCP Microscaling (MX) v1.0 specification: 32 FP4 E2M1 elements share
+ *       one E8M0 scale, value = 2^(E - 127) * element, E = 255 is NaN.
+ *       Reading for the byte layout: a 17-byte block per 32 elements along
+ *       the reduction, the E8M0 byte first, then 16 bytes of codes, byte j
+ *       holding element 2j in its low nibble and element 2j+1 in its high
+ *       nibble.
  *
  * Readings where the pages are silent (each one is listed with its reason in
  * the design notes): ties in the top-k go to the lower expert id; the clamp
@@ -44,7 +55,8 @@
  * width Is with weight 1 and no clamp.
  *
  * Every stored value is widened exactly to double (bf16, fp16, fp32; Q8_0 as
- * d*q) and every sum is taken in double; no intermediate is rounded.
+ * d*q; MXFP4 as 2^(E-127) times the E2M1 value) and every sum is taken in
+ * double; no intermediate is rounded.
  *
  * Parity pins for every function here live in tests/pins.py.  The mutant
  * switch below exists only so that tests can prove those pins catch plausible
@@ -55,7 +67,7 @@
 #include <stdlib.h>
 #include <string.h>
 
-enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_Q8_0 = 2 };
+enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_Q8_0 = 2, ORC_MXFP4 = 3 };
 enum { ORC_TOPK_SOFTMAX = 0, ORC_SOFTMAX_ALL_NORENORM = 1, ORC_SIGMOID_NORM = 2 };
 enum { ORC_BIAS_NONE = 0, ORC_BIAS_LOGIT = 1, ORC_BIAS_SELECT_ONLY = 2 };
 
@@ -88,7 +100,11 @@ enum {
     MUT_NORM_ROUTER_ONLY = 16,
     MUT_SIGMOID_BIAS_BEFORE = 17,   /* sigmoid mode: correction bias added to the logit, not the score */
     MUT_SIGMOID_NO_RENORM = 18,     /* sigmoid mode: weights are the raw scores */
-    MUT_COUNT = 19
+    MUT_FP4_NIBBLE_SWAP = 19,       /* MXFP4: element 2j read from the high nibble */
+    MUT_E8M0_BIAS_128 = 20,         /* MXFP4: scale exponent bias 128 instead of 127 */
+    MUT_FP4_NO_SUBNORMAL = 21,      /* MXFP4: exponent field 0 given an implicit leading one */
+    MUT_MX_NEXT_BLOCK_SCALE = 22,   /* MXFP4: the next block's scale */
+    MUT_COUNT = 23
 };
 static int orc_mutant = MUT_NONE;
 
@@ -117,6 +133,27 @@ static double orc_f16(uint16_t h)
     return sign ? -v : v;
 }
 
+/* An FP4 E2M1 code (OCP MX v1.0): bit 3 sign, bits 2..1 exponent with bias 1,
+ * bit 0 mantissa.  Exponent field 0 is subnormal: 0.5 * m. */
+static double orc_e2m1(unsigned code)
+{
+    const unsigned sign = (code >> 3) & 1, ex = (code >> 1) & 3, m = code & 1;
+    double v;
+    if (ex == 0 && orc_mutant != MUT_FP4_NO_SUBNORMAL)
+        v = 0.5 * m;
+    else
+        v = ldexp(1.0 + 0.5 * m, (int)ex - 1);
+    return sign ? -v : v;
+}
+
+/* An E8M0 scale (OCP MX v1.0): 2^(e - 127); e = 255 is NaN. */
+static double orc_e8m0(unsigned e)
+{
+    if (e == 255)
+        return NAN;
+    return ldexp(1.0, (int)e - (orc_mutant == MUT_E8M0_BIAS_128 ? 128 : 127));
+}
+
 /* Element (r, c) of a row-major matrix with `cols` columns stored in `fmt`. */
 static double orc_at(const void *base, int fmt, size_t r, size_t cols, size_t c)
 {
@@ -134,6 +171,15 @@ static double orc_at(const void *base, int fmt, size_t r, size_t cols, size_t c)
         uint16_t d = (uint16_t)(row[blk * 34] | (row[blk * 34 + 1] << 8));
         int8_t q = (int8_t)row[(c / 32) * 34 + 2 + c % 32];
         return orc_f16(d) * (double)q;
+    }
+    case ORC_MXFP4: {
+        size_t nb = cols / 32;
+        const uint8_t *row = (const uint8_t *)base + r * nb * 17;
+        size_t blk = c / 32, j = c % 32;
+        size_t sblk = orc_mutant == MUT_MX_NEXT_BLOCK_SCALE ? (blk + 1) % nb : blk;
+        uint8_t byte = row[blk * 17 + 1 + j / 2];
+        int high = (j % 2 == 1) != (orc_mutant == MUT_FP4_NIBBLE_SWAP);
+        return orc_e8m0(row[sblk * 17]) * orc_e2m1(high ? byte >> 4 : byte & 15);
     }
     }
     return NAN;
@@ -353,7 +399,7 @@ void orc_swiglu_act(int H, int width, int fmt, double limit, const void *gate, c
 void orc_down(int H, int width, int fmt, const void *down, int mat, const double *act, double *out)
 {
     for (int h = 0; h < H; h++) {
-        if (orc_mutant == MUT_DOWN_TRANSPOSED && fmt != ORC_Q8_0) {
+        if (orc_mutant == MUT_DOWN_TRANSPOSED && fmt != ORC_Q8_0 && fmt != ORC_MXFP4) {
             /* read element (h, i) at flat index i*H + h of the expert's block */
             double s = 0.0;
             for (int i = 0; i < width; i++) {

@@ -2,8 +2,8 @@
 
 This module is shared by the CPU oracle's tests and the HIP path's tests and
 bench. It only draws random numbers and stores them in the byte formats the
-layer reads (fp32, bf16, Q8_0 blocks); it holds none of the layer's
-arithmetic.
+layer reads (fp32, bf16, Q8_0 and MXFP4 blocks); it holds none of the
+layer's arithmetic.
 
 Byte formats produced here:
 
@@ -15,6 +15,12 @@ Byte formats produced here:
   GGUF block the turbospark-runtime pages name for their Q8_0 MoE kernels
   (``src/families/deepseek2/state.rs``, ``RealDeepseek2State::build``, the
   kernel-contract check that the dots walk whole 32-element blocks).
+* MXFP4 tensors are ``uint8`` arrays of 17-byte blocks, one block per 32
+  consecutive elements along the reduction dimension: the E8M0 scale byte,
+  then 16 bytes of 4-bit E2M1 codes, byte j holding element 2j in its low
+  nibble and element 2j+1 in its high nibble (OCP Microscaling v1.0 element
+  and scale formats; the block layout is a reading, the pages name the format
+  for gpt-oss's routed experts without giving bytes).
 * Layer tensors are row-major with the reduction dimension contiguous:
   router ``[E][H]``, gate and up ``[E][I][H]``, down ``[E][H][I]``, shared
   gate and up ``[Is][H]``, shared down ``[H][Is]``.
@@ -35,7 +41,7 @@ from typing import Dict, Optional
 
 import numpy as np
 
-F32, BF16, Q8_0 = 0, 1, 2
+F32, BF16, Q8_0, MXFP4 = 0, 1, 2, 3
 TOPK_SOFTMAX, SOFTMAX_ALL_NORENORM, SIGMOID_NORM = 0, 1, 2
 BIAS_NONE, BIAS_LOGIT, BIAS_SELECT_ONLY = 0, 1, 2
 
@@ -44,6 +50,8 @@ STREAMS = ("x", "router", "bias", "gate", "up", "down", "shared_gate",
 
 Q8_BLOCK = 32
 Q8_BYTES = 34
+MX_BLOCK = 32
+MX_BYTES = 17
 
 
 @dataclasses.dataclass(frozen=True)
@@ -69,6 +77,8 @@ class LayerSpec:
     weight_std: float = 0.02
     q8_scale_lo: float = 1e-4
     q8_scale_hi: float = 1e-3
+    mx_exp_lo: int = 118           # MXFP4 scale byte ~ U{lo..hi}: 2^-9 .. 2^-5
+    mx_exp_hi: int = 122
     seed: int = 1000
     token_counts: tuple = (1,)
 
@@ -76,8 +86,8 @@ class LayerSpec:
         return dataclasses.replace(self, **kw)
 
 
-# The five workloads: a tiny fp32 layer and four layers shaped like public MoE
-# models (no trained weights; every value is drawn here).
+# The workloads: a tiny fp32 layer and layers shaped like public MoE models
+# (no trained weights; every value is drawn here).
 SPECS: Dict[str, LayerSpec] = {
     "tiny": LayerSpec(
         name="tiny", hidden=256, num_experts=8, top_k=2, expert_inter=512,
@@ -161,10 +171,44 @@ def q8_unpack(blocks: np.ndarray, cols: int):
     return q, d
 
 
+def mx_row_bytes(cols: int) -> int:
+    return cols // MX_BLOCK * MX_BYTES
+
+
+def mx_pack(codes: np.ndarray, e8: np.ndarray) -> np.ndarray:
+    """Pack 4-bit codes ``[rows][cols]`` (values 0..15) and E8M0 scale bytes
+    ``[rows][cols/32]`` into 17-byte blocks ``[rows][cols/32*17]`` (uint8)."""
+    rows, cols = codes.shape
+    nb = cols // MX_BLOCK
+    c = np.asarray(codes, dtype=np.uint8).reshape(rows, nb, MX_BLOCK // 2, 2)
+    out = np.empty((rows, nb, MX_BYTES), dtype=np.uint8)
+    out[:, :, 0] = np.asarray(e8, dtype=np.uint8).reshape(rows, nb)
+    out[:, :, 1:] = (c[..., 0] & np.uint8(15)) | ((c[..., 1] & np.uint8(15)) << np.uint8(4))
+    return out.reshape(rows, nb * MX_BYTES)
+
+
+def mx_unpack(blocks: np.ndarray, cols: int):
+    """Split 17-byte blocks back into ``(codes uint8 [rows][cols], e8 uint8 [rows][cols/32])``."""
+    rows = blocks.shape[0]
+    nb = cols // MX_BLOCK
+    b = np.ascontiguousarray(blocks).reshape(rows, nb, MX_BYTES)
+    e8 = np.ascontiguousarray(b[:, :, 0])
+    q = b[:, :, 1:]
+    codes = np.stack([q & np.uint8(15), q >> np.uint8(4)], axis=-1).reshape(rows, cols)
+    return codes, e8
+
+
 def _draw_matrix(ss: np.random.SeedSequence, rows: int, cols: int, dtype: int,
                  std: float, scale_ss: Optional[np.random.SeedSequence],
-                 lo: float, hi: float) -> np.ndarray:
+                 lo: float, hi: float, mx_exp=(118, 122)) -> np.ndarray:
     rng = np.random.default_rng(ss)
+    if dtype == MXFP4:
+        if cols % MX_BLOCK:
+            raise ValueError("MXFP4 rows must hold whole 32-element blocks")
+        codes = rng.integers(0, 16, size=(rows, cols), dtype=np.uint8)
+        e8 = np.random.default_rng(scale_ss).integers(mx_exp[0], mx_exp[1] + 1,
+                                                       size=(rows, cols // MX_BLOCK), dtype=np.uint8)
+        return mx_pack(codes, e8)
     if dtype == Q8_0:
         if cols % Q8_BLOCK:
             raise ValueError("Q8_0 rows must hold whole 32-element blocks")
@@ -183,15 +227,15 @@ def _draw_matrix(ss: np.random.SeedSequence, rows: int, cols: int, dtype: int,
 
 def _draw_experts(ss: np.random.SeedSequence, scale_ss: np.random.SeedSequence,
                   n: int, rows: int, cols: int, dtype: int, std: float,
-                  lo: float, hi: float) -> np.ndarray:
+                  lo: float, hi: float, mx_exp=(118, 122)) -> np.ndarray:
     kids = ss.spawn(n)
     skids = scale_ss.spawn(n)
-    first = _draw_matrix(kids[0], rows, cols, dtype, std, skids[0], lo, hi)
+    first = _draw_matrix(kids[0], rows, cols, dtype, std, skids[0], lo, hi, mx_exp)
     out = np.empty((n,) + first.shape, dtype=first.dtype)
     out[0] = first
 
     def one(e):
-        out[e] = _draw_matrix(kids[e], rows, cols, dtype, std, skids[e], lo, hi)
+        out[e] = _draw_matrix(kids[e], rows, cols, dtype, std, skids[e], lo, hi, mx_exp)
 
     if n > 1:
         with _cf.ThreadPoolExecutor(max_workers=_NTHREADS) as ex:
@@ -207,6 +251,7 @@ def make_layer(spec: LayerSpec) -> Dict[str, Optional[np.ndarray]]:
     sc = dict(zip(("gate", "up", "down", "shared_gate", "shared_up", "shared_down"),
                   ch["q8_scale"].spawn(6)))
     std, lo, hi = spec.weight_std, spec.q8_scale_lo, spec.q8_scale_hi
+    mx = (spec.mx_exp_lo, spec.mx_exp_hi)
     layer: Dict[str, Optional[np.ndarray]] = {}
     layer["router"] = _draw_matrix(ch["router"], E, H, spec.router_dtype, std, None, lo, hi)
     if spec.bias_kind == "normal":
@@ -221,13 +266,13 @@ def make_layer(spec: LayerSpec) -> Dict[str, Optional[np.ndarray]]:
         layer["bias"] = (-spec.zipf_s * np.log(rank)).astype(np.float32)
     else:
         layer["bias"] = None
-    layer["gate"] = _draw_experts(ch["gate"], sc["gate"], E, I, H, spec.expert_dtype, std, lo, hi)
-    layer["up"] = _draw_experts(ch["up"], sc["up"], E, I, H, spec.expert_dtype, std, lo, hi)
-    layer["down"] = _draw_experts(ch["down"], sc["down"], E, H, I, spec.expert_dtype, std, lo, hi)
+    layer["gate"] = _draw_experts(ch["gate"], sc["gate"], E, I, H, spec.expert_dtype, std, lo, hi, mx)
+    layer["up"] = _draw_experts(ch["up"], sc["up"], E, I, H, spec.expert_dtype, std, lo, hi, mx)
+    layer["down"] = _draw_experts(ch["down"], sc["down"], E, H, I, spec.expert_dtype, std, lo, hi, mx)
     if Is > 0:
-        layer["shared_gate"] = _draw_matrix(ch["shared_gate"], Is, H, spec.shared_dtype, std, sc["shared_gate"], lo, hi)
-        layer["shared_up"] = _draw_matrix(ch["shared_up"], Is, H, spec.shared_dtype, std, sc["shared_up"], lo, hi)
-        layer["shared_down"] = _draw_matrix(ch["shared_down"], H, Is, spec.shared_dtype, std, sc["shared_down"], lo, hi)
+        layer["shared_gate"] = _draw_matrix(ch["shared_gate"], Is, H, spec.shared_dtype, std, sc["shared_gate"], lo, hi, mx)
+        layer["shared_up"] = _draw_matrix(ch["shared_up"], Is, H, spec.shared_dtype, std, sc["shared_up"], lo, hi, mx)
+        layer["shared_down"] = _draw_matrix(ch["shared_down"], H, Is, spec.shared_dtype, std, sc["shared_down"], lo, hi, mx)
     else:
         layer["shared_gate"] = layer["shared_up"] = layer["shared_down"] = None
     return layer
@@ -253,7 +298,7 @@ def small_spec(name: str = "small", **kw) -> LayerSpec:
 
 
 def expert_bytes_per_weight(dtype: int) -> float:
-    return {F32: 4.0, BF16: 2.0, Q8_0: Q8_BYTES / Q8_BLOCK}[dtype]
+    return {F32: 4.0, BF16: 2.0, Q8_0: Q8_BYTES / Q8_BLOCK, MXFP4: MX_BYTES / MX_BLOCK}[dtype]
 
 
 def storage_nbytes(dtype: int, rows: int, cols: int) -> int:

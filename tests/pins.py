@@ -15,7 +15,10 @@ Passages (turbospark-runtime 0.3.0 source pages):
   * clamped SwiGLU -- gptoss/state.rs, module doc;
   * y = shared + sum(w * expert) -- deepseek2/state.rs, RealDeepseek2State.shared_out;
   * route list and phase 1/phase 2 -- gptoss/state.rs, BatchedRoutedScratch;
-  * Q8_0 32-element blocks -- deepseek2/state.rs, RealDeepseek2State::build.
+  * Q8_0 32-element blocks -- deepseek2/state.rs, RealDeepseek2State::build;
+  * MXFP4 routed experts -- gptoss/state.rs, module doc and
+    RealGptOssState::ensure_batched; the element (FP4 E2M1) and scale (E8M0)
+    encodings are the OCP Microscaling Formats (MX) v1.0 specification's.
 """
 
 from __future__ import annotations
@@ -29,10 +32,16 @@ import numpy as np
 
 import oracle
 import synth
-from synth import BF16, F32, Q8_0, BIAS_LOGIT, BIAS_NONE, BIAS_SELECT_ONLY
+from synth import BF16, F32, MXFP4, Q8_0, BIAS_LOGIT, BIAS_NONE, BIAS_SELECT_ONLY
 from synth import SIGMOID_NORM, SOFTMAX_ALL_NORENORM, TOPK_SOFTMAX
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+# The FP4 E2M1 element values by code, as the OCP MX v1.0 specification lists
+# them (codes 8..15 are the negatives of codes 0..7).
+E2M1_VALUES = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0,
+                        -0.0, -0.5, -1.0, -1.5, -2.0, -3.0, -4.0, -6.0])
 
 
 # ---------------------------------------------------------------------------
@@ -44,6 +53,10 @@ def dequant(buf, fmt, rows, cols):
         return np.asarray(buf, np.float32).reshape(rows, cols).astype(np.float64)
     if fmt == BF16:
         return synth.bf16_to_f32(np.asarray(buf).reshape(rows, cols)).astype(np.float64)
+    if fmt == MXFP4:
+        codes, e8 = synth.mx_unpack(np.asarray(buf).reshape(rows, -1), cols)
+        scale = np.where(e8 == 255, np.nan, np.ldexp(1.0, e8.astype(np.int64) - 127))
+        return (E2M1_VALUES[codes].reshape(rows, cols // 32, 32) * scale[:, :, None]).reshape(rows, cols)
     q, d = synth.q8_unpack(np.asarray(buf).reshape(rows, -1), cols)
     return (q.astype(np.float64).reshape(rows, cols // 32, 32)
             * d.astype(np.float64)[:, :, None]).reshape(rows, cols)
@@ -270,6 +283,11 @@ def _py_matrix(buf, fmt, rows, cols):
                 row.append(float(np.float32(flat[r * cols + c])))
             elif fmt == BF16:
                 row.append(float(np.uint32(int(flat[r * cols + c]) << 16).view(np.float32)))
+            elif fmt == MXFP4:
+                base = r * (cols // 32 * 17) + (c // 32) * 17
+                byte = int(flat[base + 1 + (c % 32) // 2])
+                code = byte >> 4 if c % 2 else byte & 15
+                row.append(float(E2M1_VALUES[code]) * 2.0 ** (int(flat[base]) - 127))
             else:
                 rb = cols // 32 * 34
                 base = r * rb + (c // 32) * 34
@@ -358,6 +376,9 @@ BRUTE_CASES = [
          router_dtype=BF16, x_dtype=BF16, rms_eps=1e-3),
     dict(hidden=8, num_experts=6, top_k=3, expert_inter=4, select=SIGMOID_NORM,
          bias_mode=BIAS_SELECT_ONLY, bias_kind="normal", bias_std=0.3, router_dtype=F32),
+    dict(hidden=64, num_experts=4, top_k=2, expert_inter=32, expert_dtype=MXFP4,
+         shared_dtype=MXFP4, shared_inter=32, bias_mode=BIAS_LOGIT, bias_kind="normal",
+         swiglu_limit=0.5),
 ]
 
 
@@ -500,11 +521,44 @@ def pin_q8_vs_bf16():
 
 
 # ---------------------------------------------------------------------------
+# P10b: MXFP4 equals the bf16 layer built from its dequantised weights (every
+# E2M1 value times a power-of-two scale in bf16's range is a bf16 value)
+# ---------------------------------------------------------------------------
+def pin_mxfp4_vs_bf16():
+    spec = _spec(hidden=64, expert_inter=96, num_experts=4, top_k=2, expert_dtype=MXFP4,
+                 shared_dtype=MXFP4, shared_inter=64, x_dtype=BF16, seed=23)
+    layer = synth.make_layer(spec)
+    rng = np.random.default_rng(23)
+    bf = dict(layer)
+    shapes = {"gate": (4, 96, 64), "up": (4, 96, 64), "down": (4, 64, 96),
+              "shared_gate": (1, 64, 64), "shared_up": (1, 64, 64), "shared_down": (1, 64, 64)}
+    for key, (n, rows, cols) in shapes.items():
+        blocks, vals = [], []
+        for _ in range(n):
+            codes = rng.integers(0, 16, size=(rows, cols), dtype=np.uint8)
+            # scales differ from block to block, so a wrong block index shows
+            e8 = rng.integers(110, 131, size=(rows, cols // 32), dtype=np.uint8)
+            blocks.append(synth.mx_pack(codes, e8))
+            vals.append((E2M1_VALUES[codes].reshape(rows, cols // 32, 32)
+                         * np.ldexp(1.0, e8.astype(np.int64) - 127)[:, :, None]).reshape(rows, cols))
+        v = np.stack(vals).astype(np.float32)
+        bits = synth.bf16_bits(v)
+        assert np.array_equal(synth.bf16_to_f32(bits), v), "MXFP4 values must be bf16-exact"
+        layer[key] = np.stack(blocks) if n > 1 else blocks[0]
+        bf[key] = bits if n > 1 else bits[0]
+    x = synth.make_tokens(spec, 3)
+    a = oracle.forward(spec, layer, x)
+    b = oracle.forward(spec.replace(expert_dtype=BF16, shared_dtype=BF16), bf, x)
+    assert np.array_equal(a["ids"], b["ids"])
+    assert np.array_equal(a["y"], b["y"]), "MXFP4 and its bf16 image disagree"
+
+
+# ---------------------------------------------------------------------------
 # P11: one expert, k = 1 is a plain dense SwiGLU FFN (with and without pre-norm)
 # ---------------------------------------------------------------------------
 def pin_single_expert_dense():
     for eps in (0.0, 1e-2):
-        for fmt in (F32, BF16, Q8_0):
+        for fmt in (F32, BF16, Q8_0, MXFP4):
             spec = _spec(num_experts=1, top_k=1, hidden=64, expert_inter=96, expert_dtype=fmt,
                          rms_eps=eps, seed=20)
             layer = synth.make_layer(spec)
@@ -597,10 +651,23 @@ def pin_golden_q8_0():
         assert got == want, f"Q8_0 element {c}: {got} != {want}"
 
 
+def pin_golden_mxfp4():
+    g = _golden("mxfp4_block.json")
+    raw = np.array(g["bytes"], np.uint8).reshape(1, -1)
+    cols = g["cols"]
+    for c, want in enumerate(g["values"]):
+        got = oracle.element(raw, MXFP4, 0, cols, c)
+        if want is None:
+            assert math.isnan(got), f"MXFP4 element {c}: {got} is not NaN"
+        else:
+            assert got == want and math.copysign(1.0, got) == math.copysign(1.0, want), \
+                f"MXFP4 element {c}: {got} != {want}"
+
+
 PINS = [
     pin_dense_equivalence, pin_one_hot_router, pin_weight_sums, pin_bias_semantics,
     pin_brute_force, pin_zero_input, pin_relabel_invariance, pin_token_independence,
     pin_clamp, pin_q8_vs_bf16, pin_single_expert_dense, pin_permute,
     pin_prenorm_scale_invariance, pin_golden_selection, pin_golden_layer, pin_golden_q8_0,
-    pin_sigmoid_scoring,
+    pin_sigmoid_scoring, pin_mxfp4_vs_bf16, pin_golden_mxfp4,
 ]
