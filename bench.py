@@ -37,7 +37,7 @@ GATEUP_KERNEL = {"single": "k_gateup_m1", "gemv": "k_gateup_rows", "mfma": "k_ge
 
 # ------------------------------------------------------------------ workload
 def bytes_per_weight(dtype: int) -> float:
-    return {0: 4.0, 1: 2.0, 2: 34.0 / 32.0}[dtype]
+    return {0: 4.0, 1: 2.0, 2: 34.0 / 32.0, 3: 17.0 / 32.0}[dtype]
 
 
 def algorithmic_bytes(spec, M: int, counts: np.ndarray) -> dict:
@@ -76,6 +76,11 @@ def device_copy(spec, dev, rng_seed: int):
             d = torch.empty(rows * cols // 32, device=dev, dtype=torch.float32)
             d.uniform_(spec.q8_scale_lo, spec.q8_scale_hi, generator=g)
             return q, d.half().view(torch.int16)
+        if dtype == 3:  # MXFP4: code bytes (two E2M1 codes each) and E8M0 scale bytes
+            c = torch.randint(0, 256, (rows * cols // 2,), generator=g, device=dev, dtype=torch.uint8)
+            e = torch.randint(spec.mx_exp_lo, spec.mx_exp_hi + 1, (rows * cols // 32,), generator=g,
+                              device=dev, dtype=torch.uint8)
+            return c, e
         t = torch.empty(rows * cols, device=dev, dtype=torch.float32).normal_(0.0, spec.weight_std, generator=g)
         return (t.bfloat16() if dtype == 1 else t), None
 
@@ -100,7 +105,7 @@ def device_copy(spec, dev, rng_seed: int):
 
 def layer_bytes(spec) -> float:
     H, E, I, Is = spec.hidden, spec.num_experts, spec.expert_inter, spec.shared_inter
-    return 3 * E * H * I * bytes_per_weight(spec.expert_dtype) + 3 * H * Is * 2
+    return 3 * E * H * I * bytes_per_weight(spec.expert_dtype) + 3 * H * Is * bytes_per_weight(spec.shared_dtype)
 
 
 def cpu_baseline(spec, host_layer, M: int, budget_s: float) -> dict:
@@ -292,7 +297,7 @@ def main() -> int:
                          f"{spec.name}-shaped routed MoE layer, M={M} tokens per call"),
             "hidden": spec.hidden, "num_experts": spec.num_experts, "top_k": spec.top_k,
             "expert_inter": spec.expert_inter, "shared_inter": spec.shared_inter,
-            "expert_weights": {0: "f32", 1: "bf16", 2: "q8_0"}[spec.expert_dtype],
+            "expert_weights": {0: "f32", 1: "bf16", 2: "q8_0", 3: "mxfp4"}[spec.expert_dtype],
             "tokens_per_call": M, "layer_copies": L, "token_batches": P,
             "touched_experts_avg": touched_avg,
             "timing": "hip_graph_replay" if graph_ms is not None else "eager",

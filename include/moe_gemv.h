@@ -38,6 +38,13 @@
  *    scale * q.  moe_q8_0_split converts 34-byte GGUF-style blocks into them.
  *    Weight planes must be 16-byte aligned and scale planes 4-byte aligned
  *    (MOE_ERR_INVALID otherwise).
+ *  - MXFP4 weights (expert_dtype MOE_MXFP4) are passed as two planes too:
+ *    FP4 E2M1 codes, two per byte with the even element in the low nibble
+ *    (gate [E][I][H/2] bytes), and E8M0 scale bytes, one per 32 consecutive
+ *    elements along the reduction dimension (gate_scale [E][I][H/32]).  Value
+ *    = 2^(scale - 127) * element.  moe_mxfp4_split converts 17-byte blocks
+ *    into them.  Code planes must be 16-byte aligned; scale planes may have
+ *    any alignment.  MXFP4 layers run on the GEMV kernels at every M.
  *  - Routes: route r = t*top_k + j is slot j of token t.  "Sorted position" p
  *    is the route's index in expert-major order (experts ascending, routes
  *    ascending inside an expert), as produced by moe_permute.
@@ -74,7 +81,7 @@ typedef enum {
     MOE_ERR_HIP = 4          /* HIP runtime error; moe_last_error() has its text */
 } moe_status;
 
-typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_Q8_0 = 2 } moe_dtype;
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_Q8_0 = 2, MOE_MXFP4 = 3 } moe_dtype;
 
 typedef enum {
     MOE_TOPK_SOFTMAX = 0,         /* softmax over the k selected logits */
@@ -94,7 +101,7 @@ typedef enum {
 typedef enum {
     MOE_PATH_AUTO = 0, /* GEMV kernels for small batches, MFMA grouped GEMM for large */
     MOE_PATH_GEMV = 1, /* always the bandwidth-bound GEMV kernels */
-    MOE_PATH_MFMA = 2  /* always the MFMA grouped GEMM (bf16 x; bf16 or Q8_0 experts;
+    MOE_PATH_MFMA = 2  /* always the MFMA grouped GEMM (bf16 x; bf16 or Q8_0 experts, not MXFP4;
                           H, I and Is multiples of 64) */
 } moe_path;
 
@@ -112,8 +119,8 @@ typedef struct moe_config {
     float rms_eps;        /* > 0: x_t / sqrt(mean(x_t^2) + eps) feeds router and experts; 0: off */
     int32_t x_dtype;      /* MOE_F32 or MOE_BF16 */
     int32_t router_dtype; /* MOE_F32 or MOE_BF16 */
-    int32_t expert_dtype; /* MOE_F32, MOE_BF16 or MOE_Q8_0 */
-    int32_t shared_dtype; /* MOE_F32, MOE_BF16 or MOE_Q8_0 (ignored when shared_inter = 0) */
+    int32_t expert_dtype; /* MOE_F32, MOE_BF16, MOE_Q8_0 or MOE_MXFP4 */
+    int32_t shared_dtype; /* the expert_dtype (ignored when shared_inter = 0) */
     int32_t path;         /* moe_path */
 } moe_config;
 
@@ -124,15 +131,15 @@ typedef struct moe_weights {
     const void *gate;            /* [E][I][H] (int8 plane for Q8_0) */
     const void *up;              /* [E][I][H] */
     const void *down;            /* [E][H][I] */
-    const uint16_t *gate_scale;  /* Q8_0 only: fp16 [E][I][H/32] */
-    const uint16_t *up_scale;    /* Q8_0 only: fp16 [E][I][H/32] */
-    const uint16_t *down_scale;  /* Q8_0 only: fp16 [E][H][I/32] */
+    const void *gate_scale;      /* Q8_0: fp16 [E][I][H/32]; MXFP4: E8M0 bytes [E][I][H/32] */
+    const void *up_scale;        /* the same for up */
+    const void *down_scale;      /* Q8_0: fp16 [E][H][I/32]; MXFP4: E8M0 bytes [E][H][I/32] */
     const void *shared_gate;     /* [Is][H]; required iff shared_inter > 0 */
     const void *shared_up;       /* [Is][H] */
     const void *shared_down;     /* [H][Is] */
-    const uint16_t *shared_gate_scale; /* Q8_0 only: [Is][H/32] */
-    const uint16_t *shared_up_scale;   /* Q8_0 only: [Is][H/32] */
-    const uint16_t *shared_down_scale; /* Q8_0 only: [H][Is/32] */
+    const void *shared_gate_scale; /* Q8_0 / MXFP4 only: [Is][H/32] */
+    const void *shared_up_scale;   /* [Is][H/32] */
+    const void *shared_down_scale; /* [H][Is/32] */
 } moe_weights;
 
 typedef struct moe_plan moe_plan; /* host-side, library-owned */
@@ -254,6 +261,20 @@ int32_t moe_forward_path(const moe_plan *plan, int32_t M);
  * alignment; MOE_ERR_INVALID for rows < 0, cols <= 0 or cols % 32 != 0. */
 moe_status moe_q8_0_split(const void *blocks, int64_t rows, int32_t cols, int8_t *qs,
                           uint16_t *scales, void *stream);
+
+/* Convert MXFP4 blocks (17 bytes: the E8M0 scale byte, then 16 bytes of FP4
+ * E2M1 codes, byte j holding element 2j in its low nibble and element 2j+1 in
+ * its high nibble) of a [rows][cols] matrix, cols a multiple of 32, into the
+ * two planes the layer reads: codes [rows][cols/2] bytes (the 16 code bytes of
+ * each block, in order) and scales [rows][cols/32] E8M0 bytes.  Element and
+ * scale encodings are those of the OCP Microscaling (MX) v1.0 formats, value =
+ * 2^(scale - 127) * element; gptoss/state.rs (module doc and
+ * BatchedRoutedScratch) names MXFP4 as the format of gpt-oss's routed expert
+ * pair, and the 17-byte block layout is a reading of that.  Device pointers;
+ * codes 16-byte aligned, blocks and scales any alignment; MOE_ERR_INVALID for
+ * rows < 0, cols <= 0 or cols % 32 != 0. */
+moe_status moe_mxfp4_split(const void *blocks, int64_t rows, int32_t cols, uint8_t *codes,
+                           uint8_t *scales, void *stream);
 
 #ifdef __cplusplus
 }

@@ -18,7 +18,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe_gemv.so")
 
 MOE_OK, MOE_ERR_INVALID, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
-MOE_F32, MOE_BF16, MOE_Q8_0 = 0, 1, 2
+MOE_F32, MOE_BF16, MOE_Q8_0, MOE_MXFP4 = 0, 1, 2, 3
 MOE_TOPK_SOFTMAX, MOE_SOFTMAX_ALL_NORENORM, MOE_SIGMOID_NORM = 0, 1, 2
 MOE_BIAS_NONE, MOE_BIAS_LOGIT, MOE_BIAS_SELECT_ONLY = 0, 1, 2
 MOE_PATH_AUTO, MOE_PATH_GEMV, MOE_PATH_MFMA = 0, 1, 2
@@ -80,12 +80,13 @@ def lib() -> ctypes.CDLL:
         L.moe_forward_timed.argtypes = [P, P, W, I32, P, P, P, P, P, SZ, P,
                                         ctypes.POINTER(P), I32, P, ctypes.POINTER(I32)]
         L.moe_q8_0_split.argtypes = [P, ctypes.c_int64, I32, P, P, P]
+        L.moe_mxfp4_split.argtypes = [P, ctypes.c_int64, I32, P, P, P]
         L.moe_workspace_init.argtypes = [P, P, SZ, P]
         L.moe_workspace_init.restype = I32
         L.moe_forward_path.argtypes = [P, I32]
         L.moe_forward_path.restype = I32
         for f in ("moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_forward",
-                  "moe_forward_timed", "moe_q8_0_split"):
+                  "moe_forward_timed", "moe_q8_0_split", "moe_mxfp4_split"):
             getattr(L, f).restype = I32
         _lib = L
     return _lib
@@ -229,3 +230,8 @@ def moe_forward_timed(plan, x, weights, M, y, ids_out, w_out, counts_out, ws, ev
 def moe_q8_0_split(blocks, rows, cols, qs, scales, stream=None):
     _check(lib().moe_q8_0_split(_ptr(blocks), rows, cols, _ptr(qs), _ptr(scales),
                                 _stream(stream)))
+
+
+def moe_mxfp4_split(blocks, rows, cols, codes, scales, stream=None):
+    _check(lib().moe_mxfp4_split(_ptr(blocks), rows, cols, _ptr(codes), _ptr(scales),
+                                 _stream(stream)))

@@ -34,11 +34,17 @@ inline void launch_kernel(void (*k)(P...), dim3 grid, dim3 block, uint32_t shm, 
     }
 }
 
-enum Dtype : int { DT_F32 = 0, DT_BF16 = 1, DT_Q8 = 2 };
+enum Dtype : int { DT_F32 = 0, DT_BF16 = 1, DT_Q8 = 2, DT_MX4 = 3 };
+
+// Weight formats that carry one scale per 32-element block along the
+// reduction (Q8_0: fp16 scale and int8 values; MXFP4: E8M0 scale and FP4
+// E2M1 codes, two per byte).
+template <int DT> __host__ __device__ constexpr bool blocked() { return DT == DT_Q8 || DT == DT_MX4; }
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 // ---------------------------------------------------------------- conversions
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -52,6 +58,12 @@ __device__ __forceinline__ float f16_bits_to_f32(uint16_t h) {
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
     const uint32_t u = __float_as_uint(f);
     return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// An E8M0 scale byte as the float 2^(e - 127); 0 gives 2^-127 (a float
+// subnormal), 255 is NaN.
+__device__ __forceinline__ float e8m0_to_f32(uint32_t e) {
+    return __uint_as_float(e == 0 ? 0x00400000u : (e == 255 ? 0x7fc00000u : e << 23));
 }
 
 // Sign-extended byte b of a 32-bit word, as float.
@@ -130,11 +142,13 @@ __device__ __forceinline__ float clampf(float v, float lim) {
 
 // ---------------------------------------------------------- 16-byte chunk loads
 // A "chunk" is the elements one lane takes per 16-byte weight load:
-// 4 fp32, 8 bf16 or 16 Q8_0 int8 values (half a Q8_0 block).
+// 4 fp32, 8 bf16, 16 Q8_0 int8 values (half a Q8_0 block) or 32 MXFP4 codes
+// (one MXFP4 block).
 template <int DT> struct Chunk;
 template <> struct Chunk<DT_F32> { static constexpr int N = 4; };
 template <> struct Chunk<DT_BF16> { static constexpr int N = 8; };
 template <> struct Chunk<DT_Q8> { static constexpr int N = 16; };
+template <> struct Chunk<DT_MX4> { static constexpr int N = 32; };
 
 // Load chunk c of a weight row into floats (Q8_0: the raw q values; the
 // caller applies the block scale).
@@ -179,7 +193,7 @@ __device__ __forceinline__ void decode_chunk(u32x4 v, float *w) {
     } else if constexpr (DT == DT_BF16) {
         w[0] = bf16_lo(v.x); w[1] = bf16_hi(v.x); w[2] = bf16_lo(v.y); w[3] = bf16_hi(v.y);
         w[4] = bf16_lo(v.z); w[5] = bf16_hi(v.z); w[6] = bf16_lo(v.w); w[7] = bf16_hi(v.w);
-    } else {
+    } else if constexpr (DT == DT_Q8) {
         const uint32_t d[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
         for (int i = 0; i < 4; i++) {
@@ -188,7 +202,55 @@ __device__ __forceinline__ void decode_chunk(u32x4 v, float *w) {
             w[4 * i + 2] = i8_to_f32<2>(d[i]);
             w[4 * i + 3] = i8_to_f32<3>(d[i]);
         }
+    } else {
+        // MXFP4 codes, element 2j in the low nibble of byte j: the hardware
+        // converter takes one byte (two codes) at a time, exactly (scale 1;
+        // the block scale is applied to the chunk's dot).
+        const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const f32x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d[i], 1.0f, 0);
+            const f32x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d[i], 1.0f, 1);
+            const f32x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d[i], 1.0f, 2);
+            const f32x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d[i], 1.0f, 3);
+            w[8 * i + 0] = p0.x; w[8 * i + 1] = p0.y; w[8 * i + 2] = p1.x; w[8 * i + 3] = p1.y;
+            w[8 * i + 4] = p2.x; w[8 * i + 5] = p2.y; w[8 * i + 6] = p3.x; w[8 * i + 7] = p3.y;
+        }
     }
+}
+
+// The 32 codes of an MXFP4 chunk as 16 words of bf16 pairs (exact: every
+// E2M1 value is a bf16 value).
+typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void mx4_to_bf16x2(u32x4 v, uint32_t (&o)[16]) {
+    const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        o[4 * i + 0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d[i], 1.0f, 0));
+        o[4 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d[i], 1.0f, 1));
+        o[4 * i + 2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d[i], 1.0f, 2));
+        o[4 * i + 3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d[i], 1.0f, 3));
+    }
+}
+
+// Block scales: the stored bits of block i of a scale plane (fp16 for Q8_0,
+// an E8M0 byte for MXFP4), and their value.
+template <int DT>
+__device__ __forceinline__ uint16_t scale_bits(const void *plane, size_t i) {
+    if constexpr (DT == DT_MX4) return reinterpret_cast<const uint8_t *>(plane)[i];
+    else return reinterpret_cast<const uint16_t *>(plane)[i];
+}
+template <int DT>
+__device__ __forceinline__ float scale_value(uint16_t bits) {
+    if constexpr (DT == DT_MX4) return e8m0_to_f32(bits);
+    else return f16_bits_to_f32(bits);
+}
+// Block (index along a row) that chunk c falls in.
+template <int DT> __host__ __device__ constexpr int chunk_block(int c) { return c * Chunk<DT>::N / 32; }
+// A scale plane advanced by i blocks.
+template <int DT>
+__host__ __device__ inline const void *scale_at(const void *plane, size_t i) {
+    return reinterpret_cast<const char *>(plane) + i * (DT == DT_MX4 ? 1 : 2);
 }
 
 // 8 consecutive elements of a row stored as fp32 or bf16, as floats.
@@ -211,7 +273,10 @@ template <int DT> constexpr int dt_bytes() { return DT == DT_BF16 ? 2 : 4; }
 // Wave-uniform copy of a value the compiler cannot prove uniform.
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
-// Bytes of one stored element (Q8_0: the int8 plane only).
-template <int DT> __host__ __device__ constexpr int elem_bytes() { return DT == DT_F32 ? 4 : (DT == DT_BF16 ? 2 : 1); }
+// Bytes of n stored elements of a row (Q8_0: the int8 plane only; MXFP4: the
+// code plane only, two codes per byte; n even).
+template <int DT> __host__ __device__ constexpr size_t row_bytes(size_t n) {
+    return DT == DT_F32 ? n * 4 : (DT == DT_BF16 ? n * 2 : (DT == DT_Q8 ? n : n / 2));
+}
 
 } // namespace moe

@@ -754,8 +754,8 @@ hipError_t launch_gateup_mfma(const Layer &L, const void *x, const float *tok_sc
         a.b0 = static_cast<const uint16_t *>(routed.gate);
         a.b1 = static_cast<const uint16_t *>(routed.up);
         a.b_stride = (size_t)L.I * L.H;
-        a.s0 = routed.gate_s;
-        a.s1 = routed.up_s;
+        a.s0 = static_cast<const uint16_t *>(routed.gate_s);
+        a.s1 = static_cast<const uint16_t *>(routed.up_s);
         a.s_stride = (size_t)L.I * (L.H / 32);
         a.N = L.I;
         a.K = L.H;
@@ -775,8 +775,8 @@ hipError_t launch_gateup_mfma(const Layer &L, const void *x, const float *tok_sc
         a.max_tiles = (M + a.tile_rows - 1) / a.tile_rows;
         a.b0 = static_cast<const uint16_t *>(shared.gate);
         a.b1 = static_cast<const uint16_t *>(shared.up);
-        a.s0 = shared.gate_s;
-        a.s1 = shared.up_s;
+        a.s0 = static_cast<const uint16_t *>(shared.gate_s);
+        a.s1 = static_cast<const uint16_t *>(shared.up_s);
         a.N = L.Is;
         a.K = L.H;
         a.tok_scale = tok_scale;
@@ -805,7 +805,7 @@ hipError_t launch_down_mfma(const Layer &L, const float *act, const float *share
         a.slab = (size_t)M * L.k * L.H;
         a.b0 = static_cast<const uint16_t *>(routed.down);
         a.b_stride = (size_t)L.H * L.I;
-        a.s0 = routed.down_s;
+        a.s0 = static_cast<const uint16_t *>(routed.down_s);
         a.s_stride = (size_t)L.H * (L.I / 32);
         a.N = L.H;
         a.K = L.I;
@@ -821,7 +821,7 @@ hipError_t launch_down_mfma(const Layer &L, const float *act, const float *share
         a.tile_rows = act_split && M <= 32 ? 32 : kBM;
         a.max_tiles = (M + a.tile_rows - 1) / a.tile_rows;
         a.b0 = static_cast<const uint16_t *>(shared.down);
-        a.s0 = shared.down_s;
+        a.s0 = static_cast<const uint16_t *>(shared.down_s);
         a.N = L.H;
         a.K = L.Is;
         a.out = y_shared;

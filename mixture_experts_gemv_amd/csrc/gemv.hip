@@ -116,13 +116,13 @@ __global__ __launch_bounds__(kThreads) void k_gateup_rows(RowsGateUp a) {
         mrow0 = 0;
     }
     const Mats &m = shared ? a.shared : a.routed;
-    const size_t rbytes = (size_t)H * elem_bytes<WDT>();
+    const size_t rbytes = row_bytes<WDT>(H);
     const char *gbase = reinterpret_cast<const char *>(m.gate) + mrow0 * rbytes;
     const char *ubase = reinterpret_cast<const char *>(m.up) + mrow0 * rbytes;
-    const uint16_t *gsb = nullptr, *usb = nullptr;
-    if constexpr (WDT == DT_Q8) {
-        gsb = m.gate_s + mrow0 * (H / 32);
-        usb = m.up_s + mrow0 * (H / 32);
+    const void *gsb = nullptr, *usb = nullptr;
+    if constexpr (blocked<WDT>()) {
+        gsb = scale_at<WDT>(m.gate_s, mrow0 * (H / 32));
+        usb = scale_at<WDT>(m.up_s, mrow0 * (H / 32));
     }
     const int row_w = rt * kRowsTileGU + wave * kRowsPerWaveGU; // this wave's first row
     const int nch = H / N;
@@ -151,9 +151,9 @@ __global__ __launch_bounds__(kThreads) void k_gateup_rows(RowsGateUp a) {
             for (int cc = 0; cc < CPL; cc++) {
                 B.g[r][cc] = load_raw(gbase + (size_t)(i0 + r) * rbytes, cl[cc]);
                 B.u[r][cc] = load_raw(ubase + (size_t)(i0 + r) * rbytes, cl[cc]);
-                if constexpr (WDT == DT_Q8) {
-                    B.hg[r][cc] = gsb[(size_t)(i0 + r) * (H / 32) + (cl[cc] >> 1)];
-                    B.hu[r][cc] = usb[(size_t)(i0 + r) * (H / 32) + (cl[cc] >> 1)];
+                if constexpr (blocked<WDT>()) {
+                    B.hg[r][cc] = scale_bits<WDT>(gsb, (size_t)(i0 + r) * (H / 32) + chunk_block<WDT>(cl[cc]));
+                    B.hu[r][cc] = scale_bits<WDT>(usb, (size_t)(i0 + r) * (H / 32) + chunk_block<WDT>(cl[cc]));
                 }
             }
     };
@@ -173,12 +173,15 @@ __global__ __launch_bounds__(kThreads) void k_gateup_rows(RowsGateUp a) {
                     if constexpr (WDT == DT_Q8) {
                         q8_to_bf16x2(B.g[r][cc], wg);
                         q8_to_bf16x2(B.u[r][cc], wu);
+                    } else if constexpr (WDT == DT_MX4) {
+                        mx4_to_bf16x2(B.g[r][cc], wg);
+                        mx4_to_bf16x2(B.u[r][cc], wu);
                     } else {
                         wg[0] = B.g[r][cc].x; wg[1] = B.g[r][cc].y; wg[2] = B.g[r][cc].z; wg[3] = B.g[r][cc].w;
                         wu[0] = B.u[r][cc].x; wu[1] = B.u[r][cc].y; wu[2] = B.u[r][cc].z; wu[3] = B.u[r][cc].w;
                     }
-                    const float scg = WDT == DT_Q8 ? f16_bits_to_f32(B.hg[r][cc]) : 1.f;
-                    const float scu = WDT == DT_Q8 ? f16_bits_to_f32(B.hu[r][cc]) : 1.f;
+                    const float scg = blocked<WDT>() ? scale_value<WDT>(B.hg[r][cc]) : 1.f;
+                    const float scu = blocked<WDT>() ? scale_value<WDT>(B.hu[r][cc]) : 1.f;
 #pragma unroll
                     for (int j = 0; j < kTV; j++) {
                         if (j < nj) {
@@ -193,7 +196,7 @@ __global__ __launch_bounds__(kThreads) void k_gateup_rows(RowsGateUp a) {
                                 xw[4 * q4 + 2] = ok[cc] ? v.z : 0u;
                                 xw[4 * q4 + 3] = ok[cc] ? v.w : 0u;
                             }
-                            if constexpr (WDT == DT_Q8) {
+                            if constexpr (blocked<WDT>()) {
                                 float sg = 0.f, su = 0.f;
 #pragma unroll
                                 for (int q = 0; q < NW; q++) {
@@ -216,9 +219,9 @@ __global__ __launch_bounds__(kThreads) void k_gateup_rows(RowsGateUp a) {
                     decode_chunk<WDT>(B.g[r][cc], wg);
                     decode_chunk<WDT>(B.u[r][cc], wu);
                     float scg = ok[cc] ? 1.f : 0.f, scu = scg;
-                    if constexpr (WDT == DT_Q8) {
-                        scg *= f16_bits_to_f32(B.hg[r][cc]);
-                        scu *= f16_bits_to_f32(B.hu[r][cc]);
+                    if constexpr (blocked<WDT>()) {
+                        scg *= scale_value<WDT>(B.hg[r][cc]);
+                        scu *= scale_value<WDT>(B.hu[r][cc]);
                     }
 #pragma unroll
                     for (int j = 0; j < kTV; j++) {
@@ -339,7 +342,7 @@ static void gateup_rows_dispatch(int cpl, const RowsGateUp &a, int grid, size_t 
     }
 }
 
-static int chunk_elems(int dt) { return dt == DT_Q8 ? 16 : (dt == DT_BF16 ? 8 : 4); }
+static int chunk_elems(int dt) { return dt == DT_MX4 ? 32 : (dt == DT_Q8 ? 16 : (dt == DT_BF16 ? 8 : 4)); }
 
 // Token rows one LDS stage of the gate/up kernel holds: up to kStageMax, as
 // LDS allows, and at most kTV when a row spans several chunk blocks.
@@ -385,10 +388,12 @@ hipError_t launch_gateup_gemv(const Layer &L, const void *x, const float *tok_sc
     if (L.xdt == DT_BF16) {
         if (L.edt == DT_BF16) gateup_rows_dispatch<DT_BF16, DT_BF16>(cpl, a, grid, lds, s);
         else if (L.edt == DT_Q8) gateup_rows_dispatch<DT_BF16, DT_Q8>(cpl, a, grid, lds, s);
+        else if (L.edt == DT_MX4) gateup_rows_dispatch<DT_BF16, DT_MX4>(cpl, a, grid, lds, s);
         else gateup_rows_dispatch<DT_BF16, DT_F32>(cpl, a, grid, lds, s);
     } else {
         if (L.edt == DT_BF16) gateup_rows_dispatch<DT_F32, DT_BF16>(cpl, a, grid, lds, s);
         else if (L.edt == DT_Q8) gateup_rows_dispatch<DT_F32, DT_Q8>(cpl, a, grid, lds, s);
+        else if (L.edt == DT_MX4) gateup_rows_dispatch<DT_F32, DT_MX4>(cpl, a, grid, lds, s);
         else gateup_rows_dispatch<DT_F32, DT_F32>(cpl, a, grid, lds, s);
     }
     return hipGetLastError();
@@ -456,10 +461,10 @@ __global__ __launch_bounds__(kThreads) void k_down_rows(RowsDown a) {
     }
     const Mats &m = shared ? a.shared : a.routed;
     const int k0 = ks * KS, klen = min(KS, width - k0);
-    const size_t rbytes = (size_t)width * elem_bytes<WDT>();
-    const char *dbase = reinterpret_cast<const char *>(m.down) + mrow0 * rbytes + (size_t)k0 * elem_bytes<WDT>();
-    const uint16_t *dsb = nullptr;
-    if constexpr (WDT == DT_Q8) dsb = m.down_s + mrow0 * (width / 32) + k0 / 32;
+    const size_t rbytes = row_bytes<WDT>(width);
+    const char *dbase = reinterpret_cast<const char *>(m.down) + mrow0 * rbytes + row_bytes<WDT>(k0);
+    const void *dsb = nullptr;
+    if constexpr (blocked<WDT>()) dsb = scale_at<WDT>(m.down_s, mrow0 * (width / 32) + k0 / 32);
     float *out = shared ? a.y_shared + ks * a.slab_s : a.y_routes + ks * a.slab_r + (size_t)p0 * H;
     const int row_w = rt * kRowsTileDN + wave * kRowsPerWaveDN;
     const int nch = klen / N;
@@ -487,7 +492,8 @@ __global__ __launch_bounds__(kThreads) void k_down_rows(RowsDown a) {
 #pragma unroll
             for (int cc = 0; cc < CPL; cc++) {
                 B.w[r][cc] = load_raw(dbase + (size_t)(h0 + r) * rbytes, cl[cc]);
-                if constexpr (WDT == DT_Q8) B.h[r][cc] = dsb[(size_t)(h0 + r) * (width / 32) + (cl[cc] >> 1)];
+                if constexpr (blocked<WDT>())
+                    B.h[r][cc] = scale_bits<WDT>(dsb, (size_t)(h0 + r) * (width / 32) + chunk_block<WDT>(cl[cc]));
             }
     };
     float acc[RP][kTV];
@@ -502,7 +508,7 @@ __global__ __launch_bounds__(kThreads) void k_down_rows(RowsDown a) {
             for (int r = 0; r < RP; r++) {
                 decode_chunk<WDT>(B.w[r][cc], wv[r]);
                 float sc = ok[cc] ? 1.f : 0.f;
-                if constexpr (WDT == DT_Q8) sc *= f16_bits_to_f32(B.h[r][cc]);
+                if constexpr (blocked<WDT>()) sc *= scale_value<WDT>(B.h[r][cc]);
 #pragma unroll
                 for (int i = 0; i < N; i++) wv[r][i] *= sc;
             }
@@ -587,14 +593,16 @@ int down_gemv_slices(int width) {
     return S;
 }
 
+// (MXFP4 chunks decode to 32 values, so a group takes half the rows.)
 template <int WDT>
 static void down_rows_dispatch(int cpl, const RowsDown &a, int grid, size_t lds, hipStream_t s) {
+    constexpr int R = WDT == DT_MX4 ? 2 : 4;
     switch (cpl) {
-    case 1: launch_kernel((k_down_rows<WDT, 1, 4>), dim3(grid), dim3(kThreads), (uint32_t)lds, s, a); break;
-    case 2: launch_kernel((k_down_rows<WDT, 2, 4>), dim3(grid), dim3(kThreads), (uint32_t)lds, s, a); break;
-    case 3: launch_kernel((k_down_rows<WDT, 3, 4>), dim3(grid), dim3(kThreads), (uint32_t)lds, s, a); break;
-    case 4: launch_kernel((k_down_rows<WDT, 4, 4>), dim3(grid), dim3(kThreads), (uint32_t)lds, s, a); break;
-    default: launch_kernel((k_down_rows<WDT, 8, 2>), dim3(grid), dim3(kThreads), (uint32_t)lds, s, a); break;
+    case 1: launch_kernel((k_down_rows<WDT, 1, R>), dim3(grid), dim3(kThreads), (uint32_t)lds, s, a); break;
+    case 2: launch_kernel((k_down_rows<WDT, 2, R>), dim3(grid), dim3(kThreads), (uint32_t)lds, s, a); break;
+    case 3: launch_kernel((k_down_rows<WDT, 3, R>), dim3(grid), dim3(kThreads), (uint32_t)lds, s, a); break;
+    case 4: launch_kernel((k_down_rows<WDT, 4, R>), dim3(grid), dim3(kThreads), (uint32_t)lds, s, a); break;
+    default: launch_kernel((k_down_rows<WDT, 8, R / 2>), dim3(grid), dim3(kThreads), (uint32_t)lds, s, a); break;
     }
 }
 
@@ -629,6 +637,7 @@ hipError_t launch_down_gemv(const Layer &L, const float *act, const float *share
     const int cpl = rows_cpl(ks_max / chunk_elems(L.edt));
     if (L.edt == DT_BF16) down_rows_dispatch<DT_BF16>(cpl, a, grid, lds, s);
     else if (L.edt == DT_Q8) down_rows_dispatch<DT_Q8>(cpl, a, grid, lds, s);
+    else if (L.edt == DT_MX4) down_rows_dispatch<DT_MX4>(cpl, a, grid, lds, s);
     else down_rows_dispatch<DT_F32>(cpl, a, grid, lds, s);
     return hipGetLastError();
 }
@@ -732,10 +741,10 @@ __global__ __launch_bounds__(kThreads) void k_gateup_m1(M1GateUpArgs a) {
             }
     }
     const int routed_pairs = a.k * a.I;
-    const size_t row_bytes = (size_t)H * elem_bytes<WDT>();
+    const size_t rbytes = row_bytes<WDT>(H);
     for (int p = p_begin; p < p_end; p += RP) {
         const char *grow[RP], *urow[RP];
-        const uint16_t *gsr[RP], *usr[RP];
+        const void *gsr[RP], *usr[RP];
         int slot[RP], irow[RP];
 #pragma unroll
         for (int r = 0; r < RP; r++) {
@@ -753,11 +762,11 @@ __global__ __launch_bounds__(kThreads) void k_gateup_m1(M1GateUpArgs a) {
                 row = irow[r];
                 m = &a.shared;
             }
-            grow[r] = reinterpret_cast<const char *>(m->gate) + row * row_bytes;
-            urow[r] = reinterpret_cast<const char *>(m->up) + row * row_bytes;
-            if constexpr (WDT == DT_Q8) {
-                gsr[r] = m->gate_s + row * (H / 32);
-                usr[r] = m->up_s + row * (H / 32);
+            grow[r] = reinterpret_cast<const char *>(m->gate) + row * rbytes;
+            urow[r] = reinterpret_cast<const char *>(m->up) + row * rbytes;
+            if constexpr (blocked<WDT>()) {
+                gsr[r] = scale_at<WDT>(m->gate_s, row * (H / 32));
+                usr[r] = scale_at<WDT>(m->up_s, row * (H / 32));
             }
         }
         // issue every load of the group first
@@ -769,9 +778,9 @@ __global__ __launch_bounds__(kThreads) void k_gateup_m1(M1GateUpArgs a) {
             for (int cc = 0; cc < CPL; cc++) {
                 rg[r][cc] = load_raw(grow[r], cl[cc]);
                 ru[r][cc] = load_raw(urow[r], cl[cc]);
-                if constexpr (WDT == DT_Q8) {
-                    hg[r][cc] = gsr[r][cl[cc] >> 1];
-                    hu[r][cc] = usr[r][cl[cc] >> 1];
+                if constexpr (blocked<WDT>()) {
+                    hg[r][cc] = scale_bits<WDT>(gsr[r], chunk_block<WDT>(cl[cc]));
+                    hu[r][cc] = scale_bits<WDT>(usr[r], chunk_block<WDT>(cl[cc]));
                 }
             }
 #pragma unroll
@@ -788,9 +797,9 @@ __global__ __launch_bounds__(kThreads) void k_gateup_m1(M1GateUpArgs a) {
                     pg = fmaf(wg[n], xr[cc][n], pg);
                     pu = fmaf(wu[n], xr[cc][n], pu);
                 }
-                if constexpr (WDT == DT_Q8) {
-                    g = fmaf(f16_bits_to_f32(hg[r][cc]), pg, g);
-                    v = fmaf(f16_bits_to_f32(hu[r][cc]), pu, v);
+                if constexpr (blocked<WDT>()) {
+                    g = fmaf(scale_value<WDT>(hg[r][cc]), pg, g);
+                    v = fmaf(scale_value<WDT>(hu[r][cc]), pu, v);
                 } else {
                     g += pg;
                     v += pu;
@@ -835,7 +844,7 @@ template <int WDT>
 __global__ __launch_bounds__(kThreads) void k_down_m1(M1DownArgs a) {
     constexpr int N = Chunk<WDT>::N;
     __shared__ const char *s_row[kMaxSlots];
-    __shared__ const uint16_t *s_sc[kMaxSlots];
+    __shared__ const void *s_sc[kMaxSlots];
     __shared__ const float *s_act[kMaxSlots];
     __shared__ float s_w[kMaxSlots];
     __shared__ int s_width[kMaxSlots];
@@ -851,16 +860,16 @@ __global__ __launch_bounds__(kThreads) void k_down_m1(M1DownArgs a) {
         if (lane < n_routed) {
             // slot = rank in ascending expert id, which is the act row of the pick
             const size_t row = (size_t)my_id * H + h0;
-            s_row[my_rank] = reinterpret_cast<const char *>(a.routed.down) + row * a.I * elem_bytes<WDT>();
-            if constexpr (WDT == DT_Q8) s_sc[my_rank] = a.routed.down_s + row * (a.I / 32);
+            s_row[my_rank] = reinterpret_cast<const char *>(a.routed.down) + row * row_bytes<WDT>(a.I);
+            if constexpr (blocked<WDT>()) s_sc[my_rank] = scale_at<WDT>(a.routed.down_s, row * (a.I / 32));
             s_act[my_rank] = a.act + (size_t)my_rank * a.I;
             s_w[my_rank] = my_w;
             s_width[my_rank] = a.I;
         }
     }
     if (tid == n_routed && a.Is > 0) {
-        s_row[tid] = reinterpret_cast<const char *>(a.shared.down) + (size_t)h0 * a.Is * elem_bytes<WDT>();
-        if constexpr (WDT == DT_Q8) s_sc[tid] = a.shared.down_s + (size_t)h0 * (a.Is / 32);
+        s_row[tid] = reinterpret_cast<const char *>(a.shared.down) + (size_t)h0 * row_bytes<WDT>(a.Is);
+        if constexpr (blocked<WDT>()) s_sc[tid] = scale_at<WDT>(a.shared.down_s, (size_t)h0 * (a.Is / 32));
         s_act[tid] = a.shared_act;
         s_w[tid] = 1.0f;
         s_width[tid] = a.Is;
@@ -889,14 +898,15 @@ __global__ __launch_bounds__(kThreads) void k_down_m1(M1DownArgs a) {
                 c = tc - n_routed * nch;
             }
             const int width = s_width[slot];
-            const size_t rb = (size_t)width * elem_bytes<WDT>();
+            const size_t rb = row_bytes<WDT>(width);
             const char *row0 = s_row[slot];
             wt[u] = t < n_tasks ? s_w[slot] : 0.f;
 #pragma unroll
             for (int r = 0; r < kM1Rows; r++) {
                 const int rr = min(r, last_row);
                 raw[u][r] = load_raw(row0 + rr * rb, c);
-                if constexpr (WDT == DT_Q8) hs[u][r] = s_sc[slot][(size_t)rr * (width / 32) + (c >> 1)];
+                if constexpr (blocked<WDT>())
+                    hs[u][r] = scale_bits<WDT>(s_sc[slot], (size_t)rr * (width / 32) + chunk_block<WDT>(c));
             }
             const f32x4 *ap = reinterpret_cast<const f32x4 *>(s_act[slot] + c * N);
 #pragma unroll
@@ -916,7 +926,7 @@ __global__ __launch_bounds__(kThreads) void k_down_m1(M1DownArgs a) {
                     d = fmaf(wv[4 * n4 + 2], av[u][n4].z, d);
                     d = fmaf(wv[4 * n4 + 3], av[u][n4].w, d);
                 }
-                if constexpr (WDT == DT_Q8) d *= f16_bits_to_f32(hs[u][r]);
+                if constexpr (blocked<WDT>()) d *= scale_value<WDT>(hs[u][r]);
                 acc[r] = fmaf(wt[u], d, acc[r]);
             }
         }
@@ -950,7 +960,7 @@ static bool m1_gateup_dispatch(int cpl, const M1GateUpArgs &a, int grid, hipStre
 }
 
 bool m1_supported(const Layer &L) {
-    const int N = L.edt == DT_Q8 ? 16 : (L.edt == DT_BF16 ? 8 : 4);
+    const int N = chunk_elems(L.edt);
     const int c = m1_cpl(L.H, N);
     return c <= 8 && c != 7;
 }
@@ -980,7 +990,7 @@ hipError_t launch_gateup_m1(const Layer &L, const void *x, const float *tok_scal
     a.act = act;
     a.shared_act = shared_act;
     a.total_pairs = L.k * L.I + a.Is;
-    const int N = L.edt == DT_Q8 ? 16 : (L.edt == DT_BF16 ? 8 : 4);
+    const int N = chunk_elems(L.edt);
     const int cpl = m1_cpl(L.H, N);
     const int RP = cpl <= 4 ? 2 : 1; // keep about 16 loads of a group in flight
     const int max_waves = 2048;
@@ -992,10 +1002,12 @@ hipError_t launch_gateup_m1(const Layer &L, const void *x, const float *tok_scal
     bool ok;
     if (L.xdt == DT_BF16) {
         if (L.edt == DT_Q8) ok = RP == 2 ? m1_gateup_dispatch<DT_BF16, DT_Q8, 2>(cpl, a, grid, s) : m1_gateup_dispatch<DT_BF16, DT_Q8, 1>(cpl, a, grid, s);
+        else if (L.edt == DT_MX4) ok = RP == 2 ? m1_gateup_dispatch<DT_BF16, DT_MX4, 2>(cpl, a, grid, s) : m1_gateup_dispatch<DT_BF16, DT_MX4, 1>(cpl, a, grid, s);
         else if (L.edt == DT_BF16) ok = RP == 2 ? m1_gateup_dispatch<DT_BF16, DT_BF16, 2>(cpl, a, grid, s) : m1_gateup_dispatch<DT_BF16, DT_BF16, 1>(cpl, a, grid, s);
         else ok = RP == 2 ? m1_gateup_dispatch<DT_BF16, DT_F32, 2>(cpl, a, grid, s) : m1_gateup_dispatch<DT_BF16, DT_F32, 1>(cpl, a, grid, s);
     } else {
         if (L.edt == DT_Q8) ok = RP == 2 ? m1_gateup_dispatch<DT_F32, DT_Q8, 2>(cpl, a, grid, s) : m1_gateup_dispatch<DT_F32, DT_Q8, 1>(cpl, a, grid, s);
+        else if (L.edt == DT_MX4) ok = RP == 2 ? m1_gateup_dispatch<DT_F32, DT_MX4, 2>(cpl, a, grid, s) : m1_gateup_dispatch<DT_F32, DT_MX4, 1>(cpl, a, grid, s);
         else if (L.edt == DT_BF16) ok = RP == 2 ? m1_gateup_dispatch<DT_F32, DT_BF16, 2>(cpl, a, grid, s) : m1_gateup_dispatch<DT_F32, DT_BF16, 1>(cpl, a, grid, s);
         else ok = RP == 2 ? m1_gateup_dispatch<DT_F32, DT_F32, 2>(cpl, a, grid, s) : m1_gateup_dispatch<DT_F32, DT_F32, 1>(cpl, a, grid, s);
     }
@@ -1022,6 +1034,7 @@ hipError_t launch_down_m1(const Layer &L, const float *act, const float *shared_
     const dim3 grid((L.H + kM1Rows - 1) / kM1Rows);
     if (L.edt == DT_BF16) launch_kernel(k_down_m1<DT_BF16>, grid, dim3(kThreads), 0, s, a);
     else if (L.edt == DT_Q8) launch_kernel(k_down_m1<DT_Q8>, grid, dim3(kThreads), 0, s, a);
+    else if (L.edt == DT_MX4) launch_kernel(k_down_m1<DT_MX4>, grid, dim3(kThreads), 0, s, a);
     else launch_kernel(k_down_m1<DT_F32>, grid, dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }

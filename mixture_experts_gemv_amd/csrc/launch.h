@@ -11,13 +11,13 @@ struct Layer {
     int H, E, k, I, Is;
     int select, bias_mode;
     float limit, eps;
-    int xdt, rdt, edt, sdt; // DT_F32 / DT_BF16 / DT_Q8
+    int xdt, rdt, edt, sdt; // DT_F32 / DT_BF16 / DT_Q8 / DT_MX4 (experts only)
 };
 
 // Weights of a set of SwiGLU experts: gate/up [n][W][H], down [n][H][W].
 struct Mats {
     const void *gate, *up, *down;
-    const uint16_t *gate_s, *up_s, *down_s; // Q8_0 scale planes or null
+    const void *gate_s, *up_s, *down_s; // block scale planes (Q8_0 fp16, MXFP4 E8M0) or null
 };
 
 // Routing state produced by the permutation.
@@ -103,5 +103,7 @@ hipError_t launch_down_mfma(const Layer &L, const float *act, const float *share
 
 hipError_t launch_q8_split(const void *blocks, int64_t rows, int cols, int8_t *qs,
                            uint16_t *scales, hipStream_t s);
+hipError_t launch_mxfp4_split(const void *blocks, int64_t rows, int cols, uint8_t *codes,
+                              uint8_t *scales, hipStream_t s);
 
 } // namespace moe

@@ -141,28 +141,30 @@ moe_status need_ptr(const void *ptr, size_t align, const char *name) {
 moe_status check_experts(const moe_plan *p, const moe_weights *w, bool need_gateup, bool need_down,
                          bool need_shared) {
     if (!w) return fail(MOE_ERR_INVALID, "weights is NULL");
-    const bool q8 = p->L.edt == moe::DT_Q8;
+    // block scale planes: Q8_0 fp16 (4-byte aligned), MXFP4 E8M0 bytes (any address)
+    auto scale_align = [](int dt) -> size_t { return dt == moe::DT_Q8 ? 4 : (dt == moe::DT_MX4 ? 1 : 0); };
+    const size_t sa = scale_align(p->L.edt);
     if (need_gateup) {
         TRY(need_ptr(w->gate, 16, "weights.gate"));
         TRY(need_ptr(w->up, 16, "weights.up"));
-        if (q8) {
-            TRY(need_ptr(w->gate_scale, 4, "weights.gate_scale"));
-            TRY(need_ptr(w->up_scale, 4, "weights.up_scale"));
+        if (sa) {
+            TRY(need_ptr(w->gate_scale, sa, "weights.gate_scale"));
+            TRY(need_ptr(w->up_scale, sa, "weights.up_scale"));
         }
     }
     if (need_down) {
         TRY(need_ptr(w->down, 16, "weights.down"));
-        if (q8) TRY(need_ptr(w->down_scale, 4, "weights.down_scale"));
+        if (sa) TRY(need_ptr(w->down_scale, sa, "weights.down_scale"));
     }
     if (need_shared && p->L.Is > 0) {
-        const bool sq8 = p->L.sdt == moe::DT_Q8;
+        const size_t ssa = scale_align(p->L.sdt);
         TRY(need_ptr(w->shared_gate, 16, "weights.shared_gate"));
         TRY(need_ptr(w->shared_up, 16, "weights.shared_up"));
         TRY(need_ptr(w->shared_down, 16, "weights.shared_down"));
-        if (sq8) {
-            TRY(need_ptr(w->shared_gate_scale, 4, "weights.shared_gate_scale"));
-            TRY(need_ptr(w->shared_up_scale, 4, "weights.shared_up_scale"));
-            TRY(need_ptr(w->shared_down_scale, 4, "weights.shared_down_scale"));
+        if (ssa) {
+            TRY(need_ptr(w->shared_gate_scale, ssa, "weights.shared_gate_scale"));
+            TRY(need_ptr(w->shared_up_scale, ssa, "weights.shared_up_scale"));
+            TRY(need_ptr(w->shared_down_scale, ssa, "weights.shared_down_scale"));
         }
     }
     return MOE_OK;
@@ -206,7 +208,7 @@ moe_status moe_plan_create(const moe_config *c, moe_plan **out) {
     if (c->path < MOE_PATH_AUTO || c->path > MOE_PATH_MFMA) return fail(MOE_ERR_INVALID, "unknown path %d", c->path);
     if (!(c->swiglu_limit >= 0.f) || !(c->rms_eps >= 0.f))
         return fail(MOE_ERR_INVALID, "swiglu_limit and rms_eps must be >= 0");
-    auto known = [](int d) { return d == MOE_F32 || d == MOE_BF16 || d == MOE_Q8_0; };
+    auto known = [](int d) { return d == MOE_F32 || d == MOE_BF16 || d == MOE_Q8_0 || d == MOE_MXFP4; };
     if (!known(c->x_dtype) || !known(c->router_dtype) || !known(c->expert_dtype) ||
         (c->shared_inter > 0 && !known(c->shared_dtype)))
         return fail(MOE_ERR_INVALID, "unknown dtype");
@@ -217,7 +219,8 @@ moe_status moe_plan_create(const moe_config *c, moe_plan **out) {
     if (c->hidden % 32 || c->expert_inter % 32 || c->shared_inter % 32)
         return fail(MOE_ERR_UNSUPPORTED, "hidden, expert_inter and shared_inter must be multiples of 32");
     if (c->hidden > 16384) return fail(MOE_ERR_UNSUPPORTED, "hidden %d exceeds 16384", c->hidden);
-    if (c->x_dtype == MOE_Q8_0 || c->router_dtype == MOE_Q8_0)
+    if (c->x_dtype == MOE_Q8_0 || c->router_dtype == MOE_Q8_0 || c->x_dtype == MOE_MXFP4 ||
+        c->router_dtype == MOE_MXFP4)
         return fail(MOE_ERR_UNSUPPORTED, "x and router must be fp32 or bf16");
     if (c->shared_inter > 0 && c->shared_dtype != c->expert_dtype)
         return fail(MOE_ERR_UNSUPPORTED, "the shared expert must use the routed experts' dtype");
@@ -229,8 +232,8 @@ moe_status moe_plan_create(const moe_config *c, moe_plan **out) {
     const bool mfma_ok = moe::mfma_supported(L);
     if (c->path == MOE_PATH_MFMA && !mfma_ok)
         return fail(MOE_ERR_UNSUPPORTED,
-                    "the MFMA path needs bf16 x, bf16 or Q8_0 experts and hidden, expert_inter, shared_inter "
-                    "multiples of 64");
+                    "the MFMA path needs bf16 x, bf16 or Q8_0 experts (MXFP4 experts run on the GEMV "
+                    "kernels) and hidden, expert_inter, shared_inter multiples of 64");
     moe_plan *p = new moe_plan;
     p->cfg = *c;
     p->L = L;
@@ -533,6 +536,17 @@ moe_status moe_q8_0_split(const void *blocks, int64_t rows, int32_t cols, int8_t
     return MOE_OK;
 }
 
+moe_status moe_mxfp4_split(const void *blocks, int64_t rows, int32_t cols, uint8_t *codes,
+                           uint8_t *scales, void *stream) {
+    if (rows < 0 || cols <= 0 || cols % 32) return fail(MOE_ERR_INVALID, "rows %lld, cols %d: need rows >= 0 and cols a positive multiple of 32", (long long)rows, cols);
+    if (rows == 0) return MOE_OK;
+    TRY(need_ptr(blocks, 1, "blocks"));
+    TRY(need_ptr(codes, 16, "codes"));
+    TRY(need_ptr(scales, 1, "scales"));
+    LAUNCH(moe::launch_mxfp4_split(blocks, rows, cols, codes, scales, (hipStream_t)stream), "MXFP4 split");
+    return MOE_OK;
+}
+
 } // extern "C"
 
 // ---------------------------------------------------------------- Q8_0 split
@@ -555,6 +569,35 @@ hipError_t launch_q8_split(const void *blocks, int64_t rows, int cols, int8_t *q
     const int64_t nb = rows * (cols / 32);
     launch_kernel(k_q8_split, dim3((unsigned)((nb + 255) / 256)), dim3(256), 0, s,
                        reinterpret_cast<const uint16_t *>(blocks), nb, qs, scales);
+    return hipGetLastError();
+}
+
+} // namespace moe
+
+// ---------------------------------------------------------------- MXFP4 split
+namespace moe {
+
+// One thread per block: the E8M0 byte, then the 16 code bytes (as stored:
+// element 2j in the low nibble of byte j) written as one 16-byte store.
+__global__ __launch_bounds__(256) void k_mxfp4_split(const uint8_t *blocks, int64_t nblocks, uint8_t *codes,
+                                                     uint8_t *scales) {
+    const int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (b >= nblocks) return;
+    const uint8_t *src = blocks + b * 17;
+    scales[b] = src[0];
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+        w[i] = (uint32_t)src[1 + 4 * i] | ((uint32_t)src[2 + 4 * i] << 8) | ((uint32_t)src[3 + 4 * i] << 16) |
+               ((uint32_t)src[4 + 4 * i] << 24);
+    reinterpret_cast<u32x4 *>(codes)[b] = u32x4{w[0], w[1], w[2], w[3]};
+}
+
+hipError_t launch_mxfp4_split(const void *blocks, int64_t rows, int cols, uint8_t *codes, uint8_t *scales,
+                              hipStream_t s) {
+    const int64_t nb = rows * (cols / 32);
+    launch_kernel(k_mxfp4_split, dim3((unsigned)((nb + 255) / 256)), dim3(256), 0, s,
+                  reinterpret_cast<const uint8_t *>(blocks), nb, codes, scales);
     return hipGetLastError();
 }
 

@@ -1,9 +1,10 @@
 """Device-resident MoE layer: uploads host weights and calls the C ABI.
 
 Host weights come in their storage formats (fp32 ``float32``, bf16 as
-``uint16`` bit patterns, Q8_0 as ``uint8`` 34-byte blocks along the reduction
-dimension).  Q8_0 tensors are split on the device into the int8 and fp16-scale
-planes the kernels read (``moe_q8_0_split``).
+``uint16`` bit patterns, Q8_0 as ``uint8`` 34-byte blocks and MXFP4 as
+``uint8`` 17-byte blocks along the reduction dimension).  Q8_0 and MXFP4
+tensors are split on the device into the value and scale planes the kernels
+read (``moe_q8_0_split``, ``moe_mxfp4_split``).
 """
 
 from __future__ import annotations
@@ -13,8 +14,9 @@ from typing import Dict, Optional
 import numpy as np
 import torch
 
-from . import (MOE_BF16, MOE_F32, MOE_PATH_AUTO, MOE_Q8_0, make_weights, moe_forward,
-               moe_plan_create, moe_q8_0_split, moe_workspace_bytes, moe_workspace_init)
+from . import (MOE_BF16, MOE_F32, MOE_MXFP4, MOE_PATH_AUTO, MOE_Q8_0, make_weights, moe_forward,
+               moe_mxfp4_split, moe_plan_create, moe_q8_0_split, moe_workspace_bytes,
+               moe_workspace_init)
 
 _TORCH_DTYPE = {MOE_F32: torch.float32, MOE_BF16: torch.bfloat16}
 
@@ -54,6 +56,14 @@ class MoeLayer:
             sc = torch.empty(rows * cols // 32, dtype=torch.int16, device=self.device)
             moe_q8_0_split(blocks, rows, cols, qs, sc)
             self.tensors[name] = qs
+            self.tensors[name + "_scale"] = sc
+            del blocks
+        elif dtype == MOE_MXFP4:
+            blocks = upload(np.ascontiguousarray(arr).reshape(-1), self.device)
+            codes = torch.empty(rows * cols // 2, dtype=torch.uint8, device=self.device)
+            sc = torch.empty(rows * cols // 32, dtype=torch.uint8, device=self.device)
+            moe_mxfp4_split(blocks, rows, cols, codes, sc)
+            self.tensors[name] = codes
             self.tensors[name + "_scale"] = sc
             del blocks
         else:

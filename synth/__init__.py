@@ -122,6 +122,14 @@ SPECS: Dict[str, LayerSpec] = {
         expert_inter=1536, select=SIGMOID_NORM, bias_mode=BIAS_SELECT_ONLY,
         bias_kind="normal", bias_std=0.05, router_dtype=F32, seed=1007,
         token_counts=(1, 16)),
+    # the gpt-oss-20B shape with its routed experts in MXFP4, the format the
+    # pages name for gpt-oss's routed pair (scale bytes 2^-9..2^-5 give weights
+    # of about the Q8_0 layer's magnitude)
+    "gpt-oss-20b-mxfp4": LayerSpec(
+        name="gpt-oss-20b-mxfp4", hidden=2880, num_experts=32, top_k=4,
+        expert_inter=2880, bias_mode=BIAS_LOGIT, bias_kind="normal",
+        bias_std=0.1, swiglu_limit=7.0, expert_dtype=MXFP4, seed=1008,
+        token_counts=(1, 16)),
 }
 
 _NTHREADS = max(1, min(16, len(os.sched_getaffinity(0))))

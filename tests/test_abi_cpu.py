@@ -72,6 +72,10 @@ def _create(**kw):
     (dict(select=m.MOE_SIGMOID_NORM, bias_mode=m.MOE_BIAS_LOGIT), m.MOE_ERR_UNSUPPORTED),
     (dict(path=m.MOE_PATH_MFMA, x_dtype=m.MOE_F32), m.MOE_ERR_UNSUPPORTED),
     (dict(path=m.MOE_PATH_MFMA, expert_dtype=m.MOE_F32), m.MOE_ERR_UNSUPPORTED),
+    (dict(x_dtype=m.MOE_MXFP4), m.MOE_ERR_UNSUPPORTED),
+    (dict(router_dtype=m.MOE_MXFP4), m.MOE_ERR_UNSUPPORTED),
+    (dict(shared_inter=64, expert_dtype=m.MOE_MXFP4, shared_dtype=m.MOE_Q8_0), m.MOE_ERR_UNSUPPORTED),
+    (dict(path=m.MOE_PATH_MFMA, expert_dtype=m.MOE_MXFP4), m.MOE_ERR_UNSUPPORTED),
 ])
 def test_plan_refusals(kw, status):
     with pytest.raises(m.MoeError) as ei:
@@ -144,6 +148,22 @@ def test_call_refusals_before_any_launch():
     assert L.moe_q8_0_split(FAKE, 4, 33, FAKE, FAKE, None) == m.MOE_ERR_INVALID
     assert L.moe_q8_0_split(FAKE, -1, 32, FAKE, FAKE, None) == m.MOE_ERR_INVALID
     assert L.moe_q8_0_split(None, 0, 32, None, None, None) == m.MOE_OK
+    # MXFP4 needs its scale planes (any alignment) and code planes 16-byte aligned
+    px = _create(expert_dtype=m.MOE_MXFP4)
+    st = L.moe_expert_ffn(px.handle, FAKE, ctypes.byref(w), 4, FAKE, FAKE, FAKE, FAKE,
+                          m.moe_workspace_bytes(px, 4), None)
+    assert st == m.MOE_ERR_INVALID and "scale" in m.moe_last_error()
+    unaligned = m.make_weights(router=FAKE, gate=FAKE + 8, up=FAKE, down=FAKE, gate_scale=FAKE + 1,
+                               up_scale=FAKE + 3, down_scale=FAKE + 5)
+    assert m.moe_workspace_bytes(px, 4) > 0
+    st = L.moe_expert_ffn(px.handle, FAKE, ctypes.byref(unaligned), 4, FAKE, FAKE, FAKE, FAKE,
+                          m.moe_workspace_bytes(px, 4), None)
+    assert st == m.MOE_ERR_INVALID and "gate" in m.moe_last_error()
+    assert m.MOE_RUN_NAMES[m.moe_forward_path(px, 1)] == "single"
+    assert L.moe_mxfp4_split(FAKE, 4, 48, FAKE, FAKE, None) == m.MOE_ERR_INVALID
+    assert L.moe_mxfp4_split(FAKE, -1, 32, FAKE, FAKE, None) == m.MOE_ERR_INVALID
+    assert L.moe_mxfp4_split(FAKE, 4, 32, FAKE + 8, FAKE, None) == m.MOE_ERR_INVALID
+    assert L.moe_mxfp4_split(None, 0, 32, None, None, None) == m.MOE_OK
 
 
 def test_forward_path_choice():
@@ -152,7 +172,8 @@ def test_forward_path_choice():
     # Mixtral M=16: 4, DeepSeek M=16: 1.5, gpt-oss (Q8_0) M=16: 2
     want = {("gpt-oss-20b", 1): "single", ("gpt-oss-20b", 16): "gemv",
             ("mixtral-8x7b", 1): "single", ("mixtral-8x7b", 16): "mfma", ("mixtral-8x7b", 512): "mfma",
-            ("qwen3-30b-a3b", 2048): "mfma", ("deepseek-v2-lite", 16): "gemv"}
+            ("qwen3-30b-a3b", 2048): "mfma", ("deepseek-v2-lite", 16): "gemv",
+            ("gpt-oss-20b-mxfp4", 1): "single", ("gpt-oss-20b-mxfp4", 16): "gemv"}
     for (name, M), run in want.items():
         spec = synth.SPECS[name]
         p = m.moe_plan_create(spec.hidden, spec.num_experts, spec.top_k, spec.expert_inter,

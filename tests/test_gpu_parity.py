@@ -7,7 +7,7 @@ import pytest
 
 import oracle
 import synth
-from synth import BF16, F32, Q8_0, BIAS_LOGIT, BIAS_SELECT_ONLY, SIGMOID_NORM, SOFTMAX_ALL_NORENORM
+from synth import BF16, F32, MXFP4, Q8_0, BIAS_LOGIT, BIAS_SELECT_ONLY, SIGMOID_NORM, SOFTMAX_ALL_NORENORM
 from gpu_helpers import (SIGMOID_TAU, W_ABS, check_ids, check_ids_keys, check_y, device_layer,
                          forward_parity, host_layer, say)
 
@@ -237,6 +237,18 @@ SMALL = [
     ("sigmoid-bias", dict(hidden=256, num_experts=16, top_k=4, expert_inter=128, select=SIGMOID_NORM,
                           bias_mode=BIAS_SELECT_ONLY, bias_kind="normal", bias_std=0.05,
                           router_dtype=F32), (1, 5, 16)),
+    ("mx4-bias-clamp", dict(hidden=288, num_experts=12, top_k=4, expert_inter=320,
+                            bias_mode=BIAS_LOGIT, bias_kind="normal", swiglu_limit=7.0,
+                            expert_dtype=MXFP4), (1, 5, 16)),
+    ("mx4-shared-many", dict(hidden=128, num_experts=6, top_k=2, expert_inter=64,
+                             shared_inter=96, expert_dtype=MXFP4, shared_dtype=MXFP4), (1, 64, 100)),
+    ("f32x-mx4", dict(hidden=160, num_experts=5, top_k=2, expert_inter=64, x_dtype=F32,
+                      router_dtype=F32, expert_dtype=MXFP4), (1, 2, 12)),
+    ("mx4-wide-h", dict(hidden=4608, num_experts=4, top_k=2, expert_inter=96, expert_dtype=MXFP4),
+     (1, 3)),
+    ("mx4-all-shared-rms", dict(hidden=192, num_experts=16, top_k=6, expert_inter=2112,
+                                shared_inter=160, select=SOFTMAX_ALL_NORENORM, rms_eps=1e-6,
+                                expert_dtype=MXFP4, shared_dtype=MXFP4), (1, 9)),
 ]
 
 
@@ -401,7 +413,8 @@ FULL = [("tiny", 4, None), ("gpt-oss-20b", 1, None), ("gpt-oss-20b", 16, None), 
         ("mixtral-8x7b", 1, None), ("mixtral-8x7b", 16, None),
         ("mixtral-8x7b", 512, 12), ("qwen3-30b-a3b", 2048, 24),
         ("deepseek-v2-lite-dense", 1, None), ("deepseek-v2-lite-dense", 16, None),
-        ("deepseek-v2-lite-dense", 512, 8), ("sigmoid-e256", 1, None), ("sigmoid-e256", 16, None)]
+        ("deepseek-v2-lite-dense", 512, 8), ("sigmoid-e256", 1, None), ("sigmoid-e256", 16, None),
+        ("gpt-oss-20b-mxfp4", 1, None), ("gpt-oss-20b-mxfp4", 16, None), ("gpt-oss-20b-mxfp4", 64, 8)]
 
 
 @pytest.mark.parametrize("name,M,nsample", FULL, ids=[f"{n}-M{m}" for n, m, _ in FULL])
