@@ -45,6 +45,8 @@ MUTANTS = {
     20: "MXFP4 scale exponent bias 128",
     21: "MXFP4 exponent field 0 given an implicit one",
     22: "MXFP4 reads the next block's scale",
+    23: "norm weight applied to the router input only",
+    24: "residual stream not added",
 }
 
 
@@ -79,6 +81,7 @@ def lib():
         L = ctypes.CDLL(_LIB)
         P = ctypes.c_void_p
         L.orc_forward.argtypes = [ctypes.POINTER(_Layer), ctypes.c_int] + [P] * 16
+        L.orc_forward_fused.argtypes = [ctypes.POINTER(_Layer), ctypes.c_int] + [P] * 18
         L.orc_forward.restype = ctypes.c_int
         L.orc_select.argtypes = [ctypes.POINTER(_Layer), ctypes.c_int, P, P, P, P, P]
         L.orc_permute.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, P, P, P, P, P]
@@ -106,8 +109,13 @@ def layer_struct(spec) -> _Layer:
 
 
 def forward(spec, layer: Dict[str, Optional[np.ndarray]], x: np.ndarray,
-            forced_ids: Optional[np.ndarray] = None, want_act: bool = False) -> Dict[str, np.ndarray]:
-    """Run the whole layer on ``x [M][H]``; returns logits, ids, w, counts, y (and act)."""
+            forced_ids: Optional[np.ndarray] = None, want_act: bool = False,
+            norm_w: Optional[np.ndarray] = None,
+            residual: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
+    """Run the whole layer on ``x [M][H]``; returns logits, ids, w, counts, y (and act).
+
+    ``norm_w`` (``[H]`` in the x storage format) weights the RMS pre-norm
+    (needs ``spec.rms_eps > 0``); ``residual`` (``[M][H]`` fp32) is added to y."""
     M = x.shape[0]
     E, k, H, I = spec.num_experts, spec.top_k, spec.hidden, spec.expert_inter
     out = {
@@ -122,8 +130,11 @@ def forward(spec, layer: Dict[str, Optional[np.ndarray]], x: np.ndarray,
     bias = layer.get("bias")
     bias = None if bias is None else np.ascontiguousarray(bias, np.float32)
     st = layer_struct(spec)
-    rc = lib().orc_forward(
-        ctypes.byref(st), M, _ptr(np.ascontiguousarray(x)), _ptr(layer["router"]), _ptr(bias),
+    nw = None if norm_w is None else np.ascontiguousarray(norm_w)
+    res = None if residual is None else np.ascontiguousarray(residual, np.float32)
+    rc = lib().orc_forward_fused(
+        ctypes.byref(st), M, _ptr(np.ascontiguousarray(x)), _ptr(nw), _ptr(res),
+        _ptr(layer["router"]), _ptr(bias),
         _ptr(layer["gate"]), _ptr(layer["up"]), _ptr(layer["down"]),
         _ptr(layer.get("shared_gate")), _ptr(layer.get("shared_up")),
         _ptr(layer.get("shared_down")), _ptr(fids), _ptr(out["logits"]), _ptr(out["ids"]),

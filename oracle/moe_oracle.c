@@ -104,7 +104,9 @@ enum {
     MUT_E8M0_BIAS_128 = 20,         /* MXFP4: scale exponent bias 128 instead of 127 */
     MUT_FP4_NO_SUBNORMAL = 21,      /* MXFP4: exponent field 0 given an implicit leading one */
     MUT_MX_NEXT_BLOCK_SCALE = 22,   /* MXFP4: the next block's scale */
-    MUT_COUNT = 23
+    MUT_NORM_WEIGHT_ROUTER_ONLY = 23, /* fused norm: the experts see the unit-gain rows */
+    MUT_RESIDUAL_DROPPED = 24,      /* fused: the residual stream is not added */
+    MUT_COUNT = 25
 };
 static int orc_mutant = MUT_NONE;
 
@@ -194,8 +196,11 @@ static double orc_row_dot(const void *base, int fmt, size_t r, size_t cols, cons
     return s;
 }
 
-/* ---- step 0 (optional): RMS pre-norm with unit gain ---- */
-void orc_norm_tokens(const orc_layer *L, int M, const void *x, double *xn)
+/* ---- step 0 (optional): RMS pre-norm, x / sqrt(mean(x^2) + eps) * gamma ----
+ * deepseek2/state.rs module doc: f = rms_norm(x, post_attention_layernorm)
+ * feeds the router and the experts.  gamma (norm_w, [H] in the x format) is
+ * the norm's weight; NULL is unit gain. */
+static void norm_tokens(const orc_layer *L, int M, const void *x, const void *norm_w, double *xn)
 {
     const int H = L->hidden;
     for (int t = 0; t < M; t++) {
@@ -207,10 +212,18 @@ void orc_norm_tokens(const orc_layer *L, int M, const void *x, double *xn)
                 ss += xn[(size_t)t * H + i] * xn[(size_t)t * H + i];
             double mean = (orc_mutant == MUT_RMS_SUM_NOT_MEAN) ? ss : ss / H;
             double r = sqrt(mean + L->rms_eps);
-            for (int i = 0; i < H; i++)
+            for (int i = 0; i < H; i++) {
                 xn[(size_t)t * H + i] /= r;
+                if (norm_w)
+                    xn[(size_t)t * H + i] *= orc_at(norm_w, L->x_fmt, 0, H, i);
+            }
         }
     }
+}
+
+void orc_norm_tokens(const orc_layer *L, int M, const void *x, double *xn)
+{
+    norm_tokens(L, M, x, NULL, xn);
 }
 
 /* ---- step 1: router logits ---- */
@@ -417,14 +430,26 @@ void orc_down(int H, int width, int fmt, const void *down, int mat, const double
  * Outputs (any may be NULL except y): logits[M][E], ids[M][k], w[M][k],
  * counts[E], act[M*k][I] (route-major, r = t*k + j), y[M][H].
  * forced_ids (or NULL) fixes the selection, as described above. */
-int orc_forward(const orc_layer *L, int M, const void *x, const void *router, const float *bias,
-                const void *gate, const void *up, const void *down, const void *sgate,
-                const void *sup, const void *sdown, const int32_t *forced_ids, double *logits_out,
-                int32_t *ids_out, double *w_out, int32_t *counts_out, double *act_out, double *y)
+/* The layer with its neighbours (deepseek2/state.rs module doc: the normed
+ * rows f feed the router and the experts, and x += routed_sum + shared
+ * SwiGLU(f); gptoss/state.rs, BatchedRoutedScratch: the routed sum reaches
+ * the stream through one residual add):
+ *   y_t = residual_t + shared(f_t) + sum_j w_j expert_j(f_t),
+ *   f_t = x_t / sqrt(mean(x_t^2) + eps) * norm_w.
+ * norm_w ([H] in the x format) needs rms_eps > 0 (else the call is refused);
+ * residual ([M][H] fp32) or NULL for zeros.  orc_forward is the case
+ * norm_w = residual = NULL. */
+int orc_forward_fused(const orc_layer *L, int M, const void *x, const void *norm_w,
+                      const float *residual, const void *router, const float *bias, const void *gate,
+                      const void *up, const void *down, const void *sgate, const void *sup,
+                      const void *sdown, const int32_t *forced_ids, double *logits_out,
+                      int32_t *ids_out, double *w_out, int32_t *counts_out, double *act_out, double *y)
 {
     const int H = L->hidden, E = L->num_experts, k = L->top_k, I = L->expert_inter;
     const int Is = L->shared_inter;
     if (M < 0 || H <= 0 || E <= 0 || k <= 0 || k > E || I <= 0 || Is < 0)
+        return 1;
+    if (norm_w && !(L->rms_eps > 0.0))
         return 1;
     if (M == 0)
         return 0;
@@ -432,13 +457,17 @@ int orc_forward(const orc_layer *L, int M, const void *x, const void *router, co
     double *logits = malloc(sizeof(double) * (size_t)M * E);
     int32_t *ids = malloc(sizeof(int32_t) * (size_t)M * k);
     double *w = malloc(sizeof(double) * (size_t)M * k);
-    orc_norm_tokens(L, M, x, xn);
+    norm_tokens(L, M, x, norm_w, xn);
     if (orc_mutant == MUT_NORM_ROUTER_ONLY) {
         /* the router sees the normed rows, the experts the raw ones */
         orc_router_logits(L, M, xn, router, logits);
         orc_layer raw = *L;
         raw.rms_eps = 0.0;
-        orc_norm_tokens(&raw, M, x, xn);
+        norm_tokens(&raw, M, x, NULL, xn);
+    } else if (orc_mutant == MUT_NORM_WEIGHT_ROUTER_ONLY) {
+        /* the router sees the weighted rows, the experts the unit-gain ones */
+        orc_router_logits(L, M, xn, router, logits);
+        norm_tokens(L, M, x, NULL, xn);
     } else {
         orc_router_logits(L, M, xn, router, logits);
     }
@@ -451,14 +480,15 @@ int orc_forward(const orc_layer *L, int M, const void *x, const void *router, co
         int wmax = I > Is ? I : Is;
         double *act = malloc(sizeof(double) * wmax);
         double *out = malloc(sizeof(double) * H);
-        /* seed: the shared expert (weight 1, no clamp), else zeros */
+        /* seed: the residual stream (or zeros), plus the shared expert
+           (weight 1, no clamp) */
         for (int h = 0; h < H; h++)
-            yt[h] = 0.0;
+            yt[h] = (residual && orc_mutant != MUT_RESIDUAL_DROPPED) ? (double)residual[(size_t)t * H + h] : 0.0;
         if (Is > 0 && orc_mutant != MUT_DROP_SHARED) {
             orc_swiglu_act(H, Is, L->shared_fmt, 0.0, sgate, sup, 0, xt, act);
             orc_down(H, Is, L->shared_fmt, sdown, 0, act, out);
             for (int h = 0; h < H; h++)
-                yt[h] = out[h];
+                yt[h] += out[h];
         }
         /* routed experts, summed in slot order */
         for (int j = 0; j < k; j++) {
@@ -493,6 +523,15 @@ int orc_forward(const orc_layer *L, int M, const void *x, const void *router, co
     free(ids);
     free(w);
     return 0;
+}
+
+int orc_forward(const orc_layer *L, int M, const void *x, const void *router, const float *bias,
+                const void *gate, const void *up, const void *down, const void *sgate,
+                const void *sup, const void *sdown, const int32_t *forced_ids, double *logits_out,
+                int32_t *ids_out, double *w_out, int32_t *counts_out, double *act_out, double *y)
+{
+    return orc_forward_fused(L, M, x, NULL, NULL, router, bias, gate, up, down, sgate, sup, sdown,
+                             forced_ids, logits_out, ids_out, w_out, counts_out, act_out, y);
 }
 
 /* Expose the element reader so tests can check the format decoding against

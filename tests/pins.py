@@ -604,6 +604,65 @@ def pin_prenorm_scale_invariance():
     _close(a["y"], b["y"], rtol=1e-9, what="pre-norm scale invariance")
 
 
+def pin_fused_norm_weight_and_residual():
+    """The fused neighbours (deepseek2/state.rs module doc: f = rms_norm(x,
+    post_attention_layernorm) feeds the router and the experts; x += routed
+    sum + shared expert).  A unit norm weight is the unit-gain pre-norm; the
+    weighted norm stays invariant under scaling x; the residual adds to y."""
+    spec = _spec(num_experts=6, top_k=2, rms_eps=1e-12, shared_inter=64, x_dtype=BF16, seed=31)
+    layer = synth.make_layer(spec)
+    x = synth.make_tokens(spec, 4)
+    plain = oracle.forward(spec, layer, x)
+    ones = synth.bf16_bits(np.ones(spec.hidden, np.float32))
+    unit = oracle.forward(spec, layer, x, norm_w=ones)
+    assert np.array_equal(plain["ids"], unit["ids"])
+    _close(plain["y"], unit["y"], rtol=0, atol=0, what="unit norm weight")
+    rng = np.random.default_rng(5)
+    gamma = synth.bf16_bits(rng.uniform(0.5, 1.5, spec.hidden).astype(np.float32))
+    a = oracle.forward(spec, layer, x, norm_w=gamma)
+    x4 = synth.bf16_bits(synth.bf16_to_f32(x) * np.float32(4.0))
+    c = oracle.forward(spec, layer, x4, norm_w=gamma)
+    assert np.array_equal(a["ids"], c["ids"])
+    _close(a["y"], c["y"], rtol=1e-9, what="weighted norm scale invariance")
+    res = rng.standard_normal((4, spec.hidden)).astype(np.float32)
+    r = oracle.forward(spec, layer, x, norm_w=gamma, residual=res)
+    assert np.array_equal(a["ids"], r["ids"])
+    _close(r["y"] - a["y"], res.astype(np.float64), rtol=1e-12, atol=1e-12, what="residual add")
+    # a norm weight needs the pre-norm on
+    try:
+        oracle.forward(spec.replace(rms_eps=0.0), layer, x, norm_w=gamma)
+    except ValueError:
+        pass
+    else:
+        raise AssertionError("a norm weight without the pre-norm was accepted")
+
+
+def pin_fused_closed_form():
+    """Hand-derived case: H = I = 32, x = ones, eps = 3, so mean(x^2) + eps =
+    4 and f = gamma / 2.  Router rows e_0 and e_1 with gamma_0 = 2 and
+    gamma_1 = 4 give logits 1 and 2: expert 1 is picked (k = 1, weight 1),
+    whereas without the weight the logits tie at 0.5 and expert 0 (all-zero
+    weights) would win.  Expert 1 has identity gate, up and down, so
+    y_i = r_i + f_i * silu(f_i) = r_i + f_i^2 / (1 + exp(-f_i))."""
+    H = 32
+    spec = synth.small_spec(hidden=H, num_experts=2, top_k=1, expert_inter=H, rms_eps=3.0,
+                            x_dtype=F32, router_dtype=F32, expert_dtype=F32, shared_dtype=F32)
+    eye = np.eye(H, dtype=np.float32)
+    router = np.zeros((2, H), np.float32)
+    router[0, 0] = router[1, 1] = 1.0
+    zeros = np.zeros((H, H), np.float32)
+    layer = {"router": router, "bias": None,
+             "gate": np.stack([zeros, eye]), "up": np.stack([zeros, eye]), "down": np.stack([zeros, eye])}
+    gamma = np.array([2.0, 4.0] + [i / 4 for i in range(2, H)], np.float32)
+    x = np.ones((1, H), np.float32)
+    res = np.arange(H, dtype=np.float32).reshape(1, H) - 7.0
+    o = oracle.forward(spec, layer, x, norm_w=gamma, residual=res)
+    assert o["ids"].tolist() == [[1]], f"ids {o['ids'].tolist()}"
+    f = gamma.astype(np.float64) / 2.0
+    want = res.astype(np.float64)[0] + f * f / (1.0 + np.exp(-f))
+    _close(o["y"][0], want, rtol=1e-15, atol=1e-15, what="fused closed form")
+
+
 # ---------------------------------------------------------------------------
 # Hand-derived fixtures (tests/golden/*.json)
 # ---------------------------------------------------------------------------
@@ -670,4 +729,5 @@ PINS = [
     pin_clamp, pin_q8_vs_bf16, pin_single_expert_dense, pin_permute,
     pin_prenorm_scale_invariance, pin_golden_selection, pin_golden_layer, pin_golden_q8_0,
     pin_sigmoid_scoring, pin_mxfp4_vs_bf16, pin_golden_mxfp4,
+    pin_fused_norm_weight_and_residual, pin_fused_closed_form,
 ]
