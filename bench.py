@@ -40,7 +40,7 @@ def bytes_per_weight(dtype: int) -> float:
     return {0: 4.0, 1: 2.0, 2: 34.0 / 32.0, 3: 17.0 / 32.0}[dtype]
 
 
-def algorithmic_bytes(spec, M: int, counts: np.ndarray) -> dict:
+def algorithmic_bytes(spec, M: int, counts: np.ndarray, fused: bool = False) -> dict:
     """Bytes the layer must move per call (weights of touched experts once).
 
     `gateup_kernel` is what the gate/up kernel itself must move: the touched
@@ -54,6 +54,8 @@ def algorithmic_bytes(spec, M: int, counts: np.ndarray) -> dict:
     down = T * H * I * bpw + (H * Is * bytes_per_weight(spec.shared_dtype) if Is else 0)
     router = H * E * bytes_per_weight(spec.router_dtype) + (4 * E if spec.bias_mode else 0)
     layer = gate_up + down + router + M * H * bpx + 4 * M * H
+    if fused:  # the residual read, and the norm weight
+        layer += 4 * M * H + (H * bpx if spec.rms_eps > 0 else 0)
     gk = gate_up + M * H * bpx + 4 * (R * I + M * Is)
     return {"layer": layer, "gateup_kernel": gk, "touched": T}
 
@@ -139,6 +141,9 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches only")
+    ap.add_argument("--fused", action="store_true",
+                    help="time moe_forward_fused: the pre-norm's weight (when the workload has the "
+                         "pre-norm) and the residual stream updated in place")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run 5 plain 256 MiB device copies (counter calibration) and exit")
     args = ap.parse_args()
@@ -197,16 +202,27 @@ def main() -> int:
 
     K, W = args.steps, args.warmup
 
+    norm_w = None
+    if args.fused and spec.rms_eps > 0:
+        gw = torch.Generator(device=dev)
+        gw.manual_seed(4099)
+        nw = torch.empty(spec.hidden, device=dev).uniform_(0.25, 2.0, generator=gw)
+        norm_w = nw.bfloat16() if spec.x_dtype == 1 else nw
+    y.zero_()
+
     def step(i, cnt_out=None):
         lay = copies[i % L]
-        m.moe_forward(lay.plan, xs[i % P], lay.weights, M, y, None, None, cnt_out, ws)
+        if args.fused:
+            m.moe_forward_fused(lay.plan, xs[i % P], norm_w, y, lay.weights, M, y, None, None, cnt_out, ws)
+        else:
+            m.moe_forward(lay.plan, xs[i % P], lay.weights, M, y, None, None, cnt_out, ws)
 
     # realised expert counts of exactly the timed calls (untimed pre-pass)
     for i in range(K):
         step(i, counts[i])
     torch.cuda.synchronize()
     run = m.moe_forward_path(base.plan, M)
-    ab = [algorithmic_bytes(spec, M, c.cpu().numpy()) for c in counts]
+    ab = [algorithmic_bytes(spec, M, c.cpu().numpy(), args.fused) for c in counts]
     layer_bytes_avg = float(np.mean([a["layer"] for a in ab]))
     gateup_bytes_avg = float(np.mean([a["gateup_kernel"] for a in ab]))
     touched_avg = float(np.mean([a["touched"] for a in ab]))
@@ -301,6 +317,9 @@ def main() -> int:
             "tokens_per_call": M, "layer_copies": L, "token_batches": P,
             "touched_experts_avg": touched_avg,
             "timing": "hip_graph_replay" if graph_ms is not None else "eager",
+            "call": ("moe_forward_fused (norm weight %s, residual in place); per-kernel times from "
+                     "the unfused moe_forward_timed" % ("on" if norm_w is not None else "off")
+                     if args.fused else "moe_forward"),
         },
         "eager": {"tokens_per_s": M * K / (eager_ms * 1e-3), "ms_per_step": eager_ms / K},
         "roofline": {

@@ -217,6 +217,26 @@ moe_status moe_forward(const moe_plan *plan, const void *x, const moe_weights *w
                        float *y, int32_t *ids_out, float *w_out, int32_t *counts_out, void *ws,
                        size_t ws_bytes, void *stream);
 
+/* The layer with its neighbours fused (deepseek2/state.rs, module doc: the
+ * post-attention RMSNorm with its weight, rms_norm(x, post_attention_layernorm),
+ * feeds the router and the experts, and the routed sum plus the shared
+ * expert is added to the residual stream, x += routed_sum + shared;
+ * gptoss/state.rs, BatchedRoutedScratch: the routed sum reaches the stream
+ * through one residual add):
+ *   f_t = x_t / sqrt(mean_i x_ti^2 + rms_eps) * norm_weight,
+ *   y_t = residual_t + shared(f_t) + sum_j w_j expert_j(f_t).
+ * norm_weight: [H] stored like x (16-byte aligned), or NULL for unit gain;
+ * a non-NULL norm_weight needs a plan with rms_eps > 0 (MOE_ERR_INVALID
+ * otherwise).  residual: [M][H] fp32 (16-byte aligned) or NULL (zeros); it
+ * may be y itself, which then updates the stream in place.  The normed rows
+ * are computed once (fp32) into the workspace, which for plans with
+ * rms_eps > 0 holds room for them.  Other arguments as moe_forward; with
+ * both NULL this is moe_forward. */
+moe_status moe_forward_fused(const moe_plan *plan, const void *x, const void *norm_weight,
+                             const float *residual, const moe_weights *wts, int32_t M, float *y,
+                             int32_t *ids_out, float *w_out, int32_t *counts_out, void *ws,
+                             size_t ws_bytes, void *stream);
+
 /* Kernels of moe_forward, in launch order, as reported by moe_forward_timed. */
 typedef enum {
     MOE_STAGE_RMS = 0,     /* pre-norm scale (only when rms_eps > 0) */

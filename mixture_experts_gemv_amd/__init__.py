@@ -77,6 +77,7 @@ def lib() -> ctypes.CDLL:
         L.moe_expert_ffn.argtypes = [P, P, W, I32, P, P, P, P, SZ, P]
         L.moe_combine.argtypes = [P, P, W, I32, P, P, P, P, P, P, P, SZ, P]
         L.moe_forward.argtypes = [P, P, W, I32, P, P, P, P, P, SZ, P]
+        L.moe_forward_fused.argtypes = [P, P, P, P, W, I32, P, P, P, P, P, SZ, P]
         L.moe_forward_timed.argtypes = [P, P, W, I32, P, P, P, P, P, SZ, P,
                                         ctypes.POINTER(P), I32, P, ctypes.POINTER(I32)]
         L.moe_q8_0_split.argtypes = [P, ctypes.c_int64, I32, P, P, P]
@@ -85,7 +86,7 @@ def lib() -> ctypes.CDLL:
         L.moe_workspace_init.restype = I32
         L.moe_forward_path.argtypes = [P, I32]
         L.moe_forward_path.restype = I32
-        for f in ("moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_forward",
+        for f in ("moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_forward", "moe_forward_fused",
                   "moe_forward_timed", "moe_q8_0_split", "moe_mxfp4_split"):
             getattr(L, f).restype = I32
         _lib = L
@@ -199,6 +200,13 @@ def moe_forward(plan, x, weights, M, y, ids_out, w_out, counts_out, ws, stream=N
     _check(lib().moe_forward(plan.handle, _ptr(x), ctypes.byref(weights), M, _ptr(y),
                              _ptr(ids_out), _ptr(w_out), _ptr(counts_out), _ptr(ws), _nbytes(ws),
                              _stream(stream)))
+
+
+def moe_forward_fused(plan, x, norm_weight, residual, weights, M, y, ids_out, w_out, counts_out, ws,
+                      stream=None):
+    _check(lib().moe_forward_fused(plan.handle, _ptr(x), _ptr(norm_weight), _ptr(residual),
+                                   ctypes.byref(weights), M, _ptr(y), _ptr(ids_out), _ptr(w_out),
+                                   _ptr(counts_out), _ptr(ws), _nbytes(ws), _stream(stream)))
 
 
 MOE_STAGE_NAMES = ("rms", "router", "topk", "permute", "gateup", "down", "combine")

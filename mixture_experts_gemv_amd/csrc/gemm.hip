@@ -682,8 +682,8 @@ __global__ __launch_bounds__(kGThreads, 2) void k_gemm_reg(GemmArgs a) {
     }
 }
 
-// a_mode: 0 = bf16 A rows (gate/up), 1 = split A rows (hi/lo pairs), 2 = fp32 A rows
-// (both down).  bq: B is Q8_0 (a.s0 / a.s1 hold its scales); not with fp32 A.
+// a_mode: 0 = bf16 A rows (gate/up), 1 = split A rows (hi/lo pairs: act of down, or the fused
+// layer's normed x of gate/up), 2 = fp32 A rows (down).  bq: B is Q8_0 (a.s0 / a.s1 hold its scales); not with fp32 A.
 template <int KIND, bool AS>
 static void launch_lds(const GemmArgs &a, bool bq, unsigned grid, hipStream_t s) {
     if (a.tile_rows == 32) {
@@ -711,6 +711,7 @@ static hipError_t run_gemm(int kind, int a_mode, bool bq, GemmArgs &a, hipStream
         const unsigned grid = (unsigned)((long)a.max_tiles * per_tile);
         if (a.tile_rows != 32 && a.tile_rows != kBM) return hipErrorInvalidValue;
         if (kind == GK_GATEUP && a_mode == 0) launch_lds<GK_GATEUP, false>(a, bq, grid, s);
+        else if (kind == GK_GATEUP && a_mode == 1) launch_lds<GK_GATEUP, true>(a, bq, grid, s);
         else if (kind == GK_PLAIN && a_mode == 1) launch_lds<GK_PLAIN, true>(a, bq, grid, s);
         else return hipErrorInvalidValue;
     }
@@ -740,7 +741,8 @@ int down_ksplit(const Layer &L, int M, int tile_rows) {
 
 hipError_t launch_gateup_mfma(const Layer &L, const void *x, const float *tok_scale, const Mats &routed,
                               const Mats &shared, const Routing &rt, int M, int max_tiles, int tile_rows,
-                              float *act, float *shared_act, bool act_split, hipStream_t s) {
+                              float *act, float *shared_act, bool act_split, hipStream_t s, bool x_split) {
+    const int a_mode = x_split ? 1 : 0;
     if (act) {
         GemmArgs a{};
         a.tile_rows = tile_rows;
@@ -764,7 +766,7 @@ hipError_t launch_gateup_mfma(const Layer &L, const void *x, const float *tok_sc
         a.out = act;
         a.ldo = L.I;
         a.out_split = act_split;
-        hipError_t err = run_gemm(GK_GATEUP, 0, L.edt == DT_Q8, a, s);
+        hipError_t err = run_gemm(GK_GATEUP, a_mode, L.edt == DT_Q8, a, s);
         if (err != hipSuccess) return err;
     }
     if (shared_act && L.Is > 0) {
@@ -784,7 +786,7 @@ hipError_t launch_gateup_mfma(const Layer &L, const void *x, const float *tok_sc
         a.out = shared_act;
         a.ldo = L.Is;
         a.out_split = act_split;
-        return run_gemm(GK_GATEUP, 0, L.sdt == DT_Q8, a, s);
+        return run_gemm(GK_GATEUP, a_mode, L.sdt == DT_Q8, a, s);
     }
     return hipSuccess;
 }

@@ -40,6 +40,13 @@ constexpr int kTV = 4;                   // vectors dotted per pass over loaded 
 constexpr int kStageMax = 8;             // vectors one LDS stage holds, at most
 constexpr int kStageBytes = 64 * 1024;   // LDS for staged vectors, per workgroup
 constexpr int kSliceMax = 2048;          // reduction elements per down slice
+// Rows per load group with MXFP4 weights, whose 16-byte chunks hold half the
+// bytes of a Q8_0 row's: more rows keep as many bytes in flight per wave
+// (one-token gate/up with at most two chunks per lane; per-row gate/up with
+// at most two; per-row down with at most four).
+constexpr int kMx4RowsM1 = 2;
+constexpr int kMx4RowsGU = 2;
+constexpr int kMx4RowsDN = 2;
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
@@ -333,9 +340,10 @@ static int rows_cpl(int chunks) {
 
 template <int XDT, int WDT>
 static void gateup_rows_dispatch(int cpl, const RowsGateUp &a, int grid, size_t lds, hipStream_t s) {
+    constexpr int R = WDT == DT_MX4 ? kMx4RowsGU : 2;
     switch (cpl) {
-    case 1: launch_kernel((k_gateup_rows<XDT, WDT, 1, 2>), dim3(grid), dim3(kThreads), (uint32_t)lds, s, a); break;
-    case 2: launch_kernel((k_gateup_rows<XDT, WDT, 2, 2>), dim3(grid), dim3(kThreads), (uint32_t)lds, s, a); break;
+    case 1: launch_kernel((k_gateup_rows<XDT, WDT, 1, R>), dim3(grid), dim3(kThreads), (uint32_t)lds, s, a); break;
+    case 2: launch_kernel((k_gateup_rows<XDT, WDT, 2, R>), dim3(grid), dim3(kThreads), (uint32_t)lds, s, a); break;
     case 3: launch_kernel((k_gateup_rows<XDT, WDT, 3, 2>), dim3(grid), dim3(kThreads), (uint32_t)lds, s, a); break;
     case 4: launch_kernel((k_gateup_rows<XDT, WDT, 4, 2>), dim3(grid), dim3(kThreads), (uint32_t)lds, s, a); break;
     default: launch_kernel((k_gateup_rows<XDT, WDT, 8, 1>), dim3(grid), dim3(kThreads), (uint32_t)lds, s, a); break;
@@ -596,7 +604,7 @@ int down_gemv_slices(int width) {
 // (MXFP4 chunks decode to 32 values, so a group takes half the rows.)
 template <int WDT>
 static void down_rows_dispatch(int cpl, const RowsDown &a, int grid, size_t lds, hipStream_t s) {
-    constexpr int R = WDT == DT_MX4 ? 2 : 4;
+    constexpr int R = WDT == DT_MX4 ? kMx4RowsDN : 4;
     switch (cpl) {
     case 1: launch_kernel((k_down_rows<WDT, 1, R>), dim3(grid), dim3(kThreads), (uint32_t)lds, s, a); break;
     case 2: launch_kernel((k_down_rows<WDT, 2, R>), dim3(grid), dim3(kThreads), (uint32_t)lds, s, a); break;
@@ -959,6 +967,15 @@ static bool m1_gateup_dispatch(int cpl, const M1GateUpArgs &a, int grid, hipStre
 #undef M1_CASE
 }
 
+// MXFP4 with at most two chunks per lane: kMx4RowsM1 rows per group.
+template <int XDT>
+static bool m1_gateup_dispatch_mx4(int cpl, const M1GateUpArgs &a, int grid, hipStream_t s) {
+    if (cpl == 1) launch_kernel((k_gateup_m1<XDT, DT_MX4, 1, kMx4RowsM1>), dim3(grid), dim3(kThreads), 0, s, a);
+    else if (cpl == 2) launch_kernel((k_gateup_m1<XDT, DT_MX4, 2, kMx4RowsM1>), dim3(grid), dim3(kThreads), 0, s, a);
+    else return false;
+    return true;
+}
+
 bool m1_supported(const Layer &L) {
     const int N = chunk_elems(L.edt);
     const int c = m1_cpl(L.H, N);
@@ -992,7 +1009,8 @@ hipError_t launch_gateup_m1(const Layer &L, const void *x, const float *tok_scal
     a.total_pairs = L.k * L.I + a.Is;
     const int N = chunk_elems(L.edt);
     const int cpl = m1_cpl(L.H, N);
-    const int RP = cpl <= 4 ? 2 : 1; // keep about 16 loads of a group in flight
+    // keep about 16 loads of a group in flight
+    const int RP = L.edt == DT_MX4 && cpl <= 2 ? kMx4RowsM1 : (cpl <= 4 ? 2 : 1);
     const int max_waves = 2048;
     int ppw = (a.total_pairs + max_waves - 1) / max_waves;
     ppw = (ppw + RP - 1) / RP * RP;
@@ -1002,12 +1020,12 @@ hipError_t launch_gateup_m1(const Layer &L, const void *x, const float *tok_scal
     bool ok;
     if (L.xdt == DT_BF16) {
         if (L.edt == DT_Q8) ok = RP == 2 ? m1_gateup_dispatch<DT_BF16, DT_Q8, 2>(cpl, a, grid, s) : m1_gateup_dispatch<DT_BF16, DT_Q8, 1>(cpl, a, grid, s);
-        else if (L.edt == DT_MX4) ok = RP == 2 ? m1_gateup_dispatch<DT_BF16, DT_MX4, 2>(cpl, a, grid, s) : m1_gateup_dispatch<DT_BF16, DT_MX4, 1>(cpl, a, grid, s);
+        else if (L.edt == DT_MX4) ok = cpl <= 2 ? m1_gateup_dispatch_mx4<DT_BF16>(cpl, a, grid, s) : RP == 2 ? m1_gateup_dispatch<DT_BF16, DT_MX4, 2>(cpl, a, grid, s) : m1_gateup_dispatch<DT_BF16, DT_MX4, 1>(cpl, a, grid, s);
         else if (L.edt == DT_BF16) ok = RP == 2 ? m1_gateup_dispatch<DT_BF16, DT_BF16, 2>(cpl, a, grid, s) : m1_gateup_dispatch<DT_BF16, DT_BF16, 1>(cpl, a, grid, s);
         else ok = RP == 2 ? m1_gateup_dispatch<DT_BF16, DT_F32, 2>(cpl, a, grid, s) : m1_gateup_dispatch<DT_BF16, DT_F32, 1>(cpl, a, grid, s);
     } else {
         if (L.edt == DT_Q8) ok = RP == 2 ? m1_gateup_dispatch<DT_F32, DT_Q8, 2>(cpl, a, grid, s) : m1_gateup_dispatch<DT_F32, DT_Q8, 1>(cpl, a, grid, s);
-        else if (L.edt == DT_MX4) ok = RP == 2 ? m1_gateup_dispatch<DT_F32, DT_MX4, 2>(cpl, a, grid, s) : m1_gateup_dispatch<DT_F32, DT_MX4, 1>(cpl, a, grid, s);
+        else if (L.edt == DT_MX4) ok = cpl <= 2 ? m1_gateup_dispatch_mx4<DT_F32>(cpl, a, grid, s) : RP == 2 ? m1_gateup_dispatch<DT_F32, DT_MX4, 2>(cpl, a, grid, s) : m1_gateup_dispatch<DT_F32, DT_MX4, 1>(cpl, a, grid, s);
         else if (L.edt == DT_BF16) ok = RP == 2 ? m1_gateup_dispatch<DT_F32, DT_BF16, 2>(cpl, a, grid, s) : m1_gateup_dispatch<DT_F32, DT_BF16, 1>(cpl, a, grid, s);
         else ok = RP == 2 ? m1_gateup_dispatch<DT_F32, DT_F32, 2>(cpl, a, grid, s) : m1_gateup_dispatch<DT_F32, DT_F32, 1>(cpl, a, grid, s);
     }

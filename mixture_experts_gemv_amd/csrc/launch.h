@@ -31,6 +31,10 @@ struct Routing {
 };
 
 hipError_t launch_rms_scale(const Layer &L, const void *x, int M, float *scale, hipStream_t s);
+// xn = x * scale[t] * gamma (fp32 rows); xs (or null): the same rows split
+// into bf16 hi/lo pairs, the A layout of the grouped GEMM.
+hipError_t launch_norm_apply(const Layer &L, const void *x, const void *gamma, const float *scale, int M,
+                             float *xn, uint16_t *xs, hipStream_t s);
 hipError_t launch_router(const Layer &L, const void *x, const void *router, const float *tok_scale,
                          int M, float *logits, hipStream_t s);
 hipError_t launch_topk(const Layer &L, const float *logits, const float *bias, int M, int32_t *ids,
@@ -91,9 +95,11 @@ int mfma_tile_rows(const Layer &L, int M);     // tiles of the layer call for M 
 bool mfma_supported(const Layer &L);
 hipError_t launch_router_mfma(const Layer &L, const void *x, const void *router, const float *tok_scale,
                               int M, float *logits, hipStream_t s);
+// x_split: x rows are split bf16 hi/lo pairs (launch_norm_apply's xs) rather than bf16.
 hipError_t launch_gateup_mfma(const Layer &L, const void *x, const float *tok_scale, const Mats &routed,
                               const Mats &shared, const Routing &rt, int M, int max_tiles, int tile_rows,
-                              float *act, float *shared_act, bool act_split, hipStream_t s);
+                              float *act, float *shared_act, bool act_split, hipStream_t s,
+                              bool x_split = false);
 // act_split: act / shared_act rows hold the hi/lo bf16 pairs the gate/up GEMM
 // writes with act_split (same size as fp32 rows); else fp32 rows.
 hipError_t launch_down_mfma(const Layer &L, const float *act, const float *shared_act,

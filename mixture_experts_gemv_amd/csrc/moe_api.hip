@@ -44,7 +44,7 @@ size_t up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 // Where each workspace region starts for a call with M tokens.
 struct WsLayout {
     size_t sync, tok_scale, logits, ids, w, counts, offsets, sorted, route_pos, active, tiles;
-    size_t act, shared_act, y_routes, y_shared, total;
+    size_t act, shared_act, y_routes, y_shared, xn, xs, total;
     int max_tiles;
 };
 
@@ -93,6 +93,10 @@ WsLayout layout(const moe_plan *p, int M) {
                                : moe::down_gemv_slices(L.I);
     w.y_routes = take(slices * R * L.H * 4);
     w.y_shared = take(L.Is > 0 ? (size_t)(mfma ? 1 : moe::down_gemv_slices(L.Is)) * M * L.H * 4 : 0);
+    // the weighted pre-norm's rows (moe_forward_fused with a norm weight):
+    // fp32, and split bf16 for the grouped GEMM; only plans with the pre-norm on
+    w.xn = take(L.eps > 0.f ? (size_t)M * L.H * 4 : 0);
+    w.xs = take(L.eps > 0.f && mfma ? (size_t)M * L.H * 4 : 0);
     w.total = o;
     return w;
 }
@@ -402,26 +406,48 @@ struct Recorder {
         (rec).after(stage);                         \
     } while (0)
 
+// norm_w ([H] like x, or null) weights the pre-norm, which must be on;
+// residual ([M][H] fp32, or null; may be y) seeds the combine.
 static moe_status forward_impl(const moe_plan *p, const void *x, const moe_weights *wts, int32_t M,
                                float *y, int32_t *ids_out, float *w_out, int32_t *counts_out,
-                               void *ws, size_t ws_bytes, hipStream_t s, Recorder &rec) {
+                               void *ws, size_t ws_bytes, hipStream_t s, Recorder &rec,
+                               const void *norm_w = nullptr, const float *residual = nullptr) {
     TRY(check_call(p, M, ws, ws_bytes));
     if (M == 0) return MOE_OK;
     TRY(need_ptr(x, 16, "x"));
+    if (norm_w) {
+        if (!(p->L.eps > 0.f))
+            return fail(MOE_ERR_INVALID, "a norm weight needs the pre-norm on (rms_eps > 0)");
+        TRY(need_ptr(norm_w, 16, "norm_weight"));
+    }
+    if (residual) TRY(need_ptr(residual, 16, "residual"));
     TRY(check_router(p, wts, true));
     TRY(check_experts(p, wts, true, true, true));
     TRY(need_ptr(y, 16, "y"));
     if (ids_out) TRY(need_ptr(ids_out, 4, "ids_out"));
     if (w_out) TRY(need_ptr(w_out, 4, "w_out"));
     if (counts_out) TRY(need_ptr(counts_out, 4, "counts_out"));
-    const moe::Layer &L = p->L;
     const WsLayout lay = layout(p, M);
+    const bool mfma = use_mfma(p, M);
+    // L: what the kernels see.  With a norm weight the normed rows are
+    // written once (fp32, and split bf16 for the grouped GEMM) and the rest
+    // of the layer reads them as fp32 x with the pre-norm done.
+    moe::Layer L = p->L;
     const int R = M * L.k;
-
     float *sc = nullptr;
+    uint16_t *xsplit = nullptr;
     if (L.eps > 0.f) {
         sc = at<float>(ws, lay.tok_scale);
         STAGE(rec, moe::launch_rms_scale(L, x, M, sc, s), "rms scale", MOE_STAGE_RMS);
+        if (norm_w) {
+            float *xn = at<float>(ws, lay.xn);
+            xsplit = mfma ? at<uint16_t>(ws, lay.xs) : nullptr;
+            STAGE(rec, moe::launch_norm_apply(L, x, norm_w, sc, M, xn, xsplit, s), "norm", MOE_STAGE_RMS);
+            x = xn;
+            sc = nullptr;
+            L.xdt = moe::DT_F32;
+            L.eps = 0.f;
+        }
     }
     float *lg = at<float>(ws, lay.logits);
     int32_t *ids = ids_out ? ids_out : at<int32_t>(ws, lay.ids);
@@ -432,7 +458,6 @@ static moe_status forward_impl(const moe_plan *p, const void *x, const moe_weigh
     int32_t *rpos = at<int32_t>(ws, lay.route_pos);
     int32_t *active = at<int32_t>(ws, lay.active);
     int32_t *tiles = lay.max_tiles ? at<int32_t>(ws, lay.tiles) : nullptr;
-    const bool mfma = use_mfma(p, M);
     const int rows = moe::mfma_tile_rows(L, M); // tile height of the grouped GEMMs
     const bool single = M == 1 && !mfma && moe::m1_supported(L);
     if (single) {
@@ -443,7 +468,7 @@ static moe_status forward_impl(const moe_plan *p, const void *x, const moe_weigh
                                            sorted, rpos, active, s),
               "route", MOE_STAGE_ROUTER);
     } else {
-        if (mfma && L.rdt == moe::DT_BF16)
+        if (mfma && L.rdt == moe::DT_BF16 && L.xdt == moe::DT_BF16)
             STAGE(rec, moe::launch_router_mfma(L, x, wts->router, sc, M, lg, s), "router (MFMA)", MOE_STAGE_ROUTER);
         else
             STAGE(rec, moe::launch_router(L, x, wts->router, sc, M, lg, s), "router", MOE_STAGE_ROUTER);
@@ -457,26 +482,27 @@ static moe_status forward_impl(const moe_plan *p, const void *x, const moe_weigh
     float *yr = at<float>(ws, lay.y_routes);
     float *ysh = L.Is > 0 ? at<float>(ws, lay.y_shared) : nullptr;
     if (mfma) {
-        STAGE(rec, moe::launch_gateup_mfma(L, x, sc, routed_mats(wts), shared_mats(wts), rt, M,
-                                           lay.max_tiles, rows, act, sact, true, s),
+        STAGE(rec, moe::launch_gateup_mfma(L, xsplit ? (const void *)xsplit : x, sc, routed_mats(wts),
+                                           shared_mats(wts), rt, M, lay.max_tiles, rows, act, sact, true, s,
+                                           xsplit != nullptr),
               "gate/up (MFMA)", MOE_STAGE_GATEUP);
         STAGE(rec, moe::launch_down_mfma(L, act, sact, routed_mats(wts), shared_mats(wts), rt, M,
                                          lay.max_tiles, rows, yr, ysh, true, s),
               "down (MFMA)", MOE_STAGE_DOWN);
-        STAGE(rec, moe::launch_combine(L, yr, ysh, rpos, w, nullptr, M, y, s, moe::down_ksplit(L, M, rows), 1),
+        STAGE(rec, moe::launch_combine(L, yr, ysh, rpos, w, residual, M, y, s, moe::down_ksplit(L, M, rows), 1),
               "combine", MOE_STAGE_COMBINE);
     } else if (single) {
         STAGE(rec, moe::launch_gateup_m1(L, x, sc, routed_mats(wts), shared_mats(wts), lg, wts->bias, ids, w,
                                          counts_out, act, sact, s),
               "top-k + gate/up", MOE_STAGE_GATEUP);
-        STAGE(rec, moe::launch_down_m1(L, act, sact, routed_mats(wts), shared_mats(wts), ids, w, nullptr, y, s),
+        STAGE(rec, moe::launch_down_m1(L, act, sact, routed_mats(wts), shared_mats(wts), ids, w, residual, y, s),
               "down + combine", MOE_STAGE_DOWN);
     } else {
         STAGE(rec, moe::launch_gateup_gemv(L, x, sc, routed_mats(wts), shared_mats(wts), rt, M, act, sact, s),
               "gate/up", MOE_STAGE_GATEUP);
         STAGE(rec, moe::launch_down_gemv(L, act, sact, routed_mats(wts), shared_mats(wts), rt, M, yr, ysh, s),
               "down", MOE_STAGE_DOWN);
-        STAGE(rec, moe::launch_combine(L, yr, ysh, rpos, w, nullptr, M, y, s, moe::down_gemv_slices(L.I),
+        STAGE(rec, moe::launch_combine(L, yr, ysh, rpos, w, residual, M, y, s, moe::down_gemv_slices(L.I),
                                        moe::down_gemv_slices(L.Is)),
               "combine", MOE_STAGE_COMBINE);
     }
@@ -488,6 +514,15 @@ moe_status moe_forward(const moe_plan *p, const void *x, const moe_weights *wts,
                        size_t ws_bytes, void *stream) {
     Recorder rec;
     return forward_impl(p, x, wts, M, y, ids_out, w_out, counts_out, ws, ws_bytes, (hipStream_t)stream, rec);
+}
+
+moe_status moe_forward_fused(const moe_plan *p, const void *x, const void *norm_weight,
+                             const float *residual, const moe_weights *wts, int32_t M, float *y,
+                             int32_t *ids_out, float *w_out, int32_t *counts_out, void *ws, size_t ws_bytes,
+                             void *stream) {
+    Recorder rec;
+    return forward_impl(p, x, wts, M, y, ids_out, w_out, counts_out, ws, ws_bytes, (hipStream_t)stream, rec,
+                        norm_weight, residual);
 }
 
 moe_status moe_forward_timed(const moe_plan *p, const void *x, const moe_weights *wts, int32_t M,

@@ -39,6 +39,54 @@ hipError_t launch_rms_scale(const Layer &L, const void *x, int M, float *scale, 
     return hipGetLastError();
 }
 
+// The normed rows of the fused layer: xn[t][i] = x[t][i] * scale[t] * gamma[i]
+// (gamma stored like x; null = unit gain) as fp32 rows, and, when xs is
+// given, as the split bf16 rows the grouped GEMM reads (per 8 elements: their
+// 8 hi values bf16(v), then their 8 lo values bf16(v - hi)).  One thread per
+// 8 elements of a row.
+template <int XDT>
+__global__ __launch_bounds__(256) void k_norm_apply(const void *x, const void *gamma, const float *scale, int H,
+                                                    float *xn, uint16_t *xs) {
+    const int t = blockIdx.y;
+    const int c = blockIdx.x * 256 + threadIdx.x;
+    if (c >= H / 8) return;
+    float v[8], g[8];
+    load8<XDT>(reinterpret_cast<const char *>(x) + (size_t)t * H * dt_bytes<XDT>(), c, v);
+    if (gamma) {
+        load8<XDT>(gamma, c, g);
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; i++) g[i] = 1.f;
+    }
+    const float sc = scale[t];
+#pragma unroll
+    for (int i = 0; i < 8; i++) v[i] = v[i] * sc * g[i];
+    f32x4 *o = reinterpret_cast<f32x4 *>(xn + (size_t)t * H + (size_t)c * 8);
+    o[0] = f32x4{v[0], v[1], v[2], v[3]};
+    o[1] = f32x4{v[4], v[5], v[6], v[7]};
+    if (xs) {
+        uint32_t hi[8], lo[8];
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            hi[i] = f32_to_bf16_rne(v[i]);
+            lo[i] = f32_to_bf16_rne(v[i] - __uint_as_float(hi[i] << 16));
+        }
+        u32x4 *q = reinterpret_cast<u32x4 *>(xs + (size_t)t * H * 2 + (size_t)c * 16);
+        q[0] = u32x4{hi[0] | hi[1] << 16, hi[2] | hi[3] << 16, hi[4] | hi[5] << 16, hi[6] | hi[7] << 16};
+        q[1] = u32x4{lo[0] | lo[1] << 16, lo[2] | lo[3] << 16, lo[4] | lo[5] << 16, lo[6] | lo[7] << 16};
+    }
+}
+
+hipError_t launch_norm_apply(const Layer &L, const void *x, const void *gamma, const float *scale, int M,
+                             float *xn, uint16_t *xs, hipStream_t s) {
+    const dim3 grid((L.H / 8 + 255) / 256, M);
+    if (L.xdt == DT_BF16)
+        launch_kernel(k_norm_apply<DT_BF16>, grid, dim3(256), 0, s, x, gamma, scale, L.H, xn, xs);
+    else
+        launch_kernel(k_norm_apply<DT_F32>, grid, dim3(256), 0, s, x, gamma, scale, L.H, xn, xs);
+    return hipGetLastError();
+}
+
 // ---------------------------------------------------------------- router dots
 // One wave: logits of expert row `wrow` for tokens t0..t0+nt-1 (nt <= TM).
 // Lanes stride the row in 8-element pieces, CB pieces per lane per block.

@@ -15,7 +15,7 @@ import numpy as np
 import torch
 
 from . import (MOE_BF16, MOE_F32, MOE_MXFP4, MOE_PATH_AUTO, MOE_Q8_0, make_weights, moe_forward,
-               moe_mxfp4_split, moe_plan_create, moe_q8_0_split, moe_workspace_bytes,
+               moe_forward_fused, moe_mxfp4_split, moe_plan_create, moe_q8_0_split, moe_workspace_bytes,
                moe_workspace_init)
 
 _TORCH_DTYPE = {MOE_F32: torch.float32, MOE_BF16: torch.bfloat16}
@@ -112,4 +112,16 @@ class MoeLayer:
         if y is None:
             y = torch.empty(M, self.H, dtype=torch.float32, device=self.device)
         moe_forward(self.plan, x, self.weights, M, y, ids, w, counts, ws, stream)
+        return y
+
+    def forward_fused(self, x: torch.Tensor, norm_weight=None, residual=None, ws=None, y=None,
+                      ids=None, w=None, counts=None, stream=None) -> torch.Tensor:
+        """y = residual + layer(rms_norm(x) * norm_weight) (moe_forward_fused)."""
+        M = x.shape[0]
+        if ws is None:
+            ws = self.workspace(M)
+        if y is None:
+            y = torch.empty(M, self.H, dtype=torch.float32, device=self.device)
+        moe_forward_fused(self.plan, x, norm_weight, residual, self.weights, M, y, ids, w, counts, ws,
+                          stream)
         return y

@@ -50,11 +50,13 @@ def device_layer(spec, layer, max_tokens, path=0):
     return dl
 
 
-def selection_keys(spec, layer, x):
+def selection_keys(spec, layer, x, norm_w=None):
     """fp64 selection keys s[t][e] and the near-tie bound tau[t]."""
     xf = dequant(x, spec.x_dtype, x.shape[0], spec.hidden)
     if spec.rms_eps > 0:
         xf = xf / np.sqrt(np.mean(xf * xf, axis=1, keepdims=True) + spec.rms_eps)
+        if norm_w is not None:
+            xf = xf * dequant(np.asarray(norm_w).reshape(1, -1), spec.x_dtype, 1, spec.hidden)
     wr = dequant(layer["router"], spec.router_dtype, spec.num_experts, spec.hidden)
     logits = xf @ wr.T
     b = np.zeros(spec.num_experts) if layer.get("bias") is None else layer["bias"].astype(np.float64)
@@ -68,7 +70,7 @@ def selection_keys(spec, layer, x):
     return s, tau
 
 
-def check_ids(spec, layer, x, gpu_ids, ora_ids):
+def check_ids(spec, layer, x, gpu_ids, ora_ids, norm_w=None):
     """Apply the near-tie rule; return (forced ids for the oracle, number of near-tie tokens).
 
     Tokens whose k-th and (k+1)-th fp64 keys are further apart than tau must get
@@ -76,7 +78,7 @@ def check_ids(spec, layer, x, gpu_ids, ora_ids):
     every expert whose key clears the boundary by more than tau and draw the
     rest from keys within tau of it; the oracle is then re-run on the GPU's set.
     """
-    s, tau = selection_keys(spec, layer, x)
+    s, tau = selection_keys(spec, layer, x, norm_w)
     return check_ids_keys(s, tau, spec.top_k, gpu_ids, ora_ids)
 
 
@@ -116,28 +118,44 @@ def check_y(y_gpu, y_ref, what=""):
     return max_abs, rel
 
 
-def run_forward(dl, x_host, M=None):
+def run_forward(dl, x_host, M=None, fused=None):
+    """moe_forward, or with fused = (norm_w host array or None, residual host
+    array or None, in_place) moe_forward_fused."""
     import torch
     x = dl.x_tensor(x_host)
     M = x.shape[0]
     ids = torch.empty(M, dl.k, dtype=torch.int32, device=dl.device)
     w = torch.empty(M, dl.k, dtype=torch.float32, device=dl.device)
     counts = torch.empty(dl.E, dtype=torch.int32, device=dl.device)
-    y = dl.forward(x, ids=ids, w=w, counts=counts)
+    if fused is None:
+        y = dl.forward(x, ids=ids, w=w, counts=counts)
+    else:
+        norm_w, residual, in_place = fused
+        nw = None if norm_w is None else dl.x_tensor(np.ascontiguousarray(norm_w))
+        res = None if residual is None else torch.from_numpy(np.ascontiguousarray(residual, np.float32)).to(dl.device)
+        if in_place:
+            y = dl.forward_fused(x, norm_weight=nw, residual=res, y=res, ids=ids, w=w, counts=counts)
+        else:
+            y = dl.forward_fused(x, norm_weight=nw, residual=res, ids=ids, w=w, counts=counts)
     torch.cuda.synchronize()
     return y.cpu().numpy(), ids.cpu().numpy(), w.cpu().numpy(), counts.cpu().numpy()
 
 
-def forward_parity(spec, layer, x, dl, sample=None, what=""):
-    """Whole-layer parity: ids (near-tie rule), counts, w and y against the oracle."""
-    y, ids, w, counts = run_forward(dl, x)
+def forward_parity(spec, layer, x, dl, sample=None, what="", fused=None):
+    """Whole-layer parity: ids (near-tie rule), counts, w and y against the oracle
+    (fused: as run_forward; the oracle takes the same norm weight and residual)."""
+    y, ids, w, counts = run_forward(dl, x, fused=fused)
     if sample is None:
         sample = np.arange(x.shape[0])
     xs = np.ascontiguousarray(x[sample])
-    o = oracle.forward(spec, layer, xs)
-    forced, near = check_ids(spec, layer, xs, ids[sample], o["ids"])
+    norm_w = res = None
+    if fused is not None:
+        norm_w = fused[0]
+        res = None if fused[1] is None else np.ascontiguousarray(fused[1][sample], np.float32)
+    o = oracle.forward(spec, layer, xs, norm_w=norm_w, residual=res)
+    forced, near = check_ids(spec, layer, xs, ids[sample], o["ids"], norm_w)
     if near:
-        o = oracle.forward(spec, layer, xs, forced_ids=forced)
+        o = oracle.forward(spec, layer, xs, forced_ids=forced, norm_w=norm_w, residual=res)
     if len(sample) == x.shape[0]:
         full_forced = forced
         assert np.array_equal(counts, np.bincount(ids.reshape(-1), minlength=spec.num_experts))

@@ -164,6 +164,25 @@ def test_call_refusals_before_any_launch():
     assert L.moe_mxfp4_split(FAKE, -1, 32, FAKE, FAKE, None) == m.MOE_ERR_INVALID
     assert L.moe_mxfp4_split(FAKE, 4, 32, FAKE + 8, FAKE, None) == m.MOE_ERR_INVALID
     assert L.moe_mxfp4_split(None, 0, 32, None, None, None) == m.MOE_OK
+    # fused neighbours: a norm weight needs the pre-norm on; weight and
+    # residual must be 16-byte aligned; NULL for both is moe_forward
+    st = L.moe_forward_fused(p.handle, FAKE, FAKE, None, ctypes.byref(w), 4, FAKE, None, None, None,
+                             FAKE, need, None)
+    assert st == m.MOE_ERR_INVALID and "rms_eps" in m.moe_last_error()
+    pn = _create(rms_eps=1e-6)
+    needn = m.moe_workspace_bytes(pn, 4)
+    assert needn >= need + 4 * 256 * 4
+    st = L.moe_forward_fused(pn.handle, FAKE, FAKE + 8, None, ctypes.byref(w), 4, FAKE, None, None, None,
+                             FAKE, needn, None)
+    assert st == m.MOE_ERR_INVALID and "norm_weight" in m.moe_last_error()
+    st = L.moe_forward_fused(pn.handle, FAKE, FAKE, FAKE + 4, ctypes.byref(w), 4, FAKE, None, None, None,
+                             FAKE, needn, None)
+    assert st == m.MOE_ERR_INVALID and "residual" in m.moe_last_error()
+    st = L.moe_forward_fused(pn.handle, FAKE, FAKE, FAKE, ctypes.byref(w), 4, FAKE, None, None, None,
+                             FAKE, needn - 1, None)
+    assert st == m.MOE_ERR_WORKSPACE
+    assert L.moe_forward_fused(pn.handle, None, None, None, ctypes.byref(w), 0, None, None, None, None,
+                               None, 0, None) == m.MOE_OK
 
 
 def test_forward_path_choice():

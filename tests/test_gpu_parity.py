@@ -407,6 +407,47 @@ def test_forward_timed_matches_forward(M, path, want):
     assert np.array_equal(after, ref)
 
 
+# ------------------------------------------------------- fused neighbours
+FUSED = [
+    # name, layer, token counts, path, norm weight, residual, in place
+    ("single-norm-res", dict(hidden=256, num_experts=8, top_k=2, expert_inter=192, rms_eps=1e-6),
+     (1,), 0, True, True, False),
+    ("gemv-norm-inplace", dict(hidden=288, num_experts=12, top_k=4, expert_inter=320, rms_eps=1e-6,
+                               bias_mode=BIAS_LOGIT, bias_kind="normal", swiglu_limit=7.0,
+                               expert_dtype=Q8_0), (5, 16), 1, True, True, True),
+    ("gemv-shared-norm", dict(hidden=256, num_experts=16, top_k=6, expert_inter=160, shared_inter=320,
+                              select=SOFTMAX_ALL_NORENORM, rms_eps=1e-5), (1, 3, 16), 1, True, False, False),
+    ("mfma-norm-res", dict(hidden=256, num_experts=8, top_k=2, expert_inter=192, rms_eps=1e-6),
+     (64, 130), 2, True, True, False),
+    ("mfma-shared-q8-norm", dict(hidden=192, num_experts=16, top_k=4, expert_inter=128, shared_inter=256,
+                                 expert_dtype=Q8_0, shared_dtype=Q8_0, rms_eps=1e-6, bias_mode=BIAS_LOGIT,
+                                 bias_kind="zipf"), (3, 100), 2, True, True, True),
+    ("f32x-norm-res", dict(hidden=160, num_experts=5, top_k=2, expert_inter=64, x_dtype=F32,
+                           router_dtype=F32, rms_eps=1e-6), (1, 12), 0, True, True, False),
+    ("residual-only", dict(hidden=256, num_experts=8, top_k=2, expert_inter=192), (1, 16, 64), 0,
+     False, True, True),
+    ("mx4-norm-res", dict(hidden=288, num_experts=12, top_k=4, expert_inter=320, rms_eps=1e-6,
+                          expert_dtype=MXFP4), (1, 16), 0, True, True, False),
+]
+
+
+@pytest.mark.parametrize("name,kw,Ms,path,use_norm,use_res,in_place", FUSED, ids=[c[0] for c in FUSED])
+def test_forward_fused(name, kw, Ms, path, use_norm, use_res, in_place):
+    """moe_forward_fused (the post-attention norm with its weight, and the
+    residual add) on each kernel family against the oracle."""
+    spec = synth.small_spec(name=name, seed=1500 + len(name), **kw)
+    layer = synth.make_layer(spec)
+    dl = device_layer(spec, layer, max(Ms), path=path)
+    rng = np.random.default_rng(len(name))
+    gamma = rng.uniform(0.25, 2.0, spec.hidden).astype(np.float32)
+    norm_w = (synth.bf16_bits(gamma) if spec.x_dtype == BF16 else gamma) if use_norm else None
+    for M in Ms:
+        x = synth.make_tokens(spec, M, batch=7)
+        res = rng.standard_normal((M, spec.hidden)).astype(np.float32) if use_res else None
+        say(f"forward fused {name} M={M}")
+        forward_parity(spec, layer, x, dl, what=f"fused {name} M={M}", fused=(norm_w, res, in_place))
+
+
 # ------------------------------------------------------------ full-size layers
 FULL = [("tiny", 4, None), ("gpt-oss-20b", 1, None), ("gpt-oss-20b", 16, None), ("gpt-oss-20b", 64, 8),
         ("deepseek-v2-lite", 1, None), ("deepseek-v2-lite", 16, None),
@@ -435,3 +476,25 @@ def test_forward_full_size(name, M, nsample):
     del dl
     torch.cuda.empty_cache()
     say(f"{name} M={M}: touched experts {int((r['counts'] > 0).sum())}")
+
+
+@pytest.mark.parametrize("name,M,nsample", [("qwen3-30b-a3b", 2048, 16), ("gpt-oss-20b", 1, None),
+                                             ("deepseek-v2-lite", 16, None)],
+                         ids=["qwen3-30b-a3b-M2048", "gpt-oss-20b-M1", "deepseek-v2-lite-M16"])
+def test_forward_fused_full_size(name, M, nsample):
+    """The fused layer at full size: the post-attention norm's weight where the
+    workload has the pre-norm on, and the residual stream updated in place."""
+    say(f"generate {name}")
+    spec, layer = host_layer(name)
+    dl = device_layer(spec, layer, M)
+    rng = np.random.default_rng(M + 3)
+    norm_w = synth.bf16_bits(rng.uniform(0.25, 2.0, spec.hidden).astype(np.float32)) if spec.rms_eps > 0 else None
+    x = synth.make_tokens(spec, M, batch=11)
+    res = rng.standard_normal((M, spec.hidden)).astype(np.float32)
+    sample = None
+    if nsample:
+        sample = np.sort(rng.choice(M, size=nsample, replace=False))
+    say(f"forward fused {name} M={M}")
+    forward_parity(spec, layer, x, dl, sample=sample, what=f"fused {name} M={M}", fused=(norm_w, res, True))
+    del dl
+    torch.cuda.empty_cache()
