@@ -839,11 +839,13 @@ hipError_t launch_down_mfma(const Layer &L, const float *act, const float *share
 // kRtWaves waves split the 32-element K steps into contiguous ranges; each
 // wave loads kRtUnroll steps of both operands from global (L2) straight into
 // registers before using them.  The waves' partial tiles meet in LDS and are
-// summed in wave order.
+// summed in wave order.  XS: x rows are split bf16 hi/lo pairs (the fused
+// layer's normed rows), and each step runs one MFMA per half.
 typedef float f32x4m __attribute__((ext_vector_type(4)));
 constexpr int kRtWaves = 8;
 constexpr int kRtUnroll = 8;
 
+template <bool XS>
 __global__ __launch_bounds__(kRtWaves * kWave) void k_router_mfma16(const uint16_t *x, const uint16_t *router,
                                                                    const float *tok_scale, int M, int E, int K,
                                                                    float *logits) {
@@ -853,23 +855,34 @@ __global__ __launch_bounds__(kRtWaves * kWave) void k_router_mfma16(const uint16
     const int tm = blockIdx.x / ntE, te = blockIdx.x % ntE;
     const int t = min(tm * 16 + (lane & 15), M - 1);
     const int e = min(te * 16 + (lane & 15), E - 1);
-    const uint16_t *arow = x + (size_t)t * K + 8 * (lane >> 4);
+    // split rows: per 8 elements 8 hi then 8 lo values, so element k sits at
+    // 2k (hi) and 2k + 8 (lo) for k a multiple of 8
+    const uint16_t *arow = XS ? x + (size_t)t * K * 2 + 16 * (lane >> 4) : x + (size_t)t * K + 8 * (lane >> 4);
     const uint16_t *brow = router + (size_t)e * K + 8 * (lane >> 4);
     const int NS = K / 32, s0 = wave * NS / kRtWaves, s1 = (wave + 1) * NS / kRtWaves;
     f32x4m acc = {0.f, 0.f, 0.f, 0.f};
     for (int sb = s0; sb < s1; sb += kRtUnroll) {
-        u32x4 av[kRtUnroll], bv[kRtUnroll];
+        u32x4 av[kRtUnroll], al[kRtUnroll], bv[kRtUnroll];
 #pragma unroll
         for (int u = 0; u < kRtUnroll; u++) {
             const int k = 32 * min(sb + u, s1 - 1);
-            av[u] = *reinterpret_cast<const u32x4 *>(arow + k);
+            if constexpr (XS) {
+                av[u] = *reinterpret_cast<const u32x4 *>(arow + 2 * k);
+                al[u] = *reinterpret_cast<const u32x4 *>(arow + 2 * k + 8);
+            } else {
+                av[u] = *reinterpret_cast<const u32x4 *>(arow + k);
+            }
             bv[u] = *reinterpret_cast<const u32x4 *>(brow + k);
         }
 #pragma unroll
         for (int u = 0; u < kRtUnroll; u++)
-            if (sb + u < s1)
+            if (sb + u < s1) {
                 acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av[u]),
                                                               __builtin_bit_cast(bf16x8, bv[u]), acc, 0, 0, 0);
+                if constexpr (XS)
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, al[u]),
+                                                                  __builtin_bit_cast(bf16x8, bv[u]), acc, 0, 0, 0);
+            }
     }
     s_part[wave][lane] = acc;
     __syncthreads();
@@ -886,12 +899,17 @@ __global__ __launch_bounds__(kRtWaves * kWave) void k_router_mfma16(const uint16
 }
 
 hipError_t launch_router_mfma(const Layer &L, const void *x, const void *router, const float *tok_scale,
-                              int M, float *logits, hipStream_t s) {
+                              int M, float *logits, hipStream_t s, bool x_split) {
     if (L.H % 32) return hipErrorInvalidValue;
     const int tiles = ((M + 15) / 16) * ((L.E + 15) / 16);
-    launch_kernel(k_router_mfma16, dim3(tiles), dim3(kRtWaves * kWave), 0, s,
-                  static_cast<const uint16_t *>(x), static_cast<const uint16_t *>(router), tok_scale, M,
-                  L.E, L.H, logits);
+    if (x_split)
+        launch_kernel(k_router_mfma16<true>, dim3(tiles), dim3(kRtWaves * kWave), 0, s,
+                      static_cast<const uint16_t *>(x), static_cast<const uint16_t *>(router), tok_scale, M,
+                      L.E, L.H, logits);
+    else
+        launch_kernel(k_router_mfma16<false>, dim3(tiles), dim3(kRtWaves * kWave), 0, s,
+                      static_cast<const uint16_t *>(x), static_cast<const uint16_t *>(router), tok_scale, M,
+                      L.E, L.H, logits);
     return hipGetLastError();
 }
 

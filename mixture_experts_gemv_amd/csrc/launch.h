@@ -94,7 +94,7 @@ int mfma_tile_rows();                          // tiles of the stage-wise entry 
 int mfma_tile_rows(const Layer &L, int M);     // tiles of the layer call for M tokens
 bool mfma_supported(const Layer &L);
 hipError_t launch_router_mfma(const Layer &L, const void *x, const void *router, const float *tok_scale,
-                              int M, float *logits, hipStream_t s);
+                              int M, float *logits, hipStream_t s, bool x_split = false);
 // x_split: x rows are split bf16 hi/lo pairs (launch_norm_apply's xs) rather than bf16.
 hipError_t launch_gateup_mfma(const Layer &L, const void *x, const float *tok_scale, const Mats &routed,
                               const Mats &shared, const Routing &rt, int M, int max_tiles, int tile_rows,

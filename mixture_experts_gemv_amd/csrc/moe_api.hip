@@ -468,8 +468,10 @@ static moe_status forward_impl(const moe_plan *p, const void *x, const moe_weigh
                                            sorted, rpos, active, s),
               "route", MOE_STAGE_ROUTER);
     } else {
-        if (mfma && L.rdt == moe::DT_BF16 && L.xdt == moe::DT_BF16)
-            STAGE(rec, moe::launch_router_mfma(L, x, wts->router, sc, M, lg, s), "router (MFMA)", MOE_STAGE_ROUTER);
+        if (mfma && L.rdt == moe::DT_BF16 && (L.xdt == moe::DT_BF16 || xsplit))
+            STAGE(rec, moe::launch_router_mfma(L, xsplit ? (const void *)xsplit : x, wts->router, sc, M, lg, s,
+                                               xsplit != nullptr),
+                  "router (MFMA)", MOE_STAGE_ROUTER);
         else
             STAGE(rec, moe::launch_router(L, x, wts->router, sc, M, lg, s), "router", MOE_STAGE_ROUTER);
         STAGE(rec, moe::launch_topk(L, lg, wts->bias, M, ids, w, s), "top-k", MOE_STAGE_TOPK);

@@ -20,6 +20,8 @@ W_ABS = 1e-5
 # Near-tie bound: a GPU logit in fp32 differs from the exact one by at most
 # TAU_REL * sum_i |x_i * w_i| (+|b|) for the summation orders used here.
 TAU_REL = 2.0 ** -17
+# Relative error of a value carried as bf16 hi plus bf16 lo (lo rounds v - hi).
+SPLIT_REL = 2.0 ** -18
 # Sigmoid scoring: the fp32 sigmoid of a logit and the add of the correction
 # bias are each within a few units of 2^-24 of the exact values.
 SIGMOID_TAU = 2.0 ** -20
@@ -62,6 +64,10 @@ def selection_keys(spec, layer, x, norm_w=None):
     b = np.zeros(spec.num_experts) if layer.get("bias") is None else layer["bias"].astype(np.float64)
     A = np.abs(xf) @ np.abs(wr).T + (np.abs(b) if spec.bias_mode != 0 else 0.0)
     tau = TAU_REL * A.max(axis=1)
+    if norm_w is not None:
+        # the weighted normed rows reach the grouped-GEMM router as bf16 hi + lo,
+        # which holds each value to 2^-18 of itself: that adds 2^-18 * A
+        tau = tau + SPLIT_REL * A.max(axis=1)
     if spec.select == SIGMOID_NORM:
         # key sigmoid(l) + b: sigmoid' <= 1/4 carries the logit bound over, and
         # the fp32 sigmoid and add are covered by SIGMOID_TAU
