@@ -141,6 +141,8 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches only")
+    ap.add_argument("--path", choices=("auto", "gemv", "mfma"), default="auto",
+                    help="kernel family: the plan's choice (default) or forced")
     ap.add_argument("--fused", action="store_true",
                     help="time moe_forward_fused: the pre-norm's weight (when the workload has the "
                          "pre-norm) and the residual stream updated in place")
@@ -180,7 +182,8 @@ def main() -> int:
               expert_inter=spec.expert_inter, shared_inter=spec.shared_inter, select=spec.select,
               bias_mode=spec.bias_mode, swiglu_limit=spec.swiglu_limit, rms_eps=spec.rms_eps,
               x_dtype=spec.x_dtype, router_dtype=spec.router_dtype, expert_dtype=spec.expert_dtype,
-              shared_dtype=spec.shared_dtype, max_tokens=M, device=dev)
+              shared_dtype=spec.shared_dtype, max_tokens=M, device=dev,
+              path={"auto": m.MOE_PATH_AUTO, "gemv": m.MOE_PATH_GEMV, "mfma": m.MOE_PATH_MFMA}[args.path])
     base = MoeLayer(**kw).load(host["router"], host["bias"], host["gate"], host["up"], host["down"],
                                host.get("shared_gate"), host.get("shared_up"), host.get("shared_down"))
     # estimate touched bytes with a realised call, then size the rotation

@@ -44,7 +44,7 @@
  *    elements along the reduction dimension (gate_scale [E][I][H/32]).  Value
  *    = 2^(scale - 127) * element.  moe_mxfp4_split converts 17-byte blocks
  *    into them.  Code planes must be 16-byte aligned; scale planes may have
- *    any alignment.  MXFP4 layers run on the GEMV kernels at every M.
+ *    any alignment.
  *  - Routes: route r = t*top_k + j is slot j of token t.  "Sorted position" p
  *    is the route's index in expert-major order (experts ascending, routes
  *    ascending inside an expert), as produced by moe_permute.
@@ -101,7 +101,7 @@ typedef enum {
 typedef enum {
     MOE_PATH_AUTO = 0, /* GEMV kernels for small batches, MFMA grouped GEMM for large */
     MOE_PATH_GEMV = 1, /* always the bandwidth-bound GEMV kernels */
-    MOE_PATH_MFMA = 2  /* always the MFMA grouped GEMM (bf16 x; bf16 or Q8_0 experts, not MXFP4;
+    MOE_PATH_MFMA = 2  /* always the MFMA grouped GEMM (bf16 x; bf16, Q8_0 or MXFP4 experts;
                           H, I and Is multiples of 64) */
 } moe_path;
 

@@ -138,9 +138,13 @@ __device__ __forceinline__ size_t split_pos(int i) { return (size_t)(i >> 3) * 1
 // XOR swizzle of a 16-byte chunk within an LDS row of CH chunks: rows of 8
 // chunks (128 B) xor with row % 8; rows of 4 chunks (64 B, two rows per 128
 // bytes of banks) xor with (row / 2) % 4.  Either way the 8 rows one
-// ds_read_b128 phase touches land on 8 different 16-byte bank groups.
+// ds_read_b128 phase touches land on 8 different 16-byte bank groups.  Rows
+// of 2 chunks (MXFP4 columns, read 4 bytes at a time) xor with (row / 8) % 2,
+// which halves the conflicts of rows 8 apart.
 template <int CH>
-__device__ __forceinline__ int swz(int row) { return CH >= 8 ? (row & 7) : ((row >> 1) & 3); }
+__device__ __forceinline__ int swz(int row) {
+    return CH >= 8 ? (row & 7) : (CH == 4 ? ((row >> 1) & 3) : ((row >> 3) & 1));
+}
 
 // 8- and 4-byte LDS reads, issued like lds_load16 (the caller waits).
 __device__ __forceinline__ u32x2 lds_load8(const unsigned char *p) {
@@ -177,25 +181,33 @@ __device__ __forceinline__ u32x4 q8x8_to_bf16(u32x2 w) {
     return o;
 }
 
-// BQ: B is Q8_0 (int8 plane plus fp16 scales per 32 reduction elements).
-// Its stages span 64 reduction elements (two scale blocks; the int8 columns
-// take half the LDS of bf16 ones), and a 4-byte copy per lane brings each
-// column's two scales along.  Each block's products are accumulated by the
-// MFMAs separately and added to the accumulator times the column's scale.
-// (Stages of 128 elements with 32-row tiles measured no faster.)
-template <int KIND, bool AS, int MB, bool BQ>
+// BF (B format): 0 = bf16; 1 = Q8_0 (int8 plane plus fp16 scales per 32
+// reduction elements); 2 = MXFP4 (E2M1 codes, two a byte, plus an E8M0 scale
+// per 32 reduction elements).  Block-scaled stages span 64 reduction elements
+// (two scale blocks; int8 columns take half the LDS of bf16 ones, MXFP4
+// columns a quarter).  Q8_0: a 4-byte copy per lane brings each column's two
+// scales along.  MXFP4: each lane loads its columns' two scale bytes into
+// registers with the stage's copies (their rows are only 2-byte aligned).
+// Each block's products are accumulated by the MFMAs separately and added to
+// the accumulator times the column's scale.  (Stages of 128 elements with
+// 32-row tiles measured no faster for Q8_0.)
+template <int KIND, bool AS, int MB, int BF>
 __global__ __launch_bounds__(kGThreads, 1) void k_gemm_lds(GemmArgs a) {
+    constexpr bool BQ = BF == 1;                   // Q8_0 B
+    constexpr bool BX = BF == 2;                   // MXFP4 B
+    constexpr bool BS = BQ || BX;                  // block-scaled B
     constexpr int BM = 32 * MB;                    // rows per tile
     constexpr int NB = GemmShape<KIND>::NB;
     constexpr int WCOLS = GemmShape<KIND>::WCOLS;
     constexpr int AP = AS ? 2 : 1;                 // bf16 values of A per element (split: hi, lo)
-    constexpr int EB = BQ ? 1 : 2;                 // bytes per B element
-    constexpr int BK = BQ ? kStageK : kStageK / AP; // reduction elements per stage
-    constexpr int NBLK = BK / 32;                  // Q8_0 scale blocks per stage
+    constexpr int EB = BQ ? 1 : 2;                 // bytes per B element (bf16, Q8_0)
+    constexpr int BK = BS ? kStageK : kStageK / AP; // reduction elements per stage
+    constexpr int NBLK = BK / 32;                  // scale blocks per stage
     constexpr int SCP = BQ ? NBLK / 2 : 0;         // 4-byte scale copies per lane per stage
+    constexpr int SRG = BX ? NB : 0;               // MXFP4 scale loads per lane per stage
     constexpr int NST = kStages;                   // LDS stages
     constexpr int ARB = BK * 2 * AP;               // A bytes per row per stage
-    constexpr int BRB = BK * EB;                   // B bytes per column per stage
+    constexpr int BRB = BX ? BK / 2 : BK * EB;     // B bytes per column per stage
     constexpr int ACH = ARB / 16;                  // 16-byte chunks per A row per stage
     constexpr int BCH = BRB / 16;                  // 16-byte chunks per B column per stage
     constexpr int WBC = 64;                        // B columns per wave (gate/up: 32 gate + 32 up)
@@ -205,8 +217,9 @@ __global__ __launch_bounds__(kGThreads, 1) void k_gemm_lds(GemmArgs a) {
     constexpr int ST_BYTES = A_BYTES + kGW * WB_BYTES + kGW * WS_BYTES;
     constexpr int A_DMA = BM * ARB / (kWave * 16) / kGW; // A copies per wave per stage (each 1 KB)
     constexpr int B_DMA = WB_BYTES / (kWave * 16);        // B copies per wave per stage
-    constexpr int LPS = A_DMA + B_DMA + SCP;       // copies per lane per stage
+    constexpr int LPS = A_DMA + B_DMA + SCP + SRG; // vector memory operations per lane per stage
     static_assert(!BQ || NBLK % 2 == 0, "Q8_0 scales are copied in pairs of blocks");
+    static_assert(!BX || NBLK == 2, "MXFP4 stages hold two scale blocks (one 2-byte load per column)");
     // one LDS array per stage, named explicitly in an NST-way unrolled loop
     // (measured faster than one array indexed by kt % NST)
     __shared__ __attribute__((aligned(16))) unsigned char sm0[ST_BYTES], sm1[ST_BYTES], sm2[ST_BYTES];
@@ -286,8 +299,8 @@ __global__ __launch_bounds__(kGThreads, 1) void k_gemm_lds(GemmArgs a) {
         const int cl = q * (kWave / BCH) + lane / BCH, c = (lane % BCH) ^ swz<BCH>(cl);
         const uint16_t *mat = (KIND == GK_GATEUP && cl >= 32) ? a.b1 : a.b0;
         const int col = KIND == GK_GATEUP ? colw + (cl & 31) : colw + cl;
-        bsrc[q] = reinterpret_cast<const char *>(mat) + ((size_t)e * a.b_stride + (size_t)min(col, N - 1) * K) * EB +
-                  c * 16;
+        const size_t el = (size_t)e * a.b_stride + (size_t)min(col, N - 1) * K; // first element of the column
+        bsrc[q] = reinterpret_cast<const char *>(mat) + (BX ? el / 2 : el * EB) + c * 16;
     }
     // Q8_0: lane i copies the two scales of column i of the wave's 64
     const char *ssrc = nullptr;
@@ -296,9 +309,19 @@ __global__ __launch_bounds__(kGThreads, 1) void k_gemm_lds(GemmArgs a) {
         const int col = KIND == GK_GATEUP ? colw + (lane & 31) : colw + lane;
         ssrc = reinterpret_cast<const char *>(sm + a.s_stride * e + (size_t)min(col, N - 1) * (K / 32));
     }
-    auto issue = [&](int kt, unsigned char *st) {
+    // MXFP4: the scale bytes of the lane's column in each 32-column block nb
+    const uint8_t *xsrc[NB > 0 ? NB : 1];
+    if constexpr (BX) {
+#pragma unroll
+        for (int nb = 0; nb < NB; nb++) {
+            const uint8_t *sm = reinterpret_cast<const uint8_t *>((KIND == GK_GATEUP && nb == 1) ? a.s1 : a.s0);
+            const int col = KIND == GK_GATEUP ? colw + (lane & 31) : colw + nb * 32 + (lane & 31);
+            xsrc[nb] = sm + a.s_stride * e + (size_t)min(col, N - 1) * (K / 32);
+        }
+    }
+    auto issue = [&](int kt, unsigned char *st, uint32_t (&xs)[NB]) {
         const int k0 = (kb + kt) * BK; // first reduction element of stage kt
-        const size_t ka = (size_t)k0 * 2 * AP, kbb = (size_t)k0 * EB;
+        const size_t ka = (size_t)k0 * 2 * AP, kbb = BX ? (size_t)k0 / 2 : (size_t)k0 * EB;
 #pragma unroll
         for (int q = 0; q < A_DMA; q++)
             copy16_lds(asrc[q] + ka, st + (wave * A_DMA + q) * 1024);
@@ -310,6 +333,10 @@ __global__ __launch_bounds__(kGThreads, 1) void k_gemm_lds(GemmArgs a) {
             for (int j = 0; j < SCP; j++)
                 copy4_lds(ssrc + (size_t)(k0 / 32) * 2 + 4 * j,
                           st + A_BYTES + kGW * WB_BYTES + wave * WS_BYTES + j * (kWave * 4));
+        if constexpr (BX)
+#pragma unroll
+            for (int nb = 0; nb < NB; nb++)
+                xs[nb] = *reinterpret_cast<const uint16_t *>(xsrc[nb] + k0 / 32);
     };
 
     f32x16 acc[MB][NB];
@@ -320,9 +347,65 @@ __global__ __launch_bounds__(kGThreads, 1) void k_gemm_lds(GemmArgs a) {
 #pragma unroll
             for (int r = 0; r < 16; r++) acc[mb][nb][r] = 0.f;
 
-    auto compute = [&](const unsigned char *st) {
+    auto compute = [&](const unsigned char *st, uint32_t (&xs)[NB]) {
         const unsigned char *bw = st + A_BYTES + wave * WB_BYTES;
-        if constexpr (!BQ) {
+        if constexpr (BX) {
+            // column bytes of substep s: chunk s/2, bytes 8 (s%2) + 4 (l/32) .. +3
+            // (the codes of elements 16s + 8 (l/32) .. +7); A as below
+#pragma unroll
+            for (int bl = 0; bl < NBLK; bl++) {
+                f32x16 blk[MB][NB];
+#pragma unroll
+                for (int s = 2 * bl; s < 2 * bl + 2; s++) {
+                    const int g8 = 2 * s + (lane >> 5);
+                    uint32_t q[NB];
+                    u32x4 v[AP * MB];
+#pragma unroll
+                    for (int nb = 0; nb < NB; nb++) {
+                        const int cl = nb * 32 + (lane & 31);
+                        q[nb] = lds_load4(bw + cl * BRB + (((s >> 1) ^ swz<BCH>(cl)) * 16) + 8 * (s & 1) +
+                                          4 * (lane >> 5));
+                    }
+#pragma unroll
+                    for (int mb = 0; mb < MB; mb++) {
+                        const int r = mb * 32 + (lane & 31);
+#pragma unroll
+                        for (int h = 0; h < AP; h++)
+                            v[AP * mb + h] = lds_load16(st + r * ARB + (((AP * g8 + h) ^ swz<ACH>(r)) * 16));
+                    }
+                    asm volatile("s_waitcnt lgkmcnt(0)");
+#pragma unroll
+                    for (int nb = 0; nb < NB; nb++) lds_keep(q[nb]);
+#pragma unroll
+                    for (int i = 0; i < AP * MB; i++) lds_keep(v[i]);
+#pragma unroll
+                    for (int nb = 0; nb < NB; nb++) {
+                        u32x4 bv;
+                        bv.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q[nb], 1.0f, 0));
+                        bv.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q[nb], 1.0f, 1));
+                        bv.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q[nb], 1.0f, 2));
+                        bv.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q[nb], 1.0f, 3));
+#pragma unroll
+                        for (int mb = 0; mb < MB; mb++)
+#pragma unroll
+                            for (int h = 0; h < AP; h++) {
+                                const f32x16 c = (s == 2 * bl && h == 0) ? f32x16{} : blk[mb][nb];
+                                blk[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                                    __builtin_bit_cast(bf16x8, v[AP * mb + h]), __builtin_bit_cast(bf16x8, bv), c,
+                                    0, 0, 0);
+                            }
+                    }
+                }
+#pragma unroll
+                for (int nb = 0; nb < NB; nb++) {
+                    const float sc = e8m0_to_f32((xs[nb] >> (8 * bl)) & 255u);
+#pragma unroll
+                    for (int mb = 0; mb < MB; mb++)
+#pragma unroll
+                        for (int r = 0; r < 16; r++) acc[mb][nb][r] = fmaf(sc, blk[mb][nb][r], acc[mb][nb][r]);
+                }
+            }
+        } else if constexpr (!BQ) {
 #pragma unroll
             for (int s = 0; s < BK / 16; s++) {
                 // every read of the substep first, one wait, then the MFMAs.
@@ -426,22 +509,28 @@ __global__ __launch_bounds__(kGThreads, 1) void k_gemm_lds(GemmArgs a) {
     // waits (vmcnt) until its copies of stage kt have landed, then the
     // workgroup barrier makes every lane's copies visible.
     // stage kt lives in buffer kt % NST
-    auto step = [&](int kt, const unsigned char *cur, unsigned char *nxt) {
+    // (MXFP4: the scale registers of stage kt are xr[kt % NST], loaded by its
+    // issue and covered by the same vmcnt wait as its copies)
+    uint32_t xr0[NB], xr1[NB], xr2[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; nb++) xr0[nb] = xr1[nb] = xr2[nb] = 0u;
+    auto step = [&](int kt, const unsigned char *cur, unsigned char *nxt, uint32_t (&xc)[NB],
+                    uint32_t (&xn)[NB]) {
         const int ahead = min(nk, kt + NST - 1) - (kt + 1); // stages issued after kt
         if (ahead >= 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * LPS));
         else if (ahead == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(LPS));
         else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
         __builtin_amdgcn_s_barrier();
-        if (kt + NST - 1 < nk) issue(kt + NST - 1, nxt);
-        if (wave_on) compute(cur);
+        if (kt + NST - 1 < nk) issue(kt + NST - 1, nxt, xn);
+        if (wave_on) compute(cur, xc);
     };
-    if (nk > 0) issue(0, sm0);
-    if (nk > 1) issue(1, sm1);
+    if (nk > 0) issue(0, sm0, xr0);
+    if (nk > 1) issue(1, sm1, xr1);
     static_assert(NST == 3, "the unrolled loop below names three stage buffers");
     for (int k0 = 0; k0 < nk; k0 += 3) {
-        step(k0, sm0, sm2);
-        if (k0 + 1 < nk) step(k0 + 1, sm1, sm0);
-        if (k0 + 2 < nk) step(k0 + 2, sm2, sm1);
+        step(k0, sm0, sm2, xr0, xr2);
+        if (k0 + 1 < nk) step(k0 + 1, sm1, sm0, xr1, xr0);
+        if (k0 + 2 < nk) step(k0 + 2, sm2, sm1, xr2, xr1);
     }
     if (!wave_on) return;
 
@@ -683,19 +772,25 @@ __global__ __launch_bounds__(kGThreads, 2) void k_gemm_reg(GemmArgs a) {
 }
 
 // a_mode: 0 = bf16 A rows (gate/up), 1 = split A rows (hi/lo pairs: act of down, or the fused
-// layer's normed x of gate/up), 2 = fp32 A rows (down).  bq: B is Q8_0 (a.s0 / a.s1 hold its scales); not with fp32 A.
-template <int KIND, bool AS>
-static void launch_lds(const GemmArgs &a, bool bq, unsigned grid, hipStream_t s) {
-    if (a.tile_rows == 32) {
-        if (bq) launch_kernel((k_gemm_lds<KIND, AS, 1, true>), dim3(grid), dim3(kGThreads), 0, s, a);
-        else launch_kernel((k_gemm_lds<KIND, AS, 1, false>), dim3(grid), dim3(kGThreads), 0, s, a);
-    } else {
-        if (bq) launch_kernel((k_gemm_lds<KIND, AS, kMB, true>), dim3(grid), dim3(kGThreads), 0, s, a);
-        else launch_kernel((k_gemm_lds<KIND, AS, kMB, false>), dim3(grid), dim3(kGThreads), 0, s, a);
-    }
+// layer's normed x of gate/up), 2 = fp32 A rows (down).  bq: B format (0 bf16,
+// 1 Q8_0, 2 MXFP4; a.s0 / a.s1 hold the block scales); fp32 A takes bf16 B only.
+template <int KIND, bool AS, int MB>
+static void launch_lds_b(const GemmArgs &a, int bf, unsigned grid, hipStream_t s) {
+    if (bf == 1) launch_kernel((k_gemm_lds<KIND, AS, MB, 1>), dim3(grid), dim3(kGThreads), 0, s, a);
+    else if (bf == 2) launch_kernel((k_gemm_lds<KIND, AS, MB, 2>), dim3(grid), dim3(kGThreads), 0, s, a);
+    else launch_kernel((k_gemm_lds<KIND, AS, MB, 0>), dim3(grid), dim3(kGThreads), 0, s, a);
 }
 
-static hipError_t run_gemm(int kind, int a_mode, bool bq, GemmArgs &a, hipStream_t s) {
+template <int KIND, bool AS>
+static void launch_lds(const GemmArgs &a, int bf, unsigned grid, hipStream_t s) {
+    if (a.tile_rows == 32) launch_lds_b<KIND, AS, 1>(a, bf, grid, s);
+    else launch_lds_b<KIND, AS, kMB>(a, bf, grid, s);
+}
+
+// B format of a weight dtype: 0 bf16, 1 Q8_0, 2 MXFP4.
+static int b_format(int dt) { return dt == DT_Q8 ? 1 : (dt == DT_MX4 ? 2 : 0); }
+
+static hipError_t run_gemm(int kind, int a_mode, int bq, GemmArgs &a, hipStream_t s) {
     const int cols = kind == GK_GATEUP ? GemmShape<GK_GATEUP>::COLS : GemmShape<GK_PLAIN>::COLS;
     a.n_ntiles = (a.N + cols - 1) / cols;
     if (a.ksplit < 1) a.ksplit = 1;
@@ -719,7 +814,7 @@ static hipError_t run_gemm(int kind, int a_mode, bool bq, GemmArgs &a, hipStream
 }
 
 bool mfma_supported(const Layer &L) {
-    const auto ok = [](int dt) { return dt == DT_BF16 || dt == DT_Q8; };
+    const auto ok = [](int dt) { return dt == DT_BF16 || dt == DT_Q8 || dt == DT_MX4; };
     return L.xdt == DT_BF16 && ok(L.edt) && (L.Is == 0 || ok(L.sdt)) && L.H % kBK == 0 && L.I % kBK == 0 &&
            L.Is % kBK == 0;
 }
@@ -766,7 +861,7 @@ hipError_t launch_gateup_mfma(const Layer &L, const void *x, const float *tok_sc
         a.out = act;
         a.ldo = L.I;
         a.out_split = act_split;
-        hipError_t err = run_gemm(GK_GATEUP, a_mode, L.edt == DT_Q8, a, s);
+        hipError_t err = run_gemm(GK_GATEUP, a_mode, b_format(L.edt), a, s);
         if (err != hipSuccess) return err;
     }
     if (shared_act && L.Is > 0) {
@@ -786,7 +881,7 @@ hipError_t launch_gateup_mfma(const Layer &L, const void *x, const float *tok_sc
         a.out = shared_act;
         a.ldo = L.Is;
         a.out_split = act_split;
-        return run_gemm(GK_GATEUP, a_mode, L.sdt == DT_Q8, a, s);
+        return run_gemm(GK_GATEUP, a_mode, b_format(L.sdt), a, s);
     }
     return hipSuccess;
 }
@@ -813,7 +908,7 @@ hipError_t launch_down_mfma(const Layer &L, const float *act, const float *share
         a.K = L.I;
         a.out = y_routes;
         a.ldo = L.H;
-        hipError_t err = run_gemm(GK_PLAIN, act_split ? 1 : 2, L.edt == DT_Q8, a, s);
+        hipError_t err = run_gemm(GK_PLAIN, act_split ? 1 : 2, b_format(L.edt), a, s);
         if (err != hipSuccess) return err;
     }
     if (shared_act && L.Is > 0) {
@@ -828,7 +923,7 @@ hipError_t launch_down_mfma(const Layer &L, const float *act, const float *share
         a.K = L.Is;
         a.out = y_shared;
         a.ldo = L.H;
-        return run_gemm(GK_PLAIN, act_split ? 1 : 2, L.sdt == DT_Q8, a, s);
+        return run_gemm(GK_PLAIN, act_split ? 1 : 2, b_format(L.sdt), a, s);
     }
     return hipSuccess;
 }

@@ -52,12 +52,12 @@ bool use_mfma(const moe_plan *p, int M) {
     if (!p->mfma_capable) return false;
     if (p->cfg.path == MOE_PATH_MFMA) return true;
     if (p->cfg.path == MOE_PATH_GEMV) return false;
-    // From about two routes per expert on (four with Q8_0 experts, whose
-    // int8 conversion and block scales cost the grouped GEMM more), the
+    // From about two routes per expert on (four with Q8_0 or MXFP4 experts,
+    // whose conversion and block scales cost the grouped GEMM more), the
     // grouped GEMM (32-row tiles at small batches) beats the per-row kernels,
     // whose dot-product work grows with the tokens each expert sees.
     const long routes = (long)M * p->L.k;
-    const long per_expert = p->L.edt == moe::DT_Q8 ? 4 : 2;
+    const long per_expert = p->L.edt == moe::DT_Q8 || p->L.edt == moe::DT_MX4 ? 4 : 2;
     return M >= 8 && routes >= per_expert * p->L.E;
 }
 
@@ -86,10 +86,10 @@ WsLayout layout(const moe_plan *p, int M) {
     w.act = take(R * L.I * 4);
     w.shared_act = take(L.Is > 0 ? (size_t)M * L.Is * 4 : 0);
     // (fewer tile rows never give more reduction slices; moe_combine with
-    // Q8_0 experts uses the row kernels' slices even when the layer call
-    // takes the grouped GEMM)
+    // Q8_0 or MXFP4 experts uses the row kernels' slices even when the layer
+    // call takes the grouped GEMM)
     const size_t slices = mfma ? std::max(moe::down_ksplit(L, M, moe::mfma_tile_rows()),
-                                          L.edt == moe::DT_Q8 ? moe::down_gemv_slices(L.I) : 1)
+                                          L.edt != moe::DT_BF16 ? moe::down_gemv_slices(L.I) : 1)
                                : moe::down_gemv_slices(L.I);
     w.y_routes = take(slices * R * L.H * 4);
     w.y_shared = take(L.Is > 0 ? (size_t)(mfma ? 1 : moe::down_gemv_slices(L.Is)) * M * L.H * 4 : 0);
@@ -236,8 +236,8 @@ moe_status moe_plan_create(const moe_config *c, moe_plan **out) {
     const bool mfma_ok = moe::mfma_supported(L);
     if (c->path == MOE_PATH_MFMA && !mfma_ok)
         return fail(MOE_ERR_UNSUPPORTED,
-                    "the MFMA path needs bf16 x, bf16 or Q8_0 experts (MXFP4 experts run on the GEMV "
-                    "kernels) and hidden, expert_inter, shared_inter multiples of 64");
+                    "the MFMA path needs bf16 x, bf16, Q8_0 or MXFP4 experts and hidden, expert_inter, "
+                    "shared_inter multiples of 64");
     moe_plan *p = new moe_plan;
     p->cfg = *c;
     p->L = L;

@@ -75,7 +75,7 @@ def _create(**kw):
     (dict(x_dtype=m.MOE_MXFP4), m.MOE_ERR_UNSUPPORTED),
     (dict(router_dtype=m.MOE_MXFP4), m.MOE_ERR_UNSUPPORTED),
     (dict(shared_inter=64, expert_dtype=m.MOE_MXFP4, shared_dtype=m.MOE_Q8_0), m.MOE_ERR_UNSUPPORTED),
-    (dict(path=m.MOE_PATH_MFMA, expert_dtype=m.MOE_MXFP4), m.MOE_ERR_UNSUPPORTED),
+    (dict(path=m.MOE_PATH_MFMA, expert_dtype=m.MOE_MXFP4, hidden=288), m.MOE_ERR_UNSUPPORTED),
 ])
 def test_plan_refusals(kw, status):
     with pytest.raises(m.MoeError) as ei:

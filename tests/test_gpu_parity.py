@@ -283,6 +283,11 @@ MFMA_SMALL = [
                                   bias_kind="normal", swiglu_limit=0.5), (3, 33, 100)),
     ("sigmoid-e64", dict(hidden=256, num_experts=64, top_k=8, expert_inter=128, select=SIGMOID_NORM,
                          bias_mode=BIAS_SELECT_ONLY, bias_kind="normal", bias_std=0.05), (1, 70)),
+    ("mx4", dict(hidden=256, num_experts=8, top_k=2, expert_inter=192, expert_dtype=MXFP4), (16, 70, 200)),
+    ("mx4-shared-bias-clamp", dict(hidden=192, num_experts=16, top_k=4, expert_inter=128, shared_inter=256,
+                                   expert_dtype=MXFP4, shared_dtype=MXFP4, bias_mode=BIAS_LOGIT,
+                                   bias_kind="normal", swiglu_limit=0.5), (3, 33, 100)),
+    ("mx4-wide", dict(hidden=576, num_experts=4, top_k=1, expert_inter=704, expert_dtype=MXFP4), (129,)),
 ]
 
 
@@ -300,7 +305,7 @@ def test_forward_mfma_small(name, kw, Ms):
         forward_parity(spec, layer, x, dl, what=f"mfma {name} M={M}")
 
 
-@pytest.mark.parametrize("wdt", [BF16, Q8_0], ids=["bf16", "q8"])
+@pytest.mark.parametrize("wdt", [BF16, Q8_0, MXFP4], ids=["bf16", "q8", "mx4"])
 def test_stages_mfma(wdt):
     """moe_expert_ffn and moe_combine on the MFMA path equal the oracle (with
     Q8_0 experts moe_combine's fp32 act takes the row kernels)."""
@@ -455,7 +460,8 @@ FULL = [("tiny", 4, None), ("gpt-oss-20b", 1, None), ("gpt-oss-20b", 16, None), 
         ("mixtral-8x7b", 512, 12), ("qwen3-30b-a3b", 2048, 24),
         ("deepseek-v2-lite-dense", 1, None), ("deepseek-v2-lite-dense", 16, None),
         ("deepseek-v2-lite-dense", 512, 8), ("sigmoid-e256", 1, None), ("sigmoid-e256", 16, None),
-        ("gpt-oss-20b-mxfp4", 1, None), ("gpt-oss-20b-mxfp4", 16, None), ("gpt-oss-20b-mxfp4", 64, 8)]
+        ("gpt-oss-20b-mxfp4", 1, None), ("gpt-oss-20b-mxfp4", 16, None), ("gpt-oss-20b-mxfp4", 64, 8),
+        ("gpt-oss-20b-mxfp4", 256, 8)]
 
 
 @pytest.mark.parametrize("name,M,nsample", FULL, ids=[f"{n}-M{m}" for n, m, _ in FULL])
