@@ -711,25 +711,42 @@ __global__ __launch_bounds__(kThreads) void k_gateup_m1(M1GateUpArgs a) {
     const int p_end = min(a.total_pairs, p_begin + a.pairs_per_wave);
     const int H = a.H, nch = H / N;
     const float sc = a.tok_scale ? a.tok_scale[0] : 1.0f;
+    // MXFP4 codes with bf16 x: x stays as bf16 pairs and the codes, converted
+    // to bf16 pairs, go through v_dot2c_f32_bf16 (the pre-norm scale then
+    // multiplies the finished dots); otherwise x is held as fp32 with the
+    // scale folded in.
+    constexpr bool XD2 = XDT == DT_BF16 && WDT == DT_MX4;
     // x chunks this lane multiplies (loaded before the top-k, which does not
     // need them); lanes past the row end hold zeros and load (harmless)
     // duplicates of the last chunk.
     int cl[CPL];
-    float xr[CPL][N];
+    float xr[XD2 ? 1 : CPL][XD2 ? 1 : N];
+    uint32_t xw[XD2 ? CPL : 1][XD2 ? N / 2 : 1];
 #pragma unroll
     for (int cc = 0; cc < CPL; cc++) {
         const int c = lane + kWave * cc;
         cl[cc] = min(c, nch - 1);
         const float m = c < nch ? sc : 0.f;
+        if constexpr (XD2) {
 #pragma unroll
-        for (int n4 = 0; n4 < N; n4 += 4) {
-            if constexpr (XDT == DT_BF16) {
-                const u32x2 q = reinterpret_cast<const u32x2 *>(reinterpret_cast<const uint16_t *>(a.x) + cl[cc] * N + n4)[0];
-                xr[cc][n4] = bf16_lo(q.x) * m; xr[cc][n4 + 1] = bf16_hi(q.x) * m;
-                xr[cc][n4 + 2] = bf16_lo(q.y) * m; xr[cc][n4 + 3] = bf16_hi(q.y) * m;
-            } else {
-                const f32x4 q = reinterpret_cast<const f32x4 *>(reinterpret_cast<const float *>(a.x) + cl[cc] * N + n4)[0];
-                xr[cc][n4] = q.x * m; xr[cc][n4 + 1] = q.y * m; xr[cc][n4 + 2] = q.z * m; xr[cc][n4 + 3] = q.w * m;
+            for (int q4 = 0; q4 < N / 8; q4++) {
+                const u32x4 q = reinterpret_cast<const u32x4 *>(reinterpret_cast<const uint16_t *>(a.x) + cl[cc] * N)[q4];
+                xw[cc][4 * q4] = c < nch ? q.x : 0u;
+                xw[cc][4 * q4 + 1] = c < nch ? q.y : 0u;
+                xw[cc][4 * q4 + 2] = c < nch ? q.z : 0u;
+                xw[cc][4 * q4 + 3] = c < nch ? q.w : 0u;
+            }
+        } else {
+#pragma unroll
+            for (int n4 = 0; n4 < N; n4 += 4) {
+                if constexpr (XDT == DT_BF16) {
+                    const u32x2 q = reinterpret_cast<const u32x2 *>(reinterpret_cast<const uint16_t *>(a.x) + cl[cc] * N + n4)[0];
+                    xr[cc][n4] = bf16_lo(q.x) * m; xr[cc][n4 + 1] = bf16_hi(q.x) * m;
+                    xr[cc][n4 + 2] = bf16_lo(q.y) * m; xr[cc][n4 + 3] = bf16_hi(q.y) * m;
+                } else {
+                    const f32x4 q = reinterpret_cast<const f32x4 *>(reinterpret_cast<const float *>(a.x) + cl[cc] * N + n4)[0];
+                    xr[cc][n4] = q.x * m; xr[cc][n4 + 1] = q.y * m; xr[cc][n4 + 2] = q.z * m; xr[cc][n4 + 3] = q.w * m;
+                }
             }
         }
     }
@@ -796,14 +813,25 @@ __global__ __launch_bounds__(kThreads) void k_gateup_m1(M1GateUpArgs a) {
             float g = 0.f, v = 0.f;
 #pragma unroll
             for (int cc = 0; cc < CPL; cc++) {
-                float wg[N], wu[N];
-                decode_chunk<WDT>(rg[r][cc], wg);
-                decode_chunk<WDT>(ru[r][cc], wu);
                 float pg = 0.f, pu = 0.f;
+                if constexpr (XD2) {
+                    uint32_t wg[N / 2], wu[N / 2];
+                    mx4_to_bf16x2(rg[r][cc], wg);
+                    mx4_to_bf16x2(ru[r][cc], wu);
 #pragma unroll
-                for (int n = 0; n < N; n++) {
-                    pg = fmaf(wg[n], xr[cc][n], pg);
-                    pu = fmaf(wu[n], xr[cc][n], pu);
+                    for (int q = 0; q < N / 2; q++) {
+                        pg = dot2_bf16(wg[q], xw[cc][q], pg);
+                        pu = dot2_bf16(wu[q], xw[cc][q], pu);
+                    }
+                } else {
+                    float wg[N], wu[N];
+                    decode_chunk<WDT>(rg[r][cc], wg);
+                    decode_chunk<WDT>(ru[r][cc], wu);
+#pragma unroll
+                    for (int n = 0; n < N; n++) {
+                        pg = fmaf(wg[n], xr[cc][n], pg);
+                        pu = fmaf(wu[n], xr[cc][n], pu);
+                    }
                 }
                 if constexpr (blocked<WDT>()) {
                     g = fmaf(scale_value<WDT>(hg[r][cc]), pg, g);
@@ -815,6 +843,10 @@ __global__ __launch_bounds__(kThreads) void k_gateup_m1(M1GateUpArgs a) {
             }
             g = wave_sum(g);
             v = wave_sum(v);
+            if constexpr (XD2) {
+                g *= sc;
+                v *= sc;
+            }
             if (a.limit > 0.f && slot[r] >= 0) { // the shared expert is not clamped
                 g = clampf(g, a.limit);
                 v = clampf(v, a.limit);
@@ -831,11 +863,14 @@ __global__ __launch_bounds__(kThreads) void k_gateup_m1(M1GateUpArgs a) {
 // down (M = 1): a workgroup reads the k picks and weights the gate/up kernel
 // wrote, then owns kM1Rows output rows; its 256 threads stride
 // over the concatenated chunks of every touched expert's rows (then the
-// shared expert's), kM1Unroll rounds at a time with every load of the rounds
+// shared expert's), m1_unroll rounds at a time with every load of the rounds
 // issued first.  Each chunk's dot is scaled by its route's weight before the
 // block reduction, which is done in a fixed order.
 constexpr int kM1Rows = 4;
-constexpr int kM1Unroll = 2;
+// Rounds in flight: 4 for Q8_0 (measured 10.8 against 11.7 us at the
+// gpt-oss shape), else 2 (MXFP4 at 4: 14.3 against 10.5 us, from the
+// register footprint of its 32-element chunks).
+template <int WDT> constexpr int m1_unroll() { return WDT == DT_Q8 ? 4 : 2; }
 constexpr int kMaxSlots = 9; // top-k slots + the shared expert
 
 struct M1DownArgs {
@@ -888,6 +923,7 @@ __global__ __launch_bounds__(kThreads) void k_down_m1(M1DownArgs a) {
     float acc[kM1Rows];
 #pragma unroll
     for (int r = 0; r < kM1Rows; r++) acc[r] = 0.f;
+    constexpr int kM1Unroll = m1_unroll<WDT>();
     for (int t0 = 0; t0 < n_tasks; t0 += kThreads * kM1Unroll) {
         u32x4 raw[kM1Unroll][kM1Rows];
         uint16_t hs[kM1Unroll][kM1Rows];
