@@ -81,6 +81,8 @@ struct GemmArgs {
     int out_split;           // gate/up: write act as interleaved bf16 hi/lo (the split A of down)
     int tile_rows;           // rows per tile of the LDS kernel (32 or 128; the tile list's)
     int n_ntiles;            // column tiles
+    int units_pad;           // LDS kernel: workgroups per token tile (>= n_ntiles * ksplit; the extra ones idle)
+    int pad_units;           // caller's request: pad the units for the XCD-grouped order (see run_gemm)
 };
 
 template <int KIND>
@@ -236,9 +238,10 @@ __global__ __launch_bounds__(kGThreads, 1) void k_gemm_lds(GemmArgs a) {
     // unit's weights are read from HBM about once, and an XCD's units share
     // one reduction slice of the A rows, which its L2 then serves.  Otherwise
     // the workgroups run through (tl, c) in tile-major order, so that every
-    // XCD gets work.
+    // XCD gets work.  (A unit count a little short of a multiple of 8 is
+    // padded to one with idle workgroups, so that it takes the first order.)
     const int g = blockIdx.x;
-    const int per_tile = a.n_ntiles * a.ksplit;
+    const int per_tile = a.units_pad;
     int e = 0, ts, Te, p0, nrows;
     if (a.tiles) {
         const int q = g / per_tile;
@@ -262,6 +265,7 @@ __global__ __launch_bounds__(kGThreads, 1) void k_gemm_lds(GemmArgs a) {
         tl = local / per_tile;
         cu = local - tl * per_tile;
     }
+    if (cu >= a.n_ntiles * a.ksplit) return; // padding unit
     const int ks = cu / a.n_ntiles, nt = cu - ks * a.n_ntiles;
     if (a.tiles) {
         p0 = a.tiles[2 + a.E + 2 * (ts + tl) + 1];
@@ -803,7 +807,14 @@ static hipError_t run_gemm(int kind, int a_mode, int bq, GemmArgs &a, hipStream_
         const unsigned grid = (unsigned)(((long)a.max_tiles * per_tile + 7) / 8 * 8);
         launch_kernel((k_gemm_reg<GK_PLAIN, true>), dim3(grid), dim3(kGThreads), 0, s, a);
     } else {
-        const unsigned grid = (unsigned)((long)a.max_tiles * per_tile);
+        // pad the units of a token tile to a multiple of 8, so that the LDS
+        // kernel takes its XCD-grouped order, when the caller expects experts
+        // with several token tiles and that idles at most one workgroup in 8
+        // (measured: the gpt-oss-shaped MXFP4 gate/up at M = 256, 210 against
+        // 267 us; with one tile an expert, M = 64, padding measured slower)
+        const int pad = (per_tile + 7) / 8 * 8;
+        a.units_pad = a.pad_units && (pad - per_tile) * 8 <= per_tile ? pad : per_tile;
+        const unsigned grid = (unsigned)((long)a.max_tiles * a.units_pad);
         if (a.tile_rows != 32 && a.tile_rows != kBM) return hipErrorInvalidValue;
         if (kind == GK_GATEUP && a_mode == 0) launch_lds<GK_GATEUP, false>(a, bq, grid, s);
         else if (kind == GK_GATEUP && a_mode == 1) launch_lds<GK_GATEUP, true>(a, bq, grid, s);
@@ -841,6 +852,7 @@ hipError_t launch_gateup_mfma(const Layer &L, const void *x, const float *tok_sc
     if (act) {
         GemmArgs a{};
         a.tile_rows = tile_rows;
+        a.pad_units = (long)M * L.k >= (long)tile_rows * L.E; // about a full tile an expert, or more
         a.a = x;
         a.sorted = rt.sorted;
         a.k_route = L.k;
@@ -869,6 +881,7 @@ hipError_t launch_gateup_mfma(const Layer &L, const void *x, const float *tok_sc
         a.a = x;
         a.M = M;
         a.tile_rows = M <= 32 ? 32 : kBM;
+        a.pad_units = M > a.tile_rows;
         a.max_tiles = (M + a.tile_rows - 1) / a.tile_rows;
         a.b0 = static_cast<const uint16_t *>(shared.gate);
         a.b1 = static_cast<const uint16_t *>(shared.up);
@@ -898,6 +911,7 @@ hipError_t launch_down_mfma(const Layer &L, const float *act, const float *share
         a.E = L.E;
         a.max_tiles = max_tiles;
         a.tile_rows = tile_rows;
+        a.pad_units = (long)M * L.k >= (long)tile_rows * L.E; // about a full tile an expert, or more
         a.ksplit = down_ksplit(L, M, tile_rows);
         a.slab = (size_t)M * L.k * L.H;
         a.b0 = static_cast<const uint16_t *>(routed.down);
@@ -916,6 +930,7 @@ hipError_t launch_down_mfma(const Layer &L, const float *act, const float *share
         a.a = shared_act;
         a.M = M;
         a.tile_rows = act_split && M <= 32 ? 32 : kBM;
+        a.pad_units = M > a.tile_rows;
         a.max_tiles = (M + a.tile_rows - 1) / a.tile_rows;
         a.b0 = static_cast<const uint16_t *>(shared.down);
         a.s0 = static_cast<const uint16_t *>(shared.down_s);
