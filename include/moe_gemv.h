@@ -148,7 +148,7 @@ typedef struct moe_plan moe_plan; /* host-side, library-owned */
  * (E or k < 1, k > E, H, I <= 0, Is < 0, max_tokens < 1, unknown enums);
  * MOE_ERR_UNSUPPORTED for k > 8, E > 256, H, I or Is not a multiple of 32, a
  * dtype combination the kernels do not cover, or MOE_PATH_MFMA without bf16 x,
- * bf16 or Q8_0 experts and H, I, Is multiples of 64.  Refusal happens here,
+ * bf16, Q8_0 or MXFP4 experts and H, I, Is multiples of 64.  Refusal happens here,
  * before any device work, in the
  * manner of the pages' state constructors (llama/state.rs and
  * deepseek2/state.rs, the `build` functions' open-time checks).
@@ -158,7 +158,8 @@ void moe_plan_destroy(moe_plan *plan);
 
 /* Workspace bytes needed by any entry point called with this M (0 <= M <=
  * max_tokens); returns 0 for M out of range.  Regions for unused features
- * (shared expert, pre-norm, the MFMA path) take no space. */
+ * (shared expert, pre-norm, the MFMA path) take no space; plans with the
+ * pre-norm on hold room for moe_forward_fused's normed rows. */
 size_t moe_workspace_bytes(const moe_plan *plan, int32_t M);
 
 /* Zero the reserved counter words of a workspace (one small kernel on
