@@ -30,6 +30,36 @@ def _t(a, dtype=None):
         torch.from_numpy(np.ascontiguousarray(a)).to(dtype).cuda()
 
 
+# ------------------------------------------------------------- block splits
+@pytest.mark.parametrize("fmt", ["q8_0", "mxfp4"])
+def test_block_split_bit_exact(fmt):
+    """moe_q8_0_split / moe_mxfp4_split against the block definition (bytes
+    copied, never converted), on random bytes and ragged shapes."""
+    import mixture_experts_gemv_amd as m
+    rng = np.random.default_rng(7)
+    for rows, cols in [(1, 32), (37, 96), (5, 2880), (3, 4608)]:
+        nb = cols // 32
+        say(f"split {fmt} {rows}x{cols}")
+        if fmt == "mxfp4":
+            blocks = rng.integers(0, 256, size=(rows, nb, 17), dtype=np.uint8)
+            vals = torch.empty(rows * cols // 2, dtype=torch.uint8, device="cuda")
+            sc = torch.empty(rows * nb, dtype=torch.uint8, device="cuda")
+            m.moe_mxfp4_split(_t(blocks.reshape(-1)), rows, cols, vals, sc)
+            want_vals, want_sc = blocks[:, :, 1:].reshape(-1), blocks[:, :, 0].reshape(-1)
+            got_vals, got_sc = vals.cpu().numpy(), sc.cpu().numpy()
+        else:
+            blocks = rng.integers(0, 256, size=(rows, nb, 34), dtype=np.uint8)
+            vals = torch.empty(rows * cols, dtype=torch.int8, device="cuda")
+            sc = torch.empty(rows * nb, dtype=torch.int16, device="cuda")
+            m.moe_q8_0_split(_t(blocks.reshape(-1)), rows, cols, vals, sc)
+            want_vals = blocks[:, :, 2:].reshape(-1)
+            want_sc = np.ascontiguousarray(blocks[:, :, :2]).reshape(-1).view(np.uint16)
+            got_vals, got_sc = vals.cpu().numpy().view(np.uint8), sc.cpu().numpy().view(np.uint16)
+        torch.cuda.synchronize()
+        assert np.array_equal(got_vals, want_vals), f"{fmt} {rows}x{cols}: value plane differs"
+        assert np.array_equal(got_sc, want_sc), f"{fmt} {rows}x{cols}: scale plane differs"
+
+
 # --------------------------------------------------------------------- routing
 ROUTE_CASES = [
     dict(num_experts=8, top_k=2),
@@ -249,6 +279,7 @@ SMALL = [
     ("mx4-all-shared-rms", dict(hidden=192, num_experts=16, top_k=6, expert_inter=2112,
                                 shared_inter=160, select=SOFTMAX_ALL_NORENORM, rms_eps=1e-6,
                                 expert_dtype=MXFP4, shared_dtype=MXFP4), (1, 9)),
+    ("mx4-dense", dict(hidden=256, num_experts=1, top_k=1, expert_inter=1088, expert_dtype=MXFP4), (1, 16, 70)),
 ]
 
 
@@ -288,6 +319,7 @@ MFMA_SMALL = [
                                    expert_dtype=MXFP4, shared_dtype=MXFP4, bias_mode=BIAS_LOGIT,
                                    bias_kind="normal", swiglu_limit=0.5), (3, 33, 100)),
     ("mx4-wide", dict(hidden=576, num_experts=4, top_k=1, expert_inter=704, expert_dtype=MXFP4), (129,)),
+    ("mx4-dense", dict(hidden=256, num_experts=1, top_k=1, expert_inter=1088, expert_dtype=MXFP4), (70,)),
 ]
 
 
