@@ -40,11 +40,10 @@ constexpr int kTV = 4;                   // vectors dotted per pass over loaded 
 constexpr int kStageMax = 8;             // vectors one LDS stage holds, at most
 constexpr int kStageBytes = 64 * 1024;   // LDS for staged vectors, per workgroup
 constexpr int kSliceMax = 2048;          // reduction elements per down slice
-// Rows per load group with MXFP4 weights, whose 16-byte chunks hold half the
-// bytes of a Q8_0 row's: more rows keep as many bytes in flight per wave
-// (one-token gate/up with at most two chunks per lane; per-row gate/up with
-// at most two; per-row down with at most four).
-constexpr int kMx4RowsM1 = 2;
+// Rows per load group of the per-row kernels with MXFP4 weights (gate/up with
+// at most two chunks per lane, down with at most four).  Four rows, which
+// would keep as many bytes in flight as Q8_0's two, measured slower (the
+// register footprint costs occupancy).
 constexpr int kMx4RowsGU = 2;
 constexpr int kMx4RowsDN = 2;
 
@@ -1003,14 +1002,6 @@ static bool m1_gateup_dispatch(int cpl, const M1GateUpArgs &a, int grid, hipStre
 #undef M1_CASE
 }
 
-// MXFP4 with at most two chunks per lane: kMx4RowsM1 rows per group.
-template <int XDT>
-static bool m1_gateup_dispatch_mx4(int cpl, const M1GateUpArgs &a, int grid, hipStream_t s) {
-    if (cpl == 1) launch_kernel((k_gateup_m1<XDT, DT_MX4, 1, kMx4RowsM1>), dim3(grid), dim3(kThreads), 0, s, a);
-    else if (cpl == 2) launch_kernel((k_gateup_m1<XDT, DT_MX4, 2, kMx4RowsM1>), dim3(grid), dim3(kThreads), 0, s, a);
-    else return false;
-    return true;
-}
 
 bool m1_supported(const Layer &L) {
     const int N = chunk_elems(L.edt);
@@ -1045,8 +1036,11 @@ hipError_t launch_gateup_m1(const Layer &L, const void *x, const float *tok_scal
     a.total_pairs = L.k * L.I + a.Is;
     const int N = chunk_elems(L.edt);
     const int cpl = m1_cpl(L.H, N);
-    // keep about 16 loads of a group in flight
-    const int RP = L.edt == DT_MX4 && cpl <= 2 ? kMx4RowsM1 : (cpl <= 4 ? 2 : 1);
+    // Rows per load group: two for bf16 and fp32 rows of at most four chunks
+    // per lane (about 16 loads of a group in flight), else one.  With Q8_0
+    // and MXFP4 rows one row a group measured faster (gpt-oss shape, Q8_0:
+    // 16.9 against 18.1 us; MXFP4: 15.1 against 15.6 us; bf16 unchanged).
+    const int RP = cpl <= 4 && (L.edt == DT_BF16 || L.edt == DT_F32) ? 2 : 1;
     const int max_waves = 2048;
     int ppw = (a.total_pairs + max_waves - 1) / max_waves;
     ppw = (ppw + RP - 1) / RP * RP;
@@ -1055,13 +1049,13 @@ hipError_t launch_gateup_m1(const Layer &L, const void *x, const float *tok_scal
     const int grid = (waves + kWaves - 1) / kWaves;
     bool ok;
     if (L.xdt == DT_BF16) {
-        if (L.edt == DT_Q8) ok = RP == 2 ? m1_gateup_dispatch<DT_BF16, DT_Q8, 2>(cpl, a, grid, s) : m1_gateup_dispatch<DT_BF16, DT_Q8, 1>(cpl, a, grid, s);
-        else if (L.edt == DT_MX4) ok = cpl <= 2 ? m1_gateup_dispatch_mx4<DT_BF16>(cpl, a, grid, s) : RP == 2 ? m1_gateup_dispatch<DT_BF16, DT_MX4, 2>(cpl, a, grid, s) : m1_gateup_dispatch<DT_BF16, DT_MX4, 1>(cpl, a, grid, s);
+        if (L.edt == DT_Q8) ok = m1_gateup_dispatch<DT_BF16, DT_Q8, 1>(cpl, a, grid, s);
+        else if (L.edt == DT_MX4) ok = m1_gateup_dispatch<DT_BF16, DT_MX4, 1>(cpl, a, grid, s);
         else if (L.edt == DT_BF16) ok = RP == 2 ? m1_gateup_dispatch<DT_BF16, DT_BF16, 2>(cpl, a, grid, s) : m1_gateup_dispatch<DT_BF16, DT_BF16, 1>(cpl, a, grid, s);
         else ok = RP == 2 ? m1_gateup_dispatch<DT_BF16, DT_F32, 2>(cpl, a, grid, s) : m1_gateup_dispatch<DT_BF16, DT_F32, 1>(cpl, a, grid, s);
     } else {
-        if (L.edt == DT_Q8) ok = RP == 2 ? m1_gateup_dispatch<DT_F32, DT_Q8, 2>(cpl, a, grid, s) : m1_gateup_dispatch<DT_F32, DT_Q8, 1>(cpl, a, grid, s);
-        else if (L.edt == DT_MX4) ok = cpl <= 2 ? m1_gateup_dispatch_mx4<DT_F32>(cpl, a, grid, s) : RP == 2 ? m1_gateup_dispatch<DT_F32, DT_MX4, 2>(cpl, a, grid, s) : m1_gateup_dispatch<DT_F32, DT_MX4, 1>(cpl, a, grid, s);
+        if (L.edt == DT_Q8) ok = m1_gateup_dispatch<DT_F32, DT_Q8, 1>(cpl, a, grid, s);
+        else if (L.edt == DT_MX4) ok = m1_gateup_dispatch<DT_F32, DT_MX4, 1>(cpl, a, grid, s);
         else if (L.edt == DT_BF16) ok = RP == 2 ? m1_gateup_dispatch<DT_F32, DT_BF16, 2>(cpl, a, grid, s) : m1_gateup_dispatch<DT_F32, DT_BF16, 1>(cpl, a, grid, s);
         else ok = RP == 2 ? m1_gateup_dispatch<DT_F32, DT_F32, 2>(cpl, a, grid, s) : m1_gateup_dispatch<DT_F32, DT_F32, 1>(cpl, a, grid, s);
     }
