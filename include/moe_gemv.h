@@ -43,8 +43,8 @@
  *    (gate [E][I][H/2] bytes), and E8M0 scale bytes, one per 32 consecutive
  *    elements along the reduction dimension (gate_scale [E][I][H/32]).  Value
  *    = 2^(scale - 127) * element.  moe_mxfp4_split converts 17-byte blocks
- *    into them.  Code planes must be 16-byte aligned; scale planes may have
- *    any alignment.
+ *    into them.  Code planes must be 16-byte aligned and scale planes 2-byte
+ *    aligned (MOE_ERR_INVALID otherwise).
  *  - Routes: route r = t*top_k + j is slot j of token t.  "Sorted position" p
  *    is the route's index in expert-major order (experts ascending, routes
  *    ascending inside an expert), as produced by moe_permute.
@@ -292,7 +292,8 @@ moe_status moe_q8_0_split(const void *blocks, int64_t rows, int32_t cols, int8_t
  * 2^(scale - 127) * element; gptoss/state.rs (module doc and
  * BatchedRoutedScratch) names MXFP4 as the format of gpt-oss's routed expert
  * pair, and the 17-byte block layout is a reading of that.  Device pointers;
- * codes 16-byte aligned, blocks and scales any alignment; MOE_ERR_INVALID for
+ * codes 16-byte aligned, blocks and scales any alignment (the layer
+ * reads scale planes 2-byte aligned); MOE_ERR_INVALID for
  * rows < 0, cols <= 0 or cols % 32 != 0. */
 moe_status moe_mxfp4_split(const void *blocks, int64_t rows, int32_t cols, uint8_t *codes,
                            uint8_t *scales, void *stream);

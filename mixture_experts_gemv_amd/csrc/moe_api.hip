@@ -145,8 +145,9 @@ moe_status need_ptr(const void *ptr, size_t align, const char *name) {
 moe_status check_experts(const moe_plan *p, const moe_weights *w, bool need_gateup, bool need_down,
                          bool need_shared) {
     if (!w) return fail(MOE_ERR_INVALID, "weights is NULL");
-    // block scale planes: Q8_0 fp16 (4-byte aligned), MXFP4 E8M0 bytes (any address)
-    auto scale_align = [](int dt) -> size_t { return dt == moe::DT_Q8 ? 4 : (dt == moe::DT_MX4 ? 1 : 0); };
+    // block scale planes: Q8_0 fp16 (4-byte aligned), MXFP4 E8M0 bytes (2-byte
+    // aligned: the grouped GEMM reads a column's two scales of a stage at once)
+    auto scale_align = [](int dt) -> size_t { return dt == moe::DT_Q8 ? 4 : (dt == moe::DT_MX4 ? 2 : 0); };
     const size_t sa = scale_align(p->L.edt);
     if (need_gateup) {
         TRY(need_ptr(w->gate, 16, "weights.gate"));

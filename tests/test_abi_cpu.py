@@ -148,7 +148,7 @@ def test_call_refusals_before_any_launch():
     assert L.moe_q8_0_split(FAKE, 4, 33, FAKE, FAKE, None) == m.MOE_ERR_INVALID
     assert L.moe_q8_0_split(FAKE, -1, 32, FAKE, FAKE, None) == m.MOE_ERR_INVALID
     assert L.moe_q8_0_split(None, 0, 32, None, None, None) == m.MOE_OK
-    # MXFP4 needs its scale planes (any alignment) and code planes 16-byte aligned
+    # MXFP4 needs its scale planes (2-byte aligned) and code planes 16-byte aligned
     px = _create(expert_dtype=m.MOE_MXFP4)
     st = L.moe_expert_ffn(px.handle, FAKE, ctypes.byref(w), 4, FAKE, FAKE, FAKE, FAKE,
                           m.moe_workspace_bytes(px, 4), None)
@@ -159,6 +159,11 @@ def test_call_refusals_before_any_launch():
     st = L.moe_expert_ffn(px.handle, FAKE, ctypes.byref(unaligned), 4, FAKE, FAKE, FAKE, FAKE,
                           m.moe_workspace_bytes(px, 4), None)
     assert st == m.MOE_ERR_INVALID and "gate" in m.moe_last_error()
+    odd = m.make_weights(router=FAKE, gate=FAKE, up=FAKE, down=FAKE, gate_scale=FAKE + 2,
+                         up_scale=FAKE + 1, down_scale=FAKE + 4)
+    st = L.moe_expert_ffn(px.handle, FAKE, ctypes.byref(odd), 4, FAKE, FAKE, FAKE, FAKE,
+                          m.moe_workspace_bytes(px, 4), None)
+    assert st == m.MOE_ERR_INVALID and "up_scale" in m.moe_last_error()
     assert m.MOE_RUN_NAMES[m.moe_forward_path(px, 1)] == "single"
     assert L.moe_mxfp4_split(FAKE, 4, 48, FAKE, FAKE, None) == m.MOE_ERR_INVALID
     assert L.moe_mxfp4_split(FAKE, -1, 32, FAKE, FAKE, None) == m.MOE_ERR_INVALID
