@@ -405,6 +405,55 @@ def test_forward_repeatable():
     assert np.array_equal(a, b)
 
 
+@pytest.mark.parametrize("M,path,fused", [(1, 0, False), (9, 1, False), (130, 2, False), (1, 0, True),
+                                          (40, 2, True)],
+                         ids=["single", "gemv", "mfma", "single-fused", "mfma-fused"])
+def test_graph_replay_matches_eager(M, path, fused):
+    """The layer captured in a HIP graph (as bench.py times it): every replay,
+    with eager work and synchronisations between replays, equals the eager
+    result bitwise (the kernels are deterministic; nothing in a call is a
+    memset node)."""
+    import mixture_experts_gemv_amd as m
+    spec = synth.small_spec(hidden=256, num_experts=16, top_k=4, expert_inter=192, shared_inter=128,
+                            bias_mode=BIAS_LOGIT, bias_kind="normal", swiglu_limit=7.0, expert_dtype=Q8_0,
+                            shared_dtype=Q8_0, rms_eps=1e-6 if fused else 0.0, seed=1250)
+    layer = synth.make_layer(spec)
+    dl = device_layer(spec, layer, M, path=path)
+    x = dl.x_tensor(synth.make_tokens(spec, M))
+    ws = dl.workspace(M)
+    gamma = dl.x_tensor(synth.bf16_bits(np.linspace(0.5, 1.5, spec.hidden).astype(np.float32)))
+    res = torch.randn(M, spec.hidden, dtype=torch.float32, device="cuda")
+    y = torch.empty(M, spec.hidden, dtype=torch.float32, device="cuda")
+
+    def call():
+        if fused:
+            m.moe_forward_fused(dl.plan, x, gamma, res, dl.weights, M, y, None, None, None, ws)
+        else:
+            m.moe_forward(dl.plan, x, dl.weights, M, y, None, None, None, ws)
+
+    say(f"graph replay M={M} path={path} fused={fused}")
+    call()
+    torch.cuda.synchronize()
+    eager = y.clone()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(g, stream=cap):
+            call()
+    torch.cuda.current_stream().wait_stream(cap)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        y.fill_(float("nan"))
+        other = torch.randn(64, 64, device="cuda") @ torch.randn(64, 64, device="cuda")  # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, eager), f"replay {rep} differs from the eager call"
+        del other
+    del g
+
+
 @pytest.mark.parametrize("M,path,want", [
     (1, 0, ["router", "gateup", "down"]),
     (9, 1, ["router", "gateup", "down", "combine"]),
