@@ -654,8 +654,8 @@ hipError_t launch_down_gemv(const Layer &L, const float *act, const float *share
 // position of the route to the u-th touched expert is u.
 //
 // gate/up: each wave holds x in registers (lane l owns chunks l, l+64, ...)
-// and streams a contiguous range of (slot, row) pairs, RP pairs at a time,
-// issuing all 2*RP*CPL 16-byte loads of a group before using them.
+// and streams (slot, row) pairs, RP at a time and strided by the grid's
+// waves, issuing all 2*RP*CPL 16-byte loads of a group before using them.
 // The gate/up kernel runs the token's top-k from the router logits in its
 // prologue (every wave, DPP rounds); its first wave writes the picks and their
 // weights, which the down kernel reads.  (Computing the logits inside every
@@ -695,7 +695,7 @@ struct M1GateUpArgs {
     int32_t *ids_out, *counts_out; // written by the first wave
     float *w_out;
     int H, I, Is, k;
-    int total_pairs, pairs_per_wave;
+    int total_pairs;
     float limit;
     float *act, *shared_act;
 };
@@ -705,9 +705,13 @@ __global__ __launch_bounds__(kThreads) void k_gateup_m1(M1GateUpArgs a) {
     constexpr int N = Chunk<WDT>::N;
     const int lane = threadIdx.x & 63;
     const int gw = uniform(blockIdx.x * kWaves + (threadIdx.x >> 6));
-    const int p_begin = gw * a.pairs_per_wave;
-    if (p_begin >= a.total_pairs) return;
-    const int p_end = min(a.total_pairs, p_begin + a.pairs_per_wave);
+    // wave gw takes the RP pairs at gw * RP, then every nwv * RP further, so
+    // that the waves in flight read neighbouring rows (measured faster than
+    // a contiguous range of pairs a wave: gpt-oss-shaped Q8_0 16.1 against
+    // 17.0 us, Mixtral-shaped 75.5 against 77.3 us)
+    const int nwv = gridDim.x * kWaves;
+    if (gw * RP >= a.total_pairs) return;
+    const int p_end = a.total_pairs;
     const int H = a.H, nch = H / N;
     const float sc = a.tok_scale ? a.tok_scale[0] : 1.0f;
     // MXFP4 codes with bf16 x: x stays as bf16 pairs and the codes, converted
@@ -766,7 +770,7 @@ __global__ __launch_bounds__(kThreads) void k_gateup_m1(M1GateUpArgs a) {
     }
     const int routed_pairs = a.k * a.I;
     const size_t rbytes = row_bytes<WDT>(H);
-    for (int p = p_begin; p < p_end; p += RP) {
+    for (int p = gw * RP; p < p_end; p += nwv * RP) {
         const char *grow[RP], *urow[RP];
         const void *gsr[RP], *usr[RP];
         int slot[RP], irow[RP];
@@ -1044,7 +1048,6 @@ hipError_t launch_gateup_m1(const Layer &L, const void *x, const float *tok_scal
     const int max_waves = 2048;
     int ppw = (a.total_pairs + max_waves - 1) / max_waves;
     ppw = (ppw + RP - 1) / RP * RP;
-    a.pairs_per_wave = ppw;
     const int waves = (a.total_pairs + ppw - 1) / ppw;
     const int grid = (waves + kWaves - 1) / kWaves;
     bool ok;
