@@ -14,7 +14,7 @@
 //   the fp16 block scale multiplies each chunk's dot.  The per-token pre-norm
 //   scale multiplies the finished dot.  Epilogue: clamp (routed experts only),
 //   silu(g) * v -> act.
-// down: a workgroup owns (touched expert, tile of kRowsTileDN rows of H, slice of
+// down: a workgroup owns (touched expert, tile of 32 or 64 rows of H, slice of
 //   the reduction over I).  The slice of the expert's act rows is copied into
 //   LDS (fp32), each wave streams its rows RP at a time (every load of a group
 //   issued first), and each row's dots are written to y_routes[slice][route][h]
@@ -30,16 +30,18 @@ namespace moe {
 
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * kWave;
-// Rows per wave of one workgroup tile (measured: smaller gate/up tiles, i.e.
-// more workgroups, stream faster; the down tiles prefer 16 rows per wave).
+// Rows per wave of one gate/up workgroup tile (measured: smaller gate/up
+// tiles, i.e. more workgroups, stream faster; the down tiles' rows per wave
+// depend on the format, dn_rows_per_wave below).
 constexpr int kRowsPerWaveGU = 8;
 constexpr int kRowsTileGU = kWaves * kRowsPerWaveGU;
-constexpr int kRowsPerWaveDN = 16;
-constexpr int kRowsTileDN = kWaves * kRowsPerWaveDN;
+// Down rows per wave: 8 for bf16 weights (DeepSeek-V2-Lite shape, M = 16:
+// 74 against 85 us), 16 for the others (gpt-oss shape, Q8_0: 66 against 69 us).
+template <int WDT> constexpr int dn_rows_per_wave() { return WDT == DT_BF16 ? 8 : 16; }
+static int dn_rows_tile(int dt) { return kWaves * (dt == DT_BF16 ? 8 : 16); }
 constexpr int kTV = 4;                   // vectors dotted per pass over loaded rows
 constexpr int kStageMax = 8;             // vectors one LDS stage holds, at most
 constexpr int kStageBytes = 64 * 1024;   // LDS for staged vectors, per workgroup
-constexpr int kSliceMax = 2048;          // reduction elements per down slice
 // Rows per load group of the per-row kernels with MXFP4 weights (gate/up with
 // at most two chunks per lane, down with at most four).  Four rows, which
 // would keep as many bytes in flight as Q8_0's two, measured slower (the
@@ -430,7 +432,7 @@ template <int WDT, int CPL, int RP>
 __global__ __launch_bounds__(kThreads) void k_down_rows(RowsDown a) {
     extern __shared__ __attribute__((aligned(16))) float s_act[]; // [ncap][KS] fp32
     constexpr int N = Chunk<WDT>::N;
-    constexpr int NG = kRowsPerWaveDN / RP;
+    constexpr int NG = dn_rows_per_wave<WDT>() / RP;
     using Loads = DownLoads<WDT, CPL, RP>;
     const int tid = threadIdx.x, lane = tid & 63, wave = uniform(tid >> 6);
     const int H = a.H;
@@ -473,7 +475,7 @@ __global__ __launch_bounds__(kThreads) void k_down_rows(RowsDown a) {
     const void *dsb = nullptr;
     if constexpr (blocked<WDT>()) dsb = scale_at<WDT>(m.down_s, mrow0 * (width / 32) + k0 / 32);
     float *out = shared ? a.y_shared + ks * a.slab_s : a.y_routes + ks * a.slab_r + (size_t)p0 * H;
-    const int row_w = rt * kRowsTileDN + wave * kRowsPerWaveDN;
+    const int row_w = rt * kWaves * dn_rows_per_wave<WDT>() + wave * dn_rows_per_wave<WDT>();
     const int nch = klen / N;
     const int ncb = (nch + kWave * CPL - 1) / (kWave * CPL);
     const int ng = row_w < H ? min(NG, (H - row_w) / RP) : 0;
@@ -581,22 +583,27 @@ __global__ __launch_bounds__(kThreads) void k_down_rows(RowsDown a) {
     }
 }
 
-// Slices of a down reduction of `width` elements: each at most kSliceMax
-// wide, a multiple of 32 (whole Q8_0 blocks), as even as that allows.
-static void down_slices(int width, int *S, int *KS) {
+// Slices of a down reduction of `width` elements: each at most 64 chunks
+// (one 16-byte load per lane: 1024 Q8_0, 2048 MXFP4, 512 bf16 or 256 fp32
+// elements), a multiple of 32 (whole Q8_0 and MXFP4 blocks), as even as
+// that allows.  (Measured at the gpt-oss shape, M = 16: Q8_0 down 66 against
+// 86 us with 2048-element slices, 90 chunks on 64 lanes; MXFP4 105 against
+// 91 us with 1024-element slices, 30 chunks.)
+static void down_slices(int width, int dt, int *S, int *KS) {
     if (width <= 0) {
         *S = 0;
         *KS = 0;
         return;
     }
-    *S = (width + kSliceMax - 1) / kSliceMax;
+    const int smax = kWave * chunk_elems(dt);
+    *S = (width + smax - 1) / smax;
     *KS = ((width + *S - 1) / *S + 31) / 32 * 32;
     *S = (width + *KS - 1) / *KS;
 }
 
-int down_gemv_slices(int width) {
+int down_gemv_slices(int width, int dt) {
     int S, KS;
-    down_slices(width, &S, &KS);
+    down_slices(width, dt, &S, &KS);
     return S;
 }
 
@@ -628,9 +635,9 @@ hipError_t launch_down_gemv(const Layer &L, const float *act, const float *share
     a.I = L.I;
     a.Is = shared_act ? L.Is : 0;
     a.max_routed = act ? (L.E < M * L.k ? L.E : M * L.k) : 0;
-    a.tiles_H = (L.H + kRowsTileDN - 1) / kRowsTileDN;
-    down_slices(L.I, &a.S, &a.KS);
-    down_slices(a.Is, &a.Ss, &a.KSs);
+    a.tiles_H = (L.H + dn_rows_tile(L.edt) - 1) / dn_rows_tile(L.edt);
+    down_slices(L.I, L.edt, &a.S, &a.KS);
+    down_slices(a.Is, L.sdt, &a.Ss, &a.KSs);
     const int ks_max = a.KS > a.KSs ? a.KS : a.KSs;
     a.ncap = kStageBytes / (ks_max * 4);
     if (a.ncap > kStageMax) a.ncap = kStageMax;

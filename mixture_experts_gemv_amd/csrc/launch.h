@@ -60,11 +60,11 @@ hipError_t launch_gateup_gemv(const Layer &L, const void *x, const float *tok_sc
                               const Mats &shared, const Routing &rt, int M, float *act,
                               float *shared_act, hipStream_t s);
 // Per-route down products, split over the reduction:
-// y_routes [down_gemv_slices(I)][M*k][H], y_shared [down_gemv_slices(Is)][M][H].
+// y_routes [down_gemv_slices(I, edt)][M*k][H], y_shared [down_gemv_slices(Is, sdt)][M][H].
 hipError_t launch_down_gemv(const Layer &L, const float *act, const float *shared_act, const Mats &routed,
                             const Mats &shared, const Routing &rt, int M, float *y_routes, float *y_shared,
                             hipStream_t s);
-int down_gemv_slices(int width);
+int down_gemv_slices(int width, int dt); // dt: the weights' format
 // y[t] = seed[t] + sum_s y_shared[s][t] + sum_j w[t][j] * sum_s y_routes[s][route_pos[t*k+j]]
 // (slices of a split reduction, slabs M*k*H and M*H apart).
 hipError_t launch_combine(const Layer &L, const float *y_routes, const float *y_shared,

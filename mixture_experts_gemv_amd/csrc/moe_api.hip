@@ -89,10 +89,10 @@ WsLayout layout(const moe_plan *p, int M) {
     // Q8_0 or MXFP4 experts uses the row kernels' slices even when the layer
     // call takes the grouped GEMM)
     const size_t slices = mfma ? std::max(moe::down_ksplit(L, M, moe::mfma_tile_rows()),
-                                          L.edt != moe::DT_BF16 ? moe::down_gemv_slices(L.I) : 1)
-                               : moe::down_gemv_slices(L.I);
+                                          L.edt != moe::DT_BF16 ? moe::down_gemv_slices(L.I, L.edt) : 1)
+                               : moe::down_gemv_slices(L.I, L.edt);
     w.y_routes = take(slices * R * L.H * 4);
-    w.y_shared = take(L.Is > 0 ? (size_t)(mfma ? 1 : moe::down_gemv_slices(L.Is)) * M * L.H * 4 : 0);
+    w.y_shared = take(L.Is > 0 ? (size_t)(mfma ? 1 : moe::down_gemv_slices(L.Is, L.sdt)) * M * L.H * 4 : 0);
     // the weighted pre-norm's rows (moe_forward_fused with a norm weight):
     // fp32, and split bf16 for the grouped GEMM; only plans with the pre-norm on
     w.xn = take(L.eps > 0.f ? (size_t)M * L.H * 4 : 0);
@@ -368,7 +368,7 @@ moe_status moe_combine(const moe_plan *p, const float *act, const moe_weights *w
     } else {
         float *yr = at<float>(ws, lay.y_routes);
         LAUNCH(moe::launch_down_gemv(L, act, nullptr, routed_mats(wts), none, rt, M, yr, nullptr, s), "down");
-        LAUNCH(moe::launch_combine(L, yr, nullptr, route_pos, w, seed, M, y, s, moe::down_gemv_slices(L.I), 0),
+        LAUNCH(moe::launch_combine(L, yr, nullptr, route_pos, w, seed, M, y, s, moe::down_gemv_slices(L.I, L.edt), 0),
                "combine");
     }
     return MOE_OK;
@@ -505,8 +505,8 @@ static moe_status forward_impl(const moe_plan *p, const void *x, const moe_weigh
               "gate/up", MOE_STAGE_GATEUP);
         STAGE(rec, moe::launch_down_gemv(L, act, sact, routed_mats(wts), shared_mats(wts), rt, M, yr, ysh, s),
               "down", MOE_STAGE_DOWN);
-        STAGE(rec, moe::launch_combine(L, yr, ysh, rpos, w, residual, M, y, s, moe::down_gemv_slices(L.I),
-                                       moe::down_gemv_slices(L.Is)),
+        STAGE(rec, moe::launch_combine(L, yr, ysh, rpos, w, residual, M, y, s, moe::down_gemv_slices(L.I, L.edt),
+                                       moe::down_gemv_slices(L.Is, L.sdt)),
               "combine", MOE_STAGE_COMBINE);
     }
     return MOE_OK;
