@@ -3,11 +3,11 @@
 // After routing and permutation, every touched expert's weight rows are
 // streamed from HBM once and dotted with the vectors routed to that expert.
 //
-// gate/up: a workgroup owns one tile of kRowsTileGU rows of one touched expert
+// gate/up: a workgroup owns one tile of 16 or 32 rows of one touched expert
 //   (or of the shared expert).  The x rows of the expert's tokens are copied
-//   into LDS as stored (bf16 or fp32).  Each wave streams its kRowsPerWaveGU
+//   into LDS as stored (bf16 or fp32).  Each wave streams its 4 or 8
 //   rows RP at a time, issuing every 16-byte load of a group (gate and up)
-//   before using any, and dots each row with every staged token (kTV tokens
+//   before using any, and dots each row with every staged token (one or four tokens
 //   per pass over the loaded rows).  With bf16 x
 //   and bf16 or Q8_0 weights the products run on v_dot2c_f32_bf16: bf16
 //   weights are used as loaded, Q8_0 int8 values convert to bf16 exactly, and
@@ -30,16 +30,23 @@ namespace moe {
 
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * kWave;
-// Rows per wave of one gate/up workgroup tile (measured: smaller gate/up
-// tiles, i.e. more workgroups, stream faster; the down tiles' rows per wave
-// depend on the format, dn_rows_per_wave below).
-constexpr int kRowsPerWaveGU = 8;
-constexpr int kRowsTileGU = kWaves * kRowsPerWaveGU;
+// Rows per wave of the per-row kernels' tiles depend on the format: gate/up
+// 4 for bf16 weights (DeepSeek-V2-Lite shape, M = 16: 131 against 154 us),
+// 8 for the others; down as dn_rows_per_wave below.
+template <int WDT> constexpr int gu_rows_per_wave() { return WDT == DT_BF16 ? 4 : 8; }
+static int gu_rows_tile(int dt) { return kWaves * (dt == DT_BF16 ? 4 : 8); }
 // Down rows per wave: 8 for bf16 weights (DeepSeek-V2-Lite shape, M = 16:
 // 74 against 85 us), 16 for the others (gpt-oss shape, Q8_0: 66 against 69 us).
 template <int WDT> constexpr int dn_rows_per_wave() { return WDT == DT_BF16 ? 8 : 16; }
 static int dn_rows_tile(int dt) { return kWaves * (dt == DT_BF16 ? 8 : 16); }
-constexpr int kTV = 4;                   // vectors dotted per pass over loaded rows
+// Vectors dotted per pass over a group's loaded rows: one when a row is one
+// chunk block (each staged vector then takes its own pass over the loaded
+// registers, with the fewest accumulators), four when a row spans several
+// blocks (the sums then run across the blocks, so a stage holds at most that
+// many vectors).  Measured at M = 16 against four a pass: gpt-oss-shaped
+// Q8_0 gate/up 109 against 132 us, MXFP4 107 against 121 us.
+constexpr int kTVMulti = 4;
+template <int CPL> constexpr int tokens_per_pass() { return CPL == 8 ? kTVMulti : 1; }
 constexpr int kStageMax = 8;             // vectors one LDS stage holds, at most
 constexpr int kStageBytes = 64 * 1024;   // LDS for staged vectors, per workgroup
 // Rows per load group of the per-row kernels with MXFP4 weights (gate/up with
@@ -93,7 +100,8 @@ template <int XDT, int WDT, int CPL, int RP>
 __global__ __launch_bounds__(kThreads) void k_gateup_rows(RowsGateUp a) {
     extern __shared__ __attribute__((aligned(16))) unsigned char s_x[]; // [ncap][H] as stored
     constexpr int N = Chunk<WDT>::N;
-    constexpr int NG = kRowsPerWaveGU / RP;
+    constexpr int NG = gu_rows_per_wave<WDT>() / RP;
+    constexpr int kTV = tokens_per_pass<CPL>();
     constexpr bool DOT2 = XDT == DT_BF16 && WDT != DT_F32;
     constexpr int XB = XDT == DT_BF16 ? 2 : 4;
     constexpr int NW = N / 2; // bf16 pair words per chunk (dot2 form)
@@ -132,7 +140,7 @@ __global__ __launch_bounds__(kThreads) void k_gateup_rows(RowsGateUp a) {
         gsb = scale_at<WDT>(m.gate_s, mrow0 * (H / 32));
         usb = scale_at<WDT>(m.up_s, mrow0 * (H / 32));
     }
-    const int row_w = rt * kRowsTileGU + wave * kRowsPerWaveGU; // this wave's first row
+    const int row_w = rt * kWaves * gu_rows_per_wave<WDT>() + wave * gu_rows_per_wave<WDT>(); // this wave's first row
     const int nch = H / N;
     const int ncb = (nch + kWave * CPL - 1) / (kWave * CPL); // chunk blocks per row
     const int ng = row_w < width ? min(NG, (width - row_w) / RP) : 0;
@@ -354,13 +362,13 @@ static void gateup_rows_dispatch(int cpl, const RowsGateUp &a, int grid, size_t 
 static int chunk_elems(int dt) { return dt == DT_MX4 ? 32 : (dt == DT_Q8 ? 16 : (dt == DT_BF16 ? 8 : 4)); }
 
 // Token rows one LDS stage of the gate/up kernel holds: up to kStageMax, as
-// LDS allows, and at most kTV when a row spans several chunk blocks.
+// LDS allows, and at most kTVMulti when a row spans several chunk blocks.
 int gemv_stage_tokens(const Layer &L) {
     const int xb = L.xdt == DT_BF16 ? 2 : 4;
     int n = kStageBytes / (L.H * xb);
     if (n > kStageMax) n = kStageMax;
     const int nch = L.H / chunk_elems(L.edt), cpl = rows_cpl(nch);
-    if (nch > kWave * cpl && n > kTV) n = kTV;
+    if (nch > kWave * cpl && n > kTVMulti) n = kTVMulti;
     return n;
 }
 
@@ -381,8 +389,8 @@ hipError_t launch_gateup_gemv(const Layer &L, const void *x, const float *tok_sc
     a.I = L.I;
     a.Is = shared_act ? L.Is : 0;
     a.max_routed = act ? (L.E < M * L.k ? L.E : M * L.k) : 0;
-    a.tiles_I = (L.I + kRowsTileGU - 1) / kRowsTileGU;
-    a.tiles_Is = (a.Is + kRowsTileGU - 1) / kRowsTileGU;
+    a.tiles_I = (L.I + gu_rows_tile(L.edt) - 1) / gu_rows_tile(L.edt);
+    a.tiles_Is = (a.Is + gu_rows_tile(L.edt) - 1) / gu_rows_tile(L.edt);
     a.limit = L.limit;
     a.act = act;
     a.shared_act = shared_act;
@@ -433,6 +441,7 @@ __global__ __launch_bounds__(kThreads) void k_down_rows(RowsDown a) {
     extern __shared__ __attribute__((aligned(16))) float s_act[]; // [ncap][KS] fp32
     constexpr int N = Chunk<WDT>::N;
     constexpr int NG = dn_rows_per_wave<WDT>() / RP;
+    constexpr int kTV = tokens_per_pass<CPL>();
     using Loads = DownLoads<WDT, CPL, RP>;
     const int tid = threadIdx.x, lane = tid & 63, wave = uniform(tid >> 6);
     const int H = a.H;
