@@ -703,6 +703,19 @@ __device__ __forceinline__ M1Slots m1_slots(const M1Route &rt, int lane, int *my
     return s;
 }
 
+// Where element i of a one-token act row of `width` elements is stored.  The
+// row is cut into chunks of N elements (one down-kernel lane's share) and the
+// chunks into blocks of 64; a block is stored piece-major: the first four
+// floats of each of its chunks, then the next four, and so on.  A wave of the
+// down kernel, one chunk a lane, then reads each 16-byte piece of its chunks
+// from contiguous memory instead of 64 bytes apart.
+template <int N>
+__device__ __forceinline__ int m1_act_index(int i, int width) {
+    const int c = i / N, j = i - c * N;
+    const int blk = c >> 6, bw = min(64, width / N - (blk << 6));
+    return blk * 64 * N + (j >> 2) * bw * 4 + (c & 63) * 4 + (j & 3);
+}
+
 struct M1GateUpArgs {
     const void *x;
     const float *tok_scale;
@@ -872,8 +885,8 @@ __global__ __launch_bounds__(kThreads) void k_gateup_m1(M1GateUpArgs a) {
             }
             if (lane == 0 && p + r < p_end) {
                 const float h = silu_mul(g, v);
-                if (slot[r] >= 0) a.act[(size_t)slot[r] * a.I + irow[r]] = h;
-                else a.shared_act[irow[r]] = h;
+                if (slot[r] >= 0) a.act[(size_t)slot[r] * a.I + m1_act_index<N>(irow[r], a.I)] = h;
+                else a.shared_act[m1_act_index<N>(irow[r], a.Is)] = h;
             }
         }
     }
@@ -971,9 +984,11 @@ __global__ __launch_bounds__(kThreads) void k_down_m1(M1DownArgs a) {
                 if constexpr (blocked<WDT>())
                     hs[u][r] = scale_bits<WDT>(s_sc[slot], (size_t)rr * (width / 32) + chunk_block<WDT>(c));
             }
-            const f32x4 *ap = reinterpret_cast<const f32x4 *>(s_act[slot] + c * N);
+            // the chunk's pieces in the act layout of m1_act_index
+            const int blk = c >> 6, bw = min(64, width / N - (blk << 6));
+            const float *ap = s_act[slot] + blk * 64 * N + (c & 63) * 4;
 #pragma unroll
-            for (int n4 = 0; n4 < N / 4; n4++) av[u][n4] = ap[n4];
+            for (int n4 = 0; n4 < N / 4; n4++) av[u][n4] = *reinterpret_cast<const f32x4 *>(ap + n4 * bw * 4);
         }
 #pragma unroll
         for (int u = 0; u < kM1Unroll; u++) {
