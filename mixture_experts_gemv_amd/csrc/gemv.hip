@@ -75,6 +75,17 @@ __device__ __forceinline__ void q8_to_bf16x2(u32x4 v, uint32_t (&o)[8]) {
     }
 }
 
+// Where a row's vector pieces sit when the row is stored piece-major: the row
+// is cut into chunks of P 16-byte pieces (one lane's share of a load) and the
+// chunks into blocks of 64; a block holds piece 0 of each of its chunks, then
+// piece 1, and so on.  A wave reading piece q of 64 consecutive chunks, one
+// chunk a lane, then reads contiguous memory (no LDS bank conflicts, fewest
+// cache lines) instead of P * 16 bytes apart.  Returns the piece index.
+__device__ __forceinline__ int piece_major(int c, int q, int nch, int P) {
+    const int blk = c >> 6, bw = min(64, nch - (blk << 6));
+    return blk * 64 * P + q * bw + (c & 63);
+}
+
 // ------------------------------------------------------------------ gate/up
 struct RowsGateUp {
     const void *x;
@@ -442,6 +453,12 @@ __global__ __launch_bounds__(kThreads) void k_down_rows(RowsDown a) {
     constexpr int N = Chunk<WDT>::N;
     constexpr int NG = dn_rows_per_wave<WDT>() / RP;
     constexpr int kTV = tokens_per_pass<CPL>();
+    // act slices are staged piece-major when a chunk spans 8 pieces (MXFP4;
+    // gpt-oss shape, M = 16: down 71 against 88 us).  With 2 or 4 pieces
+    // (bf16, Q8_0) the scattered staging writes cost more than the strided
+    // reads (DeepSeek-V2-Lite shape: 73 against 71 us), so those stay linear.
+    constexpr int P = N / 4; // 16-byte pieces of act per chunk
+    constexpr bool PM = P >= 8;
     using Loads = DownLoads<WDT, CPL, RP>;
     const int tid = threadIdx.x, lane = tid & 63, wave = uniform(tid >> 6);
     const int H = a.H;
@@ -533,11 +550,11 @@ __global__ __launch_bounds__(kThreads) void k_down_rows(RowsDown a) {
 #pragma unroll
             for (int j = 0; j < kTV; j++) {
                 if (j < nj) {
-                    const f32x4 *ap = reinterpret_cast<const f32x4 *>(s_act + (size_t)(j0 + j) * KS + cl[cc] * N);
+                    const f32x4 *ap = reinterpret_cast<const f32x4 *>(s_act + (size_t)(j0 + j) * KS);
                     float av[N];
 #pragma unroll
                     for (int q4 = 0; q4 < N / 4; q4++) {
-                        const f32x4 v = ap[q4];
+                        const f32x4 v = PM ? ap[piece_major(cl[cc], q4, nch, P)] : ap[cl[cc] * P + q4];
                         av[4 * q4] = v.x; av[4 * q4 + 1] = v.y; av[4 * q4 + 2] = v.z; av[4 * q4 + 3] = v.w;
                     }
 #pragma unroll
@@ -580,7 +597,7 @@ __global__ __launch_bounds__(kThreads) void k_down_rows(RowsDown a) {
         __syncthreads();
         for (int q = tid; q < ns * cpr; q += kThreads) {
             const int j = q / cpr, c = q - j * cpr;
-            reinterpret_cast<f32x4 *>(s_act + (size_t)j * KS)[c] =
+            reinterpret_cast<f32x4 *>(s_act + (size_t)j * KS)[PM ? piece_major(c / P, c % P, nch, P) : c] =
                 reinterpret_cast<const f32x4 *>(vec + (size_t)(s0 + j) * width + k0)[c];
         }
         __syncthreads();
@@ -712,8 +729,7 @@ __device__ __forceinline__ M1Slots m1_slots(const M1Route &rt, int lane, int *my
 template <int N>
 __device__ __forceinline__ int m1_act_index(int i, int width) {
     const int c = i / N, j = i - c * N;
-    const int blk = c >> 6, bw = min(64, width / N - (blk << 6));
-    return blk * 64 * N + (j >> 2) * bw * 4 + (c & 63) * 4 + (j & 3);
+    return piece_major(c, j >> 2, width / N, N / 4) * 4 + (j & 3);
 }
 
 struct M1GateUpArgs {
@@ -985,10 +1001,9 @@ __global__ __launch_bounds__(kThreads) void k_down_m1(M1DownArgs a) {
                     hs[u][r] = scale_bits<WDT>(s_sc[slot], (size_t)rr * (width / 32) + chunk_block<WDT>(c));
             }
             // the chunk's pieces in the act layout of m1_act_index
-            const int blk = c >> 6, bw = min(64, width / N - (blk << 6));
-            const float *ap = s_act[slot] + blk * 64 * N + (c & 63) * 4;
+            const f32x4 *ap = reinterpret_cast<const f32x4 *>(s_act[slot]);
 #pragma unroll
-            for (int n4 = 0; n4 < N / 4; n4++) av[u][n4] = *reinterpret_cast<const f32x4 *>(ap + n4 * bw * 4);
+            for (int n4 = 0; n4 < N / 4; n4++) av[u][n4] = ap[piece_major(c, n4, width / N, N / 4)];
         }
 #pragma unroll
         for (int u = 0; u < kM1Unroll; u++) {
