@@ -331,8 +331,7 @@ __global__ __launch_bounds__(kThreads) void k_gateup_rows(RowsGateUp a) {
         }
     };
 
-    for (int s0 = 0; s0 < n; s0 += a.ncap) {
-        const int ns = min(a.ncap, n - s0);
+    auto stage = [&](int s0, int ns) {
         __syncthreads(); // the previous stage is no longer read
         for (int q = tid; q < ns * cpr; q += kThreads) {
             const int j = q / cpr, c = q - j * cpr;
@@ -341,13 +340,31 @@ __global__ __launch_bounds__(kThreads) void k_gateup_rows(RowsGateUp a) {
                 reinterpret_cast<const u32x4 *>(reinterpret_cast<const char *>(a.x) + (size_t)t * H * XB)[c];
         }
         __syncthreads();
-        // (Issuing the next step's loads before computing the current one
-        // measured slower: the extra registers cost more than the overlap.)
-        for (int st = 0; st < nsteps; st++) {
+    };
+    // (Issuing the next step's loads before computing the current one
+    // measured slower: the extra registers cost more than the overlap.)
+    auto steps = [&](int st0, int s0, int ns) {
+        for (int st = st0; st < nsteps; st++) {
             Loads B;
             load(B, st);
             compute(B, st, s0, ns);
         }
+    };
+    // The first step's weights depend on the expert only, so their loads are
+    // issued before the first stage is copied and overlap it (gpt-oss-shaped
+    // M = 16: Q8_0 gate/up 105.6 against 108.4 us, MXFP4 100.0 against 106.4).
+    const int ns0 = min(a.ncap, n);
+    {
+        Loads B0;
+        if (nsteps > 0) load(B0, 0);
+        stage(0, ns0);
+        if (nsteps > 0) compute(B0, 0, 0, ns0);
+    }
+    steps(1, 0, ns0);
+    for (int s0 = a.ncap; s0 < n; s0 += a.ncap) {
+        const int ns = min(a.ncap, n - s0);
+        stage(s0, ns);
+        steps(0, s0, ns);
     }
 }
 
@@ -592,6 +609,9 @@ __global__ __launch_bounds__(kThreads) void k_down_rows(RowsDown a) {
         }
     };
 
+    // (Issuing the first step's weight loads before the first stage's copy,
+    // as the gate/up kernel does, measured slower here: gpt-oss-shaped M = 16,
+    // MXFP4 down 74.7 against 71.0 us, Q8_0 65.2 against 64.2 us.)
     for (int s0 = 0; s0 < n; s0 += a.ncap) {
         const int ns = min(a.ncap, n - s0);
         __syncthreads();
