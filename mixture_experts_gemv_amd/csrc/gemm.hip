@@ -34,6 +34,7 @@
 // down GEMM, but at an output error of about 1.6e-3 relative L2 against
 // about 2.5e-6 with the split.)
 #include <algorithm>
+#include <cmath>
 
 #include "common.h"
 #include "launch.h"
@@ -45,15 +46,31 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kMB = 4;              // 32-row blocks per wave
 constexpr int kBM = 32 * kMB;       // rows per tile
+constexpr int kMBWide = 5;          // the layer call's wide tiles (bf16 or MXFP4 weights)
+constexpr int kBMWide = 32 * kMBWide;
 constexpr int kBK = 64;            // reduction granularity of K (both kernels need K % 64 == 0)
 constexpr int kLdsRow = kBK + 8;   // bf16 elements per padded LDS row of the register-staged kernel
 constexpr int kGW = 4;
 constexpr int kGThreads = kGW * kWave;
 
 // Rows of the grouped GEMM's tiles for a batch of M tokens: 32 while the
-// experts average at most 32 routes each, else 128.  The stage-wise entry
-// points with fp32 act (register-staged kernel) always use kBM.
-int mfma_tile_rows(const Layer &L, int M) { return (long)M * L.k <= 32L * L.E ? 32 : kBM; }
+// experts average at most 32 routes each; 160 when an expert's expected
+// routes (the mean, plus one standard deviation of a random spread when the
+// layer has several experts) fit one 160-row tile but not one 128-row tile,
+// else 128.  An expert a few routes over 128 otherwise runs a second, nearly
+// empty tile that streams its weights and the whole reduction again
+// (Mixtral-shaped M = 512, 128 routes an expert on average: 811 against
+// 922 us a call; a dense layer at M = 512, exactly four 128-row tiles,
+// keeps 128).  Q8_0 weights keep 128 rows: the down GEMM's three LDS stages
+// of 160 split act rows would not fit.  The stage-wise entry points always
+// use kBM.
+int mfma_tile_rows(const Layer &L, int M) {
+    const long R = (long)M * L.k;
+    if (R <= 32L * L.E) return 32;
+    const double c = (double)R / L.E, hi = c + (L.E > 1 ? std::sqrt(c) : 0.0);
+    if (L.edt != DT_Q8 && hi > kBM && hi <= kBMWide) return kBMWide;
+    return kBM;
+}
 int mfma_tile_rows() { return kBM; }
 
 enum GemmKind { GK_GATEUP = 0, GK_PLAIN = 1 };
@@ -784,7 +801,10 @@ __global__ __launch_bounds__(kGThreads, 2) void k_gemm_reg(GemmArgs a) {
 // 1 Q8_0, 2 MXFP4; a.s0 / a.s1 hold the block scales); fp32 A takes bf16 B only.
 template <int KIND, bool AS, int MB>
 static void launch_lds_b(const GemmArgs &a, int bf, unsigned grid, hipStream_t s) {
-    if (bf == 1) launch_kernel((k_gemm_lds<KIND, AS, MB, 1>), dim3(grid), dim3(kGThreads), 0, s, a);
+    if (bf == 1) {
+        // (run_gemm refuses wide tiles with Q8_0 weights)
+        if constexpr (MB != kMBWide) launch_kernel((k_gemm_lds<KIND, AS, MB, 1>), dim3(grid), dim3(kGThreads), 0, s, a);
+    }
     else if (bf == 2) launch_kernel((k_gemm_lds<KIND, AS, MB, 2>), dim3(grid), dim3(kGThreads), 0, s, a);
     else launch_kernel((k_gemm_lds<KIND, AS, MB, 0>), dim3(grid), dim3(kGThreads), 0, s, a);
 }
@@ -792,6 +812,7 @@ static void launch_lds_b(const GemmArgs &a, int bf, unsigned grid, hipStream_t s
 template <int KIND, bool AS>
 static void launch_lds(const GemmArgs &a, int bf, unsigned grid, hipStream_t s) {
     if (a.tile_rows == 32) launch_lds_b<KIND, AS, 1>(a, bf, grid, s);
+    else if (a.tile_rows == kBMWide) launch_lds_b<KIND, AS, kMBWide>(a, bf, grid, s);
     else launch_lds_b<KIND, AS, kMB>(a, bf, grid, s);
 }
 
@@ -819,7 +840,8 @@ static hipError_t run_gemm(int kind, int a_mode, int bq, GemmArgs &a, hipStream_
         const int pad = (per_tile + 7) / 8 * 8;
         a.units_pad = a.pad_units && (pad - per_tile) * 8 <= per_tile ? pad : per_tile;
         const unsigned grid = (unsigned)((long)a.max_tiles * a.units_pad);
-        if (a.tile_rows != 32 && a.tile_rows != kBM) return hipErrorInvalidValue;
+        if (a.tile_rows != 32 && a.tile_rows != kBM && !(a.tile_rows == kBMWide && bq != 1))
+            return hipErrorInvalidValue;
         if (kind == GK_GATEUP && a_mode == 0) launch_lds<GK_GATEUP, false>(a, bq, grid, s);
         else if (kind == GK_GATEUP && a_mode == 1) launch_lds<GK_GATEUP, true>(a, bq, grid, s);
         else if (kind == GK_PLAIN && a_mode == 1) launch_lds<GK_PLAIN, true>(a, bq, grid, s);
@@ -856,7 +878,7 @@ hipError_t launch_gateup_mfma(const Layer &L, const void *x, const float *tok_sc
     if (act) {
         GemmArgs a{};
         a.tile_rows = tile_rows;
-        a.pad_units = (long)M * L.k >= (long)tile_rows * L.E; // about a full tile an expert, or more
+        a.pad_units = (long)M * L.k >= (long)std::min(tile_rows, kBM) * L.E; // about 128 routes an expert, or more
         a.a = x;
         a.sorted = rt.sorted;
         a.k_route = L.k;
@@ -915,7 +937,7 @@ hipError_t launch_down_mfma(const Layer &L, const float *act, const float *share
         a.E = L.E;
         a.max_tiles = max_tiles;
         a.tile_rows = tile_rows;
-        a.pad_units = (long)M * L.k >= (long)tile_rows * L.E; // about a full tile an expert, or more
+        a.pad_units = (long)M * L.k >= (long)std::min(tile_rows, kBM) * L.E; // about 128 routes an expert, or more
         a.ksplit = down_ksplit(L, M, tile_rows);
         a.slab = (size_t)M * L.k * L.H;
         a.b0 = static_cast<const uint16_t *>(routed.down);

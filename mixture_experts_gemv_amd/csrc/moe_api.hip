@@ -85,11 +85,12 @@ WsLayout layout(const moe_plan *p, int M) {
     w.tiles = take(mfma ? (size_t)(2 + L.E + 2 * w.max_tiles) * 4 : 4 * 3);
     w.act = take(R * L.I * 4);
     w.shared_act = take(L.Is > 0 ? (size_t)M * L.Is * 4 : 0);
-    // (fewer tile rows never give more reduction slices; moe_combine with
+    // (the most reduction slices of the two tile heights; moe_combine with
     // Q8_0 or MXFP4 experts uses the row kernels' slices even when the layer
     // call takes the grouped GEMM)
-    const size_t slices = mfma ? std::max(moe::down_ksplit(L, M, moe::mfma_tile_rows()),
-                                          L.edt != moe::DT_BF16 ? moe::down_gemv_slices(L.I, L.edt) : 1)
+    const size_t slices = mfma ? std::max({moe::down_ksplit(L, M, moe::mfma_tile_rows()),
+                                           moe::down_ksplit(L, M, moe::mfma_tile_rows(L, M)),
+                                           L.edt != moe::DT_BF16 ? moe::down_gemv_slices(L.I, L.edt) : 1})
                                : moe::down_gemv_slices(L.I, L.edt);
     w.y_routes = take(slices * R * L.H * 4);
     w.y_shared = take(L.Is > 0 ? (size_t)(mfma ? 1 : moe::down_gemv_slices(L.Is, L.sdt)) * M * L.H * 4 : 0);

@@ -320,6 +320,13 @@ MFMA_SMALL = [
                                    bias_kind="normal", swiglu_limit=0.5), (3, 33, 100)),
     ("mx4-wide", dict(hidden=576, num_experts=4, top_k=1, expert_inter=704, expert_dtype=MXFP4), (129,)),
     ("mx4-dense", dict(hidden=256, num_experts=1, top_k=1, expert_inter=1088, expert_dtype=MXFP4), (70,)),
+    # about 128 routes an expert: 160-row tiles (M = 512, 560; at 560 some
+    # experts spill into a second, ragged tile) and 128-row tiles (M = 600)
+    ("k2-wide-tiles", dict(hidden=256, num_experts=8, top_k=2, expert_inter=192), (512, 560, 600)),
+    ("mx4-wide-tiles", dict(hidden=256, num_experts=8, top_k=2, expert_inter=192, expert_dtype=MXFP4),
+     (512, 560)),
+    # one expert: a single ragged 160-row tile (M = 150), then 128-row tiles
+    ("dense-tiles", dict(hidden=256, num_experts=1, top_k=1, expert_inter=320), (150, 330)),
 ]
 
 
@@ -514,6 +521,8 @@ FUSED = [
      False, True, True),
     ("mx4-norm-res", dict(hidden=288, num_experts=12, top_k=4, expert_inter=320, rms_eps=1e-6,
                           expert_dtype=MXFP4), (1, 16), 0, True, True, False),
+    ("mfma-wide-tiles-norm-res", dict(hidden=256, num_experts=8, top_k=2, expert_inter=192, rms_eps=1e-6),
+     (512,), 2, True, True, False),
 ]
 
 
