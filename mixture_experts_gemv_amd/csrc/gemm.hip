@@ -54,21 +54,23 @@ constexpr int kGW = 4;
 constexpr int kGThreads = kGW * kWave;
 
 // Rows of the grouped GEMM's tiles for a batch of M tokens: 32 while the
-// experts average at most 32 routes each; 160 when an expert's expected
-// routes (the mean, plus one standard deviation of a random spread when the
-// layer has several experts) fit one 160-row tile but not one 128-row tile,
-// else 128.  An expert a few routes over 128 otherwise runs a second, nearly
-// empty tile that streams its weights and the whole reduction again
-// (Mixtral-shaped M = 512, 128 routes an expert on average: 811 against
-// 922 us a call; a dense layer at M = 512, exactly four 128-row tiles,
-// keeps 128).  Q8_0 weights keep 128 rows: the down GEMM's three LDS stages
-// of 160 split act rows would not fit.  The stage-wise entry points always
-// use kBM.
+// experts average at most 32 routes each.  Otherwise 160 or 128, by the
+// tiles an expert's expected routes need (the mean, plus one standard
+// deviation of a random spread when the layer has several experts): 160
+// when 1.06 times its tile count (a 160-row tile runs 25% more MFMA work on
+// the same weight bytes) is below the 128-row count.  An expert a few routes
+// over a multiple of 128 otherwise runs an extra, nearly empty tile that
+// streams its weights and the whole reduction again (Mixtral-shaped,
+// 128 routes an expert on average at M = 512: 811 against 922 us a call;
+// M = 1024: 1396 against 1461 us; Qwen3-shaped M = 4096: 1019 against
+// 1031 us; a dense layer at M = 512, exactly four 128-row tiles, keeps 128).
+// Q8_0 weights keep 128 rows: the down GEMM's three LDS stages of 160 split
+// act rows would not fit.  The stage-wise entry points always use kBM.
 int mfma_tile_rows(const Layer &L, int M) {
     const long R = (long)M * L.k;
     if (R <= 32L * L.E) return 32;
     const double c = (double)R / L.E, hi = c + (L.E > 1 ? std::sqrt(c) : 0.0);
-    if (L.edt != DT_Q8 && hi > kBM && hi <= kBMWide) return kBMWide;
+    if (L.edt != DT_Q8 && std::ceil(hi / kBMWide) * 1.06 < std::ceil(hi / kBM)) return kBMWide;
     return kBM;
 }
 int mfma_tile_rows() { return kBM; }

@@ -321,12 +321,14 @@ MFMA_SMALL = [
     ("mx4-wide", dict(hidden=576, num_experts=4, top_k=1, expert_inter=704, expert_dtype=MXFP4), (129,)),
     ("mx4-dense", dict(hidden=256, num_experts=1, top_k=1, expert_inter=1088, expert_dtype=MXFP4), (70,)),
     # about 128 routes an expert: 160-row tiles (M = 512, 560; at 560 some
-    # experts spill into a second, ragged tile) and 128-row tiles (M = 600)
-    ("k2-wide-tiles", dict(hidden=256, num_experts=8, top_k=2, expert_inter=192), (512, 560, 600)),
+    # experts spill into a second, ragged tile), 128-row tiles (M = 600) and
+    # two or three 160-row tiles an expert (M = 1100)
+    ("k2-wide-tiles", dict(hidden=256, num_experts=8, top_k=2, expert_inter=192), (512, 560, 600, 1100)),
     ("mx4-wide-tiles", dict(hidden=256, num_experts=8, top_k=2, expert_inter=192, expert_dtype=MXFP4),
      (512, 560)),
-    # one expert: a single ragged 160-row tile (M = 150), then 128-row tiles
-    ("dense-tiles", dict(hidden=256, num_experts=1, top_k=1, expert_inter=320), (150, 330)),
+    # one expert: a single ragged 160-row tile (M = 150), two 160-row tiles
+    # (M = 300), three 128-row tiles (M = 330)
+    ("dense-tiles", dict(hidden=256, num_experts=1, top_k=1, expert_inter=320), (150, 300, 330)),
 ]
 
 
