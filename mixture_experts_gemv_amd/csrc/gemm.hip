@@ -56,9 +56,11 @@ constexpr int kGThreads = kGW * kWave;
 // Rows of the grouped GEMM's tiles for a batch of M tokens, by the routes
 // an expert can be expected to hold (the mean, plus one standard deviation of
 // a random spread when the layer has several experts): 32 up to 32 routes,
-// 64 up to 64 (bf16 and Q8_0 weights; an expert just over 32 routes would
-// otherwise run a second 32-row tile: gpt-oss-shaped Q8_0 M = 256, 378
-// against 398 us a call; Mixtral-shaped M = 128, 557 against 613 us;
+// then 64 and 96 up to 64 and 96 (bf16 and Q8_0 weights; an expert just
+// over 32 routes would otherwise run a second 32-row tile, and one of 65 to
+// 96 routes a 128-row tile a quarter or more empty: gpt-oss-shaped Q8_0
+// M = 256, 378 against 398 us a call, M = 512, 466 against 582 us;
+// Mixtral-shaped M = 128, 557 against 613 us, M = 256, 626 against 680 us;
 // Qwen3-shaped M = 512, 291 against 321 us.  MXFP4 keeps 32 rows while the
 // mean is at most 32: its down GEMM there gains more from the padded
 // XCD-grouped order, 357 against 363 us at gpt-oss-shaped M = 256).  Beyond
@@ -77,6 +79,7 @@ int mfma_tile_rows(const Layer &L, int M) {
     const double c = (double)R / L.E, hi = c + (L.E > 1 ? std::sqrt(c) : 0.0);
     if (L.edt == DT_MX4 ? R <= 32L * L.E : hi <= 32) return 32;
     if (L.edt != DT_MX4 && hi <= 64) return 64;
+    if (L.edt != DT_MX4 && hi <= 96) return 96;
     if (L.edt != DT_Q8 && std::ceil(hi / kBMWide) * 1.06 < std::ceil(hi / kBM)) return kBMWide;
     return kBM;
 }
@@ -105,7 +108,7 @@ struct GemmArgs {
     float *out;              // fp32 [rows][ldo]; gate/up with out_split: hi/lo bf16 rows (below)
     int ldo;
     int out_split;           // gate/up: write act as interleaved bf16 hi/lo (the split A of down)
-    int tile_rows;           // rows per tile of the LDS kernel (32, 64, 128 or 160; the tile list's)
+    int tile_rows;           // rows per tile of the LDS kernel (32, 64, 96, 128 or 160; the tile list's)
     int n_ntiles;            // column tiles
     int units_pad;           // LDS kernel: workgroups per token tile (>= n_ntiles * ksplit; the extra ones idle)
     int pad_units;           // caller's request: pad the units for the XCD-grouped order (see run_gemm)
@@ -822,6 +825,7 @@ template <int KIND, bool AS>
 static void launch_lds(const GemmArgs &a, int bf, unsigned grid, hipStream_t s) {
     if (a.tile_rows == 32) launch_lds_b<KIND, AS, 1>(a, bf, grid, s);
     else if (a.tile_rows == 64) launch_lds_b<KIND, AS, 2>(a, bf, grid, s);
+    else if (a.tile_rows == 96) launch_lds_b<KIND, AS, 3>(a, bf, grid, s);
     else if (a.tile_rows == kBMWide) launch_lds_b<KIND, AS, kMBWide>(a, bf, grid, s);
     else launch_lds_b<KIND, AS, kMB>(a, bf, grid, s);
 }
@@ -850,7 +854,7 @@ static hipError_t run_gemm(int kind, int a_mode, int bq, GemmArgs &a, hipStream_
         const int pad = (per_tile + 7) / 8 * 8;
         a.units_pad = a.pad_units && (pad - per_tile) * 8 <= per_tile ? pad : per_tile;
         const unsigned grid = (unsigned)((long)a.max_tiles * a.units_pad);
-        if (a.tile_rows != 32 && a.tile_rows != 64 && a.tile_rows != kBM && !(a.tile_rows == kBMWide && bq != 1))
+        if (a.tile_rows != 32 && a.tile_rows != 64 && a.tile_rows != 96 && a.tile_rows != kBM && !(a.tile_rows == kBMWide && bq != 1))
             return hipErrorInvalidValue;
         if (kind == GK_GATEUP && a_mode == 0) launch_lds<GK_GATEUP, false>(a, bq, grid, s);
         else if (kind == GK_GATEUP && a_mode == 1) launch_lds<GK_GATEUP, true>(a, bq, grid, s);

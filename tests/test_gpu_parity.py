@@ -300,7 +300,7 @@ def test_forward_small(name, kw, Ms):
 
 
 MFMA_SMALL = [
-    ("k2", dict(hidden=256, num_experts=8, top_k=2, expert_inter=192), (64, 70, 200)),
+    ("k2", dict(hidden=256, num_experts=8, top_k=2, expert_inter=192), (64, 70, 200, 300)),
     ("bias-clamp", dict(hidden=128, num_experts=6, top_k=3, expert_inter=128, bias_mode=BIAS_LOGIT,
                         bias_kind="normal", swiglu_limit=0.3), (65, 130)),
     ("all-shared", dict(hidden=192, num_experts=16, top_k=6, expert_inter=64, shared_inter=320,
@@ -308,7 +308,7 @@ MFMA_SMALL = [
     ("zipf-rms", dict(hidden=256, num_experts=64, top_k=8, expert_inter=128, bias_mode=BIAS_LOGIT,
                       bias_kind="zipf", rms_eps=1e-6), (1, 257)),
     ("wide-n", dict(hidden=128, num_experts=4, top_k=1, expert_inter=576), (129,)),
-    ("q8", dict(hidden=256, num_experts=8, top_k=2, expert_inter=192, expert_dtype=Q8_0), (16, 70, 200)),
+    ("q8", dict(hidden=256, num_experts=8, top_k=2, expert_inter=192, expert_dtype=Q8_0), (16, 70, 200, 300)),
     ("q8-shared-bias-clamp", dict(hidden=192, num_experts=16, top_k=4, expert_inter=128, shared_inter=256,
                                   expert_dtype=Q8_0, shared_dtype=Q8_0, bias_mode=BIAS_LOGIT,
                                   bias_kind="normal", swiglu_limit=0.5), (3, 33, 100)),
