@@ -56,14 +56,14 @@ constexpr int kGThreads = kGW * kWave;
 // Rows of the grouped GEMM's tiles for a batch of M tokens, by the routes
 // an expert can be expected to hold (the mean, plus one standard deviation of
 // a random spread when the layer has several experts): 32 up to 32 routes,
-// then 64 and 96 up to 64 and 96 (bf16 and Q8_0 weights; an expert just
-// over 32 routes would otherwise run a second 32-row tile, and one of 65 to
-// 96 routes a 128-row tile a quarter or more empty: gpt-oss-shaped Q8_0
-// M = 256, 378 against 398 us a call, M = 512, 466 against 582 us;
-// Mixtral-shaped M = 128, 557 against 613 us, M = 256, 626 against 680 us;
-// Qwen3-shaped M = 512, 291 against 321 us.  MXFP4 keeps 32 rows while the
-// mean is at most 32: its down GEMM there gains more from the padded
-// XCD-grouped order, 357 against 363 us at gpt-oss-shaped M = 256).  Beyond
+// then 64 and 96 up to 64 and 96.  An expert just over 32 routes would
+// otherwise run a second 32-row tile, and one of 33 to 96 routes a 128-row
+// tile a quarter or more empty (gpt-oss-shaped Q8_0 M = 256, 378 against
+// 398 us a call, M = 512, 466 against 582 us; MXFP4 M = 384, 375 against
+// 660 us, M = 512, 578 against 673 us; Mixtral-shaped M = 128, 557 against
+// 613 us, M = 256, 626 against 680 us; Qwen3-shaped M = 512, 291 against
+// 321 us).  MXFP4 keeps 32 rows while the mean is at most 32 (gpt-oss shape,
+// M = 256: 357 against 363 us with 64-row tiles, from the down GEMM).  Beyond
 // that 160 or 128 rows: 160 when 1.06 times its tile count (a 160-row tile
 // runs 25% more MFMA work on the same weight bytes) is below the 128-row
 // count.  An expert a few routes
@@ -78,8 +78,8 @@ int mfma_tile_rows(const Layer &L, int M) {
     const long R = (long)M * L.k;
     const double c = (double)R / L.E, hi = c + (L.E > 1 ? std::sqrt(c) : 0.0);
     if (L.edt == DT_MX4 ? R <= 32L * L.E : hi <= 32) return 32;
-    if (L.edt != DT_MX4 && hi <= 64) return 64;
-    if (L.edt != DT_MX4 && hi <= 96) return 96;
+    if (hi <= 64) return 64;
+    if (hi <= 96) return 96;
     if (L.edt != DT_Q8 && std::ceil(hi / kBMWide) * 1.06 < std::ceil(hi / kBM)) return kBMWide;
     return kBM;
 }

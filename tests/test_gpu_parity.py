@@ -314,7 +314,7 @@ MFMA_SMALL = [
                                   bias_kind="normal", swiglu_limit=0.5), (3, 33, 100)),
     ("sigmoid-e64", dict(hidden=256, num_experts=64, top_k=8, expert_inter=128, select=SIGMOID_NORM,
                          bias_mode=BIAS_SELECT_ONLY, bias_kind="normal", bias_std=0.05), (1, 70)),
-    ("mx4", dict(hidden=256, num_experts=8, top_k=2, expert_inter=192, expert_dtype=MXFP4), (16, 70, 200)),
+    ("mx4", dict(hidden=256, num_experts=8, top_k=2, expert_inter=192, expert_dtype=MXFP4), (16, 70, 200, 300)),
     ("mx4-shared-bias-clamp", dict(hidden=192, num_experts=16, top_k=4, expert_inter=128, shared_inter=256,
                                    expert_dtype=MXFP4, shared_dtype=MXFP4, bias_mode=BIAS_LOGIT,
                                    bias_kind="normal", swiglu_limit=0.5), (3, 33, 100)),
