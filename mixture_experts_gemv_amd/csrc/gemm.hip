@@ -60,10 +60,12 @@ constexpr int kGThreads = kGW * kWave;
 // otherwise run a second 32-row tile, and one of 33 to 96 routes a 128-row
 // tile a quarter or more empty (gpt-oss-shaped Q8_0 M = 256, 378 against
 // 398 us a call, M = 512, 466 against 582 us; MXFP4 M = 384, 375 against
-// 660 us, M = 512, 578 against 673 us; Mixtral-shaped M = 128, 557 against
-// 613 us, M = 256, 626 against 680 us; Qwen3-shaped M = 512, 291 against
-// 321 us).  MXFP4 keeps 32 rows while the mean is at most 32 (gpt-oss shape,
-// M = 256: 357 against 363 us with 64-row tiles, from the down GEMM).  Beyond
+// 660 us; Mixtral-shaped M = 128, 557 against 613 us, M = 256, 626 against
+// 680 us; Qwen3-shaped M = 512, 291 against 321 us).  MXFP4 keeps 32 rows
+// while the mean is at most 32 (gpt-oss shape, M = 256: 357 against 363 us
+// with 64-row tiles, from the down GEMM) and takes two 64-row tiles rather
+// than one of 96 (M = 512: 499 against 579 us; Q8_0 there: 530 against
+// 469 us, so bf16 and Q8_0 keep 96).  Beyond
 // that 160 or 128 rows: 160 when 1.06 times its tile count (a 160-row tile
 // runs 25% more MFMA work on the same weight bytes) is below the 128-row
 // count.  An expert a few routes
@@ -79,7 +81,7 @@ int mfma_tile_rows(const Layer &L, int M) {
     const double c = (double)R / L.E, hi = c + (L.E > 1 ? std::sqrt(c) : 0.0);
     if (L.edt == DT_MX4 ? R <= 32L * L.E : hi <= 32) return 32;
     if (hi <= 64) return 64;
-    if (hi <= 96) return 96;
+    if (hi <= 96) return L.edt == DT_MX4 ? 64 : 96;
     if (L.edt != DT_Q8 && std::ceil(hi / kBMWide) * 1.06 < std::ceil(hi / kBM)) return kBMWide;
     return kBM;
 }
