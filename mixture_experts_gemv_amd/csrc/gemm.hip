@@ -46,7 +46,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kMB = 4;              // 32-row blocks per wave
 constexpr int kBM = 32 * kMB;       // rows per tile
-constexpr int kMBWide = 5;          // the layer call's wide tiles (bf16 or MXFP4 weights)
+constexpr int kMBWide = 5;          // the layer call's wide tiles (bf16 weights)
 constexpr int kBMWide = 32 * kMBWide;
 constexpr int kBK = 64;            // reduction granularity of K (both kernels need K % 64 == 0)
 constexpr int kLdsRow = kBK + 8;   // bf16 elements per padded LDS row of the register-staged kernel
@@ -63,10 +63,12 @@ constexpr int kGThreads = kGW * kWave;
 // 660 us; Mixtral-shaped M = 128, 557 against 613 us, M = 256, 626 against
 // 680 us; Qwen3-shaped M = 512, 291 against 321 us).  MXFP4 keeps 32 rows
 // while the mean is at most 32 (gpt-oss shape, M = 256: 357 against 363 us
-// with 64-row tiles, from the down GEMM) and takes two 64-row tiles rather
-// than one of 96 (M = 512: 499 against 579 us; Q8_0 there: 530 against
-// 469 us, so bf16 and Q8_0 keep 96).  Beyond
-// that 160 or 128 rows: 160 when 1.06 times its tile count (a 160-row tile
+// with 64-row tiles, from the down GEMM) and otherwise always takes 64-row
+// tiles, several an expert if need be (M = 512: 499 against 579 us with
+// 96-row tiles; M = 768, 611 against 837 us, and M = 1024, 684 against
+// 996 us with 128- and 160-row tiles; Q8_0 at M = 512 the other way round:
+// 530 against 469 us, so bf16 and Q8_0 keep 96).  Beyond 96 routes bf16
+// takes 160 or 128 rows: 160 when 1.06 times its tile count (a 160-row tile
 // runs 25% more MFMA work on the same weight bytes) is below the 128-row
 // count.  An expert a few routes
 // over a multiple of 128 otherwise runs an extra, nearly empty tile that
@@ -80,9 +82,9 @@ int mfma_tile_rows(const Layer &L, int M) {
     const long R = (long)M * L.k;
     const double c = (double)R / L.E, hi = c + (L.E > 1 ? std::sqrt(c) : 0.0);
     if (L.edt == DT_MX4 ? R <= 32L * L.E : hi <= 32) return 32;
-    if (hi <= 64) return 64;
-    if (hi <= 96) return L.edt == DT_MX4 ? 64 : 96;
-    if (L.edt != DT_Q8 && std::ceil(hi / kBMWide) * 1.06 < std::ceil(hi / kBM)) return kBMWide;
+    if (hi <= 64 || L.edt == DT_MX4) return 64;
+    if (hi <= 96) return 96;
+    if (L.edt == DT_BF16 && std::ceil(hi / kBMWide) * 1.06 < std::ceil(hi / kBM)) return kBMWide;
     return kBM;
 }
 int mfma_tile_rows() { return kBM; }
