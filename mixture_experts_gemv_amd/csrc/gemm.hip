@@ -68,9 +68,11 @@ constexpr int kGThreads = kGW * kWave;
 // 96-row tiles; M = 768, 611 against 837 us, and M = 1024, 684 against
 // 996 us with 128- and 160-row tiles; Q8_0 at M = 512 the other way round:
 // 530 against 469 us, so bf16 and Q8_0 keep 96).  Beyond 96 routes bf16
-// takes 160 or 128 rows: 160 when 1.06 times its tile count (a 160-row tile
-// runs 25% more MFMA work on the same weight bytes) is below the 128-row
-// count.  An expert a few routes
+// and Q8_0 take the height of least estimated cost among 96, 128 and (bf16)
+// 160 rows: tiles times their MFMA-weighted size, which picks the 96-row
+// tile when it needs no more tiles than 128 rows (gpt-oss-shaped Q8_0
+// M = 1024: 861 against 981 us; M = 768, one 128-row tile: 661 against
+// 748 us) and 160 over 128 when it saves a tile.  An expert a few routes
 // over a multiple of 128 otherwise runs an extra, nearly empty tile that
 // streams its weights and the whole reduction again (Mixtral-shaped,
 // 128 routes an expert on average at M = 512: 811 against 922 us a call;
@@ -84,8 +86,20 @@ int mfma_tile_rows(const Layer &L, int M) {
     if (L.edt == DT_MX4 ? R <= 32L * L.E : hi <= 32) return 32;
     if (hi <= 64 || L.edt == DT_MX4) return 64;
     if (hi <= 96) return 96;
-    if (L.edt == DT_BF16 && std::ceil(hi / kBMWide) * 1.06 < std::ceil(hi / kBM)) return kBMWide;
-    return kBM;
+    // the height of least estimated cost: tiles times (1 + 0.316 rows / 128),
+    // a tile's weight stream plus MFMA work growing with its rows (0.316
+    // puts a 160-row tile at 1.06 times a 128-row one)
+    int best = kBM;
+    double best_cost = 1e300;
+    for (const int bm : {96, kBM, kBMWide}) {
+        if (bm == kBMWide && L.edt != DT_BF16) continue;
+        const double cost = std::ceil(hi / bm) * (1.0 + 0.316 * bm / kBM);
+        if (cost < best_cost) {
+            best_cost = cost;
+            best = bm;
+        }
+    }
+    return best;
 }
 int mfma_tile_rows() { return kBM; }
 

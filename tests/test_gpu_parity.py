@@ -308,7 +308,7 @@ MFMA_SMALL = [
     ("zipf-rms", dict(hidden=256, num_experts=64, top_k=8, expert_inter=128, bias_mode=BIAS_LOGIT,
                       bias_kind="zipf", rms_eps=1e-6), (1, 257)),
     ("wide-n", dict(hidden=128, num_experts=4, top_k=1, expert_inter=576), (129,)),
-    ("q8", dict(hidden=256, num_experts=8, top_k=2, expert_inter=192, expert_dtype=Q8_0), (16, 70, 200, 300)),
+    ("q8", dict(hidden=256, num_experts=8, top_k=2, expert_inter=192, expert_dtype=Q8_0), (16, 70, 200, 300, 520)),
     ("q8-shared-bias-clamp", dict(hidden=192, num_experts=16, top_k=4, expert_inter=128, shared_inter=256,
                                   expert_dtype=Q8_0, shared_dtype=Q8_0, bias_mode=BIAS_LOGIT,
                                   bias_kind="normal", swiglu_limit=0.5), (3, 33, 100)),
