@@ -13,9 +13,10 @@
 // converted exactly to bf16 in registers; each block's products are scaled
 // once).  (The router has its own small-tile kernel at the end of this file.)
 //
-// Tiles: 128 rows (tokens or routes of one expert, so that most experts'
-// tokens share one pass over the weights), or 32 rows when a batch gives the
-// experts few routes each (less MFMA and LDS work on empty rows), x 128
+// Tiles: 32, 64, 96, 128 or 160 rows (tokens or routes of one expert), by
+// the routes an expert is expected to hold (mfma_tile_rows below), so that
+// most experts' tokens share one pass over the weights without running
+// tiles that are mostly empty rows, x 128
 // (gate/up: 32 columns of gate and of up per wave) or 256 (down: 64 columns
 // per wave) output columns.  Four waves each own all rows of their columns
 // and issue v_mfma_f32_32x32x16_bf16.

@@ -84,6 +84,8 @@ def lib():
         L.orc_forward_fused.argtypes = [ctypes.POINTER(_Layer), ctypes.c_int] + [P] * 18
         L.orc_forward.restype = ctypes.c_int
         L.orc_select.argtypes = [ctypes.POINTER(_Layer), ctypes.c_int, P, P, P, P, P]
+        L.orc_route.argtypes = [ctypes.POINTER(_Layer), ctypes.c_int] + [P] * 7
+        L.orc_route.restype = ctypes.c_int
         L.orc_permute.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, P, P, P, P, P]
         L.orc_element.argtypes = [P, ctypes.c_int, ctypes.c_longlong, ctypes.c_longlong,
                                   ctypes.c_longlong]
@@ -143,6 +145,26 @@ def forward(spec, layer: Dict[str, Optional[np.ndarray]], x: np.ndarray,
         raise ValueError("oracle refused the layer shape")
     if want_act:
         out["act"] = act
+    return out
+
+
+def route(spec, layer: Dict[str, Optional[np.ndarray]], x: np.ndarray,
+          norm_w: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
+    """The routing half of :func:`forward` for every token of ``x [M][H]``:
+    logits, ids and w, as ``forward`` computes them (no expert work)."""
+    M = x.shape[0]
+    E, k = spec.num_experts, spec.top_k
+    out = {"logits": np.zeros((M, E), np.float64), "ids": np.zeros((M, k), np.int32),
+           "w": np.zeros((M, k), np.float64)}
+    bias = layer.get("bias")
+    bias = None if bias is None else np.ascontiguousarray(bias, np.float32)
+    nw = None if norm_w is None else np.ascontiguousarray(norm_w)
+    st = layer_struct(spec)
+    rc = lib().orc_route(ctypes.byref(st), M, _ptr(np.ascontiguousarray(x)), _ptr(nw),
+                         _ptr(layer["router"]), _ptr(bias), _ptr(out["logits"]), _ptr(out["ids"]),
+                         _ptr(out["w"]))
+    if rc != 0:
+        raise ValueError("oracle refused the layer shape")
     return out
 
 

@@ -16,8 +16,8 @@
  *       gptoss/state.rs, RealGptOssState.router_bias.
  *   selection       top-k of the (biased) logits, then either
  *       - softmax over the selected k: gptoss/state.rs,
- *         RealGptOssState.per_expert_ones (the per-expert weighting is a
- *         no-op, so selection reduces to softmax over the selected), or
+ *         RealGptOssState.per_expert_ones (unit per-expert weights change
+ *         nothing, so the weights are a softmax restricted to the k), or
  *       - softmax over all experts, then top-k with NO renormalisation:
  *         deepseek2/state.rs module doc (decoder-layer sketch), or
  *       - sigmoid scores: llama/state.rs, RealLlamaState::build (the
@@ -63,6 +63,7 @@
  * mistakes; it is 0 (off) unless a test sets it.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -386,6 +387,10 @@ static double orc_clamp(double v, double lim)
 void orc_swiglu_act(int H, int width, int fmt, double limit, const void *gate, const void *up,
                     int mat, const double *xn, double *act)
 {
+    /* rows are independent; spread them over the threads when the caller's
+       token loop is not itself parallel (each row's dot is the same serial
+       sum either way) */
+#pragma omp parallel for schedule(static) if (!omp_in_parallel() && (long)width * H >= (1L << 18))
     for (int i = 0; i < width; i++) {
         size_t row = (size_t)mat * width + i;
         double g = orc_row_dot(gate, fmt, row, H, xn);
@@ -411,6 +416,7 @@ void orc_swiglu_act(int H, int width, int fmt, double limit, const void *gate, c
 
 void orc_down(int H, int width, int fmt, const void *down, int mat, const double *act, double *out)
 {
+#pragma omp parallel for schedule(static) if (!omp_in_parallel() && (long)width * H >= (1L << 18))
     for (int h = 0; h < H; h++) {
         if (orc_mutant == MUT_DOWN_TRANSPOSED && fmt != ORC_Q8_0 && fmt != ORC_MXFP4) {
             /* read element (h, i) at flat index i*H + h of the expert's block */
@@ -473,7 +479,9 @@ int orc_forward_fused(const orc_layer *L, int M, const void *x, const void *norm
     }
     orc_select(L, M, logits, bias, forced_ids, ids, w);
 
-#pragma omp parallel for schedule(dynamic, 1)
+    /* tokens in parallel when there are enough of them; otherwise the expert
+       rows of each token are (orc_swiglu_act, orc_down) */
+#pragma omp parallel for schedule(dynamic, 1) if (M >= omp_get_max_threads())
     for (int t = 0; t < M; t++) {
         const double *xt = xn + (size_t)t * H;
         double *yt = y + (size_t)t * H;
@@ -534,6 +542,33 @@ int orc_forward(const orc_layer *L, int M, const void *x, const void *router, co
                              forced_ids, logits_out, ids_out, w_out, counts_out, act_out, y);
 }
 
+/* The routing half alone, for every token: the (normed, weighted) rows,
+ * the logits, the selection and its weights, computed exactly as
+ * orc_forward_fused computes them (steps 0-4).  Lets a test check every
+ * token's selection and the per-expert counts of a batch whose expert work
+ * is too slow to run whole.  norm_w as in orc_forward_fused; logits may be
+ * NULL. */
+int orc_route(const orc_layer *L, int M, const void *x, const void *norm_w, const void *router,
+              const float *bias, double *logits_out, int32_t *ids, double *w)
+{
+    const int H = L->hidden, E = L->num_experts;
+    if (M < 0 || H <= 0 || E <= 0 || L->top_k <= 0 || L->top_k > E)
+        return 1;
+    if (norm_w && !(L->rms_eps > 0.0))
+        return 1;
+    if (M == 0)
+        return 0;
+    double *xn = malloc(sizeof(double) * (size_t)M * H);
+    double *logits = logits_out ? logits_out : malloc(sizeof(double) * (size_t)M * E);
+    norm_tokens(L, M, x, norm_w, xn);
+    orc_router_logits(L, M, xn, router, logits);
+    orc_select(L, M, logits, bias, NULL, ids, w);
+    if (!logits_out)
+        free(logits);
+    free(xn);
+    return 0;
+}
+
 /* Expose the element reader so tests can check the format decoding against
  * independent closed forms. */
 double orc_element(const void *base, int fmt, long long r, long long cols, long long c)
@@ -544,10 +579,5 @@ double orc_element(const void *base, int fmt, long long r, long long cols, long 
 /* Thread count OpenMP would use (for the CPU-baseline report). */
 int orc_threads(void)
 {
-#ifdef _OPENMP
-    extern int omp_get_max_threads(void);
     return omp_get_max_threads();
-#else
-    return 1;
-#endif
 }

@@ -52,8 +52,13 @@ def device_layer(spec, layer, max_tokens, path=0):
     return dl
 
 
-def selection_keys(spec, layer, x, norm_w=None):
-    """fp64 selection keys s[t][e] and the near-tie bound tau[t]."""
+def selection_keys(spec, layer, x, norm_w=None, split=False):
+    """fp64 selection keys s[t][e] and the near-tie bound tau[t].
+
+    ``split``: the router read the weighted normed rows as bf16 hi + lo (the
+    grouped-GEMM path of moe_forward_fused with a norm weight), which holds
+    each value to 2^-18 of itself and so adds 2^-18 * A to the bound; every
+    other path reads fp32 rows and keeps the plain bound."""
     xf = dequant(x, spec.x_dtype, x.shape[0], spec.hidden)
     if spec.rms_eps > 0:
         xf = xf / np.sqrt(np.mean(xf * xf, axis=1, keepdims=True) + spec.rms_eps)
@@ -64,9 +69,7 @@ def selection_keys(spec, layer, x, norm_w=None):
     b = np.zeros(spec.num_experts) if layer.get("bias") is None else layer["bias"].astype(np.float64)
     A = np.abs(xf) @ np.abs(wr).T + (np.abs(b) if spec.bias_mode != 0 else 0.0)
     tau = TAU_REL * A.max(axis=1)
-    if norm_w is not None:
-        # the weighted normed rows reach the grouped-GEMM router as bf16 hi + lo,
-        # which holds each value to 2^-18 of itself: that adds 2^-18 * A
+    if split and norm_w is not None:
         tau = tau + SPLIT_REL * A.max(axis=1)
     if spec.select == SIGMOID_NORM:
         # key sigmoid(l) + b: sigmoid' <= 1/4 carries the logit bound over, and
@@ -76,7 +79,7 @@ def selection_keys(spec, layer, x, norm_w=None):
     return s, tau
 
 
-def check_ids(spec, layer, x, gpu_ids, ora_ids, norm_w=None):
+def check_ids(spec, layer, x, gpu_ids, ora_ids, norm_w=None, split=False):
     """Apply the near-tie rule; return (forced ids for the oracle, number of near-tie tokens).
 
     Tokens whose k-th and (k+1)-th fp64 keys are further apart than tau must get
@@ -84,7 +87,7 @@ def check_ids(spec, layer, x, gpu_ids, ora_ids, norm_w=None):
     every expert whose key clears the boundary by more than tau and draw the
     rest from keys within tau of it; the oracle is then re-run on the GPU's set.
     """
-    s, tau = selection_keys(spec, layer, x, norm_w)
+    s, tau = selection_keys(spec, layer, x, norm_w, split)
     return check_ids_keys(s, tau, spec.top_k, gpu_ids, ora_ids)
 
 
@@ -147,34 +150,57 @@ def run_forward(dl, x_host, M=None, fused=None):
     return y.cpu().numpy(), ids.cpu().numpy(), w.cpu().numpy(), counts.cpu().numpy()
 
 
+def hot_expert_sample(ids, E, stride=32):
+    """Tokens routed to the most-loaded expert, one every ``stride`` of its
+    routes in sorted (token-ascending) order, and its last: with ``stride`` the
+    smallest grouped-GEMM tile height (32 rows), every tile of that expert
+    holds one of them."""
+    counts = np.bincount(ids.reshape(-1), minlength=E)
+    hot = int(np.argmax(counts))
+    toks = np.nonzero((ids == hot).any(axis=1))[0]
+    pick = list(toks[::stride]) + ([toks[-1]] if len(toks) else [])
+    return np.asarray(pick, dtype=np.int64), hot, int(counts[hot])
+
+
 def forward_parity(spec, layer, x, dl, sample=None, what="", fused=None):
-    """Whole-layer parity: ids (near-tie rule), counts, w and y against the oracle
-    (fused: as run_forward; the oracle takes the same norm weight and residual)."""
+    """Whole-layer parity against the oracle (fused: as run_forward; the
+    oracle takes the same norm weight and residual).
+
+    Every token's expert set is checked under the near-tie rule and the
+    per-expert counts must equal those of the oracle's selection (with the
+    GPU's set forced on near-tie tokens), over the whole batch.  Weights and
+    y are compared on ``sample`` (all tokens when None), which is widened with
+    tokens in every tile of the most-loaded expert."""
+    import mixture_experts_gemv_amd as m
     y, ids, w, counts = run_forward(dl, x, fused=fused)
-    if sample is None:
-        sample = np.arange(x.shape[0])
-    xs = np.ascontiguousarray(x[sample])
-    norm_w = res = None
+    M = x.shape[0]
+    norm_w = res_all = None
     if fused is not None:
         norm_w = fused[0]
-        res = None if fused[1] is None else np.ascontiguousarray(fused[1][sample], np.float32)
-    o = oracle.forward(spec, layer, xs, norm_w=norm_w, residual=res)
-    forced, near = check_ids(spec, layer, xs, ids[sample], o["ids"], norm_w)
-    if near:
-        o = oracle.forward(spec, layer, xs, forced_ids=forced, norm_w=norm_w, residual=res)
-    if len(sample) == x.shape[0]:
-        full_forced = forced
-        assert np.array_equal(counts, np.bincount(ids.reshape(-1), minlength=spec.num_experts))
-        assert np.array_equal(counts, np.bincount(full_forced.reshape(-1), minlength=spec.num_experts)), \
-            "per-expert counts differ from the oracle's"
+        res_all = fused[1]
+    # (the grouped-GEMM router takes the weighted normed rows as bf16 hi + lo)
+    split = (m.moe_forward_path(dl.plan, M) == m.MOE_RUN_NAMES.index("mfma")
+             and spec.router_dtype == synth.BF16)
+    # the selection of every token
+    r = oracle.route(spec, layer, x, norm_w=norm_w)
+    forced, near = check_ids(spec, layer, x, ids, r["ids"], norm_w, split)
+    want_counts = np.bincount(forced.reshape(-1), minlength=spec.num_experts)
+    assert np.array_equal(counts, want_counts), "per-expert counts differ from the oracle's"
+    if sample is None:
+        sample = np.arange(M)
     else:
-        assert counts.sum() == x.shape[0] * spec.top_k
-        assert np.array_equal(counts, np.bincount(ids.reshape(-1), minlength=spec.num_experts))
+        hot_tokens, hot, hot_n = hot_expert_sample(forced, spec.num_experts)
+        sample = np.unique(np.concatenate([np.asarray(sample, np.int64), hot_tokens]))
+        say(f"{what}: y sampled on {len(sample)} tokens (expert {hot} holds {hot_n} routes)")
+    xs = np.ascontiguousarray(x[sample])
+    res = None if res_all is None else np.ascontiguousarray(res_all[sample], np.float32)
+    o = oracle.forward(spec, layer, xs, forced_ids=np.ascontiguousarray(forced[sample]), norm_w=norm_w,
+                       residual=res)
     # weights, matched by expert id
     for i, t in enumerate(sample):
         for j in range(spec.top_k):
             e = ids[t, j]
             jj = list(o["ids"][i]).index(e)
             assert abs(w[t, j] - o["w"][i, jj]) <= W_ABS, f"{what}: weight token {t} expert {e}"
-    ma, rel = check_y(y[sample], o["y"], what=f"{what} (near-tie tokens: {near})")
+    ma, rel = check_y(y[sample], o["y"], what=f"{what} (near-tie tokens: {near} of {M})")
     return dict(max_abs=ma, rel_l2=rel, near_ties=near, ids=ids, counts=counts)

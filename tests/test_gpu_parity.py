@@ -308,7 +308,10 @@ MFMA_SMALL = [
     ("zipf-rms", dict(hidden=256, num_experts=64, top_k=8, expert_inter=128, bias_mode=BIAS_LOGIT,
                       bias_kind="zipf", rms_eps=1e-6), (1, 257)),
     ("wide-n", dict(hidden=128, num_experts=4, top_k=1, expert_inter=576), (129,)),
-    ("q8", dict(hidden=256, num_experts=8, top_k=2, expert_inter=192, expert_dtype=Q8_0), (16, 70, 200, 300, 520)),
+    # Q8_0 at 32-, 64-, 96- and (M = 400: about 110 expected routes an
+    # expert) 128-row tiles
+    ("q8", dict(hidden=256, num_experts=8, top_k=2, expert_inter=192, expert_dtype=Q8_0),
+     (16, 70, 200, 300, 400, 520)),
     ("q8-shared-bias-clamp", dict(hidden=192, num_experts=16, top_k=4, expert_inter=128, shared_inter=256,
                                   expert_dtype=Q8_0, shared_dtype=Q8_0, bias_mode=BIAS_LOGIT,
                                   bias_kind="normal", swiglu_limit=0.5), (3, 33, 100)),
@@ -321,9 +324,10 @@ MFMA_SMALL = [
     ("mx4-wide", dict(hidden=576, num_experts=4, top_k=1, expert_inter=704, expert_dtype=MXFP4), (129,)),
     ("mx4-dense", dict(hidden=256, num_experts=1, top_k=1, expert_inter=1088, expert_dtype=MXFP4), (70,)),
     # about 128 routes an expert: 160-row tiles (M = 512, 560; at 560 some
-    # experts spill into a second, ragged tile), 128-row tiles (M = 600) and
-    # two or three 160-row tiles an expert (M = 1100)
+    # experts spill into a second, ragged tile), two 96-row tiles an expert
+    # (M = 600) and two or three 160-row tiles an expert (M = 1100)
     ("k2-wide-tiles", dict(hidden=256, num_experts=8, top_k=2, expert_inter=192), (512, 560, 600, 1100)),
+    # MXFP4 beyond 32 routes an expert: several 64-row tiles an expert
     ("mx4-wide-tiles", dict(hidden=256, num_experts=8, top_k=2, expert_inter=192, expert_dtype=MXFP4),
      (512, 560)),
     # one expert: a single ragged 160-row tile (M = 150), two 160-row tiles
