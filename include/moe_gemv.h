@@ -218,6 +218,22 @@ moe_status moe_forward(const moe_plan *plan, const void *x, const moe_weights *w
                        float *y, int32_t *ids_out, float *w_out, int32_t *counts_out, void *ws,
                        size_t ws_bytes, void *stream);
 
+/* moe_forward without a workspace argument, for callers that cannot
+ * allocate device memory (code under graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  The kernels use a static scratch array
+ * of the library (32 MiB of device memory on each GPU the library runs on,
+ * held until the process ends) in place of `ws`; the call allocates
+ * nothing.  MOE_ERR_WORKSPACE when moe_workspace_bytes(plan, M) exceeds
+ * 32 MiB (then call moe_forward with a workspace).  The first call on a
+ * device looks the array up and zeroes its reserved counter words on
+ * `stream`.  Every call on one GPU shares that GPU's array: calls that
+ * overlap on one GPU (concurrent streams, or threads) race and must be
+ * serialised by the caller, as calls sharing one workspace must.  Other
+ * arguments and results as moe_forward. */
+moe_status moe_forward_noalloc(const moe_plan *plan, const void *x, const moe_weights *wts, int32_t M,
+                               float *y, int32_t *ids_out, float *w_out, int32_t *counts_out,
+                               void *stream);
+
 /* The layer with its neighbours fused (deepseek2/state.rs, module doc: the
  * post-attention RMSNorm with its weight, rms_norm(x, post_attention_layernorm),
  * feeds the router and the experts, and the routed sum plus the shared

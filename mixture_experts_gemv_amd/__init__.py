@@ -78,6 +78,7 @@ def lib() -> ctypes.CDLL:
         L.moe_combine.argtypes = [P, P, W, I32, P, P, P, P, P, P, P, SZ, P]
         L.moe_forward.argtypes = [P, P, W, I32, P, P, P, P, P, SZ, P]
         L.moe_forward_fused.argtypes = [P, P, P, P, W, I32, P, P, P, P, P, SZ, P]
+        L.moe_forward_noalloc.argtypes = [P, P, W, I32, P, P, P, P, P]
         L.moe_forward_timed.argtypes = [P, P, W, I32, P, P, P, P, P, SZ, P,
                                         ctypes.POINTER(P), I32, P, ctypes.POINTER(I32)]
         L.moe_q8_0_split.argtypes = [P, ctypes.c_int64, I32, P, P, P]
@@ -87,6 +88,7 @@ def lib() -> ctypes.CDLL:
         L.moe_forward_path.argtypes = [P, I32]
         L.moe_forward_path.restype = I32
         for f in ("moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_forward", "moe_forward_fused",
+                  "moe_forward_noalloc",
                   "moe_forward_timed", "moe_q8_0_split", "moe_mxfp4_split"):
             getattr(L, f).restype = I32
         _lib = L
@@ -200,6 +202,11 @@ def moe_forward(plan, x, weights, M, y, ids_out, w_out, counts_out, ws, stream=N
     _check(lib().moe_forward(plan.handle, _ptr(x), ctypes.byref(weights), M, _ptr(y),
                              _ptr(ids_out), _ptr(w_out), _ptr(counts_out), _ptr(ws), _nbytes(ws),
                              _stream(stream)))
+
+
+def moe_forward_noalloc(plan, x, weights, M, y, ids_out, w_out, counts_out, stream=None):
+    _check(lib().moe_forward_noalloc(plan.handle, _ptr(x), ctypes.byref(weights), M, _ptr(y),
+                                     _ptr(ids_out), _ptr(w_out), _ptr(counts_out), _stream(stream)))
 
 
 def moe_forward_fused(plan, x, norm_weight, residual, weights, M, y, ids_out, w_out, counts_out, ws,

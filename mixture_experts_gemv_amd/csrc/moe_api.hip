@@ -5,6 +5,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <string>
 
 #include "common.h"
@@ -183,6 +184,43 @@ moe_status check_router(const moe_plan *p, const moe_weights *w, bool need_route
     return MOE_OK;
 }
 
+} // namespace
+
+// ------------------------------------------------------------ static scratch
+// The workspace of moe_forward_noalloc: one array in device memory per GPU,
+// held until the process ends, for callers that cannot allocate.  In host
+// code `scratch` names a host-side stand-in, not device memory: kernels and
+// copies take the device address hipGetSymbolAddress gives for the current
+// device, looked up once per device and kept in g_scratch.
+constexpr size_t kScratchBytes = size_t(32) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch[kMaxDevices];
+
+// Device address of the current device's scratch.  The first lookup on a
+// device also enqueues the zeroing of the reserved counter words on
+// `stream` (a kernel, so that a capturing caller records no memset node).
+moe_status device_scratch(hipStream_t stream, void **out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices) return fail(MOE_ERR_UNSUPPORTED, "device ordinal %d beyond %d", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        void *ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+        if (!ptr || !aligned(ptr, kAlign)) return fail(MOE_ERR_HIP, "static scratch has no usable device address");
+        e = moe::launch_zero_words(reinterpret_cast<uint32_t *>(ptr), (int)(kSyncBytes / 4), stream);
+        if (e != hipSuccess) return hip_fail(e, "scratch init");
+        g_scratch[dev] = ptr;
+    }
+    *out = g_scratch[dev];
+    return MOE_OK;
+}
 } // namespace
 
 namespace moe {
@@ -518,6 +556,23 @@ moe_status moe_forward(const moe_plan *p, const void *x, const moe_weights *wts,
                        size_t ws_bytes, void *stream) {
     Recorder rec;
     return forward_impl(p, x, wts, M, y, ids_out, w_out, counts_out, ws, ws_bytes, (hipStream_t)stream, rec);
+}
+
+moe_status moe_forward_noalloc(const moe_plan *p, const void *x, const moe_weights *wts, int32_t M,
+                               float *y, int32_t *ids_out, float *w_out, int32_t *counts_out,
+                               void *stream) {
+    if (!p) return fail(MOE_ERR_INVALID, "plan is NULL");
+    if (M < 0 || M > p->cfg.max_tokens)
+        return fail(MOE_ERR_INVALID, "M = %d outside 0..max_tokens (%d)", M, p->cfg.max_tokens);
+    if (M == 0) return MOE_OK;
+    const size_t need = layout(p, M).total;
+    if (need > kScratchBytes)
+        return fail(MOE_ERR_WORKSPACE, "M = %d needs %zu bytes of workspace; the static scratch holds %zu "
+                    "(call moe_forward with a workspace)", M, need, kScratchBytes);
+    void *ws = nullptr;
+    TRY(device_scratch((hipStream_t)stream, &ws));
+    Recorder rec;
+    return forward_impl(p, x, wts, M, y, ids_out, w_out, counts_out, ws, kScratchBytes, (hipStream_t)stream, rec);
 }
 
 moe_status moe_forward_fused(const moe_plan *p, const void *x, const void *norm_weight,
