@@ -299,11 +299,11 @@ def measure_point(spec, M: int, args, want_cpu: bool) -> dict:
     kernel = GATEUP_KERNEL[m.MOE_RUN_NAMES[run]]
     tag = f"{spec.name}_M{M}"
     trec = profiling.load_traffic(os.path.join(ROOT, "profiles"), kernel, tag)
+    flops = algorithmic_flops(spec, M)
     gateup_us = per_stage.get("gateup")
     gateup_flops = M * spec.top_k * 4 * spec.hidden * spec.expert_inter + M * 4 * spec.hidden * spec.shared_inter
     achieved = gateup_bytes_avg / (gateup_us * 1e-6) / 1e9
     layer_gbs = layer_bytes_avg / (ms_per_step * 1e-3) / 1e9
-    flops = algorithmic_flops(spec, M)
     point = {
         "workload": (f"{spec.name}-shaped dense SwiGLU layer (one expert, top-1), M={M} tokens per call"
                      if spec.num_experts == 1 else

@@ -53,12 +53,7 @@
  *    MOE_ERR_HIP reports a failed kernel launch; work enqueued before it may
  *    have run.
  *  - Workspace: `ws` must hold moe_workspace_bytes(plan, M) bytes, 256-byte
- *    aligned, and must be initialised once (moe_workspace_init, or zero-filled)
- *    before its first use: its first 256 bytes are reserved for counters with
- *    which the workgroups of one kernel could elect a last finisher (none of
- *    the current kernels uses them; a call that completes leaves them zero).
- *    The rest of the workspace carries nothing between calls.  After
- *    MOE_ERR_HIP, initialise it again.
+ *    aligned.  It needs no initialisation and carries nothing between calls.
  *    Calls that share one workspace must be ordered on one stream; calls on
  *    different streams need different workspaces.
  *  - M = 0 is a no-op returning MOE_OK.
@@ -162,11 +157,6 @@ void moe_plan_destroy(moe_plan *plan);
  * pre-norm on hold room for moe_forward_fused's normed rows. */
 size_t moe_workspace_bytes(const moe_plan *plan, int32_t M);
 
-/* Zero the reserved counter words of a workspace (one small kernel on
- * `stream`).  Call once after allocating a workspace, and again after a
- * MOE_ERR_HIP. */
-moe_status moe_workspace_init(const moe_plan *plan, void *ws, size_t ws_bytes, void *stream);
-
 /* Text of the last non-OK status returned on the calling thread. */
 const char *moe_last_error(void);
 
@@ -225,8 +215,8 @@ moe_status moe_forward(const moe_plan *plan, const void *x, const moe_weights *w
  * held until the process ends) in place of `ws`; the call allocates
  * nothing.  MOE_ERR_WORKSPACE when moe_workspace_bytes(plan, M) exceeds
  * 32 MiB (then call moe_forward with a workspace).  The first call on a
- * device looks the array up and zeroes its reserved counter words on
- * `stream`.  Every call on one GPU shares that GPU's array: calls that
+ * device looks the array's device address up.  Every call on one GPU shares
+ * that GPU's array: calls that
  * overlap on one GPU (concurrent streams, or threads) race and must be
  * serialised by the caller, as calls sharing one workspace must.  Other
  * arguments and results as moe_forward. */

@@ -83,8 +83,6 @@ def lib() -> ctypes.CDLL:
                                         ctypes.POINTER(P), I32, P, ctypes.POINTER(I32)]
         L.moe_q8_0_split.argtypes = [P, ctypes.c_int64, I32, P, P, P]
         L.moe_mxfp4_split.argtypes = [P, ctypes.c_int64, I32, P, P, P]
-        L.moe_workspace_init.argtypes = [P, P, SZ, P]
-        L.moe_workspace_init.restype = I32
         L.moe_forward_path.argtypes = [P, I32]
         L.moe_forward_path.restype = I32
         for f in ("moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_forward", "moe_forward_fused",
@@ -164,10 +162,6 @@ def moe_plan_destroy(plan: Plan) -> None:
 
 def moe_workspace_bytes(plan: Plan, M: int) -> int:
     return int(lib().moe_workspace_bytes(plan.handle, M))
-
-
-def moe_workspace_init(plan, ws, stream=None):
-    _check(lib().moe_workspace_init(plan.handle, _ptr(ws), _nbytes(ws), _stream(stream)))
 
 
 def moe_last_error() -> str:

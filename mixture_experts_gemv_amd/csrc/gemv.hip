@@ -56,12 +56,6 @@ constexpr int kStageBytes = 64 * 1024;   // LDS for staged vectors, per workgrou
 constexpr int kMx4RowsGU = 2;
 constexpr int kMx4RowsDN = 2;
 
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c,
-                                           false);
-}
 
 // The 16 int8 of a Q8_0 chunk as 8 words of bf16 pairs (exact: |q| <= 127).
 __device__ __forceinline__ void q8_to_bf16x2(u32x4 v, uint32_t (&o)[8]) {
@@ -75,16 +69,6 @@ __device__ __forceinline__ void q8_to_bf16x2(u32x4 v, uint32_t (&o)[8]) {
     }
 }
 
-// Where a row's vector pieces sit when the row is stored piece-major: the row
-// is cut into chunks of P 16-byte pieces (one lane's share of a load) and the
-// chunks into blocks of 64; a block holds piece 0 of each of its chunks, then
-// piece 1, and so on.  A wave reading piece q of 64 consecutive chunks, one
-// chunk a lane, then reads contiguous memory (no LDS bank conflicts, fewest
-// cache lines) instead of P * 16 bytes apart.  Returns the piece index.
-__device__ __forceinline__ int piece_major(int c, int q, int nch, int P) {
-    const int blk = c >> 6, bw = min(64, nch - (blk << 6));
-    return blk * 64 * P + q * bw + (c & 63);
-}
 
 // ------------------------------------------------------------------ gate/up
 struct RowsGateUp {
@@ -738,18 +722,6 @@ __device__ __forceinline__ M1Slots m1_slots(const M1Route &rt, int lane, int *my
     for (int j = 0; j < rt.k; j++)
         s.set(__builtin_amdgcn_readlane(*my_rank, j), __builtin_amdgcn_readlane(*my_id, j));
     return s;
-}
-
-// Where element i of a one-token act row of `width` elements is stored.  The
-// row is cut into chunks of N elements (one down-kernel lane's share) and the
-// chunks into blocks of 64; a block is stored piece-major: the first four
-// floats of each of its chunks, then the next four, and so on.  A wave of the
-// down kernel, one chunk a lane, then reads each 16-byte piece of its chunks
-// from contiguous memory instead of 64 bytes apart.
-template <int N>
-__device__ __forceinline__ int m1_act_index(int i, int width) {
-    const int c = i / N, j = i - c * N;
-    return piece_major(c, j >> 2, width / N, N / 4) * 4 + (j & 3);
 }
 
 struct M1GateUpArgs {

@@ -48,7 +48,6 @@ hipError_t launch_route_small(const Layer &L, const void *x, const void *router,
                               const float *tok_scale, int M, float *logits, int32_t *ids, float *w,
                               int32_t *counts, int32_t *offsets, int32_t *sorted, int32_t *route_pos,
                               int32_t *active, hipStream_t s);
-hipError_t launch_zero_words(uint32_t *p, int n, hipStream_t s);
 // Derive the active-expert list and the tile list from offsets alone.
 hipError_t launch_plan_from_offsets(int E, int tile_rows, const int32_t *offsets, int32_t *active,
                                     int32_t *tiles, hipStream_t s);

@@ -39,12 +39,11 @@ moe_status hip_fail(hipError_t e, const char *what) {
 bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 constexpr size_t kAlign = 256;
-constexpr size_t kSyncBytes = 256; // reserved counter words at the start of every workspace
 size_t up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 // Where each workspace region starts for a call with M tokens.
 struct WsLayout {
-    size_t sync, tok_scale, logits, ids, w, counts, offsets, sorted, route_pos, active, tiles;
+    size_t tok_scale, logits, ids, w, counts, offsets, sorted, route_pos, active, tiles;
     size_t act, shared_act, y_routes, y_shared, xn, xs, total;
     int max_tiles;
 };
@@ -69,7 +68,6 @@ WsLayout layout(const moe_plan *p, int M) {
     WsLayout w{};
     size_t o = 0;
     auto take = [&](size_t bytes) { size_t at = o; o += up(bytes); return at; };
-    w.sync = take(kSyncBytes);
     w.tok_scale = take(L.eps > 0.f ? (size_t)M * 4 : 0);
     w.logits = take((size_t)M * L.E * 4);
     w.ids = take(R * 4);
@@ -200,10 +198,9 @@ constexpr int kMaxDevices = 64;
 std::mutex g_scratch_mu;
 void *g_scratch[kMaxDevices];
 
-// Device address of the current device's scratch.  The first lookup on a
-// device also enqueues the zeroing of the reserved counter words on
-// `stream` (a kernel, so that a capturing caller records no memset node).
-moe_status device_scratch(hipStream_t stream, void **out) {
+// Device address of the current device's scratch (looked up on the first
+// call on each device).
+moe_status device_scratch(void **out) {
     int dev = -1;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
@@ -214,8 +211,6 @@ moe_status device_scratch(hipStream_t stream, void **out) {
         e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
         if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
         if (!ptr || !aligned(ptr, kAlign)) return fail(MOE_ERR_HIP, "static scratch has no usable device address");
-        e = moe::launch_zero_words(reinterpret_cast<uint32_t *>(ptr), (int)(kSyncBytes / 4), stream);
-        if (e != hipSuccess) return hip_fail(e, "scratch init");
         g_scratch[dev] = ptr;
     }
     *out = g_scratch[dev];
@@ -570,7 +565,7 @@ moe_status moe_forward_noalloc(const moe_plan *p, const void *x, const moe_weigh
         return fail(MOE_ERR_WORKSPACE, "M = %d needs %zu bytes of workspace; the static scratch holds %zu "
                     "(call moe_forward with a workspace)", M, need, kScratchBytes);
     void *ws = nullptr;
-    TRY(device_scratch((hipStream_t)stream, &ws));
+    TRY(device_scratch(&ws));
     Recorder rec;
     return forward_impl(p, x, wts, M, y, ids_out, w_out, counts_out, ws, kScratchBytes, (hipStream_t)stream, rec);
 }
@@ -607,16 +602,6 @@ int32_t moe_forward_path(const moe_plan *p, int32_t M) {
         return fail(MOE_ERR_INVALID, "M = %d outside [1, %d]", M, p->cfg.max_tokens), -1;
     if (use_mfma(p, M)) return MOE_RUN_MFMA;
     return M == 1 && moe::m1_supported(p->L) ? MOE_RUN_SINGLE : MOE_RUN_GEMV;
-}
-
-moe_status moe_workspace_init(const moe_plan *p, void *ws, size_t ws_bytes, void *stream) {
-    if (!p) return fail(MOE_ERR_INVALID, "plan is NULL");
-    if (ws_bytes == 0) return MOE_OK;
-    if (ws_bytes < kSyncBytes) return fail(MOE_ERR_WORKSPACE, "workspace smaller than %zu bytes", kSyncBytes);
-    TRY(need_ptr(ws, kAlign, "workspace"));
-    LAUNCH(moe::launch_zero_words(reinterpret_cast<uint32_t *>(ws), (int)(kSyncBytes / 4), (hipStream_t)stream),
-           "workspace init");
-    return MOE_OK;
 }
 
 moe_status moe_q8_0_split(const void *blocks, int64_t rows, int32_t cols, int8_t *qs,

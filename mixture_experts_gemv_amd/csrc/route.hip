@@ -542,15 +542,4 @@ hipError_t launch_router_small(const Layer &L, const void *x, const void *router
     return hipGetLastError();
 }
 
-// Zero `n` 32-bit words (the workspace's reserved synchronisation words).
-__global__ void k_zero_words(uint32_t *p, int n) {
-    const int i = blockIdx.x * 256 + threadIdx.x;
-    if (i < n) p[i] = 0u;
-}
-
-hipError_t launch_zero_words(uint32_t *p, int n, hipStream_t s) {
-    launch_kernel(k_zero_words, dim3((n + 255) / 256), dim3(256), 0, s, p, n);
-    return hipGetLastError();
-}
-
 } // namespace moe

