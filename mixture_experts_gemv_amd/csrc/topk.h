@@ -89,12 +89,17 @@ __device__ inline void topk_wave_vals(const float (&lv)[kKeysPerLane], const flo
 __device__ inline void topk_wave_core(const float *lrow, const float *bias, int E, int k, int select,
                                       int bias_mode, int lane, int *id, float *wt) {
     float lv[kKeysPerLane], bv[kKeysPerLane];
-    // all loads first (clamped index, masked in the selection) so they overlap
+    // all loads first (clamped index, masked in the selection) so they
+    // overlap; groups of 64 past E load nothing (every wave of a grid may run
+    // this on the same row, so each load is a hot cache line)
 #pragma unroll
     for (int c = 0; c < kKeysPerLane; c++) {
-        const int e = min(lane + kWave * c, E - 1);
-        lv[c] = lrow[e];
-        bv[c] = bias ? bias[e] : 0.f;
+        lv[c] = bv[c] = 0.f;
+        if (kWave * c < E) {
+            const int e = min(lane + kWave * c, E - 1);
+            lv[c] = lrow[e];
+            bv[c] = bias ? bias[e] : 0.f;
+        }
     }
     topk_wave_vals(lv, bv, E, k, select, bias_mode, lane, id, wt);
 }
