@@ -47,6 +47,8 @@ MUTANTS = {
     22: "MXFP4 reads the next block's scale",
     23: "norm weight applied to the router input only",
     24: "residual stream not added",
+    25: "router input scale ignored",
+    26: "router input scale applied to the experts too",
 }
 
 
@@ -81,10 +83,10 @@ def lib():
         L = ctypes.CDLL(_LIB)
         P = ctypes.c_void_p
         L.orc_forward.argtypes = [ctypes.POINTER(_Layer), ctypes.c_int] + [P] * 16
-        L.orc_forward_fused.argtypes = [ctypes.POINTER(_Layer), ctypes.c_int] + [P] * 18
+        L.orc_forward_fused.argtypes = [ctypes.POINTER(_Layer), ctypes.c_int] + [P] * 19
         L.orc_forward.restype = ctypes.c_int
         L.orc_select.argtypes = [ctypes.POINTER(_Layer), ctypes.c_int, P, P, P, P, P]
-        L.orc_route.argtypes = [ctypes.POINTER(_Layer), ctypes.c_int] + [P] * 7
+        L.orc_route.argtypes = [ctypes.POINTER(_Layer), ctypes.c_int] + [P] * 8
         L.orc_route.restype = ctypes.c_int
         L.orc_permute.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, P, P, P, P, P]
         L.orc_element.argtypes = [P, ctypes.c_int, ctypes.c_longlong, ctypes.c_longlong,
@@ -117,7 +119,9 @@ def forward(spec, layer: Dict[str, Optional[np.ndarray]], x: np.ndarray,
     """Run the whole layer on ``x [M][H]``; returns logits, ids, w, counts, y (and act).
 
     ``norm_w`` (``[H]`` in the x storage format) weights the RMS pre-norm
-    (needs ``spec.rms_eps > 0``); ``residual`` (``[M][H]`` fp32) is added to y."""
+    (needs ``spec.rms_eps > 0``); ``residual`` (``[M][H]`` fp32) is added to y.
+    ``layer["router_x_scale"]`` (bf16 bits ``[H]``, optional) scales the
+    router's input element by element."""
     M = x.shape[0]
     E, k, H, I = spec.num_experts, spec.top_k, spec.hidden, spec.expert_inter
     out = {
@@ -134,9 +138,11 @@ def forward(spec, layer: Dict[str, Optional[np.ndarray]], x: np.ndarray,
     st = layer_struct(spec)
     nw = None if norm_w is None else np.ascontiguousarray(norm_w)
     res = None if residual is None else np.ascontiguousarray(residual, np.float32)
+    rxs = layer.get("router_x_scale")
+    rxs = None if rxs is None else np.ascontiguousarray(rxs, np.uint16)
     rc = lib().orc_forward_fused(
         ctypes.byref(st), M, _ptr(np.ascontiguousarray(x)), _ptr(nw), _ptr(res),
-        _ptr(layer["router"]), _ptr(bias),
+        _ptr(layer["router"]), _ptr(rxs), _ptr(bias),
         _ptr(layer["gate"]), _ptr(layer["up"]), _ptr(layer["down"]),
         _ptr(layer.get("shared_gate")), _ptr(layer.get("shared_up")),
         _ptr(layer.get("shared_down")), _ptr(fids), _ptr(out["logits"]), _ptr(out["ids"]),
@@ -159,10 +165,12 @@ def route(spec, layer: Dict[str, Optional[np.ndarray]], x: np.ndarray,
     bias = layer.get("bias")
     bias = None if bias is None else np.ascontiguousarray(bias, np.float32)
     nw = None if norm_w is None else np.ascontiguousarray(norm_w)
+    rxs = layer.get("router_x_scale")
+    rxs = None if rxs is None else np.ascontiguousarray(rxs, np.uint16)
     st = layer_struct(spec)
     rc = lib().orc_route(ctypes.byref(st), M, _ptr(np.ascontiguousarray(x)), _ptr(nw),
-                         _ptr(layer["router"]), _ptr(bias), _ptr(out["logits"]), _ptr(out["ids"]),
-                         _ptr(out["w"]))
+                         _ptr(layer["router"]), _ptr(rxs), _ptr(bias), _ptr(out["logits"]),
+                         _ptr(out["ids"]), _ptr(out["w"]))
     if rc != 0:
         raise ValueError("oracle refused the layer shape")
     return out

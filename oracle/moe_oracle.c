@@ -8,10 +8,12 @@
  *
  * What it computes, and where the turbospark-runtime 0.3.0 pages state it:
  *
- *   router logits   l[t][e] = sum_i x[t][i] * Wr[e][i]
+ *   router logits   l[t][e] = sum_i x[t][i] * s[i] * Wr[e][i]
  *       llama/state.rs, RealLlamaState.router_logits_f32 (fp32 logits, one
  *       [num_experts] row per token) and deepseek2/state.rs module doc
- *       ("f @ router").
+ *       ("f @ router").  s is the INT8 router's per-element input scale
+ *       (llama/state.rs, RealLlamaState.router_ones; ones when absent) and
+ *       Wr may be Q8_0 blocks (the INT8 router's rows).
  *   router bias     added to the logits BEFORE top-k
  *       gptoss/state.rs, RealGptOssState.router_bias.
  *   selection       top-k of the (biased) logits, then either
@@ -107,7 +109,9 @@ enum {
     MUT_MX_NEXT_BLOCK_SCALE = 22,   /* MXFP4: the next block's scale */
     MUT_NORM_WEIGHT_ROUTER_ONLY = 23, /* fused norm: the experts see the unit-gain rows */
     MUT_RESIDUAL_DROPPED = 24,      /* fused: the residual stream is not added */
-    MUT_COUNT = 25
+    MUT_ROUTER_SCALE_IGNORED = 25,  /* INT8 router: the input scale is not applied */
+    MUT_ROUTER_SCALE_ON_EXPERTS = 26, /* INT8 router: the input scale also reaches the experts */
+    MUT_COUNT = 27
 };
 static int orc_mutant = MUT_NONE;
 
@@ -227,15 +231,25 @@ void orc_norm_tokens(const orc_layer *L, int M, const void *x, double *xn)
     norm_tokens(L, M, x, NULL, xn);
 }
 
-/* ---- step 1: router logits ---- */
+/* ---- step 1: router logits ----
+ * l[t][e] = sum_i (xn[t][i] * xs[i]) * Wr[e][i], xs the router's input scale
+ * (bf16 [H], or NULL for ones): the INT8 router kernel of llama/state.rs
+ * (RealLlamaState.router_ones) scales each element of its input by an
+ * effective scale, identically 1 where the architecture has no router scale
+ * (gptoss/state.rs and deepseek2/state.rs, router_ones).  The router rows
+ * may be Q8_0 blocks like the experts' (the INT8 router's weights). */
 void orc_router_logits(const orc_layer *L, int M, const double *xn, const void *router,
-                       double *logits)
+                       const uint16_t *xs, double *logits)
 {
     const int H = L->hidden, E = L->num_experts;
+    double *xr = malloc(sizeof(double) * (size_t)M * H);
+    for (size_t i = 0; i < (size_t)M * H; i++)
+        xr[i] = (xs && orc_mutant != MUT_ROUTER_SCALE_IGNORED) ? xn[i] * orc_bf16(xs[i % H]) : xn[i];
 #pragma omp parallel for collapse(2) schedule(static)
     for (int t = 0; t < M; t++)
         for (int e = 0; e < E; e++)
-            logits[(size_t)t * E + e] = orc_row_dot(router, L->router_fmt, e, H, xn + (size_t)t * H);
+            logits[(size_t)t * E + e] = orc_row_dot(router, L->router_fmt, e, H, xr + (size_t)t * H);
+    free(xr);
 }
 
 /* ---- steps 2-4: bias, top-k, weights for one token ----
@@ -443,10 +457,12 @@ void orc_down(int H, int width, int fmt, const void *down, int mat, const double
  *   y_t = residual_t + shared(f_t) + sum_j w_j expert_j(f_t),
  *   f_t = x_t / sqrt(mean(x_t^2) + eps) * norm_w.
  * norm_w ([H] in the x format) needs rms_eps > 0 (else the call is refused);
- * residual ([M][H] fp32) or NULL for zeros.  orc_forward is the case
- * norm_w = residual = NULL. */
+ * residual ([M][H] fp32) or NULL for zeros; router_xs (bf16 [H]) or NULL:
+ * the router's input scale (step 1).  orc_forward is the case
+ * norm_w = residual = router_xs = NULL. */
 int orc_forward_fused(const orc_layer *L, int M, const void *x, const void *norm_w,
-                      const float *residual, const void *router, const float *bias, const void *gate,
+                      const float *residual, const void *router, const uint16_t *router_xs,
+                      const float *bias, const void *gate,
                       const void *up, const void *down, const void *sgate, const void *sup,
                       const void *sdown, const int32_t *forced_ids, double *logits_out,
                       int32_t *ids_out, double *w_out, int32_t *counts_out, double *act_out, double *y)
@@ -466,17 +482,20 @@ int orc_forward_fused(const orc_layer *L, int M, const void *x, const void *norm
     norm_tokens(L, M, x, norm_w, xn);
     if (orc_mutant == MUT_NORM_ROUTER_ONLY) {
         /* the router sees the normed rows, the experts the raw ones */
-        orc_router_logits(L, M, xn, router, logits);
+        orc_router_logits(L, M, xn, router, router_xs, logits);
         orc_layer raw = *L;
         raw.rms_eps = 0.0;
         norm_tokens(&raw, M, x, NULL, xn);
     } else if (orc_mutant == MUT_NORM_WEIGHT_ROUTER_ONLY) {
         /* the router sees the weighted rows, the experts the unit-gain ones */
-        orc_router_logits(L, M, xn, router, logits);
+        orc_router_logits(L, M, xn, router, router_xs, logits);
         norm_tokens(L, M, x, NULL, xn);
     } else {
-        orc_router_logits(L, M, xn, router, logits);
+        orc_router_logits(L, M, xn, router, router_xs, logits);
     }
+    if (orc_mutant == MUT_ROUTER_SCALE_ON_EXPERTS && router_xs)
+        for (size_t i = 0; i < (size_t)M * H; i++)
+            xn[i] *= orc_bf16(router_xs[i % H]);
     orc_select(L, M, logits, bias, forced_ids, ids, w);
 
     /* tokens in parallel when there are enough of them; otherwise the expert
@@ -538,18 +557,18 @@ int orc_forward(const orc_layer *L, int M, const void *x, const void *router, co
                 const void *sup, const void *sdown, const int32_t *forced_ids, double *logits_out,
                 int32_t *ids_out, double *w_out, int32_t *counts_out, double *act_out, double *y)
 {
-    return orc_forward_fused(L, M, x, NULL, NULL, router, bias, gate, up, down, sgate, sup, sdown,
+    return orc_forward_fused(L, M, x, NULL, NULL, router, NULL, bias, gate, up, down, sgate, sup, sdown,
                              forced_ids, logits_out, ids_out, w_out, counts_out, act_out, y);
 }
 
 /* The routing half alone, for every token: the (normed, weighted) rows,
  * the logits, the selection and its weights, computed exactly as
- * orc_forward_fused computes them (steps 0-4).  Lets a test check every
+ * orc_forward_fused computes them (steps 0-4; router_xs as there).  Lets a test check every
  * token's selection and the per-expert counts of a batch whose expert work
  * is too slow to run whole.  norm_w as in orc_forward_fused; logits may be
  * NULL. */
 int orc_route(const orc_layer *L, int M, const void *x, const void *norm_w, const void *router,
-              const float *bias, double *logits_out, int32_t *ids, double *w)
+              const uint16_t *router_xs, const float *bias, double *logits_out, int32_t *ids, double *w)
 {
     const int H = L->hidden, E = L->num_experts;
     if (M < 0 || H <= 0 || E <= 0 || L->top_k <= 0 || L->top_k > E)
@@ -561,7 +580,7 @@ int orc_route(const orc_layer *L, int M, const void *x, const void *norm_w, cons
     double *xn = malloc(sizeof(double) * (size_t)M * H);
     double *logits = logits_out ? logits_out : malloc(sizeof(double) * (size_t)M * E);
     norm_tokens(L, M, x, norm_w, xn);
-    orc_router_logits(L, M, xn, router, logits);
+    orc_router_logits(L, M, xn, router, router_xs, logits);
     orc_select(L, M, logits, bias, NULL, ids, w);
     if (!logits_out)
         free(logits);

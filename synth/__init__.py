@@ -46,7 +46,7 @@ TOPK_SOFTMAX, SOFTMAX_ALL_NORENORM, SIGMOID_NORM = 0, 1, 2
 BIAS_NONE, BIAS_LOGIT, BIAS_SELECT_ONLY = 0, 1, 2
 
 STREAMS = ("x", "router", "bias", "gate", "up", "down", "shared_gate",
-           "shared_up", "shared_down", "zipf_perm", "q8_scale")
+           "shared_up", "shared_down", "zipf_perm", "q8_scale", "router_x_scale")
 
 Q8_BLOCK = 32
 Q8_BYTES = 34
@@ -79,6 +79,7 @@ class LayerSpec:
     q8_scale_hi: float = 1e-3
     mx_exp_lo: int = 118           # MXFP4 scale byte ~ U{lo..hi}: 2^-9 .. 2^-5
     mx_exp_hi: int = 122
+    router_x_scale: str = "none"   # "none" | "uniform": bf16 [H] ~ U[0.5, 1.5], the router's input scale
     seed: int = 1000
     token_counts: tuple = (1,)
 
@@ -122,6 +123,15 @@ SPECS: Dict[str, LayerSpec] = {
         expert_inter=1536, select=SIGMOID_NORM, bias_mode=BIAS_SELECT_ONLY,
         bias_kind="normal", bias_std=0.05, router_dtype=F32, seed=1007,
         token_counts=(1, 16)),
+    # the gpt-oss-20B shape with an INT8 router: Q8_0 router rows and a
+    # per-element bf16 scale of the router's input, the router form of the
+    # pages' INT8 router kernels (the scale drawn U[0.5, 1.5] rather than the
+    # pages' identically-one, so that it matters)
+    "gpt-oss-20b-int8-router": LayerSpec(
+        name="gpt-oss-20b-int8-router", hidden=2880, num_experts=32, top_k=4,
+        expert_inter=2880, bias_mode=BIAS_LOGIT, bias_kind="normal",
+        bias_std=0.1, swiglu_limit=7.0, expert_dtype=Q8_0, router_dtype=Q8_0,
+        router_x_scale="uniform", seed=1009, token_counts=(1, 16, 64)),
     # the gpt-oss-20B shape with its routed experts in MXFP4, the format the
     # pages name for gpt-oss's routed pair (scale bytes 2^-9..2^-5 give weights
     # of about the Q8_0 layer's magnitude)
@@ -256,12 +266,17 @@ def make_layer(spec: LayerSpec) -> Dict[str, Optional[np.ndarray]]:
     H, E, I, Is = spec.hidden, spec.num_experts, spec.expert_inter, spec.shared_inter
     ch = _children(spec.seed)
     # Each scale-bearing tensor takes its own grandchild of the q8_scale stream.
-    sc = dict(zip(("gate", "up", "down", "shared_gate", "shared_up", "shared_down"),
-                  ch["q8_scale"].spawn(6)))
+    sc = dict(zip(("gate", "up", "down", "shared_gate", "shared_up", "shared_down", "router"),
+                  ch["q8_scale"].spawn(7)))
     std, lo, hi = spec.weight_std, spec.q8_scale_lo, spec.q8_scale_hi
     mx = (spec.mx_exp_lo, spec.mx_exp_hi)
     layer: Dict[str, Optional[np.ndarray]] = {}
-    layer["router"] = _draw_matrix(ch["router"], E, H, spec.router_dtype, std, None, lo, hi)
+    layer["router"] = _draw_matrix(ch["router"], E, H, spec.router_dtype, std, sc["router"], lo, hi)
+    if spec.router_x_scale == "uniform":
+        rs = np.random.default_rng(ch["router_x_scale"]).uniform(0.5, 1.5, H).astype(np.float32)
+        layer["router_x_scale"] = bf16_bits(rs)
+    else:
+        layer["router_x_scale"] = None
     if spec.bias_kind == "normal":
         b = np.random.default_rng(ch["bias"]).standard_normal(E, dtype=np.float32)
         b *= np.float32(spec.bias_std)

@@ -664,6 +664,62 @@ def pin_fused_closed_form():
 
 
 # ---------------------------------------------------------------------------
+# P16: the INT8 router (llama/state.rs, RealLlamaState.router_ones: the INT8
+# router kernel scales each input element by an effective scale, identically
+# 1 for the pages' architectures).  The scale acts on the router's input
+# only, so folding it into the router rows gives the same layer (every
+# product below is exact in fp64: bf16 x, bf16 scale, bf16 router); a uniform
+# scale c is a softmax temperature on the selected logits; Q8_0 router rows
+# equal their bf16 image when the block scales are powers of two.
+# ---------------------------------------------------------------------------
+def pin_router_input_scale():
+    spec = _spec(num_experts=6, top_k=2, shared_inter=32, x_dtype=BF16, router_dtype=BF16, seed=41)
+    layer = synth.make_layer(spec)
+    x = synth.make_tokens(spec, 5)
+    rng = np.random.default_rng(41)
+    rs = synth.bf16_bits(rng.uniform(0.5, 1.5, spec.hidden).astype(np.float32))
+    a = oracle.forward(spec, dict(layer, router_x_scale=rs), x)
+    folded = dict(layer)
+    w = synth.bf16_to_f32(layer["router"]).astype(np.float64) * synth.bf16_to_f32(rs).astype(np.float64)
+    folded["router"] = w.astype(np.float32)
+    assert np.array_equal(folded["router"].astype(np.float64), w), "bf16 x bf16 must be fp32-exact"
+    b = oracle.forward(spec.replace(router_dtype=F32), folded, x)
+    assert np.array_equal(a["ids"], b["ids"]), "input scale vs folded router: ids"
+    assert np.array_equal(a["logits"], b["logits"]), "input scale vs folded router: logits"
+    assert np.array_equal(a["y"], b["y"]), "the router's input scale reached the experts"
+    # uniform scale 2: same picks, weights softmax(2 l) over the picks
+    two = synth.bf16_bits(np.full(spec.hidden, 2.0, np.float32))
+    c = oracle.forward(spec, dict(layer, router_x_scale=two), x)
+    p = oracle.forward(spec, layer, x)
+    assert np.array_equal(c["ids"], p["ids"])
+    for t in range(x.shape[0]):
+        sel = 2.0 * p["logits"][t, p["ids"][t]]
+        ww = np.exp(sel - sel.max())
+        _close(c["w"][t], ww / ww.sum(), rtol=1e-12, atol=1e-14, what="scale 2 as a temperature")
+
+
+def pin_q8_router_vs_bf16():
+    spec = _spec(hidden=64, expert_inter=32, num_experts=5, top_k=2, x_dtype=BF16, router_dtype=Q8_0, seed=43)
+    layer = synth.make_layer(spec)
+    rng = np.random.default_rng(43)
+    q = rng.integers(-127, 128, size=(5, 64), dtype=np.int8)
+    d = np.ldexp(1.0, rng.integers(-12, -6, size=(5, 2))).astype(np.float16)
+    layer["router"] = synth.q8_pack(q, d)
+    v = (q.astype(np.float32).reshape(5, 2, 32) * d.astype(np.float32)[:, :, None]).reshape(5, 64)
+    bf = dict(layer, router=synth.bf16_bits(v))
+    assert np.array_equal(synth.bf16_to_f32(bf["router"]), v), "power-of-two scales must be bf16-exact"
+    rs = synth.bf16_bits(rng.uniform(0.5, 1.5, 64).astype(np.float32))
+    x = synth.make_tokens(spec, 4)
+    a = oracle.forward(spec, dict(layer, router_x_scale=rs), x)
+    b = oracle.forward(spec.replace(router_dtype=BF16), dict(bf, router_x_scale=rs), x)
+    assert np.array_equal(a["logits"], b["logits"]) and np.array_equal(a["y"], b["y"]), \
+        "Q8_0 router and its bf16 image disagree"
+    # and the logits against a numpy statement of the scaled router
+    xf = dequant(x, BF16, 4, 64) * synth.bf16_to_f32(rs).astype(np.float64)
+    _close(a["logits"], xf @ v.astype(np.float64).T, rtol=1e-12, what="Q8_0 router logits")
+
+
+# ---------------------------------------------------------------------------
 # Hand-derived fixtures (tests/golden/*.json)
 # ---------------------------------------------------------------------------
 def _golden(name):
@@ -730,4 +786,5 @@ PINS = [
     pin_prenorm_scale_invariance, pin_golden_selection, pin_golden_layer, pin_golden_q8_0,
     pin_sigmoid_scoring, pin_mxfp4_vs_bf16, pin_golden_mxfp4,
     pin_fused_norm_weight_and_residual, pin_fused_closed_form,
+    pin_router_input_scale, pin_q8_router_vs_bf16,
 ]
