@@ -64,7 +64,8 @@ def algorithmic_bytes(spec, M: int, counts: np.ndarray, fused: bool = False) -> 
     R = M * spec.top_k
     gate_up = T * 2 * H * I * bpw + (2 * H * Is * bytes_per_weight(spec.shared_dtype) if Is else 0)
     down = T * H * I * bpw + (H * Is * bytes_per_weight(spec.shared_dtype) if Is else 0)
-    router = H * E * bytes_per_weight(spec.router_dtype) + (4 * E if spec.bias_mode else 0)
+    router = (H * E * bytes_per_weight(spec.router_dtype) + (4 * E if spec.bias_mode else 0)
+              + (2 * H if spec.router_x_scale != "none" else 0))
     layer = gate_up + down + router + M * H * bpx + 4 * M * H
     if fused:  # the residual read, and the norm weight
         layer += 4 * M * H + (H * bpx if spec.rms_eps > 0 else 0)
@@ -99,7 +100,11 @@ def device_copy(spec, dev, rng_seed: int):
         return (t.bfloat16() if dtype == 1 else t), None
 
     out = {}
-    out["router"], _ = mat(E, H, spec.router_dtype)
+    out["router"], rsc = mat(E, H, spec.router_dtype)
+    if rsc is not None:
+        out["router_scale"] = rsc
+    if spec.router_x_scale == "uniform":
+        out["router_x_scale"] = torch.empty(H, device=dev).uniform_(0.5, 1.5, generator=g).bfloat16()
     if spec.bias_kind == "zipf":
         # the host generator's skew with a permutation of this copy's own:
         # expert e gets rank 1 + perm[e] and the logit offset -s * ln(rank)
@@ -209,7 +214,8 @@ def measure_point(spec, M: int, args, want_cpu: bool) -> dict:
               shared_dtype=spec.shared_dtype, max_tokens=M, device=dev,
               path={"auto": m.MOE_PATH_AUTO, "gemv": m.MOE_PATH_GEMV, "mfma": m.MOE_PATH_MFMA}[args.path])
     base = MoeLayer(**kw).load(host["router"], host["bias"], host["gate"], host["up"], host["down"],
-                               host.get("shared_gate"), host.get("shared_up"), host.get("shared_down"))
+                               host.get("shared_gate"), host.get("shared_up"), host.get("shared_down"),
+                               host.get("router_x_scale"))
     # estimate touched bytes with a realised call, then size the rotation
     x0 = base.x_tensor(synth.make_tokens(spec, M, batch=0))
     cnt = torch.empty(spec.num_experts, dtype=torch.int32, device=dev)

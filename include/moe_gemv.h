@@ -113,7 +113,8 @@ typedef struct moe_config {
     float swiglu_limit;   /* > 0: clamp gate and up pre-activations to [-limit, limit]; 0: off */
     float rms_eps;        /* > 0: x_t / sqrt(mean(x_t^2) + eps) feeds router and experts; 0: off */
     int32_t x_dtype;      /* MOE_F32 or MOE_BF16 */
-    int32_t router_dtype; /* MOE_F32 or MOE_BF16 */
+    int32_t router_dtype; /* MOE_F32, MOE_BF16 or MOE_Q8_0 (the INT8 router: int8 rows plus
+                             fp16 scales per 32 elements, weights.router_scale) */
     int32_t expert_dtype; /* MOE_F32, MOE_BF16, MOE_Q8_0 or MOE_MXFP4 */
     int32_t shared_dtype; /* the expert_dtype (ignored when shared_inter = 0) */
     int32_t path;         /* moe_path */
@@ -135,6 +136,13 @@ typedef struct moe_weights {
     const void *shared_gate_scale; /* Q8_0 / MXFP4 only: [Is][H/32] */
     const void *shared_up_scale;   /* [Is][H/32] */
     const void *shared_down_scale; /* [H][Is/32] */
+    /* The INT8 router (llama/state.rs, RealLlamaState.router_ones: the INT8
+     * router kernel scales each element of its input by an effective scale,
+     * identically 1 where the architecture has no router scale):
+     * logits[t][e] = sum_i x[t][i] * router_x_scale[i] * router[e][i]. */
+    const void *router_scale;      /* router_dtype Q8_0: fp16 block scales [E][H/32] (2-byte
+                                      aligned); the router plane is then int8 [E][H] */
+    const void *router_x_scale;    /* bf16 [H] (16-byte aligned), or NULL for ones */
 } moe_weights;
 
 typedef struct moe_plan moe_plan; /* host-side, library-owned */

@@ -44,7 +44,7 @@ class moe_config(ctypes.Structure):
 
 _WEIGHT_FIELDS = ("router", "bias", "gate", "up", "down", "gate_scale", "up_scale", "down_scale",
                   "shared_gate", "shared_up", "shared_down", "shared_gate_scale",
-                  "shared_up_scale", "shared_down_scale")
+                  "shared_up_scale", "shared_down_scale", "router_scale", "router_x_scale")
 
 
 class moe_weights(ctypes.Structure):

@@ -20,6 +20,14 @@ struct Mats {
     const void *gate_s, *up_s, *down_s; // block scale planes (Q8_0 fp16, MXFP4 E8M0) or null
 };
 
+// Router weights: rows [E][H] (fp32, bf16, or the int8 plane of Q8_0 rows),
+// their Q8_0 fp16 block scales [E][H/32] (or null), and the router's
+// per-element input scale (bf16 [H], or null for ones).
+struct RouterW {
+    const void *w, *w_s;
+    const uint16_t *xs;
+};
+
 // Routing state produced by the permutation.
 struct Routing {
     const int32_t *offsets;       // [E+1]
@@ -35,7 +43,7 @@ hipError_t launch_rms_scale(const Layer &L, const void *x, int M, float *scale, 
 // into bf16 hi/lo pairs, the A layout of the grouped GEMM.
 hipError_t launch_norm_apply(const Layer &L, const void *x, const void *gamma, const float *scale, int M,
                              float *xn, uint16_t *xs, hipStream_t s);
-hipError_t launch_router(const Layer &L, const void *x, const void *router, const float *tok_scale,
+hipError_t launch_router(const Layer &L, const void *x, const RouterW &rw, const float *tok_scale,
                          int M, float *logits, hipStream_t s);
 hipError_t launch_topk(const Layer &L, const float *logits, const float *bias, int M, int32_t *ids,
                        float *w, hipStream_t s);
@@ -44,7 +52,7 @@ hipError_t launch_permute(int E, int R, int tile_rows, const int32_t *ids, int32
                           int32_t *tiles, hipStream_t s);
 // Router + top-k + permutation for M <= route_small_max_tokens() (two launches).
 int route_small_max_tokens();
-hipError_t launch_route_small(const Layer &L, const void *x, const void *router, const float *bias,
+hipError_t launch_route_small(const Layer &L, const void *x, const RouterW &rw, const float *bias,
                               const float *tok_scale, int M, float *logits, int32_t *ids, float *w,
                               int32_t *counts, int32_t *offsets, int32_t *sorted, int32_t *route_pos,
                               int32_t *active, hipStream_t s);
@@ -75,7 +83,7 @@ int down_ksplit(const Layer &L, int M, int tile_rows);
 // M = 1 decode kernels (x shared by every touched expert).
 bool m1_supported(const Layer &L);
 // Router logits only (M <= route_small_max_tokens()).
-hipError_t launch_router_small(const Layer &L, const void *x, const void *router, const float *tok_scale,
+hipError_t launch_router_small(const Layer &L, const void *x, const RouterW &rw, const float *tok_scale,
                                int M, float *logits, hipStream_t s);
 // Top-k from the logits and gate/up in one kernel; writes ids_out / w_out
 // ([k]) and counts_out ([E], may be null).

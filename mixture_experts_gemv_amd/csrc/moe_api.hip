@@ -177,9 +177,18 @@ moe_status check_experts(const moe_plan *p, const moe_weights *w, bool need_gate
 
 moe_status check_router(const moe_plan *p, const moe_weights *w, bool need_router) {
     if (!w) return fail(MOE_ERR_INVALID, "weights is NULL");
-    if (need_router) TRY(need_ptr(w->router, 16, "weights.router"));
+    if (need_router) {
+        TRY(need_ptr(w->router, 16, "weights.router"));
+        if (p->L.rdt == moe::DT_Q8) TRY(need_ptr(w->router_scale, 2, "weights.router_scale"));
+        if (w->router_x_scale) TRY(need_ptr(w->router_x_scale, 16, "weights.router_x_scale"));
+    }
     if (p->L.bias_mode != MOE_BIAS_NONE) TRY(need_ptr(w->bias, 4, "weights.bias"));
     return MOE_OK;
+}
+
+moe::RouterW router_w(const moe_plan *p, const moe_weights *w) {
+    return moe::RouterW{w->router, p->L.rdt == moe::DT_Q8 ? w->router_scale : nullptr,
+                        static_cast<const uint16_t *>(w->router_x_scale)};
 }
 
 } // namespace
@@ -258,9 +267,10 @@ moe_status moe_plan_create(const moe_config *c, moe_plan **out) {
     if (c->hidden % 32 || c->expert_inter % 32 || c->shared_inter % 32)
         return fail(MOE_ERR_UNSUPPORTED, "hidden, expert_inter and shared_inter must be multiples of 32");
     if (c->hidden > 16384) return fail(MOE_ERR_UNSUPPORTED, "hidden %d exceeds 16384", c->hidden);
-    if (c->x_dtype == MOE_Q8_0 || c->router_dtype == MOE_Q8_0 || c->x_dtype == MOE_MXFP4 ||
-        c->router_dtype == MOE_MXFP4)
-        return fail(MOE_ERR_UNSUPPORTED, "x and router must be fp32 or bf16");
+    if (c->x_dtype == MOE_Q8_0 || c->x_dtype == MOE_MXFP4)
+        return fail(MOE_ERR_UNSUPPORTED, "x must be fp32 or bf16");
+    if (c->router_dtype == MOE_MXFP4)
+        return fail(MOE_ERR_UNSUPPORTED, "the router must be fp32, bf16 or Q8_0");
     if (c->shared_inter > 0 && c->shared_dtype != c->expert_dtype)
         return fail(MOE_ERR_UNSUPPORTED, "the shared expert must use the routed experts' dtype");
     if ((long)c->max_tokens * c->top_k > (1L << 30))
@@ -311,7 +321,7 @@ moe_status moe_route(const moe_plan *p, const void *x, const moe_weights *wts, i
             sc = at<float>(ws, lay.tok_scale);
             LAUNCH(moe::launch_rms_scale(L, x, M, sc, s), "rms scale");
         }
-        LAUNCH(moe::launch_router(L, x, wts->router, sc, M, lg, s), "router");
+        LAUNCH(moe::launch_router(L, x, router_w(p, wts), sc, M, lg, s), "router");
     }
     LAUNCH(moe::launch_topk(L, lg, wts->bias, M, ids, w, s), "top-k");
     return MOE_OK;
@@ -497,18 +507,19 @@ static moe_status forward_impl(const moe_plan *p, const void *x, const moe_weigh
     const bool single = M == 1 && !mfma && moe::m1_supported(L);
     if (single) {
         // one token: the gate/up kernel runs the top-k itself from the logits
-        STAGE(rec, moe::launch_router_small(L, x, wts->router, sc, M, lg, s), "router", MOE_STAGE_ROUTER);
+        STAGE(rec, moe::launch_router_small(L, x, router_w(p, wts), sc, M, lg, s), "router", MOE_STAGE_ROUTER);
     } else if (M <= moe::route_small_max_tokens() && !mfma) {
-        STAGE(rec, moe::launch_route_small(L, x, wts->router, wts->bias, sc, M, lg, ids, w, counts, offsets,
+        STAGE(rec, moe::launch_route_small(L, x, router_w(p, wts), wts->bias, sc, M, lg, ids, w, counts, offsets,
                                            sorted, rpos, active, s),
               "route", MOE_STAGE_ROUTER);
     } else {
-        if (mfma && L.rdt == moe::DT_BF16 && (L.xdt == moe::DT_BF16 || xsplit))
+        // (the MFMA router takes bf16 rows and no input scale; otherwise the GEMV router)
+        if (mfma && L.rdt == moe::DT_BF16 && !wts->router_x_scale && (L.xdt == moe::DT_BF16 || xsplit))
             STAGE(rec, moe::launch_router_mfma(L, xsplit ? (const void *)xsplit : x, wts->router, sc, M, lg, s,
                                                xsplit != nullptr),
                   "router (MFMA)", MOE_STAGE_ROUTER);
         else
-            STAGE(rec, moe::launch_router(L, x, wts->router, sc, M, lg, s), "router", MOE_STAGE_ROUTER);
+            STAGE(rec, moe::launch_router(L, x, router_w(p, wts), sc, M, lg, s), "router", MOE_STAGE_ROUTER);
         STAGE(rec, moe::launch_topk(L, lg, wts->bias, M, ids, w, s), "top-k", MOE_STAGE_TOPK);
         STAGE(rec, moe::launch_permute(L.E, R, rows, ids, counts, offsets, sorted, rpos, active, tiles, s),
               "permute", MOE_STAGE_PERMUTE);

@@ -94,8 +94,13 @@ hipError_t launch_norm_apply(const Layer &L, const void *x, const void *gamma, c
 // is issued unconditionally before any is used: indices past the row end or
 // past the last token are clamped, and their products masked.  Each token's
 // sum is wave-reduced.
+// Q8_0 router rows (the INT8 router): piece p is 8 int8 values of the int8
+// plane and block p / 4's fp16 scale.  xs (bf16 [H], or null) is the router's
+// per-element input scale; it multiplies the router piece (x * s * w is
+// computed as x * (w * s)).
 template <int XDT, int RDT, int TM, int CB>
-__device__ __forceinline__ void router_dots(const void *x, const void *wrow, int H, int t0, int nt,
+__device__ __forceinline__ void router_dots(const void *x, const void *wrow, const void *wsrow,
+                                            const uint16_t *xs, int H, int t0, int nt,
                                             int lane, float (&acc)[TM], int cb = 0, int ce = -1) {
     const size_t xrow = (size_t)H * dt_bytes<XDT>();
     const char *xb = reinterpret_cast<const char *>(x) + (size_t)t0 * xrow;
@@ -109,7 +114,22 @@ __device__ __forceinline__ void router_dots(const void *x, const void *wrow, int
         for (int j = 0; j < CB; j++) {
             const int c = c0 + lane + kWave * j;
             cc[j] = min(c, nch - 1);
-            load8<RDT>(wrow, cc[j], w[j]);
+            if constexpr (RDT == DT_Q8) {
+                const u32x2 q = reinterpret_cast<const u32x2 *>(wrow)[cc[j]];
+                const float d = f16_bits_to_f32(reinterpret_cast<const uint16_t *>(wsrow)[cc[j] >> 2]);
+                w[j][0] = i8_to_f32<0>(q.x) * d; w[j][1] = i8_to_f32<1>(q.x) * d;
+                w[j][2] = i8_to_f32<2>(q.x) * d; w[j][3] = i8_to_f32<3>(q.x) * d;
+                w[j][4] = i8_to_f32<0>(q.y) * d; w[j][5] = i8_to_f32<1>(q.y) * d;
+                w[j][6] = i8_to_f32<2>(q.y) * d; w[j][7] = i8_to_f32<3>(q.y) * d;
+            } else {
+                load8<RDT>(wrow, cc[j], w[j]);
+            }
+            if (xs) {
+                float g[8];
+                load8<DT_BF16>(xs, cc[j], g);
+#pragma unroll
+                for (int i = 0; i < 8; i++) w[j][i] *= g[i];
+            }
         }
         float xv[TM][CB][8];
 #pragma unroll
@@ -135,21 +155,30 @@ __device__ __forceinline__ void router_dots(const void *x, const void *wrow, int
     for (int tm = 0; tm < TM; tm++) acc[tm] = tm < nt ? wave_sum(acc[tm]) : 0.f;
 }
 
-// logits[t][e] = scale[t] * sum_i x[t][i] * router[e][i].  One wave per
+// Start of expert e's router row and of its Q8_0 scale row.
+template <int RDT>
+__device__ __forceinline__ const char *router_row(const RouterW &rw, int e, int H) {
+    return reinterpret_cast<const char *>(rw.w) + (size_t)e * row_bytes<RDT>(H);
+}
+__device__ __forceinline__ const void *router_srow(const RouterW &rw, int e, int H) {
+    return rw.w_s ? reinterpret_cast<const char *>(rw.w_s) + (size_t)e * (H / 32) * 2 : nullptr;
+}
+
+// logits[t][e] = scale[t] * sum_i x[t][i] * s[i] * router[e][i].  One wave per
 // (expert, group of TM tokens).
 constexpr int kRouterTM = 4;
 
 template <int XDT, int RDT>
-__global__ __launch_bounds__(64) void k_router_gemv(const void *x, const void *router,
+__global__ __launch_bounds__(64) void k_router_gemv(const void *x, RouterW rw,
                                                     const float *tok_scale, int M, int H, int E,
                                                     float *logits) {
     const int e = blockIdx.x;
     const int t0 = blockIdx.y * kRouterTM;
     const int lane = threadIdx.x;
     const int nt = min(kRouterTM, M - t0);
-    const char *wrow = reinterpret_cast<const char *>(router) + (size_t)e * H * dt_bytes<RDT>();
     float acc[kRouterTM];
-    router_dots<XDT, RDT, kRouterTM, 2>(x, wrow, H, t0, nt, lane, acc);
+    router_dots<XDT, RDT, kRouterTM, 2>(x, router_row<RDT>(rw, e, H), router_srow(rw, e, H), rw.xs, H, t0, nt,
+                                        lane, acc);
 #pragma unroll
     for (int tm = 0; tm < kRouterTM; tm++) {
         if (tm < nt && lane == 0) {
@@ -160,17 +189,22 @@ __global__ __launch_bounds__(64) void k_router_gemv(const void *x, const void *r
     }
 }
 
-hipError_t launch_router(const Layer &L, const void *x, const void *router, const float *tok_scale,
-                         int M, float *logits, hipStream_t s) {
-    dim3 grid(L.E, (M + kRouterTM - 1) / kRouterTM);
-    if (L.xdt == DT_BF16 && L.rdt == DT_BF16)
-        launch_kernel((k_router_gemv<DT_BF16, DT_BF16>), grid, dim3(64), 0, s, x, router, tok_scale, M, L.H, L.E, logits);
-    else if (L.xdt == DT_BF16)
-        launch_kernel((k_router_gemv<DT_BF16, DT_F32>), grid, dim3(64), 0, s, x, router, tok_scale, M, L.H, L.E, logits);
-    else if (L.rdt == DT_BF16)
-        launch_kernel((k_router_gemv<DT_F32, DT_BF16>), grid, dim3(64), 0, s, x, router, tok_scale, M, L.H, L.E, logits);
+template <int XDT>
+static void router_gemv_rdt(const Layer &L, const void *x, const RouterW &rw, const float *tok_scale, int M,
+                            float *logits, hipStream_t s) {
+    const dim3 grid(L.E, (M + kRouterTM - 1) / kRouterTM);
+    if (L.rdt == DT_BF16)
+        launch_kernel((k_router_gemv<XDT, DT_BF16>), grid, dim3(64), 0, s, x, rw, tok_scale, M, L.H, L.E, logits);
+    else if (L.rdt == DT_Q8)
+        launch_kernel((k_router_gemv<XDT, DT_Q8>), grid, dim3(64), 0, s, x, rw, tok_scale, M, L.H, L.E, logits);
     else
-        launch_kernel((k_router_gemv<DT_F32, DT_F32>), grid, dim3(64), 0, s, x, router, tok_scale, M, L.H, L.E, logits);
+        launch_kernel((k_router_gemv<XDT, DT_F32>), grid, dim3(64), 0, s, x, rw, tok_scale, M, L.H, L.E, logits);
+}
+
+hipError_t launch_router(const Layer &L, const void *x, const RouterW &rw, const float *tok_scale,
+                         int M, float *logits, hipStream_t s) {
+    if (L.xdt == DT_BF16) router_gemv_rdt<DT_BF16>(L, x, rw, tok_scale, M, logits, s);
+    else router_gemv_rdt<DT_F32>(L, x, rw, tok_scale, M, logits, s);
     return hipGetLastError();
 }
 
@@ -419,7 +453,8 @@ hipError_t launch_plan_from_offsets(int E, int tile_rows, const int32_t *offsets
 constexpr int kSmallM = 16;
 
 struct RouteSmallArgs {
-    const void *x, *router;
+    const void *x;
+    RouterW rw;
     const float *bias, *tok_scale;
     int M, H, E, k, select, bias_mode;
     float *logits;
@@ -440,9 +475,9 @@ __global__ __launch_bounds__(kRouteWaves * kWave) void k_router_small(RouteSmall
     const int nt = min(kRouteTM, a.M - t0);
     const int nch = a.H / 8;
     const int cb = wave * nch / kRouteWaves, ce = (wave + 1) * nch / kRouteWaves;
-    const char *wrow = reinterpret_cast<const char *>(a.router) + (size_t)e * a.H * dt_bytes<RDT>();
     float acc[kRouteTM];
-    router_dots<XDT, RDT, kRouteTM, 2>(a.x, wrow, a.H, t0, nt, lane, acc, cb, ce);
+    router_dots<XDT, RDT, kRouteTM, 2>(a.x, router_row<RDT>(a.rw, e, a.H), router_srow(a.rw, e, a.H), a.rw.xs, a.H,
+                                       t0, nt, lane, acc, cb, ce);
     if (lane == 0)
 #pragma unroll
         for (int tm = 0; tm < kRouteTM; tm++) s_part[wave][tm] = acc[tm];
@@ -507,24 +542,25 @@ __global__ __launch_bounds__(kSelWaves * kWave) void k_select_small(RouteSmallAr
 
 int route_small_max_tokens() { return kSmallM; }
 
-static void router_small_dispatch(const Layer &L, const RouteSmallArgs &a, hipStream_t s) {
+template <int XDT>
+static void router_small_rdt(const Layer &L, const RouteSmallArgs &a, hipStream_t s) {
     const dim3 grid(L.E, (a.M + kRouteTM - 1) / kRouteTM), block(kRouteWaves * kWave);
-    if (L.xdt == DT_BF16 && L.rdt == DT_BF16)
-        launch_kernel((k_router_small<DT_BF16, DT_BF16>), grid, block, 0, s, a);
-    else if (L.xdt == DT_BF16)
-        launch_kernel((k_router_small<DT_BF16, DT_F32>), grid, block, 0, s, a);
-    else if (L.rdt == DT_BF16)
-        launch_kernel((k_router_small<DT_F32, DT_BF16>), grid, block, 0, s, a);
-    else
-        launch_kernel((k_router_small<DT_F32, DT_F32>), grid, block, 0, s, a);
+    if (L.rdt == DT_BF16) launch_kernel((k_router_small<XDT, DT_BF16>), grid, block, 0, s, a);
+    else if (L.rdt == DT_Q8) launch_kernel((k_router_small<XDT, DT_Q8>), grid, block, 0, s, a);
+    else launch_kernel((k_router_small<XDT, DT_F32>), grid, block, 0, s, a);
 }
 
-hipError_t launch_route_small(const Layer &L, const void *x, const void *router, const float *bias,
+static void router_small_dispatch(const Layer &L, const RouteSmallArgs &a, hipStream_t s) {
+    if (L.xdt == DT_BF16) router_small_rdt<DT_BF16>(L, a, s);
+    else router_small_rdt<DT_F32>(L, a, s);
+}
+
+hipError_t launch_route_small(const Layer &L, const void *x, const RouterW &rw, const float *bias,
                               const float *tok_scale, int M, float *logits, int32_t *ids, float *w,
                               int32_t *counts, int32_t *offsets, int32_t *sorted, int32_t *route_pos,
                               int32_t *active, hipStream_t s) {
     if (M > kSmallM || M * L.k > kSmallRoutes) return hipErrorInvalidValue;
-    const RouteSmallArgs a{x, router, L.bias_mode ? bias : nullptr, tok_scale, M, L.H, L.E, L.k, L.select,
+    const RouteSmallArgs a{x, rw, L.bias_mode ? bias : nullptr, tok_scale, M, L.H, L.E, L.k, L.select,
                            L.bias_mode, logits, ids, w,
                            PermuteOut{counts, offsets, sorted, route_pos, active, nullptr, 1}};
     router_small_dispatch(L, a, s);
@@ -533,10 +569,10 @@ hipError_t launch_route_small(const Layer &L, const void *x, const void *router,
 }
 
 
-hipError_t launch_router_small(const Layer &L, const void *x, const void *router, const float *tok_scale,
+hipError_t launch_router_small(const Layer &L, const void *x, const RouterW &rw, const float *tok_scale,
                                int M, float *logits, hipStream_t s) {
     if (M > kSmallM) return hipErrorInvalidValue;
-    const RouteSmallArgs a{x, router, nullptr, tok_scale, M, L.H, L.E, L.k, L.select, L.bias_mode, logits,
+    const RouteSmallArgs a{x, rw, nullptr, tok_scale, M, L.H, L.E, L.k, L.select, L.bias_mode, logits,
                            nullptr, nullptr, PermuteOut{}};
     router_small_dispatch(L, a, s);
     return hipGetLastError();

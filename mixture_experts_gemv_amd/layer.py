@@ -38,7 +38,7 @@ class MoeLayer:
         self.device = torch.device(device)
         self.H, self.E, self.k = hidden, num_experts, top_k
         self.I, self.Is = expert_inter, shared_inter
-        self.x_dtype, self.expert_dtype = x_dtype, expert_dtype
+        self.x_dtype, self.expert_dtype, self.router_dtype = x_dtype, expert_dtype, router_dtype
         self.shared_dtype = shared_dtype if shared_inter > 0 else expert_dtype
         self.max_tokens = max_tokens
         self.plan = moe_plan_create(hidden, num_experts, top_k, expert_inter, shared_inter,
@@ -70,10 +70,17 @@ class MoeLayer:
             self.tensors[name] = t
 
     def load(self, router, bias, gate, up, down, shared_gate=None, shared_up=None,
-             shared_down=None) -> "MoeLayer":
+             shared_down=None, router_x_scale=None) -> "MoeLayer":
+        """router_x_scale: the router's per-element input scale (bf16 bits
+        [H]) or None."""
         H, E, I, Is = self.H, self.E, self.I, self.Is
         self.tensors.clear()
-        self.tensors["router"] = upload(router, self.device).reshape(-1)
+        if self.router_dtype == MOE_Q8_0:
+            self._mat("router", router, E, H, MOE_Q8_0)
+        else:
+            self.tensors["router"] = upload(router, self.device).reshape(-1)
+        if router_x_scale is not None:
+            self.tensors["router_x_scale"] = upload(np.asarray(router_x_scale, np.uint16), self.device)
         if bias is not None:
             self.tensors["bias"] = upload(np.asarray(bias, np.float32), self.device)
         self._mat("gate", gate, E * I, H, self.expert_dtype)

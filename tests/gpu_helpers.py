@@ -48,7 +48,8 @@ def device_layer(spec, layer, max_tokens, path=0):
                   expert_dtype=spec.expert_dtype, shared_dtype=spec.shared_dtype,
                   max_tokens=max_tokens, path=path)
     dl.load(layer["router"], layer["bias"], layer["gate"], layer["up"], layer["down"],
-            layer.get("shared_gate"), layer.get("shared_up"), layer.get("shared_down"))
+            layer.get("shared_gate"), layer.get("shared_up"), layer.get("shared_down"),
+            layer.get("router_x_scale"))
     return dl
 
 
@@ -65,6 +66,9 @@ def selection_keys(spec, layer, x, norm_w=None, split=False):
         if norm_w is not None:
             xf = xf * dequant(np.asarray(norm_w).reshape(1, -1), spec.x_dtype, 1, spec.hidden)
     wr = dequant(layer["router"], spec.router_dtype, spec.num_experts, spec.hidden)
+    if layer.get("router_x_scale") is not None:
+        # the router's per-element input scale
+        wr = wr * synth.bf16_to_f32(layer["router_x_scale"]).astype(np.float64)[None, :]
     logits = xf @ wr.T
     b = np.zeros(spec.num_experts) if layer.get("bias") is None else layer["bias"].astype(np.float64)
     A = np.abs(xf) @ np.abs(wr).T + (np.abs(b) if spec.bias_mode != 0 else 0.0)

@@ -138,6 +138,15 @@ def test_call_refusals_before_any_launch():
     st = L.moe_expert_ffn(pq.handle, FAKE, ctypes.byref(w), 4, FAKE, FAKE, FAKE, FAKE,
                           m.moe_workspace_bytes(pq, 4), None)
     assert st == m.MOE_ERR_INVALID and "scale" in m.moe_last_error()
+    # the INT8 router: Q8_0 router rows need their scale plane; the input
+    # scale, when given, must be 16-byte aligned
+    pr = _create(router_dtype=m.MOE_Q8_0)
+    needr = m.moe_workspace_bytes(pr, 4)
+    st = L.moe_route(pr.handle, FAKE, ctypes.byref(w), 4, None, 0, FAKE, FAKE, FAKE, needr, None)
+    assert st == m.MOE_ERR_INVALID and "router_scale" in m.moe_last_error()
+    wr = m.make_weights(router=FAKE, router_scale=FAKE, router_x_scale=FAKE + 8, gate=FAKE, up=FAKE, down=FAKE)
+    st = L.moe_route(pr.handle, FAKE, ctypes.byref(wr), 4, None, 0, FAKE, FAKE, FAKE, needr, None)
+    assert st == m.MOE_ERR_INVALID and "router_x_scale" in m.moe_last_error()
     # unknown route flags
     st = L.moe_route(p.handle, FAKE, ctypes.byref(w), 4, None, 6, FAKE, FAKE, FAKE, need, None)
     assert st == m.MOE_ERR_INVALID

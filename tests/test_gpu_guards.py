@@ -74,7 +74,8 @@ def _fill_ws(plan, g):
 
 CANARY = [("gpt-oss-20b", 1), ("gpt-oss-20b", 16), ("gpt-oss-20b", 64),
           ("gpt-oss-20b-mxfp4", 1), ("gpt-oss-20b-mxfp4", 16), ("gpt-oss-20b-mxfp4", 256),
-          ("deepseek-v2-lite", 1), ("deepseek-v2-lite", 16), ("qwen3-30b-a3b", 2048)]
+          ("deepseek-v2-lite", 1), ("deepseek-v2-lite", 16), ("qwen3-30b-a3b", 2048),
+          ("gpt-oss-20b-int8-router", 16)]
 
 
 @pytest.mark.parametrize("name,M", CANARY, ids=[f"{n}-M{m}" for n, m in CANARY])

@@ -163,7 +163,9 @@ def test_route_from_x_small():
     for n, kw in enumerate([dict(num_experts=8, top_k=2, x_dtype=F32, router_dtype=F32),
                             dict(num_experts=64, top_k=6, select=SOFTMAX_ALL_NORENORM),
                             dict(num_experts=128, top_k=8, bias_mode=BIAS_LOGIT, bias_kind="zipf",
-                                 rms_eps=1e-6)]):
+                                 rms_eps=1e-6),
+                            dict(num_experts=32, top_k=4, router_dtype=Q8_0, router_x_scale="uniform",
+                                 bias_mode=BIAS_LOGIT, bias_kind="normal")]):
         spec = synth.small_spec(hidden=256, expert_inter=32, seed=950 + n, **kw)
         layer = synth.make_layer(spec)
         M = 37
@@ -280,6 +282,12 @@ SMALL = [
                                 shared_inter=160, select=SOFTMAX_ALL_NORENORM, rms_eps=1e-6,
                                 expert_dtype=MXFP4, shared_dtype=MXFP4), (1, 9)),
     ("mx4-dense", dict(hidden=256, num_experts=1, top_k=1, expert_inter=1088, expert_dtype=MXFP4), (1, 16, 70)),
+    # the INT8 router: Q8_0 router rows and a per-element input scale
+    ("q8router-scale", dict(hidden=288, num_experts=12, top_k=4, expert_inter=320, bias_mode=BIAS_LOGIT,
+                            bias_kind="normal", router_dtype=Q8_0, router_x_scale="uniform",
+                            expert_dtype=Q8_0), (1, 5, 16, 40)),
+    ("f32x-q8router-shared", dict(hidden=160, num_experts=5, top_k=2, expert_inter=64, shared_inter=96,
+                                  x_dtype=F32, router_dtype=Q8_0, router_x_scale="uniform"), (1, 12)),
 ]
 
 
@@ -333,6 +341,9 @@ MFMA_SMALL = [
     # one expert: a single ragged 160-row tile (M = 150), two 160-row tiles
     # (M = 300), three 128-row tiles (M = 330)
     ("dense-tiles", dict(hidden=256, num_experts=1, top_k=1, expert_inter=320), (150, 300, 330)),
+    # the INT8 router on the grouped-GEMM path (its logits from the GEMV router)
+    ("q8router-scale", dict(hidden=256, num_experts=16, top_k=4, expert_inter=192, router_dtype=Q8_0,
+                            router_x_scale="uniform", rms_eps=1e-6), (70, 130)),
 ]
 
 
@@ -527,6 +538,8 @@ FUSED = [
                           expert_dtype=MXFP4), (1, 16), 0, True, True, False),
     ("mfma-wide-tiles-norm-res", dict(hidden=256, num_experts=8, top_k=2, expert_inter=192, rms_eps=1e-6),
      (512,), 2, True, True, False),
+    ("q8router-norm-res", dict(hidden=256, num_experts=16, top_k=4, expert_inter=192, rms_eps=1e-6,
+                               router_dtype=Q8_0, router_x_scale="uniform"), (1, 9, 100), 0, True, True, True),
 ]
 
 
@@ -555,7 +568,8 @@ FULL = [("tiny", 4, None), ("gpt-oss-20b", 1, None), ("gpt-oss-20b", 16, None), 
         ("deepseek-v2-lite-dense", 1, None), ("deepseek-v2-lite-dense", 16, None),
         ("deepseek-v2-lite-dense", 512, 8), ("sigmoid-e256", 1, None), ("sigmoid-e256", 16, None),
         ("gpt-oss-20b-mxfp4", 1, None), ("gpt-oss-20b-mxfp4", 16, None), ("gpt-oss-20b-mxfp4", 64, 8),
-        ("gpt-oss-20b-mxfp4", 256, 8)]
+        ("gpt-oss-20b-mxfp4", 256, 8), ("gpt-oss-20b-int8-router", 1, None),
+        ("gpt-oss-20b-int8-router", 16, None), ("gpt-oss-20b-int8-router", 64, 8)]
 
 
 @pytest.mark.parametrize("name,M,nsample", FULL, ids=[f"{n}-M{m}" for n, m, _ in FULL])
