@@ -715,12 +715,49 @@ struct M1Slots {
     }
 };
 
-__device__ __forceinline__ M1Slots m1_slots(const M1Route &rt, int lane, int *my_id, float *my_w, int *my_rank) {
-    topk_wave_core(rt.logits, rt.bias, rt.E, rt.k, rt.select, rt.bias_mode, lane, my_id, my_w);
-    *my_rank = pick_rank(*my_id, rt.k, lane);
+// The token's top-k from its logit row (lv, bv as topk_load leaves them), as
+// the slot table; the grid's first wave (`writer`) also stores the picks in
+// descending key order, their weights and the per-expert counts.  Up to 64
+// experts the slot table comes from the ballot of the picks (the set bits in
+// ascending order); beyond, from each pick's rank among the picks.
+__device__ __forceinline__ M1Slots m1_topk(const M1Route &rt, int lane, const float (&lv)[kKeysPerLane],
+                                           const float (&bv)[kKeysPerLane], uint64_t *words, bool writer,
+                                           int32_t *ids_out, float *w_out, int32_t *counts_out) {
     M1Slots s{0, 0, 0, 0, 0, 0, 0, 0};
+    if (rt.E <= kWave) {
+        const LanePick p = topk_lane_small(lv[0], bv[0], rt.E, rt.k, rt.select, rt.bias_mode, lane, words);
+        uint64_t m = __ballot(p.pick); // exactly k bits: the ranks are a permutation of 0..E-1
+        for (int j = 0; j < rt.k; j++) {
+            s.set(j, __builtin_ctzll(m));
+            m &= m - 1;
+        }
+        if (writer) {
+            if (p.pick) {
+                ids_out[p.rank] = lane;
+                w_out[p.rank] = p.w;
+            }
+            if (counts_out && lane < rt.E) counts_out[lane] = p.pick ? 1 : 0;
+        }
+        return s;
+    }
+    int my_id;
+    float my_w;
+    topk_wave_vals(lv, bv, rt.E, rt.k, rt.select, rt.bias_mode, lane, &my_id, &my_w);
+    const int my_rank = pick_rank(my_id, rt.k, lane);
     for (int j = 0; j < rt.k; j++)
-        s.set(__builtin_amdgcn_readlane(*my_rank, j), __builtin_amdgcn_readlane(*my_id, j));
+        s.set(__builtin_amdgcn_readlane(my_rank, j), __builtin_amdgcn_readlane(my_id, j));
+    if (writer) {
+        if (lane < rt.k) {
+            ids_out[lane] = my_id;
+            w_out[lane] = my_w;
+        }
+        if (counts_out)
+            for (int e = lane; e < rt.E; e += kWave) {
+                int c = 0;
+                for (int u = 0; u < rt.k; u++) c += s.expert(u) == e;
+                counts_out[e] = c;
+            }
+    }
     return s;
 }
 
@@ -740,6 +777,7 @@ struct M1GateUpArgs {
 template <int XDT, int WDT, int CPL, int RP>
 __global__ __launch_bounds__(kThreads) void k_gateup_m1(M1GateUpArgs a) {
     constexpr int N = Chunk<WDT>::N;
+    __shared__ __align__(16) uint64_t s_words[kWaves][kWave];
     const int lane = threadIdx.x & 63;
     const int gw = uniform(blockIdx.x * kWaves + (threadIdx.x >> 6));
     // wave gw takes the RP pairs at gw * RP, then every nwv * RP further, so
@@ -750,61 +788,62 @@ __global__ __launch_bounds__(kThreads) void k_gateup_m1(M1GateUpArgs a) {
     if (gw * RP >= a.total_pairs) return;
     const int p_end = a.total_pairs;
     const int H = a.H, nch = H / N;
+    // the logit row first: the top-k needs it, and nothing else, before it
+    // can start
+    float lv[kKeysPerLane], bv[kKeysPerLane];
+    topk_load(a.rt.logits, a.rt.bias, a.rt.E, lane, lv, bv);
     const float sc = a.tok_scale ? a.tok_scale[0] : 1.0f;
+    // x chunks this lane multiplies, loaded as stored and converted after
+    // the top-k (which does not need them), so that the top-k does not wait
+    // for them; lanes past the row end hold zeros and load (harmless)
+    // duplicates of the last chunk.
+    int cl[CPL];
+    u32x2 xb[XDT == DT_BF16 ? CPL : 1][XDT == DT_BF16 ? N / 4 : 1];
+    f32x4 xf[XDT == DT_BF16 ? 1 : CPL][XDT == DT_BF16 ? 1 : N / 4];
+#pragma unroll
+    for (int cc = 0; cc < CPL; cc++) {
+        cl[cc] = min(lane + kWave * cc, nch - 1);
+#pragma unroll
+        for (int n4 = 0; n4 < N / 4; n4++) {
+            if constexpr (XDT == DT_BF16)
+                xb[cc][n4] = reinterpret_cast<const u32x2 *>(reinterpret_cast<const uint16_t *>(a.x) + cl[cc] * N + 4 * n4)[0];
+            else
+                xf[cc][n4] = reinterpret_cast<const f32x4 *>(reinterpret_cast<const float *>(a.x) + cl[cc] * N + 4 * n4)[0];
+        }
+    }
+    const M1Slots slots = m1_topk(a.rt, lane, lv, bv, s_words[threadIdx.x >> 6], gw == 0, a.ids_out, a.w_out,
+                                  a.counts_out);
     // MXFP4 codes with bf16 x: x stays as bf16 pairs and the codes, converted
     // to bf16 pairs, go through v_dot2c_f32_bf16 (the pre-norm scale then
     // multiplies the finished dots); otherwise x is held as fp32 with the
     // scale folded in.
     constexpr bool XD2 = XDT == DT_BF16 && WDT == DT_MX4;
-    // x chunks this lane multiplies (loaded before the top-k, which does not
-    // need them); lanes past the row end hold zeros and load (harmless)
-    // duplicates of the last chunk.
-    int cl[CPL];
     float xr[XD2 ? 1 : CPL][XD2 ? 1 : N];
     uint32_t xw[XD2 ? CPL : 1][XD2 ? N / 2 : 1];
+    // (run once, after the first group's weight loads are issued)
+    auto convert_x = [&]() {
 #pragma unroll
     for (int cc = 0; cc < CPL; cc++) {
-        const int c = lane + kWave * cc;
-        cl[cc] = min(c, nch - 1);
-        const float m = c < nch ? sc : 0.f;
-        if constexpr (XD2) {
+        const bool in = lane + kWave * cc < nch;
+        const float m = in ? sc : 0.f;
 #pragma unroll
-            for (int q4 = 0; q4 < N / 8; q4++) {
-                const u32x4 q = reinterpret_cast<const u32x4 *>(reinterpret_cast<const uint16_t *>(a.x) + cl[cc] * N)[q4];
-                xw[cc][4 * q4] = c < nch ? q.x : 0u;
-                xw[cc][4 * q4 + 1] = c < nch ? q.y : 0u;
-                xw[cc][4 * q4 + 2] = c < nch ? q.z : 0u;
-                xw[cc][4 * q4 + 3] = c < nch ? q.w : 0u;
-            }
-        } else {
-#pragma unroll
-            for (int n4 = 0; n4 < N; n4 += 4) {
-                if constexpr (XDT == DT_BF16) {
-                    const u32x2 q = reinterpret_cast<const u32x2 *>(reinterpret_cast<const uint16_t *>(a.x) + cl[cc] * N + n4)[0];
-                    xr[cc][n4] = bf16_lo(q.x) * m; xr[cc][n4 + 1] = bf16_hi(q.x) * m;
-                    xr[cc][n4 + 2] = bf16_lo(q.y) * m; xr[cc][n4 + 3] = bf16_hi(q.y) * m;
-                } else {
-                    const f32x4 q = reinterpret_cast<const f32x4 *>(reinterpret_cast<const float *>(a.x) + cl[cc] * N + n4)[0];
-                    xr[cc][n4] = q.x * m; xr[cc][n4 + 1] = q.y * m; xr[cc][n4 + 2] = q.z * m; xr[cc][n4 + 3] = q.w * m;
-                }
+        for (int n4 = 0; n4 < N / 4; n4++) {
+            if constexpr (XD2) {
+                xw[cc][2 * n4] = in ? xb[cc][n4].x : 0u;
+                xw[cc][2 * n4 + 1] = in ? xb[cc][n4].y : 0u;
+            } else if constexpr (XDT == DT_BF16) {
+                const u32x2 q = xb[cc][n4];
+                xr[cc][4 * n4] = bf16_lo(q.x) * m; xr[cc][4 * n4 + 1] = bf16_hi(q.x) * m;
+                xr[cc][4 * n4 + 2] = bf16_lo(q.y) * m; xr[cc][4 * n4 + 3] = bf16_hi(q.y) * m;
+            } else {
+                const f32x4 q = xf[cc][n4];
+                xr[cc][4 * n4] = q.x * m; xr[cc][4 * n4 + 1] = q.y * m;
+                xr[cc][4 * n4 + 2] = q.z * m; xr[cc][4 * n4 + 3] = q.w * m;
             }
         }
     }
-    int my_id, my_rank;
-    float my_w;
-    const M1Slots slots = m1_slots(a.rt, lane, &my_id, &my_w, &my_rank);
-    if (gw == 0) {
-        if (lane < a.k) {
-            a.ids_out[lane] = my_id;
-            a.w_out[lane] = my_w;
-        }
-        if (a.counts_out)
-            for (int e = lane; e < a.rt.E; e += kWave) {
-                int c = 0;
-                for (int u = 0; u < a.k; u++) c += slots.expert(u) == e;
-                a.counts_out[e] = c;
-            }
-    }
+    };
+    bool x_ready = false;
     const int routed_pairs = a.k * a.I;
     const size_t rbytes = row_bytes<WDT>(H);
     for (int p = gw * RP; p < p_end; p += nwv * RP) {
@@ -848,6 +887,10 @@ __global__ __launch_bounds__(kThreads) void k_gateup_m1(M1GateUpArgs a) {
                     hu[r][cc] = scale_bits<WDT>(usr[r], chunk_block<WDT>(cl[cc]));
                 }
             }
+        if (!x_ready) {
+            convert_x();
+            x_ready = true;
+        }
 #pragma unroll
         for (int r = 0; r < RP; r++) {
             float g = 0.f, v = 0.f;

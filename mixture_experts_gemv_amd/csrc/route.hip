@@ -209,13 +209,27 @@ hipError_t launch_router(const Layer &L, const void *x, const RouterW &rw, const
 }
 
 // ---------------------------------------------------------------- wave top-k
-// One wave per token; lane l holds experts l, l+64, l+128, l+192.
-// Selection key s = logit (+ bias for LOGIT and SELECT_ONLY); softmax input
-// u = logit (+ bias for LOGIT).  k rounds of a wave argmax on the
-// order-preserving key, ties to the lower expert id.
+// One wave per token.  Selection key s = logit (+ bias for LOGIT and
+// SELECT_ONLY); softmax input u = logit (+ bias for LOGIT); descending key,
+// ties to the lower expert id.  Up to 64 experts: one expert a lane and a
+// rank count over the wave's words in LDS (`words`, 64 entries); more: lane
+// l holds experts l, l+64, l+128, l+192 and k rounds of a wave argmax pick
+// them.  Pick j (descending key) goes to ids_row[j] and w_row[j].
 __device__ void topk_wave(const float *lrow, const float *bias, int E, int k, int select,
-                          int bias_mode, int lane, int32_t *ids_row, float *w_row,
+                          int bias_mode, int lane, int32_t *ids_row, float *w_row, uint64_t *words,
                           int *lds_ids = nullptr) {
+    if (E <= kWave) {
+        const int e = min(lane, E - 1);
+        const float lv = lrow[e];
+        const float bv = bias ? bias[e] : 0.f;
+        const LanePick p = topk_lane_small(lv, bv, E, k, select, bias_mode, lane, words);
+        if (p.pick) {
+            ids_row[p.rank] = lane;
+            w_row[p.rank] = p.w;
+            if (lds_ids) lds_ids[p.rank] = lane;
+        }
+        return;
+    }
     int id;
     float wt;
     topk_wave_core(lrow, bias, E, k, select, bias_mode, lane, &id, &wt);
@@ -229,11 +243,13 @@ __device__ void topk_wave(const float *lrow, const float *bias, int E, int k, in
 __global__ __launch_bounds__(256) void k_topk(const float *logits, const float *bias, int M, int E,
                                               int k, int select, int bias_mode, int32_t *ids,
                                               float *w) {
-    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    __shared__ __align__(16) uint64_t s_words[4][kWave];
+    const int wave = threadIdx.x >> 6;
+    const int t = blockIdx.x * 4 + wave;
     const int lane = threadIdx.x & 63;
     if (t >= M) return;
     topk_wave(logits + (size_t)t * E, bias, E, k, select, bias_mode, lane, ids + (size_t)t * k,
-              w + (size_t)t * k);
+              w + (size_t)t * k, s_words[wave]);
 }
 
 hipError_t launch_topk(const Layer &L, const float *logits, const float *bias, int M, int32_t *ids,
@@ -503,6 +519,7 @@ __global__ __launch_bounds__(kSelWaves * kWave) void k_select_small(RouteSmallAr
     __shared__ float s_logit[kSmallM * kMaxE];
     __shared__ float s_bias[kMaxE];
     __shared__ int s_scan[4];
+    __shared__ __align__(16) uint64_t s_words[kSelWaves][kWave];
     const int tid = threadIdx.x, wave = uniform(tid >> 6), lane = tid & 63;
     const int R = a.M * a.k;
     for (int i = tid; i < a.M * a.E; i += kSelWaves * kWave) s_logit[i] = a.logits[i];
@@ -511,7 +528,7 @@ __global__ __launch_bounds__(kSelWaves * kWave) void k_select_small(RouteSmallAr
     __syncthreads();
     if (wave < a.M)
         topk_wave(s_logit + wave * a.E, a.bias ? s_bias : nullptr, a.E, a.k, a.select, a.bias_mode, lane,
-                  a.ids + (size_t)wave * a.k, a.w + (size_t)wave * a.k, s_ids + wave * a.k);
+                  a.ids + (size_t)wave * a.k, a.w + (size_t)wave * a.k, s_words[wave], s_ids + wave * a.k);
     __syncthreads();
     if (tid < R) {
         const int e = s_ids[tid];

@@ -86,12 +86,12 @@ __device__ inline void topk_wave_vals(const float (&lv)[kKeysPerLane], const flo
     *wt = wj;
 }
 
-__device__ inline void topk_wave_core(const float *lrow, const float *bias, int E, int k, int select,
-                                      int bias_mode, int lane, int *id, float *wt) {
-    float lv[kKeysPerLane], bv[kKeysPerLane];
-    // all loads first (clamped index, masked in the selection) so they
-    // overlap; groups of 64 past E load nothing (every wave of a grid may run
-    // this on the same row, so each load is a hot cache line)
+// The lane's logits and biases for topk_wave_vals (lv[c], bv[c]: expert
+// lane + 64 c).  All loads are issued together (clamped index, masked in the
+// selection); groups of 64 past E load nothing (every wave of a grid may run
+// this on the same row, so each load is a hot cache line).
+__device__ inline void topk_load(const float *lrow, const float *bias, int E, int lane,
+                                 float (&lv)[kKeysPerLane], float (&bv)[kKeysPerLane]) {
 #pragma unroll
     for (int c = 0; c < kKeysPerLane; c++) {
         lv[c] = bv[c] = 0.f;
@@ -101,7 +101,70 @@ __device__ inline void topk_wave_core(const float *lrow, const float *bias, int 
             bv[c] = bias ? bias[e] : 0.f;
         }
     }
+}
+
+__device__ inline void topk_wave_core(const float *lrow, const float *bias, int E, int k, int select,
+                                      int bias_mode, int lane, int *id, float *wt) {
+    float lv[kKeysPerLane], bv[kKeysPerLane];
+    topk_load(lrow, bias, E, lane, lv, bv);
     topk_wave_vals(lv, bv, E, k, select, bias_mode, lane, id, wt);
+}
+
+// Top-k of at most 64 experts, one a lane (lane l holds expert l's logit lv
+// and bias bv; lanes past E hold nothing).  Keys, softmax inputs and the
+// three weight rules are those of topk_wave_vals.  Each lane writes one
+// 64-bit word to `words` (the wave's own 64 entries in LDS, 16-byte aligned):
+// its key in the high half and 64 - l in the low half, so that a larger word
+// comes earlier in the selection order (descending key, ties to the lower id)
+// and every valid expert's word is nonzero.  A lane's rank is the number of
+// words larger than its own, and the picks are the valid lanes of rank < k:
+// one pass over E words instead of k rounds of wave reductions.  Every lane
+// must be active.  Returns, per lane, whether it is a pick, its rank (the
+// pick's place in descending key order) and, for a pick, its weight.
+struct LanePick {
+    bool pick;
+    int rank;
+    float w;
+};
+
+__device__ inline LanePick topk_lane_small(float lv, float bv, int E, int k, int select, int bias_mode,
+                                           int lane, uint64_t *words) {
+    const bool valid = lane < E;
+    float u, sk;
+    if (select == 2) {
+        u = 1.0f / (1.0f + expf(-lv));
+        sk = bias_mode != 0 ? u + bv : u;
+    } else {
+        sk = bias_mode != 0 ? lv + bv : lv;
+        u = bias_mode == 1 ? lv + bv : lv;
+    }
+    const uint64_t mine = valid ? ((uint64_t)order_key(sk) << 32) | (uint64_t)(kWave - lane) : 0ull;
+    words[lane] = mine;
+    // LDS accesses of one wave complete in issue order; the fences keep the
+    // compiler from moving the reads above the write
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    typedef uint64_t u64x2 __attribute__((ext_vector_type(2)));
+    const u64x2 *w2 = reinterpret_cast<const u64x2 *>(words);
+    int rank = 0;
+#pragma unroll 4
+    for (int j = 0; j < (E + 1) >> 1; j++) { // words past E are zero
+        const u64x2 q = w2[j];
+        rank += q.x > mine;
+        rank += q.y > mine;
+    }
+    const bool pick = valid && rank < k;
+    float w;
+    if (select == 2) {
+        w = u / wave_sum(pick ? u : 0.f);
+    } else {
+        const bool in = select == 0 ? pick : valid; // softmax over the picks, or over all experts
+        const float m = wave_max(in ? u : -INFINITY);
+        const float ex = in ? expf(u - m) : 0.f;
+        w = ex / wave_sum(ex);
+    }
+    return LanePick{pick, rank, w};
 }
 
 // Rank of lane j's pick among the k picks in ascending expert id (lanes < k):
