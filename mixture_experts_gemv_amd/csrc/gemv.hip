@@ -944,15 +944,20 @@ __global__ __launch_bounds__(kThreads) void k_gateup_m1(M1GateUpArgs a) {
 }
 
 // down (M = 1): a workgroup reads the k picks and weights the gate/up kernel
-// wrote, then owns kM1Rows output rows; its 256 threads stride
-// over the concatenated chunks of every touched expert's rows (then the
-// shared expert's), m1_unroll rounds at a time with every load of the rounds
-// issued first.  Each chunk's dot is scaled by its route's weight before the
-// block reduction, which is done in a fixed order.
-constexpr int kM1Rows = 4;
-// Rounds in flight: 4 for Q8_0 (measured 10.8 against 11.7 us at the
-// gpt-oss shape), else 2 (MXFP4 at 4: 14.3 against 10.5 us, from the
+// wrote, then owns kM1Rows output rows; its NT threads stride over the
+// concatenated chunks of every touched expert's rows (then the shared
+// expert's), UNR rounds at a time with every load of the rounds issued first.
+// Each chunk's dot is scaled by its route's weight before the block
+// reduction, which is done in a fixed order.  When every chunk fits one
+// round of 768 threads, a workgroup takes 768 threads and one chunk a thread:
+// the same loads in flight, spread over three times the waves, so that less
+// work follows each wave's last load (gpt-oss-shaped Q8_0 layer, 720 chunks:
+// 9.2 against 10.1 us for 256 threads and three rounds, in a standalone
+// kernel).  Otherwise 256 threads take 4 rounds for Q8_0 (10.8 against
+// 11.7 us with 2), else 2 (MXFP4 at 4: 14.3 against 10.5 us, from the
 // register footprint of its 32-element chunks).
+constexpr int kM1Rows = 4;
+constexpr int kM1WideThreads = 768;
 template <int WDT> constexpr int m1_unroll() { return WDT == DT_Q8 ? 4 : 2; }
 constexpr int kMaxSlots = 9; // top-k slots + the shared expert
 
@@ -966,15 +971,16 @@ struct M1DownArgs {
     float *y;
 };
 
-template <int WDT>
-__global__ __launch_bounds__(kThreads) void k_down_m1(M1DownArgs a) {
+template <int WDT, int NT, int UNR>
+__global__ __launch_bounds__(NT) void k_down_m1(M1DownArgs a) {
     constexpr int N = Chunk<WDT>::N;
+    constexpr int NW = NT / kWave;
     __shared__ const char *s_row[kMaxSlots];
     __shared__ const void *s_sc[kMaxSlots];
     __shared__ const float *s_act[kMaxSlots];
     __shared__ float s_w[kMaxSlots];
     __shared__ int s_width[kMaxSlots];
-    __shared__ float s_part[kWaves][kM1Rows];
+    __shared__ float s_part[NW][kM1Rows];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int H = a.H, h0 = blockIdx.x * kM1Rows;
     const int n_routed = a.k; // with M = 1 every slot is a touched expert
@@ -1006,15 +1012,14 @@ __global__ __launch_bounds__(kThreads) void k_down_m1(M1DownArgs a) {
     float acc[kM1Rows];
 #pragma unroll
     for (int r = 0; r < kM1Rows; r++) acc[r] = 0.f;
-    constexpr int kM1Unroll = m1_unroll<WDT>();
-    for (int t0 = 0; t0 < n_tasks; t0 += kThreads * kM1Unroll) {
-        u32x4 raw[kM1Unroll][kM1Rows];
-        uint16_t hs[kM1Unroll][kM1Rows];
-        f32x4 av[kM1Unroll][N / 4];
-        float wt[kM1Unroll];
+    for (int t0 = 0; t0 < n_tasks; t0 += NT * UNR) {
+        u32x4 raw[UNR][kM1Rows];
+        uint16_t hs[UNR][kM1Rows];
+        f32x4 av[UNR][N / 4];
+        float wt[UNR];
 #pragma unroll
-        for (int u = 0; u < kM1Unroll; u++) {
-            const int t = t0 + u * kThreads + tid;
+        for (int u = 0; u < UNR; u++) {
+            const int t = t0 + u * NT + tid;
             const int tc = min(t, n_tasks - 1);
             int slot, c;
             if (tc < n_routed * nch) {
@@ -1041,7 +1046,7 @@ __global__ __launch_bounds__(kThreads) void k_down_m1(M1DownArgs a) {
             for (int n4 = 0; n4 < N / 4; n4++) av[u][n4] = ap[piece_major(c, n4, width / N, N / 4)];
         }
 #pragma unroll
-        for (int u = 0; u < kM1Unroll; u++) {
+        for (int u = 0; u < UNR; u++) {
 #pragma unroll
             for (int r = 0; r < kM1Rows; r++) {
                 float wv[N];
@@ -1068,9 +1073,17 @@ __global__ __launch_bounds__(kThreads) void k_down_m1(M1DownArgs a) {
     if (tid <= last_row) {
         float v = a.seed ? a.seed[h0 + tid] : 0.f;
 #pragma unroll
-        for (int wv = 0; wv < kWaves; wv++) v += s_part[wv][tid];
+        for (int wv = 0; wv < NW; wv++) v += s_part[wv][tid];
         a.y[h0 + tid] = v;
     }
+}
+
+template <int WDT>
+static void down_m1_dispatch(int n_tasks, dim3 grid, const M1DownArgs &a, hipStream_t s) {
+    if (n_tasks <= kM1WideThreads)
+        launch_kernel((k_down_m1<WDT, kM1WideThreads, 1>), grid, dim3(kM1WideThreads), 0, s, a);
+    else
+        launch_kernel((k_down_m1<WDT, kThreads, m1_unroll<WDT>()>), grid, dim3(kThreads), 0, s, a);
 }
 
 // Chunks per lane of a row of H elements, and the instantiated values.
@@ -1164,10 +1177,12 @@ hipError_t launch_down_m1(const Layer &L, const float *act, const float *shared_
     a.k = L.k;
     a.y = y;
     const dim3 grid((L.H + kM1Rows - 1) / kM1Rows);
-    if (L.edt == DT_BF16) launch_kernel(k_down_m1<DT_BF16>, grid, dim3(kThreads), 0, s, a);
-    else if (L.edt == DT_Q8) launch_kernel(k_down_m1<DT_Q8>, grid, dim3(kThreads), 0, s, a);
-    else if (L.edt == DT_MX4) launch_kernel(k_down_m1<DT_MX4>, grid, dim3(kThreads), 0, s, a);
-    else launch_kernel(k_down_m1<DT_F32>, grid, dim3(kThreads), 0, s, a);
+    const int N = chunk_elems(L.edt);
+    const int n_tasks = L.k * (L.I / N) + a.Is / N;
+    if (L.edt == DT_BF16) down_m1_dispatch<DT_BF16>(n_tasks, grid, a, s);
+    else if (L.edt == DT_Q8) down_m1_dispatch<DT_Q8>(n_tasks, grid, a, s);
+    else if (L.edt == DT_MX4) down_m1_dispatch<DT_MX4>(n_tasks, grid, a, s);
+    else down_m1_dispatch<DT_F32>(n_tasks, grid, a, s);
     return hipGetLastError();
 }
 
