@@ -303,6 +303,53 @@ __global__ __launch_bounds__(kThreads) void k_gateup_rows(RowsGateUp a) {
     auto compute = [&](const Loads &B, int st, int s0, int ns) {
         const int g = st / ncb, cb = st - g * ncb;
         const int i0 = row_w + g * RP;
+        if constexpr (DOT2 && WDT == DT_Q8 && kTV == 1) {
+            // Q8_0 rows of one chunk block: converted to bf16 pairs once,
+            // then dotted with each staged token (the conversion is most of
+            // the work a token adds otherwise); chunks past the row end get
+            // scale 0
+            int cl[CPL];
+            bool ok[CPL];
+            chunks(cb, cl, ok);
+            uint32_t wg[RP][CPL][NW], wu[RP][CPL][NW];
+            float scg[RP][CPL], scu[RP][CPL];
+#pragma unroll
+            for (int r = 0; r < RP; r++)
+#pragma unroll
+                for (int cc = 0; cc < CPL; cc++) {
+                    q8_to_bf16x2(B.g[r][cc], wg[r][cc]);
+                    q8_to_bf16x2(B.u[r][cc], wu[r][cc]);
+                    scg[r][cc] = ok[cc] ? scale_value<WDT>(B.hg[r][cc]) : 0.f;
+                    scu[r][cc] = ok[cc] ? scale_value<WDT>(B.hu[r][cc]) : 0.f;
+                }
+            for (int j = 0; j < ns; j++) {
+#pragma unroll
+                for (int r = 0; r < RP; r++) ag[r][0] = au[r][0] = 0.f;
+#pragma unroll
+                for (int cc = 0; cc < CPL; cc++) {
+                    const u32x4 *xp = reinterpret_cast<const u32x4 *>(s_x + ((size_t)j * H + (size_t)cl[cc] * N) * 2);
+                    uint32_t xw[NW];
+#pragma unroll
+                    for (int q4 = 0; q4 < NW / 4; q4++) {
+                        const u32x4 v = xp[q4];
+                        xw[4 * q4] = v.x; xw[4 * q4 + 1] = v.y; xw[4 * q4 + 2] = v.z; xw[4 * q4 + 3] = v.w;
+                    }
+#pragma unroll
+                    for (int r = 0; r < RP; r++) {
+                        float sg = 0.f, su = 0.f;
+#pragma unroll
+                        for (int q = 0; q < NW; q++) {
+                            sg = dot2_bf16(wg[r][cc][q], xw[q], sg);
+                            su = dot2_bf16(wu[r][cc][q], xw[q], su);
+                        }
+                        ag[r][0] = fmaf(scg[r][cc], sg, ag[r][0]);
+                        au[r][0] = fmaf(scu[r][cc], su, au[r][0]);
+                    }
+                }
+                epilogue(i0, s0 + j, 1);
+            }
+            return;
+        }
         for (int j0 = 0; j0 < ns; j0 += kTV) {
             const int nj = min(kTV, ns - j0);
             if (cb == 0)
@@ -569,6 +616,49 @@ __global__ __launch_bounds__(kThreads) void k_down_rows(RowsDown a) {
     auto compute = [&](const Loads &B, int st, int s0, int ns) {
         const int g = st / ncb, cb = st - g * ncb;
         const int h0 = row_w + g * RP;
+        if constexpr (kTV == 1) {
+            // rows of one chunk block: decoded and scaled once, then dotted
+            // with each staged act row (chunks past the slice end get 0)
+            int cl[CPL];
+            bool ok[CPL];
+            chunks(cb, cl, ok);
+            float wv[RP][CPL][N];
+#pragma unroll
+            for (int cc = 0; cc < CPL; cc++)
+#pragma unroll
+                for (int r = 0; r < RP; r++) {
+                    decode_chunk<WDT>(B.w[r][cc], wv[r][cc]);
+                    float sc = ok[cc] ? 1.f : 0.f;
+                    if constexpr (blocked<WDT>()) sc *= scale_value<WDT>(B.h[r][cc]);
+#pragma unroll
+                    for (int i = 0; i < N; i++) wv[r][cc][i] *= sc;
+                }
+            for (int j = 0; j < ns; j++) {
+                float d[RP];
+#pragma unroll
+                for (int r = 0; r < RP; r++) d[r] = 0.f;
+                const f32x4 *ap = reinterpret_cast<const f32x4 *>(s_act + (size_t)j * KS);
+#pragma unroll
+                for (int cc = 0; cc < CPL; cc++) {
+                    float av[N];
+#pragma unroll
+                    for (int q4 = 0; q4 < N / 4; q4++) {
+                        const f32x4 v = PM ? ap[piece_major(cl[cc], q4, nch, P)] : ap[cl[cc] * P + q4];
+                        av[4 * q4] = v.x; av[4 * q4 + 1] = v.y; av[4 * q4 + 2] = v.z; av[4 * q4 + 3] = v.w;
+                    }
+#pragma unroll
+                    for (int r = 0; r < RP; r++)
+#pragma unroll
+                        for (int i = 0; i < N; i++) d[r] = fmaf(wv[r][cc][i], av[i], d[r]);
+                }
+#pragma unroll
+                for (int r = 0; r < RP; r++) {
+                    const float v = wave_sum(d[r]);
+                    if (lane == 0) out[(size_t)(s0 + j) * H + h0 + r] = v;
+                }
+            }
+            return;
+        }
         for (int j0 = 0; j0 < ns; j0 += kTV) {
             const int nj = min(kTV, ns - j0);
             if (cb == 0)
