@@ -382,25 +382,33 @@ __global__ __launch_bounds__(kGThreads, 1) void k_gemm_lds(GemmArgs a) {
             xsrc[nb] = sm + a.s_stride * e + (size_t)min(col, N - 1) * (K / 32);
         }
     }
-    auto issue = [&](int kt, unsigned char *st, uint32_t (&xs)[NB]) {
+    // part `part` of nparts of stage kt's copies (copy c of the wave's A, B
+    // and Q8_0 scale copies goes with part c % nparts; MXFP4 scale loads with
+    // the last part), so that a compute step can spread the next stage's
+    // copies over its MFMA substeps
+    auto issue_part = [&](int kt, unsigned char *st, uint32_t (&xs)[NB], int part, int nparts) {
         const int k0 = (kb + kt) * BK; // first reduction element of stage kt
         const size_t ka = (size_t)k0 * 2 * AP, kbb = BX ? (size_t)k0 / 2 : (size_t)k0 * EB;
 #pragma unroll
         for (int q = 0; q < A_DMA; q++)
-            copy16_lds(asrc[q] + ka, st + (wave * A_DMA + q) * 1024);
+            if (q % nparts == part) copy16_lds(asrc[q] + ka, st + (wave * A_DMA + q) * 1024);
 #pragma unroll
         for (int q = 0; q < B_DMA; q++)
-            copy16_lds(bsrc[q] + kbb, st + A_BYTES + wave * WB_BYTES + q * 1024);
+            if ((A_DMA + q) % nparts == part)
+                copy16_lds(bsrc[q] + kbb, st + A_BYTES + wave * WB_BYTES + q * 1024);
         if constexpr (BQ)
 #pragma unroll
             for (int j = 0; j < SCP; j++)
-                copy4_lds(ssrc + (size_t)(k0 / 32) * 2 + 4 * j,
-                          st + A_BYTES + kGW * WB_BYTES + wave * WS_BYTES + j * (kWave * 4));
+                if ((A_DMA + B_DMA + j) % nparts == part)
+                    copy4_lds(ssrc + (size_t)(k0 / 32) * 2 + 4 * j,
+                              st + A_BYTES + kGW * WB_BYTES + wave * WS_BYTES + j * (kWave * 4));
         if constexpr (BX)
+            if (part == nparts - 1)
 #pragma unroll
-            for (int nb = 0; nb < NB; nb++)
-                xs[nb] = *reinterpret_cast<const uint16_t *>(xsrc[nb] + k0 / 32);
+                for (int nb = 0; nb < NB; nb++)
+                    xs[nb] = *reinterpret_cast<const uint16_t *>(xsrc[nb] + k0 / 32);
     };
+    auto issue = [&](int kt, unsigned char *st, uint32_t (&xs)[NB]) { issue_part(kt, st, xs, 0, 1); };
 
     f32x16 acc[MB][NB];
 #pragma unroll
@@ -410,7 +418,11 @@ __global__ __launch_bounds__(kGThreads, 1) void k_gemm_lds(GemmArgs a) {
 #pragma unroll
             for (int r = 0; r < 16; r++) acc[mb][nb][r] = 0.f;
 
-    auto compute = [&](const unsigned char *st, uint32_t (&xs)[NB]) {
+    // kn >= 0: the copies of stage kn into `nxt` (and MXFP4 scale registers
+    // xn) go out a part per substep, between that substep's LDS reads and
+    // its MFMAs
+    auto compute = [&](const unsigned char *st, uint32_t (&xs)[NB], int kn, unsigned char *nxt,
+                       uint32_t (&xn)[NB]) {
         const unsigned char *bw = st + A_BYTES + wave * WB_BYTES;
         if constexpr (BX) {
             // column bytes of substep s: chunk s/2, bytes 8 (s%2) + 4 (l/32) .. +3
@@ -436,6 +448,7 @@ __global__ __launch_bounds__(kGThreads, 1) void k_gemm_lds(GemmArgs a) {
                         for (int h = 0; h < AP; h++)
                             v[AP * mb + h] = lds_load16(st + r * ARB + (((AP * g8 + h) ^ swz<ACH>(r)) * 16));
                     }
+                    if (kn >= 0) issue_part(kn, nxt, xn, s, BK / 16);
                     asm volatile("s_waitcnt lgkmcnt(0)");
 #pragma unroll
                     for (int nb = 0; nb < NB; nb++) lds_keep(q[nb]);
@@ -488,6 +501,7 @@ __global__ __launch_bounds__(kGThreads, 1) void k_gemm_lds(GemmArgs a) {
                     for (int h = 0; h < AP; h++)
                         v[NB + AP * mb + h] = lds_load16(st + r * ARB + (((AP * g8 + h) ^ swz<ACH>(r)) * 16));
                 }
+                if (kn >= 0) issue_part(kn, nxt, xn, s, BK / 16);
                 lds_wait(v);
 #pragma unroll
                 for (int mb = 0; mb < MB; mb++)
@@ -529,6 +543,7 @@ __global__ __launch_bounds__(kGThreads, 1) void k_gemm_lds(GemmArgs a) {
                         for (int h = 0; h < AP; h++)
                             v[AP * mb + h] = lds_load16(st + r * ARB + (((AP * g8 + h) ^ swz<ACH>(r)) * 16));
                     }
+                    if (kn >= 0) issue_part(kn, nxt, xn, s, BK / 16);
                     asm volatile("s_waitcnt lgkmcnt(0)");
 #pragma unroll
                     for (int nb = 0; nb < NB; nb++) lds_keep(q[nb]);
@@ -584,8 +599,20 @@ __global__ __launch_bounds__(kGThreads, 1) void k_gemm_lds(GemmArgs a) {
         else if (ahead == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(LPS));
         else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
         __builtin_amdgcn_s_barrier();
-        if (kt + NST - 1 < nk) issue(kt + NST - 1, nxt, xn);
-        if (wave_on) compute(cur, xc);
+        // bf16 B: the next stage's copies interleave with this stage's MFMAs
+        // (issued as one burst before them, they held the MFMAs back:
+        // Mixtral-shaped M = 512, 734 against 769 us a call; Qwen3-shaped
+        // M = 2048, 527 against 552 us).  Q8_0 and MXFP4 B keep the burst
+        // (interleaved: gpt-oss-shaped Q8_0 M = 64, 296 against 286 us;
+        // MXFP4 M = 512, 493 against 478 us).
+        const int kn = kt + NST - 1 < nk ? kt + NST - 1 : -1;
+        if constexpr (!BQ && !BX) {
+            if (wave_on) compute(cur, xc, kn, nxt, xn);
+            else if (kn >= 0) issue(kn, nxt, xn);
+        } else {
+            if (kn >= 0) issue(kn, nxt, xn);
+            if (wave_on) compute(cur, xc, -1, nxt, xn);
+        }
     };
     if (nk > 0) issue(0, sm0, xr0);
     if (nk > 1) issue(1, sm1, xr1);
