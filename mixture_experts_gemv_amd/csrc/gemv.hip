@@ -48,6 +48,8 @@ static int dn_rows_tile(int dt) { return kWaves * (dt == DT_BF16 ? 8 : 16); }
 constexpr int kTVMulti = 4;
 template <int CPL> constexpr int tokens_per_pass() { return CPL == 8 ? kTVMulti : 1; }
 constexpr int kStageMax = 8;             // vectors one LDS stage holds, at most
+constexpr size_t kStreamLds = 150 * 1024; // LDS budget of the streamed gate/up kernel
+constexpr int kStreamGrid = 256;          // its workgroups: one a CU
 constexpr int kStageBytes = 64 * 1024;   // LDS for staged vectors, per workgroup
 // Rows per load group of the per-row kernels with MXFP4 weights (gate/up with
 // at most two chunks per lane, down with at most four).  Four rows, which
@@ -431,6 +433,198 @@ int gemv_stage_tokens(const Layer &L) {
     return n;
 }
 
+// ------------------------------------------------------- gate/up, streamed
+// Small batches with bf16 x, when every token row fits in LDS: the waves of
+// the grid stream (touched expert, row) pairs, strided by the grid's waves as
+// in the one-token kernel.  A pair's gate and up rows are loaded (CPL 16-byte
+// chunks a lane), converted to bf16 pairs once, and dotted with each of the
+// expert's tokens, read from the workgroup's copy of the batch in LDS.  A
+// workgroup is 1024 threads (16 waves, one workgroup a CU) and stages the
+// batch, the route-to-token table, the token scales and the routing lists
+// once.
+struct StreamGateUp {
+    const void *x; // bf16 [M][H]
+    const float *tok_scale;
+    Mats routed, shared;
+    const int32_t *offsets, *sorted, *active;
+    int M, H, k, E, I, Is;
+    float limit;
+    float *act, *shared_act;
+};
+constexpr int kStreamThreads = 1024;
+constexpr int kStreamWaves = kStreamThreads / kWave;
+
+// LDS bytes of the streamed gate/up kernel for an M-token batch.
+static size_t stream_lds_bytes(const Layer &L, int M) {
+    return (size_t)M * L.H * 2 + (size_t)M * L.k * 4 + (size_t)M * 4 + (size_t)(2 * kMaxE + 2) * 4;
+}
+
+template <int WDT, int CPL>
+__global__ __launch_bounds__(kStreamThreads) void k_gateup_stream(StreamGateUp a) {
+    extern __shared__ __attribute__((aligned(16))) unsigned char s_dyn[];
+    constexpr int N = Chunk<WDT>::N;
+    constexpr int NW = N / 2; // bf16 pair words per chunk
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int H = a.H, nch = H / N, R = a.M * a.k;
+    uint16_t *s_x = reinterpret_cast<uint16_t *>(s_dyn);                 // [M][H]
+    int *s_tok = reinterpret_cast<int *>(s_dyn + (size_t)a.M * H * 2);    // [R] token of sorted route
+    float *s_sc = reinterpret_cast<float *>(s_tok + R);                 // [M] token scales
+    int *s_act = reinterpret_cast<int *>(s_sc + a.M);                   // [1 + E] touched experts
+    int *s_off = s_act + kMaxE + 1;                                     // [E + 1] offsets
+    for (int q = tid; q < a.M * H / 8; q += kStreamThreads)
+        reinterpret_cast<u32x4 *>(s_x)[q] = reinterpret_cast<const u32x4 *>(a.x)[q];
+    for (int q = tid; q < R; q += kStreamThreads) s_tok[q] = a.sorted[q] / a.k;
+    for (int q = tid; q < a.M; q += kStreamThreads) s_sc[q] = a.tok_scale ? a.tok_scale[q] : 1.0f;
+    for (int q = tid; q <= a.E; q += kStreamThreads) {
+        s_act[q] = a.active[q];
+        s_off[q] = a.offsets[q];
+    }
+    __syncthreads();
+    const int routed_pairs = s_act[0] * a.I;
+    const int total = routed_pairs + a.Is;
+    const int nwv = gridDim.x * kStreamWaves;
+    const int gw = uniform(blockIdx.x * kStreamWaves + (tid >> 6));
+    int cl[CPL];
+    bool ok[CPL];
+#pragma unroll
+    for (int cc = 0; cc < CPL; cc++) {
+        const int c = lane + kWave * cc;
+        ok[cc] = c < nch;
+        cl[cc] = min(c, nch - 1);
+    }
+    const size_t rbytes = row_bytes<WDT>(H);
+    for (int p = gw; p < total; p += nwv) {
+        // the pair: a touched expert's row, or a shared-expert row (all tokens)
+        const bool routed = p < routed_pairs;
+        int e = 0, irow, p0 = 0, n = a.M;
+        size_t row;
+        if (routed) {
+            const int u = p / a.I;
+            irow = p - u * a.I;
+            e = s_act[1 + u];
+            p0 = s_off[e];
+            n = s_off[e + 1] - p0;
+            row = (size_t)e * a.I + irow;
+        } else {
+            irow = p - routed_pairs;
+            row = irow;
+        }
+        const Mats &m = routed ? a.routed : a.shared;
+        const char *grow = reinterpret_cast<const char *>(m.gate) + row * rbytes;
+        const char *urow = reinterpret_cast<const char *>(m.up) + row * rbytes;
+        u32x4 rg[CPL], ru[CPL];
+        uint16_t hg[CPL], hu[CPL];
+#pragma unroll
+        for (int cc = 0; cc < CPL; cc++) {
+            rg[cc] = load_raw(grow, cl[cc]);
+            ru[cc] = load_raw(urow, cl[cc]);
+            if constexpr (blocked<WDT>()) {
+                hg[cc] = scale_bits<WDT>(m.gate_s, row * (H / 32) + chunk_block<WDT>(cl[cc]));
+                hu[cc] = scale_bits<WDT>(m.up_s, row * (H / 32) + chunk_block<WDT>(cl[cc]));
+            }
+        }
+        // converted once; chunks past the row end get scale 0
+        uint32_t wg[CPL][NW], wu[CPL][NW];
+        float scg[CPL], scu[CPL];
+#pragma unroll
+        for (int cc = 0; cc < CPL; cc++) {
+            if constexpr (WDT == DT_Q8) {
+                q8_to_bf16x2(rg[cc], wg[cc]);
+                q8_to_bf16x2(ru[cc], wu[cc]);
+            } else if constexpr (WDT == DT_MX4) {
+                mx4_to_bf16x2(rg[cc], wg[cc]);
+                mx4_to_bf16x2(ru[cc], wu[cc]);
+            } else {
+                wg[cc][0] = rg[cc].x; wg[cc][1] = rg[cc].y; wg[cc][2] = rg[cc].z; wg[cc][3] = rg[cc].w;
+                wu[cc][0] = ru[cc].x; wu[cc][1] = ru[cc].y; wu[cc][2] = ru[cc].z; wu[cc][3] = ru[cc].w;
+            }
+            scg[cc] = ok[cc] ? (blocked<WDT>() ? scale_value<WDT>(hg[cc]) : 1.f) : 0.f;
+            scu[cc] = ok[cc] ? (blocked<WDT>() ? scale_value<WDT>(hu[cc]) : 1.f) : 0.f;
+        }
+        for (int j = 0; j < n; j++) {
+            const int t = routed ? s_tok[p0 + j] : j;
+            const u32x4 *xr = reinterpret_cast<const u32x4 *>(s_x + (size_t)t * H);
+            float g = 0.f, v = 0.f;
+#pragma unroll
+            for (int cc = 0; cc < CPL; cc++) {
+                uint32_t xw[NW];
+#pragma unroll
+                for (int q4 = 0; q4 < NW / 4; q4++) {
+                    const u32x4 q = xr[cl[cc] * (NW / 4) + q4];
+                    xw[4 * q4] = q.x; xw[4 * q4 + 1] = q.y; xw[4 * q4 + 2] = q.z; xw[4 * q4 + 3] = q.w;
+                }
+                float sg = 0.f, su = 0.f;
+#pragma unroll
+                for (int q = 0; q < NW; q++) {
+                    sg = dot2_bf16(wg[cc][q], xw[q], sg);
+                    su = dot2_bf16(wu[cc][q], xw[q], su);
+                }
+                g = fmaf(scg[cc], sg, g);
+                v = fmaf(scu[cc], su, v);
+            }
+            const float sc = s_sc[t];
+            g = wave_sum(g) * sc;
+            v = wave_sum(v) * sc;
+            if (routed && a.limit > 0.f) { // the shared expert is not clamped
+                g = clampf(g, a.limit);
+                v = clampf(v, a.limit);
+            }
+            if (lane == 0) {
+                const float h = silu_mul(g, v);
+                if (routed) a.act[(size_t)(p0 + j) * a.I + irow] = h;
+                else a.shared_act[(size_t)j * a.Is + irow] = h;
+            }
+        }
+    }
+}
+
+template <int WDT>
+static bool gateup_stream_dispatch(int cpl, const StreamGateUp &a, int grid, size_t lds, hipStream_t s) {
+    switch (cpl) {
+    case 1: launch_kernel((k_gateup_stream<WDT, 1>), dim3(grid), dim3(kStreamThreads), (uint32_t)lds, s, a); return true;
+    case 2: launch_kernel((k_gateup_stream<WDT, 2>), dim3(grid), dim3(kStreamThreads), (uint32_t)lds, s, a); return true;
+    case 3: launch_kernel((k_gateup_stream<WDT, 3>), dim3(grid), dim3(kStreamThreads), (uint32_t)lds, s, a); return true;
+    case 4: launch_kernel((k_gateup_stream<WDT, 4>), dim3(grid), dim3(kStreamThreads), (uint32_t)lds, s, a); return true;
+    default: return false;
+    }
+}
+
+// The streamed kernel when it applies: bf16 x, bf16, Q8_0 or MXFP4 weights
+// (the shared expert's in the same format), at most 4 chunks a lane (2 for
+// MXFP4), and the batch within the LDS budget.  Returns false to leave the call to the
+// per-row kernel.
+static bool launch_gateup_stream(const Layer &L, const void *x, const float *tok_scale, const Mats &routed,
+                                 const Mats &shared, const Routing &rt, int M, float *act, float *shared_act,
+                                 hipStream_t s) {
+    const int Is = shared_act ? L.Is : 0;
+    if (L.xdt != DT_BF16 || L.edt == DT_F32 || (Is > 0 && L.sdt != L.edt) || !act || L.E > kMaxE) return false;
+    const size_t lds = stream_lds_bytes(L, M);
+    if (lds > kStreamLds) return false;
+    const int cpl = (L.H / chunk_elems(L.edt) + kWave - 1) / kWave;
+    if (cpl > (L.edt == DT_MX4 ? 2 : 4)) return false; // (MXFP4 at 3 or more would spill)
+    StreamGateUp a;
+    a.x = x;
+    a.tok_scale = tok_scale;
+    a.routed = routed;
+    a.shared = shared;
+    a.offsets = rt.offsets;
+    a.sorted = rt.sorted;
+    a.active = rt.active;
+    a.M = M;
+    a.H = L.H;
+    a.k = L.k;
+    a.E = L.E;
+    a.I = L.I;
+    a.Is = Is;
+    a.limit = L.limit;
+    a.act = act;
+    a.shared_act = shared_act;
+    const int grid = kStreamGrid;
+    if (L.edt == DT_Q8) return gateup_stream_dispatch<DT_Q8>(cpl, a, grid, lds, s);
+    if (L.edt == DT_MX4) return gateup_stream_dispatch<DT_MX4>(cpl, a, grid, lds, s);
+    return gateup_stream_dispatch<DT_BF16>(cpl, a, grid, lds, s);
+}
+
 hipError_t launch_gateup_gemv(const Layer &L, const void *x, const float *tok_scale, const Mats &routed,
                               const Mats &shared, const Routing &rt, int M, float *act,
                               float *shared_act, hipStream_t s) {
@@ -453,6 +647,7 @@ hipError_t launch_gateup_gemv(const Layer &L, const void *x, const float *tok_sc
     a.limit = L.limit;
     a.act = act;
     a.shared_act = shared_act;
+    if (launch_gateup_stream(L, x, tok_scale, routed, shared, rt, M, act, shared_act, s)) return hipGetLastError();
     const int xb = L.xdt == DT_BF16 ? 2 : 4;
     a.ncap = gemv_stage_tokens(L);
     if (a.ncap < 1) return hipErrorInvalidValue;
