@@ -1229,7 +1229,7 @@ __global__ __launch_bounds__(kThreads) void k_gateup_m1(M1GateUpArgs a) {
 }
 
 // down (M = 1): a workgroup reads the k picks and weights the gate/up kernel
-// wrote, then owns kM1Rows output rows; its NT threads stride over the
+// wrote, then owns R output rows; its NT threads stride over the
 // concatenated chunks of every touched expert's rows (then the shared
 // expert's), UNR rounds at a time with every load of the rounds issued first.
 // Each chunk's dot is scaled by its route's weight before the block
@@ -1238,10 +1238,12 @@ __global__ __launch_bounds__(kThreads) void k_gateup_m1(M1GateUpArgs a) {
 // the same loads in flight, spread over three times the waves, so that less
 // work follows each wave's last load (gpt-oss-shaped Q8_0 layer, 720 chunks:
 // 9.2 against 10.1 us for 256 threads and three rounds, in a standalone
-// kernel).  Otherwise 256 threads take 4 rounds for Q8_0 (10.8 against
+// kernel), and 6 rows, so that the workgroups (two a CU) run in one wave
+// (layer 28.1 against 28.9 us with 4 rows; MXFP4 27.9 against 29.7 us).
+// Otherwise 256 threads and 4 rows take 4 rounds for Q8_0 (10.8 against
 // 11.7 us with 2), else 2 (MXFP4 at 4: 14.3 against 10.5 us, from the
 // register footprint of its 32-element chunks).
-constexpr int kM1Rows = 4;
+constexpr int kM1Rows = 4, kM1WideRows = 6;
 constexpr int kM1WideThreads = 768;
 template <int WDT> constexpr int m1_unroll() { return WDT == DT_Q8 ? 4 : 2; }
 constexpr int kMaxSlots = 9; // top-k slots + the shared expert
@@ -1256,7 +1258,7 @@ struct M1DownArgs {
     float *y;
 };
 
-template <int WDT, int NT, int UNR>
+template <int WDT, int NT, int UNR, int R>
 __global__ __launch_bounds__(NT) void k_down_m1(M1DownArgs a) {
     constexpr int N = Chunk<WDT>::N;
     constexpr int NW = NT / kWave;
@@ -1265,9 +1267,9 @@ __global__ __launch_bounds__(NT) void k_down_m1(M1DownArgs a) {
     __shared__ const float *s_act[kMaxSlots];
     __shared__ float s_w[kMaxSlots];
     __shared__ int s_width[kMaxSlots];
-    __shared__ float s_part[NW][kM1Rows];
+    __shared__ float s_part[NW][R];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int H = a.H, h0 = blockIdx.x * kM1Rows;
+    const int H = a.H, h0 = blockIdx.x * R;
     const int n_routed = a.k; // with M = 1 every slot is a touched expert
     const int nch = a.I / N, nch_s = a.Is / N;
     if (wave == 0) {
@@ -1293,13 +1295,13 @@ __global__ __launch_bounds__(NT) void k_down_m1(M1DownArgs a) {
     }
     __syncthreads();
     const int n_tasks = n_routed * nch + (a.Is > 0 ? nch_s : 0);
-    const int last_row = min(kM1Rows, H - h0) - 1;
-    float acc[kM1Rows];
+    const int last_row = min(R, H - h0) - 1;
+    float acc[R];
 #pragma unroll
-    for (int r = 0; r < kM1Rows; r++) acc[r] = 0.f;
+    for (int r = 0; r < R; r++) acc[r] = 0.f;
     for (int t0 = 0; t0 < n_tasks; t0 += NT * UNR) {
-        u32x4 raw[UNR][kM1Rows];
-        uint16_t hs[UNR][kM1Rows];
+        u32x4 raw[UNR][R];
+        uint16_t hs[UNR][R];
         f32x4 av[UNR][N / 4];
         float wt[UNR];
 #pragma unroll
@@ -1319,7 +1321,7 @@ __global__ __launch_bounds__(NT) void k_down_m1(M1DownArgs a) {
             const char *row0 = s_row[slot];
             wt[u] = t < n_tasks ? s_w[slot] : 0.f;
 #pragma unroll
-            for (int r = 0; r < kM1Rows; r++) {
+            for (int r = 0; r < R; r++) {
                 const int rr = min(r, last_row);
                 raw[u][r] = load_raw(row0 + rr * rb, c);
                 if constexpr (blocked<WDT>())
@@ -1333,7 +1335,7 @@ __global__ __launch_bounds__(NT) void k_down_m1(M1DownArgs a) {
 #pragma unroll
         for (int u = 0; u < UNR; u++) {
 #pragma unroll
-            for (int r = 0; r < kM1Rows; r++) {
+            for (int r = 0; r < R; r++) {
                 float wv[N];
                 decode_chunk<WDT>(raw[u][r], wv);
                 float d = 0.f;
@@ -1350,7 +1352,7 @@ __global__ __launch_bounds__(NT) void k_down_m1(M1DownArgs a) {
         }
     }
 #pragma unroll
-    for (int r = 0; r < kM1Rows; r++) {
+    for (int r = 0; r < R; r++) {
         const float v = wave_sum(acc[r]);
         if (lane == 0) s_part[wave][r] = v;
     }
@@ -1364,11 +1366,13 @@ __global__ __launch_bounds__(NT) void k_down_m1(M1DownArgs a) {
 }
 
 template <int WDT>
-static void down_m1_dispatch(int n_tasks, dim3 grid, const M1DownArgs &a, hipStream_t s) {
+static void down_m1_dispatch(int n_tasks, int H, const M1DownArgs &a, hipStream_t s) {
     if (n_tasks <= kM1WideThreads)
-        launch_kernel((k_down_m1<WDT, kM1WideThreads, 1>), grid, dim3(kM1WideThreads), 0, s, a);
+        launch_kernel((k_down_m1<WDT, kM1WideThreads, 1, kM1WideRows>), dim3((H + kM1WideRows - 1) / kM1WideRows),
+                      dim3(kM1WideThreads), 0, s, a);
     else
-        launch_kernel((k_down_m1<WDT, kThreads, m1_unroll<WDT>()>), grid, dim3(kThreads), 0, s, a);
+        launch_kernel((k_down_m1<WDT, kThreads, m1_unroll<WDT>(), kM1Rows>), dim3((H + kM1Rows - 1) / kM1Rows),
+                      dim3(kThreads), 0, s, a);
 }
 
 // Chunks per lane of a row of H elements, and the instantiated values.
@@ -1461,13 +1465,12 @@ hipError_t launch_down_m1(const Layer &L, const float *act, const float *shared_
     a.Is = shared_act ? L.Is : 0;
     a.k = L.k;
     a.y = y;
-    const dim3 grid((L.H + kM1Rows - 1) / kM1Rows);
     const int N = chunk_elems(L.edt);
     const int n_tasks = L.k * (L.I / N) + a.Is / N;
-    if (L.edt == DT_BF16) down_m1_dispatch<DT_BF16>(n_tasks, grid, a, s);
-    else if (L.edt == DT_Q8) down_m1_dispatch<DT_Q8>(n_tasks, grid, a, s);
-    else if (L.edt == DT_MX4) down_m1_dispatch<DT_MX4>(n_tasks, grid, a, s);
-    else down_m1_dispatch<DT_F32>(n_tasks, grid, a, s);
+    if (L.edt == DT_BF16) down_m1_dispatch<DT_BF16>(n_tasks, L.H, a, s);
+    else if (L.edt == DT_Q8) down_m1_dispatch<DT_Q8>(n_tasks, L.H, a, s);
+    else if (L.edt == DT_MX4) down_m1_dispatch<DT_MX4>(n_tasks, L.H, a, s);
+    else down_m1_dispatch<DT_F32>(n_tasks, L.H, a, s);
     return hipGetLastError();
 }
 
