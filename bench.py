@@ -47,6 +47,26 @@ MFMA_BF16_PEAK_TFS = 2500.0
 GATEUP_KERNEL = {"single": "k_gateup_m1", "gemv": "k_gateup_rows", "mfma": "k_gemm_lds<0"}
 
 
+def gateup_kernel(spec, M: int, path: str) -> str:
+    """Name of the gate/up kernel the library runs for this layer and M (it
+    labels the roofline object and picks the traffic record).  On the gemv
+    path the library streams (touched expert, row) pairs with the whole batch
+    in LDS when x is bf16, the weights are bf16, Q8_0 or MXFP4 (the shared
+    expert's alike), a row is at most 4 chunks a lane (2 for MXFP4) and the
+    batch fits 150 KB of LDS; otherwise it runs the per-row kernel."""
+    if path != "gemv":
+        return GATEUP_KERNEL[path]
+    H, k = spec.hidden, spec.top_k
+    n = {0: 4, 1: 8, 2: 16, 3: 32}[spec.expert_dtype]
+    cpl = (H // n + 63) // 64
+    lds = M * H * 2 + M * k * 4 + M * 4 + (2 * 256 + 2) * 4
+    stream = (spec.x_dtype == 1 and spec.expert_dtype != 0
+              and (spec.shared_inter == 0 or spec.shared_dtype == spec.expert_dtype)
+              and spec.num_experts <= 256 and lds <= 150 * 1024
+              and cpl <= (2 if spec.expert_dtype == 3 else 4))
+    return "k_gateup_stream" if stream else "k_gateup_rows"
+
+
 # ------------------------------------------------------------------ workload
 def bytes_per_weight(dtype: int) -> float:
     return {0: 4.0, 1: 2.0, 2: 34.0 / 32.0, 3: 17.0 / 32.0}[dtype]
@@ -302,7 +322,7 @@ def measure_point(spec, M: int, args, want_cpu: bool) -> dict:
     kev.close()
     ev.close()
 
-    kernel = GATEUP_KERNEL[m.MOE_RUN_NAMES[run]]
+    kernel = gateup_kernel(spec, M, m.MOE_RUN_NAMES[run])
     tag = f"{spec.name}_M{M}"
     trec = profiling.load_traffic(os.path.join(ROOT, "profiles"), kernel, tag)
     flops = algorithmic_flops(spec, M)
