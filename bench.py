@@ -323,7 +323,7 @@ def measure_point(spec, M: int, args, want_cpu: bool) -> dict:
     ev.close()
 
     kernel = gateup_kernel(spec, M, m.MOE_RUN_NAMES[run])
-    tag = f"{spec.name}_M{M}"
+    tag = f"{spec.name}_M{M}" + ("_fused" if args.fused else "")
     trec = profiling.load_traffic(os.path.join(ROOT, "profiles"), kernel, tag)
     flops = algorithmic_flops(spec, M)
     gateup_us = per_stage.get("gateup")
