@@ -129,8 +129,7 @@ struct GemmArgs {
     int out_split;           // gate/up: write act as interleaved bf16 hi/lo (the split A of down)
     int tile_rows;           // rows per tile of the LDS kernel (32, 64, 96, 128 or 160; the tile list's)
     int n_ntiles;            // column tiles
-    int units_pad;           // LDS kernel: workgroups per token tile (>= n_ntiles * ksplit; the extra ones idle)
-    int pad_units;           // caller's request: pad the units for the XCD-grouped order (see run_gemm)
+    int units;               // LDS kernel: workgroups per token tile (n_ntiles * ksplit)
 };
 
 template <int KIND>
@@ -291,16 +290,18 @@ __global__ __launch_bounds__(kGThreads, 1) void k_gemm_lds(GemmArgs a) {
 
     // ---- which tile, column block and reduction slice.  The workgroups of
     // one expert cover its column units c = (slice, column block) for every
-    // token tile tl, per_tile units a tile.  When per_tile is a multiple of 8,
-    // XCD x (equal g mod 8) takes the contiguous unit range
-    // [x * per_tile / 8, (x + 1) * per_tile / 8), all token tiles of each: a
-    // unit's weights are read from HBM about once, and an XCD's units share
-    // one reduction slice of the A rows, which its L2 then serves.  Otherwise
-    // the workgroups run through (tl, c) in tile-major order, so that every
-    // XCD gets work.  (A unit count a little short of a multiple of 8 is
-    // padded to one with idle workgroups, so that it takes the first order.)
+    // token tile tl, per_tile units a tile: per_tile * Te (unit, tile) pairs,
+    // taken in unit-major order.  Workgroups are dispatched to the 8 XCDs in
+    // turn, so the expert's local workgroup l runs on XCD offset l & 7; XCD
+    // offset s takes the s-th contiguous run of about a eighth of the pairs
+    // (its (l >> 3)-th pair).  A unit's token tiles so run on one XCD, or two
+    // where a run ends inside the unit: its weights come from HBM about once
+    // an XCD and the L2 serves the other tiles, and the XCD's units share one
+    // reduction slice of the A rows.  (Qwen3-shaped Zipf M = 2048, 6 gate/up
+    // units a tile: 1.05 against 1.26 GB fetched with the flat tile-major
+    // order, at the same time; 8 units take the same order as before.)
     const int g = blockIdx.x;
-    const int per_tile = a.units_pad;
+    const int per_tile = a.units;
     int e = 0, ts, Te, p0, nrows;
     if (a.tiles) {
         const int q = g / per_tile;
@@ -316,15 +317,14 @@ __global__ __launch_bounds__(kGThreads, 1) void k_gemm_lds(GemmArgs a) {
     }
     const int local = g - ts * per_tile;
     int tl, cu;
-    if ((per_tile & 7) == 0) {
-        const int grp = local / (8 * Te), r8 = local - grp * 8 * Te;
-        tl = r8 >> 3;
-        cu = (r8 & 7) * (per_tile >> 3) + grp;
-    } else {
-        tl = local / per_tile;
-        cu = local - tl * per_tile;
+    {
+        const int total = per_tile * Te, s8 = local & 7;
+        int before = 0; // pairs on the XCD offsets before s8
+        for (int j = 0; j < s8; j++) before += (total - j + 7) >> 3;
+        const int pr = before + (local >> 3);
+        cu = pr / Te;
+        tl = pr - cu * Te;
     }
-    if (cu >= a.n_ntiles * a.ksplit) return; // padding unit
     const int ks = cu / a.n_ntiles, nt = cu - ks * a.n_ntiles;
     if (a.tiles) {
         p0 = a.tiles[2 + a.E + 2 * (ts + tl) + 1];
@@ -907,14 +907,8 @@ static hipError_t run_gemm(int kind, int a_mode, int bq, GemmArgs &a, hipStream_
         const unsigned grid = (unsigned)(((long)a.max_tiles * per_tile + 7) / 8 * 8);
         launch_kernel((k_gemm_reg<GK_PLAIN, true>), dim3(grid), dim3(kGThreads), 0, s, a);
     } else {
-        // pad the units of a token tile to a multiple of 8, so that the LDS
-        // kernel takes its XCD-grouped order, when the caller expects experts
-        // with several token tiles and that idles at most one workgroup in 8
-        // (measured: the gpt-oss-shaped MXFP4 gate/up at M = 256, 210 against
-        // 267 us; with one tile an expert, M = 64, padding measured slower)
-        const int pad = (per_tile + 7) / 8 * 8;
-        a.units_pad = a.pad_units && (pad - per_tile) * 8 <= per_tile ? pad : per_tile;
-        const unsigned grid = (unsigned)((long)a.max_tiles * a.units_pad);
+        a.units = per_tile;
+        const unsigned grid = (unsigned)((long)a.max_tiles * a.units);
         if (a.tile_rows != 32 && a.tile_rows != 64 && a.tile_rows != 96 && a.tile_rows != kBM && !(a.tile_rows == kBMWide && bq != 1))
             return hipErrorInvalidValue;
         if (kind == GK_GATEUP && a_mode == 0) launch_lds<GK_GATEUP, false>(a, bq, grid, s);
@@ -953,7 +947,6 @@ hipError_t launch_gateup_mfma(const Layer &L, const void *x, const float *tok_sc
     if (act) {
         GemmArgs a{};
         a.tile_rows = tile_rows;
-        a.pad_units = (long)M * L.k >= (long)std::min(tile_rows, kBM) * L.E; // about 128 routes an expert, or more
         a.a = x;
         a.sorted = rt.sorted;
         a.k_route = L.k;
@@ -982,7 +975,6 @@ hipError_t launch_gateup_mfma(const Layer &L, const void *x, const float *tok_sc
         a.a = x;
         a.M = M;
         a.tile_rows = M <= 32 ? 32 : kBM;
-        a.pad_units = M > a.tile_rows;
         a.max_tiles = (M + a.tile_rows - 1) / a.tile_rows;
         a.b0 = static_cast<const uint16_t *>(shared.gate);
         a.b1 = static_cast<const uint16_t *>(shared.up);
@@ -1012,7 +1004,6 @@ hipError_t launch_down_mfma(const Layer &L, const float *act, const float *share
         a.E = L.E;
         a.max_tiles = max_tiles;
         a.tile_rows = tile_rows;
-        a.pad_units = (long)M * L.k >= (long)std::min(tile_rows, kBM) * L.E; // about 128 routes an expert, or more
         a.ksplit = down_ksplit(L, M, tile_rows);
         a.slab = (size_t)M * L.k * L.H;
         a.b0 = static_cast<const uint16_t *>(routed.down);
@@ -1031,7 +1022,6 @@ hipError_t launch_down_mfma(const Layer &L, const float *act, const float *share
         a.a = shared_act;
         a.M = M;
         a.tile_rows = act_split && M <= 32 ? 32 : kBM;
-        a.pad_units = M > a.tile_rows;
         a.max_tiles = (M + a.tile_rows - 1) / a.tile_rows;
         a.b0 = static_cast<const uint16_t *>(shared.down);
         a.s0 = static_cast<const uint16_t *>(shared.down_s);
