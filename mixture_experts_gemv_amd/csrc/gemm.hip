@@ -5,9 +5,10 @@
 // Uses:
 //   gate/up  A = gathered token rows of x, B = gate and up rows of the tile's
 //            expert, epilogue silu(clamp(g)) * clamp(v) -> act, written as
-//            fp32 or, inside the layer, as split bf16 hi/lo pairs;
-//   down     A = act rows carried as bf16 hi + lo (so the product keeps about
-//            16 bits of act), B = down rows -> per-route outputs;
+//            fp32 or, inside the layer, as fp16 (the precision the pages keep
+//            act in);
+//   down     A = fp16 act rows, B = down rows converted to fp16 in registers,
+//            fp16 MFMAs -> per-route outputs;
 //   shared   the same two with identity rows (all tokens), for a shared expert.
 // B is bf16 or Q8_0 (int8 plus fp16 scales per 32 reduction elements,
 // converted exactly to bf16 in registers; each block's products are scaled
@@ -24,16 +25,17 @@
 // Two kernels:
 //   k_gemm_lds  both operands go global -> LDS with asynchronous copies
 //     (global_load_lds_dwordx4) in a 3-stage pipeline, XOR-swizzled rows;
-//     64 reduction elements a stage for bf16 A or Q8_0 B, else 32 for split A
-//     (whose stage rows hold hi and lo chunks, and whose MFMAs run once per
-//     half);
+//     64 reduction elements a stage, except 32 for bf16 B with split A (the
+//     fused layer's normed x as bf16 hi/lo pairs, whose stage rows hold hi
+//     and lo chunks and whose MFMAs run once per half);
 //   k_gemm_reg (fp32 A handed in by a caller of the stage-wise entry points,
 //     bf16 B) A is staged through registers into LDS (double buffered, split
 //     into hi/lo once as it is written), B fragments are loaded straight into
 //     registers, one step ahead.
-// (Rounding act to a single bf16 instead measured about 1.5x faster in the
-// down GEMM, but at an output error of about 1.6e-3 relative L2 against
-// about 2.5e-6 with the split.)
+// (act as fp16 against act carried as two bf16 numbers, hi and lo, for
+// about 16 bits: the down GEMM's A bytes and MFMAs halve; Qwen3-shaped Zipf
+// M = 2048, 467 against 529 us a call, Mixtral-shaped M = 512, 634 against
+// 737 us.  A single bf16 would cost about 1.6e-3 relative L2 of the output.)
 #include <algorithm>
 #include <cmath>
 
@@ -43,7 +45,13 @@
 namespace moe {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// A operand formats of the grouped GEMM: bf16 rows (x), split bf16 hi/lo
+// rows (the fused layer's normed x, below), fp16 rows (act of the down GEMM;
+// B is then converted to fp16 in registers).
+enum AFormat { AF_BF16 = 0, AF_SPLIT = 1, AF_F16 = 2 };
 
 constexpr int kMB = 4;              // 32-row blocks per wave
 constexpr int kBM = 32 * kMB;       // rows per tile
@@ -79,8 +87,9 @@ constexpr int kGThreads = kGW * kWave;
 // 128 routes an expert on average at M = 512: 811 against 922 us a call;
 // M = 1024: 1396 against 1461 us; Qwen3-shaped M = 4096: 1019 against
 // 1031 us; a dense layer at M = 512, exactly four 128-row tiles, keeps 128).
-// Q8_0 weights keep 128 rows: the down GEMM's three LDS stages of 160 split
-// act rows would not fit.  The stage-wise entry points always use kBM.
+// Q8_0 weights keep 128 rows: with the fused layer's split x, three LDS
+// stages of 160 rows would not fit, and the Q8_0 block accumulators of 160
+// rows fill the registers.  The stage-wise entry points always use kBM.
 int mfma_tile_rows(const Layer &L, int M) {
     const long R = (long)M * L.k;
     const double c = (double)R / L.E, hi = c + (L.E > 1 ? std::sqrt(c) : 0.0);
@@ -124,9 +133,9 @@ struct GemmArgs {
     int N, K;
     const float *tok_scale;  // per-token scale of the products (pre-norm), or null
     float limit;             // gate/up clamp (0 = off)
-    float *out;              // fp32 [rows][ldo]; gate/up with out_split: hi/lo bf16 rows (below)
+    float *out;              // fp32 [rows][ldo]; gate/up with out_fmt ACT_F16: fp16 rows
     int ldo;
-    int out_split;           // gate/up: write act as interleaved bf16 hi/lo (the split A of down)
+    int out_fmt;             // gate/up act rows: ACT_F32 or ACT_F16
     int tile_rows;           // rows per tile of the LDS kernel (32, 64, 96, 128 or 160; the tile list's)
     int n_ntiles;            // column tiles
     int units;               // LDS kernel: workgroups per token tile (n_ntiles * ksplit)
@@ -139,9 +148,10 @@ struct GemmShape {
     static constexpr int COLS = kGW * WCOLS;                      // output columns per tile
 };
 
-// Reduction elements per pipeline stage (bf16 A; half that for split A) and
-// number of LDS stages of the asynchronous-copy kernel.  A stage is 16 KB of
-// A plus 32 KB (gate/up) or, with split A, 16 KB (down) of B.
+// Reduction elements per pipeline stage (bf16 or fp16 A; half that for split
+// A with bf16 B) and number of LDS stages of the asynchronous-copy kernel.  A
+// stage holds 128 bytes of each A row (20 KB for 160 rows) and of each of the
+// 256 B columns (32 KB of bf16 B; less for Q8_0 and MXFP4).
 constexpr int kStageK = 64;
 constexpr int kStages = 3;
 
@@ -177,12 +187,11 @@ __device__ __forceinline__ void copy16_lds(const void *g, unsigned char *l) {
 // vector memory operations and for nothing else.
 constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
-// Split A rows.  The down GEMM's A is the fp32 act, carried as two bf16
-// numbers per element: hi = bf16(v) and lo = bf16(v - hi), so that
-// hi*b + lo*b keeps about 16 bits of v.  A row of K elements is stored as
-// K/8 pairs of 16-byte chunks (8 hi values, then the same 8 elements' lo
-// values): 4K bytes, the size of the fp32 row.
-__device__ __forceinline__ size_t split_pos(int i) { return (size_t)(i >> 3) * 16 + (i & 7); }
+// Split A rows (the fused layer's normed x): each fp32 value carried as two
+// bf16 numbers, hi = bf16(v) and lo = bf16(v - hi), so that hi*b + lo*b
+// keeps about 16 bits of v.  A row of K elements is stored as K/8 pairs of
+// 16-byte chunks (8 hi values, then the same 8 elements' lo values): 4K
+// bytes, the size of the fp32 row.
 
 // XOR swizzle of a 16-byte chunk within an LDS row of CH chunks: rows of 8
 // or more chunks (128 B) xor with (row ^ row / 8) % 8, so that 8 consecutive
@@ -234,6 +243,45 @@ __device__ __forceinline__ u32x4 q8x8_to_bf16(u32x2 w) {
     return o;
 }
 
+// 8 Q8_0 int8 values as 8 fp16 (exact: |q| <= 127).
+__device__ __forceinline__ u32x4 q8x8_to_f16(u32x2 w) {
+    u32x4 o;
+    o.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(i8_to_f32<0>(w.x), i8_to_f32<1>(w.x)));
+    o.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(i8_to_f32<2>(w.x), i8_to_f32<3>(w.x)));
+    o.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(i8_to_f32<0>(w.y), i8_to_f32<1>(w.y)));
+    o.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(i8_to_f32<2>(w.y), i8_to_f32<3>(w.y)));
+    return o;
+}
+
+// 8 bf16 values as 8 fp16: exact wherever the value is a normal fp16
+// (6.1e-5 <= |v| <= 65504); smaller magnitudes lose low bits to the fp16
+// subnormal range (an absolute error below 2^-24), larger ones saturate.
+// (The conversion rounds toward zero, so finite values beyond the fp16
+// range come out as +-65504.)
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w) {
+    return __builtin_bit_cast(uint32_t,
+                              __builtin_amdgcn_cvt_pkrtz(__uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u)));
+}
+__device__ __forceinline__ u32x4 bf16x8_to_f16(u32x4 v) {
+    return u32x4{bf16x2_to_f16x2(v.x), bf16x2_to_f16x2(v.y), bf16x2_to_f16x2(v.z), bf16x2_to_f16x2(v.w)};
+}
+
+// One 32x32x16 MFMA on bf16 (H false) or fp16 (H true) operands.
+template <bool H>
+__device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
+    if constexpr (H)
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c,
+                                                      0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
+                                                       c, 0, 0, 0);
+}
+
+// fp32 to fp16 bits, round to nearest even, saturated to +-65504.
+__device__ __forceinline__ uint16_t f32_to_f16_sat(float v) {
+    return __builtin_bit_cast(uint16_t, (_Float16)fminf(fmaxf(v, -65504.f), 65504.f));
+}
+
 // silu(g) * v with the hardware reciprocal (v_rcp_f32, 1 ulp) in place of
 // the IEEE division: the grouped GEMM's epilogue runs on one wave a SIMD,
 // where the division's ten dependent instructions per element show.
@@ -251,8 +299,10 @@ __device__ __forceinline__ float silu_mul_rcp(float g, float v) {
 // Each block's products are accumulated by the MFMAs separately and added to
 // the accumulator times the column's scale.  (Stages of 128 elements with
 // 32-row tiles measured no faster for Q8_0.)
-template <int KIND, bool AS, int MB, int BF>
+template <int KIND, int AF, int MB, int BF>
 __global__ __launch_bounds__(kGThreads, 1) void k_gemm_lds(GemmArgs a) {
+    constexpr bool AS = AF == AF_SPLIT;            // split bf16 A
+    constexpr bool AH = AF == AF_F16;              // fp16 A (and B converted to fp16)
     constexpr bool BQ = BF == 1;                   // Q8_0 B
     constexpr bool BX = BF == 2;                   // MXFP4 B
     constexpr bool BS = BQ || BX;                  // block-scaled B
@@ -457,18 +507,23 @@ __global__ __launch_bounds__(kGThreads, 1) void k_gemm_lds(GemmArgs a) {
 #pragma unroll
                     for (int nb = 0; nb < NB; nb++) {
                         u32x4 bv;
-                        bv.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q[nb], 1.0f, 0));
-                        bv.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q[nb], 1.0f, 1));
-                        bv.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q[nb], 1.0f, 2));
-                        bv.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q[nb], 1.0f, 3));
+                        if constexpr (AH) {
+                            bv.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(q[nb], 1.0f, 0));
+                            bv.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(q[nb], 1.0f, 1));
+                            bv.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(q[nb], 1.0f, 2));
+                            bv.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(q[nb], 1.0f, 3));
+                        } else {
+                            bv.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q[nb], 1.0f, 0));
+                            bv.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q[nb], 1.0f, 1));
+                            bv.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q[nb], 1.0f, 2));
+                            bv.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q[nb], 1.0f, 3));
+                        }
 #pragma unroll
                         for (int mb = 0; mb < MB; mb++)
 #pragma unroll
                             for (int h = 0; h < AP; h++) {
                                 const f32x16 c = (s == 2 * bl && h == 0) ? f32x16{} : blk[mb][nb];
-                                blk[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                                    __builtin_bit_cast(bf16x8, v[AP * mb + h]), __builtin_bit_cast(bf16x8, bv), c,
-                                    0, 0, 0);
+                                blk[mb][nb] = mfma32<AH>(v[AP * mb + h], bv, c);
                             }
                     }
                 }
@@ -503,15 +558,15 @@ __global__ __launch_bounds__(kGThreads, 1) void k_gemm_lds(GemmArgs a) {
                 }
                 if (kn >= 0) issue_part(kn, nxt, xn, s, BK / 16);
                 lds_wait(v);
+                if constexpr (AH)
+#pragma unroll
+                    for (int nb = 0; nb < NB; nb++) v[nb] = bf16x8_to_f16(v[nb]);
 #pragma unroll
                 for (int mb = 0; mb < MB; mb++)
 #pragma unroll
                     for (int nb = 0; nb < NB; nb++)
 #pragma unroll
-                        for (int h = 0; h < AP; h++)
-                            acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                                __builtin_bit_cast(bf16x8, v[NB + AP * mb + h]), __builtin_bit_cast(bf16x8, v[nb]),
-                                acc[mb][nb], 0, 0, 0);
+                        for (int h = 0; h < AP; h++) acc[mb][nb] = mfma32<AH>(v[NB + AP * mb + h], v[nb], acc[mb][nb]);
             }
         } else {
             // this lane's columns' scales of the stage: fp16 pairs (blocks 2j, 2j+1)
@@ -557,15 +612,13 @@ __global__ __launch_bounds__(kGThreads, 1) void k_gemm_lds(GemmArgs a) {
                     }
 #pragma unroll
                     for (int nb = 0; nb < NB; nb++) {
-                        const u32x4 bv = q8x8_to_bf16(q[nb]);
+                        const u32x4 bv = AH ? q8x8_to_f16(q[nb]) : q8x8_to_bf16(q[nb]);
 #pragma unroll
                         for (int mb = 0; mb < MB; mb++)
 #pragma unroll
                             for (int h = 0; h < AP; h++) {
                                 const f32x16 c = (s == 2 * bl && h == 0) ? f32x16{} : blk[mb][nb];
-                                blk[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                                    __builtin_bit_cast(bf16x8, v[AP * mb + h]), __builtin_bit_cast(bf16x8, bv), c,
-                                    0, 0, 0);
+                                blk[mb][nb] = mfma32<AH>(v[AP * mb + h], bv, c);
                             }
                     }
                 }
@@ -647,12 +700,9 @@ __global__ __launch_bounds__(kGThreads, 1) void k_gemm_lds(GemmArgs a) {
                 }
                 const float h = silu_mul_rcp(gv, uv);
                 if (in && i < N) {
-                    if (a.out_split) {
-                        uint16_t *srow = reinterpret_cast<uint16_t *>(a.out) + (size_t)(p0 + m) * a.ldo * 2;
-                        const uint32_t hi = f32_to_bf16_rne(h);
-                        __builtin_nontemporal_store((uint16_t)hi, srow + split_pos(i));
-                        __builtin_nontemporal_store((uint16_t)f32_to_bf16_rne(h - __uint_as_float(hi << 16)),
-                                                    srow + split_pos(i) + 8);
+                    if (a.out_fmt == ACT_F16) {
+                        uint16_t *hrow = reinterpret_cast<uint16_t *>(a.out) + (size_t)(p0 + m) * a.ldo;
+                        __builtin_nontemporal_store(f32_to_f16_sat(h), hrow + i);
                     } else {
                         __builtin_nontemporal_store(h, a.out + ks * a.slab + (size_t)(p0 + m) * a.ldo + i);
                     }
@@ -848,15 +898,7 @@ __global__ __launch_bounds__(kGThreads, 2) void k_gemm_reg(GemmArgs a) {
                         gv = clampf(gv, a.limit);
                         uv = clampf(uv, a.limit);
                     }
-                    const float h = silu_mul(gv, uv);
-                    if (a.out_split) {
-                        uint16_t *srow = reinterpret_cast<uint16_t *>(a.out) + (size_t)(p0 + m) * a.ldo * 2;
-                        const uint32_t hi = f32_to_bf16_rne(h);
-                        srow[split_pos(i)] = (uint16_t)hi;
-                        srow[split_pos(i) + 8] = (uint16_t)f32_to_bf16_rne(h - __uint_as_float(hi << 16));
-                    } else {
-                        orow[i] = h;
-                    }
+                    orow[i] = silu_mul(gv, uv);
                 }
             } else {
 #pragma unroll
@@ -869,26 +911,26 @@ __global__ __launch_bounds__(kGThreads, 2) void k_gemm_reg(GemmArgs a) {
     }
 }
 
-// a_mode: 0 = bf16 A rows (gate/up), 1 = split A rows (hi/lo pairs: act of down, or the fused
-// layer's normed x of gate/up), 2 = fp32 A rows (down).  bq: B format (0 bf16,
-// 1 Q8_0, 2 MXFP4; a.s0 / a.s1 hold the block scales); fp32 A takes bf16 B only.
-template <int KIND, bool AS, int MB>
+// a_mode: 0 = bf16 A rows (gate/up), 1 = split A rows (the fused layer's normed x, gate/up),
+// 2 = fp32 A rows (down), 3 = fp16 A rows (act of down).  bq: B format (0 bf16, 1 Q8_0,
+// 2 MXFP4; a.s0 / a.s1 hold the block scales); fp32 A takes bf16 B only.
+template <int KIND, int AF, int MB>
 static void launch_lds_b(const GemmArgs &a, int bf, unsigned grid, hipStream_t s) {
     if (bf == 1) {
         // (run_gemm refuses wide tiles with Q8_0 weights)
-        if constexpr (MB != kMBWide) launch_kernel((k_gemm_lds<KIND, AS, MB, 1>), dim3(grid), dim3(kGThreads), 0, s, a);
+        if constexpr (MB != kMBWide) launch_kernel((k_gemm_lds<KIND, AF, MB, 1>), dim3(grid), dim3(kGThreads), 0, s, a);
     }
-    else if (bf == 2) launch_kernel((k_gemm_lds<KIND, AS, MB, 2>), dim3(grid), dim3(kGThreads), 0, s, a);
-    else launch_kernel((k_gemm_lds<KIND, AS, MB, 0>), dim3(grid), dim3(kGThreads), 0, s, a);
+    else if (bf == 2) launch_kernel((k_gemm_lds<KIND, AF, MB, 2>), dim3(grid), dim3(kGThreads), 0, s, a);
+    else launch_kernel((k_gemm_lds<KIND, AF, MB, 0>), dim3(grid), dim3(kGThreads), 0, s, a);
 }
 
-template <int KIND, bool AS>
+template <int KIND, int AF>
 static void launch_lds(const GemmArgs &a, int bf, unsigned grid, hipStream_t s) {
-    if (a.tile_rows == 32) launch_lds_b<KIND, AS, 1>(a, bf, grid, s);
-    else if (a.tile_rows == 64) launch_lds_b<KIND, AS, 2>(a, bf, grid, s);
-    else if (a.tile_rows == 96) launch_lds_b<KIND, AS, 3>(a, bf, grid, s);
-    else if (a.tile_rows == kBMWide) launch_lds_b<KIND, AS, kMBWide>(a, bf, grid, s);
-    else launch_lds_b<KIND, AS, kMB>(a, bf, grid, s);
+    if (a.tile_rows == 32) launch_lds_b<KIND, AF, 1>(a, bf, grid, s);
+    else if (a.tile_rows == 64) launch_lds_b<KIND, AF, 2>(a, bf, grid, s);
+    else if (a.tile_rows == 96) launch_lds_b<KIND, AF, 3>(a, bf, grid, s);
+    else if (a.tile_rows == kBMWide) launch_lds_b<KIND, AF, kMBWide>(a, bf, grid, s);
+    else launch_lds_b<KIND, AF, kMB>(a, bf, grid, s);
 }
 
 // B format of a weight dtype: 0 bf16, 1 Q8_0, 2 MXFP4.
@@ -911,9 +953,9 @@ static hipError_t run_gemm(int kind, int a_mode, int bq, GemmArgs &a, hipStream_
         const unsigned grid = (unsigned)((long)a.max_tiles * a.units);
         if (a.tile_rows != 32 && a.tile_rows != 64 && a.tile_rows != 96 && a.tile_rows != kBM && !(a.tile_rows == kBMWide && bq != 1))
             return hipErrorInvalidValue;
-        if (kind == GK_GATEUP && a_mode == 0) launch_lds<GK_GATEUP, false>(a, bq, grid, s);
-        else if (kind == GK_GATEUP && a_mode == 1) launch_lds<GK_GATEUP, true>(a, bq, grid, s);
-        else if (kind == GK_PLAIN && a_mode == 1) launch_lds<GK_PLAIN, true>(a, bq, grid, s);
+        if (kind == GK_GATEUP && a_mode == 0) launch_lds<GK_GATEUP, AF_BF16>(a, bq, grid, s);
+        else if (kind == GK_GATEUP && a_mode == 1) launch_lds<GK_GATEUP, AF_SPLIT>(a, bq, grid, s);
+        else if (kind == GK_PLAIN && a_mode == 3) launch_lds<GK_PLAIN, AF_F16>(a, bq, grid, s);
         else return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -942,7 +984,7 @@ int down_ksplit(const Layer &L, int M, int tile_rows) {
 
 hipError_t launch_gateup_mfma(const Layer &L, const void *x, const float *tok_scale, const Mats &routed,
                               const Mats &shared, const Routing &rt, int M, int max_tiles, int tile_rows,
-                              float *act, float *shared_act, bool act_split, hipStream_t s, bool x_split) {
+                              float *act, float *shared_act, int act_fmt, hipStream_t s, bool x_split) {
     const int a_mode = x_split ? 1 : 0;
     if (act) {
         GemmArgs a{};
@@ -966,7 +1008,7 @@ hipError_t launch_gateup_mfma(const Layer &L, const void *x, const float *tok_sc
         a.limit = L.limit;
         a.out = act;
         a.ldo = L.I;
-        a.out_split = act_split;
+        a.out_fmt = act_fmt;
         hipError_t err = run_gemm(GK_GATEUP, a_mode, b_format(L.edt), a, s);
         if (err != hipSuccess) return err;
     }
@@ -986,7 +1028,7 @@ hipError_t launch_gateup_mfma(const Layer &L, const void *x, const float *tok_sc
         a.limit = 0.f; // the shared expert is not clamped
         a.out = shared_act;
         a.ldo = L.Is;
-        a.out_split = act_split;
+        a.out_fmt = act_fmt;
         return run_gemm(GK_GATEUP, a_mode, b_format(L.sdt), a, s);
     }
     return hipSuccess;
@@ -994,8 +1036,9 @@ hipError_t launch_gateup_mfma(const Layer &L, const void *x, const float *tok_sc
 
 hipError_t launch_down_mfma(const Layer &L, const float *act, const float *shared_act,
                             const Mats &routed, const Mats &shared, const Routing &rt, int M,
-                            int max_tiles, int tile_rows, float *y_routes, float *y_shared, bool act_split,
+                            int max_tiles, int tile_rows, float *y_routes, float *y_shared, int act_fmt,
                             hipStream_t s) {
+    const int a_mode = act_fmt == ACT_F16 ? 3 : 2;
     if (act) {
         GemmArgs a{};
         a.a = act;
@@ -1014,14 +1057,14 @@ hipError_t launch_down_mfma(const Layer &L, const float *act, const float *share
         a.K = L.I;
         a.out = y_routes;
         a.ldo = L.H;
-        hipError_t err = run_gemm(GK_PLAIN, act_split ? 1 : 2, b_format(L.edt), a, s);
+        hipError_t err = run_gemm(GK_PLAIN, a_mode, b_format(L.edt), a, s);
         if (err != hipSuccess) return err;
     }
     if (shared_act && L.Is > 0) {
         GemmArgs a{};
         a.a = shared_act;
         a.M = M;
-        a.tile_rows = act_split && M <= 32 ? 32 : kBM;
+        a.tile_rows = act_fmt != ACT_F32 && M <= 32 ? 32 : kBM;
         a.max_tiles = (M + a.tile_rows - 1) / a.tile_rows;
         a.b0 = static_cast<const uint16_t *>(shared.down);
         a.s0 = static_cast<const uint16_t *>(shared.down_s);
@@ -1029,7 +1072,7 @@ hipError_t launch_down_mfma(const Layer &L, const float *act, const float *share
         a.K = L.Is;
         a.out = y_shared;
         a.ldo = L.H;
-        return run_gemm(GK_PLAIN, act_split ? 1 : 2, b_format(L.sdt), a, s);
+        return run_gemm(GK_PLAIN, a_mode, b_format(L.sdt), a, s);
     }
     return hipSuccess;
 }

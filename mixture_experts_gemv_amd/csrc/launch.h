@@ -105,13 +105,15 @@ hipError_t launch_router_mfma(const Layer &L, const void *x, const void *router,
 // x_split: x rows are split bf16 hi/lo pairs (launch_norm_apply's xs) rather than bf16.
 hipError_t launch_gateup_mfma(const Layer &L, const void *x, const float *tok_scale, const Mats &routed,
                               const Mats &shared, const Routing &rt, int M, int max_tiles, int tile_rows,
-                              float *act, float *shared_act, bool act_split, hipStream_t s,
+                              float *act, float *shared_act, int act_fmt, hipStream_t s,
                               bool x_split = false);
-// act_split: act / shared_act rows hold the hi/lo bf16 pairs the gate/up GEMM
-// writes with act_split (same size as fp32 rows); else fp32 rows.
+// act_fmt: the rows of act / shared_act.  ACT_F32: fp32 rows; ACT_F16: fp16
+// rows (values beyond +-65504 saturate), which the down GEMM multiplies on
+// fp16 MFMAs.
+enum ActFormat { ACT_F32 = 0, ACT_F16 = 1 };
 hipError_t launch_down_mfma(const Layer &L, const float *act, const float *shared_act,
                             const Mats &routed, const Mats &shared, const Routing &rt, int M,
-                            int max_tiles, int tile_rows, float *y_routes, float *y_shared, bool act_split,
+                            int max_tiles, int tile_rows, float *y_routes, float *y_shared, int act_fmt,
                             hipStream_t s);
 
 hipError_t launch_q8_split(const void *blocks, int64_t rows, int cols, int8_t *qs,

@@ -370,7 +370,7 @@ moe_status moe_expert_ffn(const moe_plan *p, const void *x, const moe_weights *w
     const moe::Mats none{};
     if (use_mfma(p, M))
         LAUNCH(moe::launch_gateup_mfma(L, x, sc, routed_mats(wts), none, rt, M, lay.max_tiles, moe::mfma_tile_rows(),
-                                       act, nullptr, false, s),
+                                       act, nullptr, moe::ACT_F32, s),
                "gate/up (MFMA)");
     else
         LAUNCH(moe::launch_gateup_gemv(L, x, sc, routed_mats(wts), none, rt, M, act, nullptr, s), "gate/up");
@@ -404,7 +404,7 @@ moe_status moe_combine(const moe_plan *p, const float *act, const moe_weights *w
     if (use_mfma(p, M) && L.edt == moe::DT_BF16) {
         float *yr = at<float>(ws, lay.y_routes);
         LAUNCH(moe::launch_down_mfma(L, act, nullptr, routed_mats(wts), none, rt, M, lay.max_tiles, moe::mfma_tile_rows(),
-                                     yr, nullptr, false, s),
+                                     yr, nullptr, moe::ACT_F32, s),
                "down (MFMA)");
         LAUNCH(moe::launch_combine(L, yr, nullptr, route_pos, w, seed, M, y, s,
                                    moe::down_ksplit(L, M, moe::mfma_tile_rows()), 0),
@@ -531,11 +531,11 @@ static moe_status forward_impl(const moe_plan *p, const void *x, const moe_weigh
     float *ysh = L.Is > 0 ? at<float>(ws, lay.y_shared) : nullptr;
     if (mfma) {
         STAGE(rec, moe::launch_gateup_mfma(L, xsplit ? (const void *)xsplit : x, sc, routed_mats(wts),
-                                           shared_mats(wts), rt, M, lay.max_tiles, rows, act, sact, true, s,
+                                           shared_mats(wts), rt, M, lay.max_tiles, rows, act, sact, moe::ACT_F16, s,
                                            xsplit != nullptr),
               "gate/up (MFMA)", MOE_STAGE_GATEUP);
         STAGE(rec, moe::launch_down_mfma(L, act, sact, routed_mats(wts), shared_mats(wts), rt, M,
-                                         lay.max_tiles, rows, yr, ysh, true, s),
+                                         lay.max_tiles, rows, yr, ysh, moe::ACT_F16, s),
               "down (MFMA)", MOE_STAGE_DOWN);
         STAGE(rec, moe::launch_combine(L, yr, ysh, rpos, w, residual, M, y, s, moe::down_ksplit(L, M, rows), 1),
               "combine", MOE_STAGE_COMBINE);
