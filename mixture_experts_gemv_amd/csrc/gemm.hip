@@ -1078,82 +1078,144 @@ hipError_t launch_down_mfma(const Layer &L, const float *act, const float *share
 }
 
 // ------------------------------------------------------------------ router
-// logits[t][e] = scale[t] * x[t] . router[e] for many tokens: one workgroup
-// per tile of 16 tokens x 16 experts, v_mfma_f32_16x16x32_bf16 over K.  The
-// kRtWaves waves split the 32-element K steps into contiguous ranges; each
-// wave loads kRtUnroll steps of both operands from global (L2) straight into
-// registers before using them.  The waves' partial tiles meet in LDS and are
-// summed in wave order.  XS: x rows are split bf16 hi/lo pairs (the fused
-// layer's normed rows), and each step runs one MFMA per half.
+// Router logits of the grouped-GEMM path, in reduction slices: workgroup
+// (tile, s) computes part[s][t][e] = x[t] . router[e] over slice s of the
+// reduction (32-element steps [s NS / S, (s+1) NS / S), at most
+// kRpMaxSteps) for the 64 tokens of its tile and every expert, with
+// v_mfma_f32_16x16x32_bf16.  The top-k kernel adds the S slices in slice
+// order and applies the token scale.  x is read once: the tile's rows of the
+// slice are staged in LDS, padded so that a row starts 64 bytes past a
+// multiple of 512 (the 16-byte fragment reads of 16 rows and 4 k-groups then
+// fall on 32 distinct bank groups); the router fragments go straight into
+// registers, all issued before the staging.  Waves own expert tiles (16
+// experts) w, w + 4, .. with all 4 token tiles when there are at least 4
+// expert tiles, else token tile w with every expert tile (NJ: expert tiles a
+// wave).  Workgroup b takes slice b % S.  (It replaced a kernel of one
+// workgroup per 16 tokens x 16 experts over the whole reduction, whose
+// workgroups each re-read x and the router rows: Qwen3-shaped M = 2048,
+// 134 MB of L2 reads for 8.9 MB of operands.)  XS: x rows are split bf16
+// hi/lo pairs (the fused layer's normed rows), one MFMA per half.
 typedef float f32x4m __attribute__((ext_vector_type(4)));
-constexpr int kRtWaves = 8;
-constexpr int kRtUnroll = 8;
+constexpr int kRpTok = 64;
+constexpr int kRpMaxSteps = 8;
 
-template <bool XS>
-__global__ __launch_bounds__(kRtWaves * kWave) void k_router_mfma16(const uint16_t *x, const uint16_t *router,
-                                                                   const float *tok_scale, int M, int E, int K,
-                                                                   float *logits) {
-    __shared__ f32x4m s_part[kRtWaves][kWave];
-    const int lane = threadIdx.x & 63, wave = uniform(threadIdx.x >> 6);
-    const int ntE = (E + 15) / 16;
-    const int tm = blockIdx.x / ntE, te = blockIdx.x % ntE;
-    const int t = min(tm * 16 + (lane & 15), M - 1);
-    const int e = min(te * 16 + (lane & 15), E - 1);
-    // split rows: per 8 elements 8 hi then 8 lo values, so element k sits at
-    // 2k (hi) and 2k + 8 (lo) for k a multiple of 8
-    const uint16_t *arow = XS ? x + (size_t)t * K * 2 + 16 * (lane >> 4) : x + (size_t)t * K + 8 * (lane >> 4);
-    const uint16_t *brow = router + (size_t)e * K + 8 * (lane >> 4);
-    const int NS = K / 32, s0 = wave * NS / kRtWaves, s1 = (wave + 1) * NS / kRtWaves;
-    f32x4m acc = {0.f, 0.f, 0.f, 0.f};
-    for (int sb = s0; sb < s1; sb += kRtUnroll) {
-        u32x4 av[kRtUnroll], al[kRtUnroll], bv[kRtUnroll];
+int router_slices(const Layer &L, int M) {
+    const int NS = L.H / 32, tiles = (M + kRpTok - 1) / kRpTok;
+    int S = (NS + kRpMaxSteps - 1) / kRpMaxSteps;
+    while (S < 16 && (long)tiles * S < 256 && 2 * S <= NS) S *= 2;
+    return std::min(std::max(S, (NS + kRpMaxSteps - 1) / kRpMaxSteps), NS);
+}
+
+template <bool XS, int NJ, bool BYE>
+__global__ __launch_bounds__(256) void k_router_part(const uint16_t *x, const uint16_t *router, int M, int E, int K,
+                                                     int S, float *part) {
+    constexpr int AP = XS ? 2 : 1;
+    constexpr int MT = BYE ? 4 : 1; // token tiles a wave
+    __shared__ __align__(16) unsigned char s_x[kRpTok * (kRpMaxSteps * 64 * AP + 64)];
+    const int tid = threadIdx.x, lane = tid & 63, wave = uniform(tid >> 6);
+    const int s = blockIdx.x % S, t0 = (blockIdx.x / S) * kRpTok;
+    const int NS = K / 32, st0 = s * NS / S, nst = (s + 1) * NS / S - st0; // 1 <= nst <= kRpMaxSteps
+    const int rowb = (nst * 64 * AP + 511) / 512 * 512 + 64;
+    // router fragments: expert tile n_j, 8 reduction elements (lane / 16) of
+    // each step (steps past the slice repeat its last; they are not used)
+    u32x4 bf[NJ][kRpMaxSteps];
 #pragma unroll
-        for (int u = 0; u < kRtUnroll; u++) {
-            const int k = 32 * min(sb + u, s1 - 1);
-            if constexpr (XS) {
-                av[u] = *reinterpret_cast<const u32x4 *>(arow + 2 * k);
-                al[u] = *reinterpret_cast<const u32x4 *>(arow + 2 * k + 8);
-            } else {
-                av[u] = *reinterpret_cast<const u32x4 *>(arow + k);
-            }
-            bv[u] = *reinterpret_cast<const u32x4 *>(brow + k);
+    for (int j = 0; j < NJ; j++) {
+        const int n = BYE ? wave + 4 * j : j;
+        const int e = min(n * 16 + (lane & 15), E - 1);
+        const uint16_t *row = router + (size_t)e * K + st0 * 32 + (lane >> 4) * 8;
+#pragma unroll
+        for (int st = 0; st < kRpMaxSteps; st++)
+            bf[j][st] = *reinterpret_cast<const u32x4 *>(row + min(st, nst - 1) * 32);
+    }
+    // stage the tile's x rows of the slice (16-byte chunks; rows past M repeat
+    // row M - 1, chunks past the slice repeat its last)
+    {
+        const int cpr = nst * 4 * AP;
+        constexpr int CPR = kRpMaxSteps * 4 * AP, U = kRpTok * CPR / 256;
+        u32x4 v[U];
+#pragma unroll
+        for (int u = 0; u < U; u++) {
+            const int i = u * 256 + tid, r = i / CPR, c = min(i % CPR, cpr - 1), t = min(t0 + r, M - 1);
+            v[u] = *reinterpret_cast<const u32x4 *>(x + ((size_t)t * K + st0 * 32) * AP + c * 8);
         }
 #pragma unroll
-        for (int u = 0; u < kRtUnroll; u++)
-            if (sb + u < s1) {
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av[u]),
-                                                              __builtin_bit_cast(bf16x8, bv[u]), acc, 0, 0, 0);
-                if constexpr (XS)
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, al[u]),
-                                                                  __builtin_bit_cast(bf16x8, bv[u]), acc, 0, 0, 0);
-            }
+        for (int u = 0; u < U; u++) {
+            const int i = u * 256 + tid, r = i / CPR, c = i % CPR;
+            if (c < cpr) *reinterpret_cast<u32x4 *>(s_x + r * rowb + c * 16) = v[u];
+        }
     }
-    s_part[wave][lane] = acc;
     __syncthreads();
-    if (wave != 0) return;
-    f32x4m sum = s_part[0][lane];
+    f32x4m acc[MT][NJ];
 #pragma unroll
-    for (int w = 1; w < kRtWaves; w++) sum += s_part[w][lane];
-    const int col = te * 16 + (lane & 15);
+    for (int mt = 0; mt < MT; mt++)
 #pragma unroll
-    for (int r = 0; r < 4; r++) {
-        const int row = tm * 16 + 4 * (lane >> 4) + r;
-        if (row < M && col < E) logits[(size_t)row * E + col] = sum[r] * (tok_scale ? tok_scale[row] : 1.0f);
+        for (int j = 0; j < NJ; j++) acc[mt][j] = f32x4m{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int st = 0; st < kRpMaxSteps; st++) {
+        if (st < nst) {
+#pragma unroll
+            for (int mt = 0; mt < MT; mt++) {
+                const int r = (BYE ? mt : wave) * 16 + (lane & 15);
+                const unsigned char *ap = s_x + r * rowb + (st * 4 + (lane >> 4)) * 16 * AP;
+                const u32x4 ah = *reinterpret_cast<const u32x4 *>(ap);
+                u32x4 al;
+                if constexpr (XS) al = *reinterpret_cast<const u32x4 *>(ap + 16);
+#pragma unroll
+                for (int j = 0; j < NJ; j++) {
+                    acc[mt][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ah),
+                                                                         __builtin_bit_cast(bf16x8, bf[j][st]),
+                                                                         acc[mt][j], 0, 0, 0);
+                    if constexpr (XS)
+                        acc[mt][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, al),
+                                                                             __builtin_bit_cast(bf16x8, bf[j][st]),
+                                                                             acc[mt][j], 0, 0, 0);
+                }
+            }
+        }
+    }
+    // D rows are tokens (4 (lane / 16) + r), columns experts (lane % 16)
+    float *ps = part + (size_t)s * M * E;
+#pragma unroll
+    for (int mt = 0; mt < MT; mt++) {
+#pragma unroll
+        for (int j = 0; j < NJ; j++) {
+            const int n = BYE ? wave + 4 * j : j;
+            const int e = n * 16 + (lane & 15);
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+                const int t = t0 + (BYE ? mt : wave) * 16 + 4 * (lane >> 4) + r;
+                if (t < M && e < E) ps[(size_t)t * E + e] = acc[mt][j][r];
+            }
+        }
     }
 }
 
-hipError_t launch_router_mfma(const Layer &L, const void *x, const void *router, const float *tok_scale,
-                              int M, float *logits, hipStream_t s, bool x_split) {
-    if (L.H % 32) return hipErrorInvalidValue;
-    const int tiles = ((M + 15) / 16) * ((L.E + 15) / 16);
+template <bool XS>
+static void launch_router_part(const uint16_t *x, const uint16_t *router, int M, int E, int K, int S, float *part,
+                               hipStream_t s) {
+    const int NT = (E + 15) / 16;
+    const dim3 grid((unsigned)(((M + kRpTok - 1) / kRpTok) * S));
+#define RP_LAUNCH(NJ, BYE) launch_kernel((k_router_part<XS, NJ, BYE>), grid, dim3(256), 0, s, x, router, M, E, K, S, part)
+    if (NT == 1) RP_LAUNCH(1, false);
+    else if (NT == 2) RP_LAUNCH(2, false);
+    else if (NT == 3) RP_LAUNCH(3, false);
+    else if (NT <= 4) RP_LAUNCH(1, true);
+    else if (NT <= 8) RP_LAUNCH(2, true);
+    else if (NT <= 12) RP_LAUNCH(3, true);
+    else RP_LAUNCH(4, true);
+#undef RP_LAUNCH
+}
+
+hipError_t launch_router_mfma(const Layer &L, const void *x, const void *router, int M, float *part, int S,
+                              hipStream_t s, bool x_split) {
+    if (L.H % 32 || L.E > 256 || S < 1 || (L.H / 32 + S - 1) / S > kRpMaxSteps) return hipErrorInvalidValue;
     if (x_split)
-        launch_kernel(k_router_mfma16<true>, dim3(tiles), dim3(kRtWaves * kWave), 0, s,
-                      static_cast<const uint16_t *>(x), static_cast<const uint16_t *>(router), tok_scale, M,
-                      L.E, L.H, logits);
+        launch_router_part<true>(static_cast<const uint16_t *>(x), static_cast<const uint16_t *>(router), M, L.E,
+                                 L.H, S, part, s);
     else
-        launch_kernel(k_router_mfma16<false>, dim3(tiles), dim3(kRtWaves * kWave), 0, s,
-                      static_cast<const uint16_t *>(x), static_cast<const uint16_t *>(router), tok_scale, M,
-                      L.E, L.H, logits);
+        launch_router_part<false>(static_cast<const uint16_t *>(x), static_cast<const uint16_t *>(router), M, L.E,
+                                  L.H, S, part, s);
     return hipGetLastError();
 }
 

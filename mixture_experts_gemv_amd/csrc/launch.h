@@ -50,6 +50,17 @@ hipError_t launch_topk(const Layer &L, const float *logits, const float *bias, i
 hipError_t launch_permute(int E, int R, int tile_rows, const int32_t *ids, int32_t *counts,
                           int32_t *offsets, int32_t *sorted, int32_t *route_pos, int32_t *active,
                           int32_t *tiles, hipStream_t s);
+// Top-k from S slices of partial logits part [S][M][E] (summed in slice
+// order, times tok_scale[t] when given), writing also the expert counts of
+// each group of tokens, hist [topk_hist_groups(M)][E]; then the stable
+// scatter of the routes from ids and hist (several workgroups), with the
+// outputs of launch_permute.
+int topk_hist_groups(int M);
+hipError_t launch_topk_hist(const Layer &L, const float *part, int S, const float *tok_scale, const float *bias,
+                            int M, int32_t *ids, float *w, int32_t *hist, hipStream_t s);
+hipError_t launch_scatter(int E, int M, int k, int tile_rows, const int32_t *ids, const int32_t *hist,
+                          int32_t *counts, int32_t *offsets, int32_t *sorted, int32_t *route_pos, int32_t *active,
+                          int32_t *tiles, hipStream_t s);
 // Router + top-k + permutation for M <= route_small_max_tokens() (two launches).
 int route_small_max_tokens();
 hipError_t launch_route_small(const Layer &L, const void *x, const RouterW &rw, const float *bias,
@@ -100,9 +111,12 @@ hipError_t launch_down_m1(const Layer &L, const float *act, const float *shared_
 int mfma_tile_rows();                          // tiles of the stage-wise entry points
 int mfma_tile_rows(const Layer &L, int M);     // tiles of the layer call for M tokens
 bool mfma_supported(const Layer &L);
-hipError_t launch_router_mfma(const Layer &L, const void *x, const void *router, const float *tok_scale,
-                              int M, float *logits, hipStream_t s, bool x_split = false);
+// Partial router logits part [S][M][E] over S = router_slices(L, M) slices
+// of the reduction (bf16 router; the token scale is left to the top-k).
 // x_split: x rows are split bf16 hi/lo pairs (launch_norm_apply's xs) rather than bf16.
+int router_slices(const Layer &L, int M);
+hipError_t launch_router_mfma(const Layer &L, const void *x, const void *router, int M, float *part, int S,
+                              hipStream_t s, bool x_split = false);
 hipError_t launch_gateup_mfma(const Layer &L, const void *x, const float *tok_scale, const Mats &routed,
                               const Mats &shared, const Routing &rt, int M, int max_tiles, int tile_rows,
                               float *act, float *shared_act, int act_fmt, hipStream_t s,

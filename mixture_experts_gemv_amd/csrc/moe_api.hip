@@ -43,7 +43,7 @@ size_t up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 // Where each workspace region starts for a call with M tokens.
 struct WsLayout {
-    size_t tok_scale, logits, ids, w, counts, offsets, sorted, route_pos, active, tiles;
+    size_t tok_scale, logits, ids, w, counts, offsets, sorted, route_pos, active, tiles, hist;
     size_t act, shared_act, y_routes, y_shared, xn, xs, total;
     int max_tiles;
 };
@@ -77,6 +77,8 @@ WsLayout layout(const moe_plan *p, int M) {
     w.sorted = take(R * 4);
     w.route_pos = take(R * 4);
     w.active = take((size_t)(L.E + 1) * 4);
+    // per-group expert counts of the top-k (batches past the small-batch route)
+    w.hist = take((size_t)moe::topk_hist_groups(M) * L.E * 4);
     // tile capacity for the smaller of the two tile heights (the layer call's
     // or the stage-wise entry points')
     const int tile_rows = std::min(moe::mfma_tile_rows(), moe::mfma_tile_rows(L, M));
@@ -91,7 +93,10 @@ WsLayout layout(const moe_plan *p, int M) {
                                            moe::down_ksplit(L, M, moe::mfma_tile_rows(L, M)),
                                            L.edt != moe::DT_BF16 ? moe::down_gemv_slices(L.I, L.edt) : 1})
                                : moe::down_gemv_slices(L.I, L.edt);
-    w.y_routes = take(slices * R * L.H * 4);
+    // (the grouped-GEMM router's partial logits [S][M][E] live here until the
+    // top-k has read them)
+    w.y_routes = take(std::max(slices * R * L.H * 4,
+                               mfma ? (size_t)moe::router_slices(L, M) * M * L.E * 4 : (size_t)0));
     w.y_shared = take(L.Is > 0 ? (size_t)(mfma ? 1 : moe::down_gemv_slices(L.Is, L.sdt)) * M * L.H * 4 : 0);
     // the weighted pre-norm's rows (moe_forward_fused with a norm weight):
     // fp32, and split bf16 for the grouped GEMM; only plans with the pre-norm on
@@ -513,15 +518,25 @@ static moe_status forward_impl(const moe_plan *p, const void *x, const moe_weigh
                                            sorted, rpos, active, s),
               "route", MOE_STAGE_ROUTER);
     } else {
-        // (the MFMA router takes bf16 rows and no input scale; otherwise the GEMV router)
-        if (mfma && L.rdt == moe::DT_BF16 && !wts->router_x_scale && (L.xdt == moe::DT_BF16 || xsplit))
-            STAGE(rec, moe::launch_router_mfma(L, xsplit ? (const void *)xsplit : x, wts->router, sc, M, lg, s,
+        // (the MFMA router takes bf16 rows and no input scale, and leaves the
+        // token scale to the top-k; otherwise the GEMV router)
+        const float *part = lg, *part_scale = nullptr;
+        int S = 1;
+        if (mfma && L.rdt == moe::DT_BF16 && !wts->router_x_scale && (L.xdt == moe::DT_BF16 || xsplit)) {
+            S = moe::router_slices(L, M);
+            float *pw = at<float>(ws, lay.y_routes);
+            part = pw;
+            part_scale = sc;
+            STAGE(rec, moe::launch_router_mfma(L, xsplit ? (const void *)xsplit : x, wts->router, M, pw, S, s,
                                                xsplit != nullptr),
                   "router (MFMA)", MOE_STAGE_ROUTER);
-        else
+        } else {
             STAGE(rec, moe::launch_router(L, x, router_w(p, wts), sc, M, lg, s), "router", MOE_STAGE_ROUTER);
-        STAGE(rec, moe::launch_topk(L, lg, wts->bias, M, ids, w, s), "top-k", MOE_STAGE_TOPK);
-        STAGE(rec, moe::launch_permute(L.E, R, rows, ids, counts, offsets, sorted, rpos, active, tiles, s),
+        }
+        int32_t *hist = at<int32_t>(ws, lay.hist);
+        STAGE(rec, moe::launch_topk_hist(L, part, S, part_scale, wts->bias, M, ids, w, hist, s), "top-k",
+              MOE_STAGE_TOPK);
+        STAGE(rec, moe::launch_scatter(L.E, M, L.k, rows, ids, hist, counts, offsets, sorted, rpos, active, tiles, s),
               "permute", MOE_STAGE_PERMUTE);
     }
     const moe::Routing rt{offsets, sorted, rpos, active, tiles};
