@@ -1475,6 +1475,7 @@ hipError_t launch_down_m1(const Layer &L, const float *act, const float *shared_
 }
 
 // -------------------------------------------------------------------- combine
+constexpr int kCombineSlots = 8; // top-k slots a token (the plan's limit)
 // One thread per (token, 4 consecutive h): seed, then the shared expert's
 // slices in order, then slots j = 0..k-1, each slot's slices (partial sums of
 // a split reduction) summed in slice order before its weight is applied.
@@ -1493,17 +1494,33 @@ __global__ __launch_bounds__(256) void k_combine(const float *y_routes, const fl
         for (int sl = 1; sl < Ss; sl++) v += reinterpret_cast<const f32x4 *>(row + sl * slab_s)[c];
         acc += v;
     }
-    for (int j = 0; j < k; j++) {
-        const int r = t * k + j;
-        const float *row = y_routes + (size_t)route_pos[r] * H;
-        f32x4 v = reinterpret_cast<const f32x4 *>(row)[c];
-        for (int sl = 1; sl < S; sl++) v += reinterpret_cast<const f32x4 *>(row + sl * slab)[c];
-        const float wt = w[r];
-        acc.x = fmaf(wt, v.x, acc.x);
-        acc.y = fmaf(wt, v.y, acc.y);
-        acc.z = fmaf(wt, v.z, acc.z);
-        acc.w = fmaf(wt, v.w, acc.w);
-    }
+    // the slots' positions and weights, then (up to 8 slots) every slot's
+    // first slice, are loaded before any is used: two dependent round trips
+    // a thread instead of two a slot (Qwen3-shaped M = 2048, 134 MB of
+    // per-route rows: 28.1 against 30.8 us; Mixtral-shaped M = 512, 14.9
+    // against 15.2 us)
+    int rp[kCombineSlots];
+    float wt[kCombineSlots];
+#pragma unroll
+    for (int j = 0; j < kCombineSlots; j++)
+        if (j < k) {
+            rp[j] = route_pos[t * k + j];
+            wt[j] = w[t * k + j];
+        }
+    f32x4 v[kCombineSlots];
+#pragma unroll
+    for (int j = 0; j < kCombineSlots; j++)
+        if (j < k) v[j] = reinterpret_cast<const f32x4 *>(y_routes + (size_t)rp[j] * H)[c];
+#pragma unroll
+    for (int j = 0; j < kCombineSlots; j++)
+        if (j < k) {
+            const float *row = y_routes + (size_t)rp[j] * H;
+            for (int sl = 1; sl < S; sl++) v[j] += reinterpret_cast<const f32x4 *>(row + sl * slab)[c];
+            acc.x = fmaf(wt[j], v[j].x, acc.x);
+            acc.y = fmaf(wt[j], v[j].y, acc.y);
+            acc.z = fmaf(wt[j], v[j].z, acc.z);
+            acc.w = fmaf(wt[j], v[j].w, acc.w);
+        }
     reinterpret_cast<f32x4 *>(y + (size_t)t * H)[c] = acc;
 }
 
