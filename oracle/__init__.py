@@ -92,6 +92,7 @@ def lib():
         L.orc_element.argtypes = [P, ctypes.c_int, ctypes.c_longlong, ctypes.c_longlong,
                                   ctypes.c_longlong]
         L.orc_element.restype = ctypes.c_double
+        L.orc_down.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, P, ctypes.c_int, P, P]
         L.orc_set_mutant.argtypes = [ctypes.c_int]
         L.orc_threads.restype = ctypes.c_int
         _lib = L
@@ -200,6 +201,15 @@ def permute(E: int, ids: np.ndarray):
     rp = np.zeros(M * k, np.int32)
     lib().orc_permute(E, M, k, _ptr(ids), _ptr(counts), _ptr(offsets), _ptr(sr), _ptr(rp))
     return counts, offsets, sr, rp
+
+
+def down(spec, layer: Dict[str, Optional[np.ndarray]], e: int, act_row: np.ndarray) -> np.ndarray:
+    """Expert ``e``'s down projection of one act row ``[I]`` (fp64): ``[H]``."""
+    out = np.zeros(spec.hidden, np.float64)
+    a = np.ascontiguousarray(act_row, np.float64)
+    lib().orc_down(spec.hidden, spec.expert_inter, spec.expert_dtype, _ptr(layer["down"]), int(e), _ptr(a),
+                   _ptr(out))
+    return out
 
 
 def element(buf: np.ndarray, fmt: int, r: int, cols: int, c: int) -> float:

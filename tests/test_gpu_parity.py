@@ -8,8 +8,8 @@ import pytest
 import oracle
 import synth
 from synth import BF16, F32, MXFP4, Q8_0, BIAS_LOGIT, BIAS_SELECT_ONLY, SIGMOID_NORM, SOFTMAX_ALL_NORENORM
-from gpu_helpers import (SIGMOID_TAU, W_ABS, check_ids, check_ids_keys, check_y, device_layer,
-                         forward_parity, host_layer, say)
+from gpu_helpers import (SIGMOID_TAU, W_ABS, Y_REL_L2, check_ids, check_ids_keys, check_y, device_layer,
+                         forward_parity, host_layer, run_forward, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -359,6 +359,42 @@ def test_forward_mfma_small(name, kw, Ms):
         x = synth.make_tokens(spec, M, batch=5)
         say(f"forward (MFMA) {name} M={M}")
         forward_parity(spec, layer, x, dl, what=f"mfma {name} M={M}")
+
+
+def test_forward_mfma_act_saturates():
+    """The grouped-GEMM path carries act as fp16 and saturates values beyond
+    +-65504 (the reading of the pages' fp16 act rows, gptoss/state.rs,
+    BatchedRoutedScratch.batch_acts).  Weights of std 8 drive some act values
+    past the fp16 range: y stays finite and matches the oracle's layer with
+    its act rows clamped to +-65504, and not the unclamped one."""
+    import mixture_experts_gemv_amd as m
+    spec = synth.small_spec(name="act-sat", hidden=256, num_experts=8, top_k=2, expert_inter=128,
+                            weight_std=8.0, seed=1391)
+    layer = synth.make_layer(spec)
+    M = 64
+    dl = device_layer(spec, layer, M, path=m.MOE_PATH_MFMA)
+    x = synth.make_tokens(spec, M, batch=2)
+    say("forward (MFMA) act saturation")
+    y, ids, w, counts = run_forward(dl, x)
+    assert np.isfinite(y).all(), "non-finite output"
+    o = oracle.forward(spec, layer, x, want_act=True)
+    forced, near = check_ids(spec, layer, x, ids, o["ids"])
+    o = oracle.forward(spec, layer, x, forced_ids=forced, want_act=True)
+    act = o["act"]
+    sat = int((np.abs(act) > 65504.0).sum())
+    assert sat > 0, "no act value exceeds the fp16 range; the case does not test saturation"
+    clamped = np.clip(act, -65504.0, 65504.0)
+    k = spec.top_k
+    y_sat = np.zeros_like(o["y"])
+    for t in range(M):
+        for j in range(k):
+            y_sat[t] += o["w"][t, j] * oracle.down(spec, layer, o["ids"][t, j], clamped[t * k + j])
+    rel = lambda a, b: float(np.linalg.norm(a - b) / np.linalg.norm(b))
+    r_sat, r_raw = rel(y, y_sat), rel(y, o["y"])
+    say(f"act saturation: {sat} of {act.size} act values past 65504; rel-L2 against the clamped "
+        f"oracle {r_sat:.3e}, against the unclamped {r_raw:.3e} (near-tie tokens: {near})")
+    assert r_sat <= Y_REL_L2, f"rel-L2 {r_sat:.3e} against the clamped oracle"
+    assert r_raw > 4 * r_sat, "the output does not show the saturation"
 
 
 @pytest.mark.parametrize("wdt", [BF16, Q8_0, MXFP4], ids=["bf16", "q8", "mx4"])
