@@ -311,10 +311,21 @@ __global__ __launch_bounds__(kGThreads, 1) void k_gemm_lds(GemmArgs a) {
     constexpr int WCOLS = GemmShape<KIND>::WCOLS;
     constexpr int AP = AS ? 2 : 1;                 // bf16 values of A per element (split: hi, lo)
     constexpr int EB = BQ ? 1 : 2;                 // bytes per B element (bf16, Q8_0)
-    constexpr int BK = BS ? kStageK : kStageK / AP; // reduction elements per stage
+    // reduction elements per stage: 128 for block-scaled B with 32-row tiles
+    // (a Q8_0 column then takes a whole 128-byte line a stage, an MXFP4 one
+    // half a line, and a stage moves enough bytes to cover the copies'
+    // latency: Q8_0 at H = I = 2944, M = 64, 241 against 266 us a call;
+    // MXFP4, 205 against 298 us; at the gpt-oss shape, H = I = 2880 and so a
+    // half last stage, Q8_0 M = 64 272 against 283 us, MXFP4 M = 64 236
+    // against 292 us and M = 256 301 against 330 us; with 64-row tiles it
+    // measured slower), else 64 (32 for split A with bf16 B).  K need only be
+    // a multiple of 64: a last stage of 64 elements reads its missing half
+    // from the 64 elements before it and skips those blocks.
+    constexpr int BK = (BS && MB == 1) ? 2 * kStageK : (BS ? kStageK : kStageK / AP);
+    constexpr bool RAGGED = BK > 64;               // K may end half way into a stage
     constexpr int NBLK = BK / 32;                  // scale blocks per stage
     constexpr int SCP = BQ ? NBLK / 2 : 0;         // 4-byte scale copies per lane per stage
-    constexpr int SRG = BX ? NB : 0;               // MXFP4 scale loads per lane per stage
+    constexpr int SRG = BX ? NB * (NBLK / 2) : 0;  // MXFP4 2-byte scale loads per lane per stage
     constexpr int NST = kStages;                   // LDS stages
     constexpr int ARB = BK * 2 * AP;               // A bytes per row per stage
     constexpr int BRB = BX ? BK / 2 : BK * EB;     // B bytes per column per stage
@@ -329,7 +340,7 @@ __global__ __launch_bounds__(kGThreads, 1) void k_gemm_lds(GemmArgs a) {
     constexpr int B_DMA = WB_BYTES / (kWave * 16);        // B copies per wave per stage
     constexpr int LPS = A_DMA + B_DMA + SCP + SRG; // vector memory operations per lane per stage
     static_assert(!BQ || NBLK % 2 == 0, "Q8_0 scales are copied in pairs of blocks");
-    static_assert(!BX || NBLK == 2, "MXFP4 stages hold two scale blocks (one 2-byte load per column)");
+    static_assert(!BX || NBLK == 2 || NBLK == 4, "MXFP4 stages hold 2 or 4 scale blocks (one 32-bit word)");
     // one LDS array per stage, named explicitly in an NST-way unrolled loop
     // (measured faster than one array indexed by kt % NST)
     __shared__ __attribute__((aligned(16))) unsigned char sm0[ST_BYTES], sm1[ST_BYTES], sm2[ST_BYTES];
@@ -391,7 +402,7 @@ __global__ __launch_bounds__(kGThreads, 1) void k_gemm_lds(GemmArgs a) {
     }
     __syncthreads();
 
-    const int K = a.K, N = a.N, NKS = K / BK;
+    const int K = a.K, N = a.N, NKS = (K + BK - 1) / BK;
     const int kb = ks * NKS / a.ksplit, nk = (ks + 1) * NKS / a.ksplit - kb; // this slice's stages
     const int colw = nt * GemmShape<KIND>::COLS + wave * WCOLS;
     const bool wave_on = colw < N;
@@ -400,16 +411,21 @@ __global__ __launch_bounds__(kGThreads, 1) void k_gemm_lds(GemmArgs a) {
     // columns of one stage; lane i writes LDS bytes i*16..i*16+15, which hold
     // logical 16-byte chunk (slot ^ row) of its row: an XOR swizzle that keeps
     // the MFMA operand reads below free of most bank conflicts.
+    // (RAGGED: whether the copy's chunk lies in the second half of a stage)
     const char *asrc[A_DMA];
+    bool ahi[A_DMA];
 #pragma unroll
     for (int q = 0; q < A_DMA; q++) {
         const int r = (wave * A_DMA + q) * (kWave / ACH) + lane / ACH, c = (lane % ACH) ^ swz<ACH>(r);
         asrc[q] = s_src[r] + c * 16;
+        ahi[q] = 2 * c >= ACH;
     }
     const char *bsrc[B_DMA];
+    bool bhi[B_DMA];
 #pragma unroll
     for (int q = 0; q < B_DMA; q++) {
         const int cl = q * (kWave / BCH) + lane / BCH, c = (lane % BCH) ^ swz<BCH>(cl);
+        bhi[q] = 2 * c >= BCH;
         const uint16_t *mat = (KIND == GK_GATEUP && cl >= 32) ? a.b1 : a.b0;
         const int col = KIND == GK_GATEUP ? colw + (cl & 31) : colw + cl;
         const size_t el = (size_t)e * a.b_stride + (size_t)min(col, N - 1) * K; // first element of the column
@@ -439,24 +455,32 @@ __global__ __launch_bounds__(kGThreads, 1) void k_gemm_lds(GemmArgs a) {
     auto issue_part = [&](int kt, unsigned char *st, uint32_t (&xs)[NB], int part, int nparts) {
         const int k0 = (kb + kt) * BK; // first reduction element of stage kt
         const size_t ka = (size_t)k0 * 2 * AP, kbb = BX ? (size_t)k0 / 2 : (size_t)k0 * EB;
+        // a last stage of BK / 2 elements: second-half chunks read the first
+        // half's sources again (the blocks are skipped by the compute)
+        const bool tail = RAGGED && k0 + BK > K;
+        constexpr size_t HA = BK / 2 * 2 * AP, HB = BX ? BK / 4 : BK / 2 * EB; // bytes of half a stage
 #pragma unroll
         for (int q = 0; q < A_DMA; q++)
-            if (q % nparts == part) copy16_lds(asrc[q] + ka, st + (wave * A_DMA + q) * 1024);
+            if (q % nparts == part) copy16_lds(asrc[q] + ka - (tail && ahi[q] ? HA : 0), st + (wave * A_DMA + q) * 1024);
 #pragma unroll
         for (int q = 0; q < B_DMA; q++)
             if ((A_DMA + q) % nparts == part)
-                copy16_lds(bsrc[q] + kbb, st + A_BYTES + wave * WB_BYTES + q * 1024);
+                copy16_lds(bsrc[q] + kbb - (tail && bhi[q] ? HB : 0), st + A_BYTES + wave * WB_BYTES + q * 1024);
         if constexpr (BQ)
 #pragma unroll
             for (int j = 0; j < SCP; j++)
                 if ((A_DMA + B_DMA + j) % nparts == part)
-                    copy4_lds(ssrc + (size_t)(k0 / 32) * 2 + 4 * j,
+                    copy4_lds(ssrc + (size_t)(k0 / 32) * 2 + 4 * (tail && 2 * j >= SCP ? j - SCP / 2 : j),
                               st + A_BYTES + kGW * WB_BYTES + wave * WS_BYTES + j * (kWave * 4));
         if constexpr (BX)
             if (part == nparts - 1)
 #pragma unroll
-                for (int nb = 0; nb < NB; nb++)
-                    xs[nb] = *reinterpret_cast<const uint16_t *>(xsrc[nb] + k0 / 32);
+                for (int nb = 0; nb < NB; nb++) {
+                    uint32_t w = *reinterpret_cast<const uint16_t *>(xsrc[nb] + k0 / 32);
+                    if constexpr (NBLK == 4)
+                        w |= (uint32_t)*reinterpret_cast<const uint16_t *>(xsrc[nb] + k0 / 32 + (tail ? 0 : 2)) << 16;
+                    xs[nb] = w;
+                }
     };
     auto issue = [&](int kt, unsigned char *st, uint32_t (&xs)[NB]) { issue_part(kt, st, xs, 0, 1); };
 
@@ -471,14 +495,16 @@ __global__ __launch_bounds__(kGThreads, 1) void k_gemm_lds(GemmArgs a) {
     // kn >= 0: the copies of stage kn into `nxt` (and MXFP4 scale registers
     // xn) go out a part per substep, between that substep's LDS reads and
     // its MFMAs
+    // nvb: the stage's scale blocks that lie inside K (block-scaled B)
     auto compute = [&](const unsigned char *st, uint32_t (&xs)[NB], int kn, unsigned char *nxt,
-                       uint32_t (&xn)[NB]) {
+                       uint32_t (&xn)[NB], int nvb) {
         const unsigned char *bw = st + A_BYTES + wave * WB_BYTES;
         if constexpr (BX) {
             // column bytes of substep s: chunk s/2, bytes 8 (s%2) + 4 (l/32) .. +3
             // (the codes of elements 16s + 8 (l/32) .. +7); A as below
 #pragma unroll
             for (int bl = 0; bl < NBLK; bl++) {
+                if (RAGGED && bl >= nvb) break;
                 f32x16 blk[MB][NB];
 #pragma unroll
                 for (int s = 2 * bl; s < 2 * bl + 2; s++) {
@@ -579,6 +605,7 @@ __global__ __launch_bounds__(kGThreads, 1) void k_gemm_lds(GemmArgs a) {
                                           (nb * 32 + (lane & 31)) * 4);
 #pragma unroll
             for (int bl = 0; bl < NBLK; bl++) {
+                if (RAGGED && bl >= nvb) break;
                 f32x16 blk[MB][NB];
 #pragma unroll
                 for (int s = 2 * bl; s < 2 * bl + 2; s++) {
@@ -660,11 +687,11 @@ __global__ __launch_bounds__(kGThreads, 1) void k_gemm_lds(GemmArgs a) {
         // MXFP4 M = 512, 493 against 478 us).
         const int kn = kt + NST - 1 < nk ? kt + NST - 1 : -1;
         if constexpr (!BQ && !BX) {
-            if (wave_on) compute(cur, xc, kn, nxt, xn);
+            if (wave_on) compute(cur, xc, kn, nxt, xn, NBLK);
             else if (kn >= 0) issue(kn, nxt, xn);
         } else {
             if (kn >= 0) issue(kn, nxt, xn);
-            if (wave_on) compute(cur, xc, -1, nxt, xn);
+            if (wave_on) compute(cur, xc, -1, nxt, xn, min(NBLK, (K - (kb + kt) * BK) / 32));
         }
     };
     if (nk > 0) issue(0, sm0, xr0);
