@@ -1121,7 +1121,10 @@ hipError_t launch_down_mfma(const Layer &L, const float *act, const float *share
 // workgroup per 16 tokens x 16 experts over the whole reduction, whose
 // workgroups each re-read x and the router rows: Qwen3-shaped M = 2048,
 // 134 MB of L2 reads for 8.9 MB of operands.)  XS: x rows are split bf16
-// hi/lo pairs (the fused layer's normed rows), one MFMA per half.
+// hi/lo pairs (the fused layer's normed rows), one MFMA per half.  sqp (or
+// null; bf16 rows only): each token's sum of squares over the slice,
+// sqp[s][t], from the staged rows, for the pre-norm's scale, which the top-k
+// then forms (no separate pass over x).
 typedef float f32x4m __attribute__((ext_vector_type(4)));
 constexpr int kRpTok = 64;
 constexpr int kRpMaxSteps = 8;
@@ -1135,7 +1138,7 @@ int router_slices(const Layer &L, int M) {
 
 template <bool XS, int NJ, bool BYE>
 __global__ __launch_bounds__(256) void k_router_part(const uint16_t *x, const uint16_t *router, int M, int E, int K,
-                                                     int S, float *part) {
+                                                     int S, float *part, float *sqp) {
     constexpr int AP = XS ? 2 : 1;
     constexpr int MT = BYE ? 4 : 1; // token tiles a wave
     __shared__ __align__(16) unsigned char s_x[kRpTok * (kRpMaxSteps * 64 * AP + 64)];
@@ -1173,6 +1176,24 @@ __global__ __launch_bounds__(256) void k_router_part(const uint16_t *x, const ui
         }
     }
     __syncthreads();
+    if (!XS && sqp) {
+        // four threads a token, each every fourth 16-byte chunk in order,
+        // then a fixed-order sum of the four
+        const int r = tid >> 2, q = tid & 3, cpr = nst * 4;
+        float ss = 0.f;
+        for (int c = q; c < cpr; c += 4) {
+            const u32x4 v = *reinterpret_cast<const u32x4 *>(s_x + r * rowb + c * 16);
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const float lo = __uint_as_float(v[i] << 16), hi = __uint_as_float(v[i] & 0xffff0000u);
+                ss = fmaf(lo, lo, ss);
+                ss = fmaf(hi, hi, ss);
+            }
+        }
+        ss += __shfl_xor(ss, 1);
+        ss += __shfl_xor(ss, 2);
+        if (q == 0 && t0 + r < M) sqp[(size_t)s * M + t0 + r] = ss;
+    }
     f32x4m acc[MT][NJ];
 #pragma unroll
     for (int mt = 0; mt < MT; mt++)
@@ -1220,10 +1241,11 @@ __global__ __launch_bounds__(256) void k_router_part(const uint16_t *x, const ui
 
 template <bool XS>
 static void launch_router_part(const uint16_t *x, const uint16_t *router, int M, int E, int K, int S, float *part,
-                               hipStream_t s) {
+                               float *sqp, hipStream_t s) {
     const int NT = (E + 15) / 16;
     const dim3 grid((unsigned)(((M + kRpTok - 1) / kRpTok) * S));
-#define RP_LAUNCH(NJ, BYE) launch_kernel((k_router_part<XS, NJ, BYE>), grid, dim3(256), 0, s, x, router, M, E, K, S, part)
+#define RP_LAUNCH(NJ, BYE) \
+    launch_kernel((k_router_part<XS, NJ, BYE>), grid, dim3(256), 0, s, x, router, M, E, K, S, part, sqp)
     if (NT == 1) RP_LAUNCH(1, false);
     else if (NT == 2) RP_LAUNCH(2, false);
     else if (NT == 3) RP_LAUNCH(3, false);
@@ -1235,14 +1257,15 @@ static void launch_router_part(const uint16_t *x, const uint16_t *router, int M,
 }
 
 hipError_t launch_router_mfma(const Layer &L, const void *x, const void *router, int M, float *part, int S,
-                              hipStream_t s, bool x_split) {
+                              float *sqp, hipStream_t s, bool x_split) {
+    if (x_split && sqp) return hipErrorInvalidValue;
     if (L.H % 32 || L.E > 256 || S < 1 || (L.H / 32 + S - 1) / S > kRpMaxSteps) return hipErrorInvalidValue;
     if (x_split)
         launch_router_part<true>(static_cast<const uint16_t *>(x), static_cast<const uint16_t *>(router), M, L.E,
-                                 L.H, S, part, s);
+                                 L.H, S, part, nullptr, s);
     else
         launch_router_part<false>(static_cast<const uint16_t *>(x), static_cast<const uint16_t *>(router), M, L.E,
-                                  L.H, S, part, s);
+                                  L.H, S, part, sqp, s);
     return hipGetLastError();
 }
 

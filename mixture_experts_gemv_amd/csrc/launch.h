@@ -56,8 +56,12 @@ hipError_t launch_permute(int E, int R, int tile_rows, const int32_t *ids, int32
 // scatter of the routes from ids and hist (several workgroups), with the
 // outputs of launch_permute.
 int topk_hist_groups(int M);
+// With sqp (the router's partial sums of squares [S][M]) the token scale
+// 1 / sqrt(sum / H + eps) is formed here, written to scale_out [M] and
+// applied to the logits (tok_scale is then ignored).
 hipError_t launch_topk_hist(const Layer &L, const float *part, int S, const float *tok_scale, const float *bias,
-                            int M, int32_t *ids, float *w, int32_t *hist, hipStream_t s);
+                            int M, int32_t *ids, float *w, int32_t *hist, hipStream_t s,
+                            const float *sqp = nullptr, float *scale_out = nullptr);
 hipError_t launch_scatter(int E, int M, int k, int tile_rows, const int32_t *ids, const int32_t *hist,
                           int32_t *counts, int32_t *offsets, int32_t *sorted, int32_t *route_pos, int32_t *active,
                           int32_t *tiles, hipStream_t s);
@@ -112,11 +116,13 @@ int mfma_tile_rows();                          // tiles of the stage-wise entry 
 int mfma_tile_rows(const Layer &L, int M);     // tiles of the layer call for M tokens
 bool mfma_supported(const Layer &L);
 // Partial router logits part [S][M][E] over S = router_slices(L, M) slices
-// of the reduction (bf16 router; the token scale is left to the top-k).
+// of the reduction (bf16 router; the token scale is left to the top-k), and,
+// when sqp is given (bf16 x only), the tokens' partial sums of squares
+// sqp [S][M] for the pre-norm.
 // x_split: x rows are split bf16 hi/lo pairs (launch_norm_apply's xs) rather than bf16.
 int router_slices(const Layer &L, int M);
 hipError_t launch_router_mfma(const Layer &L, const void *x, const void *router, int M, float *part, int S,
-                              hipStream_t s, bool x_split = false);
+                              float *sqp, hipStream_t s, bool x_split = false);
 hipError_t launch_gateup_mfma(const Layer &L, const void *x, const float *tok_scale, const Mats &routed,
                               const Mats &shared, const Routing &rt, int M, int max_tiles, int tile_rows,
                               float *act, float *shared_act, int act_fmt, hipStream_t s,

@@ -95,8 +95,9 @@ WsLayout layout(const moe_plan *p, int M) {
                                : moe::down_gemv_slices(L.I, L.edt);
     // (the grouped-GEMM router's partial logits [S][M][E] live here until the
     // top-k has read them)
+    // (and, for the pre-norm, their partial sums of squares [S][M])
     w.y_routes = take(std::max(slices * R * L.H * 4,
-                               mfma ? (size_t)moe::router_slices(L, M) * M * L.E * 4 : (size_t)0));
+                               mfma ? (size_t)moe::router_slices(L, M) * M * (L.E + 1) * 4 : (size_t)0));
     w.y_shared = take(L.Is > 0 ? (size_t)(mfma ? 1 : moe::down_gemv_slices(L.Is, L.sdt)) * M * L.H * 4 : 0);
     // the weighted pre-norm's rows (moe_forward_fused with a norm weight):
     // fp32, and split bf16 for the grouped GEMM; only plans with the pre-norm on
@@ -486,9 +487,13 @@ static moe_status forward_impl(const moe_plan *p, const void *x, const moe_weigh
     const int R = M * L.k;
     float *sc = nullptr;
     uint16_t *xsplit = nullptr;
+    // the grouped-GEMM router on bf16 rows; without a norm weight it also
+    // sums the squares of x for the pre-norm, and the top-k forms the scale
+    const bool mfma_router = mfma && L.rdt == moe::DT_BF16 && !wts->router_x_scale;
+    const bool rms_in_router = mfma_router && L.eps > 0.f && !norm_w && L.xdt == moe::DT_BF16;
     if (L.eps > 0.f) {
         sc = at<float>(ws, lay.tok_scale);
-        STAGE(rec, moe::launch_rms_scale(L, x, M, sc, s), "rms scale", MOE_STAGE_RMS);
+        if (!rms_in_router) STAGE(rec, moe::launch_rms_scale(L, x, M, sc, s), "rms scale", MOE_STAGE_RMS);
         if (norm_w) {
             float *xn = at<float>(ws, lay.xn);
             xsplit = mfma ? at<uint16_t>(ws, lay.xs) : nullptr;
@@ -521,21 +526,24 @@ static moe_status forward_impl(const moe_plan *p, const void *x, const moe_weigh
         // (the MFMA router takes bf16 rows and no input scale, and leaves the
         // token scale to the top-k; otherwise the GEMV router)
         const float *part = lg, *part_scale = nullptr;
+        float *sqp = nullptr;
         int S = 1;
-        if (mfma && L.rdt == moe::DT_BF16 && !wts->router_x_scale && (L.xdt == moe::DT_BF16 || xsplit)) {
+        if (mfma_router && (L.xdt == moe::DT_BF16 || xsplit)) {
             S = moe::router_slices(L, M);
             float *pw = at<float>(ws, lay.y_routes);
             part = pw;
-            part_scale = sc;
-            STAGE(rec, moe::launch_router_mfma(L, xsplit ? (const void *)xsplit : x, wts->router, M, pw, S, s,
+            if (rms_in_router) sqp = pw + (size_t)S * M * L.E;
+            else part_scale = sc;
+            STAGE(rec, moe::launch_router_mfma(L, xsplit ? (const void *)xsplit : x, wts->router, M, pw, S, sqp, s,
                                                xsplit != nullptr),
                   "router (MFMA)", MOE_STAGE_ROUTER);
         } else {
             STAGE(rec, moe::launch_router(L, x, router_w(p, wts), sc, M, lg, s), "router", MOE_STAGE_ROUTER);
         }
         int32_t *hist = at<int32_t>(ws, lay.hist);
-        STAGE(rec, moe::launch_topk_hist(L, part, S, part_scale, wts->bias, M, ids, w, hist, s), "top-k",
-              MOE_STAGE_TOPK);
+        STAGE(rec, moe::launch_topk_hist(L, part, S, part_scale, wts->bias, M, ids, w, hist, s, sqp,
+                                         sqp ? sc : nullptr),
+              "top-k", MOE_STAGE_TOPK);
         STAGE(rec, moe::launch_scatter(L.E, M, L.k, rows, ids, hist, counts, offsets, sorted, rpos, active, tiles, s),
               "permute", MOE_STAGE_PERMUTE);
     }

@@ -304,7 +304,8 @@ __device__ inline void sum_slices(const float *row, size_t slab, int S, int E, i
 __global__ __launch_bounds__(kTkWaves * kWave) void k_topk_hist(const float *part, int S, const float *tok_scale,
                                                                 const float *bias, int M, int E, int k, int select,
                                                                 int bias_mode, int32_t *ids, float *w,
-                                                                int32_t *hist) {
+                                                                int32_t *hist, const float *sqp, int H, float eps,
+                                                                float *scale_out) {
     __shared__ __align__(16) uint64_t s_words[kTkWaves][kWave];
     __shared__ int s_hist[kMaxE];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -314,14 +315,25 @@ __global__ __launch_bounds__(kTkWaves * kWave) void k_topk_hist(const float *par
     if (t < M) {
         const size_t slab = (size_t)M * E;
         const float *lrow = part + (size_t)t * E;
-        const float sc = tok_scale ? tok_scale[t] : 1.0f;
+        const bool scaled = tok_scale || sqp;
+        float sc = tok_scale ? tok_scale[t] : 1.0f;
+        if (sqp) {
+            // the pre-norm's scale from the router's per-slice sums of
+            // squares: lane s loads slice s (slices past 64 added in turn),
+            // then a wave sum
+            float ss = 0.f;
+            for (int s2 = lane; s2 < S; s2 += kWave) ss += sqp[(size_t)s2 * M + t];
+            ss = wave_sum(ss);
+            sc = 1.0f / sqrtf(ss / (float)H + eps);
+            if (lane == 0) scale_out[t] = sc;
+        }
         int32_t *ids_row = ids + (size_t)t * k;
         float *w_row = w + (size_t)t * k;
         if (E <= kWave) {
             const int e = min(lane, E - 1);
             float lv1[1];
             sum_slices<1>(lrow, slab, S, E, lane, lv1);
-            const float lv = tok_scale ? lv1[0] * sc : lv1[0];
+            const float lv = scaled ? lv1[0] * sc : lv1[0];
             const float bv = bias ? bias[e] : 0.f;
             const LanePick p = topk_lane_small(lv, bv, E, k, select, bias_mode, lane, s_words[wave]);
             if (p.pick) {
@@ -343,7 +355,7 @@ __global__ __launch_bounds__(kTkWaves * kWave) void k_topk_hist(const float *par
 #pragma unroll
             for (int c = 0; c < kKeysPerLane; c++) {
                 const int e = min(lane + kWave * c, E - 1);
-                if (tok_scale) lv[c] *= sc;
+                if (scaled) lv[c] *= sc;
                 bv[c] = bias && kWave * c < E ? bias[e] : 0.f;
             }
             int id;
@@ -361,9 +373,12 @@ __global__ __launch_bounds__(kTkWaves * kWave) void k_topk_hist(const float *par
 }
 
 hipError_t launch_topk_hist(const Layer &L, const float *part, int S, const float *tok_scale, const float *bias,
-                            int M, int32_t *ids, float *w, int32_t *hist, hipStream_t s) {
+                            int M, int32_t *ids, float *w, int32_t *hist, hipStream_t s, const float *sqp,
+                            float *scale_out) {
+    if (sqp && !scale_out) return hipErrorInvalidValue;
     launch_kernel(k_topk_hist, dim3((M + kTkWaves - 1) / kTkWaves), dim3(kTkWaves * kWave), 0, s, part, S,
-                  tok_scale, L.bias_mode ? bias : nullptr, M, L.E, L.k, L.select, L.bias_mode, ids, w, hist);
+                  tok_scale, L.bias_mode ? bias : nullptr, M, L.E, L.k, L.select, L.bias_mode, ids, w, hist, sqp,
+                  L.H, L.eps, scale_out);
     return hipGetLastError();
 }
 
