@@ -71,9 +71,11 @@ constexpr int kGThreads = kGW * kWave;
 // 398 us a call, M = 512, 466 against 582 us; MXFP4 M = 384, 375 against
 // 660 us; Mixtral-shaped M = 128, 557 against 613 us, M = 256, 626 against
 // 680 us; Qwen3-shaped M = 512, 291 against 321 us).  MXFP4 keeps 32 rows
-// while the mean is at most 32 (gpt-oss shape, M = 256: 357 against 363 us
-// with 64-row tiles, from the down GEMM) and otherwise always takes 64-row
-// tiles, several an expert if need be (M = 512: 499 against 579 us with
+// while the mean is at most 64 (gpt-oss shape, M = 256: 357 against 363 us
+// with 64-row tiles, from the down GEMM; since 32-row tiles take 128-element
+// stages, M = 512: 385 against 440 us) and otherwise always takes 64-row
+// tiles, several an expert if need be (M = 1024: 586 against 631 us with
+// 32-row tiles; before those stages, M = 512: 499 against 579 us with
 // 96-row tiles; M = 768, 611 against 837 us, and M = 1024, 684 against
 // 996 us with 128- and 160-row tiles; Q8_0 at M = 512 the other way round:
 // 530 against 469 us, so bf16 and Q8_0 keep 96).  Beyond 96 routes bf16
@@ -93,7 +95,7 @@ constexpr int kGThreads = kGW * kWave;
 int mfma_tile_rows(const Layer &L, int M) {
     const long R = (long)M * L.k;
     const double c = (double)R / L.E, hi = c + (L.E > 1 ? std::sqrt(c) : 0.0);
-    if (L.edt == DT_MX4 ? R <= 32L * L.E : hi <= 32) return 32;
+    if (L.edt == DT_MX4 ? R <= 64L * L.E : hi <= 32) return 32;
     if (hi <= 64 || L.edt == DT_MX4) return 64;
     if (hi <= 96) return 96;
     // the height of least estimated cost: tiles times (1 + 0.316 rows / 128),

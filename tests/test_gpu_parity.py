@@ -335,7 +335,7 @@ MFMA_SMALL = [
     # experts spill into a second, ragged tile), two 96-row tiles an expert
     # (M = 600) and two or three 160-row tiles an expert (M = 1100)
     ("k2-wide-tiles", dict(hidden=256, num_experts=8, top_k=2, expert_inter=192), (512, 560, 600, 1100)),
-    # MXFP4 beyond 32 routes an expert: several 64-row tiles an expert
+    # MXFP4 beyond 64 routes an expert: several 64-row tiles an expert
     ("mx4-wide-tiles", dict(hidden=256, num_experts=8, top_k=2, expert_inter=192, expert_dtype=MXFP4),
      (512, 560)),
     # one expert: a single ragged 160-row tile (M = 150), two 160-row tiles
