@@ -60,6 +60,11 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
     return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
+// fp32 to fp16 bits, round to nearest even, saturated to +-65504.
+__device__ __forceinline__ uint16_t f32_to_f16_sat(float v) {
+    return __builtin_bit_cast(uint16_t, (_Float16)fminf(fmaxf(v, -65504.f), 65504.f));
+}
+
 // An E8M0 scale byte as the float 2^(e - 127); 0 gives 2^-127 (a float
 // subnormal), 255 is NaN.
 __device__ __forceinline__ float e8m0_to_f32(uint32_t e) {

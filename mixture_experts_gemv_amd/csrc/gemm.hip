@@ -1,18 +1,20 @@
-// MFMA grouped-GEMM path of the routed MoE layer (bf16 operands, fp32
-// accumulate), for batches in which the touched experts see several tokens
+// MFMA grouped-GEMM path of the routed MoE layer (bf16 or fp16 operands,
+// fp32 accumulate), for batches in which the touched experts see several tokens
 // each: the per-expert products are then dense contractions.
 //
 // Uses:
-//   gate/up  A = gathered token rows of x, B = gate and up rows of the tile's
-//            expert, epilogue silu(clamp(g)) * clamp(v) -> act, written as
-//            fp32 or, inside the layer, as fp16 (the precision the pages keep
-//            act in);
+//   gate/up  A = gathered token rows of x (bf16; in the fused call the normed
+//            rows as fp16, with B converted to fp16 as in down), B = gate and
+//            up rows of the tile's expert, epilogue silu(clamp(g)) * clamp(v)
+//            -> act, written as fp32 or, inside the layer, as fp16 (the
+//            precision the pages keep act in);
 //   down     A = fp16 act rows, B = down rows converted to fp16 in registers,
 //            fp16 MFMAs -> per-route outputs;
 //   shared   the same two with identity rows (all tokens), for a shared expert.
-// B is bf16 or Q8_0 (int8 plus fp16 scales per 32 reduction elements,
-// converted exactly to bf16 in registers; each block's products are scaled
-// once).  (The router has its own small-tile kernel at the end of this file.)
+// B is bf16, Q8_0 (int8 plus fp16 scales per 32 reduction elements) or
+// MXFP4 (E2M1 codes plus E8M0 scales), converted exactly to bf16 (fp16 with
+// fp16 A) in registers; each block's products are scaled once.  (The
+// router's reduction-sliced kernel is at the end of this file.)
 //
 // Tiles: 32, 64, 96, 128 or 160 rows (tokens or routes of one expert), by
 // the routes an expert is expected to hold (mfma_tile_rows below), so that
@@ -25,9 +27,8 @@
 // Two kernels:
 //   k_gemm_lds  both operands go global -> LDS with asynchronous copies
 //     (global_load_lds_dwordx4) in a 3-stage pipeline, XOR-swizzled rows;
-//     64 reduction elements a stage, except 32 for bf16 B with split A (the
-//     fused layer's normed x as bf16 hi/lo pairs, whose stage rows hold hi
-//     and lo chunks and whose MFMAs run once per half);
+//     64 reduction elements a stage (128 for Q8_0 and MXFP4 B with 32-row
+//     tiles);
 //   k_gemm_reg (fp32 A handed in by a caller of the stage-wise entry points,
 //     bf16 B) A is staged through registers into LDS (double buffered, split
 //     into hi/lo once as it is written), B fragments are loaded straight into
@@ -48,10 +49,10 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-// A operand formats of the grouped GEMM: bf16 rows (x), split bf16 hi/lo
-// rows (the fused layer's normed x, below), fp16 rows (act of the down GEMM;
-// B is then converted to fp16 in registers).
-enum AFormat { AF_BF16 = 0, AF_SPLIT = 1, AF_F16 = 2 };
+// A operand formats of the grouped GEMM: bf16 rows (x), fp16 rows (act of the
+// down GEMM, and the fused layer's normed x; B is then converted to fp16 in
+// registers).
+enum AFormat { AF_BF16 = 0, AF_F16 = 1 };
 
 constexpr int kMB = 4;              // 32-row blocks per wave
 constexpr int kBM = 32 * kMB;       // rows per tile
@@ -89,9 +90,9 @@ constexpr int kGThreads = kGW * kWave;
 // 128 routes an expert on average at M = 512: 811 against 922 us a call;
 // M = 1024: 1396 against 1461 us; Qwen3-shaped M = 4096: 1019 against
 // 1031 us; a dense layer at M = 512, exactly four 128-row tiles, keeps 128).
-// Q8_0 weights keep 128 rows: with the fused layer's split x, three LDS
-// stages of 160 rows would not fit, and the Q8_0 block accumulators of 160
-// rows fill the registers.  The stage-wise entry points always use kBM.
+// Q8_0 weights keep 128 rows: 160-row tiles measured no faster (gpt-oss
+// shape, M = 1024: 760 against 748 us; M = 2048: 1266 against 1177 us).
+// The stage-wise entry points always use kBM.
 int mfma_tile_rows(const Layer &L, int M) {
     const long R = (long)M * L.k;
     const double c = (double)R / L.E, hi = c + (L.E > 1 ? std::sqrt(c) : 0.0);
@@ -189,11 +190,6 @@ __device__ __forceinline__ void copy16_lds(const void *g, unsigned char *l) {
 // vector memory operations and for nothing else.
 constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
-// Split A rows (the fused layer's normed x): each fp32 value carried as two
-// bf16 numbers, hi = bf16(v) and lo = bf16(v - hi), so that hi*b + lo*b
-// keeps about 16 bits of v.  A row of K elements is stored as K/8 pairs of
-// 16-byte chunks (8 hi values, then the same 8 elements' lo values): 4K
-// bytes, the size of the fp32 row.
 
 // XOR swizzle of a 16-byte chunk within an LDS row of CH chunks: rows of 8
 // or more chunks (128 B) xor with (row ^ row / 8) % 8, so that 8 consecutive
@@ -279,11 +275,6 @@ __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
                                                        c, 0, 0, 0);
 }
 
-// fp32 to fp16 bits, round to nearest even, saturated to +-65504.
-__device__ __forceinline__ uint16_t f32_to_f16_sat(float v) {
-    return __builtin_bit_cast(uint16_t, (_Float16)fminf(fmaxf(v, -65504.f), 65504.f));
-}
-
 // silu(g) * v with the hardware reciprocal (v_rcp_f32, 1 ulp) in place of
 // the IEEE division: the grouped GEMM's epilogue runs on one wave a SIMD,
 // where the division's ten dependent instructions per element show.
@@ -303,7 +294,6 @@ __device__ __forceinline__ float silu_mul_rcp(float g, float v) {
 // 32-row tiles measured no faster for Q8_0.)
 template <int KIND, int AF, int MB, int BF>
 __global__ __launch_bounds__(kGThreads, 1) void k_gemm_lds(GemmArgs a) {
-    constexpr bool AS = AF == AF_SPLIT;            // split bf16 A
     constexpr bool AH = AF == AF_F16;              // fp16 A (and B converted to fp16)
     constexpr bool BQ = BF == 1;                   // Q8_0 B
     constexpr bool BX = BF == 2;                   // MXFP4 B
@@ -311,7 +301,6 @@ __global__ __launch_bounds__(kGThreads, 1) void k_gemm_lds(GemmArgs a) {
     constexpr int BM = 32 * MB;                    // rows per tile
     constexpr int NB = GemmShape<KIND>::NB;
     constexpr int WCOLS = GemmShape<KIND>::WCOLS;
-    constexpr int AP = AS ? 2 : 1;                 // bf16 values of A per element (split: hi, lo)
     constexpr int EB = BQ ? 1 : 2;                 // bytes per B element (bf16, Q8_0)
     // reduction elements per stage: 128 for block-scaled B with 32-row tiles
     // (a Q8_0 column then takes a whole 128-byte line a stage, an MXFP4 one
@@ -320,16 +309,16 @@ __global__ __launch_bounds__(kGThreads, 1) void k_gemm_lds(GemmArgs a) {
     // MXFP4, 205 against 298 us; at the gpt-oss shape, H = I = 2880 and so a
     // half last stage, Q8_0 M = 64 272 against 283 us, MXFP4 M = 64 236
     // against 292 us and M = 256 301 against 330 us; with 64-row tiles it
-    // measured slower), else 64 (32 for split A with bf16 B).  K need only be
+    // measured slower), else 64.  K need only be
     // a multiple of 64: a last stage of 64 elements reads its missing half
     // from the 64 elements before it and skips those blocks.
-    constexpr int BK = (BS && MB == 1) ? 2 * kStageK : (BS ? kStageK : kStageK / AP);
+    constexpr int BK = (BS && MB == 1) ? 2 * kStageK : kStageK;
     constexpr bool RAGGED = BK > 64;               // K may end half way into a stage
     constexpr int NBLK = BK / 32;                  // scale blocks per stage
     constexpr int SCP = BQ ? NBLK / 2 : 0;         // 4-byte scale copies per lane per stage
     constexpr int SRG = BX ? NB * (NBLK / 2) : 0;  // MXFP4 2-byte scale loads per lane per stage
     constexpr int NST = kStages;                   // LDS stages
-    constexpr int ARB = BK * 2 * AP;               // A bytes per row per stage
+    constexpr int ARB = BK * 2;                    // A bytes per row per stage
     constexpr int BRB = BX ? BK / 2 : BK * EB;     // B bytes per column per stage
     constexpr int ACH = ARB / 16;                  // 16-byte chunks per A row per stage
     constexpr int BCH = BRB / 16;                  // 16-byte chunks per B column per stage
@@ -399,7 +388,7 @@ __global__ __launch_bounds__(kGThreads, 1) void k_gemm_lds(GemmArgs a) {
     if (tid < BM) {
         const int p = p0 + min(tid, nrows - 1);
         const int t = a.sorted ? a.sorted[p] / a.k_route : p;
-        s_src[tid] = reinterpret_cast<const char *>(a.a) + (size_t)t * a.K * 2 * AP;
+        s_src[tid] = reinterpret_cast<const char *>(a.a) + (size_t)t * a.K * 2;
         s_scl[tid] = a.tok_scale ? a.tok_scale[t] : 1.0f;
     }
     __syncthreads();
@@ -456,11 +445,11 @@ __global__ __launch_bounds__(kGThreads, 1) void k_gemm_lds(GemmArgs a) {
     // copies over its MFMA substeps
     auto issue_part = [&](int kt, unsigned char *st, uint32_t (&xs)[NB], int part, int nparts) {
         const int k0 = (kb + kt) * BK; // first reduction element of stage kt
-        const size_t ka = (size_t)k0 * 2 * AP, kbb = BX ? (size_t)k0 / 2 : (size_t)k0 * EB;
+        const size_t ka = (size_t)k0 * 2, kbb = BX ? (size_t)k0 / 2 : (size_t)k0 * EB;
         // a last stage of BK / 2 elements: second-half chunks read the first
         // half's sources again (the blocks are skipped by the compute)
         const bool tail = RAGGED && k0 + BK > K;
-        constexpr size_t HA = BK / 2 * 2 * AP, HB = BX ? BK / 4 : BK / 2 * EB; // bytes of half a stage
+        constexpr size_t HA = BK / 2 * 2, HB = BX ? BK / 4 : BK / 2 * EB; // bytes of half a stage
 #pragma unroll
         for (int q = 0; q < A_DMA; q++)
             if (q % nparts == part) copy16_lds(asrc[q] + ka - (tail && ahi[q] ? HA : 0), st + (wave * A_DMA + q) * 1024);
@@ -512,7 +501,7 @@ __global__ __launch_bounds__(kGThreads, 1) void k_gemm_lds(GemmArgs a) {
                 for (int s = 2 * bl; s < 2 * bl + 2; s++) {
                     const int g8 = 2 * s + (lane >> 5);
                     uint32_t q[NB];
-                    u32x4 v[AP * MB];
+                    u32x4 v[MB];
 #pragma unroll
                     for (int nb = 0; nb < NB; nb++) {
                         const int cl = nb * 32 + (lane & 31);
@@ -522,16 +511,14 @@ __global__ __launch_bounds__(kGThreads, 1) void k_gemm_lds(GemmArgs a) {
 #pragma unroll
                     for (int mb = 0; mb < MB; mb++) {
                         const int r = mb * 32 + (lane & 31);
-#pragma unroll
-                        for (int h = 0; h < AP; h++)
-                            v[AP * mb + h] = lds_load16(st + r * ARB + (((AP * g8 + h) ^ swz<ACH>(r)) * 16));
+                        v[mb] = lds_load16(st + r * ARB + ((g8 ^ swz<ACH>(r)) * 16));
                     }
                     if (kn >= 0) issue_part(kn, nxt, xn, s, BK / 16);
                     asm volatile("s_waitcnt lgkmcnt(0)");
 #pragma unroll
                     for (int nb = 0; nb < NB; nb++) lds_keep(q[nb]);
 #pragma unroll
-                    for (int i = 0; i < AP * MB; i++) lds_keep(v[i]);
+                    for (int i = 0; i < MB; i++) lds_keep(v[i]);
 #pragma unroll
                     for (int nb = 0; nb < NB; nb++) {
                         u32x4 bv;
@@ -548,11 +535,7 @@ __global__ __launch_bounds__(kGThreads, 1) void k_gemm_lds(GemmArgs a) {
                         }
 #pragma unroll
                         for (int mb = 0; mb < MB; mb++)
-#pragma unroll
-                            for (int h = 0; h < AP; h++) {
-                                const f32x16 c = (s == 2 * bl && h == 0) ? f32x16{} : blk[mb][nb];
-                                blk[mb][nb] = mfma32<AH>(v[AP * mb + h], bv, c);
-                            }
+                            blk[mb][nb] = mfma32<AH>(v[mb], bv, s == 2 * bl ? f32x16{} : blk[mb][nb]);
                     }
                 }
 #pragma unroll
@@ -569,9 +552,9 @@ __global__ __launch_bounds__(kGThreads, 1) void k_gemm_lds(GemmArgs a) {
             for (int s = 0; s < BK / 16; s++) {
                 // every read of the substep first, one wait, then the MFMAs.
                 // Lane l takes the 8 reduction elements g = 2s + l/32 of its
-                // row or column (split A: chunk 2g holds their hi, 2g+1 their lo).
+                // row or column.
                 const int g8 = 2 * s + (lane >> 5);
-                u32x4 v[NB + AP * MB];
+                u32x4 v[NB + MB];
 #pragma unroll
                 for (int nb = 0; nb < NB; nb++) {
                     const int cl = nb * 32 + (lane & 31);
@@ -580,9 +563,7 @@ __global__ __launch_bounds__(kGThreads, 1) void k_gemm_lds(GemmArgs a) {
 #pragma unroll
                 for (int mb = 0; mb < MB; mb++) {
                     const int r = mb * 32 + (lane & 31);
-#pragma unroll
-                    for (int h = 0; h < AP; h++)
-                        v[NB + AP * mb + h] = lds_load16(st + r * ARB + (((AP * g8 + h) ^ swz<ACH>(r)) * 16));
+                    v[NB + mb] = lds_load16(st + r * ARB + ((g8 ^ swz<ACH>(r)) * 16));
                 }
                 if (kn >= 0) issue_part(kn, nxt, xn, s, BK / 16);
                 lds_wait(v);
@@ -592,9 +573,7 @@ __global__ __launch_bounds__(kGThreads, 1) void k_gemm_lds(GemmArgs a) {
 #pragma unroll
                 for (int mb = 0; mb < MB; mb++)
 #pragma unroll
-                    for (int nb = 0; nb < NB; nb++)
-#pragma unroll
-                        for (int h = 0; h < AP; h++) acc[mb][nb] = mfma32<AH>(v[NB + AP * mb + h], v[nb], acc[mb][nb]);
+                    for (int nb = 0; nb < NB; nb++) acc[mb][nb] = mfma32<AH>(v[NB + mb], v[nb], acc[mb][nb]);
             }
         } else {
             // this lane's columns' scales of the stage: fp16 pairs (blocks 2j, 2j+1)
@@ -614,7 +593,7 @@ __global__ __launch_bounds__(kGThreads, 1) void k_gemm_lds(GemmArgs a) {
                     // column bytes 16s + 8 (l/32) .. +7 of chunk s; A as above
                     const int g8 = 2 * s + (lane >> 5);
                     u32x2 q[NB];
-                    u32x4 v[AP * MB];
+                    u32x4 v[MB];
 #pragma unroll
                     for (int nb = 0; nb < NB; nb++) {
                         const int cl = nb * 32 + (lane & 31);
@@ -623,16 +602,14 @@ __global__ __launch_bounds__(kGThreads, 1) void k_gemm_lds(GemmArgs a) {
 #pragma unroll
                     for (int mb = 0; mb < MB; mb++) {
                         const int r = mb * 32 + (lane & 31);
-#pragma unroll
-                        for (int h = 0; h < AP; h++)
-                            v[AP * mb + h] = lds_load16(st + r * ARB + (((AP * g8 + h) ^ swz<ACH>(r)) * 16));
+                        v[mb] = lds_load16(st + r * ARB + ((g8 ^ swz<ACH>(r)) * 16));
                     }
                     if (kn >= 0) issue_part(kn, nxt, xn, s, BK / 16);
                     asm volatile("s_waitcnt lgkmcnt(0)");
 #pragma unroll
                     for (int nb = 0; nb < NB; nb++) lds_keep(q[nb]);
 #pragma unroll
-                    for (int i = 0; i < AP * MB; i++) lds_keep(v[i]);
+                    for (int i = 0; i < MB; i++) lds_keep(v[i]);
                     if (s == 2 * bl) {
 #pragma unroll
                         for (int nb = 0; nb < NB; nb++)
@@ -644,11 +621,7 @@ __global__ __launch_bounds__(kGThreads, 1) void k_gemm_lds(GemmArgs a) {
                         const u32x4 bv = AH ? q8x8_to_f16(q[nb]) : q8x8_to_bf16(q[nb]);
 #pragma unroll
                         for (int mb = 0; mb < MB; mb++)
-#pragma unroll
-                            for (int h = 0; h < AP; h++) {
-                                const f32x16 c = (s == 2 * bl && h == 0) ? f32x16{} : blk[mb][nb];
-                                blk[mb][nb] = mfma32<AH>(v[AP * mb + h], bv, c);
-                            }
+                            blk[mb][nb] = mfma32<AH>(v[mb], bv, s == 2 * bl ? f32x16{} : blk[mb][nb]);
                     }
                 }
 #pragma unroll
@@ -940,8 +913,8 @@ __global__ __launch_bounds__(kGThreads, 2) void k_gemm_reg(GemmArgs a) {
     }
 }
 
-// a_mode: 0 = bf16 A rows (gate/up), 1 = split A rows (the fused layer's normed x, gate/up),
-// 2 = fp32 A rows (down), 3 = fp16 A rows (act of down).  bq: B format (0 bf16, 1 Q8_0,
+// a_mode: 0 = bf16 A rows (gate/up), 2 = fp32 A rows (down), 3 = fp16 A rows (act of down),
+// 4 = fp16 A rows (gate/up: the fused layer's normed x).  bq: B format (0 bf16, 1 Q8_0,
 // 2 MXFP4; a.s0 / a.s1 hold the block scales); fp32 A takes bf16 B only.
 template <int KIND, int AF, int MB>
 static void launch_lds_b(const GemmArgs &a, int bf, unsigned grid, hipStream_t s) {
@@ -983,7 +956,7 @@ static hipError_t run_gemm(int kind, int a_mode, int bq, GemmArgs &a, hipStream_
         if (a.tile_rows != 32 && a.tile_rows != 64 && a.tile_rows != 96 && a.tile_rows != kBM && !(a.tile_rows == kBMWide && bq != 1))
             return hipErrorInvalidValue;
         if (kind == GK_GATEUP && a_mode == 0) launch_lds<GK_GATEUP, AF_BF16>(a, bq, grid, s);
-        else if (kind == GK_GATEUP && a_mode == 1) launch_lds<GK_GATEUP, AF_SPLIT>(a, bq, grid, s);
+        else if (kind == GK_GATEUP && a_mode == 4) launch_lds<GK_GATEUP, AF_F16>(a, bq, grid, s);
         else if (kind == GK_PLAIN && a_mode == 3) launch_lds<GK_PLAIN, AF_F16>(a, bq, grid, s);
         else return hipErrorInvalidValue;
     }
@@ -1013,8 +986,8 @@ int down_ksplit(const Layer &L, int M, int tile_rows) {
 
 hipError_t launch_gateup_mfma(const Layer &L, const void *x, const float *tok_scale, const Mats &routed,
                               const Mats &shared, const Routing &rt, int M, int max_tiles, int tile_rows,
-                              float *act, float *shared_act, int act_fmt, hipStream_t s, bool x_split) {
-    const int a_mode = x_split ? 1 : 0;
+                              float *act, float *shared_act, int act_fmt, hipStream_t s, bool x_half) {
+    const int a_mode = x_half ? 4 : 0;
     if (act) {
         GemmArgs a{};
         a.tile_rows = tile_rows;

@@ -40,9 +40,10 @@ struct Routing {
 
 hipError_t launch_rms_scale(const Layer &L, const void *x, int M, float *scale, hipStream_t s);
 // xn = x * scale[t] * gamma (fp32 rows); xs (or null): the same rows split
-// into bf16 hi/lo pairs, the A layout of the grouped GEMM.
+// into bf16 hi/lo pairs (the grouped-GEMM router's input); xh (or null): the
+// same rows as fp16 (the grouped GEMM's A).
 hipError_t launch_norm_apply(const Layer &L, const void *x, const void *gamma, const float *scale, int M,
-                             float *xn, uint16_t *xs, hipStream_t s);
+                             float *xn, uint16_t *xs, uint16_t *xh, hipStream_t s);
 hipError_t launch_router(const Layer &L, const void *x, const RouterW &rw, const float *tok_scale,
                          int M, float *logits, hipStream_t s);
 hipError_t launch_topk(const Layer &L, const float *logits, const float *bias, int M, int32_t *ids,
@@ -126,7 +127,7 @@ hipError_t launch_router_mfma(const Layer &L, const void *x, const void *router,
 hipError_t launch_gateup_mfma(const Layer &L, const void *x, const float *tok_scale, const Mats &routed,
                               const Mats &shared, const Routing &rt, int M, int max_tiles, int tile_rows,
                               float *act, float *shared_act, int act_fmt, hipStream_t s,
-                              bool x_split = false);
+                              bool x_half = false);
 // act_fmt: the rows of act / shared_act.  ACT_F32: fp32 rows; ACT_F16: fp16
 // rows (values beyond +-65504 saturate), which the down GEMM multiplies on
 // fp16 MFMAs.

@@ -44,7 +44,7 @@ size_t up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 // Where each workspace region starts for a call with M tokens.
 struct WsLayout {
     size_t tok_scale, logits, ids, w, counts, offsets, sorted, route_pos, active, tiles, hist;
-    size_t act, shared_act, y_routes, y_shared, xn, xs, total;
+    size_t act, shared_act, y_routes, y_shared, xn, xs, xh, total;
     int max_tiles;
 };
 
@@ -100,9 +100,11 @@ WsLayout layout(const moe_plan *p, int M) {
                                mfma ? (size_t)moe::router_slices(L, M) * M * (L.E + 1) * 4 : (size_t)0));
     w.y_shared = take(L.Is > 0 ? (size_t)(mfma ? 1 : moe::down_gemv_slices(L.Is, L.sdt)) * M * L.H * 4 : 0);
     // the weighted pre-norm's rows (moe_forward_fused with a norm weight):
-    // fp32, and split bf16 for the grouped GEMM; only plans with the pre-norm on
+    // fp32, and for the grouped-GEMM path split bf16 (router) and fp16
+    // (experts); only plans with the pre-norm on
     w.xn = take(L.eps > 0.f ? (size_t)M * L.H * 4 : 0);
     w.xs = take(L.eps > 0.f && mfma ? (size_t)M * L.H * 4 : 0);
+    w.xh = take(L.eps > 0.f && mfma ? (size_t)M * L.H * 2 : 0);
     w.total = o;
     return w;
 }
@@ -481,12 +483,13 @@ static moe_status forward_impl(const moe_plan *p, const void *x, const moe_weigh
     const WsLayout lay = layout(p, M);
     const bool mfma = use_mfma(p, M);
     // L: what the kernels see.  With a norm weight the normed rows are
-    // written once (fp32, and split bf16 for the grouped GEMM) and the rest
+    // written once (fp32; on the grouped-GEMM path also split bf16 for the
+    // router and fp16 for the experts, as the pages keep the normed rows) and the rest
     // of the layer reads them as fp32 x with the pre-norm done.
     moe::Layer L = p->L;
     const int R = M * L.k;
     float *sc = nullptr;
-    uint16_t *xsplit = nullptr;
+    uint16_t *xsplit = nullptr, *xhalf = nullptr;
     // the grouped-GEMM router on bf16 rows; without a norm weight it also
     // sums the squares of x for the pre-norm, and the top-k forms the scale
     const bool mfma_router = mfma && L.rdt == moe::DT_BF16 && !wts->router_x_scale;
@@ -497,7 +500,8 @@ static moe_status forward_impl(const moe_plan *p, const void *x, const moe_weigh
         if (norm_w) {
             float *xn = at<float>(ws, lay.xn);
             xsplit = mfma ? at<uint16_t>(ws, lay.xs) : nullptr;
-            STAGE(rec, moe::launch_norm_apply(L, x, norm_w, sc, M, xn, xsplit, s), "norm", MOE_STAGE_RMS);
+            xhalf = mfma ? at<uint16_t>(ws, lay.xh) : nullptr;
+            STAGE(rec, moe::launch_norm_apply(L, x, norm_w, sc, M, xn, xsplit, xhalf, s), "norm", MOE_STAGE_RMS);
             x = xn;
             sc = nullptr;
             L.xdt = moe::DT_F32;
@@ -553,9 +557,9 @@ static moe_status forward_impl(const moe_plan *p, const void *x, const moe_weigh
     float *yr = at<float>(ws, lay.y_routes);
     float *ysh = L.Is > 0 ? at<float>(ws, lay.y_shared) : nullptr;
     if (mfma) {
-        STAGE(rec, moe::launch_gateup_mfma(L, xsplit ? (const void *)xsplit : x, sc, routed_mats(wts),
+        STAGE(rec, moe::launch_gateup_mfma(L, xhalf ? (const void *)xhalf : x, sc, routed_mats(wts),
                                            shared_mats(wts), rt, M, lay.max_tiles, rows, act, sact, moe::ACT_F16, s,
-                                           xsplit != nullptr),
+                                           xhalf != nullptr),
               "gate/up (MFMA)", MOE_STAGE_GATEUP);
         STAGE(rec, moe::launch_down_mfma(L, act, sact, routed_mats(wts), shared_mats(wts), rt, M,
                                          lay.max_tiles, rows, yr, ysh, moe::ACT_F16, s),

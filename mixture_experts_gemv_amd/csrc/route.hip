@@ -40,13 +40,14 @@ hipError_t launch_rms_scale(const Layer &L, const void *x, int M, float *scale, 
 }
 
 // The normed rows of the fused layer: xn[t][i] = x[t][i] * scale[t] * gamma[i]
-// (gamma stored like x; null = unit gain) as fp32 rows, and, when xs is
-// given, as the split bf16 rows the grouped GEMM reads (per 8 elements: their
-// 8 hi values bf16(v), then their 8 lo values bf16(v - hi)).  One thread per
+// (gamma stored like x; null = unit gain) as fp32 rows; when xs is given, as
+// the split bf16 rows the grouped-GEMM router reads (per 8 elements: their 8
+// hi values bf16(v), then their 8 lo values bf16(v - hi)); when xh is given,
+// as the fp16 rows (saturated to +-65504) the grouped GEMM's experts read.  One thread per
 // 8 elements of a row.
 template <int XDT>
 __global__ __launch_bounds__(256) void k_norm_apply(const void *x, const void *gamma, const float *scale, int H,
-                                                    float *xn, uint16_t *xs) {
+                                                    float *xn, uint16_t *xs, uint16_t *xh) {
     const int t = blockIdx.y;
     const int c = blockIdx.x * 256 + threadIdx.x;
     if (c >= H / 8) return;
@@ -75,15 +76,22 @@ __global__ __launch_bounds__(256) void k_norm_apply(const void *x, const void *g
         q[0] = u32x4{hi[0] | hi[1] << 16, hi[2] | hi[3] << 16, hi[4] | hi[5] << 16, hi[6] | hi[7] << 16};
         q[1] = u32x4{lo[0] | lo[1] << 16, lo[2] | lo[3] << 16, lo[4] | lo[5] << 16, lo[6] | lo[7] << 16};
     }
+    if (xh) {
+        uint32_t h[8];
+#pragma unroll
+        for (int i = 0; i < 8; i++) h[i] = f32_to_f16_sat(v[i]);
+        *reinterpret_cast<u32x4 *>(xh + (size_t)t * H + (size_t)c * 8) =
+            u32x4{h[0] | h[1] << 16, h[2] | h[3] << 16, h[4] | h[5] << 16, h[6] | h[7] << 16};
+    }
 }
 
 hipError_t launch_norm_apply(const Layer &L, const void *x, const void *gamma, const float *scale, int M,
-                             float *xn, uint16_t *xs, hipStream_t s) {
+                             float *xn, uint16_t *xs, uint16_t *xh, hipStream_t s) {
     const dim3 grid((L.H / 8 + 255) / 256, M);
     if (L.xdt == DT_BF16)
-        launch_kernel(k_norm_apply<DT_BF16>, grid, dim3(256), 0, s, x, gamma, scale, L.H, xn, xs);
+        launch_kernel(k_norm_apply<DT_BF16>, grid, dim3(256), 0, s, x, gamma, scale, L.H, xn, xs, xh);
     else
-        launch_kernel(k_norm_apply<DT_F32>, grid, dim3(256), 0, s, x, gamma, scale, L.H, xn, xs);
+        launch_kernel(k_norm_apply<DT_F32>, grid, dim3(256), 0, s, x, gamma, scale, L.H, xn, xs, xh);
     return hipGetLastError();
 }
 
