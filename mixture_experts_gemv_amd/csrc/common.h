@@ -108,6 +108,91 @@ __device__ __forceinline__ float wave_reduce(float v, Op op) {
     return op(op(r0, r1), op(r2, r3));
 }
 __device__ __forceinline__ float wave_sum(float v) { return wave_reduce(v, OpSum()); }
+
+// Sums over the 64 lanes of K values at once (K = 2, 4 or 8; all lanes
+// active): afterwards every lane of group q = lane / (64 / K) holds the sum
+// of v[q].  Each exchange halves the values a lane carries: with partner
+// lane ^ b (b = 32, 16, ..), lanes with bit b clear keep the first half of
+// their values and add the partner's first half, the others the second half.
+// The groups of 64 / K lanes then all-reduce their one value with the DPP
+// steps of wave_reduce.  log2(K) exchanges and one group reduction replace K
+// full reductions; the order of the additions is fixed.  (In the per-row and
+// streamed kernels, against one wave_sum a value: gpt-oss-shaped Q8_0 M = 16,
+// 162.3 against 168.2 us a call; DeepSeek-V2-Lite-shaped, 180.7 against
+// 191.7 us; MXFP4, 159.6 against 167.0 us.  With ds_bpermute exchanges in
+// place of the lane swaps it gained little and slowed the one-token down
+// kernel.)
+// The value of lane ^ 32 (b = 32) or lane ^ 16 (b = 16), or, within a
+// 16-lane row, lane ^ 8 (b = 8), with the gfx950 lane-swap instructions and
+// DPP (VALU only).  The swaps return the two operands after the exchange; with
+// both operands v, a lane in the upper half (odd row) finds its partner's
+// value in the first, a lane in the lower half (even row) in the second.
+template <int B>
+__device__ __forceinline__ float lane_xor(float v, int lane) {
+    const uint32_t u = __float_as_uint(v);
+    if constexpr (B == 32) {
+        const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+        return __uint_as_float((lane & 32) ? r[0] : r[1]);
+    } else if constexpr (B == 16) {
+        const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+        return __uint_as_float((lane & 16) ? r[0] : r[1]);
+    } else {
+        static_assert(B == 8, "lane_xor: 8, 16 or 32");
+        return __int_as_float(__builtin_amdgcn_update_dpp(0, (int)u, 0x128, 0xF, 0xF, false)); // row_ror:8
+    }
+}
+
+template <int K>
+__device__ __forceinline__ float wave_sum_split(const float (&v)[K], int lane) {
+    static_assert(K == 2 || K == 4 || K == 8, "K must be 2, 4 or 8");
+    float w[K];
+#pragma unroll
+    for (int i = 0; i < K; i++) w[i] = v[i];
+    // exchanges with lane ^ 32, then ^ 16, then ^ 8 while values remain
+    auto exchange = [&](auto bconst, int n) {
+        constexpr int b = decltype(bconst)::value;
+        const bool up = (lane & b) != 0;
+#pragma unroll
+        for (int i = 0; i < n / 2; i++) {
+            const float keep = up ? w[n / 2 + i] : w[i];
+            const float send = up ? w[i] : w[n / 2 + i];
+            w[i] = keep + lane_xor<b>(send, lane);
+        }
+    };
+    exchange(std::integral_constant<int, 32>{}, K);
+    if constexpr (K >= 4) exchange(std::integral_constant<int, 16>{}, K / 2);
+    if constexpr (K >= 8) exchange(std::integral_constant<int, 8>{}, K / 4);
+    float x = w[0];
+    if constexpr (K == 2) x += lane_xor<16>(x, lane);
+    x += __int_as_float(dpp_xor1(__float_as_int(x)));
+    x += __int_as_float(dpp_xor2(__float_as_int(x)));
+    x += __int_as_float(dpp_hmirror(__float_as_int(x)));
+    if (K <= 4) x += __int_as_float(dpp_mirror(__float_as_int(x)));
+    return x;
+}
+
+// R values (1 <= R <= 8) summed over the wave as by wave_sum_split, padded
+// with zeros to a power of two KP: lane l holds the sum of v[l / sum_lanes<R>()]
+// (for that index below R).  R = 1 is wave_sum.
+template <int R> constexpr int sum_ways() { return R <= 1 ? 1 : R <= 2 ? 2 : R <= 4 ? 4 : 8; }
+template <int R> constexpr int sum_lanes() { return 64 / sum_ways<R>(); }
+template <int R>
+__device__ __forceinline__ float wave_sum_rows(const float (&v)[R], int lane) {
+    static_assert(R >= 1 && R <= 8, "1 to 8 values");
+    constexpr int KP = sum_ways<R>();
+    if constexpr (KP == 1) {
+        return wave_sum(v[0]);
+    } else {
+        float w[KP];
+#pragma unroll
+        for (int i = 0; i < KP; i++) w[i] = i < R ? v[i] : 0.f;
+        return wave_sum_split<KP>(w, lane);
+    }
+}
+// The value lane `src` holds, in every lane.
+__device__ __forceinline__ float lane_value(float v, int src) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), src));
+}
 __device__ __forceinline__ float wave_max(float v) { return wave_reduce(v, OpMaxF()); }
 
 __device__ __forceinline__ uint32_t umax32(uint32_t a, uint32_t b) { return a > b ? a : b; }

@@ -282,10 +282,17 @@ __global__ __launch_bounds__(kThreads) void k_gateup_rows(RowsGateUp a) {
                 const int jj = jt + j;
                 const int t = shared ? jj : a.sorted[p0 + jj] / a.k;
                 const float sc = a.tok_scale ? a.tok_scale[t] : 1.0f;
+                float gv[2 * RP]; // gate and up of each row, summed together
 #pragma unroll
                 for (int r = 0; r < RP; r++) {
-                    float g = wave_sum(ag[r][j]) * sc;
-                    float v = wave_sum(au[r][j]) * sc;
+                    gv[2 * r] = ag[r][j];
+                    gv[2 * r + 1] = au[r][j];
+                }
+                const float sgv = wave_sum_rows<2 * RP>(gv, lane);
+#pragma unroll
+                for (int r = 0; r < RP; r++) {
+                    float g = lane_value(sgv, 2 * r * sum_lanes<2 * RP>()) * sc;
+                    float v = lane_value(sgv, (2 * r + 1) * sum_lanes<2 * RP>()) * sc;
                     if (!shared && a.limit > 0.f) { // the shared expert is not clamped
                         g = clampf(g, a.limit);
                         v = clampf(v, a.limit);
@@ -563,8 +570,10 @@ __global__ __launch_bounds__(kStreamThreads) void k_gateup_stream(StreamGateUp a
                 v = fmaf(scu[cc], su, v);
             }
             const float sc = s_sc[t];
-            g = wave_sum(g) * sc;
-            v = wave_sum(v) * sc;
+            const float gv[2] = {g, v};
+            const float sgv = wave_sum_rows<2>(gv, lane); // g in lanes 0-31, v in 32-63
+            g = lane_value(sgv, 0) * sc;
+            v = lane_value(sgv, 32) * sc;
             if (routed && a.limit > 0.f) { // the shared expert is not clamped
                 g = clampf(g, a.limit);
                 v = clampf(v, a.limit);
@@ -846,11 +855,8 @@ __global__ __launch_bounds__(kThreads) void k_down_rows(RowsDown a) {
 #pragma unroll
                         for (int i = 0; i < N; i++) d[r] = fmaf(wv[r][cc][i], av[i], d[r]);
                 }
-#pragma unroll
-                for (int r = 0; r < RP; r++) {
-                    const float v = wave_sum(d[r]);
-                    if (lane == 0) out[(size_t)(s0 + j) * H + h0 + r] = v;
-                }
+                const float v = wave_sum_rows<RP>(d, lane); // row lane / sum_lanes of the group
+                if (lane % sum_lanes<RP>() == 0) out[(size_t)(s0 + j) * H + h0 + lane / sum_lanes<RP>()] = v;
             }
             return;
         }
@@ -867,11 +873,11 @@ __global__ __launch_bounds__(kThreads) void k_down_rows(RowsDown a) {
                 for (int j = 0; j < kTV; j++) {
                     if (j < nj) {
                         const int jj = s0 + j0 + j;
+                        float d[RP];
 #pragma unroll
-                        for (int r = 0; r < RP; r++) {
-                            const float v = wave_sum(acc[r][j]);
-                            if (lane == 0) out[(size_t)jj * H + h0 + r] = v;
-                        }
+                        for (int r = 0; r < RP; r++) d[r] = acc[r][j];
+                        const float v = wave_sum_rows<RP>(d, lane);
+                        if (lane % sum_lanes<RP>() == 0) out[(size_t)jj * H + h0 + lane / sum_lanes<RP>()] = v;
                     }
                 }
             }
@@ -1209,8 +1215,12 @@ __global__ __launch_bounds__(kThreads) void k_gateup_m1(M1GateUpArgs a) {
                     v += pu;
                 }
             }
-            g = wave_sum(g);
-            v = wave_sum(v);
+            {
+                const float gv[2] = {g, v};
+                const float sgv = wave_sum_rows<2>(gv, lane); // g in lanes 0-31, v in 32-63
+                g = lane_value(sgv, 0);
+                v = lane_value(sgv, 32);
+            }
             if constexpr (XD2) {
                 g *= sc;
                 v *= sc;
@@ -1351,10 +1361,10 @@ __global__ __launch_bounds__(NT) void k_down_m1(M1DownArgs a) {
             }
         }
     }
-#pragma unroll
-    for (int r = 0; r < R; r++) {
-        const float v = wave_sum(acc[r]);
-        if (lane == 0) s_part[wave][r] = v;
+    {
+        const float v = wave_sum_rows<R>(acc, lane); // row lane / sum_lanes of the group
+        const int q = lane / sum_lanes<R>();
+        if (lane % sum_lanes<R>() == 0 && q < R) s_part[wave][q] = v;
     }
     __syncthreads();
     if (tid <= last_row) {
