@@ -487,7 +487,6 @@ static moe_status forward_impl(const moe_plan *p, const void *x, const moe_weigh
     // router and fp16 for the experts, as the pages keep the normed rows) and the rest
     // of the layer reads them as fp32 x with the pre-norm done.
     moe::Layer L = p->L;
-    const int R = M * L.k;
     float *sc = nullptr;
     uint16_t *xsplit = nullptr, *xhalf = nullptr;
     // the grouped-GEMM router on bf16 rows; without a norm weight it also
