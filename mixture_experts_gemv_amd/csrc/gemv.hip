@@ -1065,7 +1065,7 @@ struct M1GateUpArgs {
     float *act, *shared_act;
 };
 
-template <int XDT, int WDT, int CPL, int RP>
+template <int XDT, int WDT, int CPL, int RP, bool PRE>
 __global__ __launch_bounds__(kThreads) void k_gateup_m1(M1GateUpArgs a) {
     constexpr int N = Chunk<WDT>::N;
     __shared__ __align__(16) uint64_t s_words[kWaves][kWave];
@@ -1102,6 +1102,58 @@ __global__ __launch_bounds__(kThreads) void k_gateup_m1(M1GateUpArgs a) {
                 xf[cc][n4] = reinterpret_cast<const f32x4 *>(reinterpret_cast<const float *>(a.x) + cl[cc] * N + 4 * n4)[0];
         }
     }
+    // pairs: the shared expert's rows first (q < Is), then the picks' rows.
+    // PRE (layers with a shared expert, or one expert): a group whose rows
+    // do not depend on the picks (shared rows, or the one expert 0) has its
+    // loads issued before the top-k, so that they overlap it (DeepSeek-V2-
+    // Lite shape, 29.3 against 30.5 us a call; its dense lead layer, 27.7
+    // against 28.5 us; without PRE the registers it holds across the top-k
+    // cost the other layers 0.5 us).
+    const int routed_pairs = a.k * a.I, shared_pairs = p_end - routed_pairs;
+    const size_t rbytes = row_bytes<WDT>(H);
+    int slot[RP], irow[RP];
+    u32x4 rg[RP][CPL], ru[RP][CPL];
+    uint16_t hg[RP][CPL], hu[RP][CPL];
+    auto issue_group = [&](int p, const M1Slots &sl) {
+#pragma unroll
+        for (int r = 0; r < RP; r++) {
+            const int q = min(p + r, p_end - 1);
+            size_t row;
+            const Mats *m;
+            if (q >= shared_pairs) {
+                const int qr = q - shared_pairs;
+                slot[r] = qr / a.I;
+                irow[r] = qr - slot[r] * a.I;
+                row = (size_t)sl.expert(slot[r]) * a.I + irow[r];
+                m = &a.routed;
+            } else {
+                slot[r] = -1;
+                irow[r] = q;
+                row = q;
+                m = &a.shared;
+            }
+            const char *grow = reinterpret_cast<const char *>(m->gate) + row * rbytes;
+            const char *urow = reinterpret_cast<const char *>(m->up) + row * rbytes;
+            const void *gsr = nullptr, *usr = nullptr;
+            if constexpr (blocked<WDT>()) {
+                gsr = scale_at<WDT>(m->gate_s, row * (H / 32));
+                usr = scale_at<WDT>(m->up_s, row * (H / 32));
+            }
+            // every load of the group is issued before any is used
+#pragma unroll
+            for (int cc = 0; cc < CPL; cc++) {
+                rg[r][cc] = load_raw(grow, cl[cc]);
+                ru[r][cc] = load_raw(urow, cl[cc]);
+                if constexpr (blocked<WDT>()) {
+                    hg[r][cc] = scale_bits<WDT>(gsr, chunk_block<WDT>(cl[cc]));
+                    hu[r][cc] = scale_bits<WDT>(usr, chunk_block<WDT>(cl[cc]));
+                }
+            }
+        }
+    };
+    const int p_first = gw * RP;
+    const bool early = PRE && (a.rt.E == 1 || min(p_first + RP, p_end) <= shared_pairs);
+    if (early) issue_group(p_first, M1Slots{0, 0, 0, 0, 0, 0, 0, 0});
     const M1Slots slots = m1_topk(a.rt, lane, lv, bv, s_words[threadIdx.x >> 6], gw == 0, a.ids_out, a.w_out,
                                   a.counts_out);
     // MXFP4 codes with bf16 x: x stays as bf16 pairs and the codes, converted
@@ -1135,49 +1187,8 @@ __global__ __launch_bounds__(kThreads) void k_gateup_m1(M1GateUpArgs a) {
     }
     };
     bool x_ready = false;
-    const int routed_pairs = a.k * a.I;
-    const size_t rbytes = row_bytes<WDT>(H);
-    for (int p = gw * RP; p < p_end; p += nwv * RP) {
-        const char *grow[RP], *urow[RP];
-        const void *gsr[RP], *usr[RP];
-        int slot[RP], irow[RP];
-#pragma unroll
-        for (int r = 0; r < RP; r++) {
-            const int q = min(p + r, p_end - 1);
-            size_t row;
-            const Mats *m;
-            if (q < routed_pairs) {
-                slot[r] = q / a.I;
-                irow[r] = q - slot[r] * a.I;
-                row = (size_t)slots.expert(slot[r]) * a.I + irow[r];
-                m = &a.routed;
-            } else {
-                slot[r] = -1;
-                irow[r] = q - routed_pairs;
-                row = irow[r];
-                m = &a.shared;
-            }
-            grow[r] = reinterpret_cast<const char *>(m->gate) + row * rbytes;
-            urow[r] = reinterpret_cast<const char *>(m->up) + row * rbytes;
-            if constexpr (blocked<WDT>()) {
-                gsr[r] = scale_at<WDT>(m->gate_s, row * (H / 32));
-                usr[r] = scale_at<WDT>(m->up_s, row * (H / 32));
-            }
-        }
-        // issue every load of the group first
-        u32x4 rg[RP][CPL], ru[RP][CPL];
-        uint16_t hg[RP][CPL], hu[RP][CPL];
-#pragma unroll
-        for (int r = 0; r < RP; r++)
-#pragma unroll
-            for (int cc = 0; cc < CPL; cc++) {
-                rg[r][cc] = load_raw(grow[r], cl[cc]);
-                ru[r][cc] = load_raw(urow[r], cl[cc]);
-                if constexpr (blocked<WDT>()) {
-                    hg[r][cc] = scale_bits<WDT>(gsr[r], chunk_block<WDT>(cl[cc]));
-                    hu[r][cc] = scale_bits<WDT>(usr[r], chunk_block<WDT>(cl[cc]));
-                }
-            }
+    for (int p = p_first; p < p_end; p += nwv * RP) {
+        if (!(early && p == p_first)) issue_group(p, slots);
         if (!x_ready) {
             convert_x();
             x_ready = true;
@@ -1388,15 +1399,20 @@ static void down_m1_dispatch(int n_tasks, int H, const M1DownArgs &a, hipStream_
 // Chunks per lane of a row of H elements, and the instantiated values.
 static int m1_cpl(int H, int N) { return (H / N + kWave - 1) / kWave; }
 
-template <int XDT, int WDT, int RP>
-static bool m1_gateup_dispatch(int cpl, const M1GateUpArgs &a, int grid, hipStream_t s) {
+template <int XDT, int WDT, int RP, bool PRE>
+static bool m1_gateup_dispatch_p(int cpl, const M1GateUpArgs &a, int grid, hipStream_t s) {
 #define M1_CASE(C) \
-    case C: launch_kernel((k_gateup_m1<XDT, WDT, C, RP>), dim3(grid), dim3(kThreads), 0, s, a); return true;
+    case C: launch_kernel((k_gateup_m1<XDT, WDT, C, RP, PRE>), dim3(grid), dim3(kThreads), 0, s, a); return true;
     switch (cpl) {
         M1_CASE(1) M1_CASE(2) M1_CASE(3) M1_CASE(4) M1_CASE(5) M1_CASE(6) M1_CASE(8)
     default: return false;
     }
 #undef M1_CASE
+}
+template <int XDT, int WDT, int RP>
+static bool m1_gateup_dispatch(int cpl, const M1GateUpArgs &a, int grid, hipStream_t s) {
+    return a.Is > 0 || a.rt.E == 1 ? m1_gateup_dispatch_p<XDT, WDT, RP, true>(cpl, a, grid, s)
+                                   : m1_gateup_dispatch_p<XDT, WDT, RP, false>(cpl, a, grid, s);
 }
 
 
