@@ -729,16 +729,23 @@ __global__ __launch_bounds__(kRouteWaves * kWave) void k_router_small(RouteSmall
     }
 }
 
-// One wave per token for the top-k, then one thread per route for its place
-// (routes of smaller experts, then earlier routes of the same expert: a
-// stable counting sort) and one thread per expert for its count; offsets and
-// the touched-expert list are block scans of the counts.
+// One wave per token for the top-k.  A token picks an expert at most once,
+// so each expert's set of tokens is a bit mask (bit t: token t picked it,
+// M <= 16), built with LDS atomic ORs: its population count is the expert's
+// count, and a route (t, expert e) takes sorted place offsets[e] plus the
+// number of earlier tokens in e's mask (routes grouped by expert, tokens
+// ascending: a stable counting sort).  Offsets and the touched-expert list
+// are block scans of the counts.  (It replaced a pass over all routes per
+// route and per expert: gpt-oss-shaped M = 16, 6.2 us with those passes.)
 constexpr int kSelWaves = kSmallM;
+static_assert(kSmallM <= 32, "a token set is a 32-bit mask");
 
 __global__ __launch_bounds__(kSelWaves * kWave) void k_select_small(RouteSmallArgs a) {
     __shared__ int s_ids[kSmallRoutes];
     __shared__ float s_logit[kSmallM * kMaxE];
     __shared__ float s_bias[kMaxE];
+    __shared__ uint32_t s_mask[kMaxE];
+    __shared__ int s_off[kMaxE];
     __shared__ int s_scan[4];
     __shared__ __align__(16) uint64_t s_words[kSelWaves][kWave];
     const int tid = threadIdx.x, wave = uniform(tid >> 6), lane = tid & 63;
@@ -746,28 +753,20 @@ __global__ __launch_bounds__(kSelWaves * kWave) void k_select_small(RouteSmallAr
     for (int i = tid; i < a.M * a.E; i += kSelWaves * kWave) s_logit[i] = a.logits[i];
     if (a.bias)
         for (int i = tid; i < a.E; i += kSelWaves * kWave) s_bias[i] = a.bias[i];
+    for (int i = tid; i < a.E; i += kSelWaves * kWave) s_mask[i] = 0u;
     __syncthreads();
     if (wave < a.M)
         topk_wave(s_logit + wave * a.E, a.bias ? s_bias : nullptr, a.E, a.k, a.select, a.bias_mode, lane,
                   a.ids + (size_t)wave * a.k, a.w + (size_t)wave * a.k, s_words[wave], s_ids + wave * a.k);
     __syncthreads();
-    if (tid < R) {
-        const int e = s_ids[tid];
-        int pos = 0;
-        for (int r = 0; r < R; r++) {
-            const int v = s_ids[r];
-            pos += (v < e) || (v == e && r < tid);
-        }
-        a.o.sorted[pos] = tid;
-        a.o.route_pos[tid] = pos;
-    }
-    int cnt = 0;
-    if (tid < a.E)
-        for (int r = 0; r < R; r++) cnt += s_ids[r] == tid;
+    if (tid < R) atomicOr(&s_mask[s_ids[tid]], 1u << (tid / a.k));
+    __syncthreads();
+    const int cnt = tid < a.E ? __popc(s_mask[tid]) : 0;
     int tot, atot;
-    const int off = block_scan_256(tid < a.E ? cnt : 0, s_scan, &tot);
-    const int aoff = block_scan_256(tid < a.E && cnt > 0 ? 1 : 0, s_scan, &atot);
+    const int off = block_scan_256(cnt, s_scan, &tot);
+    const int aoff = block_scan_256(cnt > 0 ? 1 : 0, s_scan, &atot);
     if (tid < a.E) {
+        s_off[tid] = off;
         a.o.counts[tid] = cnt;
         a.o.offsets[tid] = off;
         if (cnt > 0) a.o.active[1 + aoff] = tid;
@@ -775,6 +774,13 @@ __global__ __launch_bounds__(kSelWaves * kWave) void k_select_small(RouteSmallAr
     if (tid == 0) {
         a.o.offsets[a.E] = tot;
         a.o.active[0] = atot;
+    }
+    __syncthreads();
+    if (tid < R) {
+        const int e = s_ids[tid], t = tid / a.k;
+        const int pos = s_off[e] + __popc(s_mask[e] & ((1u << t) - 1u));
+        a.o.sorted[pos] = tid;
+        a.o.route_pos[tid] = pos;
     }
 }
 
