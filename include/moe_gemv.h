@@ -211,7 +211,10 @@ moe_status moe_combine(const moe_plan *plan, const float *act, const moe_weights
 /* The whole layer (a0-a7): y [M][H] fp32 out.  The shared expert, if any,
  * seeds the sum with weight 1 (deepseek2/state.rs,
  * RealDeepseek2State.shared_out).  ids_out [M][k], w_out [M][k] and
- * counts_out [E] are optional copies of the routing (NULL = not wanted). */
+ * counts_out [E] are optional copies of the routing (NULL = not wanted).
+ * With one expert (E = 1, k = 1: a dense layer) every route is expert 0 with
+ * weight 1 whatever its logit, so no router runs and the router weights are
+ * not read. */
 moe_status moe_forward(const moe_plan *plan, const void *x, const moe_weights *wts, int32_t M,
                        float *y, int32_t *ids_out, float *w_out, int32_t *counts_out, void *ws,
                        size_t ws_bytes, void *stream);

@@ -989,7 +989,7 @@ hipError_t launch_down_gemv(const Layer &L, const float *act, const float *share
 // weights, which the down kernel reads.  (Computing the logits inside every
 // gate/up workgroup instead of in a router kernel measured slower.)
 struct M1Route {
-    const float *logits, *bias;
+    const float *logits, *bias; // logits null: one expert, no router (the pick is expert 0, weight 1)
     int E, k, select, bias_mode;
 };
 
@@ -1015,6 +1015,15 @@ __device__ __forceinline__ M1Slots m1_topk(const M1Route &rt, int lane, const fl
                                            const float (&bv)[kKeysPerLane], uint64_t *words, bool writer,
                                            int32_t *ids_out, float *w_out, int32_t *counts_out) {
     M1Slots s{0, 0, 0, 0, 0, 0, 0, 0};
+    if (!rt.logits) {
+        // one expert and no router: the pick is expert 0 with weight 1
+        if (writer && lane == 0) {
+            ids_out[0] = 0;
+            w_out[0] = 1.0f;
+            if (counts_out) counts_out[0] = 1;
+        }
+        return s;
+    }
     if (rt.E <= kWave) {
         const LanePick p = topk_lane_small(lv[0], bv[0], rt.E, rt.k, rt.select, rt.bias_mode, lane, words);
         uint64_t m = __ballot(p.pick); // exactly k bits: the ranks are a permutation of 0..E-1
@@ -1081,8 +1090,8 @@ __global__ __launch_bounds__(kThreads) void k_gateup_m1(M1GateUpArgs a) {
     const int H = a.H, nch = H / N;
     // the logit row first: the top-k needs it, and nothing else, before it
     // can start
-    float lv[kKeysPerLane], bv[kKeysPerLane];
-    topk_load(a.rt.logits, a.rt.bias, a.rt.E, lane, lv, bv);
+    float lv[kKeysPerLane] = {}, bv[kKeysPerLane] = {};
+    if (a.rt.logits) topk_load(a.rt.logits, a.rt.bias, a.rt.E, lane, lv, bv);
     const float sc = a.tok_scale ? a.tok_scale[0] : 1.0f;
     // x chunks this lane multiplies, loaded as stored and converted after
     // the top-k (which does not need them), so that the top-k does not wait
@@ -1505,6 +1514,16 @@ constexpr int kCombineSlots = 8; // top-k slots a token (the plan's limit)
 // One thread per (token, 4 consecutive h): seed, then the shared expert's
 // slices in order, then slots j = 0..k-1, each slot's slices (partial sums of
 // a split reduction) summed in slice order before its weight is applied.
+// SU: later reduction slices loaded together.  With SU > 1 every slot's
+// loads of SU slices go out before any is added; each slot's slices are
+// still added in slice order, so the sums are the same bits as one slice at
+// a time.  Taken below 512 workgroups, where the chains of dependent loads
+// set the time (one-expert layer, M = 16, 16 slices: 7.0 against 8.9 us;
+// DeepSeek-V2-Lite shape, M = 16: 5.0 against 7.6 us; 256 experts, M = 16:
+// 4.4 against 7.7 us).  Above that the registers it holds cost more waves
+// than it saves (one-expert layer, M = 512, 1024 workgroups: 19.1 against
+// 13.2 us).
+template <int SU>
 __global__ __launch_bounds__(256) void k_combine(const float *y_routes, const float *y_shared,
                                                  const int32_t *route_pos, const float *w,
                                                  const float *seed, int M, int H, int k, int S,
@@ -1517,7 +1536,15 @@ __global__ __launch_bounds__(256) void k_combine(const float *y_routes, const fl
     if (y_shared) {
         const float *row = y_shared + (size_t)t * H;
         f32x4 v = reinterpret_cast<const f32x4 *>(row)[c];
-        for (int sl = 1; sl < Ss; sl++) v += reinterpret_cast<const f32x4 *>(row + sl * slab_s)[c];
+        for (int sl = 1; sl < Ss; sl += SU) {
+            f32x4 q[SU];
+#pragma unroll
+            for (int u = 0; u < SU; u++)
+                if (sl + u < Ss) q[u] = reinterpret_cast<const f32x4 *>(row + (sl + u) * slab_s)[c];
+#pragma unroll
+            for (int u = 0; u < SU; u++)
+                if (sl + u < Ss) v += q[u];
+        }
         acc += v;
     }
     // the slots' positions and weights, then (up to 8 slots) every slot's
@@ -1537,11 +1564,29 @@ __global__ __launch_bounds__(256) void k_combine(const float *y_routes, const fl
 #pragma unroll
     for (int j = 0; j < kCombineSlots; j++)
         if (j < k) v[j] = reinterpret_cast<const f32x4 *>(y_routes + (size_t)rp[j] * H)[c];
+    if constexpr (SU > 1) {
+        for (int sl = 1; sl < S; sl += SU) {
+            f32x4 q[kCombineSlots][SU];
+#pragma unroll
+            for (int j = 0; j < kCombineSlots; j++)
+#pragma unroll
+                for (int u = 0; u < SU; u++)
+                    if (j < k && sl + u < S)
+                        q[j][u] = reinterpret_cast<const f32x4 *>(y_routes + (size_t)rp[j] * H + (sl + u) * slab)[c];
+#pragma unroll
+            for (int j = 0; j < kCombineSlots; j++)
+#pragma unroll
+                for (int u = 0; u < SU; u++)
+                    if (j < k && sl + u < S) v[j] += q[j][u];
+        }
+    }
 #pragma unroll
     for (int j = 0; j < kCombineSlots; j++)
         if (j < k) {
-            const float *row = y_routes + (size_t)rp[j] * H;
-            for (int sl = 1; sl < S; sl++) v[j] += reinterpret_cast<const f32x4 *>(row + sl * slab)[c];
+            if constexpr (SU == 1) {
+                const float *row = y_routes + (size_t)rp[j] * H;
+                for (int sl = 1; sl < S; sl++) v[j] += reinterpret_cast<const f32x4 *>(row + sl * slab)[c];
+            }
             acc.x = fmaf(wt[j], v[j].x, acc.x);
             acc.y = fmaf(wt[j], v[j].y, acc.y);
             acc.z = fmaf(wt[j], v[j].z, acc.z);
@@ -1554,7 +1599,9 @@ hipError_t launch_combine(const Layer &L, const float *y_routes, const float *y_
                           const int32_t *route_pos, const float *w, const float *seed, int M,
                           float *y, hipStream_t s, int slices, int shared_slices) {
     const size_t n = (size_t)M * (L.H / 4);
-    launch_kernel(k_combine, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, y_routes, y_shared,
+    const unsigned grid = (unsigned)((n + 255) / 256);
+    const auto kern = (slices > 1 || shared_slices > 1) && grid < 512 ? k_combine<4> : k_combine<1>;
+    launch_kernel(kern, dim3(grid), dim3(256), 0, s, y_routes, y_shared,
                   route_pos, w, seed, M, L.H, L.k, slices, (size_t)M * L.k * L.H, shared_slices,
                   (size_t)M * L.H, y);
     return hipGetLastError();

@@ -72,6 +72,11 @@ hipError_t launch_route_small(const Layer &L, const void *x, const RouterW &rw, 
                               const float *tok_scale, int M, float *logits, int32_t *ids, float *w,
                               int32_t *counts, int32_t *offsets, int32_t *sorted, int32_t *route_pos,
                               int32_t *active, hipStream_t s);
+// The routing of a one-expert layer (k = 1), which needs no router: ids 0,
+// weights 1, the identity order, counts, offsets, the touched list and (tiles
+// non-null) the tile list of tile_rows-row tiles.  One launch.
+hipError_t launch_route_one(int M, int tile_rows, int32_t *ids, float *w, int32_t *counts, int32_t *offsets,
+                            int32_t *sorted, int32_t *route_pos, int32_t *active, int32_t *tiles, hipStream_t s);
 // Derive the active-expert list and the tile list from offsets alone.
 hipError_t launch_plan_from_offsets(int E, int tile_rows, const int32_t *offsets, int32_t *active,
                                     int32_t *tiles, hipStream_t s);

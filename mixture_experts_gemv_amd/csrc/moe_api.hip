@@ -491,7 +491,10 @@ static moe_status forward_impl(const moe_plan *p, const void *x, const moe_weigh
     uint16_t *xsplit = nullptr, *xhalf = nullptr;
     // the grouped-GEMM router on bf16 rows; without a norm weight it also
     // sums the squares of x for the pre-norm, and the top-k forms the scale
-    const bool mfma_router = mfma && L.rdt == moe::DT_BF16 && !wts->router_x_scale;
+    // one expert (k = 1): every route is expert 0 with weight 1 whatever its
+    // logit, so no router runs
+    const bool one = L.E == 1;
+    const bool mfma_router = mfma && !one && L.rdt == moe::DT_BF16 && !wts->router_x_scale;
     const bool rms_in_router = mfma_router && L.eps > 0.f && !norm_w && L.xdt == moe::DT_BF16;
     if (L.eps > 0.f) {
         sc = at<float>(ws, lay.tok_scale);
@@ -520,7 +523,11 @@ static moe_status forward_impl(const moe_plan *p, const void *x, const moe_weigh
     const bool single = M == 1 && !mfma && moe::m1_supported(L);
     if (single) {
         // one token: the gate/up kernel runs the top-k itself from the logits
-        STAGE(rec, moe::launch_router_small(L, x, router_w(p, wts), sc, M, lg, s), "router", MOE_STAGE_ROUTER);
+        if (!one)
+            STAGE(rec, moe::launch_router_small(L, x, router_w(p, wts), sc, M, lg, s), "router", MOE_STAGE_ROUTER);
+    } else if (one) {
+        STAGE(rec, moe::launch_route_one(M, rows, ids, w, counts, offsets, sorted, rpos, active, tiles, s),
+              "route (one expert)", MOE_STAGE_ROUTER);
     } else if (M <= moe::route_small_max_tokens() && !mfma) {
         STAGE(rec, moe::launch_route_small(L, x, router_w(p, wts), wts->bias, sc, M, lg, ids, w, counts, offsets,
                                            sorted, rpos, active, s),
@@ -566,7 +573,8 @@ static moe_status forward_impl(const moe_plan *p, const void *x, const moe_weigh
         STAGE(rec, moe::launch_combine(L, yr, ysh, rpos, w, residual, M, y, s, moe::down_ksplit(L, M, rows), 1),
               "combine", MOE_STAGE_COMBINE);
     } else if (single) {
-        STAGE(rec, moe::launch_gateup_m1(L, x, sc, routed_mats(wts), shared_mats(wts), lg, wts->bias, ids, w,
+        STAGE(rec, moe::launch_gateup_m1(L, x, sc, routed_mats(wts), shared_mats(wts), one ? nullptr : lg,
+                                         wts->bias, ids, w,
                                          counts_out, act, sact, s),
               "top-k + gate/up", MOE_STAGE_GATEUP);
         STAGE(rec, moe::launch_down_m1(L, act, sact, routed_mats(wts), shared_mats(wts), ids, w, residual, y, s),

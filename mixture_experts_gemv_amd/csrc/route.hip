@@ -784,6 +784,48 @@ __global__ __launch_bounds__(kSelWaves * kWave) void k_select_small(RouteSmallAr
     }
 }
 
+// One expert (a dense layer, k = 1): every route is expert 0 with weight 1
+// whatever its logit (a softmax over one logit, or one sigmoid score
+// normalised by itself), so the forward call runs no router.  The plan is
+// the identity order, one count, one touched expert and ceil(M / tile_rows)
+// tiles (pairs at tiles + 2 + E, E = 1).
+__global__ __launch_bounds__(256) void k_route_one(int M, int tile_rows, int32_t *ids, float *w, int32_t *counts,
+                                                   int32_t *offsets, int32_t *sorted, int32_t *route_pos,
+                                                   int32_t *active, int32_t *tiles) {
+    const int t = blockIdx.x * 256 + threadIdx.x;
+    if (t < M) {
+        ids[t] = 0;
+        w[t] = 1.0f;
+        sorted[t] = t;
+        route_pos[t] = t;
+    }
+    const int T = tiles ? (M + tile_rows - 1) / tile_rows : 0;
+    if (t < T) {
+        tiles[3 + 2 * t] = 0;
+        tiles[4 + 2 * t] = t * tile_rows;
+    }
+    if (t == 0) {
+        counts[0] = M;
+        offsets[0] = 0;
+        offsets[1] = M;
+        active[0] = 1;
+        active[1] = 0;
+        if (tiles) {
+            tiles[0] = T;
+            tiles[1] = 0;
+            tiles[2] = T;
+        }
+    }
+}
+
+hipError_t launch_route_one(int M, int tile_rows, int32_t *ids, float *w, int32_t *counts, int32_t *offsets,
+                            int32_t *sorted, int32_t *route_pos, int32_t *active, int32_t *tiles, hipStream_t s) {
+    if (M <= 0 || tile_rows <= 0) return hipErrorInvalidValue;
+    launch_kernel(k_route_one, dim3((M + 255) / 256), dim3(256), 0, s, M, tile_rows, ids, w, counts, offsets, sorted,
+                  route_pos, active, tiles);
+    return hipGetLastError();
+}
+
 int route_small_max_tokens() { return kSmallM; }
 
 template <int XDT>
