@@ -282,6 +282,10 @@ SMALL = [
                                 shared_inter=160, select=SOFTMAX_ALL_NORENORM, rms_eps=1e-6,
                                 expert_dtype=MXFP4, shared_dtype=MXFP4), (1, 9)),
     ("mx4-dense", dict(hidden=256, num_experts=1, top_k=1, expert_inter=1088, expert_dtype=MXFP4), (1, 16, 70)),
+    # one expert (no router runs) with the pre-norm and a logit bias: the
+    # token scale from the norm kernel, the routing from the one-expert kernel
+    ("dense-rms-bias", dict(hidden=256, num_experts=1, top_k=1, expert_inter=320, rms_eps=1e-6,
+                            bias_mode=BIAS_LOGIT, bias_kind="normal"), (1, 5, 40)),
     # the INT8 router: Q8_0 router rows and a per-element input scale
     ("q8router-scale", dict(hidden=288, num_experts=12, top_k=4, expert_inter=320, bias_mode=BIAS_LOGIT,
                             bias_kind="normal", router_dtype=Q8_0, router_x_scale="uniform",
@@ -341,6 +345,9 @@ MFMA_SMALL = [
     # one expert: a single ragged 160-row tile (M = 150), two 160-row tiles
     # (M = 300), three 128-row tiles (M = 330)
     ("dense-tiles", dict(hidden=256, num_experts=1, top_k=1, expert_inter=320), (150, 300, 330)),
+    # one expert with the pre-norm (scaled in the GEMM epilogue, no router)
+    ("dense-rms-bias", dict(hidden=256, num_experts=1, top_k=1, expert_inter=320, rms_eps=1e-6,
+                            bias_mode=BIAS_LOGIT, bias_kind="normal"), (70, 150)),
     # 256 experts: the sliced router's widest expert split (four 16-expert
     # tiles a wave), four logits a lane in the top-k, a 256-expert scatter
     ("e256-zipf", dict(hidden=256, num_experts=256, top_k=8, expert_inter=64, bias_mode=BIAS_LOGIT,
@@ -580,6 +587,8 @@ FUSED = [
      (512,), 2, True, True, False),
     ("q8router-norm-res", dict(hidden=256, num_experts=16, top_k=4, expert_inter=192, rms_eps=1e-6,
                                router_dtype=Q8_0, router_x_scale="uniform"), (1, 9, 100), 0, True, True, True),
+    ("dense-norm-res", dict(hidden=256, num_experts=1, top_k=1, expert_inter=320, rms_eps=1e-6),
+     (1, 5, 70), 0, True, True, False),
 ]
 
 
