@@ -1270,11 +1270,15 @@ __global__ __launch_bounds__(kThreads) void k_gateup_m1(M1GateUpArgs a) {
 // 9.2 against 10.1 us for 256 threads and three rounds, in a standalone
 // kernel), and 6 rows, so that the workgroups (two a CU) run in one wave
 // (layer 28.1 against 28.9 us with 4 rows; MXFP4 27.9 against 29.7 us).
+// At most 384 tasks (MXFP4 rows: 32-element chunks, 90 a row of 2880) take
+// 384 threads and 6 rows, so that a workgroup's threads are not half idle
+// (gpt-oss-shaped MXFP4 layer: 22.7 against 27.3 us a call; 8 rows 23.2).
 // Otherwise 256 threads and 4 rows take 4 rounds for Q8_0 (10.8 against
 // 11.7 us with 2), else 2 (MXFP4 at 4: 14.3 against 10.5 us, from the
 // register footprint of its 32-element chunks).
 constexpr int kM1Rows = 4, kM1WideRows = 6;
 constexpr int kM1WideThreads = 768;
+constexpr int kM1NarrowThreads = 384, kM1NarrowRows = 6;
 template <int WDT> constexpr int m1_unroll() { return WDT == DT_Q8 ? 4 : 2; }
 constexpr int kMaxSlots = 9; // top-k slots + the shared expert
 
@@ -1397,7 +1401,10 @@ __global__ __launch_bounds__(NT) void k_down_m1(M1DownArgs a) {
 
 template <int WDT>
 static void down_m1_dispatch(int n_tasks, int H, const M1DownArgs &a, hipStream_t s) {
-    if (n_tasks <= kM1WideThreads)
+    if (n_tasks <= kM1NarrowThreads)
+        launch_kernel((k_down_m1<WDT, kM1NarrowThreads, 1, kM1NarrowRows>),
+                      dim3((H + kM1NarrowRows - 1) / kM1NarrowRows), dim3(kM1NarrowThreads), 0, s, a);
+    else if (n_tasks <= kM1WideThreads)
         launch_kernel((k_down_m1<WDT, kM1WideThreads, 1, kM1WideRows>), dim3((H + kM1WideRows - 1) / kM1WideRows),
                       dim3(kM1WideThreads), 0, s, a);
     else
@@ -1458,12 +1465,17 @@ hipError_t launch_gateup_m1(const Layer &L, const void *x, const float *tok_scal
     a.total_pairs = L.k * L.I + a.Is;
     const int N = chunk_elems(L.edt);
     const int cpl = m1_cpl(L.H, N);
-    // Rows per load group: two for bf16 and fp32 rows of at most four chunks
-    // per lane (about 16 loads of a group in flight), else one.  With Q8_0
-    // and MXFP4 rows one row a group measured faster (gpt-oss shape, Q8_0:
-    // 16.9 against 18.1 us; MXFP4: 15.1 against 15.6 us; bf16 unchanged).
-    const int RP = cpl <= 4 && (L.edt == DT_BF16 || L.edt == DT_F32) ? 2 : 1;
-    const int max_waves = 2048;
+    // Rows per load group: two for bf16, fp32 and (with bf16 x) MXFP4 rows
+    // of at most four chunks per lane (about 16 loads of a group in flight),
+    // else one.  With Q8_0 rows one row a group measured faster (gpt-oss
+    // shape: 16.9 against 18.1 us; bf16 unchanged).  MXFP4 rows carry half
+    // the bytes of Q8_0 ones, so they take up to 3072 waves and two rows a
+    // group (gpt-oss shape, the layer call: 22.0 against 22.6 us with one
+    // row, 23.2 with two rows and 2048 waves; one row and 2048 waves: 27.3
+    // against 26.2 us with 3072, before the narrow down kernel).
+    const bool mx2 = L.edt == DT_MX4 && L.xdt == DT_BF16;
+    const int RP = cpl <= 4 && (L.edt == DT_BF16 || L.edt == DT_F32 || mx2) ? 2 : 1;
+    const int max_waves = L.edt == DT_MX4 ? 3072 : 2048;
     int ppw = (a.total_pairs + max_waves - 1) / max_waves;
     ppw = (ppw + RP - 1) / RP * RP;
     const int waves = (a.total_pairs + ppw - 1) / ppw;
@@ -1471,7 +1483,7 @@ hipError_t launch_gateup_m1(const Layer &L, const void *x, const float *tok_scal
     bool ok;
     if (L.xdt == DT_BF16) {
         if (L.edt == DT_Q8) ok = m1_gateup_dispatch<DT_BF16, DT_Q8, 1>(cpl, a, grid, s);
-        else if (L.edt == DT_MX4) ok = m1_gateup_dispatch<DT_BF16, DT_MX4, 1>(cpl, a, grid, s);
+        else if (L.edt == DT_MX4) ok = RP == 2 ? m1_gateup_dispatch<DT_BF16, DT_MX4, 2>(cpl, a, grid, s) : m1_gateup_dispatch<DT_BF16, DT_MX4, 1>(cpl, a, grid, s);
         else if (L.edt == DT_BF16) ok = RP == 2 ? m1_gateup_dispatch<DT_BF16, DT_BF16, 2>(cpl, a, grid, s) : m1_gateup_dispatch<DT_BF16, DT_BF16, 1>(cpl, a, grid, s);
         else ok = RP == 2 ? m1_gateup_dispatch<DT_BF16, DT_F32, 2>(cpl, a, grid, s) : m1_gateup_dispatch<DT_BF16, DT_F32, 1>(cpl, a, grid, s);
     } else {
