@@ -1273,12 +1273,17 @@ __global__ __launch_bounds__(kThreads) void k_gateup_m1(M1GateUpArgs a) {
 // At most 384 tasks (MXFP4 rows: 32-element chunks, 90 a row of 2880) take
 // 384 threads and 6 rows, so that a workgroup's threads are not half idle
 // (gpt-oss-shaped MXFP4 layer: 22.7 against 27.3 us a call; 8 rows 23.2).
+// Up to 1408 tasks take 704 threads, two chunks each and 4 rows, so that the
+// second round is full (DeepSeek-V2-Lite shape, 1408 chunks: 28.7 against
+// 29.1 us a call with 256 threads in 2.75 rounds; its dense layer, 1368
+// chunks: 25.0 against 25.6 us; 6 rows 30.2 and 26.6 us).
 // Otherwise 256 threads and 4 rows take 4 rounds for Q8_0 (10.8 against
 // 11.7 us with 2), else 2 (MXFP4 at 4: 14.3 against 10.5 us, from the
 // register footprint of its 32-element chunks).
 constexpr int kM1Rows = 4, kM1WideRows = 6;
 constexpr int kM1WideThreads = 768;
 constexpr int kM1NarrowThreads = 384, kM1NarrowRows = 6;
+constexpr int kM1TwoThreads = 704, kM1TwoRows = 4;
 template <int WDT> constexpr int m1_unroll() { return WDT == DT_Q8 ? 4 : 2; }
 constexpr int kMaxSlots = 9; // top-k slots + the shared expert
 
@@ -1407,6 +1412,9 @@ static void down_m1_dispatch(int n_tasks, int H, const M1DownArgs &a, hipStream_
     else if (n_tasks <= kM1WideThreads)
         launch_kernel((k_down_m1<WDT, kM1WideThreads, 1, kM1WideRows>), dim3((H + kM1WideRows - 1) / kM1WideRows),
                       dim3(kM1WideThreads), 0, s, a);
+    else if (n_tasks <= 2 * kM1TwoThreads)
+        launch_kernel((k_down_m1<WDT, kM1TwoThreads, 2, kM1TwoRows>), dim3((H + kM1TwoRows - 1) / kM1TwoRows),
+                      dim3(kM1TwoThreads), 0, s, a);
     else
         launch_kernel((k_down_m1<WDT, kThreads, m1_unroll<WDT>(), kM1Rows>), dim3((H + kM1Rows - 1) / kM1Rows),
                       dim3(kThreads), 0, s, a);
