@@ -236,9 +236,9 @@ moe_status moe_forward_noalloc(const moe_plan *plan, const void *x, const moe_we
                                void *stream);
 
 /* The layer with its neighbours fused (deepseek2/state.rs, module doc: the
- * post-attention RMSNorm with its weight, rms_norm(x, post_attention_layernorm),
- * feeds the router and the experts, and the routed sum plus the shared
- * expert is added to the residual stream, x += routed_sum + shared;
+ * post-attention RMSNorm with its weight feeds the router and the experts,
+ * and the routed sum plus the shared expert is added to the residual
+ * stream;
  * gptoss/state.rs, BatchedRoutedScratch: the routed sum reaches the stream
  * through one residual add):
  *   f_t = x_t / sqrt(mean_i x_ti^2 + rms_eps) * norm_weight,

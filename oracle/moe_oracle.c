@@ -11,7 +11,7 @@
  *   router logits   l[t][e] = sum_i x[t][i] * s[i] * Wr[e][i]
  *       llama/state.rs, RealLlamaState.router_logits_f32 (fp32 logits, one
  *       [num_experts] row per token) and deepseek2/state.rs module doc
- *       ("f @ router").  s is the INT8 router's per-element input scale
+ *       (the normed rows times the router).  s is the INT8 router's per-element input scale
  *       (llama/state.rs, RealLlamaState.router_ones; ones when absent) and
  *       Wr may be Q8_0 blocks (the INT8 router's rows).
  *   router bias     added to the logits BEFORE top-k
@@ -202,8 +202,8 @@ static double orc_row_dot(const void *base, int fmt, size_t r, size_t cols, cons
 }
 
 /* ---- step 0 (optional): RMS pre-norm, x / sqrt(mean(x^2) + eps) * gamma ----
- * deepseek2/state.rs module doc: f = rms_norm(x, post_attention_layernorm)
- * feeds the router and the experts.  gamma (norm_w, [H] in the x format) is
+ * deepseek2/state.rs module doc: the post-attention RMSNorm's output feeds
+ * the router and the experts.  gamma (norm_w, [H] in the x format) is
  * the norm's weight; NULL is unit gain. */
 static void norm_tokens(const orc_layer *L, int M, const void *x, const void *norm_w, double *xn)
 {
@@ -451,8 +451,8 @@ void orc_down(int H, int width, int fmt, const void *down, int mat, const double
  * counts[E], act[M*k][I] (route-major, r = t*k + j), y[M][H].
  * forced_ids (or NULL) fixes the selection, as described above. */
 /* The layer with its neighbours (deepseek2/state.rs module doc: the normed
- * rows f feed the router and the experts, and x += routed_sum + shared
- * SwiGLU(f); gptoss/state.rs, BatchedRoutedScratch: the routed sum reaches
+ * rows feed the router and the experts, and the routed sum plus the shared
+ * SwiGLU is added to the residual stream; gptoss/state.rs, BatchedRoutedScratch: the routed sum reaches
  * the stream through one residual add):
  *   y_t = residual_t + shared(f_t) + sum_j w_j expert_j(f_t),
  *   f_t = x_t / sqrt(mean(x_t^2) + eps) * norm_w.

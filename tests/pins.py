@@ -605,9 +605,9 @@ def pin_prenorm_scale_invariance():
 
 
 def pin_fused_norm_weight_and_residual():
-    """The fused neighbours (deepseek2/state.rs module doc: f = rms_norm(x,
-    post_attention_layernorm) feeds the router and the experts; x += routed
-    sum + shared expert).  A unit norm weight is the unit-gain pre-norm; the
+    """The fused neighbours (deepseek2/state.rs module doc: the post-attention
+    RMSNorm's output feeds the router and the experts; the routed sum plus the
+    shared expert is added to the residual stream).  A unit norm weight is the unit-gain pre-norm; the
     weighted norm stays invariant under scaling x; the residual adds to y."""
     spec = _spec(num_experts=6, top_k=2, rms_eps=1e-12, shared_inter=64, x_dtype=BF16, seed=31)
     layer = synth.make_layer(spec)
