@@ -286,6 +286,7 @@ SMALL = [
     # token scale from the norm kernel, the routing from the one-expert kernel
     ("dense-rms-bias", dict(hidden=256, num_experts=1, top_k=1, expert_inter=320, rms_eps=1e-6,
                             bias_mode=BIAS_LOGIT, bias_kind="normal"), (1, 5, 40)),
+    ("q8-dense", dict(hidden=256, num_experts=1, top_k=1, expert_inter=320, expert_dtype=Q8_0), (1, 5, 40)),
     # the INT8 router: Q8_0 router rows and a per-element input scale
     ("q8router-scale", dict(hidden=288, num_experts=12, top_k=4, expert_inter=320, bias_mode=BIAS_LOGIT,
                             bias_kind="normal", router_dtype=Q8_0, router_x_scale="uniform",
@@ -348,6 +349,8 @@ MFMA_SMALL = [
     # one expert with the pre-norm (scaled in the GEMM epilogue, no router)
     ("dense-rms-bias", dict(hidden=256, num_experts=1, top_k=1, expert_inter=320, rms_eps=1e-6,
                             bias_mode=BIAS_LOGIT, bias_kind="normal"), (70, 150)),
+    # Q8_0 one-expert layer: one 96-row tile (M = 70), two (M = 150)
+    ("q8-dense", dict(hidden=256, num_experts=1, top_k=1, expert_inter=320, expert_dtype=Q8_0), (70, 150)),
     # 256 experts: the sliced router's widest expert split (four 16-expert
     # tiles a wave), four logits a lane in the top-k, a 256-expert scatter
     ("e256-zipf", dict(hidden=256, num_experts=256, top_k=8, expert_inter=64, bias_mode=BIAS_LOGIT,
