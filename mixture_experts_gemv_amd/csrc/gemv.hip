@@ -457,13 +457,28 @@ struct StreamGateUp {
     int M, H, k, E, I, Is;
     float limit;
     float *act, *shared_act;
+    // sel.logits non-null (M <= 16): every workgroup runs the batch's
+    // selection in its prologue (select_small) instead of reading offsets,
+    // sorted and active, and workgroup 0 writes it for the down kernel and
+    // the combine, so that no selection kernel runs between the router and
+    // this kernel
+    SelectSmall sel;
 };
 constexpr int kStreamThreads = 1024;
 constexpr int kStreamWaves = kStreamThreads / kWave;
+static_assert(kStreamWaves >= kSelMaxM, "one wave a token for the fused selection");
 
-// LDS bytes of the streamed gate/up kernel for an M-token batch.
-static size_t stream_lds_bytes(const Layer &L, int M) {
+// LDS bytes of the streamed gate/up kernel for an M-token batch: the batch,
+// route tokens, token scales, the touched list and offsets, then (with the
+// fused selection, from a 16-byte boundary) the selection's scratch.
+static size_t stream_lds_base(const Layer &L, int M) {
     return (size_t)M * L.H * 2 + (size_t)M * L.k * 4 + (size_t)M * 4 + (size_t)(2 * kMaxE + 2) * 4;
+}
+static size_t stream_lds_bytes(const Layer &L, int M, bool sel) {
+    const size_t base = stream_lds_base(L, M);
+    if (!sel) return base;
+    return (base + 15) / 16 * 16 + (size_t)kStreamWaves * kWave * 8 + (size_t)M * L.E * 4 + (size_t)L.E * 8 +
+           (size_t)M * L.k * 4 + 16;
 }
 
 template <int WDT, int CPL>
@@ -480,11 +495,24 @@ __global__ __launch_bounds__(kStreamThreads) void k_gateup_stream(StreamGateUp a
     int *s_off = s_act + kMaxE + 1;                                     // [E + 1] offsets
     for (int q = tid; q < a.M * H / 8; q += kStreamThreads)
         reinterpret_cast<u32x4 *>(s_x)[q] = reinterpret_cast<const u32x4 *>(a.x)[q];
-    for (int q = tid; q < R; q += kStreamThreads) s_tok[q] = a.sorted[q] / a.k;
     for (int q = tid; q < a.M; q += kStreamThreads) s_sc[q] = a.tok_scale ? a.tok_scale[q] : 1.0f;
-    for (int q = tid; q <= a.E; q += kStreamThreads) {
-        s_act[q] = a.active[q];
-        s_off[q] = a.offsets[q];
+    if (a.sel.logits) {
+        // the selection's scratch after the offsets (layout as stream_lds_bytes)
+        const size_t o = ((size_t)(reinterpret_cast<unsigned char *>(s_off + kMaxE + 1) - s_dyn) + 15) / 16 * 16;
+        uint64_t *s_words = reinterpret_cast<uint64_t *>(s_dyn + o);                     // [waves][64]
+        float *s_logit = reinterpret_cast<float *>(s_words + kStreamWaves * kWave);        // [M][E]
+        float *s_bias = s_logit + a.M * a.E;                                               // [E]
+        uint32_t *s_mask = reinterpret_cast<uint32_t *>(s_bias + a.E);                     // [E]
+        int *s_ids = reinterpret_cast<int *>(s_mask + a.E);                                // [R]
+        int *s_scan = s_ids + R;                                                           // [4]
+        select_small(a.sel, blockIdx.x == 0, s_logit, s_bias, s_mask, s_ids, s_scan, s_words, s_off, s_act,
+                     s_tok);
+    } else {
+        for (int q = tid; q < R; q += kStreamThreads) s_tok[q] = a.sorted[q] / a.k;
+        for (int q = tid; q <= a.E; q += kStreamThreads) {
+            s_act[q] = a.active[q];
+            s_off[q] = a.offsets[q];
+        }
     }
     __syncthreads();
     const int routed_pairs = s_act[0] * a.I;
@@ -602,16 +630,28 @@ static bool gateup_stream_dispatch(int cpl, const StreamGateUp &a, int grid, siz
 // (the shared expert's in the same format), at most 4 chunks a lane (2 for
 // MXFP4), and the batch within the LDS budget.  Returns false to leave the call to the
 // per-row kernel.
+// Whether the streamed gate/up kernel takes an M-token batch (with the
+// selection fused into it when sel).
+static bool stream_ok(const Layer &L, int M, bool shared, bool sel) {
+    const int Is = shared ? L.Is : 0;
+    if (L.xdt != DT_BF16 || L.edt == DT_F32 || (Is > 0 && L.sdt != L.edt) || L.E > kMaxE) return false;
+    if (sel && (M > kSelMaxM || M < 1)) return false;
+    if (stream_lds_bytes(L, M, sel) > kStreamLds) return false;
+    const int cpl = (L.H / chunk_elems(L.edt) + kWave - 1) / kWave;
+    return cpl <= (L.edt == DT_MX4 ? 2 : 4); // (MXFP4 at 3 or more would spill)
+}
+
+bool gateup_stream_selects(const Layer &L, int M, bool shared) { return stream_ok(L, M, shared, true); }
+
 static bool launch_gateup_stream(const Layer &L, const void *x, const float *tok_scale, const Mats &routed,
                                  const Mats &shared, const Routing &rt, int M, float *act, float *shared_act,
-                                 hipStream_t s) {
+                                 hipStream_t s, const SelectSmall *sel) {
     const int Is = shared_act ? L.Is : 0;
-    if (L.xdt != DT_BF16 || L.edt == DT_F32 || (Is > 0 && L.sdt != L.edt) || !act || L.E > kMaxE) return false;
-    const size_t lds = stream_lds_bytes(L, M);
-    if (lds > kStreamLds) return false;
+    if (!act || !stream_ok(L, M, shared_act != nullptr, sel != nullptr)) return false;
+    const size_t lds = stream_lds_bytes(L, M, sel != nullptr);
     const int cpl = (L.H / chunk_elems(L.edt) + kWave - 1) / kWave;
-    if (cpl > (L.edt == DT_MX4 ? 2 : 4)) return false; // (MXFP4 at 3 or more would spill)
     StreamGateUp a;
+    a.sel = sel ? *sel : SelectSmall{};
     a.x = x;
     a.tok_scale = tok_scale;
     a.routed = routed;
@@ -636,7 +676,7 @@ static bool launch_gateup_stream(const Layer &L, const void *x, const float *tok
 
 hipError_t launch_gateup_gemv(const Layer &L, const void *x, const float *tok_scale, const Mats &routed,
                               const Mats &shared, const Routing &rt, int M, float *act,
-                              float *shared_act, hipStream_t s) {
+                              float *shared_act, hipStream_t s, const SelectSmall *sel) {
     RowsGateUp a;
     a.x = x;
     a.tok_scale = tok_scale;
@@ -656,7 +696,8 @@ hipError_t launch_gateup_gemv(const Layer &L, const void *x, const float *tok_sc
     a.limit = L.limit;
     a.act = act;
     a.shared_act = shared_act;
-    if (launch_gateup_stream(L, x, tok_scale, routed, shared, rt, M, act, shared_act, s)) return hipGetLastError();
+    if (launch_gateup_stream(L, x, tok_scale, routed, shared, rt, M, act, shared_act, s, sel)) return hipGetLastError();
+    if (sel) return hipErrorInvalidValue; // the caller checked gateup_stream_selects
     const int xb = L.xdt == DT_BF16 ? 2 : 4;
     a.ncap = gemv_stage_tokens(L);
     if (a.ncap < 1) return hipErrorInvalidValue;

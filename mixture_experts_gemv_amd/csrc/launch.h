@@ -84,9 +84,14 @@ hipError_t launch_plan_from_offsets(int E, int tile_rows, const int32_t *offsets
 // GEMV path (any M; the expert's vectors are staged in LDS).
 // Tokens one LDS stage of the gate/up kernel holds (0: hidden too large).
 int gemv_stage_tokens(const Layer &L);
+// With sel (M <= 16 tokens, gateup_stream_selects true) the streamed kernel
+// runs the batch's selection from sel->logits itself and writes it to sel's
+// outputs; rt's offsets, sorted and active are then those outputs.
+struct SelectSmall;
+bool gateup_stream_selects(const Layer &L, int M, bool shared);
 hipError_t launch_gateup_gemv(const Layer &L, const void *x, const float *tok_scale, const Mats &routed,
                               const Mats &shared, const Routing &rt, int M, float *act,
-                              float *shared_act, hipStream_t s);
+                              float *shared_act, hipStream_t s, const SelectSmall *sel = nullptr);
 // Per-route down products, split over the reduction:
 // y_routes [down_gemv_slices(I, edt)][M*k][H], y_shared [down_gemv_slices(Is, sdt)][M][H].
 hipError_t launch_down_gemv(const Layer &L, const float *act, const float *shared_act, const Mats &routed,

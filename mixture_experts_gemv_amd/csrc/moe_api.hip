@@ -11,6 +11,7 @@
 #include "common.h"
 #include "launch.h"
 #include "moe_gemv.h"
+#include "topk.h"
 
 struct moe_plan {
     moe_config cfg;
@@ -521,6 +522,10 @@ static moe_status forward_impl(const moe_plan *p, const void *x, const moe_weigh
     int32_t *tiles = lay.max_tiles ? at<int32_t>(ws, lay.tiles) : nullptr;
     const int rows = moe::mfma_tile_rows(L, M); // tile height of the grouped GEMMs
     const bool single = M == 1 && !mfma && moe::m1_supported(L);
+    // small batches on the streamed gate/up kernel: it runs the selection in
+    // its prologue, so only the router runs before it
+    const bool fuse_sel = !single && !mfma && !one && M <= moe::route_small_max_tokens() &&
+                          moe::gateup_stream_selects(L, M, L.Is > 0);
     if (single) {
         // one token: the gate/up kernel runs the top-k itself from the logits
         if (!one)
@@ -528,6 +533,8 @@ static moe_status forward_impl(const moe_plan *p, const void *x, const moe_weigh
     } else if (one) {
         STAGE(rec, moe::launch_route_one(M, rows, ids, w, counts, offsets, sorted, rpos, active, tiles, s),
               "route (one expert)", MOE_STAGE_ROUTER);
+    } else if (fuse_sel) {
+        STAGE(rec, moe::launch_router_small(L, x, router_w(p, wts), sc, M, lg, s), "router", MOE_STAGE_ROUTER);
     } else if (M <= moe::route_small_max_tokens() && !mfma) {
         STAGE(rec, moe::launch_route_small(L, x, router_w(p, wts), wts->bias, sc, M, lg, ids, w, counts, offsets,
                                            sorted, rpos, active, s),
@@ -580,7 +587,10 @@ static moe_status forward_impl(const moe_plan *p, const void *x, const moe_weigh
         STAGE(rec, moe::launch_down_m1(L, act, sact, routed_mats(wts), shared_mats(wts), ids, w, residual, y, s),
               "down + combine", MOE_STAGE_DOWN);
     } else {
-        STAGE(rec, moe::launch_gateup_gemv(L, x, sc, routed_mats(wts), shared_mats(wts), rt, M, act, sact, s),
+        const moe::SelectSmall sel{lg, L.bias_mode ? wts->bias : nullptr, M, L.E, L.k, L.select, L.bias_mode,
+                                   ids, w, counts, offsets, sorted, rpos, active};
+        STAGE(rec, moe::launch_gateup_gemv(L, x, sc, routed_mats(wts), shared_mats(wts), rt, M, act, sact, s,
+                                           fuse_sel ? &sel : nullptr),
               "gate/up", MOE_STAGE_GATEUP);
         STAGE(rec, moe::launch_down_gemv(L, act, sact, routed_mats(wts), shared_mats(wts), rt, M, yr, ysh, s),
               "down", MOE_STAGE_DOWN);

@@ -217,37 +217,6 @@ hipError_t launch_router(const Layer &L, const void *x, const RouterW &rw, const
 }
 
 // ---------------------------------------------------------------- wave top-k
-// One wave per token.  Selection key s = logit (+ bias for LOGIT and
-// SELECT_ONLY); softmax input u = logit (+ bias for LOGIT); descending key,
-// ties to the lower expert id.  Up to 64 experts: one expert a lane and a
-// rank count over the wave's words in LDS (`words`, 64 entries); more: lane
-// l holds experts l, l+64, l+128, l+192 and k rounds of a wave argmax pick
-// them.  Pick j (descending key) goes to ids_row[j] and w_row[j].
-__device__ void topk_wave(const float *lrow, const float *bias, int E, int k, int select,
-                          int bias_mode, int lane, int32_t *ids_row, float *w_row, uint64_t *words,
-                          int *lds_ids = nullptr) {
-    if (E <= kWave) {
-        const int e = min(lane, E - 1);
-        const float lv = lrow[e];
-        const float bv = bias ? bias[e] : 0.f;
-        const LanePick p = topk_lane_small(lv, bv, E, k, select, bias_mode, lane, words);
-        if (p.pick) {
-            ids_row[p.rank] = lane;
-            w_row[p.rank] = p.w;
-            if (lds_ids) lds_ids[p.rank] = lane;
-        }
-        return;
-    }
-    int id;
-    float wt;
-    topk_wave_core(lrow, bias, E, k, select, bias_mode, lane, &id, &wt);
-    if (lane < k) {
-        ids_row[lane] = id;
-        w_row[lane] = wt;
-        if (lds_ids) lds_ids[lane] = id;
-    }
-}
-
 __global__ __launch_bounds__(256) void k_topk(const float *logits, const float *bias, int M, int E,
                                               int k, int select, int bias_mode, int32_t *ids,
                                               float *w) {
@@ -416,27 +385,6 @@ struct PermuteSmem {
     int scan[kMaxE + 1];
 };
 
-// Exclusive scan of v over threads 0..255 (others pass 0); returns the
-// thread's exclusive prefix and the total in *total.  All threads of the
-// block call it; the block has at least 256 threads.  Waves 0-3 scan their
-// 64 values with shuffles, then add the totals of the waves before them.
-__device__ int block_scan_256(int v, int *lds /*[>= 4]*/, int *total) {
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    int x = tid < 256 ? v : 0;
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-        const int y = __shfl_up(x, off);
-        if (lane >= off) x += y;
-    }
-    if (wave < 4 && lane == kWave - 1) lds[wave] = x;
-    __syncthreads();
-    int before = 0;
-#pragma unroll
-    for (int w = 0; w < 4; w++) before += (w < wave) ? lds[w] : 0;
-    *total = lds[0] + lds[1] + lds[2] + lds[3];
-    __syncthreads();
-    return tid < 256 ? x + before - v : 0;
-}
 
 // Touched-expert list and GEMM tile list.  Tile list layout (E experts):
 //   tiles[0]           number of tiles T
@@ -729,59 +677,25 @@ __global__ __launch_bounds__(kRouteWaves * kWave) void k_router_small(RouteSmall
     }
 }
 
-// One wave per token for the top-k.  A token picks an expert at most once,
-// so each expert's set of tokens is a bit mask (bit t: token t picked it,
-// M <= 16), built with LDS atomic ORs: its population count is the expert's
-// count, and a route (t, expert e) takes sorted place offsets[e] plus the
-// number of earlier tokens in e's mask (routes grouped by expert, tokens
-// ascending: a stable counting sort).  Offsets and the touched-expert list
-// are block scans of the counts.  (It replaced a pass over all routes per
-// route and per expert: gpt-oss-shaped M = 16, 6.2 us with those passes.)
+// The selection as one workgroup of kSmallM waves (select_small; the
+// streamed gate/up kernel runs the same selection in its prologue instead,
+// when it takes the batch).  (The per-expert bit masks replaced a pass over
+// all routes per route and per expert: gpt-oss-shaped M = 16, 6.2 us with
+// those passes.)
 constexpr int kSelWaves = kSmallM;
-static_assert(kSmallM <= 32, "a token set is a 32-bit mask");
+static_assert(kSmallM <= kSelMaxM, "select_small takes at most kSelMaxM tokens");
 
 __global__ __launch_bounds__(kSelWaves * kWave) void k_select_small(RouteSmallArgs a) {
     __shared__ int s_ids[kSmallRoutes];
     __shared__ float s_logit[kSmallM * kMaxE];
     __shared__ float s_bias[kMaxE];
     __shared__ uint32_t s_mask[kMaxE];
-    __shared__ int s_off[kMaxE];
+    __shared__ int s_off[kMaxE + 1], s_act[kMaxE + 1];
     __shared__ int s_scan[4];
     __shared__ __align__(16) uint64_t s_words[kSelWaves][kWave];
-    const int tid = threadIdx.x, wave = uniform(tid >> 6), lane = tid & 63;
-    const int R = a.M * a.k;
-    for (int i = tid; i < a.M * a.E; i += kSelWaves * kWave) s_logit[i] = a.logits[i];
-    if (a.bias)
-        for (int i = tid; i < a.E; i += kSelWaves * kWave) s_bias[i] = a.bias[i];
-    for (int i = tid; i < a.E; i += kSelWaves * kWave) s_mask[i] = 0u;
-    __syncthreads();
-    if (wave < a.M)
-        topk_wave(s_logit + wave * a.E, a.bias ? s_bias : nullptr, a.E, a.k, a.select, a.bias_mode, lane,
-                  a.ids + (size_t)wave * a.k, a.w + (size_t)wave * a.k, s_words[wave], s_ids + wave * a.k);
-    __syncthreads();
-    if (tid < R) atomicOr(&s_mask[s_ids[tid]], 1u << (tid / a.k));
-    __syncthreads();
-    const int cnt = tid < a.E ? __popc(s_mask[tid]) : 0;
-    int tot, atot;
-    const int off = block_scan_256(cnt, s_scan, &tot);
-    const int aoff = block_scan_256(cnt > 0 ? 1 : 0, s_scan, &atot);
-    if (tid < a.E) {
-        s_off[tid] = off;
-        a.o.counts[tid] = cnt;
-        a.o.offsets[tid] = off;
-        if (cnt > 0) a.o.active[1 + aoff] = tid;
-    }
-    if (tid == 0) {
-        a.o.offsets[a.E] = tot;
-        a.o.active[0] = atot;
-    }
-    __syncthreads();
-    if (tid < R) {
-        const int e = s_ids[tid], t = tid / a.k;
-        const int pos = s_off[e] + __popc(s_mask[e] & ((1u << t) - 1u));
-        a.o.sorted[pos] = tid;
-        a.o.route_pos[tid] = pos;
-    }
+    const SelectSmall sel{a.logits, a.bias, a.M, a.E, a.k, a.select, a.bias_mode, a.ids, a.w,
+                          a.o.counts, a.o.offsets, a.o.sorted, a.o.route_pos, a.o.active};
+    select_small(sel, true, s_logit, s_bias, s_mask, s_ids, s_scan, &s_words[0][0], s_off, s_act, nullptr);
 }
 
 // One expert (a dense layer, k = 1): every route is expert 0 with weight 1

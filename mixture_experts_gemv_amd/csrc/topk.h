@@ -178,4 +178,139 @@ __device__ inline int pick_rank(int my_id, int k, int lane) {
     return lane < k ? rank : 0;
 }
 
+// Exclusive scan of v over threads 0..255 (others pass 0); returns the
+// thread's exclusive prefix and the total in *total.  All threads of the
+// block call it; the block has at least 256 threads.  Waves 0-3 scan their
+// 64 values with shuffles, then add the totals of the waves before them.
+__device__ inline int block_scan_256(int v, int *lds /*[>= 4]*/, int *total) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    int x = tid < 256 ? v : 0;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        const int y = __shfl_up(x, off);
+        if (lane >= off) x += y;
+    }
+    if (wave < 4 && lane == kWave - 1) lds[wave] = x;
+    __syncthreads();
+    int before = 0;
+#pragma unroll
+    for (int w = 0; w < 4; w++) before += (w < wave) ? lds[w] : 0;
+    *total = lds[0] + lds[1] + lds[2] + lds[3];
+    __syncthreads();
+    return tid < 256 ? x + before - v : 0;
+}
+
+
+// One wave per token.  Selection key s = logit (+ bias for LOGIT and
+// SELECT_ONLY); softmax input u = logit (+ bias for LOGIT); descending key,
+// ties to the lower expert id.  Up to 64 experts: one expert a lane and a
+// rank count over the wave's words in LDS (`words`, 64 entries); more: lane
+// l holds experts l, l+64, l+128, l+192 and k rounds of a wave argmax pick
+// them.  Pick j (descending key) goes to ids_row[j] and w_row[j] (both skipped
+// when ids_row is null) and to lds_ids[j] when given.
+__device__ inline void topk_wave(const float *lrow, const float *bias, int E, int k, int select,
+                          int bias_mode, int lane, int32_t *ids_row, float *w_row, uint64_t *words,
+                          int *lds_ids = nullptr) {
+    if (E <= kWave) {
+        const int e = min(lane, E - 1);
+        const float lv = lrow[e];
+        const float bv = bias ? bias[e] : 0.f;
+        const LanePick p = topk_lane_small(lv, bv, E, k, select, bias_mode, lane, words);
+        if (p.pick) {
+            if (ids_row) {
+                ids_row[p.rank] = lane;
+                w_row[p.rank] = p.w;
+            }
+            if (lds_ids) lds_ids[p.rank] = lane;
+        }
+        return;
+    }
+    int id;
+    float wt;
+    topk_wave_core(lrow, bias, E, k, select, bias_mode, lane, &id, &wt);
+    if (lane < k) {
+        if (ids_row) {
+            ids_row[lane] = id;
+            w_row[lane] = wt;
+        }
+        if (lds_ids) lds_ids[lane] = id;
+    }
+}
+
+
+// The selection of a batch of M <= 16 tokens in one workgroup (at least
+// max(M, 4) waves).  One wave per token for the top-k.  A token picks an
+// expert at most once, so each expert's set of tokens is a bit mask (bit t:
+// token t picked it), built with LDS atomic ORs: its population count is the
+// expert's count, and a route (t, expert e) takes sorted place offsets[e]
+// plus the number of earlier tokens in e's mask (routes grouped by expert,
+// tokens ascending: a stable counting sort).  Offsets and the touched-expert
+// list are block scans of the counts.  The workgroup's own copy of the
+// result goes to LDS (s_off [E + 1], s_act [1 + E], s_tok [M * k]: the token
+// of each sorted place, when given); with `writer` it is also written to
+// global memory (ids, w [M][k]; counts [E]; offsets [E + 1]; sorted and
+// route_pos [M * k]; active [1 + E]).  LDS scratch: s_logit [M * E], s_bias
+// [E], s_mask [E], s_ids [M * k], s_scan [4], s_words [waves][64] (16-byte
+// aligned).  Every thread of the workgroup calls it; it ends on a barrier.
+constexpr int kSelMaxM = 16;
+static_assert(kSelMaxM <= 32, "a token set is a 32-bit mask");
+struct SelectSmall {
+    const float *logits, *bias; // logits [M][E] fp32; bias [E] or null
+    int M, E, k, select, bias_mode;
+    int32_t *ids;
+    float *w;
+    int32_t *counts, *offsets, *sorted, *route_pos, *active;
+};
+__device__ inline void select_small(const SelectSmall &a, bool writer, float *s_logit, float *s_bias,
+                                    uint32_t *s_mask, int *s_ids, int *s_scan, uint64_t *s_words, int *s_off,
+                                    int *s_act, int *s_tok) {
+    const int tid = threadIdx.x, nthr = blockDim.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6),
+              lane = tid & 63;
+    const int R = a.M * a.k;
+    for (int i = tid; i < a.M * a.E; i += nthr) s_logit[i] = a.logits[i];
+    if (a.bias)
+        for (int i = tid; i < a.E; i += nthr) s_bias[i] = a.bias[i];
+    for (int i = tid; i < a.E; i += nthr) s_mask[i] = 0u;
+    __syncthreads();
+    if (wave < a.M)
+        topk_wave(s_logit + wave * a.E, a.bias ? s_bias : nullptr, a.E, a.k, a.select, a.bias_mode, lane,
+                  writer ? a.ids + (size_t)wave * a.k : nullptr, writer ? a.w + (size_t)wave * a.k : nullptr,
+                  s_words + (size_t)wave * kWave, s_ids + wave * a.k);
+    __syncthreads();
+    if (tid < R) atomicOr(&s_mask[s_ids[tid]], 1u << (tid / a.k));
+    __syncthreads();
+    const int cnt = tid < a.E ? __popc(s_mask[tid]) : 0;
+    int tot, atot;
+    const int off = block_scan_256(cnt, s_scan, &tot);
+    const int aoff = block_scan_256(cnt > 0 ? 1 : 0, s_scan, &atot);
+    if (tid < a.E) {
+        s_off[tid] = off;
+        if (cnt > 0) s_act[1 + aoff] = tid;
+        if (writer) {
+            a.counts[tid] = cnt;
+            a.offsets[tid] = off;
+            if (cnt > 0) a.active[1 + aoff] = tid;
+        }
+    }
+    if (tid == 0) {
+        s_off[a.E] = tot;
+        s_act[0] = atot;
+        if (writer) {
+            a.offsets[a.E] = tot;
+            a.active[0] = atot;
+        }
+    }
+    __syncthreads();
+    if (tid < R) {
+        const int e = s_ids[tid], t = tid / a.k;
+        const int pos = s_off[e] + __popc(s_mask[e] & ((1u << t) - 1u));
+        if (s_tok) s_tok[pos] = t;
+        if (writer) {
+            a.sorted[pos] = tid;
+            a.route_pos[tid] = pos;
+        }
+    }
+    __syncthreads();
+}
+
 } // namespace moe
