@@ -354,7 +354,7 @@ MFMA_SMALL = [
     # 256 experts: the sliced router's widest expert split (four 16-expert
     # tiles a wave), four logits a lane in the top-k, a 256-expert scatter
     ("e256-zipf", dict(hidden=256, num_experts=256, top_k=8, expert_inter=64, bias_mode=BIAS_LOGIT,
-                       bias_kind="zipf"), (70, 300)),
+                       bias_kind="zipf"), (40, 70, 300)),
     # the INT8 router on the grouped-GEMM path (its logits from the GEMV router)
     ("q8router-scale", dict(hidden=256, num_experts=16, top_k=4, expert_inter=192, router_dtype=Q8_0,
                             router_x_scale="uniform", rms_eps=1e-6), (70, 130)),
