@@ -1521,7 +1521,9 @@ hipError_t launch_gateup_m1(const Layer &L, const void *x, const float *tok_scal
     // the bytes of Q8_0 ones, so they take up to 3072 waves and two rows a
     // group (gpt-oss shape, the layer call: 22.0 against 22.6 us with one
     // row, 23.2 with two rows and 2048 waves; one row and 2048 waves: 27.3
-    // against 26.2 us with 3072, before the narrow down kernel).
+    // against 26.2 us with 3072, before the narrow down kernel).  Q8_0 rows
+    // keep 2048 waves (the gpt-oss-shaped call: 28.0 against 29.4 us with
+    // 2560 and 28.1 with 3072).
     const bool mx2 = L.edt == DT_MX4 && L.xdt == DT_BF16;
     const int RP = cpl <= 4 && (L.edt == DT_BF16 || L.edt == DT_F32 || mx2) ? 2 : 1;
     const int max_waves = L.edt == DT_MX4 ? 3072 : 2048;
